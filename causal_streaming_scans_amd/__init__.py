@@ -1,0 +1,205 @@
+"""MI355X (gfx950) forward path of second-order Higher-order Linear Attention.
+
+Thin Python binding over the C ABI of ``libhla.so`` (``include/hla.h``): it
+only checks tensor shapes, allocates outputs and the workspace with PyTorch,
+and passes raw device pointers plus the current HIP stream.  Every step of
+the computation runs in the library's HIP kernels; there is no CPU path, and
+every entry point raises ``HLAError`` when the library is not built.
+
+Operators (page: "Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)",
+gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",
+"2. ... (AHLA)", "4. ... Escaneos Asociativos"):
+
+    hla2        o = tril(tril(QK^T) tril(QK^T)^T) V        (optional decay g_h)
+    hla2_ratio  the same over its v == 1 denominator
+    ahla        o = tril(QK^T) tril(QK^T) V
+    ahla_ratio  the same over its v == 1 denominator
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["HLAError", "VARIANTS", "load", "library_path", "hla_forward", "hla_step",
+           "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libhla.so")
+_lib = None
+
+VARIANTS = {"hla2": 0, "hla2_ratio": 1, "ahla": 2, "ahla_ratio": 3}
+_DTYPES = {"f32": 0, "bf16": 1}
+MAX_DECAY_HEADS = 256
+
+
+class HLAError(RuntimeError):
+    """Raised for a missing library or a non-zero hla_status."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libhla.so (after torch, so that both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise HLAError(f"{_LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; "
+                       f"g.build()'` or `python causal_streaming_scans_amd/build.py`")
+    import torch  # noqa: F401  (binds the library to torch's HIP runtime)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.hla_state_floats.argtypes = [I, I, I]
+    lib.hla_state_floats.restype = Z
+    lib.hla_default_seg_chunks.argtypes = [I, I, I, I, I]
+    lib.hla_default_seg_chunks.restype = I
+    lib.hla_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.hla_workspace_bytes.restype = Z
+    lib.hla_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P, Z, P]
+    lib.hla_forward.restype = I
+    lib.hla_step.argtypes = [P, P, P, P, I, I, I, I, I, I, FP, P, P]
+    lib.hla_step.restype = I
+    lib.hla_status_str.argtypes = [I]
+    lib.hla_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load().hla_status_str(int(code)).decode()
+
+
+def _variant(v) -> int:
+    if isinstance(v, str):
+        if v not in VARIANTS:
+            raise ValueError(f"unknown variant {v!r}; one of {sorted(VARIANTS)}")
+        return VARIANTS[v]
+    return int(v)
+
+
+def state_floats(variant, d: int, dv: int) -> int:
+    return int(load().hla_state_floats(_variant(variant), d, dv))
+
+
+def default_seg_chunks(variant, B, H, n, chunk) -> int:
+    return int(load().hla_default_seg_chunks(_variant(variant), B, H, n, chunk))
+
+
+def workspace_bytes(variant, B, H, n, d, dv, chunk, seg_chunks=0) -> int:
+    return int(load().hla_workspace_bytes(_variant(variant), B, H, n, d, dv, chunk, seg_chunks))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _DTYPES["bf16"]
+    if t.dtype == torch.float32:
+        return _DTYPES["f32"]
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _gamma_arg(gamma, H):
+    if gamma is None:
+        return None, None
+    import numpy as np
+    try:
+        import torch
+        if isinstance(gamma, torch.Tensor):
+            gamma = gamma.detach().float().cpu().numpy()
+    except ImportError:
+        pass
+    g = np.ascontiguousarray(np.asarray(gamma, dtype=np.float32).reshape(-1))
+    if g.size != H:
+        raise ValueError(f"gamma has {g.size} values, expected H = {H}")
+    return g, g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def _check_device_tensor(name, t):
+    if not t.is_cuda:
+        raise HLAError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise HLAError(f"{name} must be contiguous")
+
+
+def _stream_ptr(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
+                state_in=None, state_out=None, out=None, workspace=None, stream=None):
+    """Chunked HLA-2 / AHLA forward.  q, k: [B, H, n, d]; v: [B, H, n, dv];
+    bf16 or fp32, contiguous, on one GPU.  gamma: None or H decays in (0, 1].
+    state_in / state_out: None or fp32 [B, H, state_floats] device tensors.
+    Returns o [B, H, n, dv] (``out`` if given)."""
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise HLAError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}: "
+                       "expected [B,H,n,d], [B,H,n,d], [B,H,n,dv]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise HLAError("q, k, v must share one dtype")
+    B, H, n, d = q.shape
+    dv = v.shape[3]
+    vid = _variant(variant)
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=q.device)
+    else:
+        _check_device_tensor("out", out)
+        if out.shape != (B, H, n, dv) or out.dtype != q.dtype:
+            raise HLAError("out has the wrong shape or dtype")
+    stf = state_floats(vid, d, dv)
+    for name, t in (("state_in", state_in), ("state_out", state_out)):
+        if t is not None:
+            _check_device_tensor(name, t)
+            if t.dtype != torch.float32 or t.numel() != B * H * stf:
+                raise HLAError(f"{name} must be fp32 with B*H*{stf} elements")
+    need = workspace_bytes(vid, B, H, n, d, dv, chunk, seg_chunks)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    g_keep, g_ptr = _gamma_arg(gamma, H)
+    with torch.cuda.device(q.device):
+        rc = lib.hla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             B, H, n, d, dv, _dtype_code(q), vid, g_ptr, chunk, seg_chunks,
+                             state_in.data_ptr() if state_in is not None else None,
+                             state_out.data_ptr() if state_out is not None else None,
+                             ws_ptr, ws_len, _stream_ptr(stream, q.device))
+    del g_keep
+    if rc != 0:
+        raise HLAError(f"hla_forward failed: {status_str(rc)} (code {rc})")
+    return out
+
+
+def hla_step(q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):
+    """One decode step.  q, k: [B, H, d]; v: [B, H, dv]; state: fp32 device
+    tensor with B*H*state_floats elements, updated in place.  Returns o."""
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
+        _check_device_tensor(name, t)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise HLAError("expected q, k: [B, H, d], v: [B, H, dv]")
+    B, H, d = q.shape
+    dv = v.shape[2]
+    vid = _variant(variant)
+    if state.dtype != torch.float32 or state.numel() != B * H * state_floats(vid, d, dv):
+        raise HLAError("state must be fp32 with B*H*state_floats elements")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    g_keep, g_ptr = _gamma_arg(gamma, H)
+    with torch.cuda.device(q.device):
+        rc = lib.hla_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, d, dv,
+                          _dtype_code(q), vid, g_ptr, state.data_ptr(),
+                          _stream_ptr(stream, q.device))
+    del g_keep
+    if rc != 0:
+        raise HLAError(f"hla_step failed: {status_str(rc)} (code {rc})")
+    return out

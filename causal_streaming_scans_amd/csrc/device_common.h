@@ -1,0 +1,146 @@
+// device_common.h -- building blocks shared by the HLA kernels (gfx950 only).
+//
+// Every dense product in the forward path is written in one "NT" form,
+//     C[i][j] += sum_k A[i][k] * Bt[j][k],
+// with both operands in LDS, row-major, read contiguously along k.  A 16x16
+// output tile lives in one wave as an MFMA accumulator: lane l holds rows
+// 4*(l/16) + r (r = 0..3) of column l%16.
+//
+// bf16 tiles use V_MFMA_F32_16X16X32_BF16 (8 k-values per lane) and, for a
+// trailing 16-wide k block, V_MFMA_F32_16X16X16_BF16; fp32 tiles use
+// V_MFMA_F32_16X16X4_F32.  Both operands of one instruction take the same
+// (lane group, slot) -> k assignment, so the sum over k is the plain dot
+// product whatever order the hardware visits the k values in.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
+
+// padding (in elements) that keeps every LDS row 16-byte aligned and shifts
+// consecutive rows across banks
+template <typename T> constexpr int pad_of() { return 16 / (int)sizeof(T); }
+template <typename T> constexpr int ld_of(int cols) { return cols + pad_of<T>(); }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ---------------------------------------------------------------- MFMA tiles
+
+// acc += A[0:16][kbeg:kend] * Bt[0:16][kbeg:kend]^T, k range a multiple of 16.
+__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const bf16 *A, int lda, const bf16 *Bt,
+                                        int ldb, int kbeg, int kend) {
+    const int l = lane_id();
+    const int r = l & 15, g = l >> 4;
+    const bf16 *a = A + r * lda;
+    const bf16 *b = Bt + r * ldb;
+    int k = kbeg;
+    for (; k + 32 <= kend; k += 32) {
+        bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + k + g * 8);
+        bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + k + g * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    }
+    if (k < kend) {
+        i16x4 av = *reinterpret_cast<const i16x4 *>(a + k + g * 4);
+        i16x4 bv = *reinterpret_cast<const i16x4 *>(b + k + g * 4);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// fp32 operands: exact fp32 products, fp32 accumulation.  k range multiple of 4.
+__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const float *A, int lda, const float *Bt,
+                                        int ldb, int kbeg, int kend) {
+    const int l = lane_id();
+    const int r = l & 15, g = l >> 4;
+    const float *a = A + r * lda + g;
+    const float *b = Bt + r * ldb + g;
+    for (int k = kbeg; k < kend; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k], acc, 0, 0, 0);
+    return acc;
+}
+
+// Row / column of accumulator element r held by this lane within its tile.
+__device__ __forceinline__ int acc_row(int r) { return ((lane_id() >> 4) << 2) + r; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+// ------------------------------------------------------------- global loads
+
+// 16-byte vector of T from global memory
+template <typename T> struct Vec16 {
+    static constexpr int N = 16 / (int)sizeof(T);
+    T v[N];
+};
+
+template <typename T>
+__device__ __forceinline__ Vec16<T> load16(const T *p) {
+    Vec16<T> r;
+    *reinterpret_cast<uint4 *>(r.v) = *reinterpret_cast<const uint4 *>(p);
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void store16(T *p, const Vec16<T> &x) {
+    *reinterpret_cast<uint4 *>(p) = *reinterpret_cast<const uint4 *>(x.v);
+}
+
+// Stage `rows_valid` rows (of `ROWS`) of a [ROWS][COLS] global tile into LDS,
+// row-major (dst, leading dim ldr) and/or transposed (dstT, leading dim ldt,
+// dstT[c][r] = src[r][c]).  Rows >= rows_valid are written as zeros.  The
+// optional transposed copy dstTw gets the value times w[r] (decay weights).
+template <typename T, int ROWS, int COLS, int NT>
+__device__ __forceinline__ void stage_tile(const T *__restrict__ src, int rows_valid, T *dst,
+                                           int ldr, T *dstT, int ldt, T *dstTw = nullptr,
+                                           const float *w = nullptr) {
+    constexpr int VE = Vec16<T>::N;
+    constexpr int VPR = COLS / VE;      // vectors per row
+    constexpr int NV = ROWS * VPR;
+    for (int idx = threadIdx.x; idx < NV; idx += NT) {
+        const int r = idx / VPR, c = (idx % VPR) * VE;
+        Vec16<T> x;
+        if (r < rows_valid) {
+            x = load16(src + (size_t)r * COLS + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(0.f);
+        }
+        if (dst) store16(dst + r * ldr + c, x);
+        if (dstT) {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) dstT[(c + e) * ldt + r] = x.v[e];
+        }
+        if (dstTw) {
+            const float wr = (r < rows_valid) ? w[r] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) dstTw[(c + e) * ldt + r] = from_f<T>(to_f(x.v[e]) * wr);
+        }
+    }
+}
+
+// Powers g^e for e = 0..count-1 into LDS, from fp64 exp2(e * log2 g) rounded
+// once to fp32 (no accumulated rounding from repeated multiplication).
+template <int NT>
+__device__ __forceinline__ void fill_pow_table(float *tab, int count, float g) {
+    const double lg = log2((double)g);
+    for (int e = threadIdx.x; e < count; e += NT) tab[e] = (float)exp2(lg * (double)e);
+}
+
+__device__ __forceinline__ float pow_int(float g, long e) {
+    if (e == 0 || g == 1.0f) return 1.0f;
+    return (float)exp2(log2((double)g) * (double)e);
+}
+
+}  // namespace hla

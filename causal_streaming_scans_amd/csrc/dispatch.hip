@@ -1,0 +1,63 @@
+// dispatch.hip -- decode-step instances, the small copy kernel, and the
+// run-time lookup from argument values to kernel instances.
+#include "launch.h"
+#include "step_kernel.h"
+
+namespace hla {
+
+__global__ void copy_or_zero_kernel(const float *src, float *dst, size_t count) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s) {
+    if (count == 0) return hipSuccess;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, count);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool AHLA>
+hipError_t launch_step(const StepParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((step_kernel<T, D, D, AHLA, 256>), dim3(p.BH), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+static bool step_for(bool ahla, int d, StepLaunch *out) {
+    switch (d) {
+        case 16: *out = ahla ? launch_step<T, 16, true> : launch_step<T, 16, false>; return true;
+        case 32: *out = ahla ? launch_step<T, 32, true> : launch_step<T, 32, false>; return true;
+        case 64: *out = ahla ? launch_step<T, 64, true> : launch_step<T, 64, false>; return true;
+        case 128: *out = ahla ? launch_step<T, 128, true> : launch_step<T, 128, false>; return true;
+        default: return false;
+    }
+}
+
+bool lookup_step(int dtype, bool ahla, int d, int dv, StepLaunch *out) {
+    if (d != dv) return false;
+    return dtype == 0 ? step_for<float>(ahla, d, out) : step_for<bf16>(ahla, d, out);
+}
+
+bool lookup_forward(int dtype, bool ahla, int d, int dv, int chunk, bool decay, FwdKernels *out) {
+    if (d != dv) return false;
+    if (dtype == 0) {
+        switch (d) {
+            case 16: return lookup_forward_f32_16(ahla, chunk, decay, out);
+            case 32: return lookup_forward_f32_32(ahla, chunk, decay, out);
+            case 64: return lookup_forward_f32_64(ahla, chunk, decay, out);
+            default: return false;
+        }
+    }
+    switch (d) {
+        case 16: return lookup_forward_bf16_16(ahla, chunk, decay, out);
+        case 32: return lookup_forward_bf16_32(ahla, chunk, decay, out);
+        case 64: return lookup_forward_bf16_64(ahla, chunk, decay, out);
+        case 128: return lookup_forward_bf16_128(ahla, chunk, decay, out);
+        default: return false;
+    }
+}
+
+}  // namespace hla

@@ -1,0 +1,203 @@
+// hla_api.cpp -- the C ABI declared in include/hla.h.
+//
+// Validation runs first and touches no HIP API, so every error code below is
+// reachable on a host without a GPU.  Then the forward pass enqueues, on the
+// caller's stream:
+//   1. the segment-summary kernel over segments 0 .. nseg-2 (the last
+//      segment's summary would only feed the total, which an exclusive scan
+//      never uses),
+//   2. the exclusive Blelloch scan of those summaries per (b,h), which also
+//      folds in the caller's initial state,
+//   3. the chunked forward kernel over every segment from its carried state.
+// With a single segment only step 3 runs, starting from state_in or zero.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/hla.h"
+#include "launch.h"
+
+using namespace hla;
+
+namespace {
+
+bool valid_variant(int v) { return v >= HLA_HLA2 && v <= HLA_AHLA_RATIO; }
+bool is_ahla(int v) { return v == HLA_AHLA || v == HLA_AHLA_RATIO; }
+bool is_ratio(int v) { return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO; }
+
+long ceil_div(long a, long b) { return (a + b - 1) / b; }
+
+long next_pow2(long x) {
+    long p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int effective_seg_chunks(int variant, int B, int H, int n, int chunk, int seg_chunks) {
+    return seg_chunks > 0 ? seg_chunks : hla_default_seg_chunks(variant, B, H, n, chunk);
+}
+
+long num_segments(int n, int chunk, int seg_chunks) {
+    if (n <= 0) return 0;
+    return ceil_div(n, (long)chunk * seg_chunks);
+}
+
+// Shared argument checks of forward and step.  Returns HLA_OK or the error.
+hla_status check_common(int B, int H, int d, int dv, int dtype, int variant, const float *gamma) {
+    if (dtype != HLA_F32 && dtype != HLA_BF16) return HLA_ERR_ARG;
+    if (!valid_variant(variant)) return HLA_ERR_ARG;
+    if (B < 1 || H < 1 || d < 1 || dv < 1) return HLA_ERR_SHAPE;
+    if ((long)B * H > 65535) return HLA_ERR_UNSUPPORTED;
+    if (gamma) {
+        if (is_ahla(variant)) return HLA_ERR_UNSUPPORTED;
+        if (H > HLA_MAX_DECAY_HEADS) return HLA_ERR_UNSUPPORTED;
+        for (int h = 0; h < H; ++h)
+            if (!(gamma[h] > 0.f && gamma[h] <= 1.f)) return HLA_ERR_ARG;  // also rejects NaN
+    }
+    return HLA_OK;
+}
+
+void fill_gamma(float *dst, const float *gamma, int H) {
+    for (int h = 0; h < kMaxDecayHeads; ++h) dst[h] = (gamma && h < H) ? gamma[h] : 1.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hla_state_floats(int variant, int d, int dv) {
+    if (!valid_variant(variant) || d < 1 || dv < 1) return 0;
+    return is_ahla(variant) ? (size_t)ahla_state_floats(d, dv) : (size_t)hla2_state_floats(d, dv);
+}
+
+int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk) {
+    (void)variant;
+    if (B < 1 || H < 1 || n < 1 || chunk < 1) return 1;
+    const long nch = ceil_div(n, chunk);
+    const long bh = (long)B * H;
+    // Enough segments to give the 256 compute units about two workgroups
+    // each, but no segment shorter than 8 chunks: short segments add summary
+    // work and scan depth without adding useful parallelism.
+    const long target_wg = 512;
+    long nseg = ceil_div(target_wg, bh);
+    if (nseg <= 1) return (int)nch;
+    long g = ceil_div(nch, nseg);
+    if (g < 8) g = 8;
+    if (g > nch) g = nch;
+    return (int)g;
+}
+
+size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int chunk,
+                           int seg_chunks) {
+    if (!valid_variant(variant) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || chunk < 1 ||
+        seg_chunks < 0)
+        return 0;
+    const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
+    const long nseg = num_segments(n, chunk, g);
+    if (nseg <= 1) return 0;
+    const long spad = next_pow2(nseg);
+    return (size_t)B * H * 2 * spad * (size_t)summary_floats(d, dv) * sizeof(float);
+}
+
+hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int B, int H, int n,
+                       int d, int dv, int dtype, int variant, const float *gamma_host, int chunk,
+                       int seg_chunks, const float *state_in, float *state_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
+    if (st != HLA_OK) return st;
+    if (n < 0) return HLA_ERR_SHAPE;
+    if (chunk < 0 || seg_chunks < 0) return HLA_ERR_ARG;
+    if (n > 0 && (!q || !k || !v || !o)) return HLA_ERR_NULL;
+    if (state_in && state_out && state_in == state_out) return HLA_ERR_ARG;
+
+    const bool ahla = is_ahla(variant);
+    const bool decay = gamma_host != nullptr;
+    FwdKernels kern;
+    if (!lookup_forward(dtype, ahla, d, dv, chunk, decay, &kern)) return HLA_ERR_UNSUPPORTED;
+
+    const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
+    if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    const long nseg = num_segments(n, chunk, g);
+    if (nseg > INT32_MAX / 4) return HLA_ERR_UNSUPPORTED;
+    const size_t need = hla_workspace_bytes(variant, B, H, n, d, dv, chunk, g);
+    if (need > 0) {
+        if (!workspace) return HLA_ERR_NULL;
+        if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = B * H;
+    if (n == 0) {
+        // no tokens: the state passes through unchanged
+        if (state_out) {
+            const size_t cnt = (size_t)BH * hla_state_floats(variant, d, dv);
+            if (launch_copy_or_zero(state_in, state_out, cnt, s) != hipSuccess) return HLA_ERR_DEVICE;
+        }
+        return HLA_OK;
+    }
+
+    FwdParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.BH = BH;
+    p.H = H;
+    p.n = n;
+    p.seg_len = chunk * g;
+    p.nseg = (int)nseg;
+    p.spad = (int)next_pow2(nseg);
+    p.ratio = is_ratio(variant) ? 1 : 0;
+    p.ws = static_cast<float *>(workspace);
+    p.state_in = state_in;
+    p.state_out = state_out;
+    fill_gamma(p.gamma, gamma_host, H);
+
+    if (nseg > 1) {
+        if (kern.summary(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+        if (kern.scan(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+    }
+    if (kern.forward(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+    return HLA_OK;
+}
+
+hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B, int H, int d,
+                    int dv, int dtype, int variant, const float *gamma_host, float *state,
+                    void *stream) {
+    hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
+    if (st != HLA_OK) return st;
+    if (!q || !k || !v || !o || !state) return HLA_ERR_NULL;
+    StepLaunch fn;
+    if (!lookup_step(dtype, is_ahla(variant), d, dv, &fn)) return HLA_ERR_UNSUPPORTED;
+    StepParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.state = state;
+    p.BH = B * H;
+    p.H = H;
+    p.ratio = is_ratio(variant) ? 1 : 0;
+    fill_gamma(p.gamma, gamma_host, H);
+    if (fn(p, static_cast<hipStream_t>(stream)) != hipSuccess) return HLA_ERR_DEVICE;
+    return HLA_OK;
+}
+
+const char *hla_status_str(int status) {
+    switch (status) {
+        case HLA_OK: return "ok";
+        case HLA_ERR_NULL: return "a required pointer is NULL";
+        case HLA_ERR_SHAPE: return "bad shape (B, H, d, dv must be >= 1 and n >= 0)";
+        case HLA_ERR_UNSUPPORTED: return "no kernel for this dtype / d / dv / chunk / variant";
+        case HLA_ERR_WORKSPACE: return "workspace smaller than hla_workspace_bytes()";
+        case HLA_ERR_DEVICE: return "a HIP launch or runtime call failed";
+        case HLA_ERR_ARG: return "bad argument value (enum, gamma outside (0, 1], negative chunk)";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

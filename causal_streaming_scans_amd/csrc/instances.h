@@ -1,0 +1,113 @@
+// instances.h -- kernel instantiation for one (element type, head dim); each
+// inst_*.hip includes this once so the instances compile in parallel.
+#pragma once
+
+#include "ahla_kernels.h"
+#include "hla2_kernels.h"
+#include "launch.h"
+#include "scan_kernel.h"
+
+namespace hla {
+
+constexpr size_t kLdsBytes = 160 * 1024;   // gfx950 LDS per workgroup
+
+template <typename T> constexpr int default_waves(int D) { return 4; }
+
+template <typename T, int D, int C, bool DECAY>
+constexpr bool hla2_fits() {
+    constexpr int NW = default_waves<T>(D);
+    return sizeof(Hla2FwdSmem<T, D, D, C, DECAY, NW>) <= kLdsBytes &&
+           sizeof(Hla2SumSmem<T, D, D, C, DECAY, NW>) <= kLdsBytes;
+}
+
+template <typename T, int D, int C>
+constexpr bool ahla_fits() {
+    constexpr int NW = default_waves<T>(D);
+    return sizeof(AhlaFwdSmem<T, D, D, C, NW>) <= kLdsBytes &&
+           sizeof(AhlaSumSmem<T, D, D, C, NW>) <= kLdsBytes;
+}
+
+template <typename T, int D, int C, bool DECAY>
+hipError_t launch_hla2_summary(const FwdParams &p, hipStream_t s) {
+    constexpr int NW = default_waves<T>(D);
+    hipLaunchKernelGGL((hla2_summary_kernel<T, D, D, C, DECAY, NW>), dim3(p.nseg - 1, p.BH),
+                       dim3(NW * kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C, bool DECAY>
+hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
+    constexpr int NW = default_waves<T>(D);
+    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY, NW>), dim3(p.nseg, p.BH),
+                       dim3(NW * kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C>
+hipError_t launch_ahla_summary(const FwdParams &p, hipStream_t s) {
+    constexpr int NW = default_waves<T>(D);
+    hipLaunchKernelGGL((ahla_summary_kernel<T, D, D, C, NW>), dim3(p.nseg - 1, p.BH),
+                       dim3(NW * kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C>
+hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
+    constexpr int NW = default_waves<T>(D);
+    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C, NW>), dim3(p.nseg, p.BH),
+                       dim3(NW * kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, bool HLA2>
+hipError_t launch_scan(const FwdParams &p, hipStream_t s) {
+    constexpr bool F32 = sizeof(T) == 4;
+    hipLaunchKernelGGL((scan_kernel<F32, D, D, HLA2, 8>), dim3(p.BH), dim3(8 * kWave), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C>
+bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
+    if (ahla) {
+        if (decay) return false;
+        if constexpr (ahla_fits<T, D, C>()) {
+            *out = {launch_ahla_summary<T, D, C>, launch_scan<T, D, false>,
+                    launch_ahla_forward<T, D, C>};
+            return true;
+        }
+        return false;
+    }
+    if (decay) {
+        if constexpr (hla2_fits<T, D, C, true>()) {
+            *out = {launch_hla2_summary<T, D, C, true>, launch_scan<T, D, true>,
+                    launch_hla2_forward<T, D, C, true>};
+            return true;
+        }
+        return false;
+    }
+    if constexpr (hla2_fits<T, D, C, false>()) {
+        *out = {launch_hla2_summary<T, D, C, false>, launch_scan<T, D, true>,
+                launch_hla2_forward<T, D, C, false>};
+        return true;
+    }
+    return false;
+}
+
+template <typename T, int D>
+bool lookup_dim(bool ahla, int chunk, bool decay, FwdKernels *out) {
+    switch (chunk) {
+        case 16: return lookup_chunk<T, D, 16>(ahla, decay, out);
+        case 32: return lookup_chunk<T, D, 32>(ahla, decay, out);
+        case 64: return lookup_chunk<T, D, 64>(ahla, decay, out);
+        default: return false;
+    }
+}
+
+}  // namespace hla
+
+#define HLA_DEFINE_LOOKUP(NAME, T, D)                                                   \
+    namespace hla {                                                                     \
+    bool NAME(bool ahla, int chunk, bool decay, FwdKernels *out) {                      \
+        return lookup_dim<T, D>(ahla, chunk, decay, out);                               \
+    }                                                                                   \
+    }

@@ -1,0 +1,36 @@
+// launch.h -- internal dispatch between the C ABI and the kernel templates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "params.h"
+
+namespace hla {
+
+typedef hipError_t (*FwdLaunch)(const FwdParams &, hipStream_t);
+typedef hipError_t (*StepLaunch)(const StepParams &, hipStream_t);
+
+struct FwdKernels {
+    FwdLaunch summary;   // grid (nseg-1, BH): segment summaries from zero state
+    FwdLaunch scan;      // grid (BH): exclusive Blelloch scan (+ initial state)
+    FwdLaunch forward;   // grid (nseg, BH): chunked forward from the carried state
+};
+
+// dtype: 0 = fp32, 1 = bf16.  ahla: AHLA family (else HLA-2).  Returns false
+// when no instance exists for these compile-time parameters.
+bool lookup_forward(int dtype, bool ahla, int d, int dv, int chunk, bool decay, FwdKernels *out);
+bool lookup_step(int dtype, bool ahla, int d, int dv, StepLaunch *out);
+
+// per-(dtype, d) tables, one translation unit each
+bool lookup_forward_f32_16(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_f32_32(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_f32_64(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_bf16_16(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_bf16_32(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_bf16_64(bool ahla, int chunk, bool decay, FwdKernels *out);
+bool lookup_forward_bf16_128(bool ahla, int chunk, bool decay, FwdKernels *out);
+
+// fill dst[0:count) with src[0:count), or with zeros when src is null
+hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s);
+
+}  // namespace hla

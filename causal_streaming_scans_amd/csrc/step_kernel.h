@@ -1,0 +1,146 @@
+// step_kernel.h -- one streaming (decode) step of HLA-2 / AHLA per (b,h).
+//
+// Page: "Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)",
+// gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden" and
+// "Resultados y Afirmaciones": a constant-size state per head and an
+// O(d^2 + d dv) update per token, independent of the sequence length;
+// section "2. ... (AHLA)" for the asymmetric summaries.
+//
+// HLA-2: S <- g S + k k^T ; z = S q ; W <- g^2 W + z v^T ; u <- g^2 u + z ;
+//        o = q^T W  (ratio: / q^T u)
+// AHLA : P <- P + k v^T ; y = P^T q ; E <- E + k y^T ; mK <- mK + k ;
+//        nk <- nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
+//
+// One workgroup of NT threads per (b,h).  The state is read once and written
+// once (fp32, row-major); rows are streamed with consecutive threads on
+// consecutive columns so every access is coalesced.
+#pragma once
+
+#include "device_common.h"
+#include "params.h"
+
+namespace hla {
+
+template <typename T, int D, int DV, bool AHLA, int NT>
+__global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
+    constexpr int RG = NT / DV;   // row groups for the column-parallel passes
+    static_assert(NT % DV == 0 && NT % D == 0, "block shape");
+    __shared__ float sq[D], sk[D], sv[DV], sz[D], sy[DV];
+    __shared__ float part[RG][DV];
+    __shared__ float red[NT / kWave];
+    __shared__ float scal[2];
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float g = AHLA ? 1.f : p.gamma[bh % p.H];
+    const float g2 = g * g;
+    const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
+    const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
+    const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
+    T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
+    constexpr int STF = AHLA ? ahla_state_floats(D, DV) : hla2_state_floats(D, DV);
+    float *st = p.state + (size_t)bh * STF;
+
+    for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
+    for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
+    __syncthreads();
+
+    const int col = tid % DV, rg = tid / DV;
+    auto block_sum = [&](float x) -> float {
+        // sum over the whole block
+        for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = x;
+        __syncthreads();
+        float s = 0.f;
+        for (int i = 0; i < NT / kWave; ++i) s += red[i];
+        __syncthreads();
+        return s;
+    };
+
+    if (!AHLA) {
+        float *S = st, *W = st + D * D, *u = st + D * D + D * DV;
+        // S <- g S + k k^T ; z = S q   (rows split over D threads-groups)
+        constexpr int TPR = NT / D;            // threads per row
+        const int row = tid / TPR, sub = tid % TPR;
+        float zp = 0.f;
+        for (int c = sub; c < D; c += TPR) {
+            const float s = g * S[row * D + c] + sk[row] * sk[c];
+            S[row * D + c] = s;
+            zp += s * sq[c];
+        }
+        for (int m = TPR / 2; m >= 1; m >>= 1) zp += __shfl_xor(zp, m, TPR);
+        if (sub == 0) sz[row] = zp;
+        __syncthreads();
+        // W <- g^2 W + z v^T ; partial o = q^T W
+        float op = 0.f;
+        for (int r = rg; r < D; r += RG) {
+            const float wv = g2 * W[r * DV + col] + sz[r] * sv[col];
+            W[r * DV + col] = wv;
+            op += sq[r] * wv;
+        }
+        part[rg][col] = op;
+        // u <- g^2 u + z ; den = q^T u
+        float dp = 0.f;
+        for (int r = tid; r < D; r += NT) {
+            const float uv = g2 * u[r] + sz[r];
+            u[r] = uv;
+            dp += sq[r] * uv;
+        }
+        const float den = block_sum(dp);   // contains the barrier that publishes part[]
+        if (tid < DV) {
+            float s = 0.f;
+            for (int i = 0; i < RG; ++i) s += part[i][tid];
+            if (p.ratio) s = s / den;
+            o[tid] = from_f<T>(s);
+        }
+    } else {
+        float *P = st, *E = st + D * DV, *mK = st + 2 * D * DV, *nk = mK + D;
+        // P <- P + k v^T ; partial y = P^T q
+        float yp = 0.f;
+        for (int r = rg; r < D; r += RG) {
+            const float pv = P[r * DV + col] + sk[r] * sv[col];
+            P[r * DV + col] = pv;
+            yp += sq[r] * pv;
+        }
+        part[rg][col] = yp;
+        // mK <- mK + k ; s = q . mK
+        float sp = 0.f;
+        for (int r = tid; r < D; r += NT) {
+            const float mv = mK[r] + sk[r];
+            mK[r] = mv;
+            sp += sq[r] * mv;
+        }
+        const float s_all = block_sum(sp);
+        if (tid < DV) {
+            float s = 0.f;
+            for (int i = 0; i < RG; ++i) s += part[i][tid];
+            sy[tid] = s;
+        }
+        __syncthreads();
+        // E <- E + k y^T ; partial o = q^T E
+        float op = 0.f;
+        for (int r = rg; r < D; r += RG) {
+            const float ev = E[r * DV + col] + sk[r] * sy[col];
+            E[r * DV + col] = ev;
+            op += sq[r] * ev;
+        }
+        __syncthreads();
+        part[rg][col] = op;
+        // nk <- nk + k s ; den = q . nk
+        float dp = 0.f;
+        for (int r = tid; r < D; r += NT) {
+            const float nv = nk[r] + sk[r] * s_all;
+            nk[r] = nv;
+            dp += sq[r] * nv;
+        }
+        const float den = block_sum(dp);
+        if (tid < DV) {
+            float s = 0.f;
+            for (int i = 0; i < RG; ++i) s += part[i][tid];
+            if (p.ratio) s = s / den;
+            o[tid] = from_f<T>(s);
+        }
+    }
+}
+
+}  // namespace hla

@@ -1,0 +1,154 @@
+/*
+ * hla.h -- C ABI of the MI355X (gfx950) forward path of second-order
+ * Higher-order Linear Attention (HLA-2) and of the asymmetric AHLA operator.
+ *
+ * Defining passages ("Resumen Tecnico: Atencion Lineal de Orden Superior
+ * (HLA)", gist.science/es/paper/2510.27258):
+ *   section "1. HLA de Segundo Orden"  -- prefix moments, cross-summaries, the
+ *       output q^T (S^K C^QV - G) and the ratio-normalised form;
+ *   section "2. ... (AHLA)"           -- the asymmetric operator Q (K^T Q)(K^T V);
+ *   section "4. Entrenamiento Paralelo mediante Escaneos Asociativos" --
+ *       chunk-parallel evaluation by an exclusive Blelloch scan of segment
+ *       summaries under a semidirect-product combine;
+ *   section "Contribuciones Clave", item 2 -- masked operators with
+ *       exponential decay;
+ *   section "Resultados y Afirmaciones" -- O(d^2 + d dv) per-token streaming
+ *       cost, strict causality (output t depends on tokens j <= t only).
+ *
+ * Operators computed (A = Q K^T, L = tril(A) with the diagonal):
+ *   HLA_HLA2        o = tril(L L^T) V, i.e.
+ *                   o_t = sum_{j<=t} sum_{i<=j} g^((t-i)+(t-j)) A[t,i] A[j,i] v_j
+ *   HLA_HLA2_RATIO  the HLA_HLA2 numerator divided, row by row, by the same
+ *                   double sum with v == 1 (no epsilon; a zero denominator
+ *                   gives IEEE inf/NaN in that row)
+ *   HLA_AHLA        o = (L L) V,  o_t = sum_{i<=t} sum_{j<=i} A[t,i] A[i,j] v_j
+ *   HLA_AHLA_RATIO  the AHLA numerator over the same sum with v == 1
+ * g is the per-head decay (1 when gamma is NULL).  No 1/sqrt(d) or other
+ * scaling is applied inside.
+ *
+ * Layout (all row-major, contiguous, device memory):
+ *   q, k : [B][H][n][d]     v, o : [B][H][n][dv]    element type = dtype
+ *   state: fp32, one block per (b,h) of hla_state_floats() floats:
+ *     HLA-2 : [ S (d*d) | W (d*dv) | u (d) ]    S = sum g^(t-i) k_i k_i^T,
+ *             W = S^K C^QV - G, u = S^K m^Q - h  (the page's five summaries
+ *             folded into the three that a continuation needs)
+ *     AHLA  : [ P (d*dv) | E (d*dv) | mK (d) | nk (d) ]  the page's P^KV, E, m^K, n
+ *
+ * Ownership: the caller allocates and owns every buffer, including the
+ * workspace.  The library allocates no memory, keeps no mutable global state,
+ * never prints and never aborts.  All work is enqueued on `stream` (a
+ * hipStream_t passed as void*, NULL = the null stream); the call returns
+ * after enqueueing.  Concurrent calls on different streams are safe if they
+ * use different workspaces and outputs.
+ *
+ * Errors: arguments are validated first, on the host, with no HIP call; on a
+ * validation error nothing is enqueued.  A failed launch returns
+ * HLA_ERR_DEVICE.  Faults inside kernels surface at the caller's next
+ * synchronisation, as usual for HIP.
+ */
+#ifndef HLA_H
+#define HLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HLA_OK = 0,
+    HLA_ERR_NULL = 1,         /* a required pointer is NULL                     */
+    HLA_ERR_SHAPE = 2,        /* B, H, d or dv < 1, or n < 0                     */
+    HLA_ERR_UNSUPPORTED = 3,  /* no kernel for this (dtype, d, dv, chunk, variant) */
+    HLA_ERR_WORKSPACE = 4,    /* workspace smaller than hla_workspace_bytes()    */
+    HLA_ERR_DEVICE = 5,       /* a HIP launch or runtime call failed             */
+    HLA_ERR_ARG = 6           /* bad enum value, gamma outside (0, 1], chunk or
+                                 seg_chunks < 0                                  */
+} hla_status;
+
+typedef enum { HLA_F32 = 0, HLA_BF16 = 1 } hla_dtype;
+
+typedef enum {
+    HLA_HLA2 = 0,
+    HLA_HLA2_RATIO = 1,
+    HLA_AHLA = 2,
+    HLA_AHLA_RATIO = 3
+} hla_variant;
+
+/* Largest H for which a per-head decay can be given (it travels in the kernel
+ * arguments). */
+#define HLA_MAX_DECAY_HEADS 256
+
+/* Floats of streaming state per (b,h) for `variant` (see Layout above);
+ * 0 for an unknown variant. */
+size_t hla_state_floats(int variant, int d, int dv);
+
+/* Segment length, in chunks, that hla_forward uses when seg_chunks == 0. */
+int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk);
+
+/* Bytes of device workspace hla_forward needs for these arguments
+ * (seg_chunks == 0 means the default).  0 when the sequence is one segment. */
+size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
+                           int chunk, int seg_chunks);
+
+/*
+ * Chunked forward pass over a whole sequence.
+ *
+ * q, k, v, o     device pointers, layout above (may be NULL only if n == 0)
+ * B, H, n, d, dv sizes; n may be any value >= 0 (a partial last chunk and a
+ *                partial last segment are masked)
+ * dtype          HLA_F32 (fp32 inputs, fp32 arithmetic and MFMA) or HLA_BF16
+ *                (bf16 inputs and output, bf16 MFMA operands, fp32
+ *                accumulation and fp32 state)
+ * variant        hla_variant
+ * gamma_host     NULL (no decay) or host array of H floats in (0, 1]: decay of
+ *                head h, shared by every batch index; HLA-2 variants only,
+ *                H <= HLA_MAX_DECAY_HEADS
+ * chunk          tokens per intra-chunk tile: 16, 32 or 64 (64 needs d <= 64)
+ * seg_chunks     chunks per segment of the scan; 0 = hla_default_seg_chunks().
+ *                The sequence is split into ceil(n / (chunk*seg_chunks))
+ *                segments: their summaries are built in parallel, combined by
+ *                an exclusive Blelloch scan, and each segment's outputs are
+ *                then computed from its carried state.
+ * state_in       NULL (zero state) or device fp32 [B*H][hla_state_floats()]:
+ *                the state after some earlier tokens; the pass continues it
+ * state_out      NULL or device fp32 [B*H][hla_state_floats()]: receives the
+ *                state after token n-1 (may not alias state_in)
+ * workspace      device buffer of at least hla_workspace_bytes() bytes
+ *                (may be NULL when that is 0); its contents on entry are
+ *                ignored and on return are unspecified
+ * stream         hipStream_t as void*
+ *
+ * Supported: d == dv in {16, 32, 64, 128} for both dtypes (fp32 with
+ * d = 128 only for chunk 16).
+ */
+hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
+                       int B, int H, int n, int d, int dv, int dtype, int variant,
+                       const float *gamma_host, int chunk, int seg_chunks,
+                       const float *state_in, float *state_out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One streaming (decode) step: for every (b,h) take the single token
+ * q, k : [B][H][d], v : [B][H][dv], update `state` in place and write
+ * o : [B][H][dv].  The update is the same recurrence the forward pass
+ * carries between chunks (page section "1. HLA de Segundo Orden",
+ * "Resultados y Afirmaciones": constant state, O(d^2 + d dv) per token):
+ *   HLA-2: S <- g S + k k^T; z = S q; W <- g^2 W + z v^T; u <- g^2 u + z;
+ *          o = q^T W  (ratio: / q^T u)
+ *   AHLA : P <- P + k v^T; y = P^T q; E <- E + k y^T; mK <- mK + k;
+ *          nk <- nk + k (q . mK); o = q^T E  (ratio: / q^T nk)
+ * state is device fp32 [B*H][hla_state_floats()], never NULL.
+ */
+hla_status hla_step(const void *q, const void *k, const void *v, void *o,
+                    int B, int H, int d, int dv, int dtype, int variant,
+                    const float *gamma_host, float *state, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *hla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HLA_H */

@@ -1,0 +1,140 @@
+"""The C ABI on a host without a GPU: the library loads, exports every
+function include/hla.h declares, sizes are right, and argument validation
+returns its error codes before any HIP call (nothing here launches work)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import causal_streaming_scans_amd as hla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hla.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_DEV, ERR_ARG = range(7)
+F32, BF16 = 0, 1
+HLA2, HLA2_RATIO, AHLA, AHLA_RATIO = range(4)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hla.library_path()):
+        import causal_streaming_scans_amd.build as b
+        b.build()
+    return hla.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hla_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"hla_forward", "hla_step", "hla_state_floats", "hla_workspace_bytes",
+            "hla_default_seg_chunks", "hla_status_str"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = hla.status_str(code)
+        assert s and s != "unknown status"
+    assert hla.status_str(99) == "unknown status"
+
+
+def test_state_floats(lib):
+    assert hla.state_floats("hla2", 64, 64) == 64 * 64 + 64 * 64 + 64
+    assert hla.state_floats("hla2_ratio", 16, 32) == 16 * 16 + 16 * 32 + 16
+    assert hla.state_floats("ahla", 64, 64) == 2 * 64 * 64 + 2 * 64
+    assert lib.hla_state_floats(7, 64, 64) == 0
+
+
+def test_workspace_bytes(lib):
+    # one segment: no workspace
+    assert hla.workspace_bytes("hla2", 1, 1, 256, 16, 16, 32, 8) == 0
+    # 4 segments -> padded to 4, two arrays (summaries, prefixes)
+    sumf = 64 * 64 + 2 * 64 * 64 + 2 * 64
+    assert hla.workspace_bytes("hla2", 2, 3, 1024, 64, 64, 64, 4) == 2 * 3 * 2 * 4 * sumf * 4
+    # 3 segments pad to 4
+    assert hla.workspace_bytes("ahla", 1, 1, 600, 64, 64, 64, 4) == 1 * 2 * 4 * sumf * 4
+
+
+def test_default_segments_fill_the_chip(lib):
+    # 128 heads x 4096 tokens: 4 segments of 16 chunks
+    assert hla.default_seg_chunks("hla2_ratio", 8, 16, 4096, 64) == 16
+    # 32 heads x 65536 tokens: 16 segments of 64 chunks
+    assert hla.default_seg_chunks("ahla", 1, 32, 65536, 64) == 64
+    # short sequences are never split below 8 chunks
+    assert hla.default_seg_chunks("hla2", 1, 1, 256, 32) == 8
+
+
+def _fwd(lib, q=1, k=1, v=1, o=1, B=1, H=1, n=64, d=64, dv=64, dtype=BF16, variant=HLA2,
+         gamma=None, chunk=64, seg=0, si=None, so=None, ws=None, wsb=0):
+    gp = None
+    if gamma is not None:
+        g = np.asarray(gamma, np.float32)
+        gp = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    return lib.hla_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gp, chunk, seg, si, so,
+                           ws, wsb, None)
+
+
+def test_forward_validation_errors(lib):
+    fake = 0x1000  # never dereferenced: every call below fails validation
+    assert _fwd(lib, q=None, k=fake, v=fake, o=fake) == ERR_NULL
+    assert _fwd(lib, q=fake, k=fake, v=fake, o=None) == ERR_NULL
+    assert _fwd(lib, fake, fake, fake, fake, B=0) == ERR_SHAPE
+    assert _fwd(lib, fake, fake, fake, fake, n=-1) == ERR_SHAPE
+    assert _fwd(lib, fake, fake, fake, fake, d=0) == ERR_SHAPE
+    assert _fwd(lib, fake, fake, fake, fake, dtype=5) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, variant=9) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, chunk=-16) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, seg=-1) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, chunk=48) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, d=48, dv=48) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, d=64, dv=32) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, d=128, dv=128, chunk=64) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, dtype=F32, d=128, dv=128, chunk=16) == ERR_UNSUP
+    # decay: AHLA has none; gamma must lie in (0, 1]; H bounded
+    assert _fwd(lib, fake, fake, fake, fake, variant=AHLA, gamma=[0.9]) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, gamma=[0.0]) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, gamma=[1.5]) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, gamma=[float("nan")]) == ERR_ARG
+    assert _fwd(lib, fake, fake, fake, fake, H=300, gamma=[0.9] * 300) == ERR_UNSUP
+    # workspace: needed when the sequence has several segments
+    assert _fwd(lib, fake, fake, fake, fake, n=1024, seg=2, ws=None) == ERR_NULL
+    need = hla.workspace_bytes("hla2", 1, 1, 1024, 64, 64, 64, 2)
+    assert need > 0
+    assert _fwd(lib, fake, fake, fake, fake, n=1024, seg=2, ws=fake, wsb=need - 1) == ERR_WS
+    # state_in may not alias state_out
+    assert _fwd(lib, fake, fake, fake, fake, si=fake, so=fake) == ERR_ARG
+
+
+def test_step_validation_errors(lib):
+    fake = 0x1000
+
+    def step(q=fake, st=fake, B=1, H=1, d=64, dv=64, dtype=BF16, variant=HLA2, gamma=None):
+        gp = None
+        if gamma is not None:
+            g = np.asarray(gamma, np.float32)
+            gp = g.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+        return lib.hla_step(q, fake, fake, fake, B, H, d, dv, dtype, variant, gp, st, None)
+
+    assert step(q=None) == ERR_NULL
+    assert step(st=None) == ERR_NULL
+    assert step(B=0) == ERR_SHAPE
+    assert step(d=24, dv=24) == ERR_UNSUP
+    assert step(variant=AHLA_RATIO, gamma=[0.5]) == ERR_UNSUP
+    assert step(gamma=[-0.5]) == ERR_ARG
+    assert step(dtype=3) == ERR_ARG
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(hla.HLAError):
+        hla.hla_forward(x, x, x, chunk=16)

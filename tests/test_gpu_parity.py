@@ -1,0 +1,127 @@
+"""HIP path vs oracle, element by element on the same seeded inputs.
+
+Bars (relative L2 over the whole output): 1e-5 for fp32 inputs, 1e-2 for
+bf16 inputs with the oracle run on the same bf16-rounded values.  Sizes here
+are small enough for the whole oracle yet span several chunks, several
+segments and a ragged tail; the full-size workloads are in
+test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+
+from causal_streaming_scans_amd import inputs as I
+from hla_testlib import TOL, gpu_forward, oracle_forward, rel_l2, say, worst_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, H, n, d, dtype, dist, seed, decay=False):
+    return I.make_inputs(B, H, n, d, d, dtype=dtype, dist=dist, seed=seed, decay=decay)
+
+
+CASES = [
+    # dtype, variant, B, H, n, d, chunk, seg_chunks, decay, dist
+    ("f32", "hla2", 1, 1, 256, 16, 32, 0, False, "normal_scaled"),
+    ("f32", "hla2", 1, 2, 256, 16, 32, 1, False, "normal_scaled"),
+    ("f32", "hla2", 1, 2, 203, 16, 32, 2, False, "normal_scaled"),
+    ("f32", "hla2", 2, 2, 203, 32, 16, 3, True, "normal_scaled"),
+    ("f32", "hla2_ratio", 1, 2, 150, 64, 32, 2, False, "uniform_pos"),
+    ("f32", "ahla", 1, 2, 203, 16, 32, 2, False, "normal_scaled"),
+    ("f32", "ahla_ratio", 1, 2, 100, 32, 16, 2, False, "uniform_pos"),
+    ("bf16", "hla2", 2, 2, 300, 64, 64, 0, False, "l2norm"),
+    ("bf16", "hla2", 2, 2, 300, 64, 64, 1, False, "l2norm"),
+    ("bf16", "hla2", 1, 3, 1000, 64, 64, 3, False, "l2norm"),
+    ("bf16", "hla2", 1, 2, 517, 64, 32, 2, False, "l2norm"),
+    ("bf16", "hla2", 1, 2, 517, 64, 16, 5, False, "l2norm"),
+    ("bf16", "hla2_ratio", 2, 2, 777, 64, 64, 2, False, "uniform_pos"),
+    ("bf16", "hla2", 1, 4, 640, 64, 64, 2, True, "l2norm"),
+    ("bf16", "hla2_ratio", 1, 2, 640, 64, 32, 3, True, "uniform_pos"),
+    ("bf16", "hla2", 1, 2, 400, 128, 32, 2, True, "l2norm"),
+    ("bf16", "hla2", 1, 2, 333, 128, 16, 4, False, "l2norm"),
+    ("bf16", "hla2", 1, 2, 200, 32, 32, 2, False, "l2norm"),
+    ("bf16", "hla2", 1, 2, 200, 16, 16, 3, True, "l2norm"),
+    ("bf16", "ahla", 1, 2, 1000, 64, 64, 3, False, "l2norm"),
+    ("bf16", "ahla", 1, 2, 517, 64, 32, 2, False, "l2norm"),
+    ("bf16", "ahla_ratio", 1, 2, 517, 64, 64, 2, False, "uniform_pos"),
+    ("bf16", "ahla", 1, 2, 300, 128, 32, 2, False, "l2norm"),
+    ("bf16", "ahla", 1, 2, 300, 16, 16, 4, False, "l2norm"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(x) for x in c))
+def test_forward_matches_oracle(case):
+    dtype, variant, B, H, n, d, chunk, seg, decay, dist = case
+    say(f"[parity] {case}")
+    x = _inputs(B, H, n, d, dtype, dist, seed=hash(case) % 10000, decay=decay)
+    got = gpu_forward(x, variant, B, H, dtype, chunk, seg, gamma=x["gamma"])
+    want = oracle_forward(x, variant, H, gamma=x["gamma"])
+    err = rel_l2(got, want)
+    say(f"   rel_l2 {err:.3e}  worst head {worst_head(got, want):.3e}")
+    assert np.isfinite(got).all()
+    assert err < TOL[dtype]
+
+
+@pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_out_and_resume(variant, dtype):
+    """forward(n1) -> state_out -> forward(n2, state_in) equals forward(n1+n2),
+    and state_out equals the oracle's state."""
+    say(f"[resume] {variant} {dtype}")
+    B, H, n1, n2, d = 1, 2, 230, 181, 32
+    dist = "uniform_pos" if variant.endswith("ratio") else "normal_scaled"
+    decay = variant.startswith("hla2")
+    x = _inputs(B, H, n1 + n2, d, dtype, dist, seed=77, decay=decay)
+    g = x["gamma"]
+    x1 = {kk: x[kk][:, :n1] for kk in ("q", "k", "v")}
+    x2 = {kk: x[kk][:, n1:] for kk in ("q", "k", "v")}
+    o1, st = gpu_forward(x1, variant, B, H, dtype, 32, 2, gamma=g, want_state=True)
+    w1, wst = oracle_forward(x1, variant, H, gamma=g, want_state=True)
+    assert rel_l2(st, wst) < 10 * TOL[dtype]
+    o2 = gpu_forward(x2, variant, B, H, dtype, 32, 3, gamma=g, state_in=st)
+    whole = oracle_forward(x, variant, H, gamma=g)
+    err = rel_l2(np.concatenate([o1, o2], axis=1), whole)
+    say(f"   rel_l2 {err:.3e}")
+    assert err < TOL[dtype]
+    # one segment path (no scan) from the same state
+    o2b = gpu_forward(x2, variant, B, H, dtype, 32, 1000, gamma=g, state_in=st)
+    assert rel_l2(np.concatenate([o1, o2b], axis=1), whole) < TOL[dtype]
+
+
+def test_empty_sequence_passes_state_through():
+    import torch
+    import causal_streaming_scans_amd as hla
+    say("[empty]")
+    B, H, d = 1, 2, 16
+    q = torch.zeros((B, H, 0, d), device="cuda")
+    stf = hla.state_floats("hla2", d, d)
+    si = torch.randn(B * H * stf, device="cuda")
+    so = torch.empty_like(si)
+    o = hla.hla_forward(q, q, q, chunk=16, state_in=si, state_out=so)
+    torch.cuda.synchronize()
+    assert o.shape == (B, H, 0, d)
+    assert torch.equal(si, so)
+
+
+def test_deterministic():
+    """Two runs give bit-identical outputs (no atomics in any reduction that
+    reaches the output, except the LDS row sums of the ratio form, whose order
+    is fixed per wave)."""
+    import torch
+    say("[determinism]")
+    x = _inputs(1, 4, 900, 64, "bf16", "uniform_pos", seed=5)
+    a = gpu_forward(x, "hla2_ratio", 1, 4, "bf16", 64, 3)
+    b = gpu_forward(x, "hla2_ratio", 1, 4, "bf16", 64, 3)
+    assert np.array_equal(a, b)
+
+
+def test_causality_on_gpu():
+    """Perturbing tokens after t leaves outputs up to t unchanged."""
+    say("[causality]")
+    x = _inputs(1, 2, 512, 64, "bf16", "l2norm", seed=6)
+    y = {kk: x[kk].copy() for kk in ("q", "k", "v")}
+    t0 = 300
+    y["q"][:, t0 + 1:] = x["q"][:, t0 + 1:][:, ::-1]
+    y["v"][:, t0 + 1:] *= -2.0
+    a = gpu_forward(x, "hla2", 1, 2, "bf16", 64, 2)
+    b = gpu_forward(y, "hla2", 1, 2, "bf16", 64, 2)
+    assert np.array_equal(a[:, :t0 + 1], b[:, :t0 + 1])
