@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the HLA-2 forward hot path on one MI355X.
+
+One step = one whole forward pass (segment summaries -> exclusive Blelloch
+scan -> chunked forward) over one batch of the headline workload: ratio-
+normalised HLA-2, B=8, H=16, n=4096, d=dv=64, bf16 inputs and output, fp32
+state, q, k ~ U[0,1)/sqrt(d), v ~ N(0,1), seeded.  Inputs are resident in
+HBM before the timed region.  Prints ONE JSON line on stdout; progress goes
+to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Timing: K steps between two synchronisations, each stage bracketed by HIP
+events on the stream the library launches on (torch's current stream), so
+the per-kernel durations behind the roofline figure come from the same timed
+region.  The CPU baseline is the fp64 oracle on the same inputs (all heads),
+on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3
+METRIC = "HLA-2 forward tokens/sec (B·H·n/s) + % MFMA peak, n=4096 d=64 bf16"
+KERNEL_SOURCES = ["hla2_kernels.h", "device_common.h", "params.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_streaming_scans_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hla2_forward_counters.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def flops_per_token(c, d, dv):
+    # dense products of the chunked method per token: scores 2cd, Q S0 2d^2,
+    # L K 2cd, Q Z^T 2cd, P V 2c dv, Q W0 2d dv, S update 2d^2, W update 2d dv
+    return 6 * c * d + 2 * c * dv + 4 * d * d + 4 * d * dv
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--seg-chunks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import causal_streaming_scans_amd as hla
+    from causal_streaming_scans_amd import inputs as I
+
+    hla.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = I.WORKLOADS["ratio_n4096"]
+    B, H, n, d, dv, chunk = w.B, w.H, w.n, w.d, w.dv, args.chunk
+    variant = w.variant
+    seg = args.seg_chunks or hla.default_seg_chunks(variant, B, H, n, chunk)
+    nseg = -(-n // (chunk * seg))
+    log(f"[bench] workload {w.name}: chunk {chunk}, {seg} chunks/segment, {nseg} segments")
+
+    x = I.workload_inputs("ratio_n4096")
+
+    def to_dev(a, shape):
+        return torch.from_numpy(a).reshape(shape).to(torch.bfloat16).to(dev).contiguous()
+
+    q = to_dev(x["q"], (B, H, n, d))
+    k = to_dev(x["k"], (B, H, n, d))
+    v = to_dev(x["v"], (B, H, n, dv))
+    o = torch.empty((B, H, n, dv), dtype=torch.bfloat16, device=dev)
+    ws_bytes = hla.workspace_bytes(variant, B, H, n, d, dv, chunk, seg)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kw = dict(variant=variant, chunk=chunk, seg_chunks=seg, out=o, workspace=ws)
+
+    def step():
+        hla.hla_forward(q, k, v, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps, every stage bracketed by events
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(K):
+        ev[s][0].record()
+        for stage in (1, 2, 3):
+            hla.hla_forward_stage(stage, q, k, v, **kw)
+            ev[s][stage].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / K
+    stage_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
+                for i in range(3)]
+    tokens = B * H * n
+    tok_s = tokens / (ms_per_step * 1e-3)
+    log(f"[bench] {ms_per_step:.4f} ms/step, {tok_s / 1e9:.3f} G tokens/s; stages (ms) "
+        f"summary {stage_ms[0]:.4f} scan {stage_ms[1]:.4f} forward {stage_ms[2]:.4f}")
+
+    # ---- spot parity of the benchmarked output on two heads
+    import oracle
+    heads = [0, B * H - 1]
+    got = o.float().cpu().numpy().reshape(B * H, n, dv)[heads]
+    want = oracle.hla2(x["q"][heads], x["k"][heads], x["v"][heads], ratio=True)
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    log(f"[bench] spot check vs oracle (heads {heads}): rel_l2 {rel:.3e}")
+
+    # ---- roofline of the dominant kernel (largest measured stage)
+    names = ["hla2_summary_kernel", "scan_kernel", "hla2_forward_kernel"]
+    dom = int(np.argmax(stage_ms))
+    esz = 2  # bf16
+    per_token_bytes = (2 * d + 2 * dv) * esz          # q, k, v in, o out
+    sumf = d * d + 2 * d * dv + 2 * d
+    if dom == 2:
+        alg_bytes = tokens * per_token_bytes
+    elif dom == 0:
+        tok_sum = B * H * min(n, (nseg - 1) * chunk * seg)
+        alg_bytes = tok_sum * (2 * d + dv) * esz + B * H * (nseg - 1) * sumf * 4
+    else:
+        alg_bytes = B * H * 2 * nseg * sumf * 4
+    achieved = alg_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    traffic = stored_traffic(names[dom])
+    fl_tok = flops_per_token(chunk, d, dv)
+    mfma_tflops_fwd = tokens * fl_tok / (stage_ms[2] * 1e-3) / 1e12
+    mfma_tflops_step = tokens * fl_tok / (ms_per_step * 1e-3) / 1e12
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": names[dom],
+                "kernel_ms": round(stage_ms[dom], 5), "alg_bytes_per_launch": int(alg_bytes)}
+
+    # ---- decode step (one token per head, AHLA state of 32 heads, d = 64)
+    decode = None
+    if args.decode_steps > 0:
+        dw = I.WORKLOADS["ahla_n65536"]
+        BHd = dw.B * dw.H
+        stf = hla.state_floats("ahla", dw.d, dw.dv)
+        state = torch.zeros(BHd * stf, dtype=torch.float32, device=dev)
+        qd = torch.randn((dw.B, dw.H, dw.d), device=dev).to(torch.bfloat16)
+        kd = torch.randn((dw.B, dw.H, dw.d), device=dev).to(torch.bfloat16)
+        vd = torch.randn((dw.B, dw.H, dw.dv), device=dev).to(torch.bfloat16)
+        od = torch.empty((dw.B, dw.H, dw.dv), dtype=torch.bfloat16, device=dev)
+        for _ in range(10):
+            hla.hla_step(qd, kd, vd, state, variant="ahla", out=od)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.decode_steps):
+            hla.hla_step(qd, kd, vd, state, variant="ahla", out=od)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        st_bytes = 2 * BHd * stf * 4 + BHd * (2 * dw.d + 2 * dw.dv) * 2
+        decode = {"workload": "AHLA decode step, B=1 H=32 d=dv=64 bf16, fp32 state",
+                  "us_per_step": round(us, 3), "tokens_per_s": round(BHd / (us * 1e-6), 1),
+                  "state_bytes_per_step": st_bytes,
+                  "achieved_GBs": round(st_bytes / (us * 1e-6) / 1e9, 2)}
+        log(f"[bench] decode: {us:.2f} us/step")
+
+    # ---- CPU baseline: the oracle on the same inputs, all heads
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        oracle.hla2(x["q"], x["k"], x["v"], ratio=True, threads=threads)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"whole workload: all {B * H} heads x {n} tokens, fp64 serial "
+                         f"recurrence, {dt:.2f} s wall"}
+        log(f"[bench] cpu oracle: {dt:.2f} s on {threads} threads")
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "variant": variant, "B": B, "H": H, "n": n, "d": d,
+                   "dv": dv, "chunk": chunk, "seg_chunks": seg, "segments": nseg,
+                   "global_batch": B, "seq_len": n, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "mfma": {"alg_flops_per_token": fl_tok, "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                 "forward_kernel_tflops": round(mfma_tflops_fwd, 2),
+                 "forward_kernel_frac": round(mfma_tflops_fwd / BF16_MFMA_PEAK_TFLOPS, 4),
+                 "whole_step_tflops": round(mfma_tflops_step, 2),
+                 "whole_step_frac": round(mfma_tflops_step / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "stages_ms": {"summary": round(stage_ms[0], 5), "scan": round(stage_ms[1], 5),
+                      "forward": round(stage_ms[2], 5)},
+        "parity_spot_rel_l2": rel,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -20,7 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["HLAError", "VARIANTS", "load", "library_path", "hla_forward", "hla_step",
+__all__ = ["HLAError", "VARIANTS", "load", "library_path", "hla_forward", "hla_forward_stage",
+           "hla_step",
            "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +61,8 @@ def load():
     lib.hla_workspace_bytes.restype = Z
     lib.hla_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P, Z, P]
     lib.hla_forward.restype = I
+    lib.hla_forward_stage.argtypes = [I] + lib.hla_forward.argtypes
+    lib.hla_forward_stage.restype = I
     lib.hla_step.argtypes = [P, P, P, P, I, I, I, I, I, I, FP, P, P]
     lib.hla_step.restype = I
     lib.hla_status_str.argtypes = [I]
@@ -130,12 +133,8 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
-                state_in=None, state_out=None, out=None, workspace=None, stream=None):
-    """Chunked HLA-2 / AHLA forward.  q, k: [B, H, n, d]; v: [B, H, n, dv];
-    bf16 or fp32, contiguous, on one GPU.  gamma: None or H decays in (0, 1].
-    state_in / state_out: None or fp32 [B, H, state_floats] device tensors.
-    Returns o [B, H, n, dv] (``out`` if given)."""
+def _forward_call(stage, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
+                  workspace, stream):
     import torch
     lib = load()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -162,20 +161,47 @@ def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks
                 raise HLAError(f"{name} must be fp32 with B*H*{stf} elements")
     need = workspace_bytes(vid, B, H, n, d, dv, chunk, seg_chunks)
     if workspace is None and need > 0:
+        if stage is not None:
+            raise HLAError("hla_forward_stage needs the caller's workspace (shared by the stages)")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     g_keep, g_ptr = _gamma_arg(gamma, H)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            B, H, n, d, dv, _dtype_code(q), vid, g_ptr, chunk, seg_chunks,
+            state_in.data_ptr() if state_in is not None else None,
+            state_out.data_ptr() if state_out is not None else None,
+            ws_ptr, ws_len, _stream_ptr(stream, q.device))
     with torch.cuda.device(q.device):
-        rc = lib.hla_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                             B, H, n, d, dv, _dtype_code(q), vid, g_ptr, chunk, seg_chunks,
-                             state_in.data_ptr() if state_in is not None else None,
-                             state_out.data_ptr() if state_out is not None else None,
-                             ws_ptr, ws_len, _stream_ptr(stream, q.device))
+        if stage is None:
+            rc = lib.hla_forward(*args)
+        else:
+            rc = lib.hla_forward_stage(int(stage), *args)
     del g_keep
     if rc != 0:
-        raise HLAError(f"hla_forward failed: {status_str(rc)} (code {rc})")
+        name = "hla_forward" if stage is None else f"hla_forward_stage({stage})"
+        raise HLAError(f"{name} failed: {status_str(rc)} (code {rc})")
     return out
+
+
+def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
+                state_in=None, state_out=None, out=None, workspace=None, stream=None):
+    """Chunked HLA-2 / AHLA forward.  q, k: [B, H, n, d]; v: [B, H, n, dv];
+    bf16 or fp32, contiguous, on one GPU.  gamma: None or H decays in (0, 1].
+    state_in / state_out: None or fp32 [B, H, state_floats] device tensors.
+    Returns o [B, H, n, dv] (``out`` if given)."""
+    return _forward_call(None, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out,
+                         out, workspace, stream)
+
+
+def hla_forward_stage(stage, q, k, v, variant="hla2", gamma=None, chunk: int = 64,
+                      seg_chunks: int = 0, state_in=None, state_out=None, out=None,
+                      workspace=None, stream=None):
+    """One stage (1 = segment summaries, 2 = Blelloch scan, 3 = chunked
+    forward) of hla_forward; stages 1, 2, 3 in order with the same arguments
+    (and the same workspace and out) equal hla_forward."""
+    return _forward_call(stage, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out,
+                         out, workspace, stream)
 
 
 def hla_step(q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):

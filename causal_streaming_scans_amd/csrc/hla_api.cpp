@@ -101,22 +101,21 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
     return (size_t)B * H * 2 * spad * (size_t)summary_floats(d, dv) * sizeof(float);
 }
 
-hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int B, int H, int n,
-                       int d, int dv, int dtype, int variant, const float *gamma_host, int chunk,
-                       int seg_chunks, const float *state_in, float *state_out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+// Validate, pick the kernels and fill the argument block; shared by
+// hla_forward and hla_forward_stage.
+static hla_status prepare_forward(const void *q, const void *k, const void *v, void *o, int B,
+                                  int H, int n, int d, int dv, int dtype, int variant,
+                                  const float *gamma_host, int chunk, int seg_chunks,
+                                  const float *state_in, float *state_out, void *workspace,
+                                  size_t workspace_bytes, FwdKernels *kern, FwdParams *p) {
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
     if (chunk < 0 || seg_chunks < 0) return HLA_ERR_ARG;
     if (n > 0 && (!q || !k || !v || !o)) return HLA_ERR_NULL;
     if (state_in && state_out && state_in == state_out) return HLA_ERR_ARG;
-
-    const bool ahla = is_ahla(variant);
-    const bool decay = gamma_host != nullptr;
-    FwdKernels kern;
-    if (!lookup_forward(dtype, ahla, d, dv, chunk, decay, &kern)) return HLA_ERR_UNSUPPORTED;
-
+    if (!lookup_forward(dtype, is_ahla(variant), d, dv, chunk, gamma_host != nullptr, kern))
+        return HLA_ERR_UNSUPPORTED;
     const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, chunk, g);
@@ -126,42 +125,75 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int
         if (!workspace) return HLA_ERR_NULL;
         if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
     }
+    memset(p, 0, sizeof(*p));
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->o = o;
+    p->BH = B * H;
+    p->H = H;
+    p->n = n;
+    p->seg_len = chunk * g;
+    p->nseg = (int)nseg;
+    p->spad = nseg > 0 ? (int)next_pow2(nseg) : 0;
+    p->ratio = is_ratio(variant) ? 1 : 0;
+    p->ws = static_cast<float *>(workspace);
+    p->state_in = state_in;
+    p->state_out = state_out;
+    fill_gamma(p->gamma, gamma_host, H);
+    return HLA_OK;
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int BH = B * H;
-    if (n == 0) {
-        // no tokens: the state passes through unchanged
-        if (state_out) {
-            const size_t cnt = (size_t)BH * hla_state_floats(variant, d, dv);
-            if (launch_copy_or_zero(state_in, state_out, cnt, s) != hipSuccess) return HLA_ERR_DEVICE;
+// one stage of the forward pass (1 = summaries, 2 = scan, 3 = chunked forward)
+static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &p, int variant,
+                            int d, int dv, hipStream_t s) {
+    if (p.n == 0) {
+        // no tokens: the state passes through unchanged (done by the last stage)
+        if (stage == 3 && p.state_out) {
+            const size_t cnt = (size_t)p.BH * hla_state_floats(variant, d, dv);
+            if (launch_copy_or_zero(p.state_in, p.state_out, cnt, s) != hipSuccess)
+                return HLA_ERR_DEVICE;
         }
         return HLA_OK;
     }
+    hipError_t e = hipSuccess;
+    if (stage == 1 && p.nseg > 1) e = kern.summary(p, s);
+    if (stage == 2 && p.nseg > 1) e = kern.scan(p, s);
+    if (stage == 3) e = kern.forward(p, s);
+    return e == hipSuccess ? HLA_OK : HLA_ERR_DEVICE;
+}
 
+hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int B, int H, int n,
+                       int d, int dv, int dtype, int variant, const float *gamma_host, int chunk,
+                       int seg_chunks, const float *state_in, float *state_out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    FwdKernels kern;
     FwdParams p;
-    memset(&p, 0, sizeof(p));
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.BH = BH;
-    p.H = H;
-    p.n = n;
-    p.seg_len = chunk * g;
-    p.nseg = (int)nseg;
-    p.spad = (int)next_pow2(nseg);
-    p.ratio = is_ratio(variant) ? 1 : 0;
-    p.ws = static_cast<float *>(workspace);
-    p.state_in = state_in;
-    p.state_out = state_out;
-    fill_gamma(p.gamma, gamma_host, H);
-
-    if (nseg > 1) {
-        if (kern.summary(p, s) != hipSuccess) return HLA_ERR_DEVICE;
-        if (kern.scan(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+    hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
+                                    seg_chunks, state_in, state_out, workspace, workspace_bytes,
+                                    &kern, &p);
+    if (st != HLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int stage = 1; stage <= 3; ++stage) {
+        st = run_stage(stage, kern, p, variant, d, dv, s);
+        if (st != HLA_OK) return st;
     }
-    if (kern.forward(p, s) != hipSuccess) return HLA_ERR_DEVICE;
     return HLA_OK;
+}
+
+hla_status hla_forward_stage(int stage, const void *q, const void *k, const void *v, void *o,
+                             int B, int H, int n, int d, int dv, int dtype, int variant,
+                             const float *gamma_host, int chunk, int seg_chunks,
+                             const float *state_in, float *state_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    if (stage < 1 || stage > 3) return HLA_ERR_ARG;
+    FwdKernels kern;
+    FwdParams p;
+    hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
+                                    seg_chunks, state_in, state_out, workspace, workspace_bytes,
+                                    &kern, &p);
+    if (st != HLA_OK) return st;
+    return run_stage(stage, kern, p, variant, d, dv, static_cast<hipStream_t>(stream));
 }
 
 hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B, int H, int d,

@@ -104,7 +104,7 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  * gamma_host     NULL (no decay) or host array of H floats in (0, 1]: decay of
  *                head h, shared by every batch index; HLA-2 variants only,
  *                H <= HLA_MAX_DECAY_HEADS
- * chunk          tokens per intra-chunk tile: 16, 32 or 64 (64 needs d <= 64)
+ * chunk          tokens per intra-chunk tile: 16, 32 or 64 (see Supported)
  * seg_chunks     chunks per segment of the scan; 0 = hla_default_seg_chunks().
  *                The sequence is split into ceil(n / (chunk*seg_chunks))
  *                segments: their summaries are built in parallel, combined by
@@ -119,14 +119,38 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  *                ignored and on return are unspecified
  * stream         hipStream_t as void*
  *
- * Supported: d == dv in {16, 32, 64, 128} for both dtypes (fp32 with
- * d = 128 only for chunk 16).
+ * Supported (otherwise HLA_ERR_UNSUPPORTED): d == dv;
+ *   HLA_BF16: d in {16, 32, 64} with chunk 16, 32 or 64; d = 128 with chunk
+ *             16 or 32;
+ *   HLA_F32:  d in {16, 32} with chunk 16, 32 or 64; d = 64 with chunk 16 or
+ *             32.
  */
 hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        int B, int H, int n, int d, int dv, int dtype, int variant,
                        const float *gamma_host, int chunk, int seg_chunks,
                        const float *state_in, float *state_out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The three stages hla_forward runs, one at a time, on the same arguments:
+ *   stage 1  segment summaries of segments 0 .. nseg-2 into the workspace
+ *            (page section "4. ... Escaneos Asociativos": segment summaries);
+ *   stage 2  exclusive Blelloch scan of those summaries under the
+ *            semidirect-product combine, then the initial state folded in
+ *            front (same section);
+ *   stage 3  chunked forward of every segment from its carried state, and
+ *            state_out.
+ * Calling stages 1, 2, 3 in order on one stream with identical arguments is
+ * exactly hla_forward.  With a single segment stages 1 and 2 enqueue nothing.
+ * Meant for callers that time the stages or place them themselves (a caller
+ * that shards a sequence can exchange segment summaries between stages 1 and
+ * 2).  Returns HLA_ERR_ARG for a stage outside 1..3, otherwise as hla_forward.
+ */
+hla_status hla_forward_stage(int stage, const void *q, const void *k, const void *v, void *o,
+                             int B, int H, int n, int d, int dv, int dtype, int variant,
+                             const float *gamma_host, int chunk, int seg_chunks,
+                             const float *state_in, float *state_out,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * One streaming (decode) step: for every (b,h) take the single token

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert {"hla_forward", "hla_step", "hla_state_floats", "hla_workspace_bytes",
+    assert {"hla_forward", "hla_forward_stage", "hla_step", "hla_state_floats",
+            "hla_workspace_bytes",
             "hla_default_seg_chunks", "hla_status_str"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -112,6 +113,22 @@ def test_forward_validation_errors(lib):
     assert _fwd(lib, fake, fake, fake, fake, n=1024, seg=2, ws=fake, wsb=need - 1) == ERR_WS
     # state_in may not alias state_out
     assert _fwd(lib, fake, fake, fake, fake, si=fake, so=fake) == ERR_ARG
+
+
+def test_stage_validation_errors(lib):
+    fake = 0x1000
+
+    def stage(st, **kw):
+        args = dict(B=1, H=1, n=64, d=64, dv=64, dtype=BF16, variant=HLA2, chunk=64, seg=0)
+        args.update(kw)
+        return lib.hla_forward_stage(st, fake, fake, fake, fake, args["B"], args["H"], args["n"],
+                                     args["d"], args["dv"], args["dtype"], args["variant"], None,
+                                     args["chunk"], args["seg"], None, None, None, 0, None)
+    assert stage(0) == ERR_ARG
+    assert stage(4) == ERR_ARG
+    assert stage(1, B=0) == ERR_SHAPE
+    assert stage(2, chunk=48) == ERR_UNSUP
+    assert stage(3, n=1024, seg=2) == ERR_NULL   # workspace missing
 
 
 def test_step_validation_errors(lib):

@@ -1,0 +1,94 @@
+"""Full-size workloads, in the launch configuration the benchmark uses (default
+segment length), against the oracle.  Small workloads are compared whole;
+for the two largest the oracle runs on a seeded sample of whole heads (every
+head is independent, so a sampled head is checked element by element over
+its full length).
+
+Bars: relative L2 <= 1e-5 (fp32 inputs), <= 1e-2 (bf16 inputs, oracle on the
+same bf16-rounded values).
+"""
+import numpy as np
+import pytest
+
+from causal_streaming_scans_amd import inputs as I
+from hla_testlib import TOL, gpu_forward, oracle_forward, rel_l2, say, worst_head
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(key, heads=None, seg_chunks=0):
+    w = I.WORKLOADS[key]
+    say(f"[workload] {key}: {w.name}, chunk {w.chunk}, heads {heads if heads else 'all'}")
+    x = I.workload_inputs(key)
+    got = gpu_forward(x, w.variant, w.B, w.H, w.dtype, w.chunk, seg_chunks, gamma=x["gamma"])
+    assert np.isfinite(got).all()
+    if heads is not None:
+        want = oracle_forward(x, w.variant, w.H, gamma=x["gamma"], heads=heads)
+        got = got[heads]
+    else:
+        want = oracle_forward(x, w.variant, w.H, gamma=x["gamma"])
+    err = rel_l2(got, want)
+    say(f"   rel_l2 {err:.3e}  worst head {worst_head(got, want):.3e}")
+    assert err < TOL[w.dtype]
+    return x
+
+
+def test_small_f32_whole():
+    _check("small_f32")
+
+
+def test_small_f32_every_segment_split():
+    for seg in (1, 2, 3, 5):
+        _check("small_f32", seg_chunks=seg)
+
+
+def test_hla2_n2048_whole():
+    _check("hla2_n2048")
+
+
+def test_ratio_n4096_whole():
+    _check("ratio_n4096")
+
+
+def test_decay_n16384_sampled_heads():
+    rng = np.random.default_rng(4)
+    heads = sorted(rng.choice(32, size=4, replace=False).tolist())
+    _check("decay_n16384", heads=heads)
+
+
+def test_ahla_n65536_sampled_heads_and_decode():
+    """AHLA forward over 65536 tokens, then 1024 decode steps continuing from
+    the forward pass's final state, both against the oracle's own
+    continuation on sampled heads."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    from hla_testlib import to_dev
+    key = "ahla_n65536"
+    w = I.WORKLOADS[key]
+    rng = np.random.default_rng(5)
+    heads = sorted(rng.choice(w.B * w.H, size=3, replace=False).tolist())
+    say(f"[workload] {key} forward + {w.decode_tokens} decode steps, heads {heads}")
+    x = I.workload_inputs(key)
+    got, st = gpu_forward(x, w.variant, w.B, w.H, w.dtype, w.chunk, 0, want_state=True)
+    want, wst = oracle_forward(x, w.variant, w.H, heads=heads, want_state=True)
+    err = rel_l2(got[heads], want)
+    say(f"   forward rel_l2 {err:.3e}")
+    assert np.isfinite(got).all() and err < TOL[w.dtype]
+    st_err = rel_l2(st[heads], wst)
+    say(f"   state rel_l2 {st_err:.3e}")
+    assert st_err < TOL[w.dtype]
+
+    state = torch.from_numpy(st.astype(np.float32).reshape(-1)).cuda()
+    T = w.decode_tokens
+    qd = to_dev(x["q_dec"], "bf16", (T, w.B, w.H, w.d))
+    kd = to_dev(x["k_dec"], "bf16", (T, w.B, w.H, w.d))
+    vd = to_dev(x["v_dec"], "bf16", (T, w.B, w.H, w.dv))
+    outs = [hla.hla_step(qd[t], kd[t], vd[t], state, variant=w.variant) for t in range(T)]
+    torch.cuda.synchronize()
+    got_dec = torch.stack(outs).float().cpu().numpy().reshape(T, w.B * w.H, w.dv)
+    got_dec = got_dec.transpose(1, 0, 2)[heads]
+    xd = {kk: np.ascontiguousarray(x[kk + "_dec"].transpose(1, 0, 2)[heads]) for kk in "qkv"}
+    want_dec = oracle_forward(xd, w.variant, w.H, state_in=wst)
+    derr = rel_l2(got_dec, want_dec)
+    say(f"   decode rel_l2 {derr:.3e}")
+    assert np.isfinite(got_dec).all() and derr < TOL[w.dtype]
