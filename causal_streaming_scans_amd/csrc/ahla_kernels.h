@@ -15,65 +15,108 @@
 // The summary kernel runs this from zero over one segment and also forms
 // M = sum_t k_t q_t^T, the factor the segment combine's cross term M_B P_A
 // needs.
+//
+// Work split as for HLA-2: wave (r, cg) owns row tile r and column tiles cg,
+// cg + NCG, ...  The transposed scores L^T = K Q^T serve twice from
+// registers: as the A operand of L V (rows tau) and as the B operand of
+// Y^T L^T (for O^T).  Y is written to LDS transposed (for Y^T L^T and
+// K^T Y), O^T goes straight to global memory.
 #pragma once
 
-#include "device_common.h"
+#include "chunk_common.h"
 #include "hla2_kernels.h"
-#include "params.h"
 
 namespace hla {
 
-template <typename T, int D, int DV, int C, int NW>
+template <typename T, int D, int DV, int C>
 struct AhlaCfg {
-    static constexpr int NT = NW * kWave;
-    static constexpr int LDD = ld_of<T>(D), LDC = ld_of<T>(C), LDV = ld_of<T>(DV);
-    static constexpr int nTC = C / 16, nTD = D / 16, nTV = DV / 16;
-    static constexpr int TY = nTC * nTV;                 // C x DV tiles (Y, O)
-    static constexpr int TP = nTD * nTV;                 // D x DV tiles (P, E)
-    static constexpr int TM = nTD * nTD;                 // D x D tiles (M)
-    static constexpr int PY = (TY + NW - 1) / NW, PP = (TP + NW - 1) / NW, PM = (TM + NW - 1) / NW;
+    using WS = WaveShape<C, D>;
+    static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
+    static constexpr int LDD = ld_of<T>(D), LDC = ld_of<T>(C);
+    static constexpr int nTD = D / 16, nTV = DV / 16;
+    static constexpr int OJ = (nTV + NCG - 1) / NCG;      // Y / O^T tiles per wave
+    static constexpr int TP = nTD * nTV, TM = nTD * nTD;
+    static constexpr int PP = (TP + NW - 1) / NW, PM = (TM + NW - 1) / NW;
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = ahla_state_floats(D, DV);
-    static constexpr int KO = (C * LDD > C * LDV) ? C * LDD : C * LDV;
 };
 
-template <typename T, int D, int DV, int C, int NW>
+template <typename T, int D, int DV, int C>
 struct AhlaFwdSmem {
-    using G = AhlaCfg<T, D, DV, C, NW>;
+    using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T Q[C * G::LDD];
-    alignas(16) T K[G::KO];            // K rows (scores), later output staging
+    alignas(16) T K[C * G::LDD];
     alignas(16) T Kt[D * G::LDC];
     alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T L[C * G::LDC];
     alignas(16) T Yt[DV * G::LDC];
     alignas(16) T Pt[DV * G::LDD];     // Pt[j][i] = P0[i][j]
     alignas(16) T Et[DV * G::LDD];     // Et[j][i] = E0[i][j]
-    float mK[D], nk[D], y1[C], den[C];
+    float mK[D], nk[D], y1[C];
 };
 
-template <typename T, int D, int DV, int C, int NW>
+template <typename T, int D, int DV, int C>
 struct AhlaSumSmem {
-    using G = AhlaCfg<T, D, DV, C, NW>;
+    using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T Q[C * G::LDD];
     alignas(16) T Qt[D * G::LDC];
     alignas(16) T K[C * G::LDD];
     alignas(16) T Kt[D * G::LDC];
     alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T L[C * G::LDC];
     alignas(16) T Yt[DV * G::LDC];
     alignas(16) T Pt[DV * G::LDD];
     float mK[D], nk[D], y1[C];
 };
 
-template <typename T, int D, int DV, int C, int NW>
-__global__ __launch_bounds__(NW * kWave) void ahla_forward_kernel(FwdParams p) {
-    using G = AhlaCfg<T, D, DV, C, NW>;
-    constexpr int NT = G::NT, LDD = G::LDD, LDC = G::LDC, LDV = G::LDV;
-    constexpr int nTV = G::nTV;
-    __shared__ AhlaFwdSmem<T, D, DV, C, NW> sm;
+// Y = Q P0 + L V for row tile r (rows tau), written to Yt transposed; also
+// y1[tau] = q_tau . mK + sum_sigma L[tau][sigma].
+template <typename T, int D, int DV, int C, int RT, int NCG, int OJ, int LDD, int LDC>
+__device__ __forceinline__ void ahla_y_phase(const Frag16<T> (&Lf)[RT], int r, int cg, int tau,
+                                             const T *Q, const T *Pt, const T *Vt, T *Yt,
+                                             const float *mK, float *y1) {
+    constexpr int nTV = DV / 16;
+    const int g4 = (lane_id() >> 4) << 2;
+    const T *Qr = Q + 16 * r * LDD;
+#pragma unroll
+    for (int jj = 0; jj < OJ; ++jj) {
+        const int jv = cg + jj * NCG;
+        if (jv < nTV) {
+            // accumulator rows are tokens 16r + 4g + i, columns features 16 jv + c
+            f32x4 y = mma_nt(zero4(), Qr, LDD, Pt + 16 * jv * LDD, LDD, 0, D);
+            f32x4 yc = zero4();
+#pragma unroll
+            for (int s = 0; s < RT; ++s)
+                if (s <= r) yc = mma16(yc, Lf[s], ld_frag(Vt + 16 * jv * LDC + 16 * s, LDC));
+            y += yc;
+            store4(Yt + (16 * jv + acc_col()) * LDC + 16 * r + g4, y);
+        }
+    }
+    if (cg == 0) {
+        float rs = 0.f;
+#pragma unroll
+        for (int s = 0; s < RT; ++s)
+            if (s <= r) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rs += frag_val(Lf[s], i);
+            }
+        const float yv = lane_dot<T, D>(Q + tau * LDD, mK) + sum_groups(rs);
+        if (lane_id() < 16) y1[tau] = yv;
+    }
+}
+
+template <typename T, int D, int DV, int C>
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT),
+                             (hla2_min_blocks<AhlaCfg<T, D, DV, C>::NT, 0, D, DV>()))
+void ahla_forward_kernel(FwdParams p) {
+    using G = AhlaCfg<T, D, DV, C>;
+    constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
+    constexpr int LDD = G::LDD, LDC = G::LDC, nTV = G::nTV;
+    __shared__ AhlaFwdSmem<T, D, DV, C> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
+    const int r = w / NCG, cg = w % NCG;
+    const int col = acc_col(), g = lane_id() >> 4, g4 = g << 2;
+    const int tau = 16 * r + col;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
@@ -102,17 +145,15 @@ __global__ __launch_bounds__(NW * kWave) void ahla_forward_kernel(FwdParams p) {
         accP[s] = zero4();
         accE[s] = zero4();
         if (t < G::TP) {
-            const int ti = t / nTV, tj = t % nTV;
+            const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                const float xp = P0 ? P0[row * DV + col] : 0.f;
-                const float xe = E0 ? E0[row * DV + col] : 0.f;
-                accP[s][r] = xp;
-                accE[s][r] = xe;
-                sm.Pt[col * LDD + row] = from_f<T>(xp);
-                sm.Et[col * LDD + row] = from_f<T>(xe);
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                accP[s][i] = P0 ? P0[idx] : 0.f;
+                accE[s][i] = E0 ? E0[idx] : 0.f;
             }
+            store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
+            store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[s]);
         }
     }
     for (int i = threadIdx.x; i < D; i += NT) {
@@ -120,133 +161,88 @@ __global__ __launch_bounds__(NW * kWave) void ahla_forward_kernel(FwdParams p) {
         sm.nk[i] = nk0 ? nk0[i] : 0.f;
     }
 
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-        const int cv = min(C, t_end - c0);
-        __syncthreads();
-        stage_tile<T, C, D, NT>(q + (size_t)c0 * D, cv, sm.Q, LDD, nullptr, 0);
-        stage_tile<T, C, D, NT>(k + (size_t)c0 * D, cv, sm.K, LDD, sm.Kt, LDC);
-        stage_tile<T, C, DV, NT>(v + (size_t)c0 * DV, cv, nullptr, 0, sm.Vt, LDC);
-        __syncthreads();
+    ChunkRegs<T, C, D, NT> rq, rk;
+    ChunkRegs<T, C, DV, NT> rv;
+    int c0 = t_begin;
+    int cv = min(C, t_end - c0);
+    rq.load(q + (size_t)c0 * D, cv);
+    rk.load(k + (size_t)c0 * D, cv);
+    rv.load(v + (size_t)c0 * DV, cv);
 
-        // scores and carried-state terms Q P0, Q E0, Q mK0, Q nk0
-        scores_tril<T, D, C, false, NW, LDD, LDC>(sm.Q, sm.K, sm.L, nullptr);
-        f32x4 accY[G::PY], accO[G::PY];
-#pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            accY[s] = zero4();
-            accO[s] = zero4();
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-                accY[s] = mma_nt(accY[s], sm.Q + ti * 16 * LDD, LDD, sm.Pt + tj * 16 * LDD, LDD, 0, D);
-                accO[s] = mma_nt(accO[s], sm.Q + ti * 16 * LDD, LDD, sm.Et + tj * 16 * LDD, LDD, 0, D);
-            }
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            float a = 0.f, b = 0.f;
-            for (int c = 0; c < D; ++c) {
-                const float x = to_f(sm.Q[i * LDD + c]);
-                a += x * sm.mK[c];
-                b += x * sm.nk[c];
-            }
-            sm.y1[i] = a;
-            sm.den[i] = b;
+    while (c0 < t_end) {
+        __syncthreads();
+        rq.store_rows(sm.Q, LDD);
+        rk.store_rows(sm.K, LDD);
+        rk.store_cols(sm.Kt, LDC);
+        rv.store_cols(sm.Vt, LDC);
+        const int n0 = c0 + C;
+        const int ncv = min(C, t_end - n0);
+        if (n0 < t_end) {
+            rq.load(q + (size_t)n0 * D, ncv);
+            rk.load(k + (size_t)n0 * D, ncv);
+            rv.load(v + (size_t)n0 * DV, ncv);
         }
         __syncthreads();
 
-        // Y = Q P0 + L V ; P0 += K^T V ; y1 += L 1
+        const T *Qr = sm.Q + 16 * r * LDD;
+        Frag16<T> Lf[RT];
+        scores_t<T, D, RT, LDD, false>(Lf, sm.K, Qr, r, tau, nullptr, 1);
+        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
+                                                            sm.Yt, sm.mK, sm.y1);
+        // carried part of the output and of its denominator
+        f32x4 accO[G::OJ];
 #pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-                accY[s] = mma_nt(accY[s], sm.L + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
+        for (int jj = 0; jj < G::OJ; ++jj) {
+            const int jv = cg + jj * NCG;
+            accO[jj] = zero4();
+            if (jv < nTV) accO[jj] = mma_nt(zero4(), sm.Et + 16 * jv * LDD, LDD, Qr, LDD, 0, D);
+        }
+        float den = 0.f;
+        if (p.ratio) den = lane_dot<T, D>(sm.Q + tau * LDD, sm.nk);
+        __syncthreads();
+
+        // O^T += Y^T L^T ; den += sum_sigma L[tau][sigma] y1[sigma]
+        if (p.ratio) {
+            float a = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Yt[(tj * 16 + acc_col()) * LDC + ti * 16 + acc_row(r)] = from_f<T>(accY[s][r]);
+            for (int s = 0; s < RT; ++s)
+                if (s <= r) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a += frag_val(Lf[s], i) * sm.y1[16 * s + g4 + i];
+                }
+            den += sum_groups(a);
+        }
+#pragma unroll
+        for (int jj = 0; jj < G::OJ; ++jj) {
+            const int jv = cg + jj * NCG;
+            if (jv < nTV) {
+                f32x4 oc = zero4();
+#pragma unroll
+                for (int s = 0; s < RT; ++s)
+                    if (s <= r) oc = mma16(oc, ld_frag(sm.Yt + 16 * jv * LDC + 16 * s, LDC), Lf[s]);
+                f32x4 ov = accO[jj] + oc;
+                if (p.ratio) ov *= 1.f / den;
+                if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
             }
         }
+        // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
 #pragma unroll
         for (int s = 0; s < G::PP; ++s) {
             const int t = w + s * NW;
             if (t < G::TP) {
-                const int ti = t / nTV, tj = t % nTV;
-                accP[s] = mma_nt(accP[s], sm.Kt + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Pt[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accP[s][r]);
+                const int ti = t / nTV, tv = t % nTV;
+                accP[s] = mma_nt(accP[s], sm.Kt + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
+                accE[s] = mma_nt(accE[s], sm.Kt + 16 * ti * LDC, LDC, sm.Yt + 16 * tv * LDC, LDC, 0, C);
+                store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
+                store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[s]);
             }
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            float a = 0.f;
-            for (int c = 0; c <= i; ++c) a += to_f(sm.L[i * LDC + c]);
-            sm.y1[i] += a;
-        }
-        __syncthreads();
-
-        // O = Q E0 + L Y ; E0 += K^T Y ; den += L y1 ; nk += K^T y1 ; mK += K^T 1
-#pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-                accO[s] = mma_nt(accO[s], sm.L + ti * 16 * LDC, LDC, sm.Yt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < G::PP; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TP) {
-                const int ti = t / nTV, tj = t % nTV;
-                accE[s] = mma_nt(accE[s], sm.Kt + ti * 16 * LDC, LDC, sm.Yt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Et[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accE[s][r]);
-            }
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            float a = 0.f;
-            for (int c = 0; c <= i; ++c) a += to_f(sm.L[i * LDC + c]) * sm.y1[c];
-            sm.den[i] += a;
         }
         for (int i = threadIdx.x; i < D; i += NT) {
-            float a = 0.f, b = 0.f;
-            for (int c = 0; c < C; ++c) {
-                const float x = to_f(sm.Kt[i * LDC + c]);
-                a += x;
-                b += x * sm.y1[c];
-            }
-            sm.mK[i] += a;
-            sm.nk[i] += b;
+            sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
+            sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
         }
-        __syncthreads();
-
-        T *Os = sm.K;
-#pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                    float ov = accO[s][r];
-                    if (p.ratio) ov = ov / sm.den[row];
-                    Os[row * LDV + col] = from_f<T>(ov);
-                }
-            }
-        }
-        __syncthreads();
-        {
-            constexpr int VE = Vec16<T>::N;
-            constexpr int VPR = DV / VE;
-            for (int idx = threadIdx.x; idx < cv * VPR; idx += NT) {
-                const int r = idx / VPR, c = (idx % VPR) * VE;
-                store16(o + (size_t)(c0 + r) * DV + c, load16(Os + r * LDV + c));
-            }
-        }
+        c0 = n0;
+        cv = ncv;
     }
 
     if (p.state_out && seg == p.nseg - 1) {
@@ -255,12 +251,12 @@ __global__ __launch_bounds__(NW * kWave) void ahla_forward_kernel(FwdParams p) {
         for (int s = 0; s < G::PP; ++s) {
             const int t = w + s * NW;
             if (t < G::TP) {
-                const int ti = t / nTV, tj = t % nTV;
+                const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                    so[idx] = accP[s][r];
-                    so[D * DV + idx] = accE[s][r];
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                    so[idx] = accP[s][i];
+                    so[D * DV + idx] = accE[s][i];
                 }
             }
         }
@@ -272,15 +268,20 @@ __global__ __launch_bounds__(NW * kWave) void ahla_forward_kernel(FwdParams p) {
     }
 }
 
-template <typename T, int D, int DV, int C, int NW>
-__global__ __launch_bounds__(NW * kWave) void ahla_summary_kernel(FwdParams p) {
-    using G = AhlaCfg<T, D, DV, C, NW>;
-    constexpr int NT = G::NT, LDD = G::LDD, LDC = G::LDC;
-    constexpr int nTD = G::nTD, nTV = G::nTV;
-    __shared__ AhlaSumSmem<T, D, DV, C, NW> sm;
+template <typename T, int D, int DV, int C>
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT),
+                             (hla2_min_blocks<AhlaCfg<T, D, DV, C>::NT, 0, D, DV>()))
+void ahla_summary_kernel(FwdParams p) {
+    using G = AhlaCfg<T, D, DV, C>;
+    constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
+    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    __shared__ AhlaSumSmem<T, D, DV, C> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
+    const int r = w / NCG, cg = w % NCG;
+    const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    const int tau = 16 * r + col;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
@@ -289,74 +290,57 @@ __global__ __launch_bounds__(NW * kWave) void ahla_summary_kernel(FwdParams p) {
 
     f32x4 accP[G::PP], accE[G::PP], accM[G::PM];
 #pragma unroll
-    for (int s = 0; s < G::PP; ++s) { accP[s] = zero4(); accE[s] = zero4(); }
+    for (int s = 0; s < G::PP; ++s) {
+        accP[s] = zero4();
+        accE[s] = zero4();
+    }
 #pragma unroll
     for (int s = 0; s < G::PM; ++s) accM[s] = zero4();
     for (int i = threadIdx.x; i < DV * LDD; i += NT) sm.Pt[i] = from_f<T>(0.f);
-    for (int i = threadIdx.x; i < D; i += NT) { sm.mK[i] = 0.f; sm.nk[i] = 0.f; }
+    for (int i = threadIdx.x; i < D; i += NT) {
+        sm.mK[i] = 0.f;
+        sm.nk[i] = 0.f;
+    }
 
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-        const int cv = min(C, t_end - c0);
-        __syncthreads();
-        stage_tile<T, C, D, NT>(q + (size_t)c0 * D, cv, sm.Q, LDD, sm.Qt, LDC);
-        stage_tile<T, C, D, NT>(k + (size_t)c0 * D, cv, sm.K, LDD, sm.Kt, LDC);
-        stage_tile<T, C, DV, NT>(v + (size_t)c0 * DV, cv, nullptr, 0, sm.Vt, LDC);
-        __syncthreads();
+    ChunkRegs<T, C, D, NT> rq, rk;
+    ChunkRegs<T, C, DV, NT> rv;
+    int c0 = t_begin;
+    int cv = min(C, t_end - c0);
+    rq.load(q + (size_t)c0 * D, cv);
+    rk.load(k + (size_t)c0 * D, cv);
+    rv.load(v + (size_t)c0 * DV, cv);
 
-        scores_tril<T, D, C, false, NW, LDD, LDC>(sm.Q, sm.K, sm.L, nullptr);
-        f32x4 accY[G::PY];
-#pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            accY[s] = zero4();
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-                accY[s] = mma_nt(accY[s], sm.Q + ti * 16 * LDD, LDD, sm.Pt + tj * 16 * LDD, LDD, 0, D);
-            }
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            float a = 0.f;
-            for (int c = 0; c < D; ++c) a += to_f(sm.Q[i * LDD + c]) * sm.mK[c];
-            sm.y1[i] = a;
+    while (c0 < t_end) {
+        __syncthreads();
+        rq.store_rows(sm.Q, LDD);
+        rq.store_cols(sm.Qt, LDC);
+        rk.store_rows(sm.K, LDD);
+        rk.store_cols(sm.Kt, LDC);
+        rv.store_cols(sm.Vt, LDC);
+        const int n0 = c0 + C;
+        const int ncv = min(C, t_end - n0);
+        if (n0 < t_end) {
+            rq.load(q + (size_t)n0 * D, ncv);
+            rk.load(k + (size_t)n0 * D, ncv);
+            rv.load(v + (size_t)n0 * DV, ncv);
         }
         __syncthreads();
 
-#pragma unroll
-        for (int s = 0; s < G::PY; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TY) {
-                const int ti = t / nTV, tj = t % nTV;
-                accY[s] = mma_nt(accY[s], sm.L + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Yt[(tj * 16 + acc_col()) * LDC + ti * 16 + acc_row(r)] = from_f<T>(accY[s][r]);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < G::PP; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TP) {
-                const int ti = t / nTV, tj = t % nTV;
-                accP[s] = mma_nt(accP[s], sm.Kt + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Pt[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accP[s][r]);
-            }
-        }
-        for (int i = threadIdx.x; i < C; i += NT) {
-            float a = 0.f;
-            for (int c = 0; c <= i; ++c) a += to_f(sm.L[i * LDC + c]);
-            sm.y1[i] += a;
-        }
+        const T *Qr = sm.Q + 16 * r * LDD;
+        Frag16<T> Lf[RT];
+        scores_t<T, D, RT, LDD, false>(Lf, sm.K, Qr, r, tau, nullptr, 1);
+        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
+                                                            sm.Yt, sm.mK, sm.y1);
         __syncthreads();
 
 #pragma unroll
         for (int s = 0; s < G::PP; ++s) {
             const int t = w + s * NW;
             if (t < G::TP) {
-                const int ti = t / nTV, tj = t % nTV;
-                accE[s] = mma_nt(accE[s], sm.Kt + ti * 16 * LDC, LDC, sm.Yt + tj * 16 * LDC, LDC, 0, C);
+                const int ti = t / nTV, tv = t % nTV;
+                accP[s] = mma_nt(accP[s], sm.Kt + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
+                accE[s] = mma_nt(accE[s], sm.Kt + 16 * ti * LDC, LDC, sm.Yt + 16 * tv * LDC, LDC, 0, C);
+                store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
             }
         }
 #pragma unroll
@@ -364,19 +348,15 @@ __global__ __launch_bounds__(NW * kWave) void ahla_summary_kernel(FwdParams p) {
             const int t = w + s * NW;
             if (t < G::TM) {
                 const int ti = t / nTD, tj = t % nTD;
-                accM[s] = mma_nt(accM[s], sm.Kt + ti * 16 * LDC, LDC, sm.Qt + tj * 16 * LDC, LDC, 0, C);
+                accM[s] = mma_nt(accM[s], sm.Kt + 16 * ti * LDC, LDC, sm.Qt + 16 * tj * LDC, LDC, 0, C);
             }
         }
         for (int i = threadIdx.x; i < D; i += NT) {
-            float a = 0.f, b = 0.f;
-            for (int c = 0; c < C; ++c) {
-                const float x = to_f(sm.Kt[i * LDC + c]);
-                a += x;
-                b += x * sm.y1[c];
-            }
-            sm.mK[i] += a;
-            sm.nk[i] += b;
+            sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
+            sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
         }
+        c0 = n0;
+        cv = ncv;
     }
     __syncthreads();
 
@@ -388,20 +368,19 @@ __global__ __launch_bounds__(NW * kWave) void ahla_summary_kernel(FwdParams p) {
         if (t < G::TM) {
             const int ti = t / nTD, tj = t % nTD;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                e[(ti * 16 + acc_row(r)) * D + tj * 16 + acc_col()] = accM[s][r];
+            for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accM[s][i];
         }
     }
 #pragma unroll
     for (int s = 0; s < G::PP; ++s) {
         const int t = w + s * NW;
         if (t < G::TP) {
-            const int ti = t / nTV, tj = t % nTV;
+            const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                e[D * D + idx] = accP[s][r];
-                e[D * D + D * DV + idx] = accE[s][r];
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                e[D * D + idx] = accP[s][i];
+                e[D * D + D * DV + idx] = accE[s][i];
             }
         }
     }

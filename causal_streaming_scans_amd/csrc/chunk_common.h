@@ -1,0 +1,120 @@
+// chunk_common.h -- pieces shared by the chunk kernels of HLA-2 and AHLA.
+#pragma once
+
+#include "device_common.h"
+#include "params.h"
+
+namespace hla {
+
+// Waves per workgroup for a chunk of C tokens and head size D: one row tile of
+// 16 tokens per wave group, column groups added until there are 4 waves (8 for
+// D >= 128, whose fp32 state needs the registers of 8 waves).
+template <int C, int D>
+struct WaveShape {
+    static constexpr int RT = C / 16;                       // row tiles per chunk
+    static constexpr int target = D >= 128 ? 8 : 4;
+    static constexpr int ncg0 = target / RT > 0 ? target / RT : 1;
+    static constexpr int NCG = ncg0 < D / 16 ? ncg0 : D / 16;  // column groups
+    static constexpr int NW = RT * NCG;
+    static constexpr int NT = NW * kWave;
+};
+
+// One thread's share of a [C][COLS] chunk tile, held in registers between the
+// global load (issued a chunk ahead) and the LDS store.
+template <typename T, int C, int COLS, int NT>
+struct ChunkRegs {
+    static constexpr int VE = Vec16<T>::N;
+    static constexpr int VPR = COLS / VE;
+    static constexpr int NVEC = C * VPR;
+    static constexpr int NV = (NVEC + NT - 1) / NT;
+    Vec16<T> x[NV];
+
+    __device__ __forceinline__ void load(const T *__restrict__ src, int rows_valid) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            const int r = idx / VPR, c = (idx % VPR) * VE;
+            if (idx < NVEC && r < rows_valid) {
+                x[i] = load16(src + (size_t)r * COLS + c);
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) x[i].v[e] = from_f<T>(0.f);
+            }
+        }
+    }
+    // dst[r][c] (row-major, leading dim ld)
+    __device__ __forceinline__ void store_rows(T *dst, int ld) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) store16(dst + (idx / VPR) * ld + (idx % VPR) * VE, x[i]);
+        }
+    }
+    // dstT[c][r] (transposed, leading dim ld)
+    __device__ __forceinline__ void store_cols(T *dstT, int ld) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) {
+                const int r = idx / VPR, c = (idx % VPR) * VE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = x[i].v[e];
+            }
+        }
+    }
+    // dstT[c][r] = src[r][c] * w, w = gp[wofs - r] for r <= wofs, else 0
+    __device__ __forceinline__ void store_cols_w(T *dstT, int ld, const float *gp, int wofs) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) {
+                const int r = idx / VPR, c = (idx % VPR) * VE;
+                const float wr = r <= wofs ? gp[wofs - r] : 0.f;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = from_f<T>(to_f(x[i].v[e]) * wr);
+            }
+        }
+    }
+};
+
+// Sum of the first C entries of row i of a [*][ld] LDS matrix (vector reads).
+template <typename T, int C>
+__device__ __forceinline__ float row_sum(const T *m, int ld, int i) {
+    constexpr int VE = Vec16<T>::N;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; c += VE) {
+        const Vec16<T> x = load16(m + i * ld + c);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s += to_f(x.v[e]);
+    }
+    return s;
+}
+
+// sum_c m[i][c] * w[c] over the first C columns
+template <typename T, int C>
+__device__ __forceinline__ float row_dot(const T *m, int ld, int i, const float *w) {
+    constexpr int VE = Vec16<T>::N;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; c += VE) {
+        const Vec16<T> x = load16(m + i * ld + c);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s += to_f(x.v[e]) * w[c + e];
+    }
+    return s;
+}
+
+// q_tau . vec for the lane's token: each lane group takes a quarter of D,
+// then the groups are summed.  Qrow points at Q[tau][0].
+template <typename T, int D>
+__device__ __forceinline__ float lane_dot(const T *Qrow, const float *vec) {
+    constexpr int Q4 = D / 4;
+    const int g = lane_id() >> 4;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < Q4; ++k) s += to_f(Qrow[g * Q4 + k]) * vec[g * Q4 + k];
+    return sum_groups(s);
+}
+
+}  // namespace hla

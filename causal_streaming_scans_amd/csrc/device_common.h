@@ -41,22 +41,28 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // ---------------------------------------------------------------- MFMA tiles
 
 // acc += A[0:16][kbeg:kend] * Bt[0:16][kbeg:kend]^T, k range a multiple of 16.
+// One instruction shape per call: 16x16x32 when the range is a multiple of
+// 32, else 16x16x16 throughout.  An accumulation chain never switches MFMA
+// shape -- on gfx950 a 16x16x16 that takes a 16x16x32 result as its
+// accumulator back to back has been seen to read it before it is final.
 __device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const bf16 *A, int lda, const bf16 *Bt,
                                         int ldb, int kbeg, int kend) {
     const int l = lane_id();
     const int r = l & 15, g = l >> 4;
     const bf16 *a = A + r * lda;
     const bf16 *b = Bt + r * ldb;
-    int k = kbeg;
-    for (; k + 32 <= kend; k += 32) {
-        bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + k + g * 8);
-        bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + k + g * 8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-    }
-    if (k < kend) {
-        i16x4 av = *reinterpret_cast<const i16x4 *>(a + k + g * 4);
-        i16x4 bv = *reinterpret_cast<const i16x4 *>(b + k + g * 4);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+    if (((kend - kbeg) & 31) == 0) {
+        for (int k = kbeg; k < kend; k += 32) {
+            bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + k + g * 8);
+            bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + k + g * 8);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+        }
+    } else {
+        for (int k = kbeg; k < kend; k += 16) {
+            i16x4 av = *reinterpret_cast<const i16x4 *>(a + k + g * 4);
+            i16x4 bv = *reinterpret_cast<const i16x4 *>(b + k + g * 4);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+        }
     }
     return acc;
 }
@@ -71,6 +77,83 @@ __device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const float *A, int lda, cons
     for (int k = kbeg; k < kend; k += 4)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k], acc, 0, 0, 0);
     return acc;
+}
+
+// ------------------------------------------------ register-chained operands
+//
+// A 16x16 accumulator tile C (lane l holds C[4g + i][c], g = l/16, c = l%16)
+// is, once rounded to the operand type, directly the B operand of a product
+// with k running over the tile's 16 rows: lane l supplies B[k = 4g + i][c].
+// The matching A operand has lane l supply A[c][4g + i] (row c, four
+// consecutive k), which is also what a 16x16 accumulator of A^T holds.
+// bf16: one V_MFMA_F32_16X16X16_BF16 per 16-deep step.  fp32: four
+// V_MFMA_F32_16X16X4_F32, instruction m pairing slot m of every lane group
+// (k = 4g + m) on both sides.  A chain of mma16 steps starts from its own
+// zero accumulator and is added to any 16x16x32 partial sum with VALU adds
+// (see mma_nt).
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> { i16x4 v; };
+template <> struct Frag16<float> { f32x4 v; };
+
+template <typename T> __device__ __forceinline__ Frag16<T> to_frag(f32x4 a);
+template <> __device__ __forceinline__ Frag16<bf16> to_frag<bf16>(f32x4 a) {
+    union { bf16 h[4]; i16x4 v; } u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u.h[i] = (bf16)a[i];
+    return Frag16<bf16>{u.v};
+}
+template <> __device__ __forceinline__ Frag16<float> to_frag<float>(f32x4 a) { return Frag16<float>{a}; }
+
+// value of slot i of a fragment (as the rounded operand the MFMA consumes)
+__device__ __forceinline__ float frag_val(const Frag16<bf16> &f, int i) {
+    union { i16x4 v; bf16 h[4]; } u;
+    u.v = f.v;
+    return (float)u.h[i];
+}
+__device__ __forceinline__ float frag_val(const Frag16<float> &f, int i) { return f.v[i]; }
+
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, Frag16<bf16> a, Frag16<bf16> b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, Frag16<float> a, Frag16<float> b) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[m], b.v[m], acc, 0, 0, 0);
+    return acc;
+}
+
+// Fragment whose four k-values are contiguous in LDS: lane l reads
+// base[(l%16) * ld + 4g .. 4g+3].
+__device__ __forceinline__ Frag16<bf16> ld_frag(const bf16 *base, int ld) {
+    const int l = lane_id();
+    return Frag16<bf16>{*reinterpret_cast<const i16x4 *>(base + (l & 15) * ld + ((l >> 4) << 2))};
+}
+__device__ __forceinline__ Frag16<float> ld_frag(const float *base, int ld) {
+    const int l = lane_id();
+    return Frag16<float>{*reinterpret_cast<const f32x4 *>(base + (l & 15) * ld + ((l >> 4) << 2))};
+}
+
+// Store four consecutive T values (one accumulator's slots, converted).
+__device__ __forceinline__ void store4(bf16 *p, f32x4 a) {
+    union { bf16 h[4]; uint2 v; } u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u.h[i] = (bf16)a[i];
+    *reinterpret_cast<uint2 *>(p) = u.v;
+}
+__device__ __forceinline__ void store4(float *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
+
+// Sum over the 16 lanes of each lane group (same g, all c).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 16);
+    x += __shfl_xor(x, 2, 16);
+    x += __shfl_xor(x, 4, 16);
+    x += __shfl_xor(x, 8, 16);
+    return x;
+}
+// Sum over the 4 lane groups (same c, all g).
+__device__ __forceinline__ float sum_groups(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
 }
 
 // Row / column of accumulator element r held by this lane within its tile.

@@ -23,107 +23,115 @@
 // segment and also accumulates C = sum g^(e-t) q v^T and m = sum g^(e-t) q,
 // which the segment combine needs for its cross term.
 //
-// Work split: NW waves; every product is a set of 16x16 MFMA tiles dealt
-// round-robin to the waves.  The fp32 state S0, W0 lives in MFMA accumulators
-// for the whole segment; its T-typed copy (transposed, the Bt operand of
-// Q S0 and Q W0) is refreshed in LDS once per chunk.
+// Work split.  Wave (r, cg) owns row tile r (16 tokens) of the chunk and the
+// output column tiles cg, cg + NCG, ...  The scores are formed transposed
+// (L^T = K Q^T), so the accumulator is directly the operand of K^T L^T (for
+// Z^T) without an LDS round trip; likewise P^T = Z Q^T feeds V^T P^T (for
+// O^T).  O^T's accumulator holds four consecutive output features of one
+// token, so the output is written straight from registers.  Z goes through
+// LDS (row-major for P, and decay-weighted transposed for the W update),
+// since every row tile needs all earlier rows of it.  The fp32 state S0, W0
+// is spread over all waves as MFMA accumulators for the whole segment; its
+// T-typed transposed copy in LDS is the operand of Q S0 and Q W0.  The next
+// chunk's Q, K, V are loaded into registers while the current one computes.
 #pragma once
 
-#include "device_common.h"
-#include "params.h"
+#include "chunk_common.h"
 
 namespace hla {
 
-template <typename T, int D, int DV, int C, bool DECAY, int NW>
+template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2Cfg {
-    static constexpr int NT = NW * kWave;
+    using WS = WaveShape<C, D>;
+    static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
     static constexpr int LDD = ld_of<T>(D);   // rows of length D
     static constexpr int LDC = ld_of<T>(C);   // rows of length C
-    static constexpr int LDV = ld_of<T>(DV);  // rows of length DV
-    static constexpr int nTC = C / 16, nTD = D / 16, nTV = DV / 16;
-    static constexpr int TZ = nTC * nTD, TO = nTC * nTV, TS = nTD * nTD, TW = nTD * nTV;
-    static constexpr int TL = nTC * (nTC + 1) / 2;       // lower-triangular chunk tiles
-    static constexpr int PZ = (TZ + NW - 1) / NW, PO = (TO + NW - 1) / NW;
+    static constexpr int nTD = D / 16, nTV = DV / 16;
+    static constexpr int ZJ = (nTD + NCG - 1) / NCG;    // Z^T tiles per wave
+    static constexpr int OJ = (nTV + NCG - 1) / NCG;    // O^T tiles per wave
+    static constexpr int TS = nTD * nTD, TW = nTD * nTV;
     static constexpr int PS = (TS + NW - 1) / NW, PW = (TW + NW - 1) / NW;
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = hla2_state_floats(D, DV);
-    static constexpr int KO = (C * LDD > C * LDV) ? C * LDD : C * LDV;  // K rows / output staging
     static constexpr int NPOW = 2 * C + 2;
     static_assert(D % 16 == 0 && DV % 16 == 0 && C % 16 == 0, "tile multiples");
 };
 
-template <typename T, int D, int DV, int C, bool DECAY, int NW>
+template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2FwdSmem {
-    using G = Hla2Cfg<T, D, DV, C, DECAY, NW>;
+    using G = Hla2Cfg<T, D, DV, C, DECAY>;
     alignas(16) T Q[C * G::LDD];
-    alignas(16) T K[G::KO];            // K rows in stage 1, output staging in stage 4
+    alignas(16) T K[C * G::LDD];
     alignas(16) T Kt[D * G::LDC];
-    alignas(16) T Ktw[DECAY ? D * G::LDC : 8];
+    alignas(16) T Ktw[DECAY ? D * G::LDC : 8];   // K^T weighted by g^(c-1-tau)
     alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T L[C * G::LDC];
     alignas(16) T Z[C * G::LDD];
-    alignas(16) T Ztw[D * G::LDC];
-    alignas(16) T P[C * G::LDC];
-    alignas(16) T St[D * G::LDD];      // St[j][i] = S0[i][j]
-    alignas(16) T Wt[DV * G::LDD];     // Wt[j][i] = W0[i][j]
-    float u[D];
-    float den[C];                      // carried-state part of the denominator
-    float denp[C][G::nTC];             // row sums of P, one per 16-column tile
+    alignas(16) T Ztw[D * G::LDC];               // Z^T weighted by g^(2(c-1-tau))
+    alignas(16) T St[D * G::LDD];                // St[j][i] = S0[i][j]
+    alignas(16) T Wt[DV * G::LDD];               // Wt[j][i] = W0[i][j]
+    float u0[D];
     float gp[G::NPOW];
 };
 
-template <typename T, int D, int DV, int C, bool DECAY, int NW>
+template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
-    using G = Hla2Cfg<T, D, DV, C, DECAY, NW>;
+    using G = Hla2Cfg<T, D, DV, C, DECAY>;
     alignas(16) T Q[C * G::LDD];
-    alignas(16) T Qtw[D * G::LDC];     // Q^T weighted by g^(c-1-tau)
     alignas(16) T K[C * G::LDD];
     alignas(16) T Kt[D * G::LDC];
     alignas(16) T Ktw[DECAY ? D * G::LDC : 8];
+    alignas(16) T Qtw[D * G::LDC];               // Q^T weighted by g^(c-1-tau)
     alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T L[C * G::LDC];
     alignas(16) T Ztw[D * G::LDC];
     alignas(16) T St[D * G::LDD];
-    float u[D];
-    float m[D];
+    float u0[D];
+    float m0[D];
     float gp[G::NPOW];
 };
 
-// ---------------------------------------------------------------- helpers
+template <int NT, int NW, int D, int DV>
+constexpr int hla2_min_blocks() {
+    return (D <= 64 && DV <= 64 && NT <= 256) ? 2 : 1;
+}
 
-// scores L = D_g * tril(Q K^T) into LDS (lower tiles only; upper tiles of L
-// are never read because every consumer stops its k loop at the diagonal)
-template <typename T, int D, int C, bool DECAY, int NW, int LDD, int LDC>
-__device__ __forceinline__ void scores_tril(const T *Q, const T *K, T *L, const float *gp) {
-    constexpr int nTC = C / 16;
-    const int w = wave_id();
-    int t = 0;
-    for (int ti = 0; ti < nTC; ++ti) {
-        for (int tj = 0; tj <= ti; ++tj, ++t) {
-            if (t % NW != w) continue;
-            f32x4 a = mma_nt(zero4(), Q + ti * 16 * LDD, LDD, K + tj * 16 * LDD, LDD, 0, D);
+// L^T tiles of row tile r as operand fragments: Lf[s] holds
+// (D_g * tril(Q K^T))^T[sigma in tile s][tau in tile r], s <= r.
+template <typename T, int D, int RT, int LDD, bool DECAY>
+__device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[RT], const T *K, const T *Qr, int r,
+                                         int tau, const float *gp, int gexp) {
+    const int g4 = (lane_id() >> 4) << 2;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                float val = 0.f;
-                if (col <= row) val = DECAY ? a[r] * gp[row - col] : a[r];
-                L[row * LDC + col] = from_f<T>(val);
+    for (int s = 0; s < RT; ++s) {
+        if (s <= r) {
+            f32x4 a = mma_nt(zero4(), K + 16 * s * LDD, LDD, Qr, LDD, 0, D);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sigma = 16 * s + g4 + i;
+                float m = 0.f;
+                if (sigma <= tau) m = DECAY ? a[i] * gp[gexp * (tau - sigma)] : a[i];
+                a[i] = m;
             }
+            Lf[s] = to_frag<T>(a);
         }
     }
 }
 
 // ------------------------------------------------------------ forward kernel
 
-template <typename T, int D, int DV, int C, bool DECAY, int NW>
-__global__ __launch_bounds__(NW * kWave) void hla2_forward_kernel(FwdParams p) {
-    using G = Hla2Cfg<T, D, DV, C, DECAY, NW>;
-    constexpr int NT = G::NT, LDD = G::LDD, LDC = G::LDC, LDV = G::LDV;
-    constexpr int nTC = G::nTC, nTD = G::nTD, nTV = G::nTV;
-    __shared__ Hla2FwdSmem<T, D, DV, C, DECAY, NW> sm;
+template <typename T, int D, int DV, int C, bool DECAY>
+__global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
+                             (hla2_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, 0, D, DV>()))
+void hla2_forward_kernel(FwdParams p) {
+    using G = Hla2Cfg<T, D, DV, C, DECAY>;
+    constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
+    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    __shared__ Hla2FwdSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
+    const int r = w / NCG, cg = w % NCG;
+    const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    const int tau = 16 * r + col;          // the lane's token within the chunk
     const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
@@ -156,12 +164,9 @@ __global__ __launch_bounds__(NW * kWave) void hla2_forward_kernel(FwdParams p) {
         if (t < G::TS) {
             const int ti = t / nTD, tj = t % nTD;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                const float x = S0 ? S0[row * D + col] : 0.f;
-                accS[s][r] = x;
-                sm.St[col * LDD + row] = from_f<T>(x);
-            }
+            for (int i = 0; i < 4; ++i)
+                accS[s][i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
+            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
         }
     }
 #pragma unroll
@@ -169,129 +174,108 @@ __global__ __launch_bounds__(NW * kWave) void hla2_forward_kernel(FwdParams p) {
         const int t = w + s * NW;
         accW[s] = zero4();
         if (t < G::TW) {
-            const int ti = t / nTV, tj = t % nTV;
+            const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                const float x = W0 ? W0[row * DV + col] : 0.f;
-                accW[s][r] = x;
-                sm.Wt[col * LDD + row] = from_f<T>(x);
-            }
+            for (int i = 0; i < 4; ++i)
+                accW[s][i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
+            store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[s]);
         }
     }
-    for (int i = threadIdx.x; i < D; i += NT) sm.u[i] = u0 ? u0[i] : 0.f;
+    for (int i = threadIdx.x; i < D; i += NT) sm.u0[i] = u0 ? u0[i] : 0.f;
 
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-        const int cv = min(C, t_end - c0);
-        __syncthreads();  // previous chunk's output staging has been stored; gp ready
-        // ---- a-1: stage Q, K (row-major, transposed, decay-weighted) and V^T
-        stage_tile<T, C, D, NT>(q + (size_t)c0 * D, cv, sm.Q, LDD, nullptr, 0);
-        if (DECAY) {
-            // weights g^(cv-1-tau) for the S0 update
-            const int VE = Vec16<T>::N;
-            for (int idx = threadIdx.x; idx < C * (D / VE); idx += NT) {
-                const int r = idx / (D / VE), c = (idx % (D / VE)) * VE;
-                Vec16<T> x;
-                if (r < cv) x = load16(k + (size_t)(c0 + r) * D + c);
-                else {
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(0.f);
-                }
-                store16(sm.K + r * LDD + c, x);
-                const float wr = (r < cv) ? sm.gp[cv - 1 - r] : 0.f;
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    sm.Kt[(c + e) * LDC + r] = x.v[e];
-                    sm.Ktw[(c + e) * LDC + r] = from_f<T>(to_f(x.v[e]) * wr);
-                }
-            }
-        } else {
-            stage_tile<T, C, D, NT>(k + (size_t)c0 * D, cv, sm.K, LDD, sm.Kt, LDC);
+    ChunkRegs<T, C, D, NT> rq, rk;
+    ChunkRegs<T, C, DV, NT> rv;
+    int c0 = t_begin;
+    int cv = min(C, t_end - c0);
+    rq.load(q + (size_t)c0 * D, cv);
+    rk.load(k + (size_t)c0 * D, cv);
+    rv.load(v + (size_t)c0 * DV, cv);
+
+    while (c0 < t_end) {
+        __syncthreads();   // previous chunk's readers are done; setup is visible
+        // ---- a-1: stage this chunk, then start loading the next one
+        rq.store_rows(sm.Q, LDD);
+        rk.store_rows(sm.K, LDD);
+        rk.store_cols(sm.Kt, LDC);
+        if (DECAY) rk.store_cols_w(sm.Ktw, LDC, sm.gp, cv - 1);
+        rv.store_cols(sm.Vt, LDC);
+        const int n0 = c0 + C;
+        const int ncv = min(C, t_end - n0);
+        if (n0 < t_end) {
+            rq.load(q + (size_t)n0 * D, ncv);
+            rk.load(k + (size_t)n0 * D, ncv);
+            rv.load(v + (size_t)n0 * DV, ncv);
         }
-        stage_tile<T, C, DV, NT>(v + (size_t)c0 * DV, cv, nullptr, 0, sm.Vt, LDC);
         __syncthreads();
 
-        // ---- a-2: scores; a-3/a-4 carried-state terms Q S0, Q W0 (and Q u0)
-        scores_tril<T, D, C, DECAY, NW, LDD, LDC>(sm.Q, sm.K, sm.L, sm.gp);
-        f32x4 accZ[G::PZ], accO[G::PO];
+        const T *Qr = sm.Q + 16 * r * LDD;
+        // ---- a-2: L^T for this row tile, as operand fragments
+        Frag16<T> Lf[RT];
+        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, Qr, r, tau, sm.gp, 1);
+
+        // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
+        const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
 #pragma unroll
-        for (int s = 0; s < G::PZ; ++s) {
-            const int t = w + s * NW;
-            accZ[s] = zero4();
-            if (t < G::TZ) {
-                const int ti = t / nTD, tj = t % nTD;
-                accZ[s] = mma_nt(accZ[s], sm.Q + ti * 16 * LDD, LDD, sm.St + tj * 16 * LDD, LDD, 0, D);
+        for (int jj = 0; jj < G::ZJ; ++jj) {
+            const int jt = cg + jj * NCG;
+            if (jt < nTD) {
+                f32x4 z = mma_nt(zero4(), sm.St + 16 * jt * LDD, LDD, Qr, LDD, 0, D);
+                f32x4 zc = zero4();
+#pragma unroll
+                for (int s = 0; s < RT; ++s)
+                    if (s <= r) zc = mma16(zc, ld_frag(sm.Kt + 16 * jt * LDC + 16 * s, LDC), Lf[s]);
+                z = (DECAY ? z * sm.gp[tau + 1] : z) + zc;
+                store4(sm.Z + tau * LDD + 16 * jt + g4, z);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sm.Ztw[(16 * jt + g4 + i) * LDC + tau] = from_f<T>(z[i] * wz);
             }
         }
+        // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T, den = that for u0
+        f32x4 accO[G::OJ];
 #pragma unroll
-        for (int s = 0; s < G::PO; ++s) {
-            const int t = w + s * NW;
-            accO[s] = zero4();
-            if (t < G::TO) {
-                const int ti = t / nTV, tj = t % nTV;
-                accO[s] = mma_nt(accO[s], sm.Q + ti * 16 * LDD, LDD, sm.Wt + tj * 16 * LDD, LDD, 0, D);
+        for (int jj = 0; jj < G::OJ; ++jj) {
+            const int jv = cg + jj * NCG;
+            accO[jj] = zero4();
+            if (jv < nTV) {
+                accO[jj] = mma_nt(zero4(), sm.Wt + 16 * jv * LDD, LDD, Qr, LDD, 0, D);
+                if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
             }
         }
+        float den = 0.f;
         if (p.ratio) {
-            for (int i = threadIdx.x; i < C; i += NT) {
-                float s = 0.f;
-                for (int a = 0; a < D; ++a) s += to_f(sm.Q[i * LDD + a]) * sm.u[a];
-                sm.den[i] = DECAY ? s * sm.gp[2 * (i + 1)] : s;
-            }
+            den = lane_dot<T, D>(sm.Q + tau * LDD, sm.u0);
+            if (DECAY) den *= sm.gp[2 * (tau + 1)];
         }
         __syncthreads();
 
-        // ---- a-3: Z = diag(g^(tau+1)) Q S0 + L K
+        // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
+        Frag16<T> Pf[RT];
+        scores_t<T, D, RT, LDD, DECAY>(Pf, sm.Z, Qr, r, tau, sm.gp, 2);
+        if (p.ratio) {
+            float rs = 0.f;
 #pragma unroll
-        for (int s = 0; s < G::PZ; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TZ) {
-                const int ti = t / nTD, tj = t % nTD;
-                if (DECAY) {
+            for (int s = 0; s < RT; ++s)
+                if (s <= r) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) accZ[s][r] *= sm.gp[ti * 16 + acc_row(r) + 1];
+                    for (int i = 0; i < 4; ++i) rs += frag_val(Pf[s], i);
                 }
-                accZ[s] = mma_nt(accZ[s], sm.L + ti * 16 * LDC, LDC, sm.Kt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
+            den += sum_groups(rs);
+        }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                    const float z = accZ[s][r];
-                    sm.Z[row * LDD + col] = from_f<T>(z);
-                    float wz = 0.f;
-                    if (row < cv) wz = DECAY ? sm.gp[2 * (cv - 1 - row)] : 1.f;
-                    sm.Ztw[col * LDC + row] = from_f<T>(z * wz);
-                }
+        for (int jj = 0; jj < G::OJ; ++jj) {
+            const int jv = cg + jj * NCG;
+            if (jv < nTV) {
+                f32x4 oc = zero4();
+#pragma unroll
+                for (int s = 0; s < RT; ++s)
+                    if (s <= r) oc = mma16(oc, ld_frag(sm.Vt + 16 * jv * LDC + 16 * s, LDC), Pf[s]);
+                f32x4 ov = accO[jj] + oc;
+                if (p.ratio) ov *= 1.f / den;
+                if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
             }
         }
-        __syncthreads();
 
-        // ---- a-4: P = D_{g^2} * tril(Q Z^T) (+ row sums for the ratio form)
-        {
-            int t = 0;
-            for (int ti = 0; ti < nTC; ++ti) {
-                for (int tj = 0; tj <= ti; ++tj, ++t) {
-                    if (t % NW != w) continue;
-                    f32x4 a = mma_nt(zero4(), sm.Q + ti * 16 * LDD, LDD, sm.Z + tj * 16 * LDD, LDD, 0, D);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                        float val = 0.f;
-                        if (col <= row) val = DECAY ? a[r] * sm.gp[2 * (row - col)] : a[r];
-                        const T tv = from_f<T>(val);
-                        sm.P[row * LDC + col] = tv;
-                        if (p.ratio) {
-                            float rs = to_f(tv);
-                            rs += __shfl_xor(rs, 1, 16);
-                            rs += __shfl_xor(rs, 2, 16);
-                            rs += __shfl_xor(rs, 4, 16);
-                            rs += __shfl_xor(rs, 8, 16);
-                            if (acc_col() == 0) sm.denp[row][tj] = rs;
-                        }
-                    }
-                }
-            }
-        }
         // ---- a-7: advance the carried state by this chunk
         const float gc = DECAY ? sm.gp[cv] : 1.f;
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
@@ -302,66 +286,24 @@ __global__ __launch_bounds__(NW * kWave) void hla2_forward_kernel(FwdParams p) {
             if (t < G::TS) {
                 const int ti = t / nTD, tj = t % nTD;
                 if (DECAY) accS[s] *= gc;
-                accS[s] = mma_nt(accS[s], KA + ti * 16 * LDC, LDC, sm.Kt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.St[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accS[s][r]);
+                accS[s] = mma_nt(accS[s], KA + 16 * ti * LDC, LDC, sm.Kt + 16 * tj * LDC, LDC, 0, C);
+                store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
             }
         }
 #pragma unroll
         for (int s = 0; s < G::PW; ++s) {
             const int t = w + s * NW;
             if (t < G::TW) {
-                const int ti = t / nTV, tj = t % nTV;
+                const int ti = t / nTV, tv = t % nTV;
                 if (DECAY) accW[s] *= gc2;
-                accW[s] = mma_nt(accW[s], sm.Ztw + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.Wt[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accW[s][r]);
+                accW[s] = mma_nt(accW[s], sm.Ztw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
+                store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[s]);
             }
         }
-        for (int i = threadIdx.x; i < D; i += NT) {
-            float s = 0.f;
-            for (int c = 0; c < C; ++c) s += to_f(sm.Ztw[i * LDC + c]);
-            sm.u[i] = gc2 * sm.u[i] + s;
-        }
-        __syncthreads();
-
-        // ---- a-4: O = diag(g^(2(tau+1))) Q W0 + P V  (/ den)
-        T *Os = sm.K;
-#pragma unroll
-        for (int s = 0; s < G::PO; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TO) {
-                const int ti = t / nTV, tj = t % nTV;
-                if (DECAY) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) accO[s][r] *= sm.gp[2 * (ti * 16 + acc_row(r) + 1)];
-                }
-                accO[s] = mma_nt(accO[s], sm.P + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                    float ov = accO[s][r];
-                    if (p.ratio) {
-                        float den = sm.den[row];
-                        for (int c = 0; c <= ti; ++c) den += sm.denp[row][c];
-                        ov = ov / den;
-                    }
-                    Os[row * LDV + col] = from_f<T>(ov);
-                }
-            }
-        }
-        __syncthreads();
-        {
-            constexpr int VE = Vec16<T>::N;
-            constexpr int VPR = DV / VE;
-            for (int idx = threadIdx.x; idx < cv * VPR; idx += NT) {
-                const int r = idx / VPR, c = (idx % VPR) * VE;
-                store16(o + (size_t)(c0 + r) * DV + c, load16(Os + r * LDV + c));
-            }
-        }
+        for (int i = threadIdx.x; i < D; i += NT)
+            sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
+        c0 = n0;
+        cv = ncv;
     }
 
     if (p.state_out && seg == p.nseg - 1) {
@@ -372,36 +314,40 @@ __global__ __launch_bounds__(NW * kWave) void hla2_forward_kernel(FwdParams p) {
             if (t < G::TS) {
                 const int ti = t / nTD, tj = t % nTD;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    so[(ti * 16 + acc_row(r)) * D + tj * 16 + acc_col()] = accS[s][r];
+                for (int i = 0; i < 4; ++i) so[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[s][i];
             }
         }
 #pragma unroll
         for (int s = 0; s < G::PW; ++s) {
             const int t = w + s * NW;
             if (t < G::TW) {
-                const int ti = t / nTV, tj = t % nTV;
+                const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    so[D * D + (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col()] = accW[s][r];
+                for (int i = 0; i < 4; ++i)
+                    so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = accW[s][i];
             }
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < D; i += NT) so[D * D + D * DV + i] = sm.u[i];
+        for (int i = threadIdx.x; i < D; i += NT) so[D * D + D * DV + i] = sm.u0[i];
     }
 }
 
 // ------------------------------------------------------------ summary kernel
 
-template <typename T, int D, int DV, int C, bool DECAY, int NW>
-__global__ __launch_bounds__(NW * kWave) void hla2_summary_kernel(FwdParams p) {
-    using G = Hla2Cfg<T, D, DV, C, DECAY, NW>;
-    constexpr int NT = G::NT, LDD = G::LDD, LDC = G::LDC;
-    constexpr int nTD = G::nTD, nTV = G::nTV;
-    __shared__ Hla2SumSmem<T, D, DV, C, DECAY, NW> sm;
+template <typename T, int D, int DV, int C, bool DECAY>
+__global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
+                             (hla2_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, 0, D, DV>()))
+void hla2_summary_kernel(FwdParams p) {
+    using G = Hla2Cfg<T, D, DV, C, DECAY>;
+    constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
+    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    __shared__ Hla2SumSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
+    const int r = w / NCG, cg = w % NCG;
+    const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    const int tau = 16 * r + col;
     const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
@@ -414,70 +360,59 @@ __global__ __launch_bounds__(NW * kWave) void hla2_summary_kernel(FwdParams p) {
 #pragma unroll
     for (int s = 0; s < G::PS; ++s) accS[s] = zero4();
 #pragma unroll
-    for (int s = 0; s < G::PW; ++s) { accW[s] = zero4(); accC[s] = zero4(); }
+    for (int s = 0; s < G::PW; ++s) {
+        accW[s] = zero4();
+        accC[s] = zero4();
+    }
     for (int i = threadIdx.x; i < D * LDD; i += NT) sm.St[i] = from_f<T>(0.f);
-    for (int i = threadIdx.x; i < D; i += NT) { sm.u[i] = 0.f; sm.m[i] = 0.f; }
+    for (int i = threadIdx.x; i < D; i += NT) {
+        sm.u0[i] = 0.f;
+        sm.m0[i] = 0.f;
+    }
 
-    for (int c0 = t_begin; c0 < t_end; c0 += C) {
-        const int cv = min(C, t_end - c0);
-        __syncthreads();
-        {
-            constexpr int VE = Vec16<T>::N;
-            for (int idx = threadIdx.x; idx < C * (D / VE); idx += NT) {
-                const int r = idx / (D / VE), c = (idx % (D / VE)) * VE;
-                Vec16<T> xq, xk;
-                if (r < cv) {
-                    xq = load16(q + (size_t)(c0 + r) * D + c);
-                    xk = load16(k + (size_t)(c0 + r) * D + c);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) { xq.v[e] = from_f<T>(0.f); xk.v[e] = from_f<T>(0.f); }
-                }
-                store16(sm.Q + r * LDD + c, xq);
-                store16(sm.K + r * LDD + c, xk);
-                const float wr = (r < cv) ? (DECAY ? sm.gp[cv - 1 - r] : 1.f) : 0.f;
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    sm.Qtw[(c + e) * LDC + r] = DECAY ? from_f<T>(to_f(xq.v[e]) * wr) : xq.v[e];
-                    sm.Kt[(c + e) * LDC + r] = xk.v[e];
-                    if (DECAY) sm.Ktw[(c + e) * LDC + r] = from_f<T>(to_f(xk.v[e]) * wr);
-                }
-            }
-        }
-        stage_tile<T, C, DV, NT>(v + (size_t)c0 * DV, cv, nullptr, 0, sm.Vt, LDC);
-        __syncthreads();
+    ChunkRegs<T, C, D, NT> rq, rk;
+    ChunkRegs<T, C, DV, NT> rv;
+    int c0 = t_begin;
+    int cv = min(C, t_end - c0);
+    rq.load(q + (size_t)c0 * D, cv);
+    rk.load(k + (size_t)c0 * D, cv);
+    rv.load(v + (size_t)c0 * DV, cv);
 
-        scores_tril<T, D, C, DECAY, NW, LDD, LDC>(sm.Q, sm.K, sm.L, sm.gp);
-        f32x4 accZ[G::PZ];
-#pragma unroll
-        for (int s = 0; s < G::PZ; ++s) {
-            const int t = w + s * NW;
-            accZ[s] = zero4();
-            if (t < G::TZ) {
-                const int ti = t / nTD, tj = t % nTD;
-                accZ[s] = mma_nt(accZ[s], sm.Q + ti * 16 * LDD, LDD, sm.St + tj * 16 * LDD, LDD, 0, D);
-            }
+    while (c0 < t_end) {
+        __syncthreads();
+        rq.store_rows(sm.Q, LDD);
+        if (DECAY) rq.store_cols_w(sm.Qtw, LDC, sm.gp, cv - 1);
+        else rq.store_cols(sm.Qtw, LDC);
+        rk.store_rows(sm.K, LDD);
+        rk.store_cols(sm.Kt, LDC);
+        if (DECAY) rk.store_cols_w(sm.Ktw, LDC, sm.gp, cv - 1);
+        rv.store_cols(sm.Vt, LDC);
+        const int n0 = c0 + C;
+        const int ncv = min(C, t_end - n0);
+        if (n0 < t_end) {
+            rq.load(q + (size_t)n0 * D, ncv);
+            rk.load(k + (size_t)n0 * D, ncv);
+            rv.load(v + (size_t)n0 * DV, ncv);
         }
         __syncthreads();
 
+        const T *Qr = sm.Q + 16 * r * LDD;
+        Frag16<T> Lf[RT];
+        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, Qr, r, tau, sm.gp, 1);
+        const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
 #pragma unroll
-        for (int s = 0; s < G::PZ; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TZ) {
-                const int ti = t / nTD, tj = t % nTD;
-                if (DECAY) {
+        for (int jj = 0; jj < G::ZJ; ++jj) {
+            const int jt = cg + jj * NCG;
+            if (jt < nTD) {
+                f32x4 z = mma_nt(zero4(), sm.St + 16 * jt * LDD, LDD, Qr, LDD, 0, D);
+                f32x4 zc = zero4();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) accZ[s][r] *= sm.gp[ti * 16 + acc_row(r) + 1];
-                }
-                accZ[s] = mma_nt(accZ[s], sm.L + ti * 16 * LDC, LDC, sm.Kt + tj * 16 * LDC, LDC, 0,
-                                 (ti + 1) * 16);
+                for (int s = 0; s < RT; ++s)
+                    if (s <= r) zc = mma16(zc, ld_frag(sm.Kt + 16 * jt * LDC + 16 * s, LDC), Lf[s]);
+                z = (DECAY ? z * sm.gp[tau + 1] : z) + zc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = ti * 16 + acc_row(r), col = tj * 16 + acc_col();
-                    float wz = 0.f;
-                    if (row < cv) wz = DECAY ? sm.gp[2 * (cv - 1 - row)] : 1.f;
-                    sm.Ztw[col * LDC + row] = from_f<T>(accZ[s][r] * wz);
-                }
+                for (int i = 0; i < 4; ++i)
+                    sm.Ztw[(16 * jt + g4 + i) * LDC + tau] = from_f<T>(z[i] * wz);
             }
         }
         __syncthreads();
@@ -491,31 +426,29 @@ __global__ __launch_bounds__(NW * kWave) void hla2_summary_kernel(FwdParams p) {
             if (t < G::TS) {
                 const int ti = t / nTD, tj = t % nTD;
                 if (DECAY) accS[s] *= gc;
-                accS[s] = mma_nt(accS[s], KA + ti * 16 * LDC, LDC, sm.Kt + tj * 16 * LDC, LDC, 0, C);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.St[(tj * 16 + acc_col()) * LDD + ti * 16 + acc_row(r)] = from_f<T>(accS[s][r]);
+                accS[s] = mma_nt(accS[s], KA + 16 * ti * LDC, LDC, sm.Kt + 16 * tj * LDC, LDC, 0, C);
+                store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
             }
         }
 #pragma unroll
         for (int s = 0; s < G::PW; ++s) {
             const int t = w + s * NW;
             if (t < G::TW) {
-                const int ti = t / nTV, tj = t % nTV;
-                if (DECAY) { accW[s] *= gc2; accC[s] *= gc; }
-                accW[s] = mma_nt(accW[s], sm.Ztw + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0, C);
-                accC[s] = mma_nt(accC[s], sm.Qtw + ti * 16 * LDC, LDC, sm.Vt + tj * 16 * LDC, LDC, 0, C);
+                const int ti = t / nTV, tv = t % nTV;
+                if (DECAY) {
+                    accW[s] *= gc2;
+                    accC[s] *= gc;
+                }
+                accW[s] = mma_nt(accW[s], sm.Ztw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
+                accC[s] = mma_nt(accC[s], sm.Qtw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
             }
         }
         for (int i = threadIdx.x; i < D; i += NT) {
-            float su = 0.f, sq = 0.f;
-            for (int c = 0; c < C; ++c) {
-                su += to_f(sm.Ztw[i * LDC + c]);
-                sq += to_f(sm.Qtw[i * LDC + c]);
-            }
-            sm.u[i] = gc2 * sm.u[i] + su;
-            sm.m[i] = gc * sm.m[i] + sq;
+            sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
+            sm.m0[i] = gc * sm.m0[i] + row_sum<T, C>(sm.Qtw, LDC, i);
         }
+        c0 = n0;
+        cv = ncv;
     }
     __syncthreads();
 
@@ -527,26 +460,25 @@ __global__ __launch_bounds__(NW * kWave) void hla2_summary_kernel(FwdParams p) {
         if (t < G::TS) {
             const int ti = t / nTD, tj = t % nTD;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                e[(ti * 16 + acc_row(r)) * D + tj * 16 + acc_col()] = accS[s][r];
+            for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[s][i];
         }
     }
 #pragma unroll
     for (int s = 0; s < G::PW; ++s) {
         const int t = w + s * NW;
         if (t < G::TW) {
-            const int ti = t / nTV, tj = t % nTV;
+            const int ti = t / nTV, tv = t % nTV;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                e[D * D + idx] = accC[s][r];
-                e[D * D + D * DV + idx] = accW[s][r];
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                e[D * D + idx] = accC[s][i];
+                e[D * D + D * DV + idx] = accW[s][i];
             }
         }
     }
     for (int i = threadIdx.x; i < D; i += NT) {
-        e[D * D + 2 * D * DV + i] = sm.m[i];
-        e[D * D + 2 * D * DV + D + i] = sm.u[i];
+        e[D * D + 2 * D * DV + i] = sm.m0[i];
+        e[D * D + 2 * D * DV + D + i] = sm.u0[i];
     }
 }
 

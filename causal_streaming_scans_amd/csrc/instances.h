@@ -11,58 +11,51 @@ namespace hla {
 
 constexpr size_t kLdsBytes = 160 * 1024;   // gfx950 LDS per workgroup
 
-template <typename T> constexpr int default_waves(int D) { return 4; }
-
 template <typename T, int D, int C, bool DECAY>
 constexpr bool hla2_fits() {
-    constexpr int NW = default_waves<T>(D);
-    return sizeof(Hla2FwdSmem<T, D, D, C, DECAY, NW>) <= kLdsBytes &&
-           sizeof(Hla2SumSmem<T, D, D, C, DECAY, NW>) <= kLdsBytes;
+    return sizeof(Hla2FwdSmem<T, D, D, C, DECAY>) <= kLdsBytes &&
+           sizeof(Hla2SumSmem<T, D, D, C, DECAY>) <= kLdsBytes;
 }
 
 template <typename T, int D, int C>
 constexpr bool ahla_fits() {
-    constexpr int NW = default_waves<T>(D);
-    return sizeof(AhlaFwdSmem<T, D, D, C, NW>) <= kLdsBytes &&
-           sizeof(AhlaSumSmem<T, D, D, C, NW>) <= kLdsBytes;
+    return sizeof(AhlaFwdSmem<T, D, D, C>) <= kLdsBytes &&
+           sizeof(AhlaSumSmem<T, D, D, C>) <= kLdsBytes;
 }
 
 template <typename T, int D, int C, bool DECAY>
 hipError_t launch_hla2_summary(const FwdParams &p, hipStream_t s) {
-    constexpr int NW = default_waves<T>(D);
-    hipLaunchKernelGGL((hla2_summary_kernel<T, D, D, C, DECAY, NW>), dim3(p.nseg - 1, p.BH),
-                       dim3(NW * kWave), 0, s, p);
+    hipLaunchKernelGGL((hla2_summary_kernel<T, D, D, C, DECAY>), dim3(p.nseg - 1, p.BH),
+                       dim3(Hla2Cfg<T, D, D, C, DECAY>::NT), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, int C, bool DECAY>
 hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
-    constexpr int NW = default_waves<T>(D);
-    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY, NW>), dim3(p.nseg, p.BH),
-                       dim3(NW * kWave), 0, s, p);
+    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg, p.BH),
+                       dim3(Hla2Cfg<T, D, D, C, DECAY>::NT), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, int C>
 hipError_t launch_ahla_summary(const FwdParams &p, hipStream_t s) {
-    constexpr int NW = default_waves<T>(D);
-    hipLaunchKernelGGL((ahla_summary_kernel<T, D, D, C, NW>), dim3(p.nseg - 1, p.BH),
-                       dim3(NW * kWave), 0, s, p);
+    hipLaunchKernelGGL((ahla_summary_kernel<T, D, D, C>), dim3(p.nseg - 1, p.BH),
+                       dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, int C>
 hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
-    constexpr int NW = default_waves<T>(D);
-    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C, NW>), dim3(p.nseg, p.BH),
-                       dim3(NW * kWave), 0, s, p);
+    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C>), dim3(p.nseg, p.BH),
+                       dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, bool HLA2>
 hipError_t launch_scan(const FwdParams &p, hipStream_t s) {
     constexpr bool F32 = sizeof(T) == 4;
-    hipLaunchKernelGGL((scan_kernel<F32, D, D, HLA2, 8>), dim3(p.BH), dim3(8 * kWave), 0, s, p);
+    hipLaunchKernelGGL((scan_kernel<F32, D, D, HLA2>), dim3(p.BH), dim3(ScanCfg<F32, D, D>::NT), 0,
+                       s, p);
     return hipGetLastError();
 }
 

@@ -16,13 +16,18 @@
 //          N = N_A + N_B + X_B Y_A,        nv = nv_A + nv_B + X_B y_A
 // The identity is the zero summary.
 //
-// One workgroup per (b,h).  The up-sweep combines in place in the "e" array;
-// the down-sweep writes the exclusive prefixes into the separate "p" array
-// (p[left] <- p[right]; p[right] <- p[right] (+) e[left]).  The up-sweep
-// skips every combine that only feeds the total (the pairs ending at the last
-// slot), since an exclusive scan discards it.  Finally the caller's initial
-// state, if any, is folded in front of every prefix.  All pairs of one tree
-// level run concurrently across the waves.
+// One workgroup per (b,h).  The up-sweep combines in place in the "e" array
+// (e[i] <- e[i-s] (+) e[i]); the down-sweep writes the exclusive prefixes
+// into the separate "p" array (p[i-s] <- p[i]; p[i] <- p[i] (+) e[i-s]).  The
+// up-sweep skips every combine that only feeds the total (the pairs ending at
+// the last slot), since an exclusive scan discards it.  Finally the caller's
+// initial state, if any, is folded in front of every prefix.
+//
+// Each tree level runs in batches of pairs.  A batch first stages the two
+// factors of every pair's cross term in LDS with coalesced vector loads (one
+// round trip to memory), then one phase forms the cross terms on MFMA and
+// updates every part of every pair, each element owned by one thread, so all
+// of a phase's global reads are independent of each other.
 #pragma once
 
 #include "device_common.h"
@@ -30,28 +35,58 @@
 
 namespace hla {
 
-// acc = Xc[ti*16 .. +16][0:K] * Yc[0:K][tj*16 .. +16], fp32 operands read from
-// global memory.  F32: exact fp32 MFMA.  Otherwise each operand is split into
-// bf16 hi + lo parts and the product is hi*hi + hi*lo + lo*hi (relative error
-// about 2^-16 per product, far below the bf16 path's own rounding).
-template <bool F32, int K>
-__device__ __forceinline__ f32x4 cross_tile(const float *Xc, int ldx, const float *Yc, int ldy,
-                                            int ti, int tj) {
+template <int D, int DV>
+struct SumOfs {
+    static constexpr int X = 0, Y = D * D, N = D * D + D * DV, y = D * D + 2 * D * DV,
+                         nv = D * D + 2 * D * DV + D;
+};
+
+// Parts of one combine operand; a null part reads as zero.
+struct ScanOp {
+    const float *X, *Y, *N, *y, *nv;
+};
+
+__device__ __forceinline__ ScanOp scan_op(const float *base, int D, int DV) {
+    return ScanOp{base, base + D * D, base + D * D + D * DV, base + D * D + 2 * D * DV,
+                  base + D * D + 2 * D * DV + D};
+}
+
+__device__ __forceinline__ float rd(const float *p, int i) { return p ? p[i] : 0.f; }
+
+// One combine of a batch: dst = A (+) B; if copy != null it also receives A
+// (the down-sweep's left child).  The factor a = g^(length of B) comes from a
+// separate functor, evaluated once per pair.
+struct ScanPair {
+    ScanOp A, B;
+    float *dst;
+    float *copy;
+};
+
+template <bool F32, int D, int DV>
+struct ScanCfg {
+    static constexpr int NT = 512, NW = NT / kWave;
+    static constexpr int LDX = D + 4, LDY = DV + 4;     // fp32 rows, 16-byte aligned
+    static constexpr int PAIR_FLOATS = D * LDX + D * LDY + D;
+    static constexpr int PB0 = (150 * 1024) / (PAIR_FLOATS * 4);
+    static constexpr int PB = PB0 < 1 ? 1 : (PB0 > 8 ? 8 : PB0);   // pairs per batch
+};
+
+// 16x16 cross-term tile from LDS: Xs rows ti*16.., Ys columns tj*16..
+template <bool F32, int D, int LDX, int LDY>
+__device__ __forceinline__ f32x4 cross_tile_lds(const float *Xs, const float *Ys, int ti, int tj) {
     const int l = lane_id();
     const int r = l & 15, gq = l >> 4;
     f32x4 acc = zero4();
+    const float *a = Xs + (ti * 16 + r) * LDX;
+    const float *b = Ys + tj * 16 + r;
     if constexpr (F32) {
-        const float *a = Xc + (ti * 16 + r) * ldx + gq;
-        const float *b = Yc + gq * ldy + tj * 16 + r;
 #pragma unroll 4
-        for (int k = 0; k < K; k += 4)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k * ldy], acc, 0, 0, 0);
-    } else {
-        const float *a = Xc + (ti * 16 + r) * ldx;
-        const float *b = Yc + tj * 16 + r;
-        int k = 0;
+        for (int k = 0; k < D; k += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k + gq], b[(k + gq) * LDY], acc, 0, 0, 0);
+    } else if constexpr (D % 32 == 0) {
+        // bf16 hi/lo split: hi*hi + hi*lo + lo*hi, one instruction shape
 #pragma unroll
-        for (; k + 32 <= K; k += 32) {
+        for (int k = 0; k < D; k += 32) {
             bf16x8 ah, al, bh, bl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -59,7 +94,7 @@ __device__ __forceinline__ f32x4 cross_tile(const float *Xc, int ldx, const floa
                 const bf16 xh = (bf16)x;
                 ah[e] = xh;
                 al[e] = (bf16)(x - (float)xh);
-                const float y = b[(k + gq * 8 + e) * ldy];
+                const float y = b[(k + gq * 8 + e) * LDY];
                 const bf16 yh = (bf16)y;
                 bh[e] = yh;
                 bl[e] = (bf16)(y - (float)yh);
@@ -68,7 +103,9 @@ __device__ __forceinline__ f32x4 cross_tile(const float *Xc, int ldx, const floa
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
         }
-        if constexpr (K % 32 == 16) {
+    } else {
+#pragma unroll
+        for (int k = 0; k < D; k += 16) {
             union { bf16 h[4]; i16x4 v; } ah, al, bh, bl;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -76,7 +113,7 @@ __device__ __forceinline__ f32x4 cross_tile(const float *Xc, int ldx, const floa
                 const bf16 xh = (bf16)x;
                 ah.h[e] = xh;
                 al.h[e] = (bf16)(x - (float)xh);
-                const float y = b[(k + gq * 4 + e) * ldy];
+                const float y = b[(k + gq * 4 + e) * LDY];
                 const bf16 yh = (bf16)y;
                 bh.h[e] = yh;
                 bl.h[e] = (bf16)(y - (float)yh);
@@ -89,77 +126,143 @@ __device__ __forceinline__ f32x4 cross_tile(const float *Xc, int ldx, const floa
     return acc;
 }
 
-template <int D, int DV>
-struct SumOfs {
-    static constexpr int X = 0, Y = D * D, N = D * D + D * DV, y = D * D + 2 * D * DV,
-                         nv = D * D + 2 * D * DV + D;
-};
-
-// dst.N = a2 * A.N + B.N + a * Xc Yc ;  dst.nv = a2 * A.nv + B.nv + a * Xc yc
-// for `npair` pairs given by pair(j, &A, &B, &dst, &a).  Xc, Yc, yc come from
-// B / A as the variant says.  Waves take (pair, 16-row slab) items; threads
-// take (pair, row) items of nv.  dst may equal B (each element is read and
-// written by one owner) but A and B are not written.
-template <bool F32, int D, int DV, bool HLA2, int NW, typename PairFn>
-__device__ __forceinline__ void cross_phase(int npair, PairFn pair) {
-    using O = SumOfs<D, DV>;
-    constexpr int NT = NW * kWave, nTD = D / 16, nTV = DV / 16;
-    const int w = wave_id();
-    for (int it = w; it < npair * nTD; it += NW) {
-        const int j = it / nTD, ti = it % nTD;
-        const float *A, *B;
-        float *Dst;
-        float a;
-        pair(j, A, B, Dst, a);
-        const float *Xc = HLA2 ? A + O::X : B + O::X;
-        const float *Yc = HLA2 ? B + O::Y : A + O::Y;
-        const float a2 = a * a;
-        for (int tj = 0; tj < nTV; ++tj) {
-            const f32x4 c = cross_tile<F32, D>(Xc, D, Yc, DV, ti, tj);
+// dst[0:len) = a * pa + pb (when upd) and copy[0:len) = pa, as float4
+// vectors; every thread issues all of its loads before any of its stores.
+// len is a multiple of 4; null pa / pb read as zero.
+template <int NT, int U>
+__device__ __forceinline__ void lin_part(float *__restrict__ dst, float *__restrict__ copy,
+                                         const float *pa, const float *pb, int len, float a,
+                                         bool upd) {
+    const int nv4 = len / 4;
+    for (int v0 = threadIdx.x; v0 < nv4; v0 += NT * U) {
+        f32x4 xa[U], xb[U];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                Dst[O::N + idx] = a2 * A[O::N + idx] + B[O::N + idx] + a * c[r];
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * NT;
+            xa[u] = (v < nv4 && pa) ? reinterpret_cast<const f32x4 *>(pa)[v] : zero4();
+            xb[u] = (v < nv4 && pb) ? reinterpret_cast<const f32x4 *>(pb)[v] : zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int v = v0 + u * NT;
+            if (v < nv4) {
+                if (upd) reinterpret_cast<f32x4 *>(dst)[v] = a * xa[u] + xb[u];
+                if (copy) reinterpret_cast<f32x4 *>(copy)[v] = xa[u];
             }
         }
     }
-    for (int it = threadIdx.x; it < npair * D; it += NT) {
-        const int j = it / D, row = it % D;
-        const float *A, *B;
-        float *Dst;
-        float a;
-        pair(j, A, B, Dst, a);
-        const float *Xc = HLA2 ? A + O::X : B + O::X;
-        const float *yc = HLA2 ? B + O::y : A + O::y;
-        float s = 0.f;
-        for (int c = 0; c < D; ++c) s += Xc[row * D + c] * yc[c];
-        Dst[O::nv + row] = a * a * A[O::nv + row] + B[O::nv + row] + a * s;
+}
+
+// Run `npair` combines (pair(j) -> ScanPair, afac(j) -> a) in batches.
+// updX/updY: whether X and (Y, y) of dst are written (N and nv always are).
+template <bool F32, int D, int DV, bool HLA2, typename PairFn, typename AFn>
+__device__ __forceinline__ void scan_level(float *smem, float *sa, int npair, PairFn pair,
+                                           AFn afac, bool updX, bool updY) {
+    using G = ScanCfg<F32, D, DV>;
+    using O = SumOfs<D, DV>;
+    constexpr int NT = G::NT, NW = G::NW, LDX = G::LDX, LDY = G::LDY, PB = G::PB;
+    constexpr int nTD = D / 16, nTV = DV / 16;
+    const int w = wave_id();
+    for (int j0 = 0; j0 < npair; j0 += PB) {
+        const int nb = min(PB, npair - j0);
+        // ---- stage the cross-term factors (Xc, Yc, yc) of every pair in the batch
+        for (int b = 0; b < nb; ++b) {
+            const ScanPair pr = pair(j0 + b);
+            const float *Xc = HLA2 ? pr.A.X : pr.B.X;
+            const float *Yc = HLA2 ? pr.B.Y : pr.A.Y;
+            const float *yc = HLA2 ? pr.B.y : pr.A.y;
+            float *Xs = smem + b * G::PAIR_FLOATS;
+            float *Ys = Xs + D * LDX;
+            float *ys = Ys + D * LDY;
+            constexpr int NX4 = D * D / 4, NY4 = D * DV / 4;
+            constexpr int UX = (NX4 + NT - 1) / NT, UY = (NY4 + NT - 1) / NT;
+            f32x4 bx[UX], by[UY];
+#pragma unroll
+            for (int u = 0; u < UX; ++u) {
+                const int idx = threadIdx.x + u * NT;
+                bx[u] = (idx < NX4 && Xc) ? reinterpret_cast<const f32x4 *>(Xc)[idx] : zero4();
+            }
+#pragma unroll
+            for (int u = 0; u < UY; ++u) {
+                const int idx = threadIdx.x + u * NT;
+                by[u] = (idx < NY4 && Yc) ? reinterpret_cast<const f32x4 *>(Yc)[idx] : zero4();
+            }
+            float byv = (threadIdx.x < D) ? rd(yc, threadIdx.x) : 0.f;
+#pragma unroll
+            for (int u = 0; u < UX; ++u) {
+                const int idx = threadIdx.x + u * NT;
+                if (idx < NX4) {
+                    const int rr = idx / (D / 4), c = (idx % (D / 4)) * 4;
+                    *reinterpret_cast<f32x4 *>(Xs + rr * LDX + c) = bx[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UY; ++u) {
+                const int idx = threadIdx.x + u * NT;
+                if (idx < NY4) {
+                    const int rr = idx / (DV / 4), c = (idx % (DV / 4)) * 4;
+                    *reinterpret_cast<f32x4 *>(Ys + rr * LDY + c) = by[u];
+                }
+            }
+            if (threadIdx.x < D) ys[threadIdx.x] = byv;
+            if (threadIdx.x == 0) sa[b] = afac(j0 + b);
+        }
+        __syncthreads();
+        // ---- N = a^2 N_A + N_B + a Xc Yc  (MFMA tiles, one wave per tile)
+        for (int it = w; it < nb * nTD * nTV; it += NW) {
+            const int b = it / (nTD * nTV), t = it % (nTD * nTV);
+            const int ti = t / nTV, tj = t % nTV;
+            const ScanPair pr = pair(j0 + b);
+            float na[4], nbv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (ti * 16 + acc_row(i)) * DV + tj * 16 + acc_col();
+                na[i] = rd(pr.A.N, idx);
+                nbv[i] = rd(pr.B.N, idx);
+            }
+            const float *Xs = smem + b * G::PAIR_FLOATS;
+            const f32x4 c = cross_tile_lds<F32, D, LDX, LDY>(Xs, Xs + D * LDX, ti, tj);
+            const float a = sa[b];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (ti * 16 + acc_row(i)) * DV + tj * 16 + acc_col();
+                pr.dst[O::N + idx] = a * a * na[i] + nbv[i] + a * c[i];
+                if (pr.copy) pr.copy[O::N + idx] = na[i];
+            }
+        }
+        // ---- nv = a^2 nv_A + nv_B + a Xc yc ; the linear parts X, Y, y
+#pragma unroll 1
+        for (int b = 0; b < nb; ++b) {
+            const ScanPair pr = pair(j0 + b);
+            const float a = sa[b];
+            const float *Xs = smem + b * G::PAIR_FLOATS;
+            const float *ys = Xs + D * LDX + D * LDY;
+            for (int row = threadIdx.x; row < D; row += NT) {
+                const float na = rd(pr.A.nv, row), nbv = rd(pr.B.nv, row);
+                float s = 0.f;
+#pragma unroll 8
+                for (int c = 0; c < D; ++c) s += Xs[row * LDX + c] * ys[c];
+                pr.dst[O::nv + row] = a * a * na + nbv + a * s;
+                if (pr.copy) pr.copy[O::nv + row] = na;
+            }
+            lin_part<NT, 4>(pr.dst + O::X, pr.copy ? pr.copy + O::X : nullptr, pr.A.X, pr.B.X,
+                            D * D, a, updX);
+            lin_part<NT, 4>(pr.dst + O::Y, pr.copy ? pr.copy + O::Y : nullptr, pr.A.Y, pr.B.Y,
+                            D * DV, a, updY);
+            lin_part<NT, 1>(pr.dst + O::y, pr.copy ? pr.copy + O::y : nullptr, pr.A.y, pr.B.y, D,
+                            a, updY);
+        }
+        __syncthreads();
     }
 }
 
-// dst.{X,Y,y} = a * A.{X,Y,y} + B.{X,Y,y}
-template <int D, int DV, int NW, typename PairFn>
-__device__ __forceinline__ void linear_phase(int npair, PairFn pair) {
-    using O = SumOfs<D, DV>;
-    constexpr int NT = NW * kWave;
-    constexpr int NX = D * D + D * DV;   // X and Y are contiguous
-    constexpr int PER = NX + D;
-    for (int it = threadIdx.x; it < npair * PER; it += NT) {
-        const int j = it / PER, x = it % PER;
-        const float *A, *B;
-        float *Dst;
-        float a;
-        pair(j, A, B, Dst, a);
-        const int idx = x < NX ? x : O::y + (x - NX);
-        Dst[idx] = a * A[idx] + B[idx];
-    }
-}
-
-template <bool F32, int D, int DV, bool HLA2, int NW>
-__global__ __launch_bounds__(NW * kWave) void scan_kernel(FwdParams p) {
-    using O = SumOfs<D, DV>;
-    constexpr int NT = NW * kWave;
+template <bool F32, int D, int DV, bool HLA2>
+__global__ __launch_bounds__(512) void scan_kernel(FwdParams p) {
     constexpr int SUMF = summary_floats(D, DV);
+    using G = ScanCfg<F32, D, DV>;
+    constexpr int NT = G::NT;
+    __shared__ alignas(16) float smem[G::PB * G::PAIR_FLOATS];
+    __shared__ float sa[G::PB];
     const int bh = blockIdx.x;
     const int spad = p.spad, nreal = p.nseg - 1;  // e[0 .. nreal-1] hold real summaries
     const float g = HLA2 ? p.gamma[bh % p.H] : 1.f;
@@ -170,6 +273,7 @@ __global__ __launch_bounds__(NW * kWave) void scan_kernel(FwdParams p) {
         hi = min(hi, nreal - 1);
         return hi >= lo ? (long)(hi - lo + 1) * p.seg_len : 0L;
     };
+    auto elem = [&](float *base, int i) { return base + (size_t)i * SUMF; };
 
     for (size_t idx = threadIdx.x; idx < (size_t)(spad - nreal) * SUMF; idx += NT)
         E[(size_t)nreal * SUMF + idx] = 0.f;
@@ -180,108 +284,63 @@ __global__ __launch_bounds__(NW * kWave) void scan_kernel(FwdParams p) {
     for (int s = 1; s < spad; s <<= 1) {
         const int npair = spad / (2 * s) - 1;
         if (npair <= 0) continue;
-        auto pair = [&](int j, const float *&A, const float *&B, float *&Dst, float &a) {
+        auto pair = [&](int j) {
             const int i = (j + 1) * 2 * s - 1;
-            A = E + (size_t)(i - s) * SUMF;
-            B = E + (size_t)i * SUMF;
-            Dst = E + (size_t)i * SUMF;
-            a = HLA2 ? pow_int(g, span(i - s + 1, i)) : 1.f;
+            ScanPair pr;
+            pr.A = scan_op(elem(E, i - s), D, DV);
+            pr.B = scan_op(elem(E, i), D, DV);
+            pr.dst = elem(E, i);
+            pr.copy = nullptr;
+            return pr;
         };
-        cross_phase<F32, D, DV, HLA2, NW>(npair, pair);
-        __syncthreads();
-        linear_phase<D, DV, NW>(npair, pair);
-        __syncthreads();
+        auto afac = [&](int j) {
+            const int i = (j + 1) * 2 * s - 1;
+            return HLA2 ? pow_int(g, span(i - s + 1, i)) : 1.f;
+        };
+        scan_level<F32, D, DV, HLA2>(smem, sa, npair, pair, afac, true, true);
     }
 
     // ---- down-sweep: p[i-s] <- p[i];  p[i] <- p[i] (+) e[i-s]
     for (int s = spad >> 1; s >= 1; s >>= 1) {
         const int npair = spad / (2 * s);
-        for (size_t it = threadIdx.x; it < (size_t)npair * SUMF; it += NT) {
-            const int j = (int)(it / SUMF), x = (int)(it % SUMF);
+        auto pair = [&](int j) {
             const int i = (j + 1) * 2 * s - 1;
-            Pr[(size_t)(i - s) * SUMF + x] = Pr[(size_t)i * SUMF + x];
-        }
-        __syncthreads();
-        auto pair = [&](int j, const float *&A, const float *&B, float *&Dst, float &a) {
-            const int i = (j + 1) * 2 * s - 1;
-            A = Pr + (size_t)(i - s) * SUMF;   // copy of the old p[i]
-            B = E + (size_t)(i - s) * SUMF;    // aggregate of the left subtree
-            Dst = Pr + (size_t)i * SUMF;
-            a = HLA2 ? pow_int(g, span(i - 2 * s + 1, i - s)) : 1.f;
+            ScanPair pr;
+            pr.A = scan_op(elem(Pr, i), D, DV);        // the prefix before the left subtree
+            pr.B = scan_op(elem(E, i - s), D, DV);     // aggregate of the left subtree
+            pr.dst = elem(Pr, i);
+            pr.copy = elem(Pr, i - s);
+            return pr;
         };
-        cross_phase<F32, D, DV, HLA2, NW>(npair, pair);
-        linear_phase<D, DV, NW>(npair, pair);
-        __syncthreads();
+        auto afac = [&](int j) {
+            const int i = (j + 1) * 2 * s - 1;
+            return HLA2 ? pow_int(g, span(i - 2 * s + 1, i - s)) : 1.f;
+        };
+        scan_level<F32, D, DV, HLA2>(smem, sa, npair, pair, afac, true, true);
     }
 
     // ---- fold the caller's initial state in front of every prefix
     if (p.state_in) {
         const int STF = HLA2 ? hla2_state_floats(D, DV) : ahla_state_floats(D, DV);
         const float *st = p.state_in + (size_t)bh * STF;
-        const int nseg = p.nseg;
-        const int w = wave_id();
-        constexpr int nTD = D / 16, nTV = DV / 16;
-        if (HLA2) {
-            // state_in = (S, W, u) with C = m = 0:  X += a S, N = a^2 W + N + a S Y,
-            // nv = a^2 u + nv + a S y ;  Y, y unchanged
-            const float *S = st, *W = st + D * D, *u = st + D * D + D * DV;
-            for (int it = w; it < nseg * nTD; it += NW) {
-                const int s = it / nTD, ti = it % nTD;
-                float *Bp = Pr + (size_t)s * SUMF;
-                const float a = pow_int(g, (long)s * p.seg_len);
-                for (int tj = 0; tj < nTV; ++tj) {
-                    const f32x4 c = cross_tile<F32, D>(S, D, Bp + O::Y, DV, ti, tj);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                        Bp[O::N + idx] = a * a * W[idx] + Bp[O::N + idx] + a * c[r];
-                    }
-                }
-            }
-            for (int it = threadIdx.x; it < nseg * D; it += NT) {
-                const int s = it / D, row = it % D;
-                float *Bp = Pr + (size_t)s * SUMF;
-                const float a = pow_int(g, (long)s * p.seg_len);
-                float acc = 0.f;
-                for (int c = 0; c < D; ++c) acc += S[row * D + c] * Bp[O::y + c];
-                Bp[O::nv + row] = a * a * u[row] + Bp[O::nv + row] + a * acc;
-            }
-            for (int it = threadIdx.x; it < nseg * D * D; it += NT) {
-                const int s = it / (D * D), x = it % (D * D);
-                float *Bp = Pr + (size_t)s * SUMF;
-                Bp[O::X + x] = pow_int(g, (long)s * p.seg_len) * S[x] + Bp[O::X + x];
-            }
-        } else {
-            // state_in = (P, E, mK, nk):  Y += P, y += mK, N = E + N + M P,
-            // nv = nk + nv + M mK  (M = X of the prefix)
-            const float *P = st, *Ein = st + D * DV, *mK = st + 2 * D * DV, *nk = mK + D;
-            for (int it = w; it < nseg * nTD; it += NW) {
-                const int s = it / nTD, ti = it % nTD;
-                float *Bp = Pr + (size_t)s * SUMF;
-                for (int tj = 0; tj < nTV; ++tj) {
-                    const f32x4 c = cross_tile<F32, D>(Bp + O::X, D, P, DV, ti, tj);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int idx = (ti * 16 + acc_row(r)) * DV + tj * 16 + acc_col();
-                        Bp[O::N + idx] = Ein[idx] + Bp[O::N + idx] + c[r];
-                    }
-                }
-            }
-            for (int it = threadIdx.x; it < nseg * D; it += NT) {
-                const int s = it / D, row = it % D;
-                float *Bp = Pr + (size_t)s * SUMF;
-                float acc = 0.f;
-                for (int c = 0; c < D; ++c) acc += Bp[O::X + row * D + c] * mK[c];
-                Bp[O::nv + row] = nk[row] + Bp[O::nv + row] + acc;
-            }
-            __syncthreads();  // the M reads above precede nothing that writes M; Y, y next
-            for (int it = threadIdx.x; it < nseg * (D * DV + D); it += NT) {
-                const int s = it / (D * DV + D), x = it % (D * DV + D);
-                float *Bp = Pr + (size_t)s * SUMF;
-                if (x < D * DV) Bp[O::Y + x] += P[x];
-                else Bp[O::y + (x - D * DV)] += mK[x - D * DV];
-            }
+        ScanOp A;
+        if (HLA2) {   // (S, W, u) with C = m = 0
+            A = ScanOp{st, nullptr, st + D * D, nullptr, st + D * D + D * DV};
+        } else {      // (P, E, mK, nk) with M = 0
+            A = ScanOp{nullptr, st, st + D * DV, st + 2 * D * DV, st + 2 * D * DV + D};
         }
+        auto pair = [&](int j) {
+            ScanPair pr;
+            pr.A = A;
+            pr.B = scan_op(elem(Pr, j), D, DV);
+            pr.dst = elem(Pr, j);
+            pr.copy = nullptr;
+            return pr;
+        };
+        auto afac = [&](int j) { return HLA2 ? pow_int(g, (long)j * p.seg_len) : 1.f; };
+        // HLA-2 leaves Y, y (C, m) as they are (A's are zero and the forward
+        // kernel does not read them); AHLA leaves X (M).
+        scan_level<F32, D, DV, HLA2>(smem, sa, p.nseg, pair, afac, HLA2, !HLA2);
     }
 }
 
