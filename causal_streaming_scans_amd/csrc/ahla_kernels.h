@@ -35,8 +35,8 @@ struct AhlaCfg {
     static constexpr int LDD = ld_of<T>(D), LDC = ld_of<T>(C);
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int OJ = (nTV + NCG - 1) / NCG;      // Y / O^T tiles per wave
-    static constexpr int TP = nTD * nTV, TM = nTD * nTD;
-    static constexpr int PP = (TP + NW - 1) / NW, PM = (TM + NW - 1) / NW;
+    using PBk = TileBlocks<nTD, nTV, NW>;   // ownership of P, E tiles
+    using MBk = TileBlocks<nTD, nTD, NW>;   // ownership of M tiles
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = ahla_state_floats(D, DV);
 };
@@ -70,18 +70,17 @@ struct AhlaSumSmem {
 // Y = Q P0 + L V for row tile r (rows tau), written to Yt transposed; also
 // y1[tau] = q_tau . mK + sum_sigma L[tau][sigma].
 template <typename T, int D, int DV, int C, int RT, int NCG, int OJ, int LDD, int LDC>
-__device__ __forceinline__ void ahla_y_phase(const Frag16<T> (&Lf)[RT], int r, int cg, int tau,
-                                             const T *Q, const T *Pt, const T *Vt, T *Yt,
-                                             const float *mK, float *y1) {
+__device__ __forceinline__ void ahla_y_phase(const Frag16<T> (&Lf)[RT], const RowFrags<T, D> &qf,
+                                             int r, int cg, int tau, const T *Q, const T *Pt,
+                                             const T *Vt, T *Yt, const float *mK, float *y1) {
     constexpr int nTV = DV / 16;
     const int g4 = (lane_id() >> 4) << 2;
-    const T *Qr = Q + 16 * r * LDD;
 #pragma unroll
     for (int jj = 0; jj < OJ; ++jj) {
         const int jv = cg + jj * NCG;
         if (jv < nTV) {
             // accumulator rows are tokens 16r + 4g + i, columns features 16 jv + c
-            f32x4 y = mma_nt(zero4(), Qr, LDD, Pt + 16 * jv * LDD, LDD, 0, D);
+            f32x4 y = mma_nt_fa(zero4(), qf, Pt + 16 * jv * LDD, LDD);
             f32x4 yc = zero4();
 #pragma unroll
             for (int s = 0; s < RT; ++s)
@@ -138,24 +137,21 @@ void ahla_forward_kernel(FwdParams p) {
         mK0 = e + 2 * D * DV;
         nk0 = mK0 + D;
     }
-    f32x4 accP[G::PP], accE[G::PP];
+    using PBk = typename G::PBk;
+    f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
+    for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+        f32x4 a, b;
 #pragma unroll
-    for (int s = 0; s < G::PP; ++s) {
-        const int t = w + s * NW;
-        accP[s] = zero4();
-        accE[s] = zero4();
-        if (t < G::TP) {
-            const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-                accP[s][i] = P0 ? P0[idx] : 0.f;
-                accE[s][i] = E0 ? E0[idx] : 0.f;
-            }
-            store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
-            store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[s]);
+        for (int i = 0; i < 4; ++i) {
+            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+            a[i] = P0 ? P0[idx] : 0.f;
+            b[i] = E0 ? E0[idx] : 0.f;
         }
-    }
+        accP[pb][x][y] = a;
+        accE[pb][x][y] = b;
+        store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, a);
+        store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, b);
+    });
     for (int i = threadIdx.x; i < D; i += NT) {
         sm.mK[i] = mK0 ? mK0[i] : 0.f;
         sm.nk[i] = nk0 ? nk0[i] : 0.f;
@@ -184,10 +180,11 @@ void ahla_forward_kernel(FwdParams p) {
         }
         __syncthreads();
 
-        const T *Qr = sm.Q + 16 * r * LDD;
+        RowFrags<T, D> qf;
+        qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, false>(Lf, sm.K, Qr, r, tau, nullptr, 1);
-        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
+        scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
+        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, qf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
                                                             sm.Yt, sm.mK, sm.y1);
         // carried part of the output and of its denominator
         f32x4 accO[G::OJ];
@@ -195,7 +192,7 @@ void ahla_forward_kernel(FwdParams p) {
         for (int jj = 0; jj < G::OJ; ++jj) {
             const int jv = cg + jj * NCG;
             accO[jj] = zero4();
-            if (jv < nTV) accO[jj] = mma_nt(zero4(), sm.Et + 16 * jv * LDD, LDD, Qr, LDD, 0, D);
+            if (jv < nTV) accO[jj] = mma_nt_f(zero4(), sm.Et + 16 * jv * LDD, LDD, qf);
         }
         float den = 0.f;
         if (p.ratio) den = lane_dot<T, D>(sm.Q + tau * LDD, sm.nk);
@@ -226,17 +223,18 @@ void ahla_forward_kernel(FwdParams p) {
             }
         }
         // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
+        for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
+            mma_nt_blk<PBk::BR, C>(accP[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+            mma_nt_blk<PBk::BR, C>(accE[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Yt + 16 * tv0 * LDC, LDC);
 #pragma unroll
-        for (int s = 0; s < G::PP; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TP) {
-                const int ti = t / nTV, tv = t % nTV;
-                accP[s] = mma_nt(accP[s], sm.Kt + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
-                accE[s] = mma_nt(accE[s], sm.Kt + 16 * ti * LDC, LDC, sm.Yt + 16 * tv * LDC, LDC, 0, C);
-                store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
-                store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[s]);
-            }
-        }
+            for (int x = 0; x < PBk::BR; ++x)
+#pragma unroll
+                for (int y = 0; y < PBk::BR; ++y) {
+                    const int o = (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4;
+                    store4(sm.Pt + o, accP[pb][x][y]);
+                    store4(sm.Et + o, accE[pb][x][y]);
+                }
+        });
         for (int i = threadIdx.x; i < D; i += NT) {
             sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
             sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
@@ -247,19 +245,14 @@ void ahla_forward_kernel(FwdParams p) {
 
     if (p.state_out && seg == p.nseg - 1) {
         float *so = p.state_out + (size_t)bh * G::STF;
+        for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-        for (int s = 0; s < G::PP; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TP) {
-                const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-                    so[idx] = accP[s][i];
-                    so[D * DV + idx] = accE[s][i];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                so[idx] = accP[pb][x][y][i];
+                so[D * DV + idx] = accE[pb][x][y][i];
             }
-        }
+        });
         __syncthreads();
         for (int i = threadIdx.x; i < D; i += NT) {
             so[2 * D * DV + i] = sm.mK[i];
@@ -288,14 +281,25 @@ void ahla_summary_kernel(FwdParams p) {
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
-    f32x4 accP[G::PP], accE[G::PP], accM[G::PM];
+    using PBk = typename G::PBk;
+    using MBk = typename G::MBk;
+    f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
+    f32x4 accM[MBk::PB][MBk::BR][MBk::BR];
 #pragma unroll
-    for (int s = 0; s < G::PP; ++s) {
-        accP[s] = zero4();
-        accE[s] = zero4();
-    }
+    for (int pb = 0; pb < PBk::PB; ++pb)
 #pragma unroll
-    for (int s = 0; s < G::PM; ++s) accM[s] = zero4();
+        for (int x = 0; x < PBk::BR; ++x)
+#pragma unroll
+            for (int y = 0; y < PBk::BR; ++y) {
+                accP[pb][x][y] = zero4();
+                accE[pb][x][y] = zero4();
+            }
+#pragma unroll
+    for (int pb = 0; pb < MBk::PB; ++pb)
+#pragma unroll
+        for (int x = 0; x < MBk::BR; ++x)
+#pragma unroll
+            for (int y = 0; y < MBk::BR; ++y) accM[pb][x][y] = zero4();
     for (int i = threadIdx.x; i < DV * LDD; i += NT) sm.Pt[i] = from_f<T>(0.f);
     for (int i = threadIdx.x; i < D; i += NT) {
         sm.mK[i] = 0.f;
@@ -326,31 +330,26 @@ void ahla_summary_kernel(FwdParams p) {
         }
         __syncthreads();
 
-        const T *Qr = sm.Q + 16 * r * LDD;
+        RowFrags<T, D> qf;
+        qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, false>(Lf, sm.K, Qr, r, tau, nullptr, 1);
-        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
+        scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
+        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, qf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
                                                             sm.Yt, sm.mK, sm.y1);
         __syncthreads();
 
+        for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
+            mma_nt_blk<PBk::BR, C>(accP[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+            mma_nt_blk<PBk::BR, C>(accE[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Yt + 16 * tv0 * LDC, LDC);
 #pragma unroll
-        for (int s = 0; s < G::PP; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TP) {
-                const int ti = t / nTV, tv = t % nTV;
-                accP[s] = mma_nt(accP[s], sm.Kt + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
-                accE[s] = mma_nt(accE[s], sm.Kt + 16 * ti * LDC, LDC, sm.Yt + 16 * tv * LDC, LDC, 0, C);
-                store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[s]);
-            }
-        }
+            for (int x = 0; x < PBk::BR; ++x)
 #pragma unroll
-        for (int s = 0; s < G::PM; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TM) {
-                const int ti = t / nTD, tj = t % nTD;
-                accM[s] = mma_nt(accM[s], sm.Kt + 16 * ti * LDC, LDC, sm.Qt + 16 * tj * LDC, LDC, 0, C);
-            }
-        }
+                for (int y = 0; y < PBk::BR; ++y)
+                    store4(sm.Pt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accP[pb][x][y]);
+        });
+        for_blocks<MBk, NW>(w, [&](int pb, int ti0, int tj0) {
+            mma_nt_blk<MBk::BR, C>(accM[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Qt + 16 * tj0 * LDC, LDC);
+        });
         for (int i = threadIdx.x; i < D; i += NT) {
             sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
             sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
@@ -362,28 +361,18 @@ void ahla_summary_kernel(FwdParams p) {
 
     // summary [X = M | Y = P | N = E | y = mK | nv = nk]
     float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
+    for_owned<MBk, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
-    for (int s = 0; s < G::PM; ++s) {
-        const int t = w + s * NW;
-        if (t < G::TM) {
-            const int ti = t / nTD, tj = t % nTD;
+        for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accM[pb][x][y][i];
+    });
+    for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accM[s][i];
+        for (int i = 0; i < 4; ++i) {
+            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+            e[D * D + idx] = accP[pb][x][y][i];
+            e[D * D + D * DV + idx] = accE[pb][x][y][i];
         }
-    }
-#pragma unroll
-    for (int s = 0; s < G::PP; ++s) {
-        const int t = w + s * NW;
-        if (t < G::TP) {
-            const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-                e[D * D + idx] = accP[s][i];
-                e[D * D + D * DV + idx] = accE[s][i];
-            }
-        }
-    }
+    });
     for (int i = threadIdx.x; i < D; i += NT) {
         e[D * D + 2 * D * DV + i] = sm.mK[i];
         e[D * D + 2 * D * DV + D + i] = sm.nk[i];

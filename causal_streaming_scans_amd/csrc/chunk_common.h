@@ -20,34 +20,53 @@ struct WaveShape {
 };
 
 // One thread's share of a [C][COLS] chunk tile, held in registers between the
-// global load (issued a chunk ahead) and the LDS store.
+// global load (issued a chunk ahead) and the LDS store.  The loads are
+// unconditional -- a row past the end of the sequence reads row 0 of the
+// chunk instead (always in bounds) -- and the raw 16-byte values are kept
+// whole; rows past the end are zeroed only when stored to LDS.  So nothing
+// consumes a load until the next chunk is staged, and no wait for it lands
+// in the middle of the current chunk.
+//
+// Lanes run along the tokens (item idx -> token idx % C, 16-byte column
+// group idx / C): one transposed store instruction then writes consecutive
+// tokens of one feature row, which keeps the 2-byte writes free of LDS bank
+// conflicts; row-major stores stay conflict-free per quarter wave.
 template <typename T, int C, int COLS, int NT>
 struct ChunkRegs {
     static constexpr int VE = Vec16<T>::N;
     static constexpr int VPR = COLS / VE;
     static constexpr int NVEC = C * VPR;
     static constexpr int NV = (NVEC + NT - 1) / NT;
-    Vec16<T> x[NV];
+    uint4 raw[NV];
+    int rows_valid;
 
-    __device__ __forceinline__ void load(const T *__restrict__ src, int rows_valid) {
+    __device__ __forceinline__ void load(const T *__restrict__ src, int rv) {
+        rows_valid = rv;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
-            const int r = idx / VPR, c = (idx % VPR) * VE;
-            if (idx < NVEC && r < rows_valid) {
-                x[i] = load16(src + (size_t)r * COLS + c);
-            } else {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) x[i].v[e] = from_f<T>(0.f);
-            }
+            int r = idx % C;
+            const int c = ((idx / C) % VPR) * VE;
+            if (!(idx < NVEC && r < rv)) r = 0;
+            raw[i] = *reinterpret_cast<const uint4 *>(src + (size_t)r * COLS + c);
         }
+    }
+    __device__ __forceinline__ bool ok(int i) const {
+        const int idx = threadIdx.x + i * NT;
+        return idx < NVEC && idx % C < rows_valid;
+    }
+    __device__ __forceinline__ Vec16<T> get(int i) const {
+        Vec16<T> x;
+        const uint4 z = ok(i) ? raw[i] : make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4 *>(x.v) = z;
+        return x;
     }
     // dst[r][c] (row-major, leading dim ld)
     __device__ __forceinline__ void store_rows(T *dst, int ld) const {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) store16(dst + (idx / VPR) * ld + (idx % VPR) * VE, x[i]);
+            if (idx < NVEC) store16(dst + (idx % C) * ld + (idx / C) * VE, get(i));
         }
     }
     // dstT[c][r] (transposed, leading dim ld)
@@ -56,9 +75,10 @@ struct ChunkRegs {
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
             if (idx < NVEC) {
-                const int r = idx / VPR, c = (idx % VPR) * VE;
+                const int r = idx % C, c = (idx / C) * VE;
+                const Vec16<T> x = get(i);
 #pragma unroll
-                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = x[i].v[e];
+                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = x.v[e];
             }
         }
     }
@@ -68,10 +88,11 @@ struct ChunkRegs {
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
             if (idx < NVEC) {
-                const int r = idx / VPR, c = (idx % VPR) * VE;
+                const int r = idx % C, c = (idx / C) * VE;
                 const float wr = r <= wofs ? gp[wofs - r] : 0.f;
+                const Vec16<T> x = get(i);
 #pragma unroll
-                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = from_f<T>(to_f(x[i].v[e]) * wr);
+                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = from_f<T>(to_f(x.v[e]) * wr);
             }
         }
     }

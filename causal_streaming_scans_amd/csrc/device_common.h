@@ -26,7 +26,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// wave index, marked wave-uniform so branches on it stay scalar
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return static_cast<T>(x); }
@@ -78,6 +81,165 @@ __device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const float *A, int lda, cons
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k], acc, 0, 0, 0);
     return acc;
 }
+
+// ------------------------------------------ operands kept in registers
+
+// MFMA operand fragments of one 16-row tile over k = 0..K, loaded from LDS
+// once and reused: lane l holds row l%16 at the k offsets both operand
+// slots of mma_nt use (A and Bt fragments are addressed alike).
+template <typename T, int K> struct RowFrags;
+template <int K> struct RowFrags<bf16, K> {
+    static constexpr bool W32 = (K % 32) == 0;
+    bf16x8 v8[W32 ? K / 32 : 1];
+    i16x4 v4[W32 ? 1 : K / 16];
+    __device__ __forceinline__ void load(const bf16 *base, int ld) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+        if constexpr (W32) {
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s)
+                v8[s] = *reinterpret_cast<const bf16x8 *>(base + r * ld + 32 * s + 8 * g);
+        } else {
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                v4[s] = *reinterpret_cast<const i16x4 *>(base + r * ld + 16 * s + 4 * g);
+        }
+    }
+};
+template <int K> struct RowFrags<float, K> {
+    float v[K / 4];
+    __device__ __forceinline__ void load(const float *base, int ld) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) v[s] = base[r * ld + 4 * s + g];
+    }
+};
+
+// acc += A[0:16][0:K] * F^T with A in LDS and F preloaded (F as the Bt side)
+template <int K>
+__device__ __forceinline__ f32x4 mma_nt_f(f32x4 acc, const bf16 *A, int lda,
+                                          const RowFrags<bf16, K> &f) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+    if constexpr (RowFrags<bf16, K>::W32) {
+#pragma unroll
+        for (int s = 0; s < K / 32; ++s) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(A + r * lda + 32 * s + 8 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.v8[s], acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) {
+            const i16x4 av = *reinterpret_cast<const i16x4 *>(A + r * lda + 16 * s + 4 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, f.v4[s], acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+template <int K>
+__device__ __forceinline__ f32x4 mma_nt_f(f32x4 acc, const float *A, int lda,
+                                          const RowFrags<float, K> &f) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + 4 * s + g], f.v[s], acc, 0, 0, 0);
+    return acc;
+}
+// acc += F * Bt[0:16][0:K]^T with F preloaded (F as the A side)
+template <int K>
+__device__ __forceinline__ f32x4 mma_nt_fa(f32x4 acc, const RowFrags<bf16, K> &f,
+                                           const bf16 *Bt, int ldb) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+    if constexpr (RowFrags<bf16, K>::W32) {
+#pragma unroll
+        for (int s = 0; s < K / 32; ++s) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(Bt + r * ldb + 32 * s + 8 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v8[s], bv, acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) {
+            const i16x4 bv = *reinterpret_cast<const i16x4 *>(Bt + r * ldb + 16 * s + 4 * g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v4[s], bv, acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+template <int K>
+__device__ __forceinline__ f32x4 mma_nt_fa(f32x4 acc, const RowFrags<float, K> &f,
+                                           const float *Bt, int ldb) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s], Bt[r * ldb + 4 * s + g], acc, 0, 0, 0);
+    return acc;
+}
+
+// A BR x BR block of 16x16 tiles: acc[x][y] += A[16x..][0:K] * Bt[16y..][0:K]^T,
+// each operand row loaded once per k step (halves LDS reads at BR = 2).
+template <int BR, int K>
+__device__ __forceinline__ void mma_nt_blk(f32x4 (&acc)[BR][BR], const bf16 *A, int lda,
+                                           const bf16 *Bt, int ldb) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+    if constexpr (K % 32 == 0) {
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a[BR], b[BR];
+#pragma unroll
+            for (int x = 0; x < BR; ++x) {
+                a[x] = *reinterpret_cast<const bf16x8 *>(A + (16 * x + r) * lda + k + 8 * g);
+                b[x] = *reinterpret_cast<const bf16x8 *>(Bt + (16 * x + r) * ldb + k + 8 * g);
+            }
+#pragma unroll
+            for (int x = 0; x < BR; ++x)
+#pragma unroll
+                for (int y = 0; y < BR; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k += 16) {
+            i16x4 a[BR], b[BR];
+#pragma unroll
+            for (int x = 0; x < BR; ++x) {
+                a[x] = *reinterpret_cast<const i16x4 *>(A + (16 * x + r) * lda + k + 4 * g);
+                b[x] = *reinterpret_cast<const i16x4 *>(Bt + (16 * x + r) * ldb + k + 4 * g);
+            }
+#pragma unroll
+            for (int x = 0; x < BR; ++x)
+#pragma unroll
+                for (int y = 0; y < BR; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+    }
+}
+template <int BR, int K>
+__device__ __forceinline__ void mma_nt_blk(f32x4 (&acc)[BR][BR], const float *A, int lda,
+                                           const float *Bt, int ldb) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) {
+        float a[BR], b[BR];
+#pragma unroll
+        for (int x = 0; x < BR; ++x) {
+            a[x] = A[(16 * x + r) * lda + k + g];
+            b[x] = Bt[(16 * x + r) * ldb + k + g];
+        }
+#pragma unroll
+        for (int x = 0; x < BR; ++x)
+#pragma unroll
+            for (int y = 0; y < BR; ++y)
+                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
+}
+
+// Ownership of the tiles of an (nTR x nTC)-tile matrix by NW waves, in
+// BR x BR blocks (BR = 2 when that still gives every wave a block).
+template <int nTR, int nTC, int NW>
+struct TileBlocks {
+    static constexpr bool two = (nTR % 2 == 0) && (nTC % 2 == 0) && (nTR * nTC / 4 >= NW);
+    static constexpr int BR = two ? 2 : 1;
+    static constexpr int nBR = nTR / BR, nBC = nTC / BR, NB = nBR * nBC;
+    static constexpr int PB = (NB + NW - 1) / NW;   // blocks per wave
+};
 
 // ------------------------------------------------ register-chained operands
 //

@@ -49,13 +49,39 @@ struct Hla2Cfg {
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int ZJ = (nTD + NCG - 1) / NCG;    // Z^T tiles per wave
     static constexpr int OJ = (nTV + NCG - 1) / NCG;    // O^T tiles per wave
-    static constexpr int TS = nTD * nTD, TW = nTD * nTV;
-    static constexpr int PS = (TS + NW - 1) / NW, PW = (TW + NW - 1) / NW;
+    using SB = TileBlocks<nTD, nTD, NW>;    // ownership of S tiles
+    using WB = TileBlocks<nTD, nTV, NW>;    // ownership of W (and C) tiles
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = hla2_state_floats(D, DV);
     static constexpr int NPOW = 2 * C + 2;
     static_assert(D % 16 == 0 && DV % 16 == 0 && C % 16 == 0, "tile multiples");
 };
+
+// Visit the tiles a wave owns in a blocked layout: f(p, x, y, ti, tj) with
+// compile-time p, x, y (the accumulator indices) and run-time tile indices.
+template <typename TB, int NW, typename F>
+__device__ __forceinline__ void for_owned(int w, F f) {
+#pragma unroll
+    for (int pb = 0; pb < TB::PB; ++pb) {
+        const int blk = w + pb * NW;
+        if (blk < TB::NB) {
+            const int bi = blk / TB::nBC, bj = blk % TB::nBC;
+#pragma unroll
+            for (int x = 0; x < TB::BR; ++x)
+#pragma unroll
+                for (int y = 0; y < TB::BR; ++y) f(pb, x, y, bi * TB::BR + x, bj * TB::BR + y);
+        }
+    }
+}
+// The blocks a wave owns: g(p, ti0, tj0) with the block's first tile.
+template <typename TB, int NW, typename F>
+__device__ __forceinline__ void for_blocks(int w, F f) {
+#pragma unroll
+    for (int pb = 0; pb < TB::PB; ++pb) {
+        const int blk = w + pb * NW;
+        if (blk < TB::NB) f(pb, (blk / TB::nBC) * TB::BR, (blk % TB::nBC) * TB::BR);
+    }
+}
 
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2FwdSmem {
@@ -97,13 +123,13 @@ constexpr int hla2_min_blocks() {
 // L^T tiles of row tile r as operand fragments: Lf[s] holds
 // (D_g * tril(Q K^T))^T[sigma in tile s][tau in tile r], s <= r.
 template <typename T, int D, int RT, int LDD, bool DECAY>
-__device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[RT], const T *K, const T *Qr, int r,
-                                         int tau, const float *gp, int gexp) {
+__device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[RT], const T *K, const RowFrags<T, D> &qf,
+                                         int r, int tau, const float *gp, int gexp) {
     const int g4 = (lane_id() >> 4) << 2;
 #pragma unroll
     for (int s = 0; s < RT; ++s) {
         if (s <= r) {
-            f32x4 a = mma_nt(zero4(), K + 16 * s * LDD, LDD, Qr, LDD, 0, D);
+            f32x4 a = mma_nt_f(zero4(), K + 16 * s * LDD, LDD, qf);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int sigma = 16 * s + g4 + i;
@@ -156,31 +182,23 @@ void hla2_forward_kernel(FwdParams p) {
         W0 = e + D * D;
         u0 = e + D * D + D * DV;
     }
-    f32x4 accS[G::PS], accW[G::PW];
+    using SB = typename G::SB;
+    using WB = typename G::WB;
+    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR];
+    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+        f32x4 a;
 #pragma unroll
-    for (int s = 0; s < G::PS; ++s) {
-        const int t = w + s * NW;
-        accS[s] = zero4();
-        if (t < G::TS) {
-            const int ti = t / nTD, tj = t % nTD;
+        for (int i = 0; i < 4; ++i) a[i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
+        accS[pb][x][y] = a;
+        store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, a);
+    });
+    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+        f32x4 a;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                accS[s][i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
-            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < G::PW; ++s) {
-        const int t = w + s * NW;
-        accW[s] = zero4();
-        if (t < G::TW) {
-            const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                accW[s][i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
-            store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[s]);
-        }
-    }
+        for (int i = 0; i < 4; ++i) a[i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
+        accW[pb][x][y] = a;
+        store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, a);
+    });
     for (int i = threadIdx.x; i < D; i += NT) sm.u0[i] = u0 ? u0[i] : 0.f;
 
     ChunkRegs<T, C, D, NT> rq, rk;
@@ -208,10 +226,12 @@ void hla2_forward_kernel(FwdParams p) {
         }
         __syncthreads();
 
-        const T *Qr = sm.Q + 16 * r * LDD;
+        // the row tile's Q, kept in registers: an operand of four products
+        RowFrags<T, D> qf;
+        qf.load(sm.Q + 16 * r * LDD, LDD);
         // ---- a-2: L^T for this row tile, as operand fragments
         Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, Qr, r, tau, sm.gp, 1);
+        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
 
         // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
         const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
@@ -219,7 +239,7 @@ void hla2_forward_kernel(FwdParams p) {
         for (int jj = 0; jj < G::ZJ; ++jj) {
             const int jt = cg + jj * NCG;
             if (jt < nTD) {
-                f32x4 z = mma_nt(zero4(), sm.St + 16 * jt * LDD, LDD, Qr, LDD, 0, D);
+                f32x4 z = mma_nt_f(zero4(), sm.St + 16 * jt * LDD, LDD, qf);
                 f32x4 zc = zero4();
 #pragma unroll
                 for (int s = 0; s < RT; ++s)
@@ -238,7 +258,7 @@ void hla2_forward_kernel(FwdParams p) {
             const int jv = cg + jj * NCG;
             accO[jj] = zero4();
             if (jv < nTV) {
-                accO[jj] = mma_nt(zero4(), sm.Wt + 16 * jv * LDD, LDD, Qr, LDD, 0, D);
+                accO[jj] = mma_nt_f(zero4(), sm.Wt + 16 * jv * LDD, LDD, qf);
                 if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
             }
         }
@@ -251,7 +271,7 @@ void hla2_forward_kernel(FwdParams p) {
 
         // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
         Frag16<T> Pf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Pf, sm.Z, Qr, r, tau, sm.gp, 2);
+        scores_t<T, D, RT, LDD, DECAY>(Pf, sm.Z, qf, r, tau, sm.gp, 2);
         if (p.ratio) {
             float rs = 0.f;
 #pragma unroll
@@ -280,26 +300,34 @@ void hla2_forward_kernel(FwdParams p) {
         const float gc = DECAY ? sm.gp[cv] : 1.f;
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
         const T *KA = DECAY ? sm.Ktw : sm.Kt;
+        for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
+            if (DECAY) {
 #pragma unroll
-        for (int s = 0; s < G::PS; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TS) {
-                const int ti = t / nTD, tj = t % nTD;
-                if (DECAY) accS[s] *= gc;
-                accS[s] = mma_nt(accS[s], KA + 16 * ti * LDC, LDC, sm.Kt + 16 * tj * LDC, LDC, 0, C);
-                store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
-            }
-        }
+                for (int x = 0; x < SB::BR; ++x)
 #pragma unroll
-        for (int s = 0; s < G::PW; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TW) {
-                const int ti = t / nTV, tv = t % nTV;
-                if (DECAY) accW[s] *= gc2;
-                accW[s] = mma_nt(accW[s], sm.Ztw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
-                store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[s]);
+                    for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
-        }
+            mma_nt_blk<SB::BR, C>(accS[pb], KA + 16 * ti0 * LDC, LDC, sm.Kt + 16 * tj0 * LDC, LDC);
+#pragma unroll
+            for (int x = 0; x < SB::BR; ++x)
+#pragma unroll
+                for (int y = 0; y < SB::BR; ++y)
+                    store4(sm.St + (16 * (tj0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accS[pb][x][y]);
+        });
+        for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
+            if (DECAY) {
+#pragma unroll
+                for (int x = 0; x < WB::BR; ++x)
+#pragma unroll
+                    for (int y = 0; y < WB::BR; ++y) accW[pb][x][y] *= gc2;
+            }
+            mma_nt_blk<WB::BR, C>(accW[pb], sm.Ztw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+#pragma unroll
+            for (int x = 0; x < WB::BR; ++x)
+#pragma unroll
+                for (int y = 0; y < WB::BR; ++y)
+                    store4(sm.Wt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accW[pb][x][y]);
+        });
         for (int i = threadIdx.x; i < D; i += NT)
             sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
         c0 = n0;
@@ -308,25 +336,16 @@ void hla2_forward_kernel(FwdParams p) {
 
     if (p.state_out && seg == p.nseg - 1) {
         float *so = p.state_out + (size_t)bh * G::STF;
+        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
-        for (int s = 0; s < G::PS; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TS) {
-                const int ti = t / nTD, tj = t % nTD;
+            for (int i = 0; i < 4; ++i)
+                so[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];
+        });
+        for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) so[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[s][i];
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < G::PW; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TW) {
-                const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = accW[s][i];
-            }
-        }
+            for (int i = 0; i < 4; ++i)
+                so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = accW[pb][x][y][i];
+        });
         __syncthreads();
         for (int i = threadIdx.x; i < D; i += NT) so[D * D + D * DV + i] = sm.u0[i];
     }
@@ -356,14 +375,24 @@ void hla2_summary_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
     if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
-    f32x4 accS[G::PS], accW[G::PW], accC[G::PW];
+    using SB = typename G::SB;
+    using WB = typename G::WB;
+    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accC[WB::PB][WB::BR][WB::BR];
 #pragma unroll
-    for (int s = 0; s < G::PS; ++s) accS[s] = zero4();
+    for (int pb = 0; pb < SB::PB; ++pb)
 #pragma unroll
-    for (int s = 0; s < G::PW; ++s) {
-        accW[s] = zero4();
-        accC[s] = zero4();
-    }
+        for (int x = 0; x < SB::BR; ++x)
+#pragma unroll
+            for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] = zero4();
+#pragma unroll
+    for (int pb = 0; pb < WB::PB; ++pb)
+#pragma unroll
+        for (int x = 0; x < WB::BR; ++x)
+#pragma unroll
+            for (int y = 0; y < WB::BR; ++y) {
+                accW[pb][x][y] = zero4();
+                accC[pb][x][y] = zero4();
+            }
     for (int i = threadIdx.x; i < D * LDD; i += NT) sm.St[i] = from_f<T>(0.f);
     for (int i = threadIdx.x; i < D; i += NT) {
         sm.u0[i] = 0.f;
@@ -396,15 +425,16 @@ void hla2_summary_kernel(FwdParams p) {
         }
         __syncthreads();
 
-        const T *Qr = sm.Q + 16 * r * LDD;
+        RowFrags<T, D> qf;
+        qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, Qr, r, tau, sm.gp, 1);
+        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
         const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
 #pragma unroll
         for (int jj = 0; jj < G::ZJ; ++jj) {
             const int jt = cg + jj * NCG;
             if (jt < nTD) {
-                f32x4 z = mma_nt(zero4(), sm.St + 16 * jt * LDD, LDD, Qr, LDD, 0, D);
+                f32x4 z = mma_nt_f(zero4(), sm.St + 16 * jt * LDD, LDD, qf);
                 f32x4 zc = zero4();
 #pragma unroll
                 for (int s = 0; s < RT; ++s)
@@ -420,29 +450,33 @@ void hla2_summary_kernel(FwdParams p) {
         const float gc = DECAY ? sm.gp[cv] : 1.f;
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
         const T *KA = DECAY ? sm.Ktw : sm.Kt;
+        for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
+            if (DECAY) {
 #pragma unroll
-        for (int s = 0; s < G::PS; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TS) {
-                const int ti = t / nTD, tj = t % nTD;
-                if (DECAY) accS[s] *= gc;
-                accS[s] = mma_nt(accS[s], KA + 16 * ti * LDC, LDC, sm.Kt + 16 * tj * LDC, LDC, 0, C);
-                store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[s]);
-            }
-        }
+                for (int x = 0; x < SB::BR; ++x)
 #pragma unroll
-        for (int s = 0; s < G::PW; ++s) {
-            const int t = w + s * NW;
-            if (t < G::TW) {
-                const int ti = t / nTV, tv = t % nTV;
-                if (DECAY) {
-                    accW[s] *= gc2;
-                    accC[s] *= gc;
-                }
-                accW[s] = mma_nt(accW[s], sm.Ztw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
-                accC[s] = mma_nt(accC[s], sm.Qtw + 16 * ti * LDC, LDC, sm.Vt + 16 * tv * LDC, LDC, 0, C);
+                    for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
-        }
+            mma_nt_blk<SB::BR, C>(accS[pb], KA + 16 * ti0 * LDC, LDC, sm.Kt + 16 * tj0 * LDC, LDC);
+#pragma unroll
+            for (int x = 0; x < SB::BR; ++x)
+#pragma unroll
+                for (int y = 0; y < SB::BR; ++y)
+                    store4(sm.St + (16 * (tj0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accS[pb][x][y]);
+        });
+        for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
+            if (DECAY) {
+#pragma unroll
+                for (int x = 0; x < WB::BR; ++x)
+#pragma unroll
+                    for (int y = 0; y < WB::BR; ++y) {
+                        accW[pb][x][y] *= gc2;
+                        accC[pb][x][y] *= gc;
+                    }
+            }
+            mma_nt_blk<WB::BR, C>(accW[pb], sm.Ztw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+            mma_nt_blk<WB::BR, C>(accC[pb], sm.Qtw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+        });
         for (int i = threadIdx.x; i < D; i += NT) {
             sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
             sm.m0[i] = gc * sm.m0[i] + row_sum<T, C>(sm.Qtw, LDC, i);
@@ -454,28 +488,18 @@ void hla2_summary_kernel(FwdParams p) {
 
     // summary [X = S | Y = C | N = W | y = m | nv = u]
     float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
+    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
-    for (int s = 0; s < G::PS; ++s) {
-        const int t = w + s * NW;
-        if (t < G::TS) {
-            const int ti = t / nTD, tj = t % nTD;
+        for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];
+    });
+    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[s][i];
+        for (int i = 0; i < 4; ++i) {
+            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+            e[D * D + idx] = accC[pb][x][y][i];
+            e[D * D + D * DV + idx] = accW[pb][x][y][i];
         }
-    }
-#pragma unroll
-    for (int s = 0; s < G::PW; ++s) {
-        const int t = w + s * NW;
-        if (t < G::TW) {
-            const int ti = t / nTV, tv = t % nTV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-                e[D * D + idx] = accC[s][i];
-                e[D * D + D * DV + idx] = accW[s][i];
-            }
-        }
-    }
+    });
     for (int i = threadIdx.x; i < D; i += NT) {
         e[D * D + 2 * D * DV + i] = sm.m0[i];
         e[D * D + 2 * D * DV + D + i] = sm.u0[i];
