@@ -69,6 +69,21 @@ struct ChunkRegs {
             if (idx < NVEC) store16(dst + (idx % C) * ld + (idx / C) * VE, get(i));
         }
     }
+    // dst[r][c] = src[r][c] * w, w = gp[wofs - r] for r <= wofs, else 0
+    __device__ __forceinline__ void store_rows_w(T *dst, int ld, const float *gp, int wofs) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) {
+                const int r = idx % C;
+                const float wr = r <= wofs ? gp[wofs - r] : 0.f;
+                Vec16<T> x = get(i);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(to_f(x.v[e]) * wr);
+                store16(dst + r * ld + (idx / C) * VE, x);
+            }
+        }
+    }
     // dstT[c][r] (transposed, leading dim ld)
     __device__ __forceinline__ void store_cols(T *dstT, int ld) const {
 #pragma unroll

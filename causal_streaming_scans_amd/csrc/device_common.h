@@ -88,10 +88,40 @@ __device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const float *A, int lda, cons
 // once and reused: lane l holds row l%16 at the k offsets both operand
 // slots of mma_nt use (A and Bt fragments are addressed alike).
 template <typename T, int K> struct RowFrags;
+//
+// load_rows_g reads the 16 rows straight from global memory: lane l reads
+// row l%16 when that row is below rows_valid and row 0 (which the caller
+// guarantees to exist) otherwise, so the load is unconditional and in
+// bounds; mask_rows later zeroes the rows at or past rows_valid.
 template <int K> struct RowFrags<bf16, K> {
     static constexpr bool W32 = (K % 32) == 0;
     bf16x8 v8[W32 ? K / 32 : 1];
     i16x4 v4[W32 ? 1 : K / 16];
+    __device__ __forceinline__ void load_rows_g(const bf16 *__restrict__ base, int ld,
+                                                int rows_valid) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+        const bf16 *row = base + (size_t)(r < rows_valid ? r : 0) * ld;
+        if constexpr (W32) {
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s)
+                v8[s] = *reinterpret_cast<const bf16x8 *>(row + 32 * s + 8 * g);
+        } else {
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                v4[s] = *reinterpret_cast<const i16x4 *>(row + 16 * s + 4 * g);
+        }
+    }
+    __device__ __forceinline__ void mask_rows(int rows_valid) {
+        if ((lane_id() & 15) >= rows_valid) {
+            if constexpr (W32) {
+#pragma unroll
+                for (int s = 0; s < K / 32; ++s) v8[s] = bf16x8{};
+            } else {
+#pragma unroll
+                for (int s = 0; s < K / 16; ++s) v4[s] = i16x4{};
+            }
+        }
+    }
     __device__ __forceinline__ void load(const bf16 *base, int ld) {
         const int l = lane_id(), r = l & 15, g = l >> 4;
         if constexpr (W32) {
@@ -107,6 +137,19 @@ template <int K> struct RowFrags<bf16, K> {
 };
 template <int K> struct RowFrags<float, K> {
     float v[K / 4];
+    __device__ __forceinline__ void load_rows_g(const float *__restrict__ base, int ld,
+                                                int rows_valid) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+        const float *row = base + (size_t)(r < rows_valid ? r : 0) * ld;
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) v[s] = row[4 * s + g];
+    }
+    __device__ __forceinline__ void mask_rows(int rows_valid) {
+        if ((lane_id() & 15) >= rows_valid) {
+#pragma unroll
+            for (int s = 0; s < K / 4; ++s) v[s] = 0.f;
+        }
+    }
     __device__ __forceinline__ void load(const float *base, int ld) {
         const int l = lane_id(), r = l & 15, g = l >> 4;
 #pragma unroll
@@ -292,6 +335,102 @@ __device__ __forceinline__ Frag16<bf16> ld_frag(const bf16 *base, int ld) {
 __device__ __forceinline__ Frag16<float> ld_frag(const float *base, int ld) {
     const int l = lane_id();
     return Frag16<float>{*reinterpret_cast<const f32x4 *>(base + (l & 15) * ld + ((l >> 4) << 2))};
+}
+
+// ------------------------------------------------ k-major operands (gfx950)
+//
+// Products that contract over the row index of an LDS matrix M[k][m] (m
+// contiguous) -- the token index of a row-major chunk tile -- read their
+// operands with DS_READ_B64_TR_B16.  That instruction transposes within each
+// 16-lane group: when lane s of group g names the 8 bytes at
+// M[4g + s/4][4(s%4) .. 4(s%4)+3], lane i of the group receives M[4g + e][i]
+// in slot e, i.e. the operand layout "row i, k = 4g + e" that the MFMA
+// instructions take.  No transposed copy of the tile is ever stored.
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const bf16 *p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<bf16 *>(p)));
+}
+
+// Operand fragment of rows m0..m0+15, k = k0..k0+15 of M[k][m]; M points at
+// M[k0][m0].  Lane l gets M[k0 + 4g + e][m0 + l%16] in slot e.
+__device__ __forceinline__ Frag16<bf16> ld_frag_t(const bf16 *M, int ld) {
+    const int l = lane_id(), g = l >> 4, s = l & 15;
+    return Frag16<bf16>{ds_read_tr16(M + (4 * g + (s >> 2)) * ld + 4 * (s & 3))};
+}
+__device__ __forceinline__ Frag16<float> ld_frag_t(const float *M, int ld) {
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = M[(4 * g + i) * ld + c];
+    return Frag16<float>{v};
+}
+
+// 16x16x32 operand from M[k][m]: slot j holds k = k0 + 8g + j (the slot
+// order of a contiguous 16-byte load, so it pairs with either kind).
+__device__ __forceinline__ bf16x8 ld_op8_t(const bf16 *M, int ld) {
+    const int l = lane_id(), g = l >> 4, s = l & 15;
+    const bf16 *p = M + (8 * g + (s >> 2)) * ld + 4 * (s & 3);
+    const i16x4 lo = ds_read_tr16(p), hi = ds_read_tr16(p + 4 * ld);
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// A BR x BR block of 16x16 tiles contracting over the rows of two k-major
+// LDS matrices: acc[x][y] += sum_k A[k][16x + i] * B[k][16y + j], k = 0..K.
+template <int BR, int K>
+__device__ __forceinline__ void mma_tn_blk(f32x4 (&acc)[BR][BR], const bf16 *A, int lda,
+                                           const bf16 *B, int ldb) {
+    if constexpr (K % 32 == 0) {
+#pragma unroll
+        for (int k = 0; k < K; k += 32) {
+            bf16x8 a[BR], b[BR];
+#pragma unroll
+            for (int x = 0; x < BR; ++x) {
+                a[x] = ld_op8_t(A + k * lda + 16 * x, lda);
+                b[x] = ld_op8_t(B + k * ldb + 16 * x, ldb);
+            }
+#pragma unroll
+            for (int x = 0; x < BR; ++x)
+#pragma unroll
+                for (int y = 0; y < BR; ++y)
+                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; k += 16) {
+            Frag16<bf16> a[BR], b[BR];
+#pragma unroll
+            for (int x = 0; x < BR; ++x) {
+                a[x] = ld_frag_t(A + k * lda + 16 * x, lda);
+                b[x] = ld_frag_t(B + k * ldb + 16 * x, ldb);
+            }
+#pragma unroll
+            for (int x = 0; x < BR; ++x)
+#pragma unroll
+                for (int y = 0; y < BR; ++y) acc[x][y] = mma16(acc[x][y], a[x], b[y]);
+        }
+    }
+}
+template <int BR, int K>
+__device__ __forceinline__ void mma_tn_blk(f32x4 (&acc)[BR][BR], const float *A, int lda,
+                                           const float *B, int ldb) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll 4
+    for (int k = 0; k < K; k += 4) {
+        float a[BR], b[BR];
+#pragma unroll
+        for (int x = 0; x < BR; ++x) {
+            a[x] = A[(k + g) * lda + 16 * x + r];
+            b[x] = B[(k + g) * ldb + 16 * x + r];
+        }
+#pragma unroll
+        for (int x = 0; x < BR; ++x)
+#pragma unroll
+            for (int y = 0; y < BR; ++y)
+                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
 }
 
 // Store four consecutive T values (one accumulator's slots, converted).

@@ -28,12 +28,20 @@
 // (L^T = K Q^T), so the accumulator is directly the operand of K^T L^T (for
 // Z^T) without an LDS round trip; likewise P^T = Z Q^T feeds V^T P^T (for
 // O^T).  O^T's accumulator holds four consecutive output features of one
-// token, so the output is written straight from registers.  Z goes through
-// LDS (row-major for P, and decay-weighted transposed for the W update),
-// since every row tile needs all earlier rows of it.  The fp32 state S0, W0
-// is spread over all waves as MFMA accumulators for the whole segment; its
-// T-typed transposed copy in LDS is the operand of Q S0 and Q W0.  The next
-// chunk's Q, K, V are loaded into registers while the current one computes.
+// token, so the output is written straight from registers.
+//
+// LDS holds chunk tiles row-major only ([token][feature]).  Every product
+// that contracts over the tokens (K^T L^T, V^T P^T, the state updates) reads
+// its operands with the transposing LDS read, so no transposed copy is ever
+// written.  The forward kernel's Q never enters LDS: each wave reads its own
+// 16 query rows from global memory into operand registers, a chunk ahead.
+// V is widened by one 16-column tile whose first column is all ones: the
+// same products then give u = Z^T 1 (column DV of the widened W) and the
+// ratio denominator Q u0 + P 1 (column DV of the widened O), and m = Q^T 1
+// in the summary kernel.  The fp32 state S0, W0 (and u0) is spread over all
+// waves as MFMA accumulators for the whole segment; its T-typed transposed
+// copy in LDS is the operand of Q S0 and Q W0.  Z goes through LDS, since
+// every row tile needs all earlier rows of it.
 #pragma once
 
 #include "chunk_common.h"
@@ -44,11 +52,13 @@ template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2Cfg {
     using WS = WaveShape<C, D>;
     static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
+    static constexpr int DVX = DV + 16;       // V, W widened by the ones / u column tile
     static constexpr int LDD = ld_of<T>(D);   // rows of length D
-    static constexpr int LDC = ld_of<T>(C);   // rows of length C
+    static constexpr int LDV = ld_of<T>(DVX); // rows of the widened V
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int ZJ = (nTD + NCG - 1) / NCG;    // Z^T tiles per wave
     static constexpr int OJ = (nTV + NCG - 1) / NCG;    // O^T tiles per wave
+    static constexpr int UJ = (nTD + NW - 1) / NW;      // tiles of the u (m) column per wave
     using SB = TileBlocks<nTD, nTD, NW>;    // ownership of S tiles
     using WB = TileBlocks<nTD, nTV, NW>;    // ownership of W (and C) tiles
     static constexpr int SUMF = summary_floats(D, DV);
@@ -82,20 +92,42 @@ __device__ __forceinline__ void for_blocks(int w, F f) {
         if (blk < TB::NB) f(pb, (blk / TB::nBC) * TB::BR, (blk % TB::nBC) * TB::BR);
     }
 }
+// The row tiles ti of a single 16-column stripe a wave owns: f(j, ti).
+template <int UJ, int NW, int NTILE, typename F>
+__device__ __forceinline__ void for_stripe(int w, F f) {
+#pragma unroll
+    for (int j = 0; j < UJ; ++j) {
+        const int ti = w + j * NW;
+        if (ti < NTILE) f(j, ti);
+    }
+}
+
+// Columns DV..DV+15 of the widened V: (1, 0, ..., 0) in every row.  Staging
+// never writes them, so they are set once.
+template <typename T, int C, int LDV, int DV, int NT>
+__device__ __forceinline__ void init_ones_column(T *V) {
+    for (int i = threadIdx.x; i < C * 16; i += NT)
+        V[(i / 16) * LDV + DV + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
+}
+
+// acc += A^T B over the C token rows for one 16x16 tile (k-major operands)
+template <int C, typename T>
+__device__ __forceinline__ f32x4 mma_tn_tile(f32x4 acc, const T *A, int lda, const T *B, int ldb) {
+    f32x4 a[1][1] = {{acc}};
+    mma_tn_blk<1, C>(a, A, lda, B, ldb);
+    return a[0][0];
+}
 
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2FwdSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
-    alignas(16) T Q[C * G::LDD];
     alignas(16) T K[C * G::LDD];
-    alignas(16) T Kt[D * G::LDC];
-    alignas(16) T Ktw[DECAY ? D * G::LDC : 8];   // K^T weighted by g^(c-1-tau)
-    alignas(16) T Vt[DV * G::LDC];
+    alignas(16) T Kw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(c-1-tau)
+    alignas(16) T V[C * G::LDV];                 // widened: columns DV.. = (1, 0, ..)
     alignas(16) T Z[C * G::LDD];
-    alignas(16) T Ztw[D * G::LDC];               // Z^T weighted by g^(2(c-1-tau))
+    alignas(16) T Zw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(2(c-1-tau))
     alignas(16) T St[D * G::LDD];                // St[j][i] = S0[i][j]
-    alignas(16) T Wt[DV * G::LDD];               // Wt[j][i] = W0[i][j]
-    float u0[D];
+    alignas(16) T Wt[G::DVX * G::LDD];           // Wt[j][i] = W0[i][j]; row DV = u0
     float gp[G::NPOW];
 };
 
@@ -103,21 +135,35 @@ template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     alignas(16) T Q[C * G::LDD];
+    alignas(16) T Qw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(c-1-tau)
     alignas(16) T K[C * G::LDD];
-    alignas(16) T Kt[D * G::LDC];
-    alignas(16) T Ktw[DECAY ? D * G::LDC : 8];
-    alignas(16) T Qtw[D * G::LDC];               // Q^T weighted by g^(c-1-tau)
-    alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T Ztw[D * G::LDC];
+    alignas(16) T Kw[DECAY ? C * G::LDD : 8];
+    alignas(16) T V[C * G::LDV];
+    alignas(16) T Z[C * G::LDD];                 // rows weighted by g^(2(c-1-tau))
     alignas(16) T St[D * G::LDD];
-    float u0[D];
-    float m0[D];
     float gp[G::NPOW];
 };
 
 template <int NT, int NW, int D, int DV>
 constexpr int hla2_min_blocks() {
     return (D <= 64 && DV <= 64 && NT <= 256) ? 2 : 1;
+}
+
+// Workgroups per CU the kernel is built for: as many as the LDS allows, up
+// to 3 (12 waves of 256-thread groups, 168 VGPRs each).
+template <int NT, int SMEM>
+constexpr int hla_min_blocks() {
+    const int by_lds = (160 * 1024) / SMEM;
+    const int cap = NT <= 256 ? 3 : 1;
+    return by_lds < 1 ? 1 : (by_lds < cap ? by_lds : cap);
+}
+template <typename T, int D, int DV, int C, bool DECAY>
+constexpr int hla2_fwd_blocks() {
+    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdSmem<T, D, DV, C, DECAY>)>();
+}
+template <typename T, int D, int DV, int C, bool DECAY>
+constexpr int hla2_sum_blocks() {
+    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2SumSmem<T, D, DV, C, DECAY>)>();
 }
 
 // L^T tiles of row tile r as operand fragments: Lf[s] holds
@@ -142,15 +188,38 @@ __device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[RT], const T *K, const 
     }
 }
 
+// Z^T tiles of row tile r: Z = diag(g^(tau+1)) Q S0 + L K, stored row-major
+// (times w) into Zd.  Shared by the forward and summary kernels.
+template <typename T, int D, int C, int RT, int NCG, int ZJ, int LDD, bool DECAY>
+__device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[RT],
+                                        const T *St, const T *K, T *Zd, T *Zwd, float wz,
+                                        const float *gp, int r, int cg, int tau) {
+    const int g4 = (lane_id() >> 4) << 2;
+#pragma unroll
+    for (int jj = 0; jj < ZJ; ++jj) {
+        const int jt = cg + jj * NCG;
+        if (jt < D / 16) {
+            f32x4 z = mma_nt_f(zero4(), St + 16 * jt * LDD, LDD, qf);
+            f32x4 zc = zero4();
+#pragma unroll
+            for (int s = 0; s < RT; ++s)
+                if (s <= r) zc = mma16(zc, ld_frag_t(K + 16 * s * LDD + 16 * jt, LDD), Lf[s]);
+            z = (DECAY ? z * gp[tau + 1] : z) + zc;
+            if (Zd) store4(Zd + tau * LDD + 16 * jt + g4, z);
+            if (Zwd) store4(Zwd + tau * LDD + 16 * jt + g4, z * wz);
+        }
+    }
+}
+
 // ------------------------------------------------------------ forward kernel
 
 template <typename T, int D, int DV, int C, bool DECAY>
 __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
-                             (hla2_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, 0, D, DV>()))
+                             (hla2_fwd_blocks<T, D, DV, C, DECAY>()))
 void hla2_forward_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
     __shared__ Hla2FwdSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -161,12 +230,16 @@ void hla2_forward_kernel(FwdParams p) {
     const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
+    const bool ratio = p.ratio != 0;
+    const bool last = seg == p.nseg - 1;
+    const bool need_u = ratio || (p.state_out != nullptr && last);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
 
     if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
 
     // carried state at the start of this segment: the exclusive prefix from
     // the scan, or the caller's state, or zero
@@ -184,7 +257,7 @@ void hla2_forward_kernel(FwdParams p) {
     }
     using SB = typename G::SB;
     using WB = typename G::WB;
-    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR];
+    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accU[G::UJ];
     for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
         f32x4 a;
 #pragma unroll
@@ -199,59 +272,52 @@ void hla2_forward_kernel(FwdParams p) {
         accW[pb][x][y] = a;
         store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, a);
     });
-    for (int i = threadIdx.x; i < D; i += NT) sm.u0[i] = u0 ? u0[i] : 0.f;
+    // u0 as column DV of the widened W (the other 15 columns stay zero)
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        f32x4 a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
+        accU[j] = a;
+        store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, a);
+    });
 
-    ChunkRegs<T, C, D, NT> rq, rk;
+    // next chunk's data in registers: K, V for LDS; this wave's Q rows
+    ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
+    RowFrags<T, D> qn;
+    auto load_chunk = [&](int c, int valid) {
+        const int tv = valid - 16 * r;     // valid rows of this wave's tile
+        qn.load_rows_g(q + (size_t)(c + (tv > 0 ? 16 * r : 0)) * D, D, tv > 0 ? tv : 0);
+        rk.load(k + (size_t)c * D, valid);
+        rv.load(v + (size_t)c * DV, valid);
+    };
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
-    rq.load(q + (size_t)c0 * D, cv);
-    rk.load(k + (size_t)c0 * D, cv);
-    rv.load(v + (size_t)c0 * DV, cv);
+    load_chunk(c0, cv);
 
     while (c0 < t_end) {
         __syncthreads();   // previous chunk's readers are done; setup is visible
         // ---- a-1: stage this chunk, then start loading the next one
-        rq.store_rows(sm.Q, LDD);
         rk.store_rows(sm.K, LDD);
-        rk.store_cols(sm.Kt, LDC);
-        if (DECAY) rk.store_cols_w(sm.Ktw, LDC, sm.gp, cv - 1);
-        rv.store_cols(sm.Vt, LDC);
+        if (DECAY) rk.store_rows_w(sm.Kw, LDD, sm.gp, cv - 1);
+        rv.store_rows(sm.V, LDV);
+        RowFrags<T, D> qf = qn;            // the row tile's Q: operand of four products
+        qf.mask_rows(cv - 16 * r);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
-        if (n0 < t_end) {
-            rq.load(q + (size_t)n0 * D, ncv);
-            rk.load(k + (size_t)n0 * D, ncv);
-            rv.load(v + (size_t)n0 * DV, ncv);
-        }
+        if (n0 < t_end) load_chunk(n0, ncv);
         __syncthreads();
 
-        // the row tile's Q, kept in registers: an operand of four products
-        RowFrags<T, D> qf;
-        qf.load(sm.Q + 16 * r * LDD, LDD);
         // ---- a-2: L^T for this row tile, as operand fragments
         Frag16<T> Lf[RT];
         scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
 
         // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
-        const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
-#pragma unroll
-        for (int jj = 0; jj < G::ZJ; ++jj) {
-            const int jt = cg + jj * NCG;
-            if (jt < nTD) {
-                f32x4 z = mma_nt_f(zero4(), sm.St + 16 * jt * LDD, LDD, qf);
-                f32x4 zc = zero4();
-#pragma unroll
-                for (int s = 0; s < RT; ++s)
-                    if (s <= r) zc = mma16(zc, ld_frag(sm.Kt + 16 * jt * LDC + 16 * s, LDC), Lf[s]);
-                z = (DECAY ? z * sm.gp[tau + 1] : z) + zc;
-                store4(sm.Z + tau * LDD + 16 * jt + g4, z);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.Ztw[(16 * jt + g4 + i) * LDC + tau] = from_f<T>(z[i] * wz);
-            }
-        }
-        // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T, den = that for u0
+        const float wz = DECAY ? (tau < cv ? sm.gp[2 * (cv - 1 - tau)] : 0.f) : 1.f;
+        z_tiles<T, D, C, RT, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, sm.Z,
+                                                     DECAY ? sm.Zw : nullptr, wz, sm.gp, r, cg, tau);
+        // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T; the
+        // denominator's carried part q . u0 is row DV of the widened product
         f32x4 accO[G::OJ];
 #pragma unroll
         for (int jj = 0; jj < G::OJ; ++jj) {
@@ -262,25 +328,25 @@ void hla2_forward_kernel(FwdParams p) {
                 if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
             }
         }
-        float den = 0.f;
-        if (p.ratio) {
-            den = lane_dot<T, D>(sm.Q + tau * LDD, sm.u0);
-            if (DECAY) den *= sm.gp[2 * (tau + 1)];
+        f32x4 accD = zero4();
+        if (ratio) {
+            accD = mma_nt_f(zero4(), sm.Wt + DV * LDD, LDD, qf);
+            if (DECAY) accD *= sm.gp[2 * (tau + 1)];
         }
         __syncthreads();
 
         // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
         Frag16<T> Pf[RT];
         scores_t<T, D, RT, LDD, DECAY>(Pf, sm.Z, qf, r, tau, sm.gp, 2);
-        if (p.ratio) {
-            float rs = 0.f;
+        float rden = 1.f;
+        if (ratio) {
+            // den = q . u0 + P 1: row DV of the widened O^T, held in slot 0 of
+            // the token's lane in group 0
+            f32x4 dc = zero4();
 #pragma unroll
             for (int s = 0; s < RT; ++s)
-                if (s <= r) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rs += frag_val(Pf[s], i);
-                }
-            den += sum_groups(rs);
+                if (s <= r) dc = mma16(dc, ld_frag_t(sm.V + 16 * s * LDV + DV, LDV), Pf[s]);
+            rden = 1.f / __shfl(accD[0] + dc[0], col);
         }
 #pragma unroll
         for (int jj = 0; jj < G::OJ; ++jj) {
@@ -289,9 +355,9 @@ void hla2_forward_kernel(FwdParams p) {
                 f32x4 oc = zero4();
 #pragma unroll
                 for (int s = 0; s < RT; ++s)
-                    if (s <= r) oc = mma16(oc, ld_frag(sm.Vt + 16 * jv * LDC + 16 * s, LDC), Pf[s]);
+                    if (s <= r) oc = mma16(oc, ld_frag_t(sm.V + 16 * s * LDV + 16 * jv, LDV), Pf[s]);
                 f32x4 ov = accO[jj] + oc;
-                if (p.ratio) ov *= 1.f / den;
+                if (ratio) ov *= rden;
                 if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
             }
         }
@@ -299,7 +365,8 @@ void hla2_forward_kernel(FwdParams p) {
         // ---- a-7: advance the carried state by this chunk
         const float gc = DECAY ? sm.gp[cv] : 1.f;
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
-        const T *KA = DECAY ? sm.Ktw : sm.Kt;
+        const T *KA = DECAY ? sm.Kw : sm.K;
+        const T *ZA = DECAY ? sm.Zw : sm.Z;
         for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
             if (DECAY) {
 #pragma unroll
@@ -307,7 +374,7 @@ void hla2_forward_kernel(FwdParams p) {
 #pragma unroll
                     for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
-            mma_nt_blk<SB::BR, C>(accS[pb], KA + 16 * ti0 * LDC, LDC, sm.Kt + 16 * tj0 * LDC, LDC);
+            mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
 #pragma unroll
             for (int x = 0; x < SB::BR; ++x)
 #pragma unroll
@@ -321,20 +388,25 @@ void hla2_forward_kernel(FwdParams p) {
 #pragma unroll
                     for (int y = 0; y < WB::BR; ++y) accW[pb][x][y] *= gc2;
             }
-            mma_nt_blk<WB::BR, C>(accW[pb], sm.Ztw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+            mma_tn_blk<WB::BR, C>(accW[pb], ZA + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
 #pragma unroll
             for (int x = 0; x < WB::BR; ++x)
 #pragma unroll
                 for (int y = 0; y < WB::BR; ++y)
                     store4(sm.Wt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accW[pb][x][y]);
         });
-        for (int i = threadIdx.x; i < D; i += NT)
-            sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
+        if (need_u) {
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], ZA + 16 * ti, LDD,
+                                         sm.V + DV, LDV);
+                store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, accU[j]);
+            });
+        }
         c0 = n0;
         cv = ncv;
     }
 
-    if (p.state_out && seg == p.nseg - 1) {
+    if (p.state_out && last) {
         float *so = p.state_out + (size_t)bh * G::STF;
         for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
@@ -346,8 +418,12 @@ void hla2_forward_kernel(FwdParams p) {
             for (int i = 0; i < 4; ++i)
                 so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = accW[pb][x][y][i];
         });
-        __syncthreads();
-        for (int i = threadIdx.x; i < D; i += NT) so[D * D + D * DV + i] = sm.u0[i];
+        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+            if (col == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) so[D * D + D * DV + 16 * ti + g4 + i] = accU[j][i];
+            }
+        });
     }
 }
 
@@ -355,11 +431,11 @@ void hla2_forward_kernel(FwdParams p) {
 
 template <typename T, int D, int DV, int C, bool DECAY>
 __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
-                             (hla2_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, 0, D, DV>()))
+                             (hla2_sum_blocks<T, D, DV, C, DECAY>()))
 void hla2_summary_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD;
     __shared__ Hla2SumSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -375,9 +451,11 @@ void hla2_summary_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
     if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
     using SB = typename G::SB;
     using WB = typename G::WB;
     f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accC[WB::PB][WB::BR][WB::BR];
+    f32x4 accU[G::UJ], accM[G::UJ];
 #pragma unroll
     for (int pb = 0; pb < SB::PB; ++pb)
 #pragma unroll
@@ -393,11 +471,12 @@ void hla2_summary_kernel(FwdParams p) {
                 accW[pb][x][y] = zero4();
                 accC[pb][x][y] = zero4();
             }
-    for (int i = threadIdx.x; i < D * LDD; i += NT) sm.St[i] = from_f<T>(0.f);
-    for (int i = threadIdx.x; i < D; i += NT) {
-        sm.u0[i] = 0.f;
-        sm.m0[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::UJ; ++j) {
+        accU[j] = zero4();
+        accM[j] = zero4();
     }
+    for (int i = threadIdx.x; i < D * LDD; i += NT) sm.St[i] = from_f<T>(0.f);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -410,12 +489,10 @@ void hla2_summary_kernel(FwdParams p) {
     while (c0 < t_end) {
         __syncthreads();
         rq.store_rows(sm.Q, LDD);
-        if (DECAY) rq.store_cols_w(sm.Qtw, LDC, sm.gp, cv - 1);
-        else rq.store_cols(sm.Qtw, LDC);
+        if (DECAY) rq.store_rows_w(sm.Qw, LDD, sm.gp, cv - 1);
         rk.store_rows(sm.K, LDD);
-        rk.store_cols(sm.Kt, LDC);
-        if (DECAY) rk.store_cols_w(sm.Ktw, LDC, sm.gp, cv - 1);
-        rv.store_cols(sm.Vt, LDC);
+        if (DECAY) rk.store_rows_w(sm.Kw, LDD, sm.gp, cv - 1);
+        rv.store_rows(sm.V, LDV);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
         if (n0 < t_end) {
@@ -429,27 +506,16 @@ void hla2_summary_kernel(FwdParams p) {
         qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
         scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
+        // Z rows weighted by g^(2(c-1-tau)): only the W and u updates use Z here
         const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
-#pragma unroll
-        for (int jj = 0; jj < G::ZJ; ++jj) {
-            const int jt = cg + jj * NCG;
-            if (jt < nTD) {
-                f32x4 z = mma_nt_f(zero4(), sm.St + 16 * jt * LDD, LDD, qf);
-                f32x4 zc = zero4();
-#pragma unroll
-                for (int s = 0; s < RT; ++s)
-                    if (s <= r) zc = mma16(zc, ld_frag(sm.Kt + 16 * jt * LDC + 16 * s, LDC), Lf[s]);
-                z = (DECAY ? z * sm.gp[tau + 1] : z) + zc;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sm.Ztw[(16 * jt + g4 + i) * LDC + tau] = from_f<T>(z[i] * wz);
-            }
-        }
+        z_tiles<T, D, C, RT, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz,
+                                                     sm.gp, r, cg, tau);
         __syncthreads();
 
         const float gc = DECAY ? sm.gp[cv] : 1.f;
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
-        const T *KA = DECAY ? sm.Ktw : sm.Kt;
+        const T *KA = DECAY ? sm.Kw : sm.K;
+        const T *QA = DECAY ? sm.Qw : sm.Q;
         for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
             if (DECAY) {
 #pragma unroll
@@ -457,7 +523,7 @@ void hla2_summary_kernel(FwdParams p) {
 #pragma unroll
                     for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
-            mma_nt_blk<SB::BR, C>(accS[pb], KA + 16 * ti0 * LDC, LDC, sm.Kt + 16 * tj0 * LDC, LDC);
+            mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
 #pragma unroll
             for (int x = 0; x < SB::BR; ++x)
 #pragma unroll
@@ -474,17 +540,17 @@ void hla2_summary_kernel(FwdParams p) {
                         accC[pb][x][y] *= gc;
                     }
             }
-            mma_nt_blk<WB::BR, C>(accW[pb], sm.Ztw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
-            mma_nt_blk<WB::BR, C>(accC[pb], sm.Qtw + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
+            mma_tn_blk<WB::BR, C>(accW[pb], sm.Z + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
+            mma_tn_blk<WB::BR, C>(accC[pb], QA + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
         });
-        for (int i = threadIdx.x; i < D; i += NT) {
-            sm.u0[i] = gc2 * sm.u0[i] + row_sum<T, C>(sm.Ztw, LDC, i);
-            sm.m0[i] = gc * sm.m0[i] + row_sum<T, C>(sm.Qtw, LDC, i);
-        }
+        // u = Z^T 1 and m = Q^T 1: the ones column of the widened V
+        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+            accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], sm.Z + 16 * ti, LDD, sm.V + DV, LDV);
+            accM[j] = mma_tn_tile<C>(DECAY ? accM[j] * gc : accM[j], QA + 16 * ti, LDD, sm.V + DV, LDV);
+        });
         c0 = n0;
         cv = ncv;
     }
-    __syncthreads();
 
     // summary [X = S | Y = C | N = W | y = m | nv = u]
     float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
@@ -500,10 +566,15 @@ void hla2_summary_kernel(FwdParams p) {
             e[D * D + D * DV + idx] = accW[pb][x][y][i];
         }
     });
-    for (int i = threadIdx.x; i < D; i += NT) {
-        e[D * D + 2 * D * DV + i] = sm.m0[i];
-        e[D * D + 2 * D * DV + D + i] = sm.u0[i];
-    }
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        if (col == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[D * D + 2 * D * DV + 16 * ti + g4 + i] = accM[j][i];
+                e[D * D + 2 * D * DV + D + 16 * ti + g4 + i] = accU[j][i];
+            }
+        }
+    });
 }
 
 }  // namespace hla

@@ -121,9 +121,8 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  *
  * Supported (otherwise HLA_ERR_UNSUPPORTED): d == dv;
  *   HLA_BF16: d in {16, 32, 64} with chunk 16, 32 or 64; d = 128 with chunk
- *             16 or 32;
- *   HLA_F32:  d in {16, 32} with chunk 16, 32 or 64; d = 64 with chunk 16 or
- *             32.
+ *             16 or 32 (AHLA variants also chunk 64);
+ *   HLA_F32:  d in {16, 32, 64} with chunk 16, 32 or 64.
  */
 hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        int B, int H, int n, int d, int dv, int dtype, int variant,

@@ -61,6 +61,31 @@ def test_forward_matches_oracle(case):
     assert err < TOL[dtype]
 
 
+# Every kernel instance the library ships: (dtype, d, chunk) for each family.
+SUPPORT = [(dt, d, c, fam)
+           for dt, dims in (("f32", (16, 32, 64)), ("bf16", (16, 32, 64, 128)))
+           for d in dims for c in (16, 32, 64) for fam in ("hla2", "ahla")
+           if not (dt == "bf16" and d == 128 and c == 64 and fam == "hla2")]
+
+
+@pytest.mark.parametrize("case", SUPPORT, ids=lambda c: "-".join(str(x) for x in c))
+def test_support_matrix(case):
+    """One small ragged, multi-segment case per kernel instance: HLA-2 with a
+    per-head decay and the ratio form, AHLA with the ratio form."""
+    dtype, d, chunk, fam = case
+    variant = fam + "_ratio"
+    B, H, seg = 1, 2, 2
+    n = 2 * chunk * seg + chunk // 2 + 3
+    say(f"[support] {case} n={n}")
+    x = _inputs(B, H, n, d, dtype, "uniform_pos", seed=5000 + d + chunk, decay=fam == "hla2")
+    got = gpu_forward(x, variant, B, H, dtype, chunk, seg, gamma=x["gamma"])
+    want = oracle_forward(x, variant, H, gamma=x["gamma"])
+    err = rel_l2(got, want)
+    say(f"   rel_l2 {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err < TOL[dtype]
+
+
 @pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_state_out_and_resume(variant, dtype):
