@@ -16,11 +16,16 @@
 // M = sum_t k_t q_t^T, the factor the segment combine's cross term M_B P_A
 // needs.
 //
-// Work split as for HLA-2: wave (r, cg) owns row tile r and column tiles cg,
-// cg + NCG, ...  The transposed scores L^T = K Q^T serve twice from
-// registers: as the A operand of L V (rows tau) and as the B operand of
-// Y^T L^T (for O^T).  Y is written to LDS transposed (for Y^T L^T and
-// K^T Y), O^T goes straight to global memory.
+// Work split and LDS layout as for HLA-2: wave (r, cg) owns row tile r and
+// column tiles cg, cg + NCG, ...; chunk tiles sit in LDS row-major and every
+// product over the tokens reads them through the transposing LDS read.  The
+// transposed scores L^T = K Q^T stay in registers and serve as the B operand
+// of V^T L^T (for Y^T) and of Y^T L^T (for O^T).  Y^T's accumulator holds
+// four consecutive features of one token, so Y goes to LDS row-major with
+// one 8-byte store per tile.  V and Y are widened by a ones / y1 column tile
+// and P, E by the matching mK / nk column: the same products then give
+// y1 = Q mK0 + L 1 (column DV of Y), the ratio denominator Q nk0 + L y1
+// (column DV of O), mK += K^T 1 and nk += K^T y1.
 #pragma once
 
 #include "chunk_common.h"
@@ -32,97 +37,94 @@ template <typename T, int D, int DV, int C>
 struct AhlaCfg {
     using WS = WaveShape<C, D>;
     static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
-    static constexpr int LDD = ld_of<T>(D), LDC = ld_of<T>(C);
+    static constexpr int DVX = DV + 16;       // V, Y, P, E widened by one column tile
+    static constexpr int LDD = ld_of<T>(D), LDV = ld_of<T>(DVX);
     static constexpr int nTD = D / 16, nTV = DV / 16;
-    static constexpr int OJ = (nTV + NCG - 1) / NCG;      // Y / O^T tiles per wave
+    static constexpr int OJ = (nTV + NCG - 1) / NCG;      // O^T tiles per wave
+    static constexpr int YJ = (nTV + 1 + NCG - 1) / NCG;  // Y^T tiles per wave, widened
+    static constexpr int UJ = (nTD + NW - 1) / NW;        // mK / nk column tiles per wave
     using PBk = TileBlocks<nTD, nTV, NW>;   // ownership of P, E tiles
     using MBk = TileBlocks<nTD, nTD, NW>;   // ownership of M tiles
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = ahla_state_floats(D, DV);
+    static_assert(D % 16 == 0 && DV % 16 == 0 && C % 16 == 0, "tile multiples");
 };
 
 template <typename T, int D, int DV, int C>
 struct AhlaFwdSmem {
     using G = AhlaCfg<T, D, DV, C>;
-    alignas(16) T Q[C * G::LDD];
     alignas(16) T K[C * G::LDD];
-    alignas(16) T Kt[D * G::LDC];
-    alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T Yt[DV * G::LDC];
-    alignas(16) T Pt[DV * G::LDD];     // Pt[j][i] = P0[i][j]
-    alignas(16) T Et[DV * G::LDD];     // Et[j][i] = E0[i][j]
-    float mK[D], nk[D], y1[C];
+    alignas(16) T V[C * G::LDV];       // widened: columns DV.. = (1, 0, ..)
+    alignas(16) T Y[C * G::LDV];       // widened: column DV = y1
+    alignas(16) T Pt[G::DVX * G::LDD]; // Pt[j][i] = P0[i][j]; row DV = mK0
+    alignas(16) T Et[G::DVX * G::LDD]; // Et[j][i] = E0[i][j]; row DV = nk0
 };
 
 template <typename T, int D, int DV, int C>
 struct AhlaSumSmem {
     using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T Q[C * G::LDD];
-    alignas(16) T Qt[D * G::LDC];
     alignas(16) T K[C * G::LDD];
-    alignas(16) T Kt[D * G::LDC];
-    alignas(16) T Vt[DV * G::LDC];
-    alignas(16) T Yt[DV * G::LDC];
-    alignas(16) T Pt[DV * G::LDD];
-    float mK[D], nk[D], y1[C];
+    alignas(16) T V[C * G::LDV];
+    alignas(16) T Y[C * G::LDV];
+    alignas(16) T Pt[G::DVX * G::LDD];
 };
 
-// Y = Q P0 + L V for row tile r (rows tau), written to Yt transposed; also
-// y1[tau] = q_tau . mK + sum_sigma L[tau][sigma].
-template <typename T, int D, int DV, int C, int RT, int NCG, int OJ, int LDD, int LDC>
-__device__ __forceinline__ void ahla_y_phase(const Frag16<T> (&Lf)[RT], const RowFrags<T, D> &qf,
-                                             int r, int cg, int tau, const T *Q, const T *Pt,
-                                             const T *Vt, T *Yt, const float *mK, float *y1) {
+template <typename T, int D, int DV, int C>
+constexpr int ahla_fwd_blocks() {
+    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdSmem<T, D, DV, C>)>();
+}
+template <typename T, int D, int DV, int C>
+constexpr int ahla_sum_blocks() {
+    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C>)>();
+}
+
+// Y^T tiles of row tile r: Y = Q P0 + L V, with the widened tile (column DV =
+// y1) when `wide`; stored row-major.
+template <typename T, int D, int DV, int RT, int NCG, int YJ, int LDD, int LDV>
+__device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[RT],
+                                             const T *Pt, const T *V, T *Y, int r, int cg,
+                                             int tau, bool wide) {
     constexpr int nTV = DV / 16;
     const int g4 = (lane_id() >> 4) << 2;
 #pragma unroll
-    for (int jj = 0; jj < OJ; ++jj) {
+    for (int jj = 0; jj < YJ; ++jj) {
         const int jv = cg + jj * NCG;
-        if (jv < nTV) {
-            // accumulator rows are tokens 16r + 4g + i, columns features 16 jv + c
-            f32x4 y = mma_nt_fa(zero4(), qf, Pt + 16 * jv * LDD, LDD);
+        if (jv < nTV || (wide && jv == nTV)) {
+            const f32x4 y = mma_nt_f(zero4(), Pt + 16 * jv * LDD, LDD, qf);
             f32x4 yc = zero4();
 #pragma unroll
             for (int s = 0; s < RT; ++s)
-                if (s <= r) yc = mma16(yc, Lf[s], ld_frag(Vt + 16 * jv * LDC + 16 * s, LDC));
-            y += yc;
-            store4(Yt + (16 * jv + acc_col()) * LDC + 16 * r + g4, y);
+                if (s <= r) yc = mma16(yc, ld_frag_t(V + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
+            store4(Y + tau * LDV + 16 * jv + g4, y + yc);
         }
-    }
-    if (cg == 0) {
-        float rs = 0.f;
-#pragma unroll
-        for (int s = 0; s < RT; ++s)
-            if (s <= r) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rs += frag_val(Lf[s], i);
-            }
-        const float yv = lane_dot<T, D>(Q + tau * LDD, mK) + sum_groups(rs);
-        if (lane_id() < 16) y1[tau] = yv;
     }
 }
 
 template <typename T, int D, int DV, int C>
-__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT),
-                             (hla2_min_blocks<AhlaCfg<T, D, DV, C>::NT, 0, D, DV>()))
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_fwd_blocks<T, D, DV, C>()))
 void ahla_forward_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDC = G::LDC, nTV = G::nTV;
+    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
     __shared__ AhlaFwdSmem<T, D, DV, C> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
-    const int col = acc_col(), g = lane_id() >> 4, g4 = g << 2;
+    const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
     const int tau = 16 * r + col;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
+    const bool ratio = p.ratio != 0;
+    const bool last = seg == p.nseg - 1;
+    const bool need_u = ratio || (p.state_out != nullptr && last);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
 
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
     const float *P0 = nullptr, *E0 = nullptr, *mK0 = nullptr, *nk0 = nullptr;
     if (p.nseg > 1) {
         const float *e = p.ws + ws_elem(bh, 1, p.spad, seg, G::SUMF);
@@ -139,6 +141,7 @@ void ahla_forward_kernel(FwdParams p) {
     }
     using PBk = typename G::PBk;
     f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
+    f32x4 accMK[G::UJ], accNK[G::UJ];
     for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
         f32x4 a, b;
 #pragma unroll
@@ -152,41 +155,48 @@ void ahla_forward_kernel(FwdParams p) {
         store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, a);
         store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, b);
     });
-    for (int i = threadIdx.x; i < D; i += NT) {
-        sm.mK[i] = mK0 ? mK0[i] : 0.f;
-        sm.nk[i] = nk0 ? nk0[i] : 0.f;
-    }
+    // mK0, nk0 as column DV of the widened P, E (the other 15 columns zero)
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        f32x4 a, b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = (mK0 && col == 0) ? mK0[16 * ti + g4 + i] : 0.f;
+            b[i] = (nk0 && col == 0) ? nk0[16 * ti + g4 + i] : 0.f;
+        }
+        accMK[j] = a;
+        accNK[j] = b;
+        store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, a);
+        store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, b);
+    });
 
-    ChunkRegs<T, C, D, NT> rq, rk;
+    ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
+    RowFrags<T, D> qn;
+    auto load_chunk = [&](int c, int valid) {
+        const int tv = valid - 16 * r;
+        qn.load_rows_g(q + (size_t)(c + (tv > 0 ? 16 * r : 0)) * D, D, tv > 0 ? tv : 0);
+        rk.load(k + (size_t)c * D, valid);
+        rv.load(v + (size_t)c * DV, valid);
+    };
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
-    rq.load(q + (size_t)c0 * D, cv);
-    rk.load(k + (size_t)c0 * D, cv);
-    rv.load(v + (size_t)c0 * DV, cv);
+    load_chunk(c0, cv);
 
     while (c0 < t_end) {
         __syncthreads();
-        rq.store_rows(sm.Q, LDD);
         rk.store_rows(sm.K, LDD);
-        rk.store_cols(sm.Kt, LDC);
-        rv.store_cols(sm.Vt, LDC);
+        rv.store_rows(sm.V, LDV);
+        RowFrags<T, D> qf = qn;
+        qf.mask_rows(cv - 16 * r);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
-        if (n0 < t_end) {
-            rq.load(q + (size_t)n0 * D, ncv);
-            rk.load(k + (size_t)n0 * D, ncv);
-            rv.load(v + (size_t)n0 * DV, ncv);
-        }
+        if (n0 < t_end) load_chunk(n0, ncv);
         __syncthreads();
 
-        RowFrags<T, D> qf;
-        qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
         scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
-        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, qf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
-                                                            sm.Yt, sm.mK, sm.y1);
-        // carried part of the output and of its denominator
+        ahla_y_tiles<T, D, DV, RT, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, r, cg, tau, need_u);
+        // carried part of the output and of its denominator (row DV)
         f32x4 accO[G::OJ];
 #pragma unroll
         for (int jj = 0; jj < G::OJ; ++jj) {
@@ -194,20 +204,18 @@ void ahla_forward_kernel(FwdParams p) {
             accO[jj] = zero4();
             if (jv < nTV) accO[jj] = mma_nt_f(zero4(), sm.Et + 16 * jv * LDD, LDD, qf);
         }
-        float den = 0.f;
-        if (p.ratio) den = lane_dot<T, D>(sm.Q + tau * LDD, sm.nk);
+        f32x4 accD = zero4();
+        if (ratio) accD = mma_nt_f(zero4(), sm.Et + DV * LDD, LDD, qf);
         __syncthreads();
 
-        // O^T += Y^T L^T ; den += sum_sigma L[tau][sigma] y1[sigma]
-        if (p.ratio) {
-            float a = 0.f;
+        // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
+        float rden = 1.f;
+        if (ratio) {
+            f32x4 dc = zero4();
 #pragma unroll
             for (int s = 0; s < RT; ++s)
-                if (s <= r) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a += frag_val(Lf[s], i) * sm.y1[16 * s + g4 + i];
-                }
-            den += sum_groups(a);
+                if (s <= r) dc = mma16(dc, ld_frag_t(sm.Y + 16 * s * LDV + DV, LDV), Lf[s]);
+            rden = 1.f / __shfl(accD[0] + dc[0], col);
         }
 #pragma unroll
         for (int jj = 0; jj < G::OJ; ++jj) {
@@ -216,34 +224,38 @@ void ahla_forward_kernel(FwdParams p) {
                 f32x4 oc = zero4();
 #pragma unroll
                 for (int s = 0; s < RT; ++s)
-                    if (s <= r) oc = mma16(oc, ld_frag(sm.Yt + 16 * jv * LDC + 16 * s, LDC), Lf[s]);
+                    if (s <= r) oc = mma16(oc, ld_frag_t(sm.Y + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
                 f32x4 ov = accO[jj] + oc;
-                if (p.ratio) ov *= 1.f / den;
+                if (ratio) ov *= rden;
                 if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
             }
         }
         // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_nt_blk<PBk::BR, C>(accP[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
-            mma_nt_blk<PBk::BR, C>(accE[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Yt + 16 * tv0 * LDC, LDC);
+            mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
+            mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
 #pragma unroll
             for (int x = 0; x < PBk::BR; ++x)
 #pragma unroll
                 for (int y = 0; y < PBk::BR; ++y) {
-                    const int o = (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4;
-                    store4(sm.Pt + o, accP[pb][x][y]);
-                    store4(sm.Et + o, accE[pb][x][y]);
+                    const int oo = (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4;
+                    store4(sm.Pt + oo, accP[pb][x][y]);
+                    store4(sm.Et + oo, accE[pb][x][y]);
                 }
         });
-        for (int i = threadIdx.x; i < D; i += NT) {
-            sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
-            sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
+        if (need_u) {
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
+                accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+                store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
+                store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, accNK[j]);
+            });
         }
         c0 = n0;
         cv = ncv;
     }
 
-    if (p.state_out && seg == p.nseg - 1) {
+    if (p.state_out && last) {
         float *so = p.state_out + (size_t)bh * G::STF;
         for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
@@ -253,21 +265,24 @@ void ahla_forward_kernel(FwdParams p) {
                 so[D * DV + idx] = accE[pb][x][y][i];
             }
         });
-        __syncthreads();
-        for (int i = threadIdx.x; i < D; i += NT) {
-            so[2 * D * DV + i] = sm.mK[i];
-            so[2 * D * DV + D + i] = sm.nk[i];
-        }
+        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+            if (col == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    so[2 * D * DV + 16 * ti + g4 + i] = accMK[j][i];
+                    so[2 * D * DV + D + 16 * ti + g4 + i] = accNK[j][i];
+                }
+            }
+        });
     }
 }
 
 template <typename T, int D, int DV, int C>
-__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT),
-                             (hla2_min_blocks<AhlaCfg<T, D, DV, C>::NT, 0, D, DV>()))
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_sum_blocks<T, D, DV, C>()))
 void ahla_summary_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDC = G::LDC, nTD = G::nTD, nTV = G::nTV;
+    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD;
     __shared__ AhlaSumSmem<T, D, DV, C> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -281,10 +296,11 @@ void ahla_summary_kernel(FwdParams p) {
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
     using PBk = typename G::PBk;
     using MBk = typename G::MBk;
     f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
-    f32x4 accM[MBk::PB][MBk::BR][MBk::BR];
+    f32x4 accM[MBk::PB][MBk::BR][MBk::BR], accMK[G::UJ], accNK[G::UJ];
 #pragma unroll
     for (int pb = 0; pb < PBk::PB; ++pb)
 #pragma unroll
@@ -300,11 +316,12 @@ void ahla_summary_kernel(FwdParams p) {
         for (int x = 0; x < MBk::BR; ++x)
 #pragma unroll
             for (int y = 0; y < MBk::BR; ++y) accM[pb][x][y] = zero4();
-    for (int i = threadIdx.x; i < DV * LDD; i += NT) sm.Pt[i] = from_f<T>(0.f);
-    for (int i = threadIdx.x; i < D; i += NT) {
-        sm.mK[i] = 0.f;
-        sm.nk[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::UJ; ++j) {
+        accMK[j] = zero4();
+        accNK[j] = zero4();
     }
+    for (int i = threadIdx.x; i < G::DVX * LDD; i += NT) sm.Pt[i] = from_f<T>(0.f);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -317,10 +334,8 @@ void ahla_summary_kernel(FwdParams p) {
     while (c0 < t_end) {
         __syncthreads();
         rq.store_rows(sm.Q, LDD);
-        rq.store_cols(sm.Qt, LDC);
         rk.store_rows(sm.K, LDD);
-        rk.store_cols(sm.Kt, LDC);
-        rv.store_cols(sm.Vt, LDC);
+        rv.store_rows(sm.V, LDV);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
         if (n0 < t_end) {
@@ -334,13 +349,12 @@ void ahla_summary_kernel(FwdParams p) {
         qf.load(sm.Q + 16 * r * LDD, LDD);
         Frag16<T> Lf[RT];
         scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
-        ahla_y_phase<T, D, DV, C, RT, NCG, G::OJ, LDD, LDC>(Lf, qf, r, cg, tau, sm.Q, sm.Pt, sm.Vt,
-                                                            sm.Yt, sm.mK, sm.y1);
+        ahla_y_tiles<T, D, DV, RT, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, r, cg, tau, true);
         __syncthreads();
 
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_nt_blk<PBk::BR, C>(accP[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Vt + 16 * tv0 * LDC, LDC);
-            mma_nt_blk<PBk::BR, C>(accE[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Yt + 16 * tv0 * LDC, LDC);
+            mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
+            mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
 #pragma unroll
             for (int x = 0; x < PBk::BR; ++x)
 #pragma unroll
@@ -348,16 +362,16 @@ void ahla_summary_kernel(FwdParams p) {
                     store4(sm.Pt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accP[pb][x][y]);
         });
         for_blocks<MBk, NW>(w, [&](int pb, int ti0, int tj0) {
-            mma_nt_blk<MBk::BR, C>(accM[pb], sm.Kt + 16 * ti0 * LDC, LDC, sm.Qt + 16 * tj0 * LDC, LDC);
+            mma_tn_blk<MBk::BR, C>(accM[pb], sm.K + 16 * ti0, LDD, sm.Q + 16 * tj0, LDD);
         });
-        for (int i = threadIdx.x; i < D; i += NT) {
-            sm.mK[i] += row_sum<T, C>(sm.Kt, LDC, i);
-            sm.nk[i] += row_dot<T, C>(sm.Kt, LDC, i, sm.y1);
-        }
+        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+            accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
+            accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+            store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
+        });
         c0 = n0;
         cv = ncv;
     }
-    __syncthreads();
 
     // summary [X = M | Y = P | N = E | y = mK | nv = nk]
     float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
@@ -373,10 +387,15 @@ void ahla_summary_kernel(FwdParams p) {
             e[D * D + D * DV + idx] = accE[pb][x][y][i];
         }
     });
-    for (int i = threadIdx.x; i < D; i += NT) {
-        e[D * D + 2 * D * DV + i] = sm.mK[i];
-        e[D * D + 2 * D * DV + D + i] = sm.nk[i];
-    }
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        if (col == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e[D * D + 2 * D * DV + 16 * ti + g4 + i] = accMK[j][i];
+                e[D * D + 2 * D * DV + D + 16 * ti + g4 + i] = accNK[j][i];
+            }
+        }
+    });
 }
 
 }  // namespace hla

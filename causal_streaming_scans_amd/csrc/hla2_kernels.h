@@ -144,11 +144,6 @@ struct Hla2SumSmem {
     float gp[G::NPOW];
 };
 
-template <int NT, int NW, int D, int DV>
-constexpr int hla2_min_blocks() {
-    return (D <= 64 && DV <= 64 && NT <= 256) ? 2 : 1;
-}
-
 // Workgroups per CU the kernel is built for: as many as the LDS allows, up
 // to 3 (12 waves of 256-thread groups, 168 VGPRs each).
 template <int NT, int SMEM>

@@ -119,10 +119,9 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  *                ignored and on return are unspecified
  * stream         hipStream_t as void*
  *
- * Supported (otherwise HLA_ERR_UNSUPPORTED): d == dv;
- *   HLA_BF16: d in {16, 32, 64} with chunk 16, 32 or 64; d = 128 with chunk
- *             16 or 32 (AHLA variants also chunk 64);
- *   HLA_F32:  d in {16, 32, 64} with chunk 16, 32 or 64.
+ * Supported (otherwise HLA_ERR_UNSUPPORTED): d == dv, chunk 16, 32 or 64;
+ *   HLA_BF16: d in {16, 32, 64, 128};
+ *   HLA_F32:  d in {16, 32, 64}.
  */
 hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        int B, int H, int n, int d, int dv, int dtype, int variant,

@@ -98,7 +98,8 @@ def test_forward_validation_errors(lib):
     assert _fwd(lib, fake, fake, fake, fake, chunk=48) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, d=48, dv=48) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, d=64, dv=32) == ERR_UNSUP
-    assert _fwd(lib, fake, fake, fake, fake, d=128, dv=128, chunk=64) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, d=128, dv=128, dtype=0) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, chunk=128) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, dtype=F32, d=128, dv=128, chunk=16) == ERR_UNSUP
     # decay: AHLA has none; gamma must lie in (0, 1]; H bounded
     assert _fwd(lib, fake, fake, fake, fake, variant=AHLA, gamma=[0.9]) == ERR_UNSUP

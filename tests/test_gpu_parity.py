@@ -64,8 +64,7 @@ def test_forward_matches_oracle(case):
 # Every kernel instance the library ships: (dtype, d, chunk) for each family.
 SUPPORT = [(dt, d, c, fam)
            for dt, dims in (("f32", (16, 32, 64)), ("bf16", (16, 32, 64, 128)))
-           for d in dims for c in (16, 32, 64) for fam in ("hla2", "ahla")
-           if not (dt == "bf16" and d == 128 and c == 64 and fam == "hla2")]
+           for d in dims for c in (16, 32, 64) for fam in ("hla2", "ahla")]
 
 
 @pytest.mark.parametrize("case", SUPPORT, ids=lambda c: "-".join(str(x) for x in c))
