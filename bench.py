@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the HLA-2 forward hot path on one MI355X.
 
-One step = one whole forward pass (segment summaries -> exclusive Blelloch
-scan -> chunked forward) over one batch of the headline workload: ratio-
+One step = one whole forward pass (segment summaries -> up-sweep of the
+exclusive Blelloch scan -> per-segment prefix and chunked forward) over one
+batch of the headline workload: ratio-
 normalised HLA-2, B=8, H=16, n=4096, d=dv=64, bf16 inputs and output, fp32
 state, q, k ~ U[0,1)/sqrt(d), v ~ N(0,1), seeded.  Inputs are resident in
 HBM before the timed region.  Prints ONE JSON line on stdout; progress goes
@@ -160,7 +161,7 @@ def main():
     tokens = B * H * n
     tok_s = tokens / (ms_per_step * 1e-3)
     log(f"[bench] {ms_per_step:.4f} ms/step, {tok_s / 1e9:.3f} G tokens/s; stages (ms) "
-        f"summary {stage_ms[0]:.4f} scan {stage_ms[1]:.4f} forward {stage_ms[2]:.4f}")
+        f"summary {stage_ms[0]:.4f} up-sweep {stage_ms[1]:.4f} forward {stage_ms[2]:.4f}")
 
     # ---- spot parity of the benchmarked output on two heads
     import oracle
@@ -171,7 +172,7 @@ def main():
     log(f"[bench] spot check vs oracle (heads {heads}): rel_l2 {rel:.3e}")
 
     # ---- roofline of the dominant kernel (largest measured stage)
-    names = ["hla2_summary_kernel", "scan_kernel", "hla2_forward_kernel"]
+    names = ["hla2_summary_kernel", "up_sweep_kernel", "hla2_forward_kernel"]
     dom = int(np.argmax(stage_ms))
     esz = 2  # bf16
     per_token_bytes = (2 * d + 2 * dv) * esz          # q, k, v in, o out
@@ -181,8 +182,9 @@ def main():
     elif dom == 0:
         tok_sum = B * H * min(n, (nseg - 1) * chunk * seg)
         alg_bytes = tok_sum * (2 * d + dv) * esz + B * H * (nseg - 1) * sumf * 4
-    else:
-        alg_bytes = B * H * 2 * nseg * sumf * 4
+    else:   # each up-sweep combine reads two summaries and writes one
+        ncomb = sum(max(0, (nseg - 1) >> b) for b in range(1, 32))
+        alg_bytes = B * H * ncomb * 3 * sumf * 4
     achieved = alg_bytes / (stage_ms[dom] * 1e-3) / 1e9
     traffic = stored_traffic(names[dom])
     fl_tok = flops_per_token(chunk, d, dv)
@@ -253,8 +255,8 @@ def main():
                  "forward_kernel_frac": round(mfma_tflops_fwd / BF16_MFMA_PEAK_TFLOPS, 4),
                  "whole_step_tflops": round(mfma_tflops_step, 2),
                  "whole_step_frac": round(mfma_tflops_step / BF16_MFMA_PEAK_TFLOPS, 4)},
-        "stages_ms": {"summary": round(stage_ms[0], 5), "scan": round(stage_ms[1], 5),
-                      "forward": round(stage_ms[2], 5)},
+        "stages_ms": {"summary": round(stage_ms[0], 5), "up_sweep": round(stage_ms[1], 5),
+                      "prefix_and_forward": round(stage_ms[2], 5)},
         "parity_spot_rel_l2": rel,
         "decode": decode,
         "cpu_baseline": cpu,

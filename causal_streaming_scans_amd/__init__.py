@@ -197,9 +197,10 @@ def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks
 def hla_forward_stage(stage, q, k, v, variant="hla2", gamma=None, chunk: int = 64,
                       seg_chunks: int = 0, state_in=None, state_out=None, out=None,
                       workspace=None, stream=None):
-    """One stage (1 = segment summaries, 2 = Blelloch scan, 3 = chunked
-    forward) of hla_forward; stages 1, 2, 3 in order with the same arguments
-    (and the same workspace and out) equal hla_forward."""
+    """One stage of hla_forward: 1 = segment summaries, 2 = up-sweep of the
+    exclusive Blelloch scan over them, 3 = per-segment prefix from the
+    up-sweep nodes and the chunked forward.  Stages 1, 2, 3 in order with the
+    same arguments (and the same workspace and out) equal hla_forward."""
     return _forward_call(stage, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out,
                          out, workspace, stream)
 

@@ -61,6 +61,9 @@ struct AhlaFwdSmem {
 };
 
 template <typename T, int D, int DV, int C>
+using AhlaFwdLds = LdsWithScratch<AhlaFwdSmem<T, D, DV, C>, CrossLds<D, DV>::FLOATS>;
+
+template <typename T, int D, int DV, int C>
 struct AhlaSumSmem {
     using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T Q[C * G::LDD];
@@ -72,7 +75,7 @@ struct AhlaSumSmem {
 
 template <typename T, int D, int DV, int C>
 constexpr int ahla_fwd_blocks() {
-    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdSmem<T, D, DV, C>)>();
+    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdLds<T, D, DV, C>)>();
 }
 template <typename T, int D, int DV, int C>
 constexpr int ahla_sum_blocks() {
@@ -107,7 +110,8 @@ void ahla_forward_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
     constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
-    __shared__ AhlaFwdSmem<T, D, DV, C> sm;
+    __shared__ AhlaFwdLds<T, D, DV, C> lds;
+    auto &sm = lds.s;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
@@ -124,51 +128,7 @@ void ahla_forward_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
 
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
-    const float *P0 = nullptr, *E0 = nullptr, *mK0 = nullptr, *nk0 = nullptr;
-    if (p.nseg > 1) {
-        const float *e = p.ws + ws_elem(bh, 1, p.spad, seg, G::SUMF);
-        P0 = e + D * D;
-        E0 = e + D * D + D * DV;
-        mK0 = e + D * D + 2 * D * DV;
-        nk0 = mK0 + D;
-    } else if (p.state_in) {
-        const float *e = p.state_in + (size_t)bh * G::STF;
-        P0 = e;
-        E0 = e + D * DV;
-        mK0 = e + 2 * D * DV;
-        nk0 = mK0 + D;
-    }
-    using PBk = typename G::PBk;
-    f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
-    f32x4 accMK[G::UJ], accNK[G::UJ];
-    for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-        f32x4 a, b;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-            a[i] = P0 ? P0[idx] : 0.f;
-            b[i] = E0 ? E0[idx] : 0.f;
-        }
-        accP[pb][x][y] = a;
-        accE[pb][x][y] = b;
-        store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, a);
-        store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, b);
-    });
-    // mK0, nk0 as column DV of the widened P, E (the other 15 columns zero)
-    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        f32x4 a, b;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a[i] = (mK0 && col == 0) ? mK0[16 * ti + g4 + i] : 0.f;
-            b[i] = (nk0 && col == 0) ? nk0[16 * ti + g4 + i] : 0.f;
-        }
-        accMK[j] = a;
-        accNK[j] = b;
-        store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, a);
-        store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, b);
-    });
-
+    // the next chunk's data in registers: K, V for LDS; this wave's Q rows
     ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
     RowFrags<T, D> qn;
@@ -178,6 +138,97 @@ void ahla_forward_kernel(FwdParams p) {
         rk.load(k + (size_t)c * D, valid);
         rv.load(v + (size_t)c * DV, valid);
     };
+
+    // carried state at the start of this segment: the caller's state (or
+    // zero), then the up-sweep nodes covering segments 0 .. seg-1
+    const float *P0 = nullptr, *E0 = nullptr, *mK0 = nullptr, *nk0 = nullptr;
+    if (p.state_in) {
+        const float *e = p.state_in + (size_t)bh * G::STF;
+        P0 = e;
+        E0 = e + D * DV;
+        mK0 = e + 2 * D * DV;
+        nk0 = mK0 + D;
+    }
+    using PBk = typename G::PBk;
+    using O = SumOfs<D, DV>;
+    f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
+    f32x4 accMK[G::UJ], accNK[G::UJ];
+    for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+            accP[pb][x][y][i] = P0 ? P0[idx] : 0.f;
+            accE[pb][x][y][i] = E0 ? E0[idx] : 0.f;
+        }
+    });
+    // mK, nk as column DV of the widened P, E (the other 15 columns zero)
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            accMK[j][i] = (mK0 && col == 0) ? mK0[16 * ti + g4 + i] : 0.f;
+            accNK[j][i] = (nk0 && col == 0) ? nk0[16 * ti + g4 + i] : 0.f;
+        }
+    });
+    if (seg > 0) {
+        // fold node B (later) into the running state A: E <- E + E_B + M_B P,
+        // nk <- nk + nk_B + M_B mK, P <- P + P_B, mK <- mK + mK_B; the node's
+        // M and the old widened [P | mK] are staged in LDS (fp32)
+        using L = CrossLds<D, DV>;
+        float *Ms = lds.f, *Ps = lds.f + D * L::LDA;
+        const float *nodes = p.ws + ws_node(bh, 0, p.nreal, G::SUMF);
+        int done = 0;
+        for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
+            if (!((seg >> b) & 1)) continue;
+            const float *e = nodes + (size_t)node_slot(b, done >> b) * G::SUMF;
+            for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Ps[(16 * ti + g4 + i) * L::LDB + 16 * tv + col] = accP[pb][x][y][i];
+            });
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ps[(16 * ti + g4 + i) * L::LDB + DV + col] = accMK[j][i];
+            });
+            stage_f32<D, D, NT>(Ms, L::LDA, e + O::X, D);
+            // the linear terms now (the old P, mK are already staged); the
+            // cross terms once the staging has landed
+            for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
+                    accE[pb][x][y][i] += e[O::N + idx];
+                    accP[pb][x][y][i] += e[O::Y + idx];
+                }
+            });
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * ti + g4 + i;
+                    accNK[j][i] += col == 0 ? e[O::nv + row] : 0.f;
+                    accMK[j][i] += col == 0 ? e[O::y + row] : 0.f;
+                }
+            });
+            __syncthreads();
+            for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+                accE[pb][x][y] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + 16 * tv, L::LDB);
+            });
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                accNK[j] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + DV, L::LDB);
+            });
+            __syncthreads();
+            done += 1 << b;
+        }
+    }
+    for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+        store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[pb][x][y]);
+        store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[pb][x][y]);
+    });
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
+        store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, accNK[j]);
+    });
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
+
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
     load_chunk(c0, cv);
@@ -374,7 +425,7 @@ void ahla_summary_kernel(FwdParams p) {
     }
 
     // summary [X = M | Y = P | N = E | y = mK | nv = nk]
-    float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
+    float *e = p.ws + ws_node(bh, seg, p.nreal, G::SUMF);
     for_owned<MBk, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accM[pb][x][y][i];

@@ -45,6 +45,7 @@
 #pragma once
 
 #include "chunk_common.h"
+#include "combine.h"
 
 namespace hla {
 
@@ -132,6 +133,9 @@ struct Hla2FwdSmem {
 };
 
 template <typename T, int D, int DV, int C, bool DECAY>
+using Hla2FwdLds = LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY>, CrossLds<D, DV>::FLOATS>;
+
+template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     alignas(16) T Q[C * G::LDD];
@@ -154,7 +158,7 @@ constexpr int hla_min_blocks() {
 }
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int hla2_fwd_blocks() {
-    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdSmem<T, D, DV, C, DECAY>)>();
+    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdLds<T, D, DV, C, DECAY>)>();
 }
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int hla2_sum_blocks() {
@@ -215,7 +219,8 @@ void hla2_forward_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
     constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
-    __shared__ Hla2FwdSmem<T, D, DV, C, DECAY> sm;
+    __shared__ Hla2FwdLds<T, D, DV, C, DECAY> lds;
+    auto &sm = lds.s;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
     const int w = wave_id();
@@ -233,50 +238,7 @@ void hla2_forward_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
 
-    if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
-
-    // carried state at the start of this segment: the exclusive prefix from
-    // the scan, or the caller's state, or zero
-    const float *S0 = nullptr, *W0 = nullptr, *u0 = nullptr;
-    if (p.nseg > 1) {
-        const float *e = p.ws + ws_elem(bh, 1, p.spad, seg, G::SUMF);
-        S0 = e;
-        W0 = e + D * D + D * DV;
-        u0 = e + D * D + 2 * D * DV + D;
-    } else if (p.state_in) {
-        const float *e = p.state_in + (size_t)bh * G::STF;
-        S0 = e;
-        W0 = e + D * D;
-        u0 = e + D * D + D * DV;
-    }
-    using SB = typename G::SB;
-    using WB = typename G::WB;
-    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accU[G::UJ];
-    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-        f32x4 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
-        accS[pb][x][y] = a;
-        store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, a);
-    });
-    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-        f32x4 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
-        accW[pb][x][y] = a;
-        store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, a);
-    });
-    // u0 as column DV of the widened W (the other 15 columns stay zero)
-    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        f32x4 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
-        accU[j] = a;
-        store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, a);
-    });
-
-    // next chunk's data in registers: K, V for LDS; this wave's Q rows
+    // the next chunk's data in registers: K, V for LDS; this wave's Q rows
     ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
     RowFrags<T, D> qn;
@@ -286,6 +248,96 @@ void hla2_forward_kernel(FwdParams p) {
         rk.load(k + (size_t)c * D, valid);
         rv.load(v + (size_t)c * DV, valid);
     };
+
+    // ---- a-6 / a-7: carried state at the start of this segment: the caller's
+    // state (or zero), then the up-sweep nodes covering segments 0 .. seg-1
+    const float *S0 = nullptr, *W0 = nullptr, *u0 = nullptr;
+    if (p.state_in) {
+        const float *e = p.state_in + (size_t)bh * G::STF;
+        S0 = e;
+        W0 = e + D * D;
+        u0 = e + D * D + D * DV;
+    }
+    using SB = typename G::SB;
+    using WB = typename G::WB;
+    using O = SumOfs<D, DV>;
+    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accU[G::UJ];
+    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            accS[pb][x][y][i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
+    });
+    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            accW[pb][x][y][i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
+    });
+    // u as column DV of the widened W (the other 15 columns stay zero)
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accU[j][i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
+    });
+    if (seg > 0) {
+        // fold node B (later) into the running state A: W <- a^2 W + N_B +
+        // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
+        // the node's [Y | y] are staged in LDS (fp32) as the cross factors
+        using L = CrossLds<D, DV>;
+        float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
+        const float *nodes = p.ws + ws_node(bh, 0, p.nreal, G::SUMF);
+        int done = 0;
+        for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
+            if (!((seg >> b) & 1)) continue;
+            const float *e = nodes + (size_t)node_slot(b, done >> b) * G::SUMF;
+            const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
+            for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = accS[pb][x][y][i];
+            });
+            stage_right_ext<D, DV, NT>(Bs, e + O::Y, e + O::y);
+            // the linear terms now (the old S is already staged); the cross
+            // terms once the staging has landed
+            for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    accW[pb][x][y][i] = a * a * accW[pb][x][y][i] +
+                                        e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col];
+            });
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    accU[j][i] = a * a * accU[j][i] + (col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f);
+            });
+            for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    accS[pb][x][y][i] =
+                        a * accS[pb][x][y][i] + e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col];
+            });
+            __syncthreads();
+            for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+                accW[pb][x][y] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+            });
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                accU[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+            });
+            __syncthreads();
+            done += 1 << b;
+        }
+    }
+    // T-typed transposed copies: the operands of Q S0 and Q W0 (row DV of Wt = u)
+    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+        store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
+    });
+    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+        store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[pb][x][y]);
+    });
+    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+        store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, accU[j]);
+    });
+    if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
+    init_ones_column<T, C, LDV, DV, NT>(sm.V);
+
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
     load_chunk(c0, cv);
@@ -548,7 +600,7 @@ void hla2_summary_kernel(FwdParams p) {
     }
 
     // summary [X = S | Y = C | N = W | y = m | nv = u]
-    float *e = p.ws + ws_elem(bh, 0, p.spad, seg, G::SUMF);
+    float *e = p.ws + ws_node(bh, seg, p.nreal, G::SUMF);
     for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];

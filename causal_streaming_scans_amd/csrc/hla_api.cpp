@@ -3,13 +3,14 @@
 // Validation runs first and touches no HIP API, so every error code below is
 // reachable on a host without a GPU.  Then the forward pass enqueues, on the
 // caller's stream:
-//   1. the segment-summary kernel over segments 0 .. nseg-2 (the last
+//   stage 1: the segment-summary kernel over segments 0 .. nseg-2 (the last
 //      segment's summary would only feed the total, which an exclusive scan
-//      never uses),
-//   2. the exclusive Blelloch scan of those summaries per (b,h), which also
-//      folds in the caller's initial state,
-//   3. the chunked forward kernel over every segment from its carried state.
-// With a single segment only step 3 runs, starting from state_in or zero.
+//      never uses);
+//   stage 2: the up-sweep of the exclusive Blelloch scan over the summaries;
+//   stage 3: the chunked forward kernel over every segment: each workgroup
+//      first folds the caller's initial state and the up-sweep nodes left of
+//      its segment into its carried state (the down-sweep's value for it).
+// With a single segment only stage 3 runs, starting from state_in or zero.
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -28,12 +29,6 @@ bool is_ahla(int v) { return v == HLA_AHLA || v == HLA_AHLA_RATIO; }
 bool is_ratio(int v) { return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO; }
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
-
-long next_pow2(long x) {
-    long p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
 
 int effective_seg_chunks(int variant, int B, int H, int n, int chunk, int seg_chunks) {
     return seg_chunks > 0 ? seg_chunks : hla_default_seg_chunks(variant, B, H, n, chunk);
@@ -97,8 +92,8 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
     const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
     const long nseg = num_segments(n, chunk, g);
     if (nseg <= 1) return 0;
-    const long spad = next_pow2(nseg);
-    return (size_t)B * H * 2 * spad * (size_t)summary_floats(d, dv) * sizeof(float);
+    const size_t nreal = (size_t)(nseg - 1);
+    return (size_t)B * H * nreal * (size_t)summary_floats(d, dv) * sizeof(float);
 }
 
 // Validate, pick the kernels and fill the argument block; shared by
@@ -135,7 +130,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     p->n = n;
     p->seg_len = chunk * g;
     p->nseg = (int)nseg;
-    p->spad = nseg > 0 ? (int)next_pow2(nseg) : 0;
+    p->nreal = nseg > 1 ? (int)(nseg - 1) : 0;
     p->ratio = is_ratio(variant) ? 1 : 0;
     p->ws = static_cast<float *>(workspace);
     p->state_in = state_in;
@@ -144,7 +139,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     return HLA_OK;
 }
 
-// one stage of the forward pass (1 = summaries, 2 = scan, 3 = chunked forward)
+// one stage of the forward pass (1 = summaries, 2 = up-sweep, 3 = chunked forward)
 static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &p, int variant,
                             int d, int dv, hipStream_t s) {
     if (p.n == 0) {
@@ -158,7 +153,7 @@ static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &
     }
     hipError_t e = hipSuccess;
     if (stage == 1 && p.nseg > 1) e = kern.summary(p, s);
-    if (stage == 2 && p.nseg > 1) e = kern.scan(p, s);
+    if (stage == 2 && p.nseg > 2) e = kern.up_sweep(p, s);
     if (stage == 3) e = kern.forward(p, s);
     return e == hipSuccess ? HLA_OK : HLA_ERR_DEVICE;
 }

@@ -5,7 +5,6 @@
 #include "ahla_kernels.h"
 #include "hla2_kernels.h"
 #include "launch.h"
-#include "scan_kernel.h"
 
 namespace hla {
 
@@ -13,13 +12,13 @@ constexpr size_t kLdsBytes = 160 * 1024;   // gfx950 LDS per workgroup
 
 template <typename T, int D, int C, bool DECAY>
 constexpr bool hla2_fits() {
-    return sizeof(Hla2FwdSmem<T, D, D, C, DECAY>) <= kLdsBytes &&
+    return sizeof(Hla2FwdLds<T, D, D, C, DECAY>) <= kLdsBytes &&
            sizeof(Hla2SumSmem<T, D, D, C, DECAY>) <= kLdsBytes;
 }
 
 template <typename T, int D, int C>
 constexpr bool ahla_fits() {
-    return sizeof(AhlaFwdSmem<T, D, D, C>) <= kLdsBytes &&
+    return sizeof(AhlaFwdLds<T, D, D, C>) <= kLdsBytes &&
            sizeof(AhlaSumSmem<T, D, D, C>) <= kLdsBytes;
 }
 
@@ -52,10 +51,9 @@ hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
 }
 
 template <typename T, int D, bool HLA2>
-hipError_t launch_scan(const FwdParams &p, hipStream_t s) {
-    constexpr bool F32 = sizeof(T) == 4;
-    hipLaunchKernelGGL((scan_kernel<F32, D, D, HLA2>), dim3(p.BH), dim3(ScanCfg<F32, D, D>::NT), 0,
-                       s, p);
+hipError_t launch_up_sweep(const FwdParams &p, hipStream_t s) {
+    constexpr int NT = D >= 128 ? 512 : 256;
+    hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(p.BH), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -64,7 +62,7 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
     if (ahla) {
         if (decay) return false;
         if constexpr (ahla_fits<T, D, C>()) {
-            *out = {launch_ahla_summary<T, D, C>, launch_scan<T, D, false>,
+            *out = {launch_ahla_summary<T, D, C>, launch_up_sweep<T, D, false>,
                     launch_ahla_forward<T, D, C>};
             return true;
         }
@@ -72,14 +70,14 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
     }
     if (decay) {
         if constexpr (hla2_fits<T, D, C, true>()) {
-            *out = {launch_hla2_summary<T, D, C, true>, launch_scan<T, D, true>,
+            *out = {launch_hla2_summary<T, D, C, true>, launch_up_sweep<T, D, true>,
                     launch_hla2_forward<T, D, C, true>};
             return true;
         }
         return false;
     }
     if constexpr (hla2_fits<T, D, C, false>()) {
-        *out = {launch_hla2_summary<T, D, C, false>, launch_scan<T, D, true>,
+        *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
                 launch_hla2_forward<T, D, C, false>};
         return true;
     }

@@ -12,8 +12,8 @@ typedef hipError_t (*StepLaunch)(const StepParams &, hipStream_t);
 
 struct FwdKernels {
     FwdLaunch summary;   // grid (nseg-1, BH): segment summaries from zero state
-    FwdLaunch scan;      // grid (BH): exclusive Blelloch scan (+ initial state)
-    FwdLaunch forward;   // grid (nseg, BH): chunked forward from the carried state
+    FwdLaunch up_sweep;  // grid (BH): up-sweep of the exclusive Blelloch scan
+    FwdLaunch forward;   // grid (nseg, BH): prefix from the up-sweep nodes, chunked forward
 };
 
 // dtype: 0 = fp32, 1 = bf16.  ahla: AHLA family (else HLA-2).  Returns false

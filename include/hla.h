@@ -87,7 +87,8 @@ size_t hla_state_floats(int variant, int d, int dv);
 int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk);
 
 /* Bytes of device workspace hla_forward needs for these arguments
- * (seg_chunks == 0 means the default).  0 when the sequence is one segment. */
+ * (seg_chunks == 0 means the default): B*H*(nseg-1) fp32 segment summaries of
+ * d*d + 2*d*dv + 2*d floats.  0 when the sequence is one segment. */
 size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
                            int chunk, int seg_chunks);
 
@@ -108,8 +109,9 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  * seg_chunks     chunks per segment of the scan; 0 = hla_default_seg_chunks().
  *                The sequence is split into ceil(n / (chunk*seg_chunks))
  *                segments: their summaries are built in parallel, combined by
- *                an exclusive Blelloch scan, and each segment's outputs are
- *                then computed from its carried state.
+ *                an exclusive Blelloch scan (each segment forms its own
+ *                exclusive prefix from the up-sweep nodes), and each
+ *                segment's outputs are then computed from its carried state.
  * state_in       NULL (zero state) or device fp32 [B*H][hla_state_floats()]:
  *                the state after some earlier tokens; the pass continues it
  * state_out      NULL or device fp32 [B*H][hla_state_floats()]: receives the
@@ -130,14 +132,19 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The three stages hla_forward runs, one at a time, on the same arguments:
- *   stage 1  segment summaries of segments 0 .. nseg-2 into the workspace
- *            (page section "4. ... Escaneos Asociativos": segment summaries);
- *   stage 2  exclusive Blelloch scan of those summaries under the
- *            semidirect-product combine, then the initial state folded in
- *            front (same section);
- *   stage 3  chunked forward of every segment from its carried state, and
- *            state_out.
+ * The three stages hla_forward runs, one at a time, on the same arguments
+ * (page section "4. ... Escaneos Asociativos": segment summaries combined by
+ * an exclusive Blelloch scan under the semidirect-product combine).  With
+ * SUMF = d*d + 2*d*dv + 2*d and slot s of head bh at floats
+ * ws + (bh*(nseg-1) + s)*SUMF (parts X | Y | N | y | nv):
+ *   stage 1  the summary of segment s into slot s, s = 0 .. nseg-2;
+ *   stage 2  the up-sweep of the scan, in place: afterwards slot s holds the
+ *            combine of segments s+1-2^b .. s, 2^b the largest power of two
+ *            dividing s+1;
+ *   stage 3  for every segment, the initial state and the slots covering
+ *            the earlier segments folded into its carried state (what the
+ *            scan's down-sweep delivers), then the chunked forward from
+ *            that state, and state_out.
  * Calling stages 1, 2, 3 in order on one stream with identical arguments is
  * exactly hla_forward.  With a single segment stages 1 and 2 enqueue nothing.
  * Meant for callers that time the stages or place them themselves (a caller

@@ -1,9 +1,11 @@
-"""Stage-level parity: the workspace after each stage of the forward pass
-against the fp64 chunk-scan algebra of oracle/chunk_scan.py.
+"""Stage-level parity: the workspace after stage 1 (segment summaries) and
+after stage 2 (the up-sweep of the exclusive Blelloch scan) against the fp64
+chunk-scan algebra of oracle/chunk_scan.py.
 
-Stage 1 writes the segment summaries (X, Y, N, y, nv per segment); stage 2
-leaves the exclusive prefixes in the second half of the workspace.  Layout:
-ws[bh][which][spad][summary floats], which = 0 (summaries), 1 (prefixes).
+Layout: ws[bh][slot][summary floats] (X, Y, N, y, nv).  After stage 1 slot
+s holds the summary of segment s; after stage 2 it holds the combine of
+segments s+1-2^b .. s, 2^b the largest power of two dividing s+1.  Stage 3's
+use of the nodes is covered by the forward parity tests.
 """
 import numpy as np
 import pytest
@@ -39,6 +41,11 @@ def _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g):
     return sums
 
 
+def _node_span(slot):
+    b = ((slot + 1) & -(slot + 1)).bit_length() - 1
+    return slot + 1 - (1 << b), slot
+
+
 @pytest.mark.parametrize("dtype,variant,d,chunk,seg,decay", [
     ("f32", "hla2", 32, 16, 2, False),
     ("bf16", "hla2", 64, 64, 1, False),
@@ -47,11 +54,12 @@ def _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g):
     ("bf16", "hla2", 128, 32, 2, True),
     ("bf16", "ahla", 64, 64, 1, False),
     ("bf16", "ahla", 64, 32, 2, False),
+    ("f32", "ahla", 32, 16, 1, False),
 ])
-def test_summaries_and_prefixes(dtype, variant, d, chunk, seg, decay):
+def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
     import torch
     import causal_streaming_scans_amd as hla
-    B, H, n = 1, 2, 5 * chunk * seg + 7
+    B, H, n = 1, 2, 9 * chunk * seg + 7          # 10 segments: nodes up to 8 wide
     say(f"[stages] {dtype} {variant} d={d} chunk={chunk} seg={seg} decay={decay} n={n}")
     x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="l2norm", seed=31, decay=decay)
     gam = x["gamma"]
@@ -61,44 +69,42 @@ def test_summaries_and_prefixes(dtype, variant, d, chunk, seg, decay):
     nbytes = hla.workspace_bytes(variant, B, H, n, d, d, chunk, seg)
     ws = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
     kw = dict(variant=variant, gamma=gam, chunk=chunk, seg_chunks=seg, workspace=ws)
-    hla.hla_forward_stage(1, q, k, v, **kw)
-    torch.cuda.synchronize()
     seg_len = chunk * seg
     nseg = -(-n // seg_len)
-    spad = 1
-    while spad < nseg:
-        spad *= 2
+    nreal = nseg - 1
     sumf = d * d + 2 * d * d + 2 * d
-    e = ws.cpu().numpy().astype(np.float64).reshape(B * H, 2, spad, sumf)
     tol = 10 * TOL[dtype]
-    for bh in range(B * H):
-        g = 1.0 if gam is None else float(gam[bh % H])
-        ref = _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g)
-        for s in range(nseg - 1):
-            got = _unpack(e[bh, 0, s], d, d)
-            for name, a, b in zip(("X", "Y", "N", "y", "nv"), got, ref[s]):
-                err = rel_l2(a, b)
-                assert err < tol, f"summary head {bh} seg {s} part {name}: {err:.3e}"
+
+    def slots():
+        torch.cuda.synchronize()
+        return ws.cpu().numpy().astype(np.float64).reshape(B * H, nreal, sumf)
+
+    hla.hla_forward_stage(1, q, k, v, **kw)
+    e1 = slots()
     hla.hla_forward_stage(2, q, k, v, **kw)
-    torch.cuda.synchronize()
-    e = ws.cpu().numpy().astype(np.float64).reshape(B * H, 2, spad, sumf)
+    e = slots()
     for bh in range(B * H):
         g = 1.0 if gam is None else float(gam[bh % H])
         ref = _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g)
         if variant.startswith("hla2"):
             items = [dict(S=r[0], C=r[1], W=r[2], m=r[3], u=r[4], l=seg_len) for r in ref]
-            pref = CS.blelloch_exclusive(items, lambda A, Bq: CS.hla2_combine(A, Bq, g),
-                                         lambda: CS.hla2_zero(d, d))
-            want = [(p["S"], p["W"], p["u"]) for p in pref]
-            parts = (0, 2, 4)
+            comb = lambda A, Bq: CS.hla2_combine(A, Bq, g)
+            parts = lambda it: (it["S"], it["C"], it["W"], it["m"], it["u"])
         else:
             items = [dict(M=r[0], P=r[1], E=r[2], mK=r[3], nk=r[4]) for r in ref]
-            pref = CS.blelloch_exclusive(items, CS.ahla_combine, lambda: CS.ahla_zero(d, d))
-            want = [(p["P"], p["E"], p["mK"], p["nk"]) for p in pref]
-            parts = (1, 2, 3, 4)
-        for s in range(1, nseg):
-            got = _unpack(e[bh, 1, s], d, d)
-            for j, pidx in enumerate(parts):
-                err = rel_l2(got[pidx], want[s][j])
-                assert err < tol, f"prefix head {bh} seg {s} part {pidx}: {err:.3e}"
-    say("   summaries and prefixes match")
+            comb = CS.ahla_combine
+            parts = lambda it: (it["M"], it["P"], it["E"], it["mK"], it["nk"])
+        for slot in range(nreal):
+            for name, a, b in zip(("X", "Y", "N", "y", "nv"), _unpack(e1[bh, slot], d, d),
+                                  parts(items[slot])):
+                err = rel_l2(a, b)
+                assert err < tol, f"head {bh} summary {slot} part {name}: {err:.3e}"
+            lo, hi = _node_span(slot)
+            node = items[lo]
+            for j in range(lo + 1, hi + 1):
+                node = comb(node, items[j])
+            got = _unpack(e[bh, slot], d, d)
+            for name, a, b in zip(("X", "Y", "N", "y", "nv"), got, parts(node)):
+                err = rel_l2(a, b)
+                assert err < tol, f"head {bh} slot {slot} [{lo}..{hi}] part {name}: {err:.3e}"
+    say(f"   {nreal} slots per head match")
