@@ -82,25 +82,31 @@ constexpr int ahla_sum_blocks() {
     return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C>)>();
 }
 
-// Y^T tiles of row tile r: Y = Q P0 + L V, with the widened tile (column DV =
-// y1) when `wide`; stored row-major.
-template <typename T, int D, int DV, int RT, int NCG, int YJ, int LDD, int LDV>
-__device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[RT],
-                                             const T *Pt, const T *V, T *Y, int r, int cg,
-                                             int tau, bool wide) {
+// Y^T tiles of row tile R: Y = Q P0 + L V, with the widened tile (column DV =
+// y1) when `wide`; stored row-major after every product.
+template <typename T, int D, int DV, int R, int NCG, int YJ, int LDD, int LDV>
+__device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
+                                             const T *Pt, const T *V, T *Y, int cg, int tau,
+                                             bool wide) {
     constexpr int nTV = DV / 16;
     const int g4 = (lane_id() >> 4) << 2;
+    f32x4 y[YJ];
 #pragma unroll
     for (int jj = 0; jj < YJ; ++jj) {
         const int jv = cg + jj * NCG;
+        y[jj] = zero4();
         if (jv < nTV || (wide && jv == nTV)) {
-            const f32x4 y = mma_nt_f(zero4(), Pt + 16 * jv * LDD, LDD, qf);
+            const f32x4 yq = mma_nt_f(zero4(), Pt + 16 * jv * LDD, LDD, qf);
             f32x4 yc = zero4();
 #pragma unroll
-            for (int s = 0; s < RT; ++s)
-                if (s <= r) yc = mma16(yc, ld_frag_t(V + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
-            store4(Y + tau * LDV + 16 * jv + g4, y + yc);
+            for (int s = 0; s <= R; ++s) yc = mma16(yc, ld_frag_t(V + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
+            y[jj] = yq + yc;
         }
+    }
+#pragma unroll
+    for (int jj = 0; jj < YJ; ++jj) {
+        const int jv = cg + jj * NCG;
+        if (jv < nTV || (wide && jv == nTV)) store4(Y + tau * LDV + 16 * jv + g4, y[jj]);
     }
 }
 
@@ -117,7 +123,6 @@ void ahla_forward_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const int tau = 16 * r + col;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const bool ratio = p.ratio != 0;
@@ -244,43 +249,46 @@ void ahla_forward_kernel(FwdParams p) {
         if (n0 < t_end) load_chunk(n0, ncv);
         __syncthreads();
 
-        Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
-        ahla_y_tiles<T, D, DV, RT, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, r, cg, tau, need_u);
-        // carried part of the output and of its denominator (row DV)
-        f32x4 accO[G::OJ];
+        with_row_tile<RT>(r, [&](auto rt) {
+            constexpr int R = decltype(rt)::value;
+            const int tau = 16 * R + col;
+            Frag16<T> Lf[R + 1];
+            scores_t<T, D, R, LDD, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, need_u);
+            // carried part of the output and of its denominator (row DV)
+            f32x4 accO[G::OJ];
 #pragma unroll
-        for (int jj = 0; jj < G::OJ; ++jj) {
-            const int jv = cg + jj * NCG;
-            accO[jj] = zero4();
-            if (jv < nTV) accO[jj] = mma_nt_f(zero4(), sm.Et + 16 * jv * LDD, LDD, qf);
-        }
-        f32x4 accD = zero4();
-        if (ratio) accD = mma_nt_f(zero4(), sm.Et + DV * LDD, LDD, qf);
-        __syncthreads();
-
-        // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
-        float rden = 1.f;
-        if (ratio) {
-            f32x4 dc = zero4();
-#pragma unroll
-            for (int s = 0; s < RT; ++s)
-                if (s <= r) dc = mma16(dc, ld_frag_t(sm.Y + 16 * s * LDV + DV, LDV), Lf[s]);
-            rden = 1.f / __shfl(accD[0] + dc[0], col);
-        }
-#pragma unroll
-        for (int jj = 0; jj < G::OJ; ++jj) {
-            const int jv = cg + jj * NCG;
-            if (jv < nTV) {
-                f32x4 oc = zero4();
-#pragma unroll
-                for (int s = 0; s < RT; ++s)
-                    if (s <= r) oc = mma16(oc, ld_frag_t(sm.Y + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
-                f32x4 ov = accO[jj] + oc;
-                if (ratio) ov *= rden;
-                if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+            for (int jj = 0; jj < G::OJ; ++jj) {
+                const int jv = cg + jj * NCG;
+                accO[jj] = zero4();
+                if (jv < nTV) accO[jj] = mma_nt_f(zero4(), sm.Et + 16 * jv * LDD, LDD, qf);
             }
-        }
+            f32x4 accD = zero4();
+            if (ratio) accD = mma_nt_f(zero4(), sm.Et + DV * LDD, LDD, qf);
+            __syncthreads();
+
+            // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
+            float rden = 1.f;
+            if (ratio) {
+                f32x4 dc = zero4();
+#pragma unroll
+                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_t(sm.Y + 16 * s * LDV + DV, LDV), Lf[s]);
+                rden = 1.f / __shfl(accD[0] + dc[0], col);
+            }
+#pragma unroll
+            for (int jj = 0; jj < G::OJ; ++jj) {
+                const int jv = cg + jj * NCG;
+                if (jv < nTV) {
+                    f32x4 oc = zero4();
+#pragma unroll
+                    for (int s = 0; s <= R; ++s)
+                        oc = mma16(oc, ld_frag_t(sm.Y + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
+                    f32x4 ov = accO[jj] + oc;
+                    if (ratio) ov *= rden;
+                    if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                }
+            }
+        });
         // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
             mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
@@ -340,7 +348,6 @@ void ahla_summary_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const int tau = 16 * r + col;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
@@ -398,9 +405,13 @@ void ahla_summary_kernel(FwdParams p) {
 
         RowFrags<T, D> qf;
         qf.load(sm.Q + 16 * r * LDD, LDD);
-        Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, false>(Lf, sm.K, qf, r, tau, nullptr, 1);
-        ahla_y_tiles<T, D, DV, RT, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, r, cg, tau, true);
+        with_row_tile<RT>(r, [&](auto rt) {
+            constexpr int R = decltype(rt)::value;
+            const int tau = 16 * R + col;
+            Frag16<T> Lf[R + 1];
+            scores_t<T, D, R, LDD, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, true);
+        });
         __syncthreads();
 
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {

@@ -1,6 +1,8 @@
 // chunk_common.h -- pieces shared by the chunk kernels of HLA-2 and AHLA.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "params.h"
 
@@ -18,6 +20,18 @@ struct WaveShape {
     static constexpr int NW = RT * NCG;
     static constexpr int NT = NW * kWave;
 };
+
+// f(std::integral_constant<int, r>) for the wave-uniform row tile r in
+// [0, RT): each wave runs the intra-chunk phases unrolled for its own row
+// tile, with no per-tile branches, so every operand load of a phase can be
+// issued ahead of its products.
+template <int RT, int I = 0, typename F>
+__device__ __forceinline__ void with_row_tile(int r, F &&f) {
+    if constexpr (I < RT) {
+        if (r == I) f(std::integral_constant<int, I>{});
+        else with_row_tile<RT, I + 1>(r, static_cast<F &&>(f));
+    }
+}
 
 // One thread's share of a [C][COLS] chunk tile, held in registers between the
 // global load (issued a chunk ahead) and the LDS store.  The loads are

@@ -158,54 +158,65 @@ constexpr int hla_min_blocks() {
 }
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int hla2_fwd_blocks() {
-    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdLds<T, D, DV, C, DECAY>)>();
+    const int b = hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdLds<T, D, DV, C, DECAY>)>();
+    return b > 2 ? 2 : b;
 }
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int hla2_sum_blocks() {
     return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2SumSmem<T, D, DV, C, DECAY>)>();
 }
 
-// L^T tiles of row tile r as operand fragments: Lf[s] holds
-// (D_g * tril(Q K^T))^T[sigma in tile s][tau in tile r], s <= r.
-template <typename T, int D, int RT, int LDD, bool DECAY>
-__device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[RT], const T *K, const RowFrags<T, D> &qf,
-                                         int r, int tau, const float *gp, int gexp) {
+// L^T tiles of row tile R as operand fragments: Lf[s] holds
+// (D_g * tril(Q K^T))^T[sigma in tile s][tau in tile R], s <= R.  Only the
+// diagonal tile s == R needs the causal mask.
+template <typename T, int D, int R, int LDD, bool DECAY>
+__device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[R + 1], const T *K, const RowFrags<T, D> &qf,
+                                         int tau, const float *gp, int gexp) {
     const int g4 = (lane_id() >> 4) << 2;
+    f32x4 a[R + 1];
 #pragma unroll
-    for (int s = 0; s < RT; ++s) {
-        if (s <= r) {
-            f32x4 a = mma_nt_f(zero4(), K + 16 * s * LDD, LDD, qf);
+    for (int s = 0; s <= R; ++s) a[s] = mma_nt_f(zero4(), K + 16 * s * LDD, LDD, qf);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sigma = 16 * s + g4 + i;
-                float m = 0.f;
-                if (sigma <= tau) m = DECAY ? a[i] * gp[gexp * (tau - sigma)] : a[i];
-                a[i] = m;
-            }
-            Lf[s] = to_frag<T>(a);
+    for (int s = 0; s <= R; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sigma = 16 * s + g4 + i;
+            float m = a[s][i];
+            if (s == R && sigma > tau) m = 0.f;
+            else if (DECAY) m *= gp[gexp * (tau - sigma)];
+            a[s][i] = m;
         }
+        Lf[s] = to_frag<T>(a[s]);
     }
 }
 
-// Z^T tiles of row tile r: Z = diag(g^(tau+1)) Q S0 + L K, stored row-major
+// Z^T tiles of row tile R: Z = diag(g^(tau+1)) Q S0 + L K, stored row-major
 // (times w) into Zd.  Shared by the forward and summary kernels.
-template <typename T, int D, int C, int RT, int NCG, int ZJ, int LDD, bool DECAY>
-__device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[RT],
+template <typename T, int D, int R, int NCG, int ZJ, int LDD, bool DECAY>
+__device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
                                         const T *St, const T *K, T *Zd, T *Zwd, float wz,
-                                        const float *gp, int r, int cg, int tau) {
+                                        const float *gp, int cg, int tau) {
     const int g4 = (lane_id() >> 4) << 2;
+    f32x4 z[ZJ];
+#pragma unroll
+    for (int jj = 0; jj < ZJ; ++jj) {
+        const int jt = cg + jj * NCG;
+        z[jj] = zero4();
+        if (jt < D / 16) {
+            f32x4 zq = mma_nt_f(zero4(), St + 16 * jt * LDD, LDD, qf);
+            f32x4 zc = zero4();
+#pragma unroll
+            for (int s = 0; s <= R; ++s) zc = mma16(zc, ld_frag_t(K + 16 * s * LDD + 16 * jt, LDD), Lf[s]);
+            z[jj] = (DECAY ? zq * gp[tau + 1] : zq) + zc;
+        }
+    }
+    // the stores after every product, so no load above waits for them
 #pragma unroll
     for (int jj = 0; jj < ZJ; ++jj) {
         const int jt = cg + jj * NCG;
         if (jt < D / 16) {
-            f32x4 z = mma_nt_f(zero4(), St + 16 * jt * LDD, LDD, qf);
-            f32x4 zc = zero4();
-#pragma unroll
-            for (int s = 0; s < RT; ++s)
-                if (s <= r) zc = mma16(zc, ld_frag_t(K + 16 * s * LDD + 16 * jt, LDD), Lf[s]);
-            z = (DECAY ? z * gp[tau + 1] : z) + zc;
-            if (Zd) store4(Zd + tau * LDD + 16 * jt + g4, z);
-            if (Zwd) store4(Zwd + tau * LDD + 16 * jt + g4, z * wz);
+            if (Zd) store4(Zd + tau * LDD + 16 * jt + g4, z[jj]);
+            if (Zwd) store4(Zwd + tau * LDD + 16 * jt + g4, z[jj] * wz);
         }
     }
 }
@@ -226,7 +237,6 @@ void hla2_forward_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const int tau = 16 * r + col;          // the lane's token within the chunk
     const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
@@ -355,59 +365,62 @@ void hla2_forward_kernel(FwdParams p) {
         if (n0 < t_end) load_chunk(n0, ncv);
         __syncthreads();
 
-        // ---- a-2: L^T for this row tile, as operand fragments
-        Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
+        with_row_tile<RT>(r, [&](auto rt) {
+            constexpr int R = decltype(rt)::value;
+            const int tau = 16 * R + col;    // the lane's token within the chunk
+            // ---- a-2: L^T for this row tile, as operand fragments
+            Frag16<T> Lf[R + 1];
+            scores_t<T, D, R, LDD, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
 
-        // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
-        const float wz = DECAY ? (tau < cv ? sm.gp[2 * (cv - 1 - tau)] : 0.f) : 1.f;
-        z_tiles<T, D, C, RT, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, sm.Z,
-                                                     DECAY ? sm.Zw : nullptr, wz, sm.gp, r, cg, tau);
-        // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T; the
-        // denominator's carried part q . u0 is row DV of the widened product
-        f32x4 accO[G::OJ];
+            // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
+            const float wz = DECAY ? (tau < cv ? sm.gp[2 * (cv - 1 - tau)] : 0.f) : 1.f;
+            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, sm.Z, DECAY ? sm.Zw : nullptr,
+                                                     wz, sm.gp, cg, tau);
+            // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T; the
+            // denominator's carried part q . u0 is row DV of the widened product
+            f32x4 accO[G::OJ];
 #pragma unroll
-        for (int jj = 0; jj < G::OJ; ++jj) {
-            const int jv = cg + jj * NCG;
-            accO[jj] = zero4();
-            if (jv < nTV) {
-                accO[jj] = mma_nt_f(zero4(), sm.Wt + 16 * jv * LDD, LDD, qf);
-                if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
+            for (int jj = 0; jj < G::OJ; ++jj) {
+                const int jv = cg + jj * NCG;
+                accO[jj] = zero4();
+                if (jv < nTV) {
+                    accO[jj] = mma_nt_f(zero4(), sm.Wt + 16 * jv * LDD, LDD, qf);
+                    if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
+                }
             }
-        }
-        f32x4 accD = zero4();
-        if (ratio) {
-            accD = mma_nt_f(zero4(), sm.Wt + DV * LDD, LDD, qf);
-            if (DECAY) accD *= sm.gp[2 * (tau + 1)];
-        }
-        __syncthreads();
+            f32x4 accD = zero4();
+            if (ratio) {
+                accD = mma_nt_f(zero4(), sm.Wt + DV * LDD, LDD, qf);
+                if (DECAY) accD *= sm.gp[2 * (tau + 1)];
+            }
+            __syncthreads();
 
-        // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
-        Frag16<T> Pf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Pf, sm.Z, qf, r, tau, sm.gp, 2);
-        float rden = 1.f;
-        if (ratio) {
-            // den = q . u0 + P 1: row DV of the widened O^T, held in slot 0 of
-            // the token's lane in group 0
-            f32x4 dc = zero4();
+            // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
+            Frag16<T> Pf[R + 1];
+            scores_t<T, D, R, LDD, DECAY>(Pf, sm.Z, qf, tau, sm.gp, 2);
+            float rden = 1.f;
+            if (ratio) {
+                // den = q . u0 + P 1: row DV of the widened O^T, held in slot 0
+                // of the token's lane in group 0
+                f32x4 dc = zero4();
 #pragma unroll
-            for (int s = 0; s < RT; ++s)
-                if (s <= r) dc = mma16(dc, ld_frag_t(sm.V + 16 * s * LDV + DV, LDV), Pf[s]);
-            rden = 1.f / __shfl(accD[0] + dc[0], col);
-        }
-#pragma unroll
-        for (int jj = 0; jj < G::OJ; ++jj) {
-            const int jv = cg + jj * NCG;
-            if (jv < nTV) {
-                f32x4 oc = zero4();
-#pragma unroll
-                for (int s = 0; s < RT; ++s)
-                    if (s <= r) oc = mma16(oc, ld_frag_t(sm.V + 16 * s * LDV + 16 * jv, LDV), Pf[s]);
-                f32x4 ov = accO[jj] + oc;
-                if (ratio) ov *= rden;
-                if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_t(sm.V + 16 * s * LDV + DV, LDV), Pf[s]);
+                rden = 1.f / __shfl(accD[0] + dc[0], col);
             }
-        }
+#pragma unroll
+            for (int jj = 0; jj < G::OJ; ++jj) {
+                const int jv = cg + jj * NCG;
+                if (jv < nTV) {
+                    f32x4 oc = zero4();
+#pragma unroll
+                    for (int s = 0; s <= R; ++s)
+                        oc = mma16(oc, ld_frag_t(sm.V + 16 * s * LDV + 16 * jv, LDV), Pf[s]);
+                    f32x4 ov = accO[jj] + oc;
+                    if (ratio) ov *= rden;
+                    if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                }
+            }
+        });
 
         // ---- a-7: advance the carried state by this chunk
         const float gc = DECAY ? sm.gp[cv] : 1.f;
@@ -489,7 +502,6 @@ void hla2_summary_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const int tau = 16 * r + col;
     const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
@@ -551,12 +563,16 @@ void hla2_summary_kernel(FwdParams p) {
 
         RowFrags<T, D> qf;
         qf.load(sm.Q + 16 * r * LDD, LDD);
-        Frag16<T> Lf[RT];
-        scores_t<T, D, RT, LDD, DECAY>(Lf, sm.K, qf, r, tau, sm.gp, 1);
-        // Z rows weighted by g^(2(c-1-tau)): only the W and u updates use Z here
-        const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
-        z_tiles<T, D, C, RT, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz,
-                                                     sm.gp, r, cg, tau);
+        with_row_tile<RT>(r, [&](auto rt) {
+            constexpr int R = decltype(rt)::value;
+            const int tau = 16 * R + col;
+            Frag16<T> Lf[R + 1];
+            scores_t<T, D, R, LDD, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
+            // Z rows weighted by g^(2(c-1-tau)): only the W and u updates use Z here
+            const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
+            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz, sm.gp, cg,
+                                                     tau);
+        });
         __syncthreads();
 
         const float gc = DECAY ? sm.gp[cv] : 1.f;
