@@ -290,22 +290,24 @@ void ahla_forward_kernel(FwdParams p) {
             }
         });
         // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
+        // all products first, then the T-typed copies
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
             mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
             mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
-#pragma unroll
-            for (int x = 0; x < PBk::BR; ++x)
-#pragma unroll
-                for (int y = 0; y < PBk::BR; ++y) {
-                    const int oo = (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4;
-                    store4(sm.Pt + oo, accP[pb][x][y]);
-                    store4(sm.Et + oo, accE[pb][x][y]);
-                }
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
                 accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
                 accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+            });
+        }
+        for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            const int oo = (16 * tv + col) * LDD + 16 * ti + g4;
+            store4(sm.Pt + oo, accP[pb][x][y]);
+            store4(sm.Et + oo, accE[pb][x][y]);
+        });
+        if (need_u) {
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
                 store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
                 store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, accNK[j]);
             });
@@ -417,11 +419,6 @@ void ahla_summary_kernel(FwdParams p) {
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
             mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
             mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
-#pragma unroll
-            for (int x = 0; x < PBk::BR; ++x)
-#pragma unroll
-                for (int y = 0; y < PBk::BR; ++y)
-                    store4(sm.Pt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accP[pb][x][y]);
         });
         for_blocks<MBk, NW>(w, [&](int pb, int ti0, int tj0) {
             mma_tn_blk<MBk::BR, C>(accM[pb], sm.K + 16 * ti0, LDD, sm.Q + 16 * tj0, LDD);
@@ -429,6 +426,12 @@ void ahla_summary_kernel(FwdParams p) {
         for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
             accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
             accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+        });
+        // the running widened P's T-typed copy after every product of the chunk
+        for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[pb][x][y]);
+        });
+        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
             store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
         });
         c0 = n0;

@@ -427,6 +427,8 @@ void hla2_forward_kernel(FwdParams p) {
         const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
         const T *KA = DECAY ? sm.Kw : sm.K;
         const T *ZA = DECAY ? sm.Zw : sm.Z;
+        // all products first, then the T-typed copies, so no operand load
+        // waits behind a store
         for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
             if (DECAY) {
 #pragma unroll
@@ -435,11 +437,6 @@ void hla2_forward_kernel(FwdParams p) {
                     for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
             mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
-#pragma unroll
-            for (int x = 0; x < SB::BR; ++x)
-#pragma unroll
-                for (int y = 0; y < SB::BR; ++y)
-                    store4(sm.St + (16 * (tj0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accS[pb][x][y]);
         });
         for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
             if (DECAY) {
@@ -449,16 +446,21 @@ void hla2_forward_kernel(FwdParams p) {
                     for (int y = 0; y < WB::BR; ++y) accW[pb][x][y] *= gc2;
             }
             mma_tn_blk<WB::BR, C>(accW[pb], ZA + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-#pragma unroll
-            for (int x = 0; x < WB::BR; ++x)
-#pragma unroll
-                for (int y = 0; y < WB::BR; ++y)
-                    store4(sm.Wt + (16 * (tv0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accW[pb][x][y]);
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
                 accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], ZA + 16 * ti, LDD,
                                          sm.V + DV, LDV);
+            });
+        }
+        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
+        });
+        for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[pb][x][y]);
+        });
+        if (need_u) {
+            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
                 store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, accU[j]);
             });
         }
@@ -587,11 +589,6 @@ void hla2_summary_kernel(FwdParams p) {
                     for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
             }
             mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
-#pragma unroll
-            for (int x = 0; x < SB::BR; ++x)
-#pragma unroll
-                for (int y = 0; y < SB::BR; ++y)
-                    store4(sm.St + (16 * (tj0 + y) + col) * LDD + 16 * (ti0 + x) + g4, accS[pb][x][y]);
         });
         for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
             if (DECAY) {
@@ -610,6 +607,10 @@ void hla2_summary_kernel(FwdParams p) {
         for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
             accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], sm.Z + 16 * ti, LDD, sm.V + DV, LDV);
             accM[j] = mma_tn_tile<C>(DECAY ? accM[j] * gc : accM[j], QA + 16 * ti, LDD, sm.V + DV, LDV);
+        });
+        // the running S's T-typed copy after every product of the chunk
+        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
         });
         c0 = n0;
         cv = ncv;
