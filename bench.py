@@ -132,10 +132,12 @@ def main():
     o = torch.empty((B, H, n, dv), dtype=torch.bfloat16, device=dev)
     ws_bytes = hla.workspace_bytes(variant, B, H, n, d, dv, chunk, seg)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    kw = dict(variant=variant, chunk=chunk, seg_chunks=seg, out=o, workspace=ws)
+    # arguments marshalled once: each stage below is one library call
+    plan = hla.ForwardPlan(q, k, v, variant=variant, chunk=chunk, seg_chunks=seg, out=o,
+                           workspace=ws, staged=True)
 
     def step():
-        hla.hla_forward(q, k, v, **kw)
+        plan.run()
 
     for _ in range(args.warmup):
         step()
@@ -151,7 +153,7 @@ def main():
     for s in range(K):
         ev[s][0].record()
         for stage in (1, 2, 3):
-            hla.hla_forward_stage(stage, q, k, v, **kw)
+            plan.stage(stage)
             ev[s][stage].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -206,13 +208,14 @@ def main():
         kd = torch.randn((dw.B, dw.H, dw.d), device=dev).to(torch.bfloat16)
         vd = torch.randn((dw.B, dw.H, dw.dv), device=dev).to(torch.bfloat16)
         od = torch.empty((dw.B, dw.H, dw.dv), dtype=torch.bfloat16, device=dev)
+        splan = hla.StepPlan(qd, kd, vd, state, variant="ahla", out=od)
         for _ in range(10):
-            hla.hla_step(qd, kd, vd, state, variant="ahla", out=od)
+            splan.run()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.decode_steps):
-            hla.hla_step(qd, kd, vd, state, variant="ahla", out=od)
+            splan.run()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.decode_steps

@@ -20,7 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["HLAError", "VARIANTS", "load", "library_path", "hla_forward", "hla_forward_stage",
+__all__ = ["HLAError", "VARIANTS", "load", "library_path", "ForwardPlan", "StepPlan",
+           "hla_forward", "hla_forward_stage",
            "hla_step",
            "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
 
@@ -133,55 +134,84 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class ForwardPlan:
+    """The arguments of one forward pass, checked and marshalled once.
+
+    ``run()`` enqueues the whole pass and ``stage(s)`` one stage of it (see
+    hla_forward_stage), each as a single call into the library on the plan's
+    stream; the plan keeps every tensor it points at alive.  For callers that
+    launch the same shapes repeatedly (a timing loop, a decode server)."""
+
+    def __init__(self, q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
+                 state_in=None, state_out=None, out=None, workspace=None, stream=None,
+                 staged=False):
+        import torch
+        lib = load()
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _check_device_tensor(name, t)
+        if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+            raise HLAError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}: "
+                           "expected [B,H,n,d], [B,H,n,d], [B,H,n,dv]")
+        if not (q.dtype == k.dtype == v.dtype):
+            raise HLAError("q, k, v must share one dtype")
+        B, H, n, d = q.shape
+        dv = v.shape[3]
+        vid = _variant(variant)
+        if out is None:
+            out = torch.empty((B, H, n, dv), dtype=q.dtype, device=q.device)
+        else:
+            _check_device_tensor("out", out)
+            if out.shape != (B, H, n, dv) or out.dtype != q.dtype:
+                raise HLAError("out has the wrong shape or dtype")
+        stf = state_floats(vid, d, dv)
+        for name, t in (("state_in", state_in), ("state_out", state_out)):
+            if t is not None:
+                _check_device_tensor(name, t)
+                if t.dtype != torch.float32 or t.numel() != B * H * stf:
+                    raise HLAError(f"{name} must be fp32 with B*H*{stf} elements")
+        need = workspace_bytes(vid, B, H, n, d, dv, chunk, seg_chunks)
+        if workspace is None and need > 0:
+            if staged:
+                raise HLAError("hla_forward_stage needs the caller's workspace (shared by the stages)")
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        self.out = out
+        self._keep = (q, k, v, out, state_in, state_out, workspace)
+        self._gamma, g_ptr = _gamma_arg(gamma, H)
+        VP, CI = ctypes.c_void_p, ctypes.c_int
+        ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        self._args = (VP(q.data_ptr()), VP(k.data_ptr()), VP(v.data_ptr()), VP(out.data_ptr()),
+                      CI(B), CI(H), CI(n), CI(d), CI(dv), CI(_dtype_code(q)), CI(vid), g_ptr,
+                      CI(chunk), CI(seg_chunks),
+                      VP(state_in.data_ptr() if state_in is not None else None),
+                      VP(state_out.data_ptr() if state_out is not None else None),
+                      VP(workspace.data_ptr() if workspace is not None else None),
+                      ctypes.c_size_t(ws_len), _stream_ptr(stream, q.device))
+        self._dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+        self._lib = lib
+
+    def _call(self, fn, *lead):
+        import torch
+        if torch.cuda.current_device() == self._dev:
+            rc = fn(*lead, *self._args)
+        else:
+            with torch.cuda.device(self._dev):
+                rc = fn(*lead, *self._args)
+        if rc != 0:
+            raise HLAError(f"{fn.__name__} failed: {status_str(rc)} (code {rc})")
+        return self.out
+
+    def run(self):
+        return self._call(self._lib.hla_forward)
+
+    def stage(self, stage: int):
+        return self._call(self._lib.hla_forward_stage, ctypes.c_int(int(stage)))
+
+
 def _forward_call(stage, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
                   workspace, stream):
-    import torch
-    lib = load()
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_device_tensor(name, t)
-    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
-        raise HLAError(f"shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}: "
-                       "expected [B,H,n,d], [B,H,n,d], [B,H,n,dv]")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise HLAError("q, k, v must share one dtype")
-    B, H, n, d = q.shape
-    dv = v.shape[3]
-    vid = _variant(variant)
-    if out is None:
-        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=q.device)
-    else:
-        _check_device_tensor("out", out)
-        if out.shape != (B, H, n, dv) or out.dtype != q.dtype:
-            raise HLAError("out has the wrong shape or dtype")
-    stf = state_floats(vid, d, dv)
-    for name, t in (("state_in", state_in), ("state_out", state_out)):
-        if t is not None:
-            _check_device_tensor(name, t)
-            if t.dtype != torch.float32 or t.numel() != B * H * stf:
-                raise HLAError(f"{name} must be fp32 with B*H*{stf} elements")
-    need = workspace_bytes(vid, B, H, n, d, dv, chunk, seg_chunks)
-    if workspace is None and need > 0:
-        if stage is not None:
-            raise HLAError("hla_forward_stage needs the caller's workspace (shared by the stages)")
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    g_keep, g_ptr = _gamma_arg(gamma, H)
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-            B, H, n, d, dv, _dtype_code(q), vid, g_ptr, chunk, seg_chunks,
-            state_in.data_ptr() if state_in is not None else None,
-            state_out.data_ptr() if state_out is not None else None,
-            ws_ptr, ws_len, _stream_ptr(stream, q.device))
-    with torch.cuda.device(q.device):
-        if stage is None:
-            rc = lib.hla_forward(*args)
-        else:
-            rc = lib.hla_forward_stage(int(stage), *args)
-    del g_keep
-    if rc != 0:
-        name = "hla_forward" if stage is None else f"hla_forward_stage({stage})"
-        raise HLAError(f"{name} failed: {status_str(rc)} (code {rc})")
-    return out
+    plan = ForwardPlan(q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
+                       workspace, stream, staged=stage is not None)
+    return plan.run() if stage is None else plan.stage(stage)
 
 
 def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
@@ -205,28 +235,47 @@ def hla_forward_stage(stage, q, k, v, variant="hla2", gamma=None, chunk: int = 6
                          out, workspace, stream)
 
 
+class StepPlan:
+    """One decode step's arguments, checked and marshalled once; ``run()``
+    enqueues the step (state updated in place) as a single library call."""
+
+    def __init__(self, q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):
+        import torch
+        lib = load()
+        for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
+            _check_device_tensor(name, t)
+        if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+            raise HLAError("expected q, k: [B, H, d], v: [B, H, dv]")
+        B, H, d = q.shape
+        dv = v.shape[2]
+        vid = _variant(variant)
+        if state.dtype != torch.float32 or state.numel() != B * H * state_floats(vid, d, dv):
+            raise HLAError("state must be fp32 with B*H*state_floats elements")
+        if out is None:
+            out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+        self.out = out
+        self._keep = (q, k, v, out, state)
+        self._gamma, g_ptr = _gamma_arg(gamma, H)
+        VP, CI = ctypes.c_void_p, ctypes.c_int
+        self._args = (VP(q.data_ptr()), VP(k.data_ptr()), VP(v.data_ptr()), VP(out.data_ptr()),
+                      CI(B), CI(H), CI(d), CI(dv), CI(_dtype_code(q)), CI(vid), g_ptr,
+                      VP(state.data_ptr()), _stream_ptr(stream, q.device))
+        self._dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+        self._lib = lib
+
+    def run(self):
+        import torch
+        if torch.cuda.current_device() == self._dev:
+            rc = self._lib.hla_step(*self._args)
+        else:
+            with torch.cuda.device(self._dev):
+                rc = self._lib.hla_step(*self._args)
+        if rc != 0:
+            raise HLAError(f"hla_step failed: {status_str(rc)} (code {rc})")
+        return self.out
+
+
 def hla_step(q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):
     """One decode step.  q, k: [B, H, d]; v: [B, H, dv]; state: fp32 device
     tensor with B*H*state_floats elements, updated in place.  Returns o."""
-    import torch
-    lib = load()
-    for name, t in (("q", q), ("k", k), ("v", v), ("state", state)):
-        _check_device_tensor(name, t)
-    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
-        raise HLAError("expected q, k: [B, H, d], v: [B, H, dv]")
-    B, H, d = q.shape
-    dv = v.shape[2]
-    vid = _variant(variant)
-    if state.dtype != torch.float32 or state.numel() != B * H * state_floats(vid, d, dv):
-        raise HLAError("state must be fp32 with B*H*state_floats elements")
-    if out is None:
-        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
-    g_keep, g_ptr = _gamma_arg(gamma, H)
-    with torch.cuda.device(q.device):
-        rc = lib.hla_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, d, dv,
-                          _dtype_code(q), vid, g_ptr, state.data_ptr(),
-                          _stream_ptr(stream, q.device))
-    del g_keep
-    if rc != 0:
-        raise HLAError(f"hla_step failed: {status_str(rc)} (code {rc})")
-    return out
+    return StepPlan(q, k, v, state, variant, gamma, out, stream).run()

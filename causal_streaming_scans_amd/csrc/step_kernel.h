@@ -12,8 +12,9 @@
 //        nk <- nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
 //
 // One workgroup of NT threads per (b,h).  The state is read once and written
-// once (fp32, row-major); rows are streamed with consecutive threads on
-// consecutive columns so every access is coalesced.
+// once (fp32, row-major), with consecutive threads on consecutive columns so
+// every access is coalesced.  Every thread issues all of its state loads at
+// the start, so the step costs one memory round trip plus its reductions.
 #pragma once
 
 #include "device_common.h"
@@ -23,12 +24,14 @@ namespace hla {
 
 template <typename T, int D, int DV, bool AHLA, int NT>
 __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
-    constexpr int RG = NT / DV;   // row groups for the column-parallel passes
-    static_assert(NT % DV == 0 && NT % D == 0, "block shape");
+    constexpr int RG = NT / DV;     // row groups of the column-parallel passes
+    constexpr int RPT = D / RG;     // rows per thread in those passes
+    constexpr int TPR = NT / D;     // threads per row of the S pass (HLA-2)
+    constexpr int CPT = D / TPR;    // S columns per thread
+    static_assert(NT % DV == 0 && NT % D == 0 && D % RG == 0 && D % TPR == 0, "block shape");
     __shared__ float sq[D], sk[D], sv[DV], sz[D], sy[DV];
     __shared__ float part[RG][DV];
     __shared__ float red[NT / kWave];
-    __shared__ float scal[2];
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
@@ -40,18 +43,14 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
     constexpr int STF = AHLA ? ahla_state_floats(D, DV) : hla2_state_floats(D, DV);
     float *st = p.state + (size_t)bh * STF;
-
-    for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
-    for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
-    __syncthreads();
-
     const int col = tid % DV, rg = tid / DV;
+
     auto block_sum = [&](float x) -> float {
-        // sum over the whole block
         for (int m = kWave / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
         if ((tid & (kWave - 1)) == 0) red[tid / kWave] = x;
         __syncthreads();
         float s = 0.f;
+#pragma unroll
         for (int i = 0; i < NT / kWave; ++i) s += red[i];
         __syncthreads();
         return s;
@@ -59,83 +58,114 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
     if (!AHLA) {
         float *S = st, *W = st + D * D, *u = st + D * D + D * DV;
-        // S <- g S + k k^T ; z = S q   (rows split over D threads-groups)
-        constexpr int TPR = NT / D;            // threads per row
         const int row = tid / TPR, sub = tid % TPR;
+        float sv_[CPT], wv[RPT], uv = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) sv_[i] = S[row * D + sub + i * TPR];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) wv[i] = W[(rg + i * RG) * DV + col];
+        if (tid < D) uv = u[tid];
+        for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
+        for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
+        __syncthreads();
+        // S <- g S + k k^T ; z = S q
         float zp = 0.f;
-        for (int c = sub; c < D; c += TPR) {
-            const float s = g * S[row * D + c] + sk[row] * sk[c];
-            S[row * D + c] = s;
-            zp += s * sq[c];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = sub + i * TPR;
+            const float sn = g * sv_[i] + sk[row] * sk[c];
+            S[row * D + c] = sn;
+            zp += sn * sq[c];
         }
         for (int m = TPR / 2; m >= 1; m >>= 1) zp += __shfl_xor(zp, m, TPR);
         if (sub == 0) sz[row] = zp;
         __syncthreads();
         // W <- g^2 W + z v^T ; partial o = q^T W
         float op = 0.f;
-        for (int r = rg; r < D; r += RG) {
-            const float wv = g2 * W[r * DV + col] + sz[r] * sv[col];
-            W[r * DV + col] = wv;
-            op += sq[r] * wv;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float wn = g2 * wv[i] + sz[r] * sv[col];
+            W[r * DV + col] = wn;
+            op += sq[r] * wn;
         }
         part[rg][col] = op;
         // u <- g^2 u + z ; den = q^T u
         float dp = 0.f;
-        for (int r = tid; r < D; r += NT) {
-            const float uv = g2 * u[r] + sz[r];
-            u[r] = uv;
-            dp += sq[r] * uv;
+        if (tid < D) {
+            const float un = g2 * uv + sz[tid];
+            u[tid] = un;
+            dp = sq[tid] * un;
         }
-        const float den = block_sum(dp);   // contains the barrier that publishes part[]
+        const float den = block_sum(dp);   // its barrier also publishes part[]
         if (tid < DV) {
             float s = 0.f;
+#pragma unroll
             for (int i = 0; i < RG; ++i) s += part[i][tid];
             if (p.ratio) s = s / den;
             o[tid] = from_f<T>(s);
         }
     } else {
         float *P = st, *E = st + D * DV, *mK = st + 2 * D * DV, *nk = mK + D;
+        float pv[RPT], ev[RPT], mkv = 0.f, nkv = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            pv[i] = P[(rg + i * RG) * DV + col];
+            ev[i] = E[(rg + i * RG) * DV + col];
+        }
+        if (tid < D) {
+            mkv = mK[tid];
+            nkv = nk[tid];
+        }
+        for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
+        for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
+        __syncthreads();
         // P <- P + k v^T ; partial y = P^T q
         float yp = 0.f;
-        for (int r = rg; r < D; r += RG) {
-            const float pv = P[r * DV + col] + sk[r] * sv[col];
-            P[r * DV + col] = pv;
-            yp += sq[r] * pv;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float pn = pv[i] + sk[r] * sv[col];
+            P[r * DV + col] = pn;
+            yp += sq[r] * pn;
         }
         part[rg][col] = yp;
         // mK <- mK + k ; s = q . mK
         float sp = 0.f;
-        for (int r = tid; r < D; r += NT) {
-            const float mv = mK[r] + sk[r];
-            mK[r] = mv;
-            sp += sq[r] * mv;
+        if (tid < D) {
+            mkv += sk[tid];
+            mK[tid] = mkv;
+            sp = sq[tid] * mkv;
         }
-        const float s_all = block_sum(sp);
+        const float s_all = block_sum(sp);   // its barrier also publishes part[]
         if (tid < DV) {
             float s = 0.f;
+#pragma unroll
             for (int i = 0; i < RG; ++i) s += part[i][tid];
             sy[tid] = s;
         }
         __syncthreads();
         // E <- E + k y^T ; partial o = q^T E
         float op = 0.f;
-        for (int r = rg; r < D; r += RG) {
-            const float ev = E[r * DV + col] + sk[r] * sy[col];
-            E[r * DV + col] = ev;
-            op += sq[r] * ev;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float en = ev[i] + sk[r] * sy[col];
+            E[r * DV + col] = en;
+            op += sq[r] * en;
         }
-        __syncthreads();
         part[rg][col] = op;
         // nk <- nk + k s ; den = q . nk
         float dp = 0.f;
-        for (int r = tid; r < D; r += NT) {
-            const float nv = nk[r] + sk[r] * s_all;
-            nk[r] = nv;
-            dp += sq[r] * nv;
+        if (tid < D) {
+            nkv += sk[tid] * s_all;
+            nk[tid] = nkv;
+            dp = sq[tid] * nkv;
         }
         const float den = block_sum(dp);
         if (tid < DV) {
             float s = 0.f;
+#pragma unroll
             for (int i = 0; i < RG; ++i) s += part[i][tid];
             if (p.ratio) s = s / den;
             o[tid] = from_f<T>(s);

@@ -149,3 +149,30 @@ def test_causality_on_gpu():
     a = gpu_forward(x, "hla2", 1, 2, "bf16", 64, 2)
     b = gpu_forward(y, "hla2", 1, 2, "bf16", 64, 2)
     assert np.array_equal(a[:, :t0 + 1], b[:, :t0 + 1])
+
+
+def test_forward_plan_matches_forward():
+    """A prepared plan (arguments marshalled once) gives bit-identical output
+    to hla_forward, run whole and stage by stage, and again on a second run."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    say("[plan] hla2_ratio bf16 d=64 chunk 64, 3 segments")
+    B, H, n, d = 1, 3, 3 * 64 * 2 + 17, 64
+    x = _inputs(B, H, n, d, "bf16", "uniform_pos", seed=404)
+    q, k, v = (torch.from_numpy(x[kk]).reshape(B, H, n, d).to(torch.bfloat16).cuda()
+               for kk in ("q", "k", "v"))
+    ref = hla.hla_forward(q, k, v, variant="hla2_ratio", chunk=64, seg_chunks=2)
+    ws = torch.empty(hla.workspace_bytes("hla2_ratio", B, H, n, d, d, 64, 2), dtype=torch.uint8,
+                     device="cuda")
+    plan = hla.ForwardPlan(q, k, v, variant="hla2_ratio", chunk=64, seg_chunks=2, workspace=ws,
+                           staged=True)
+    for _ in range(2):
+        plan.out.zero_()
+        for st in (1, 2, 3):
+            plan.stage(st)
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, ref)
+        plan.out.zero_()
+        plan.run()
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, ref)
