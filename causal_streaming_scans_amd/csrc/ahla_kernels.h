@@ -178,13 +178,12 @@ void ahla_forward_kernel(FwdParams p) {
         // fold node B (later) into the running state A: E <- E + E_B + M_B P,
         // nk <- nk + nk_B + M_B mK, P <- P + P_B, mK <- mK + mK_B; the node's
         // M and the old widened [P | mK] are staged in LDS (fp32)
-        using L = CrossLds<D, DV>;
+        using L = CrossLds<D, DV>;  // fold: whole right factor
         float *Ms = lds.f, *Ps = lds.f + D * L::LDA;
-        const float *nodes = p.ws + ws_node(bh, 0, p.nreal, G::SUMF);
         int done = 0;
         for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
             if (!((seg >> b) & 1)) continue;
-            const float *e = nodes + (size_t)node_slot(b, done >> b) * G::SUMF;
+            const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
             for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -439,7 +438,7 @@ void ahla_summary_kernel(FwdParams p) {
     }
 
     // summary [X = M | Y = P | N = E | y = mK | nv = nk]
-    float *e = p.ws + ws_node(bh, seg, p.nreal, G::SUMF);
+    float *e = p.ws + node_offset(bh, 0, seg, p.BH, p.nreal, G::SUMF);
     for_owned<MBk, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accM[pb][x][y][i];

@@ -15,9 +15,9 @@
 //   AHLA : X = X_A + X_B, Y = Y_A + Y_B, y = y_A + y_B,
 //          N = N_A + N_B + X_B Y_A,        nv = nv_A + nv_B + X_B y_A
 //
-// The scan's up-sweep runs as its own kernel over the stored summaries, one
-// workgroup per (b,h), level by level: node (b, m) (layout in params.h) is
-// the combine of its two children, written over the right child.  Its
+// The scan's up-sweep runs over the stored summaries level by level, one
+// launch per level and a few workgroups per combine (column slices): node
+// (b, m) (layout in params.h) is the combine of its two children.  Its
 // down-sweep is never materialised: the exclusive prefix of segment s is the
 // combine, left to right, of the up-sweep nodes that tile [0, s) -- one per
 // set bit of s, largest first -- and each forward workgroup forms its own
@@ -31,24 +31,6 @@
 #include "params.h"
 
 namespace hla {
-
-// LDS staging of the two cross-term factors, fp32: the left factor as
-// [D][D + 4] and the right factor widened to [D][DV + 20] -- its DV columns,
-// then the vector (y or mK) as column DV, then 15 zero columns -- so one
-// pass of 16-column tiles gives both the matrix and the vector cross terms.
-template <int D, int DV>
-struct CrossLds {
-    static constexpr int LDA = D + 4, LDB = DV + 20;
-    static constexpr int FLOATS = D * LDA + D * LDB;
-};
-
-// A kernel's chunk buffers overlaid with the cross-factor staging area used
-// before its first chunk.
-template <typename S, int FLOATS>
-union LdsWithScratch {
-    S s;
-    float f[FLOATS];
-};
 
 // dst[r][c] = src[r][c] for a [ROWS][COLS] fp32 block (COLS a multiple of 4),
 // float4-wise by NT threads, every load issued before any store.
@@ -68,14 +50,33 @@ __device__ __forceinline__ void stage_f32(float *dst, int ldd, const float *src,
     }
 }
 
-// the widened right factor [Y | y | 0 ...] of a summary into LDS
-template <int D, int DV, int NT>
-__device__ __forceinline__ void stage_right_ext(float *dst, const float *Y, const float *y) {
-    constexpr int LDB = CrossLds<D, DV>::LDB;
-    stage_f32<D, DV, NT>(dst, LDB, Y, DV);
+// The right cross factor widened by one 16-column tile: [Y[:, c0 .. c0+CW) |
+// y | 0 ...] into LDS [D][CW + 20], the vector column only when `with_vec`
+// (else zeros).  One pass of 16-column tiles then gives the matrix and the
+// vector cross terms together.
+template <int D, int DV, int CW, int NT>
+__device__ __forceinline__ void stage_right_ext(float *dst, const float *Y, int c0, const float *y,
+                                                bool with_vec) {
+    constexpr int LDB = CW + 20;
+    stage_f32<D, CW, NT>(dst, LDB, Y + c0, DV);
     for (int i = threadIdx.x; i < D * 16; i += NT)
-        dst[(i / 16) * LDB + DV + (i % 16)] = (i % 16) == 0 ? y[i / 16] : 0.f;
+        dst[(i / 16) * LDB + CW + (i % 16)] = ((i % 16) == 0 && with_vec) ? y[i / 16] : 0.f;
 }
+
+// LDS floats of the staged factors: left [D][D + 4], right [D][CW + 20].
+template <int D, int CW>
+struct CrossLds {
+    static constexpr int LDA = D + 4, LDB = CW + 20;
+    static constexpr int FLOATS = D * LDA + D * LDB;
+};
+
+// A kernel's chunk buffers overlaid with the cross-factor staging area used
+// before its first chunk.
+template <typename S, int FLOATS>
+union LdsWithScratch {
+    S s;
+    float f[FLOATS];
+};
 
 // 16x16 tile of A B, A [16 rows][K] row-major (lda, rows 16-byte aligned),
 // B [K][16 columns] row-major (ldb), both in LDS.  Lane (c, g) pairs
@@ -95,84 +96,132 @@ __device__ __forceinline__ f32x4 tile_ab_f32(const float *A, int lda, const floa
     return acc;
 }
 
-// eB <- eA (+) eB for two summaries in global memory, in place, by all NT
-// threads of the workgroup; `lds` holds CrossLds<D, DV>::FLOATS floats.
-// The cross factors are staged first, so every later global access of a
-// thread touches only the elements that thread itself rewrites.
-template <bool HLA2, int D, int DV, int NT>
-__device__ void combine_nodes(const float *eA, float *eB, float a, float *lds) {
+// Column slices a combine is split into (each a multiple of 16 columns).
+template <int DV>
+constexpr int combine_slices() { return DV / 16 < 4 ? DV / 16 : 4; }
+
+// Slice cs of eD = eA (+) eB, by all NT threads of the workgroup, eD a
+// separate node (nothing is read that any slice writes).  The slice owns the
+// columns [cs CW, (cs+1) CW) of Y and N, rows [cs D/CS, (cs+1) D/CS) of X,
+// and (slice 0) y and nv.  `lds` holds CrossLds<D, CW>::FLOATS floats.  The
+// staged factors and this wave's N / nv elements are loaded first; the linear
+// parts are loaded once the staging has landed, under the MFMA work.
+template <bool HLA2, int D, int DV, int NT, int CS>
+__device__ void combine_slice(const float *eA, const float *eB, float *eD, float a, int cs,
+                              float *lds) {
     using O = SumOfs<D, DV>;
-    using L = CrossLds<D, DV>;
-    constexpr int NW = NT / kWave, nTD = D / 16, nTV = DV / 16;
-    constexpr int NTILE = nTD * (nTV + 1);   // N tiles, then the nv column per row tile
+    constexpr int CW = DV / CS;
+    using L = CrossLds<D, CW>;
+    constexpr int NW = NT / kWave, nTD = D / 16, nTW = CW / 16;
+    constexpr int NTILE = nTD * (nTW + 1);   // N tiles of the slice, then the nv column
     constexpr int PT = (NTILE + NW - 1) / NW;
     const int w = wave_id(), col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    const int c0 = cs * CW;
+    const bool first = cs == 0;
     const float *Xc = HLA2 ? eA + O::X : eB + O::X;
     const float *Yc = HLA2 ? eB + O::Y : eA + O::Y;
     const float *yc = HLA2 ? eB + O::y : eA + O::y;
     const float lin = HLA2 ? a : 1.f, quad = HLA2 ? a * a : 1.f;
     float *As = lds, *Bs = lds + D * L::LDA;
-    stage_f32<D, D, NT>(As, L::LDA, Xc, D);
-    stage_right_ext<D, DV, NT>(Bs, Yc, yc);
-    // this wave's N / nv elements of both operands, loaded while staging lands
+    // which of this wave's tiles exist: the nv column only in slice 0
+    auto tile_ok = [&](int t) { return t < nTD * nTW || (first && t < NTILE); };
     float na[PT][4], nb[PT][4];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int t = w + j * NW;
-        if (t < NTILE) {
-            const int ti = t / (nTV + 1), tj = t % (nTV + 1);
+        if (tile_ok(t)) {
+            const bool nvt = t >= nTD * nTW;
+            const int ti = nvt ? t - nTD * nTW : t / nTW, tj = nvt ? 0 : t % nTW;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + g4 + i;
-                const int idx = tj < nTV ? O::N + row * DV + 16 * tj + col : O::nv + row;
-                const bool use = tj < nTV || col == 0;
+                const int idx = nvt ? O::nv + row : O::N + row * DV + c0 + 16 * tj + col;
+                const bool use = !nvt || col == 0;
                 na[j][i] = use ? eA[idx] : 0.f;
                 nb[j][i] = use ? eB[idx] : 0.f;
             }
         }
     }
+    stage_f32<D, D, NT>(As, L::LDA, Xc, D);
+    stage_right_ext<D, DV, CW, NT>(Bs, Yc, c0, yc, first);
     __syncthreads();
+    // linear parts of the slice: X rows [r0, r0 + D/CS), Y columns [c0, c0+CW), y
+    constexpr int XR = D / CS, NX4 = XR * D / 4, NY4 = D * CW / 4;
+    constexpr int UX = (NX4 + NT - 1) / NT, UY = (NY4 + NT - 1) / NT;
+    const int r0 = cs * XR;
+    f32x4 xa[UX], xb[UX], ya[UY], yb[UY];
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+        const int v = threadIdx.x + u * NT;
+        if (v < NX4) {
+            const int off = O::X + r0 * D + 4 * v;
+            xa[u] = *reinterpret_cast<const f32x4 *>(eA + off);
+            xb[u] = *reinterpret_cast<const f32x4 *>(eB + off);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < UY; ++u) {
+        const int v = threadIdx.x + u * NT;
+        if (v < NY4) {
+            const int off = O::Y + (v / (CW / 4)) * DV + c0 + 4 * (v % (CW / 4));
+            ya[u] = *reinterpret_cast<const f32x4 *>(eA + off);
+            yb[u] = *reinterpret_cast<const f32x4 *>(eB + off);
+        }
+    }
+    float vya = 0.f, vyb = 0.f;
+    if (first && threadIdx.x < D) {
+        vya = eA[O::y + threadIdx.x];
+        vyb = eB[O::y + threadIdx.x];
+    }
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int t = w + j * NW;
-        if (t < NTILE) {
-            const int ti = t / (nTV + 1), tj = t % (nTV + 1);
+        if (tile_ok(t)) {
+            const bool nvt = t >= nTD * nTW;
+            const int ti = nvt ? t - nTD * nTW : t / nTW, tj = nvt ? nTW : t % nTW;
             const f32x4 cr = tile_ab_f32<D>(As + 16 * ti * L::LDA, L::LDA, Bs + 16 * tj, L::LDB);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * ti + g4 + i;
                 const float val = quad * na[j][i] + nb[j][i] + lin * cr[i];
-                if (tj < nTV) eB[O::N + row * DV + 16 * tj + col] = val;
-                else if (col == 0) eB[O::nv + row] = val;
+                if (!nvt) eD[O::N + row * DV + c0 + 16 * tj + col] = val;
+                else if (col == 0) eD[O::nv + row] = val;
             }
         }
     }
-    // X and Y are adjacent: one float4 pass, then y
-    constexpr int NXY4 = (D * D + D * DV) / 4;
-    const f32x4 *A4 = reinterpret_cast<const f32x4 *>(eA);
-    f32x4 *B4 = reinterpret_cast<f32x4 *>(eB);
-    for (int v = threadIdx.x; v < NXY4; v += NT) B4[v] = lin * A4[v] + B4[v];
-    for (int i = threadIdx.x; i < D; i += NT) eB[O::y + i] = lin * eA[O::y + i] + eB[O::y + i];
-}
-
-// Up-sweep of the exclusive Blelloch scan for head blockIdx.x: every node
-// whose segments all have summaries, lowest level first.  A node that ends
-// at or past nreal would only feed prefixes no segment needs.
-template <bool HLA2, int D, int DV, int NT>
-__global__ __launch_bounds__(NT) void up_sweep_kernel(FwdParams p) {
-    constexpr int SUMF = summary_floats(D, DV);
-    __shared__ alignas(16) float lds[CrossLds<D, DV>::FLOATS];
-    const int bh = blockIdx.x;
-    float *base = p.ws + ws_node(bh, 0, p.nreal, SUMF);
-    const float g = HLA2 ? p.gamma[bh % p.H] : 1.f;
-    for (int b = 0; node_slot(b + 1, 0) <= p.nreal - 1; ++b) {
-        const float a = HLA2 ? pow_int(g, (long)p.seg_len << b) : 1.f;   // g^(tokens of a child)
-        for (int m = 0; node_slot(b + 1, m) <= p.nreal - 1; ++m) {
-            combine_nodes<HLA2, D, DV, NT>(base + (size_t)node_slot(b, 2 * m) * SUMF,
-                                           base + (size_t)node_slot(b, 2 * m + 1) * SUMF, a, lds);
-            __syncthreads();   // the parent is complete before anything reads it
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+        const int v = threadIdx.x + u * NT;
+        if (v < NX4) *reinterpret_cast<f32x4 *>(eD + O::X + r0 * D + 4 * v) = lin * xa[u] + xb[u];
+    }
+#pragma unroll
+    for (int u = 0; u < UY; ++u) {
+        const int v = threadIdx.x + u * NT;
+        if (v < NY4) {
+            const int off = O::Y + (v / (CW / 4)) * DV + c0 + 4 * (v % (CW / 4));
+            *reinterpret_cast<f32x4 *>(eD + off) = lin * ya[u] + yb[u];
         }
     }
+    if (first && threadIdx.x < D) eD[O::y + threadIdx.x] = lin * vya + vyb;
+}
+
+// One level of the up-sweep of the exclusive Blelloch scan: workgroup
+// (m * CS + cs, bh) forms column slice cs of node (b+1, m) of head bh from
+// its children (b, 2m) and (b, 2m+1).  The host launches the levels in
+// order, one launch each, over the nodes that end below nreal (a node ending
+// at or past it would only feed prefixes no segment needs).
+template <bool HLA2, int D, int DV, int NT>
+__global__ __launch_bounds__(NT) void up_sweep_kernel(FwdParams p, int b) {
+    constexpr int SUMF = summary_floats(D, DV);
+    constexpr int CS = combine_slices<DV>();
+    __shared__ alignas(16) float lds[CrossLds<D, DV / CS>::FLOATS];
+    const int m = blockIdx.x / CS, cs = blockIdx.x % CS, bh = blockIdx.y;
+    const float g = HLA2 ? p.gamma[bh % p.H] : 1.f;
+    const float a = HLA2 ? pow_int(g, (long)p.seg_len << b) : 1.f;   // g^(tokens of a child)
+    combine_slice<HLA2, D, DV, NT, CS>(p.ws + node_offset(bh, b, 2 * m, p.BH, p.nreal, SUMF),
+                                       p.ws + node_offset(bh, b, 2 * m + 1, p.BH, p.nreal, SUMF),
+                                       p.ws + node_offset(bh, b + 1, m, p.BH, p.nreal, SUMF), a, cs,
+                                       lds);
 }
 
 }  // namespace hla

@@ -291,20 +291,19 @@ void hla2_forward_kernel(FwdParams p) {
         // fold node B (later) into the running state A: W <- a^2 W + N_B +
         // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
         // the node's [Y | y] are staged in LDS (fp32) as the cross factors
-        using L = CrossLds<D, DV>;
+        using L = CrossLds<D, DV>;  // fold: whole right factor
         float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
-        const float *nodes = p.ws + ws_node(bh, 0, p.nreal, G::SUMF);
         int done = 0;
         for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
             if (!((seg >> b) & 1)) continue;
-            const float *e = nodes + (size_t)node_slot(b, done >> b) * G::SUMF;
+            const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
             const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
             for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = accS[pb][x][y][i];
             });
-            stage_right_ext<D, DV, NT>(Bs, e + O::Y, e + O::y);
+            stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
             // the linear terms now (the old S is already staged); the cross
             // terms once the staging has landed
             for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
@@ -617,7 +616,7 @@ void hla2_summary_kernel(FwdParams p) {
     }
 
     // summary [X = S | Y = C | N = W | y = m | nv = u]
-    float *e = p.ws + ws_node(bh, seg, p.nreal, G::SUMF);
+    float *e = p.ws + node_offset(bh, 0, seg, p.BH, p.nreal, G::SUMF);
     for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];

@@ -93,7 +93,8 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
     const long nseg = num_segments(n, chunk, g);
     if (nseg <= 1) return 0;
     const size_t nreal = (size_t)(nseg - 1);
-    return (size_t)B * H * nreal * (size_t)summary_floats(d, dv) * sizeof(float);
+    // leaves, then internal nodes of the up-sweep (fewer than nreal per head)
+    return 2 * (size_t)B * H * nreal * (size_t)summary_floats(d, dv) * sizeof(float);
 }
 
 // Validate, pick the kernels and fill the argument block; shared by

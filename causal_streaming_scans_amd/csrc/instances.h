@@ -52,9 +52,15 @@ hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
 
 template <typename T, int D, bool HLA2>
 hipError_t launch_up_sweep(const FwdParams &p, hipStream_t s) {
-    constexpr int NT = D >= 128 ? 512 : 256;
-    hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(p.BH), dim3(NT), 0, s, p);
-    return hipGetLastError();
+    constexpr int NT = 256, CS = combine_slices<D>();
+    for (int b = 0; (p.nreal >> (b + 1)) > 0; ++b) {
+        const int npair = p.nreal >> (b + 1);
+        hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(npair * CS, p.BH), dim3(NT), 0, s,
+                           p, b);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename T, int D, int C>

@@ -12,7 +12,7 @@ typedef hipError_t (*StepLaunch)(const StepParams &, hipStream_t);
 
 struct FwdKernels {
     FwdLaunch summary;   // grid (nseg-1, BH): segment summaries from zero state
-    FwdLaunch up_sweep;  // grid (BH): up-sweep of the exclusive Blelloch scan
+    FwdLaunch up_sweep;  // one launch per level, grid (pairs, BH): up-sweep of the scan
     FwdLaunch forward;   // grid (nseg, BH): prefix from the up-sweep nodes, chunked forward
 };
 

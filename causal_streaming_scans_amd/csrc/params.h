@@ -32,12 +32,12 @@ struct FwdParams {
 //   HLA-2:   S        C        W      m     u      (W = S^K C^QV - G, u = S^K m^Q - h)
 //   AHLA :   M        P        E      mK    nk     (M = sum k q^T)
 //
-// Workspace: for head bh, `nreal` summary slots, ws + (bh*nreal + slot) *
-// summary_floats.  Slot s first receives the summary of segment s; the
-// up-sweep of the scan then combines in place: node (b, m) covers segments
-// [m 2^b, (m+1) 2^b - 1] and lives in the slot of its last segment, so a
-// parent overwrites its right child, which nothing reads afterwards.  Only
-// nodes ending below nreal are formed.
+// Workspace (fp32): the leaves, then the internal nodes of the scan's
+// up-sweep tree.  Node (b, m) covers segments [m 2^b, (m+1) 2^b - 1]; only
+// nodes ending below nreal exist, so level b has nreal >> b of them.  Leaf
+// (0, s) is the summary of segment s, at ws + (bh*nreal + s) * summary_floats;
+// internal node (b >= 1, m) is at ws + (BH*nreal + bh*nreal + node_index(b, m))
+// * summary_floats.
 __host__ __device__ constexpr int summary_floats(int D, int DV) { return D * D + 2 * D * DV + 2 * D; }
 __host__ __device__ constexpr int hla2_state_floats(int D, int DV) { return D * D + D * DV + D; }
 __host__ __device__ constexpr int ahla_state_floats(int D, int DV) { return 2 * D * DV + 2 * D; }
@@ -48,10 +48,17 @@ struct SumOfs {
                          nv = D * D + 2 * D * DV + D;
 };
 
-__host__ __device__ inline size_t ws_node(int bh, int slot, int nreal, int sumf) {
-    return ((size_t)bh * nreal + slot) * (size_t)sumf;
+// index of internal node (b >= 1, m) among its head's internal nodes
+__host__ __device__ inline int node_index(int b, int m, int nreal) {
+    int off = 0;
+    for (int l = 1; l < b; ++l) off += nreal >> l;
+    return off + m;
 }
-__host__ __device__ inline int node_slot(int b, int m) { return ((m + 1) << b) - 1; }
+__host__ __device__ inline size_t node_offset(int bh, int b, int m, int BH, int nreal, int sumf) {
+    const size_t slot = b == 0 ? (size_t)bh * nreal + m
+                               : (size_t)BH * nreal + (size_t)bh * nreal + node_index(b, m, nreal);
+    return slot * (size_t)sumf;
+}
 
 // Decode step arguments.
 struct StepParams {

@@ -87,8 +87,9 @@ size_t hla_state_floats(int variant, int d, int dv);
 int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk);
 
 /* Bytes of device workspace hla_forward needs for these arguments
- * (seg_chunks == 0 means the default): B*H*(nseg-1) fp32 segment summaries of
- * d*d + 2*d*dv + 2*d floats.  0 when the sequence is one segment. */
+ * (seg_chunks == 0 means the default): 2*B*H*(nseg-1) fp32 summaries of
+ * d*d + 2*d*dv + 2*d floats (the segment summaries and the nodes of the
+ * scan's up-sweep).  0 when the sequence is one segment. */
 size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
                            int chunk, int seg_chunks);
 
@@ -135,16 +136,17 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
  * The three stages hla_forward runs, one at a time, on the same arguments
  * (page section "4. ... Escaneos Asociativos": segment summaries combined by
  * an exclusive Blelloch scan under the semidirect-product combine).  With
- * SUMF = d*d + 2*d*dv + 2*d and slot s of head bh at floats
- * ws + (bh*(nseg-1) + s)*SUMF (parts X | Y | N | y | nv):
- *   stage 1  the summary of segment s into slot s, s = 0 .. nseg-2;
- *   stage 2  the up-sweep of the scan, in place: afterwards slot s holds the
- *            combine of segments s+1-2^b .. s, 2^b the largest power of two
- *            dividing s+1;
- *   stage 3  for every segment, the initial state and the slots covering
- *            the earlier segments folded into its carried state (what the
- *            scan's down-sweep delivers), then the chunked forward from
- *            that state, and state_out.
+ * SUMF = d*d + 2*d*dv + 2*d, R = nseg-1, parts X | Y | N | y | nv:
+ *   stage 1  the summary of segment s, s = 0 .. R-1, into the leaf at floats
+ *            ws + (bh*R + s)*SUMF;
+ *   stage 2  the up-sweep of the scan: node (b, m), b >= 1, the combine of
+ *            segments m*2^b .. (m+1)*2^b - 1, for every such node that ends
+ *            below R, at ws + (B*H*R + bh*R + i)*SUMF, where i counts the
+ *            nodes of levels 1 .. b-1 (R >> l of them at level l) plus m;
+ *   stage 3  for every segment s, the initial state and the nodes that tile
+ *            segments 0 .. s-1 (one per set bit of s) folded into its carried
+ *            state (what the scan's down-sweep delivers), then the chunked
+ *            forward from that state, and state_out.
  * Calling stages 1, 2, 3 in order on one stream with identical arguments is
  * exactly hla_forward.  With a single segment stages 1 and 2 enqueue nothing.
  * Meant for callers that time the stages or place them themselves (a caller

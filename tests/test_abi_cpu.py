@@ -58,11 +58,11 @@ def test_state_floats(lib):
 def test_workspace_bytes(lib):
     # one segment: no workspace
     assert hla.workspace_bytes("hla2", 1, 1, 256, 16, 16, 32, 8) == 0
-    # 4 segments -> 3 fp32 summary slots per head
+    # 4 segments -> 3 fp32 summaries per head, and room for as many up-sweep nodes
     sumf = 64 * 64 + 2 * 64 * 64 + 2 * 64
-    assert hla.workspace_bytes("hla2", 2, 3, 1024, 64, 64, 64, 4) == 2 * 3 * 3 * sumf * 4
-    # 3 segments (the last one partial) -> 2 slots
-    assert hla.workspace_bytes("ahla", 1, 1, 600, 64, 64, 64, 4) == 1 * 2 * sumf * 4
+    assert hla.workspace_bytes("hla2", 2, 3, 1024, 64, 64, 64, 4) == 2 * 2 * 3 * 3 * sumf * 4
+    # 3 segments (the last one partial) -> 2 summaries
+    assert hla.workspace_bytes("ahla", 1, 1, 600, 64, 64, 64, 4) == 2 * 1 * 2 * sumf * 4
 
 
 def test_default_segments_fill_the_chip(lib):

@@ -2,10 +2,11 @@
 after stage 2 (the up-sweep of the exclusive Blelloch scan) against the fp64
 chunk-scan algebra of oracle/chunk_scan.py.
 
-Layout: ws[bh][slot][summary floats] (X, Y, N, y, nv).  After stage 1 slot
-s holds the summary of segment s; after stage 2 it holds the combine of
-segments s+1-2^b .. s, 2^b the largest power of two dividing s+1.  Stage 3's
-use of the nodes is covered by the forward parity tests.
+Layout (R = nseg - 1 summarised segments per head, parts X, Y, N, y, nv):
+leaf s of head bh at slot bh*R + s; internal node (b >= 1, m), the combine of
+segments m*2^b .. (m+1)*2^b - 1, at slot B*H*R + bh*R + (nodes of levels
+1 .. b-1) + m, for every such node ending below R.  Stage 3's use of the
+nodes is covered by the forward parity tests.
 """
 import numpy as np
 import pytest
@@ -41,9 +42,16 @@ def _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g):
     return sums
 
 
-def _node_span(slot):
-    b = ((slot + 1) & -(slot + 1)).bit_length() - 1
-    return slot + 1 - (1 << b), slot
+def _nodes(nreal):
+    """(b, m, first segment, last segment, slot index within the head) of
+    every internal node of the up-sweep."""
+    out, off, b = [], 0, 1
+    while (nreal >> b) > 0:
+        for m in range(nreal >> b):
+            out.append((b, m, m << b, ((m + 1) << b) - 1, off + m))
+        off += nreal >> b
+        b += 1
+    return out
 
 
 @pytest.mark.parametrize("dtype,variant,d,chunk,seg,decay", [
@@ -77,7 +85,7 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
 
     def slots():
         torch.cuda.synchronize()
-        return ws.cpu().numpy().astype(np.float64).reshape(B * H, nreal, sumf)
+        return ws.cpu().numpy().astype(np.float64).reshape(2 * B * H, nreal, sumf)
 
     hla.hla_forward_stage(1, q, k, v, **kw)
     e1 = slots()
@@ -94,17 +102,18 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
             items = [dict(M=r[0], P=r[1], E=r[2], mK=r[3], nk=r[4]) for r in ref]
             comb = CS.ahla_combine
             parts = lambda it: (it["M"], it["P"], it["E"], it["mK"], it["nk"])
-        for slot in range(nreal):
-            for name, a, b in zip(("X", "Y", "N", "y", "nv"), _unpack(e1[bh, slot], d, d),
-                                  parts(items[slot])):
-                err = rel_l2(a, b)
-                assert err < tol, f"head {bh} summary {slot} part {name}: {err:.3e}"
-            lo, hi = _node_span(slot)
+        for s_ in range(nreal):
+            for stage_ws in (e1, e):      # the leaves are not touched by stage 2
+                for name, a, b in zip(("X", "Y", "N", "y", "nv"), _unpack(stage_ws[bh, s_], d, d),
+                                      parts(items[s_])):
+                    err = rel_l2(a, b)
+                    assert err < tol, f"head {bh} summary {s_} part {name}: {err:.3e}"
+        for (lev, m, lo, hi, idx) in _nodes(nreal):
             node = items[lo]
             for j in range(lo + 1, hi + 1):
                 node = comb(node, items[j])
-            got = _unpack(e[bh, slot], d, d)
+            got = _unpack(e[B * H + bh, idx], d, d)
             for name, a, b in zip(("X", "Y", "N", "y", "nv"), got, parts(node)):
                 err = rel_l2(a, b)
-                assert err < tol, f"head {bh} slot {slot} [{lo}..{hi}] part {name}: {err:.3e}"
+                assert err < tol, f"head {bh} node ({lev},{m}) [{lo}..{hi}] part {name}: {err:.3e}"
     say(f"   {nreal} slots per head match")
