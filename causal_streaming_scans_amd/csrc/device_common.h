@@ -41,6 +41,26 @@ template <typename T> constexpr int ld_of(int cols) { return cols + pad_of<T>();
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// LDS layout of a row-major [rows][COLS] matrix of T.  bf16 matrices of 64
+// columns use unpadded 128-byte rows whose eight 16-byte granules are
+// permuted by XOR with sw(r) = (r & 7) ^ 5 * bit3(r) (a function of r mod
+// 16, so 16-row blocks stay additive).  On gfx950's LDS (32 banks for
+// writes, 64 for reads) that keeps the chunk kernels' operand-row reads,
+// both transposing-read shapes and the staging stores free of bank
+// conflicts, and leaves the accumulator stores at the two-way minimum of an
+// 8-byte-per-lane store; a padded pitch fixes one of those at the cost of
+// another.  Other matrices are padded by 16 bytes a row.
+template <typename T, int COLS>
+struct LdsTile {
+    static constexpr bool SWZ = sizeof(T) == 2 && COLS == 64;
+    static constexpr int LD = SWZ ? COLS : ld_of<T>(COLS);
+    // element (r, c); c a multiple of 4 when the access is 8 or 16 bytes wide
+    __device__ static __forceinline__ int off(int r, int c) {
+        if constexpr (SWZ) return r * LD + ((((c >> 3) ^ (r & 7) ^ (((r >> 3) & 1) * 5)) << 3) | (c & 7));
+        else return r * LD + c;
+    }
+};
+
 // ---------------------------------------------------------------- MFMA tiles
 
 // acc += A[0:16][kbeg:kend] * Bt[0:16][kbeg:kend]^T, k range a multiple of 16.
@@ -184,6 +204,33 @@ __device__ __forceinline__ f32x4 mma_nt_f(f32x4 acc, const float *A, int lda,
 #pragma unroll
     for (int s = 0; s < K / 4; ++s)
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + 4 * s + g], f.v[s], acc, 0, 0, 0);
+    return acc;
+}
+// mma_nt_f with A the 16-row block of an LdsTile matrix that starts at A
+template <typename TL, int K>
+__device__ __forceinline__ f32x4 mma_nt_ft(f32x4 acc, const bf16 *A, const RowFrags<bf16, K> &f) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+    if constexpr (RowFrags<bf16, K>::W32) {
+#pragma unroll
+        for (int s = 0; s < K / 32; ++s) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(A + TL::off(r, 32 * s + 8 * g));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.v8[s], acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < K / 16; ++s) {
+            const i16x4 av = *reinterpret_cast<const i16x4 *>(A + TL::off(r, 16 * s + 4 * g));
+            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, f.v4[s], acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+template <typename TL, int K>
+__device__ __forceinline__ f32x4 mma_nt_ft(f32x4 acc, const float *A, const RowFrags<float, K> &f) {
+    const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+    for (int s = 0; s < K / 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[TL::off(r, 4 * s + g)], f.v[s], acc, 0, 0, 0);
     return acc;
 }
 // acc += F * Bt[0:16][0:K]^T with F preloaded (F as the A side)

@@ -56,6 +56,7 @@ struct Hla2Cfg {
     static constexpr int DVX = DV + 16;       // V, W widened by the ones / u column tile
     static constexpr int LDD = ld_of<T>(D);   // rows of length D
     static constexpr int LDV = ld_of<T>(DVX); // rows of the widened V
+    using TS = LdsTile<T, D>;                 // the state copies St, Wt
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int ZJ = (nTD + NCG - 1) / NCG;    // Z^T tiles per wave
     static constexpr int OJ = (nTV + NCG - 1) / NCG;    // O^T tiles per wave
@@ -127,8 +128,8 @@ struct Hla2FwdSmem {
     alignas(16) T V[C * G::LDV];                 // widened: columns DV.. = (1, 0, ..)
     alignas(16) T Z[C * G::LDD];
     alignas(16) T Zw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(2(c-1-tau))
-    alignas(16) T St[D * G::LDD];                // St[j][i] = S0[i][j]
-    alignas(16) T Wt[G::DVX * G::LDD];           // Wt[j][i] = W0[i][j]; row DV = u0
+    alignas(16) T St[D * G::TS::LD];             // St[j][i] = S0[i][j]
+    alignas(16) T Wt[G::DVX * G::TS::LD];        // Wt[j][i] = W0[i][j]; row DV = u0
     float gp[G::NPOW];
 };
 
@@ -144,7 +145,7 @@ struct Hla2SumSmem {
     alignas(16) T Kw[DECAY ? C * G::LDD : 8];
     alignas(16) T V[C * G::LDV];
     alignas(16) T Z[C * G::LDD];                 // rows weighted by g^(2(c-1-tau))
-    alignas(16) T St[D * G::LDD];
+    alignas(16) T St[D * G::TS::LD];
     float gp[G::NPOW];
 };
 
@@ -192,7 +193,7 @@ __device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[R + 1], const T *K, con
 
 // Z^T tiles of row tile R: Z = diag(g^(tau+1)) Q S0 + L K, stored row-major
 // (times w) into Zd.  Shared by the forward and summary kernels.
-template <typename T, int D, int R, int NCG, int ZJ, int LDD, bool DECAY>
+template <typename T, int D, int R, int NCG, int ZJ, int LDD, bool DECAY, typename TS>
 __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
                                         const T *St, const T *K, T *Zd, T *Zwd, float wz,
                                         const float *gp, int cg, int tau) {
@@ -203,7 +204,7 @@ __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T
         const int jt = cg + jj * NCG;
         z[jj] = zero4();
         if (jt < D / 16) {
-            f32x4 zq = mma_nt_f(zero4(), St + 16 * jt * LDD, LDD, qf);
+            f32x4 zq = mma_nt_ft<TS>(zero4(), St + 16 * jt * TS::LD, qf);
             f32x4 zc = zero4();
 #pragma unroll
             for (int s = 0; s <= R; ++s) zc = mma16(zc, ld_frag_t(K + 16 * s * LDD + 16 * jt, LDD), Lf[s]);
@@ -336,13 +337,13 @@ void hla2_forward_kernel(FwdParams p) {
     }
     // T-typed transposed copies: the operands of Q S0 and Q W0 (row DV of Wt = u)
     for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-        store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
+        store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
     });
     for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-        store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[pb][x][y]);
+        store4(sm.Wt + G::TS::off(16 * tv + col, 16 * ti + g4), accW[pb][x][y]);
     });
     for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, accU[j]);
+        store4(sm.Wt + G::TS::off(DV + col, 16 * ti + g4), accU[j]);
     });
     if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
     init_ones_column<T, C, LDV, DV, NT>(sm.V);
@@ -373,7 +374,7 @@ void hla2_forward_kernel(FwdParams p) {
 
             // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
             const float wz = DECAY ? (tau < cv ? sm.gp[2 * (cv - 1 - tau)] : 0.f) : 1.f;
-            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, sm.Z, DECAY ? sm.Zw : nullptr,
+            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, sm.Z, DECAY ? sm.Zw : nullptr,
                                                      wz, sm.gp, cg, tau);
             // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T; the
             // denominator's carried part q . u0 is row DV of the widened product
@@ -383,13 +384,13 @@ void hla2_forward_kernel(FwdParams p) {
                 const int jv = cg + jj * NCG;
                 accO[jj] = zero4();
                 if (jv < nTV) {
-                    accO[jj] = mma_nt_f(zero4(), sm.Wt + 16 * jv * LDD, LDD, qf);
+                    accO[jj] = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + 16 * jv * G::TS::LD, qf);
                     if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
                 }
             }
             f32x4 accD = zero4();
             if (ratio) {
-                accD = mma_nt_f(zero4(), sm.Wt + DV * LDD, LDD, qf);
+                accD = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + DV * G::TS::LD, qf);
                 if (DECAY) accD *= sm.gp[2 * (tau + 1)];
             }
             __syncthreads();
@@ -453,14 +454,14 @@ void hla2_forward_kernel(FwdParams p) {
             });
         }
         for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
+            store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
         });
         for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-            store4(sm.Wt + (16 * tv + col) * LDD + 16 * ti + g4, accW[pb][x][y]);
+            store4(sm.Wt + G::TS::off(16 * tv + col, 16 * ti + g4), accW[pb][x][y]);
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                store4(sm.Wt + (DV + col) * LDD + 16 * ti + g4, accU[j]);
+                store4(sm.Wt + G::TS::off(DV + col, 16 * ti + g4), accU[j]);
             });
         }
         c0 = n0;
@@ -536,7 +537,7 @@ void hla2_summary_kernel(FwdParams p) {
         accU[j] = zero4();
         accM[j] = zero4();
     }
-    for (int i = threadIdx.x; i < D * LDD; i += NT) sm.St[i] = from_f<T>(0.f);
+    for (int i = threadIdx.x; i < D * G::TS::LD; i += NT) sm.St[i] = from_f<T>(0.f);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -571,7 +572,7 @@ void hla2_summary_kernel(FwdParams p) {
             scores_t<T, D, R, LDD, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
             // Z rows weighted by g^(2(c-1-tau)): only the W and u updates use Z here
             const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
-            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz, sm.gp, cg,
+            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz, sm.gp, cg,
                                                      tau);
         });
         __syncthreads();
@@ -609,7 +610,7 @@ void hla2_summary_kernel(FwdParams p) {
         });
         // the running S's T-typed copy after every product of the chunk
         for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-            store4(sm.St + (16 * tj + col) * LDD + 16 * ti + g4, accS[pb][x][y]);
+            store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
         });
         c0 = n0;
         cv = ncv;
