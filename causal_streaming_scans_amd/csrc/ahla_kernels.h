@@ -184,42 +184,70 @@ void ahla_forward_kernel(FwdParams p) {
         for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
             if (!((seg >> b) & 1)) continue;
             const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
-            for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            // with no caller state the first node folds into zero: no cross terms
+            const bool cross = p.state_in != nullptr || done > 0;
+            // The node's linear parts: with d <= 64 they are loaded into
+            // registers ahead of the staging, so every global load of the node
+            // is in flight at once (larger heads have no registers to spare)
+            constexpr bool PRE = D <= 64;
+            float ne[PBk::PB][PBk::BR][PBk::BR][PRE ? 4 : 1], np[PBk::PB][PBk::BR][PBk::BR][PRE ? 4 : 1];
+            float nn[G::UJ][PRE ? 4 : 1], nm[G::UJ][PRE ? 4 : 1];
+            auto ev = [&](int ofs, int ti, int tv, int i) { return e[ofs + (16 * ti + g4 + i) * DV + 16 * tv + col]; };
+            auto vv = [&](int ofs, int ti, int i) { return col == 0 ? e[ofs + 16 * ti + g4 + i] : 0.f; };
+            if constexpr (PRE) {
+                for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Ps[(16 * ti + g4 + i) * L::LDB + 16 * tv + col] = accP[pb][x][y][i];
-            });
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                    for (int i = 0; i < 4; ++i) {
+                        ne[pb][x][y][i] = ev(O::N, ti, tv, i);
+                        np[pb][x][y][i] = ev(O::Y, ti, tv, i);
+                    }
+                });
+                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Ps[(16 * ti + g4 + i) * L::LDB + DV + col] = accMK[j][i];
-            });
-            stage_f32<D, D, NT>(Ms, L::LDA, e + O::X, D);
+                    for (int i = 0; i < 4; ++i) {
+                        nn[j][i] = vv(O::nv, ti, i);
+                        nm[j][i] = vv(O::y, ti, i);
+                    }
+                });
+            }
+            if (cross) {
+                for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Ps[(16 * ti + g4 + i) * L::LDB + 16 * tv + col] = accP[pb][x][y][i];
+                });
+                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Ps[(16 * ti + g4 + i) * L::LDB + DV + col] = accMK[j][i];
+                });
+                stage_f32<D, D, NT>(Ms, L::LDA, e + O::X, D);
+            }
             // the linear terms now (the old P, mK are already staged); the
             // cross terms once the staging has landed
             for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-                    accE[pb][x][y][i] += e[O::N + idx];
-                    accP[pb][x][y][i] += e[O::Y + idx];
+                    accE[pb][x][y][i] += PRE ? ne[pb][x][y][PRE ? i : 0] : ev(O::N, ti, tv, i);
+                    accP[pb][x][y][i] += PRE ? np[pb][x][y][PRE ? i : 0] : ev(O::Y, ti, tv, i);
                 }
             });
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * ti + g4 + i;
-                    accNK[j][i] += col == 0 ? e[O::nv + row] : 0.f;
-                    accMK[j][i] += col == 0 ? e[O::y + row] : 0.f;
+                    accNK[j][i] += PRE ? nn[j][PRE ? i : 0] : vv(O::nv, ti, i);
+                    accMK[j][i] += PRE ? nm[j][PRE ? i : 0] : vv(O::y, ti, i);
                 }
             });
-            __syncthreads();
-            for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-                accE[pb][x][y] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + 16 * tv, L::LDB);
-            });
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                accNK[j] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + DV, L::LDB);
-            });
-            __syncthreads();
+            if (cross) {
+                __syncthreads();
+                for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+                    accE[pb][x][y] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + 16 * tv, L::LDB);
+                });
+                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                    accNK[j] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + DV, L::LDB);
+                });
+                __syncthreads();
+            }
             done += 1 << b;
         }
     }

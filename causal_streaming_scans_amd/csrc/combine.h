@@ -58,9 +58,20 @@ template <int D, int DV, int CW, int NT>
 __device__ __forceinline__ void stage_right_ext(float *dst, const float *Y, int c0, const float *y,
                                                 bool with_vec) {
     constexpr int LDB = CW + 20;
+    static_assert(D <= NT, "one vector element per thread");
+    // the vector element is loaded with the matrix, under the same wait
+    const int t = threadIdx.x;
+    float yv = 0.f;
+    if (with_vec && t < D) yv = y[t];
     stage_f32<D, CW, NT>(dst, LDB, Y + c0, DV);
-    for (int i = threadIdx.x; i < D * 16; i += NT)
-        dst[(i / 16) * LDB + CW + (i % 16)] = ((i % 16) == 0 && with_vec) ? y[i / 16] : 0.f;
+    // the rest of the widening tile is zero
+    constexpr int NZ = D * 16, UZ = (NZ + NT - 1) / NT;
+#pragma unroll
+    for (int u = 0; u < UZ; ++u) {
+        const int i = t + u * NT;
+        if (i < NZ && (i % 16) != 0) dst[(i / 16) * LDB + CW + (i % 16)] = 0.f;
+    }
+    if (t < D) dst[t * LDB + CW] = yv;
 }
 
 // LDS floats of the staged factors: left [D][D + 4], right [D][CW + 20].

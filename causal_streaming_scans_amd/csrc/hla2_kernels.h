@@ -299,39 +299,65 @@ void hla2_forward_kernel(FwdParams p) {
             if (!((seg >> b) & 1)) continue;
             const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
             const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
-            for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+            // with no caller state the first node folds into zero: no cross terms
+            const bool cross = p.state_in != nullptr || done > 0;
+            // The node's linear parts: with d <= 64 they are loaded into
+            // registers ahead of the staging, so every global load of the node
+            // is in flight at once (larger heads have no registers to spare)
+            constexpr bool PRE = D <= 64;
+            float nw[WB::PB][WB::BR][WB::BR][PRE ? 4 : 1], nx[SB::PB][SB::BR][SB::BR][PRE ? 4 : 1],
+                nu[G::UJ][PRE ? 4 : 1];
+            auto w_lin = [&](int ti, int tv, int i) { return e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col]; };
+            auto u_lin = [&](int ti, int i) { return col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f; };
+            auto s_lin = [&](int ti, int tj, int i) { return e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col]; };
+            if constexpr (PRE) {
+                for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = accS[pb][x][y][i];
-            });
-            stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
-            // the linear terms now (the old S is already staged); the cross
-            // terms once the staging has landed
+                    for (int i = 0; i < 4; ++i) nw[pb][x][y][i] = w_lin(ti, tv, i);
+                });
+                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nu[j][i] = u_lin(ti, i);
+                });
+                for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nx[pb][x][y][i] = s_lin(ti, tj, i);
+                });
+            }
+            if (cross) {
+                for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = accS[pb][x][y][i];
+                });
+                stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+            }
+            // the linear terms (the old S is already staged); the cross terms
+            // once the staging has landed
             for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    accW[pb][x][y][i] = a * a * accW[pb][x][y][i] +
-                                        e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col];
+                    accW[pb][x][y][i] = a * a * accW[pb][x][y][i] + (PRE ? nw[pb][x][y][PRE ? i : 0] : w_lin(ti, tv, i));
             });
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    accU[j][i] = a * a * accU[j][i] + (col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f);
+                for (int i = 0; i < 4; ++i) accU[j][i] = a * a * accU[j][i] + (PRE ? nu[j][PRE ? i : 0] : u_lin(ti, i));
             });
             for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    accS[pb][x][y][i] =
-                        a * accS[pb][x][y][i] + e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col];
+                    accS[pb][x][y][i] = a * accS[pb][x][y][i] + (PRE ? nx[pb][x][y][PRE ? i : 0] : s_lin(ti, tj, i));
             });
-            __syncthreads();
-            for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-                accW[pb][x][y] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
-            });
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                accU[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
-            });
-            __syncthreads();
+            if (cross) {
+                __syncthreads();
+                for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+                    accW[pb][x][y] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+                });
+                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                    accU[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+                });
+                __syncthreads();
+            }
             done += 1 << b;
         }
     }
