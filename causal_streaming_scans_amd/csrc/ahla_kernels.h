@@ -119,7 +119,8 @@ void ahla_forward_kernel(FwdParams p) {
     __shared__ AhlaFwdLds<T, D, DV, C> lds;
     auto &sm = lds.s;
 
-    const int seg = blockIdx.x, bh = blockIdx.y;
+    int seg, bh;
+    forward_slot(p, blockIdx.x, &seg, &bh);
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;

@@ -234,7 +234,8 @@ void hla2_forward_kernel(FwdParams p) {
     __shared__ Hla2FwdLds<T, D, DV, C, DECAY> lds;
     auto &sm = lds.s;
 
-    const int seg = blockIdx.x, bh = blockIdx.y;
+    int seg, bh;
+    forward_slot(p, blockIdx.x, &seg, &bh);
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;

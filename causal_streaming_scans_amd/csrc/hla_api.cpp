@@ -54,6 +54,29 @@ hla_status check_common(int B, int H, int d, int dv, int dtype, int variant, con
     return HLA_OK;
 }
 
+// Forward launch order of the segments (see forward_slot): by the number of
+// up-sweep nodes a segment folds into its prefix, costliest first over the
+// first half of the ranks and cheapest first over the second half, so that
+// the two workgroups a compute unit holds at once pair a costly prefix with
+// a cheap one.
+void fill_order(FwdParams *p) {
+    const int n = p->nseg;
+    if (n > kMaxOrder) return;
+    int idx[kMaxOrder];
+    for (int i = 0; i < n; ++i) idx[i] = i;
+    for (int i = 1; i < n; ++i)   // insertion sort: fold count, then index, descending
+        for (int j = i; j > 0; --j) {
+            const int a = idx[j - 1], b = idx[j];
+            const int ca = __builtin_popcount(a), cb = __builtin_popcount(b);
+            if (ca > cb || (ca == cb && a > b)) break;
+            idx[j - 1] = b;
+            idx[j] = a;
+        }
+    const int h = (n + 1) / 2;
+    for (int i = 0; i < h; ++i) p->seg_order[i] = (short)idx[i];
+    for (int j = 0; j < n - h; ++j) p->seg_order[h + j] = (short)idx[n - 1 - j];
+}
+
 void fill_gamma(float *dst, const float *gamma, int H) {
     for (int h = 0; h < kMaxDecayHeads; ++h) dst[h] = (gamma && h < H) ? gamma[h] : 1.f;
 }
@@ -116,6 +139,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, chunk, g);
     if (nseg > INT32_MAX / 4) return HLA_ERR_UNSUPPORTED;
+    if (nseg * B * H > INT32_MAX) return HLA_ERR_UNSUPPORTED;   // one-dimensional forward grid
     const size_t need = hla_workspace_bytes(variant, B, H, n, d, dv, chunk, g);
     if (need > 0) {
         if (!workspace) return HLA_ERR_NULL;
@@ -137,6 +161,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     p->state_in = state_in;
     p->state_out = state_out;
     fill_gamma(p->gamma, gamma_host, H);
+    fill_order(p);
     return HLA_OK;
 }
 

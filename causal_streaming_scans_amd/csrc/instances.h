@@ -31,7 +31,7 @@ hipError_t launch_hla2_summary(const FwdParams &p, hipStream_t s) {
 
 template <typename T, int D, int C, bool DECAY>
 hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg, p.BH),
+    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg * p.BH),
                        dim3(Hla2Cfg<T, D, D, C, DECAY>::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -45,7 +45,7 @@ hipError_t launch_ahla_summary(const FwdParams &p, hipStream_t s) {
 
 template <typename T, int D, int C>
 hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C>), dim3(p.nseg, p.BH),
+    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C>), dim3(p.nseg * p.BH),
                        dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }

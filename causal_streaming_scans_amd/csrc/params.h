@@ -6,6 +6,7 @@
 namespace hla {
 
 constexpr int kMaxDecayHeads = 256;
+constexpr int kMaxOrder = 64;   // segments whose forward launch order is chosen
 
 // One block of arguments for every forward-path kernel.  Sequence layout:
 // head bh = b*H + h owns rows [bh*n, (bh+1)*n) of q, k ([.., d]) and v, o
@@ -25,7 +26,19 @@ struct FwdParams {
     const float *state_in;   // [BH][state floats] or null
     float *state_out;        // [BH][state floats] or null
     float gamma[kMaxDecayHeads];  // decay of head h (1 when none)
+    short seg_order[kMaxOrder];    // forward: segment run by rank r (nseg <= kMaxOrder)
 };
+
+// Forward workgroup L of the 1-D grid of nseg * BH: heads vary fastest, so
+// consecutive workgroups -- dealt to different XCDs -- share one segment
+// rank, and every XCD gets every segment; rank r runs segment seg_order[r]
+// (ranks ordered so the workgroups that meet on a compute unit pair a costly
+// prefix with a cheap one).
+__device__ inline void forward_slot(const FwdParams &p, int L, int *seg, int *bh) {
+    const int r = L / p.BH;
+    *bh = L - r * p.BH;
+    *seg = p.nseg <= kMaxOrder ? p.seg_order[r] : r;
+}
 
 // Segment summary, fp32, D x D then D x DV then D x DV then D then D:
 //            X        Y        N      y     nv

@@ -112,6 +112,8 @@ def test_forward_validation_errors(lib):
     need = hla.workspace_bytes("hla2", 1, 1, 1024, 64, 64, 64, 2)
     assert need > 0
     assert _fwd(lib, fake, fake, fake, fake, n=1024, seg=2, ws=fake, wsb=need - 1) == ERR_WS
+    # the forward grid has one workgroup per (segment, head): at most 2^31 - 1
+    assert _fwd(lib, fake, fake, fake, fake, B=64, H=1000, n=1 << 21, chunk=16, seg=1) == ERR_UNSUP
     # state_in may not alias state_out
     assert _fwd(lib, fake, fake, fake, fake, si=fake, so=fake) == ERR_ARG
 
