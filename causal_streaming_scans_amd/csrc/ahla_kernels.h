@@ -33,6 +33,14 @@
 
 namespace hla {
 
+// Columns DV..DV+15 of the widened V: (1, 0, ..., 0) in every row.  Staging
+// never writes them, so they are set once.
+template <typename T, int C, int LDV, int DV, int NT>
+__device__ __forceinline__ void init_ones_column(T *V) {
+    for (int i = threadIdx.x; i < C * 16; i += NT)
+        V[(i / 16) * LDV + DV + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
+}
+
 template <typename T, int D, int DV, int C>
 struct AhlaCfg {
     using WS = WaveShape<C, D>;
@@ -281,7 +289,7 @@ void ahla_forward_kernel(FwdParams p) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, LDD, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            scores_t<T, D, R, PadTile<T, D>, false>(Lf, sm.K, qf, tau, nullptr, 1);
             ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, need_u);
             // carried part of the output and of its denominator (row DV)
             f32x4 accO[G::OJ];
@@ -439,7 +447,7 @@ void ahla_summary_kernel(FwdParams p) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, LDD, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            scores_t<T, D, R, PadTile<T, D>, false>(Lf, sm.K, qf, tau, nullptr, 1);
             ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, true);
         });
         __syncthreads();

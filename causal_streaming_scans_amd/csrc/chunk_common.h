@@ -41,16 +41,18 @@ __device__ __forceinline__ void with_row_tile(int r, F &&f) {
 // consumes a load until the next chunk is staged, and no wait for it lands
 // in the middle of the current chunk.
 //
-// Lanes run along the tokens (item idx -> token idx % C, 16-byte column
-// group idx / C): one transposed store instruction then writes consecutive
-// tokens of one feature row, which keeps the 2-byte writes free of LDS bank
-// conflicts; row-major stores stay conflict-free per quarter wave.
+// Lanes run along the columns of a row (item idx -> row idx / VPR, 16-byte
+// column group idx % VPR): one load instruction covers whole rows, i.e.
+// whole cache lines, and the row-major LDS store writes whole rows.  With
+// lanes along the tokens instead, every lane of a load touches its own cache
+// line and the vector memory path handles eight times the line requests.
 template <typename T, int C, int COLS, int NT>
 struct ChunkRegs {
     static constexpr int VE = Vec16<T>::N;
     static constexpr int VPR = COLS / VE;
     static constexpr int NVEC = C * VPR;
     static constexpr int NV = (NVEC + NT - 1) / NT;
+    static_assert(COLS % VE == 0, "rows of whole 16-byte groups");
     uint4 raw[NV];
     int rows_valid;
 
@@ -59,15 +61,15 @@ struct ChunkRegs {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
-            int r = idx % C;
-            const int c = ((idx / C) % VPR) * VE;
+            int r = idx / VPR;
+            const int c = (idx % VPR) * VE;
             if (!(idx < NVEC && r < rv)) r = 0;
             raw[i] = *reinterpret_cast<const uint4 *>(src + (size_t)r * COLS + c);
         }
     }
     __device__ __forceinline__ bool ok(int i) const {
         const int idx = threadIdx.x + i * NT;
-        return idx < NVEC && idx % C < rows_valid;
+        return idx < NVEC && idx / VPR < rows_valid;
     }
     __device__ __forceinline__ Vec16<T> get(int i) const {
         Vec16<T> x;
@@ -80,7 +82,31 @@ struct ChunkRegs {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) store16(dst + (idx % C) * ld + (idx / C) * VE, get(i));
+            if (idx < NVEC) store16(dst + (idx / VPR) * ld + (idx % VPR) * VE, get(i));
+        }
+    }
+    // the same into an LdsTile matrix
+    template <typename TL>
+    __device__ __forceinline__ void store_tile(T *dst) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) store16(dst + TL::off(idx / VPR, (idx % VPR) * VE), get(i));
+        }
+    }
+    template <typename TL>
+    __device__ __forceinline__ void store_tile_w(T *dst, const float *gp, int wofs) const {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) {
+                const int r = idx / VPR;
+                const float wr = r <= wofs ? gp[wofs - r] : 0.f;
+                Vec16<T> x = get(i);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(to_f(x.v[e]) * wr);
+                store16(dst + TL::off(r, (idx % VPR) * VE), x);
+            }
         }
     }
     // dst[r][c] = src[r][c] * w, w = gp[wofs - r] for r <= wofs, else 0
@@ -89,39 +115,12 @@ struct ChunkRegs {
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
             if (idx < NVEC) {
-                const int r = idx % C;
+                const int r = idx / VPR;
                 const float wr = r <= wofs ? gp[wofs - r] : 0.f;
                 Vec16<T> x = get(i);
 #pragma unroll
                 for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(to_f(x.v[e]) * wr);
-                store16(dst + r * ld + (idx / C) * VE, x);
-            }
-        }
-    }
-    // dstT[c][r] (transposed, leading dim ld)
-    __device__ __forceinline__ void store_cols(T *dstT, int ld) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) {
-                const int r = idx % C, c = (idx / C) * VE;
-                const Vec16<T> x = get(i);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = x.v[e];
-            }
-        }
-    }
-    // dstT[c][r] = src[r][c] * w, w = gp[wofs - r] for r <= wofs, else 0
-    __device__ __forceinline__ void store_cols_w(T *dstT, int ld, const float *gp, int wofs) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) {
-                const int r = idx % C, c = (idx / C) * VE;
-                const float wr = r <= wofs ? gp[wofs - r] : 0.f;
-                const Vec16<T> x = get(i);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) dstT[(c + e) * ld + r] = from_f<T>(to_f(x.v[e]) * wr);
+                store16(dst + r * ld + (idx % VPR) * VE, x);
             }
         }
     }

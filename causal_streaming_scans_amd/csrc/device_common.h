@@ -61,6 +61,14 @@ struct LdsTile {
     }
 };
 
+// A plain row-major [rows][COLS] layout padded by 16 bytes a row, in the
+// same form as LdsTile.
+template <typename T, int COLS>
+struct PadTile {
+    static constexpr int LD = ld_of<T>(COLS);
+    __device__ static __forceinline__ int off(int r, int c) { return r * LD + c; }
+};
+
 // ---------------------------------------------------------------- MFMA tiles
 
 // acc += A[0:16][kbeg:kend] * Bt[0:16][kbeg:kend]^T, k range a multiple of 16.
@@ -153,6 +161,19 @@ template <int K> struct RowFrags<bf16, K> {
             for (int s = 0; s < K / 16; ++s)
                 v4[s] = *reinterpret_cast<const i16x4 *>(base + r * ld + 16 * s + 4 * g);
         }
+    }    // the 16-row block of an LdsTile matrix that starts at base
+    template <typename TL>
+    __device__ __forceinline__ void load_t(const bf16 *base) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+        if constexpr (W32) {
+#pragma unroll
+            for (int s = 0; s < K / 32; ++s)
+                v8[s] = *reinterpret_cast<const bf16x8 *>(base + TL::off(r, 32 * s + 8 * g));
+        } else {
+#pragma unroll
+            for (int s = 0; s < K / 16; ++s)
+                v4[s] = *reinterpret_cast<const i16x4 *>(base + TL::off(r, 16 * s + 4 * g));
+        }
     }
 };
 template <int K> struct RowFrags<float, K> {
@@ -174,6 +195,11 @@ template <int K> struct RowFrags<float, K> {
         const int l = lane_id(), r = l & 15, g = l >> 4;
 #pragma unroll
         for (int s = 0; s < K / 4; ++s) v[s] = base[r * ld + 4 * s + g];
+    }    template <typename TL>
+    __device__ __forceinline__ void load_t(const float *base) {
+        const int l = lane_id(), r = l & 15, g = l >> 4;
+#pragma unroll
+        for (int s = 0; s < K / 4; ++s) v[s] = base[TL::off(r, 4 * s + g)];
     }
 };
 
@@ -422,6 +448,48 @@ __device__ __forceinline__ bf16x8 ld_op8_t(const bf16 *M, int ld) {
     const i16x4 lo = ds_read_tr16(p), hi = ds_read_tr16(p + 4 * ld);
     const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, both);
+}
+
+// The same operand reads from an LdsTile matrix M (its base), for the
+// sub-tile whose first row (k) is row0 and first column col0, both multiples
+// of 16.
+template <typename TL>
+__device__ __forceinline__ Frag16<bf16> ld_frag_tt(const bf16 *M, int row0, int col0) {
+    const int l = lane_id(), g = l >> 4, s = l & 15;
+    return Frag16<bf16>{ds_read_tr16(M + TL::off(row0 + 4 * g + (s >> 2), col0 + 4 * (s & 3)))};
+}
+template <typename TL>
+__device__ __forceinline__ Frag16<float> ld_frag_tt(const float *M, int row0, int col0) {
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    f32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = M[TL::off(row0 + 4 * g + i, col0 + c)];
+    return Frag16<float>{v};
+}
+template <typename TL>
+__device__ __forceinline__ bf16x8 ld_op8_tt(const bf16 *M, int row0, int col0) {
+    const int l = lane_id(), g = l >> 4, s = l & 15;
+    const int r = row0 + 8 * g + (s >> 2), c = col0 + 4 * (s & 3);
+    const i16x4 lo = ds_read_tr16(M + TL::off(r, c)), hi = ds_read_tr16(M + TL::off(r + 4, c));
+    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+// Operand fragments of a column tile that is (1, 0, ..., 0) in every row:
+// entry (k, m) is 1 for m = 0.  Either operand side holds m (or n) = l % 16,
+// so the fragment is the same constant for both.
+template <typename T> __device__ __forceinline__ Frag16<T> ones_frag();
+template <> __device__ __forceinline__ Frag16<bf16> ones_frag<bf16>() {
+    const short one = (lane_id() & 15) == 0 ? (short)0x3F80 : (short)0;   // bf16 1.0
+    return Frag16<bf16>{i16x4{one, one, one, one}};
+}
+template <> __device__ __forceinline__ Frag16<float> ones_frag<float>() {
+    const float one = (lane_id() & 15) == 0 ? 1.f : 0.f;
+    return Frag16<float>{f32x4{one, one, one, one}};
+}
+__device__ __forceinline__ bf16x8 ones_op8() {
+    const short one = (lane_id() & 15) == 0 ? (short)0x3F80 : (short)0;
+    return __builtin_bit_cast(bf16x8, i16x8{one, one, one, one, one, one, one, one});
 }
 
 // A BR x BR block of 16x16 tiles contracting over the rows of two k-major

@@ -35,17 +35,19 @@
 // its operands with the transposing LDS read, so no transposed copy is ever
 // written.  The forward kernel's Q never enters LDS: each wave reads its own
 // 16 query rows from global memory into operand registers, a chunk ahead.
-// V is widened by one 16-column tile whose first column is all ones: the
-// same products then give u = Z^T 1 (column DV of the widened W) and the
-// ratio denominator Q u0 + P 1 (column DV of the widened O), and m = Q^T 1
-// in the summary kernel.  The fp32 state S0, W0 (and u0) is spread over all
-// waves as MFMA accumulators for the whole segment; its T-typed transposed
-// copy in LDS is the operand of Q S0 and Q W0.  Z goes through LDS, since
-// every row tile needs all earlier rows of it.
+// A ones column tile (1, 0, ..., 0 in every row) is a constant operand
+// fragment in registers: its products with Z^T, Q^T and P^T give u = Z^T 1
+// (the column tile after W), m = Q^T 1 (after C) and the ratio denominator's
+// P 1.  The fp32 state S0, W0 (and u0) is spread over the waves as MFMA
+// accumulators for the whole segment; its T-typed transposed copy in LDS is
+// the operand of Q S0 and Q W0.  Z goes through LDS, since every row tile
+// needs all earlier rows of it.  Chunk tiles and state copies use the LdsTile
+// layout (swizzled 128-byte rows for bf16 with 64 columns).
 #pragma once
 
 #include "chunk_common.h"
 #include "combine.h"
+#include "state_plan.h"
 
 namespace hla {
 
@@ -53,16 +55,23 @@ template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2Cfg {
     using WS = WaveShape<C, D>;
     static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
-    static constexpr int DVX = DV + 16;       // V, W widened by the ones / u column tile
-    static constexpr int LDD = ld_of<T>(D);   // rows of length D
-    static constexpr int LDV = ld_of<T>(DVX); // rows of the widened V
+    static constexpr int DVX = DV + 16;       // W widened by the u column tile
+    using TK = LdsTile<T, D>;                 // chunk rows of length D: Q, K, Z (and weighted copies)
+    using TV = LdsTile<T, DV>;                // chunk rows of V
     using TS = LdsTile<T, D>;                 // the state copies St, Wt
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int ZJ = (nTD + NCG - 1) / NCG;    // Z^T tiles per wave
     static constexpr int OJ = (nTV + NCG - 1) / NCG;    // O^T tiles per wave
     static constexpr int UJ = (nTD + NW - 1) / NW;      // tiles of the u (m) column per wave
-    using SB = TileBlocks<nTD, nTD, NW>;    // ownership of S tiles
-    using WB = TileBlocks<nTD, nTV, NW>;    // ownership of W (and C) tiles
+    using SB = TileBlocks<nTD, nTD, NW>;    // even ownership of S tiles
+    using WB = TileBlocks<nTD, nTV, NW>;    // even ownership of W (and C) tiles
+    // which wave holds which state tiles: a balanced table for the common
+    // shape, the even round-robin layout otherwise
+    static constexpr bool BAL = C == 64 && D == 64 && DV == 64 && NCG == 1;
+    template <int R>
+    using FwdPlan = std::conditional_t<BAL, FixedPlan<Hla2Fwd64Tab, R>, RoundRobinPlan<nTD, nTV, NW, false>>;
+    template <int R>
+    using SumPlan = std::conditional_t<BAL, FixedPlan<Hla2Sum64Tab, R>, RoundRobinPlan<nTD, nTV, NW, true>>;
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = hla2_state_floats(D, DV);
     static constexpr int NPOW = 2 * C + 2;
@@ -104,14 +113,6 @@ __device__ __forceinline__ void for_stripe(int w, F f) {
     }
 }
 
-// Columns DV..DV+15 of the widened V: (1, 0, ..., 0) in every row.  Staging
-// never writes them, so they are set once.
-template <typename T, int C, int LDV, int DV, int NT>
-__device__ __forceinline__ void init_ones_column(T *V) {
-    for (int i = threadIdx.x; i < C * 16; i += NT)
-        V[(i / 16) * LDV + DV + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
-}
-
 // acc += A^T B over the C token rows for one 16x16 tile (k-major operands)
 template <int C, typename T>
 __device__ __forceinline__ f32x4 mma_tn_tile(f32x4 acc, const T *A, int lda, const T *B, int ldb) {
@@ -123,11 +124,11 @@ __device__ __forceinline__ f32x4 mma_tn_tile(f32x4 acc, const T *A, int lda, con
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2FwdSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
-    alignas(16) T K[C * G::LDD];
-    alignas(16) T Kw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(c-1-tau)
-    alignas(16) T V[C * G::LDV];                 // widened: columns DV.. = (1, 0, ..)
-    alignas(16) T Z[C * G::LDD];
-    alignas(16) T Zw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(2(c-1-tau))
+    alignas(16) T K[C * G::TK::LD];
+    alignas(16) T Kw[DECAY ? C * G::TK::LD : 8];    // rows weighted by g^(c-1-tau)
+    alignas(16) T V[C * G::TV::LD];
+    alignas(16) T Z[C * G::TK::LD];
+    alignas(16) T Zw[DECAY ? C * G::TK::LD : 8];    // rows weighted by g^(2(c-1-tau))
     alignas(16) T St[D * G::TS::LD];             // St[j][i] = S0[i][j]
     alignas(16) T Wt[G::DVX * G::TS::LD];        // Wt[j][i] = W0[i][j]; row DV = u0
     float gp[G::NPOW];
@@ -139,12 +140,12 @@ using Hla2FwdLds = LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY>, CrossLds<D, D
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
-    alignas(16) T Q[C * G::LDD];
-    alignas(16) T Qw[DECAY ? C * G::LDD : 8];    // rows weighted by g^(c-1-tau)
-    alignas(16) T K[C * G::LDD];
-    alignas(16) T Kw[DECAY ? C * G::LDD : 8];
-    alignas(16) T V[C * G::LDV];
-    alignas(16) T Z[C * G::LDD];                 // rows weighted by g^(2(c-1-tau))
+    alignas(16) T Q[C * G::TK::LD];
+    alignas(16) T Qw[DECAY ? C * G::TK::LD : 8];    // rows weighted by g^(c-1-tau)
+    alignas(16) T K[C * G::TK::LD];
+    alignas(16) T Kw[DECAY ? C * G::TK::LD : 8];
+    alignas(16) T V[C * G::TV::LD];
+    alignas(16) T Z[C * G::TK::LD];                 // rows weighted by g^(2(c-1-tau))
     alignas(16) T St[D * G::TS::LD];
     float gp[G::NPOW];
 };
@@ -162,21 +163,25 @@ constexpr int hla2_fwd_blocks() {
     const int b = hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2FwdLds<T, D, DV, C, DECAY>)>();
     return b > 2 ? 2 : b;
 }
+// The balanced plan's row tile 0 holds 17 state tiles: built for two
+// workgroups per CU (the summary stage has fewer workgroups than the forward
+// stage, so a third slot per CU mostly stays empty).
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int hla2_sum_blocks() {
-    return hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2SumSmem<T, D, DV, C, DECAY>)>();
+    const int b = hla_min_blocks<Hla2Cfg<T, D, DV, C, DECAY>::NT, (int)sizeof(Hla2SumSmem<T, D, DV, C, DECAY>)>();
+    return Hla2Cfg<T, D, DV, C, DECAY>::BAL && b > 2 ? 2 : b;
 }
 
 // L^T tiles of row tile R as operand fragments: Lf[s] holds
 // (D_g * tril(Q K^T))^T[sigma in tile s][tau in tile R], s <= R.  Only the
 // diagonal tile s == R needs the causal mask.
-template <typename T, int D, int R, int LDD, bool DECAY>
+template <typename T, int D, int R, typename TL, bool DECAY>
 __device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[R + 1], const T *K, const RowFrags<T, D> &qf,
                                          int tau, const float *gp, int gexp) {
     const int g4 = (lane_id() >> 4) << 2;
     f32x4 a[R + 1];
 #pragma unroll
-    for (int s = 0; s <= R; ++s) a[s] = mma_nt_f(zero4(), K + 16 * s * LDD, LDD, qf);
+    for (int s = 0; s <= R; ++s) a[s] = mma_nt_ft<TL>(zero4(), K + 16 * s * TL::LD, qf);
 #pragma unroll
     for (int s = 0; s <= R; ++s) {
 #pragma unroll
@@ -193,7 +198,7 @@ __device__ __forceinline__ void scores_t(Frag16<T> (&Lf)[R + 1], const T *K, con
 
 // Z^T tiles of row tile R: Z = diag(g^(tau+1)) Q S0 + L K, stored row-major
 // (times w) into Zd.  Shared by the forward and summary kernels.
-template <typename T, int D, int R, int NCG, int ZJ, int LDD, bool DECAY, typename TS>
+template <typename T, int D, int R, int NCG, int ZJ, typename TK, bool DECAY, typename TS>
 __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
                                         const T *St, const T *K, T *Zd, T *Zwd, float wz,
                                         const float *gp, int cg, int tau) {
@@ -207,7 +212,7 @@ __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T
             f32x4 zq = mma_nt_ft<TS>(zero4(), St + 16 * jt * TS::LD, qf);
             f32x4 zc = zero4();
 #pragma unroll
-            for (int s = 0; s <= R; ++s) zc = mma16(zc, ld_frag_t(K + 16 * s * LDD + 16 * jt, LDD), Lf[s]);
+            for (int s = 0; s <= R; ++s) zc = mma16(zc, ld_frag_tt<TK>(K, 16 * s, 16 * jt), Lf[s]);
             z[jj] = (DECAY ? zq * gp[tau + 1] : zq) + zc;
         }
     }
@@ -216,8 +221,8 @@ __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T
     for (int jj = 0; jj < ZJ; ++jj) {
         const int jt = cg + jj * NCG;
         if (jt < D / 16) {
-            if (Zd) store4(Zd + tau * LDD + 16 * jt + g4, z[jj]);
-            if (Zwd) store4(Zwd + tau * LDD + 16 * jt + g4, z[jj] * wz);
+            if (Zd) store4(Zd + TK::off(tau, 16 * jt + g4), z[jj]);
+            if (Zwd) store4(Zwd + TK::off(tau, 16 * jt + g4), z[jj] * wz);
         }
     }
 }
@@ -230,7 +235,9 @@ __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
 void hla2_forward_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
+    constexpr int nTV = G::nTV;
+    using TK = typename G::TK;
+    using TV = typename G::TV;
     __shared__ Hla2FwdLds<T, D, DV, C, DECAY> lds;
     auto &sm = lds.s;
 
@@ -270,139 +277,170 @@ void hla2_forward_kernel(FwdParams p) {
         W0 = e + D * D;
         u0 = e + D * D + D * DV;
     }
-    using SB = typename G::SB;
-    using WB = typename G::WB;
     using O = SumOfs<D, DV>;
-    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accU[G::UJ];
-    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+
+    // Everything below runs unrolled for the wave's row tile R, so each wave
+    // holds exactly the state tiles its plan gives it.
+    with_row_tile<RT>(r, [&](auto rt) {
+        constexpr int R = decltype(rt)::value;
+        using P = typename G::template FwdPlan<R>;
+        const int tau = 16 * R + col;    // the lane's token within the chunk
+
+        // the fp32 state tiles this wave holds (u as column tile nTV of W)
+        f32x4 acc[P::NA];
+        for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            accS[pb][x][y][i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
-    });
-    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            for (int i = 0; i < 4; ++i) acc[j][i] = S0 ? S0[(16 * ti + g4 + i) * D + 16 * tj + col] : 0.f;
+        });
+        for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            accW[pb][x][y][i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
-    });
-    // u as column DV of the widened W (the other 15 columns stay zero)
-    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+            for (int i = 0; i < 4; ++i) acc[j][i] = W0 ? W0[(16 * ti + g4 + i) * DV + 16 * tv + col] : 0.f;
+        });
+        for_tiles<P, kU>(w, [&](int j, int ti, int) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accU[j][i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
-    });
-    if (seg > 0) {
-        // fold node B (later) into the running state A: W <- a^2 W + N_B +
-        // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
-        // the node's [Y | y] are staged in LDS (fp32) as the cross factors
-        using L = CrossLds<D, DV>;  // fold: whole right factor
-        float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
-        int done = 0;
-        for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
-            if (!((seg >> b) & 1)) continue;
-            const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
-            const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
-            // with no caller state the first node folds into zero: no cross terms
-            const bool cross = p.state_in != nullptr || done > 0;
-            // The node's linear parts: with d <= 64 they are loaded into
-            // registers ahead of the staging, so every global load of the node
-            // is in flight at once (larger heads have no registers to spare)
-            constexpr bool PRE = D <= 64;
-            float nw[WB::PB][WB::BR][WB::BR][PRE ? 4 : 1], nx[SB::PB][SB::BR][SB::BR][PRE ? 4 : 1],
-                nu[G::UJ][PRE ? 4 : 1];
-            auto w_lin = [&](int ti, int tv, int i) { return e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col]; };
-            auto u_lin = [&](int ti, int i) { return col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f; };
-            auto s_lin = [&](int ti, int tj, int i) { return e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col]; };
-            if constexpr (PRE) {
-                for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
+            for (int i = 0; i < 4; ++i) acc[j][i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
+        });
+        if (seg > 0) {
+            // fold node B (later) into the running state A: W <- a^2 W + N_B +
+            // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
+            // the node's [Y | y] are staged in LDS (fp32) as the cross factors
+            using L = CrossLds<D, DV>;  // fold: whole right factor
+            float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
+            int done = 0;
+            for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
+                if (!((seg >> b) & 1)) continue;
+                const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
+                const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
+                // with no caller state the first node folds into zero: no cross terms
+                const bool cross = p.state_in != nullptr || done > 0;
+                // The node's linear parts: with d <= 64 they are loaded into
+                // registers ahead of the staging, so every global load of the
+                // node is in flight at once (larger heads have no registers to
+                // spare)
+                constexpr bool PRE = D <= 64;
+                f32x4 nl[PRE ? P::NA : 1];
+                auto w_lin = [&](int ti, int tv, int i) {
+                    return e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col];
+                };
+                auto u_lin = [&](int ti, int i) { return col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f; };
+                auto s_lin = [&](int ti, int tj, int i) { return e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col]; };
+                if constexpr (PRE) {
+                    for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) nw[pb][x][y][i] = w_lin(ti, tv, i);
-                });
-                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
+                        for (int i = 0; i < 4; ++i) nl[j][i] = w_lin(ti, tv, i);
+                    });
+                    for_tiles<P, kU>(w, [&](int j, int ti, int) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) nu[j][i] = u_lin(ti, i);
-                });
-                for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+                        for (int i = 0; i < 4; ++i) nl[j][i] = u_lin(ti, i);
+                    });
+                    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) nx[pb][x][y][i] = s_lin(ti, tj, i);
-                });
-            }
-            if (cross) {
-                for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
+                        for (int i = 0; i < 4; ++i) nl[j][i] = s_lin(ti, tj, i);
+                    });
+                }
+                if (cross) {
+                    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
+                    });
+                    stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                }
+                // the linear terms (the old S is already staged); the cross
+                // terms once the staging has landed
+                for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = accS[pb][x][y][i];
+                        acc[j][i] = a * a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : w_lin(ti, tv, i));
                 });
-                stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                for_tiles<P, kU>(w, [&](int j, int ti, int) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] = a * a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : u_lin(ti, i));
+                });
+                for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[j][i] = a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : s_lin(ti, tj, i));
+                });
+                if (cross) {
+                    __syncthreads();
+                    for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+                    });
+                    for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+                    });
+                    __syncthreads();
+                }
+                done += 1 << b;
             }
-            // the linear terms (the old S is already staged); the cross terms
-            // once the staging has landed
-            for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    accW[pb][x][y][i] = a * a * accW[pb][x][y][i] + (PRE ? nw[pb][x][y][PRE ? i : 0] : w_lin(ti, tv, i));
-            });
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accU[j][i] = a * a * accU[j][i] + (PRE ? nu[j][PRE ? i : 0] : u_lin(ti, i));
-            });
-            for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    accS[pb][x][y][i] = a * accS[pb][x][y][i] + (PRE ? nx[pb][x][y][PRE ? i : 0] : s_lin(ti, tj, i));
-            });
-            if (cross) {
-                __syncthreads();
-                for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-                    accW[pb][x][y] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
-                });
-                for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                    accU[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
-                });
-                __syncthreads();
-            }
-            done += 1 << b;
         }
-    }
-    // T-typed transposed copies: the operands of Q S0 and Q W0 (row DV of Wt = u)
-    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-        store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
-    });
-    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-        store4(sm.Wt + G::TS::off(16 * tv + col, 16 * ti + g4), accW[pb][x][y]);
-    });
-    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        store4(sm.Wt + G::TS::off(DV + col, 16 * ti + g4), accU[j]);
-    });
-    if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
+        // T-typed transposed copies: the operands of Q S0 and Q W0 (row DV of Wt = u)
+        auto store_copies = [&](bool with_u) {
+            for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+                store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), acc[j]);
+            });
+            for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+                store4(sm.Wt + G::TS::off(16 * tv + col, 16 * ti + g4), acc[j]);
+            });
+            if (with_u) {
+                for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                    store4(sm.Wt + G::TS::off(DV + col, 16 * ti + g4), acc[j]);
+                });
+            }
+        };
+        store_copies(true);
+        if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
 
-    int c0 = t_begin;
-    int cv = min(C, t_end - c0);
-    load_chunk(c0, cv);
+        int c0 = t_begin;
+        int cv = min(C, t_end - c0);
+        load_chunk(c0, cv);
 
-    while (c0 < t_end) {
-        __syncthreads();   // previous chunk's readers are done; setup is visible
-        // ---- a-1: stage this chunk, then start loading the next one
-        rk.store_rows(sm.K, LDD);
-        if (DECAY) rk.store_rows_w(sm.Kw, LDD, sm.gp, cv - 1);
-        rv.store_rows(sm.V, LDV);
-        RowFrags<T, D> qf = qn;            // the row tile's Q: operand of four products
-        qf.mask_rows(cv - 16 * r);
-        const int n0 = c0 + C;
-        const int ncv = min(C, t_end - n0);
-        if (n0 < t_end) load_chunk(n0, ncv);
-        __syncthreads();
+        while (c0 < t_end) {
+            __syncthreads();   // previous chunk's readers are done; setup is visible
+            // ---- a-1: stage this chunk, then start loading the next one
+            rk.template store_tile<TK>(sm.K);
+            if (DECAY) rk.template store_tile_w<TK>(sm.Kw, sm.gp, cv - 1);
+            rv.template store_tile<TV>(sm.V);
+            RowFrags<T, D> qf = qn;            // the row tile's Q: operand of four products
+            qf.mask_rows(cv - 16 * R);
+            const int n0 = c0 + C;
+            const int ncv = min(C, t_end - n0);
+            if (n0 < t_end) load_chunk(n0, ncv);
+            __syncthreads();
 
-        with_row_tile<RT>(r, [&](auto rt) {
-            constexpr int R = decltype(rt)::value;
-            const int tau = 16 * R + col;    // the lane's token within the chunk
+            // ---- a-7: advance the held state tiles of phase PH by this chunk
+            const float gc = DECAY ? sm.gp[cv] : 1.f;
+            const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
+            const T *KA = DECAY ? sm.Kw : sm.K;
+            const T *ZA = DECAY ? sm.Zw : sm.Z;
+            auto advance = [&](auto ph) {
+                for_groups<P, -1, decltype(ph)::value>(w, [&](auto gi, int ti0, int tj0) {
+                    constexpr Grp gr = P::grp(decltype(gi)::value);
+                    f32x4 *a = acc + gr.first;
+                    if constexpr (gr.mat == kS) {
+                        if (DECAY) {
+#pragma unroll
+                            for (int x = 0; x < gr.nr * gr.nc; ++x) a[x] *= gc;
+                        }
+                        mma_tn_grp<gr.nr, gr.nc, C, TK, TK, false>(a, KA, 16 * ti0, sm.K, 16 * tj0);
+                    } else if (gr.mat == kW || need_u) {
+                        if (DECAY) {
+#pragma unroll
+                            for (int x = 0; x < gr.nr * gr.nc; ++x) a[x] *= gc2;
+                        }
+                        mma_tn_grp<gr.nr, gr.nc, C, TK, TV, gr.mat == kU>(a, ZA, 16 * ti0, sm.V, 16 * tj0);
+                    }
+                });
+            };
+
             // ---- a-2: L^T for this row tile, as operand fragments
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, LDD, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
+            scores_t<T, D, R, TK, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
 
             // ---- a-3: Z^T = diag(g^(tau+1)) (Q S0)^T + K^T L^T
             const float wz = DECAY ? (tau < cv ? sm.gp[2 * (cv - 1 - tau)] : 0.f) : 1.f;
-            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, sm.Z, DECAY ? sm.Zw : nullptr,
-                                                     wz, sm.gp, cg, tau);
+            z_tiles<T, D, R, NCG, G::ZJ, TK, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, sm.Z,
+                                                                     DECAY ? sm.Zw : nullptr, wz, sm.gp, cg, tau);
             // ---- a-4 (carried part): O^T = diag(g^(2(tau+1))) (Q W0)^T; the
             // denominator's carried part q . u0 is row DV of the widened product
             f32x4 accO[G::OJ];
@@ -420,18 +458,22 @@ void hla2_forward_kernel(FwdParams p) {
                 accD = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + DV * G::TS::LD, qf);
                 if (DECAY) accD *= sm.gp[2 * (tau + 1)];
             }
+            // products of the staged chunk alone (S += K^T K), while the waves
+            // of later row tiles finish Z
+            advance(std::integral_constant<int, 0>{});
             __syncthreads();
 
             // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
             Frag16<T> Pf[R + 1];
-            scores_t<T, D, R, LDD, DECAY>(Pf, sm.Z, qf, tau, sm.gp, 2);
+            scores_t<T, D, R, TK, DECAY>(Pf, sm.Z, qf, tau, sm.gp, 2);
             float rden = 1.f;
             if (ratio) {
-                // den = q . u0 + P 1: row DV of the widened O^T, held in slot 0
-                // of the token's lane in group 0
+                // den = q . u0 + P 1: the product with a ones column tile puts
+                // P 1 in slot 0 of the token's lane in group 0
                 f32x4 dc = zero4();
+                const Frag16<T> ones = ones_frag<T>();
 #pragma unroll
-                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_t(sm.V + 16 * s * LDV + DV, LDV), Pf[s]);
+                for (int s = 0; s <= R; ++s) dc = mma16(dc, ones, Pf[s]);
                 rden = 1.f / __shfl(accD[0] + dc[0], col);
             }
 #pragma unroll
@@ -441,79 +483,39 @@ void hla2_forward_kernel(FwdParams p) {
                     f32x4 oc = zero4();
 #pragma unroll
                     for (int s = 0; s <= R; ++s)
-                        oc = mma16(oc, ld_frag_t(sm.V + 16 * s * LDV + 16 * jv, LDV), Pf[s]);
+                        oc = mma16(oc, ld_frag_tt<TV>(sm.V, 16 * s, 16 * jv), Pf[s]);
                     f32x4 ov = accO[jj] + oc;
                     if (ratio) ov *= rden;
                     if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
                 }
             }
-        });
 
-        // ---- a-7: advance the carried state by this chunk
-        const float gc = DECAY ? sm.gp[cv] : 1.f;
-        const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
-        const T *KA = DECAY ? sm.Kw : sm.K;
-        const T *ZA = DECAY ? sm.Zw : sm.Z;
-        // all products first, then the T-typed copies, so no operand load
-        // waits behind a store
-        for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
-            if (DECAY) {
+            // the rest of the state (W, u: products of Z) after every product,
+            // then the T-typed copies, so no operand load waits behind a store
+            advance(std::integral_constant<int, 1>{});
+            store_copies(need_u);
+            c0 = n0;
+            cv = ncv;
+        }
+
+        if (p.state_out && last) {
+            float *so = p.state_out + (size_t)bh * G::STF;
+            for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-                for (int x = 0; x < SB::BR; ++x)
+                for (int i = 0; i < 4; ++i) so[(16 * ti + g4 + i) * D + 16 * tj + col] = acc[j][i];
+            });
+            for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
 #pragma unroll
-                    for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
-            }
-            mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
-        });
-        for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
-            if (DECAY) {
+                for (int i = 0; i < 4; ++i) so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = acc[j][i];
+            });
+            for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                if (col == 0) {
 #pragma unroll
-                for (int x = 0; x < WB::BR; ++x)
-#pragma unroll
-                    for (int y = 0; y < WB::BR; ++y) accW[pb][x][y] *= gc2;
-            }
-            mma_tn_blk<WB::BR, C>(accW[pb], ZA + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-        });
-        if (need_u) {
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], ZA + 16 * ti, LDD,
-                                         sm.V + DV, LDV);
+                    for (int i = 0; i < 4; ++i) so[D * D + D * DV + 16 * ti + g4 + i] = acc[j][i];
+                }
             });
         }
-        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-            store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
-        });
-        for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-            store4(sm.Wt + G::TS::off(16 * tv + col, 16 * ti + g4), accW[pb][x][y]);
-        });
-        if (need_u) {
-            for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                store4(sm.Wt + G::TS::off(DV + col, 16 * ti + g4), accU[j]);
-            });
-        }
-        c0 = n0;
-        cv = ncv;
-    }
-
-    if (p.state_out && last) {
-        float *so = p.state_out + (size_t)bh * G::STF;
-        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                so[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];
-        });
-        for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                so[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = accW[pb][x][y][i];
-        });
-        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-            if (col == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) so[D * D + D * DV + 16 * ti + g4 + i] = accU[j][i];
-            }
-        });
-    }
+    });
 }
 
 // ------------------------------------------------------------ summary kernel
@@ -524,7 +526,8 @@ __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
 void hla2_summary_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD;
+    using TK = typename G::TK;
+    using TV = typename G::TV;
     __shared__ Hla2SumSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -539,132 +542,114 @@ void hla2_summary_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
     if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
-    using SB = typename G::SB;
-    using WB = typename G::WB;
-    f32x4 accS[SB::PB][SB::BR][SB::BR], accW[WB::PB][WB::BR][WB::BR], accC[WB::PB][WB::BR][WB::BR];
-    f32x4 accU[G::UJ], accM[G::UJ];
-#pragma unroll
-    for (int pb = 0; pb < SB::PB; ++pb)
-#pragma unroll
-        for (int x = 0; x < SB::BR; ++x)
-#pragma unroll
-            for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] = zero4();
-#pragma unroll
-    for (int pb = 0; pb < WB::PB; ++pb)
-#pragma unroll
-        for (int x = 0; x < WB::BR; ++x)
-#pragma unroll
-            for (int y = 0; y < WB::BR; ++y) {
-                accW[pb][x][y] = zero4();
-                accC[pb][x][y] = zero4();
-            }
-#pragma unroll
-    for (int j = 0; j < G::UJ; ++j) {
-        accU[j] = zero4();
-        accM[j] = zero4();
-    }
     for (int i = threadIdx.x; i < D * G::TS::LD; i += NT) sm.St[i] = from_f<T>(0.f);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
-    int c0 = t_begin;
-    int cv = min(C, t_end - c0);
-    rq.load(q + (size_t)c0 * D, cv);
-    rk.load(k + (size_t)c0 * D, cv);
-    rv.load(v + (size_t)c0 * DV, cv);
 
-    while (c0 < t_end) {
-        __syncthreads();
-        rq.store_rows(sm.Q, LDD);
-        if (DECAY) rq.store_rows_w(sm.Qw, LDD, sm.gp, cv - 1);
-        rk.store_rows(sm.K, LDD);
-        if (DECAY) rk.store_rows_w(sm.Kw, LDD, sm.gp, cv - 1);
-        rv.store_rows(sm.V, LDV);
-        const int n0 = c0 + C;
-        const int ncv = min(C, t_end - n0);
-        if (n0 < t_end) {
-            rq.load(q + (size_t)n0 * D, ncv);
-            rk.load(k + (size_t)n0 * D, ncv);
-            rv.load(v + (size_t)n0 * DV, ncv);
-        }
-        __syncthreads();
+    // Everything below runs unrolled for the wave's row tile R, so each wave
+    // holds exactly the summary tiles its plan gives it.
+    with_row_tile<RT>(r, [&](auto rt) {
+        constexpr int R = decltype(rt)::value;
+        using P = typename G::template SumPlan<R>;
+        const int tau = 16 * R + col;
+        // S, W, C and the stripes u = Z^T 1, m = Q^T 1, all from zero
+        f32x4 acc[P::NA];
+#pragma unroll
+        for (int j = 0; j < P::NA; ++j) acc[j] = zero4();
 
-        RowFrags<T, D> qf;
-        qf.load(sm.Q + 16 * r * LDD, LDD);
-        with_row_tile<RT>(r, [&](auto rt) {
-            constexpr int R = decltype(rt)::value;
-            const int tau = 16 * R + col;
+        int c0 = t_begin;
+        int cv = min(C, t_end - c0);
+        rq.load(q + (size_t)c0 * D, cv);
+        rk.load(k + (size_t)c0 * D, cv);
+        rv.load(v + (size_t)c0 * DV, cv);
+
+        while (c0 < t_end) {
+            __syncthreads();
+            rq.template store_tile<TK>(sm.Q);
+            if (DECAY) rq.template store_tile_w<TK>(sm.Qw, sm.gp, cv - 1);
+            rk.template store_tile<TK>(sm.K);
+            if (DECAY) rk.template store_tile_w<TK>(sm.Kw, sm.gp, cv - 1);
+            rv.template store_tile<TV>(sm.V);
+            const int n0 = c0 + C;
+            const int ncv = min(C, t_end - n0);
+            if (n0 < t_end) {
+                rq.load(q + (size_t)n0 * D, ncv);
+                rk.load(k + (size_t)n0 * D, ncv);
+                rv.load(v + (size_t)n0 * DV, ncv);
+            }
+            __syncthreads();
+
+            const float gc = DECAY ? sm.gp[cv] : 1.f;
+            const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
+            const T *KA = DECAY ? sm.Kw : sm.K;
+            const T *QA = DECAY ? sm.Qw : sm.Q;
+            // advance the held tiles of phase PH by this chunk: S += K^T K,
+            // C (m) += Q^T [V | 1], W (u) += Z^T [V | 1]
+            auto advance = [&](auto ph) {
+                for_groups<P, -1, decltype(ph)::value>(w, [&](auto gi, int ti0, int tj0) {
+                    constexpr Grp gr = P::grp(decltype(gi)::value);
+                    f32x4 *a = acc + gr.first;
+                    const float sc = (gr.mat == kW || gr.mat == kU) ? gc2 : gc;
+                    if (DECAY) {
+#pragma unroll
+                        for (int x = 0; x < gr.nr * gr.nc; ++x) a[x] *= sc;
+                    }
+                    if constexpr (gr.mat == kS)
+                        mma_tn_grp<gr.nr, gr.nc, C, TK, TK, false>(a, KA, 16 * ti0, sm.K, 16 * tj0);
+                    else if constexpr (gr.mat == kW || gr.mat == kU)
+                        mma_tn_grp<gr.nr, gr.nc, C, TK, TV, gr.mat == kU>(a, sm.Z, 16 * ti0, sm.V, 16 * tj0);
+                    else
+                        mma_tn_grp<gr.nr, gr.nc, C, TK, TV, gr.mat == kM>(a, QA, 16 * ti0, sm.V, 16 * tj0);
+                });
+            };
+
+            RowFrags<T, D> qf;
+            qf.template load_t<TK>(sm.Q + 16 * R * TK::LD);
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, LDD, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
+            scores_t<T, D, R, TK, DECAY>(Lf, sm.K, qf, tau, sm.gp, 1);
             // Z rows weighted by g^(2(c-1-tau)): only the W and u updates use Z here
             const float wz = tau < cv ? (DECAY ? sm.gp[2 * (cv - 1 - tau)] : 1.f) : 0.f;
-            z_tiles<T, D, R, NCG, G::ZJ, LDD, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz, sm.gp, cg,
-                                                     tau);
-        });
-        __syncthreads();
-
-        const float gc = DECAY ? sm.gp[cv] : 1.f;
-        const float gc2 = DECAY ? sm.gp[2 * cv] : 1.f;
-        const T *KA = DECAY ? sm.Kw : sm.K;
-        const T *QA = DECAY ? sm.Qw : sm.Q;
-        for_blocks<SB, NW>(w, [&](int pb, int ti0, int tj0) {
-            if (DECAY) {
-#pragma unroll
-                for (int x = 0; x < SB::BR; ++x)
-#pragma unroll
-                    for (int y = 0; y < SB::BR; ++y) accS[pb][x][y] *= gc;
-            }
-            mma_tn_blk<SB::BR, C>(accS[pb], KA + 16 * ti0, LDD, sm.K + 16 * tj0, LDD);
-        });
-        for_blocks<WB, NW>(w, [&](int pb, int ti0, int tv0) {
-            if (DECAY) {
-#pragma unroll
-                for (int x = 0; x < WB::BR; ++x)
-#pragma unroll
-                    for (int y = 0; y < WB::BR; ++y) {
-                        accW[pb][x][y] *= gc2;
-                        accC[pb][x][y] *= gc;
-                    }
-            }
-            mma_tn_blk<WB::BR, C>(accW[pb], sm.Z + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-            mma_tn_blk<WB::BR, C>(accC[pb], QA + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-        });
-        // u = Z^T 1 and m = Q^T 1: the ones column of the widened V
-        for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-            accU[j] = mma_tn_tile<C>(DECAY ? accU[j] * gc2 : accU[j], sm.Z + 16 * ti, LDD, sm.V + DV, LDV);
-            accM[j] = mma_tn_tile<C>(DECAY ? accM[j] * gc : accM[j], QA + 16 * ti, LDD, sm.V + DV, LDV);
-        });
-        // the running S's T-typed copy after every product of the chunk
-        for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-            store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), accS[pb][x][y]);
-        });
-        c0 = n0;
-        cv = ncv;
-    }
-
-    // summary [X = S | Y = C | N = W | y = m | nv = u]
-    float *e = p.ws + node_offset(bh, 0, seg, p.BH, p.nreal, G::SUMF);
-    for_owned<SB, NW>(w, [&](int pb, int x, int y, int ti, int tj) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = accS[pb][x][y][i];
-    });
-    for_owned<WB, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = (16 * ti + g4 + i) * DV + 16 * tv + col;
-            e[D * D + idx] = accC[pb][x][y][i];
-            e[D * D + D * DV + idx] = accW[pb][x][y][i];
+            z_tiles<T, D, R, NCG, G::ZJ, TK, DECAY, typename G::TS>(qf, Lf, sm.St, sm.K, nullptr, sm.Z, wz, sm.gp,
+                                                                     cg, tau);
+            // products of the staged chunk alone, while later row tiles finish Z
+            advance(std::integral_constant<int, 0>{});
+            __syncthreads();
+            advance(std::integral_constant<int, 1>{});
+            // the running S's T-typed copy after every product of the chunk
+            for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+                store4(sm.St + G::TS::off(16 * tj + col, 16 * ti + g4), acc[j]);
+            });
+            c0 = n0;
+            cv = ncv;
         }
-    });
-    for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        if (col == 0) {
+
+        // summary [X = S | Y = C | N = W | y = m | nv = u]
+        float *e = p.ws + node_offset(bh, 0, seg, p.BH, p.nreal, G::SUMF);
+        for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                e[D * D + 2 * D * DV + 16 * ti + g4 + i] = accM[j][i];
-                e[D * D + 2 * D * DV + D + 16 * ti + g4 + i] = accU[j][i];
+            for (int i = 0; i < 4; ++i) e[(16 * ti + g4 + i) * D + 16 * tj + col] = acc[j][i];
+        });
+        for_tiles<P, kC>(w, [&](int j, int ti, int tv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[D * D + (16 * ti + g4 + i) * DV + 16 * tv + col] = acc[j][i];
+        });
+        for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[D * D + D * DV + (16 * ti + g4 + i) * DV + 16 * tv + col] = acc[j][i];
+        });
+        for_tiles<P, kM>(w, [&](int j, int ti, int) {
+            if (col == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e[D * D + 2 * D * DV + 16 * ti + g4 + i] = acc[j][i];
             }
-        }
+        });
+        for_tiles<P, kU>(w, [&](int j, int ti, int) {
+            if (col == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) e[D * D + 2 * D * DV + D + 16 * ti + g4 + i] = acc[j][i];
+            }
+        });
     });
 }
 
