@@ -22,10 +22,12 @@
 // transposed scores L^T = K Q^T stay in registers and serve as the B operand
 // of V^T L^T (for Y^T) and of Y^T L^T (for O^T).  Y^T's accumulator holds
 // four consecutive features of one token, so Y goes to LDS row-major with
-// one 8-byte store per tile.  V and Y are widened by a ones / y1 column tile
-// and P, E by the matching mK / nk column: the same products then give
-// y1 = Q mK0 + L 1 (column DV of Y), the ratio denominator Q nk0 + L y1
-// (column DV of O), mK += K^T 1 and nk += K^T y1.
+// one 8-byte store per tile.  P, E are widened by the mK / nk column, and
+// the products that need the matching column of V or Y take a ones column
+// tile (a constant operand fragment) or the y1 column tile (its own small
+// LDS tile): y1 = Q mK0 + L 1, the ratio denominator Q nk0 + L y1,
+// mK += K^T 1 and nk += K^T y1.  Chunk tiles and state copies use the
+// LdsTile layout (swizzled 128-byte rows for bf16 with 64 columns).
 #pragma once
 
 #include "chunk_common.h"
@@ -33,20 +35,14 @@
 
 namespace hla {
 
-// Columns DV..DV+15 of the widened V: (1, 0, ..., 0) in every row.  Staging
-// never writes them, so they are set once.
-template <typename T, int C, int LDV, int DV, int NT>
-__device__ __forceinline__ void init_ones_column(T *V) {
-    for (int i = threadIdx.x; i < C * 16; i += NT)
-        V[(i / 16) * LDV + DV + (i % 16)] = from_f<T>((i % 16) == 0 ? 1.f : 0.f);
-}
-
 template <typename T, int D, int DV, int C>
 struct AhlaCfg {
     using WS = WaveShape<C, D>;
     static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
-    static constexpr int DVX = DV + 16;       // V, Y, P, E widened by one column tile
-    static constexpr int LDD = ld_of<T>(D), LDV = ld_of<T>(DVX);
+    static constexpr int DVX = DV + 16;       // P, E widened by the mK / nk column tile
+    using TK = LdsTile<T, D>;                 // Q, K chunk rows; the state copies Pt, Et
+    using TV = LdsTile<T, DV>;                // V, Y chunk rows
+    using TY1 = PadTile<T, 16>;               // the y1 column tile of Y
     static constexpr int nTD = D / 16, nTV = DV / 16;
     static constexpr int OJ = (nTV + NCG - 1) / NCG;      // O^T tiles per wave
     static constexpr int YJ = (nTV + 1 + NCG - 1) / NCG;  // Y^T tiles per wave, widened
@@ -61,11 +57,12 @@ struct AhlaCfg {
 template <typename T, int D, int DV, int C>
 struct AhlaFwdSmem {
     using G = AhlaCfg<T, D, DV, C>;
-    alignas(16) T K[C * G::LDD];
-    alignas(16) T V[C * G::LDV];       // widened: columns DV.. = (1, 0, ..)
-    alignas(16) T Y[C * G::LDV];       // widened: column DV = y1
-    alignas(16) T Pt[G::DVX * G::LDD]; // Pt[j][i] = P0[i][j]; row DV = mK0
-    alignas(16) T Et[G::DVX * G::LDD]; // Et[j][i] = E0[i][j]; row DV = nk0
+    alignas(16) T K[C * G::TK::LD];
+    alignas(16) T V[C * G::TV::LD];
+    alignas(16) T Y[C * G::TV::LD];
+    alignas(16) T Y1[C * G::TY1::LD];      // column 0 = y1
+    alignas(16) T Pt[G::DVX * G::TK::LD];  // Pt[j][i] = P0[i][j]; row DV = mK0
+    alignas(16) T Et[G::DVX * G::TK::LD];  // Et[j][i] = E0[i][j]; row DV = nk0
 };
 
 template <typename T, int D, int DV, int C>
@@ -74,28 +71,35 @@ using AhlaFwdLds = LdsWithScratch<AhlaFwdSmem<T, D, DV, C>, CrossLds<D, DV>::FLO
 template <typename T, int D, int DV, int C>
 struct AhlaSumSmem {
     using G = AhlaCfg<T, D, DV, C>;
-    alignas(16) T Q[C * G::LDD];
-    alignas(16) T K[C * G::LDD];
-    alignas(16) T V[C * G::LDV];
-    alignas(16) T Y[C * G::LDV];
-    alignas(16) T Pt[G::DVX * G::LDD];
+    alignas(16) T Q[C * G::TK::LD];
+    alignas(16) T K[C * G::TK::LD];
+    alignas(16) T V[C * G::TV::LD];
+    alignas(16) T Y[C * G::TV::LD];
+    alignas(16) T Y1[C * G::TY1::LD];
+    alignas(16) T Pt[G::DVX * G::TK::LD];
 };
 
+// Built for at most two workgroups per CU: the register budget of a third
+// (168 VGPRs) makes both kernels spill at chunk 64.
 template <typename T, int D, int DV, int C>
 constexpr int ahla_fwd_blocks() {
-    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdLds<T, D, DV, C>)>();
+    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdLds<T, D, DV, C>)>();
+    return b > 2 ? 2 : b;
 }
 template <typename T, int D, int DV, int C>
 constexpr int ahla_sum_blocks() {
-    return hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C>)>();
+    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C>)>();
+    return C >= 64 && b > 2 ? 2 : b;
 }
 
-// Y^T tiles of row tile R: Y = Q P0 + L V, with the widened tile (column DV =
-// y1) when `wide`; stored row-major after every product.
-template <typename T, int D, int DV, int R, int NCG, int YJ, int LDD, int LDV>
+// Y^T tiles of row tile R: Y = Q P0 + L V, and the y1 tile (Q mK0 + L 1, in
+// Y1) when `wide`; stored row-major after every product.
+template <typename T, int D, int DV, int R, int NCG, int YJ, typename G>
 __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
-                                             const T *Pt, const T *V, T *Y, int cg, int tau,
+                                             const T *Pt, const T *V, T *Y, T *Y1, int cg, int tau,
                                              bool wide) {
+    using TK = typename G::TK;
+    using TV = typename G::TV;
     constexpr int nTV = DV / 16;
     const int g4 = (lane_id() >> 4) << 2;
     f32x4 y[YJ];
@@ -104,17 +108,19 @@ __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Fra
         const int jv = cg + jj * NCG;
         y[jj] = zero4();
         if (jv < nTV || (wide && jv == nTV)) {
-            const f32x4 yq = mma_nt_f(zero4(), Pt + 16 * jv * LDD, LDD, qf);
+            const f32x4 yq = mma_nt_ft<TK>(zero4(), Pt + 16 * jv * TK::LD, qf);
             f32x4 yc = zero4();
 #pragma unroll
-            for (int s = 0; s <= R; ++s) yc = mma16(yc, ld_frag_t(V + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
+            for (int s = 0; s <= R; ++s)
+                yc = mma16(yc, jv < nTV ? ld_frag_tt<TV>(V, 16 * s, 16 * jv) : ones_frag<T>(), Lf[s]);
             y[jj] = yq + yc;
         }
     }
 #pragma unroll
     for (int jj = 0; jj < YJ; ++jj) {
         const int jv = cg + jj * NCG;
-        if (jv < nTV || (wide && jv == nTV)) store4(Y + tau * LDV + 16 * jv + g4, y[jj]);
+        if (jv < nTV) store4(Y + TV::off(tau, 16 * jv + g4), y[jj]);
+        else if (wide && jv == nTV) store4(Y1 + G::TY1::off(tau, g4), y[jj]);
     }
 }
 
@@ -123,7 +129,10 @@ __global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_fwd_blocks<T, D, 
 void ahla_forward_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD, nTV = G::nTV;
+    constexpr int nTD = G::nTD, nTV = G::nTV;
+    using TK = typename G::TK;
+    using TV = typename G::TV;
+    using TY1 = typename G::TY1;
     __shared__ AhlaFwdLds<T, D, DV, C> lds;
     auto &sm = lds.s;
 
@@ -261,14 +270,13 @@ void ahla_forward_kernel(FwdParams p) {
         }
     }
     for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-        store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[pb][x][y]);
-        store4(sm.Et + (16 * tv + col) * LDD + 16 * ti + g4, accE[pb][x][y]);
+        store4(sm.Pt + TK::off(16 * tv + col, 16 * ti + g4), accP[pb][x][y]);
+        store4(sm.Et + TK::off(16 * tv + col, 16 * ti + g4), accE[pb][x][y]);
     });
     for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-        store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
-        store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, accNK[j]);
+        store4(sm.Pt + TK::off(DV + col, 16 * ti + g4), accMK[j]);
+        store4(sm.Et + TK::off(DV + col, 16 * ti + g4), accNK[j]);
     });
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
 
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
@@ -276,8 +284,8 @@ void ahla_forward_kernel(FwdParams p) {
 
     while (c0 < t_end) {
         __syncthreads();
-        rk.store_rows(sm.K, LDD);
-        rv.store_rows(sm.V, LDV);
+        rk.template store_tile<TK>(sm.K);
+        rv.template store_tile<TV>(sm.V);
         RowFrags<T, D> qf = qn;
         qf.mask_rows(cv - 16 * r);
         const int n0 = c0 + C;
@@ -289,18 +297,18 @@ void ahla_forward_kernel(FwdParams p) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, PadTile<T, D>, false>(Lf, sm.K, qf, tau, nullptr, 1);
-            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, need_u);
+            scores_t<T, D, R, TK, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau, need_u);
             // carried part of the output and of its denominator (row DV)
             f32x4 accO[G::OJ];
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
                 const int jv = cg + jj * NCG;
                 accO[jj] = zero4();
-                if (jv < nTV) accO[jj] = mma_nt_f(zero4(), sm.Et + 16 * jv * LDD, LDD, qf);
+                if (jv < nTV) accO[jj] = mma_nt_ft<TK>(zero4(), sm.Et + 16 * jv * TK::LD, qf);
             }
             f32x4 accD = zero4();
-            if (ratio) accD = mma_nt_f(zero4(), sm.Et + DV * LDD, LDD, qf);
+            if (ratio) accD = mma_nt_ft<TK>(zero4(), sm.Et + DV * TK::LD, qf);
             __syncthreads();
 
             // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
@@ -308,7 +316,7 @@ void ahla_forward_kernel(FwdParams p) {
             if (ratio) {
                 f32x4 dc = zero4();
 #pragma unroll
-                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_t(sm.Y + 16 * s * LDV + DV, LDV), Lf[s]);
+                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_tt<TY1>(sm.Y1, 16 * s, 0), Lf[s]);
                 rden = 1.f / __shfl(accD[0] + dc[0], col);
             }
 #pragma unroll
@@ -318,7 +326,7 @@ void ahla_forward_kernel(FwdParams p) {
                     f32x4 oc = zero4();
 #pragma unroll
                     for (int s = 0; s <= R; ++s)
-                        oc = mma16(oc, ld_frag_t(sm.Y + 16 * s * LDV + 16 * jv, LDV), Lf[s]);
+                        oc = mma16(oc, ld_frag_tt<TV>(sm.Y, 16 * s, 16 * jv), Lf[s]);
                     f32x4 ov = accO[jj] + oc;
                     if (ratio) ov *= rden;
                     if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
@@ -328,24 +336,24 @@ void ahla_forward_kernel(FwdParams p) {
         // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
         // all products first, then the T-typed copies
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-            mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], sm.K, 16 * ti0, sm.V, 16 * tv0);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], sm.K, 16 * ti0, sm.Y, 16 * tv0);
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
-                accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+                mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], sm.K, 16 * ti, sm.V, 0);
+                mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], sm.K, 16 * ti, sm.Y1, 0);
             });
         }
         for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-            const int oo = (16 * tv + col) * LDD + 16 * ti + g4;
+            const int oo = TK::off(16 * tv + col, 16 * ti + g4);
             store4(sm.Pt + oo, accP[pb][x][y]);
             store4(sm.Et + oo, accE[pb][x][y]);
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
-                store4(sm.Et + (DV + col) * LDD + 16 * ti + g4, accNK[j]);
+                store4(sm.Pt + TK::off(DV + col, 16 * ti + g4), accMK[j]);
+                store4(sm.Et + TK::off(DV + col, 16 * ti + g4), accNK[j]);
             });
         }
         c0 = n0;
@@ -379,7 +387,10 @@ __global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_sum_blocks<T, D, 
 void ahla_summary_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
-    constexpr int LDD = G::LDD, LDV = G::LDV, nTD = G::nTD;
+    constexpr int nTD = G::nTD;
+    using TK = typename G::TK;
+    using TV = typename G::TV;
+    using TY1 = typename G::TY1;
     __shared__ AhlaSumSmem<T, D, DV, C> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
@@ -392,7 +403,6 @@ void ahla_summary_kernel(FwdParams p) {
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
 
-    init_ones_column<T, C, LDV, DV, NT>(sm.V);
     using PBk = typename G::PBk;
     using MBk = typename G::MBk;
     f32x4 accP[PBk::PB][PBk::BR][PBk::BR], accE[PBk::PB][PBk::BR][PBk::BR];
@@ -417,7 +427,7 @@ void ahla_summary_kernel(FwdParams p) {
         accMK[j] = zero4();
         accNK[j] = zero4();
     }
-    for (int i = threadIdx.x; i < G::DVX * LDD; i += NT) sm.Pt[i] = from_f<T>(0.f);
+    for (int i = threadIdx.x; i < G::DVX * TK::LD; i += NT) sm.Pt[i] = from_f<T>(0.f);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -429,9 +439,9 @@ void ahla_summary_kernel(FwdParams p) {
 
     while (c0 < t_end) {
         __syncthreads();
-        rq.store_rows(sm.Q, LDD);
-        rk.store_rows(sm.K, LDD);
-        rv.store_rows(sm.V, LDV);
+        rq.template store_tile<TK>(sm.Q);
+        rk.template store_tile<TK>(sm.K);
+        rv.template store_tile<TV>(sm.V);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
         if (n0 < t_end) {
@@ -442,33 +452,33 @@ void ahla_summary_kernel(FwdParams p) {
         __syncthreads();
 
         RowFrags<T, D> qf;
-        qf.load(sm.Q + 16 * r * LDD, LDD);
+        qf.template load_t<TK>(sm.Q + 16 * r * TK::LD);
         with_row_tile<RT>(r, [&](auto rt) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, PadTile<T, D>, false>(Lf, sm.K, qf, tau, nullptr, 1);
-            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, LDD, LDV>(qf, Lf, sm.Pt, sm.V, sm.Y, cg, tau, true);
+            scores_t<T, D, R, TK, false>(Lf, sm.K, qf, tau, nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau, true);
         });
         __syncthreads();
 
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_tn_blk<PBk::BR, C>(accP[pb], sm.K + 16 * ti0, LDD, sm.V + 16 * tv0, LDV);
-            mma_tn_blk<PBk::BR, C>(accE[pb], sm.K + 16 * ti0, LDD, sm.Y + 16 * tv0, LDV);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], sm.K, 16 * ti0, sm.V, 16 * tv0);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], sm.K, 16 * ti0, sm.Y, 16 * tv0);
         });
         for_blocks<MBk, NW>(w, [&](int pb, int ti0, int tj0) {
-            mma_tn_blk<MBk::BR, C>(accM[pb], sm.K + 16 * ti0, LDD, sm.Q + 16 * tj0, LDD);
+            mma_tn_grp<MBk::BR, MBk::BR, C, TK, TK, false>(&accM[pb][0][0], sm.K, 16 * ti0, sm.Q, 16 * tj0);
         });
         for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-            accMK[j] = mma_tn_tile<C>(accMK[j], sm.K + 16 * ti, LDD, sm.V + DV, LDV);
-            accNK[j] = mma_tn_tile<C>(accNK[j], sm.K + 16 * ti, LDD, sm.Y + DV, LDV);
+            mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], sm.K, 16 * ti, sm.V, 0);
+            mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], sm.K, 16 * ti, sm.Y1, 0);
         });
         // the running widened P's T-typed copy after every product of the chunk
         for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-            store4(sm.Pt + (16 * tv + col) * LDD + 16 * ti + g4, accP[pb][x][y]);
+            store4(sm.Pt + TK::off(16 * tv + col, 16 * ti + g4), accP[pb][x][y]);
         });
         for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-            store4(sm.Pt + (DV + col) * LDD + 16 * ti + g4, accMK[j]);
+            store4(sm.Pt + TK::off(DV + col, 16 * ti + g4), accMK[j]);
         });
         c0 = n0;
         cv = ncv;
