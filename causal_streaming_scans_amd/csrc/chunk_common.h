@@ -77,14 +77,6 @@ struct ChunkRegs {
         *reinterpret_cast<uint4 *>(x.v) = z;
         return x;
     }
-    // dst[r][c] (row-major, leading dim ld)
-    __device__ __forceinline__ void store_rows(T *dst, int ld) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) store16(dst + (idx / VPR) * ld + (idx % VPR) * VE, get(i));
-        }
-    }
     // the same into an LdsTile matrix
     template <typename TL>
     __device__ __forceinline__ void store_tile(T *dst) const {
@@ -109,61 +101,9 @@ struct ChunkRegs {
             }
         }
     }
-    // dst[r][c] = src[r][c] * w, w = gp[wofs - r] for r <= wofs, else 0
-    __device__ __forceinline__ void store_rows_w(T *dst, int ld, const float *gp, int wofs) const {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
-            if (idx < NVEC) {
-                const int r = idx / VPR;
-                const float wr = r <= wofs ? gp[wofs - r] : 0.f;
-                Vec16<T> x = get(i);
-#pragma unroll
-                for (int e = 0; e < VE; ++e) x.v[e] = from_f<T>(to_f(x.v[e]) * wr);
-                store16(dst + r * ld + (idx % VPR) * VE, x);
-            }
-        }
-    }
 };
 
-// Sum of the first C entries of row i of a [*][ld] LDS matrix (vector reads).
-template <typename T, int C>
-__device__ __forceinline__ float row_sum(const T *m, int ld, int i) {
-    constexpr int VE = Vec16<T>::N;
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; c += VE) {
-        const Vec16<T> x = load16(m + i * ld + c);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) s += to_f(x.v[e]);
-    }
-    return s;
-}
 
-// sum_c m[i][c] * w[c] over the first C columns
-template <typename T, int C>
-__device__ __forceinline__ float row_dot(const T *m, int ld, int i, const float *w) {
-    constexpr int VE = Vec16<T>::N;
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; c += VE) {
-        const Vec16<T> x = load16(m + i * ld + c);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) s += to_f(x.v[e]) * w[c + e];
-    }
-    return s;
-}
 
-// q_tau . vec for the lane's token: each lane group takes a quarter of D,
-// then the groups are summed.  Qrow points at Q[tau][0].
-template <typename T, int D>
-__device__ __forceinline__ float lane_dot(const T *Qrow, const float *vec) {
-    constexpr int Q4 = D / 4;
-    const int g = lane_id() >> 4;
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < Q4; ++k) s += to_f(Qrow[g * Q4 + k]) * vec[g * Q4 + k];
-    return sum_groups(s);
-}
 
 }  // namespace hla

@@ -69,52 +69,16 @@ struct PadTile {
     __device__ static __forceinline__ int off(int r, int c) { return r * LD + c; }
 };
 
-// ---------------------------------------------------------------- MFMA tiles
-
-// acc += A[0:16][kbeg:kend] * Bt[0:16][kbeg:kend]^T, k range a multiple of 16.
-// One instruction shape per call: 16x16x32 when the range is a multiple of
+// ------------------------------------------ operands kept in registers
+//
+// MFMA shapes: a product over k uses 16x16x32 steps when k is a multiple of
 // 32, else 16x16x16 throughout.  An accumulation chain never switches MFMA
 // shape -- on gfx950 a 16x16x16 that takes a 16x16x32 result as its
 // accumulator back to back has been seen to read it before it is final.
-__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const bf16 *A, int lda, const bf16 *Bt,
-                                        int ldb, int kbeg, int kend) {
-    const int l = lane_id();
-    const int r = l & 15, g = l >> 4;
-    const bf16 *a = A + r * lda;
-    const bf16 *b = Bt + r * ldb;
-    if (((kend - kbeg) & 31) == 0) {
-        for (int k = kbeg; k < kend; k += 32) {
-            bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + k + g * 8);
-            bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + k + g * 8);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
-        }
-    } else {
-        for (int k = kbeg; k < kend; k += 16) {
-            i16x4 av = *reinterpret_cast<const i16x4 *>(a + k + g * 4);
-            i16x4 bv = *reinterpret_cast<const i16x4 *>(b + k + g * 4);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
-        }
-    }
-    return acc;
-}
 
-// fp32 operands: exact fp32 products, fp32 accumulation.  k range multiple of 4.
-__device__ __forceinline__ f32x4 mma_nt(f32x4 acc, const float *A, int lda, const float *Bt,
-                                        int ldb, int kbeg, int kend) {
-    const int l = lane_id();
-    const int r = l & 15, g = l >> 4;
-    const float *a = A + r * lda + g;
-    const float *b = Bt + r * ldb + g;
-    for (int k = kbeg; k < kend; k += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k], b[k], acc, 0, 0, 0);
-    return acc;
-}
-
-// ------------------------------------------ operands kept in registers
-
-// MFMA operand fragments of one 16-row tile over k = 0..K, loaded from LDS
-// once and reused: lane l holds row l%16 at the k offsets both operand
-// slots of mma_nt use (A and Bt fragments are addressed alike).
+// MFMA operand fragments of one 16-row tile over k = 0..K, loaded once and
+// reused: lane l holds row l%16 at the k offsets both operand slots use (A
+// and Bt fragments are addressed alike).
 template <typename T, int K> struct RowFrags;
 //
 // load_rows_g reads the 16 rows straight from global memory: lane l reads
@@ -150,18 +114,7 @@ template <int K> struct RowFrags<bf16, K> {
             }
         }
     }
-    __device__ __forceinline__ void load(const bf16 *base, int ld) {
-        const int l = lane_id(), r = l & 15, g = l >> 4;
-        if constexpr (W32) {
-#pragma unroll
-            for (int s = 0; s < K / 32; ++s)
-                v8[s] = *reinterpret_cast<const bf16x8 *>(base + r * ld + 32 * s + 8 * g);
-        } else {
-#pragma unroll
-            for (int s = 0; s < K / 16; ++s)
-                v4[s] = *reinterpret_cast<const i16x4 *>(base + r * ld + 16 * s + 4 * g);
-        }
-    }    // the 16-row block of an LdsTile matrix that starts at base
+    // the 16-row block of an LdsTile matrix that starts at base
     template <typename TL>
     __device__ __forceinline__ void load_t(const bf16 *base) {
         const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -191,11 +144,7 @@ template <int K> struct RowFrags<float, K> {
             for (int s = 0; s < K / 4; ++s) v[s] = 0.f;
         }
     }
-    __device__ __forceinline__ void load(const float *base, int ld) {
-        const int l = lane_id(), r = l & 15, g = l >> 4;
-#pragma unroll
-        for (int s = 0; s < K / 4; ++s) v[s] = base[r * ld + 4 * s + g];
-    }    template <typename TL>
+    template <typename TL>
     __device__ __forceinline__ void load_t(const float *base) {
         const int l = lane_id(), r = l & 15, g = l >> 4;
 #pragma unroll
@@ -203,36 +152,8 @@ template <int K> struct RowFrags<float, K> {
     }
 };
 
-// acc += A[0:16][0:K] * F^T with A in LDS and F preloaded (F as the Bt side)
-template <int K>
-__device__ __forceinline__ f32x4 mma_nt_f(f32x4 acc, const bf16 *A, int lda,
-                                          const RowFrags<bf16, K> &f) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-    if constexpr (RowFrags<bf16, K>::W32) {
-#pragma unroll
-        for (int s = 0; s < K / 32; ++s) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(A + r * lda + 32 * s + 8 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, f.v8[s], acc, 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < K / 16; ++s) {
-            const i16x4 av = *reinterpret_cast<const i16x4 *>(A + r * lda + 16 * s + 4 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, f.v4[s], acc, 0, 0, 0);
-        }
-    }
-    return acc;
-}
-template <int K>
-__device__ __forceinline__ f32x4 mma_nt_f(f32x4 acc, const float *A, int lda,
-                                          const RowFrags<float, K> &f) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-#pragma unroll
-    for (int s = 0; s < K / 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + 4 * s + g], f.v[s], acc, 0, 0, 0);
-    return acc;
-}
-// mma_nt_f with A the 16-row block of an LdsTile matrix that starts at A
+// acc += A[0:16][0:K] * F^T with A the 16-row block of an LdsTile matrix
+// that starts at A and F preloaded (F as the Bt side)
 template <typename TL, int K>
 __device__ __forceinline__ f32x4 mma_nt_ft(f32x4 acc, const bf16 *A, const RowFrags<bf16, K> &f) {
     const int l = lane_id(), r = l & 15, g = l >> 4;
@@ -259,93 +180,7 @@ __device__ __forceinline__ f32x4 mma_nt_ft(f32x4 acc, const float *A, const RowF
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[TL::off(r, 4 * s + g)], f.v[s], acc, 0, 0, 0);
     return acc;
 }
-// acc += F * Bt[0:16][0:K]^T with F preloaded (F as the A side)
-template <int K>
-__device__ __forceinline__ f32x4 mma_nt_fa(f32x4 acc, const RowFrags<bf16, K> &f,
-                                           const bf16 *Bt, int ldb) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-    if constexpr (RowFrags<bf16, K>::W32) {
-#pragma unroll
-        for (int s = 0; s < K / 32; ++s) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(Bt + r * ldb + 32 * s + 8 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.v8[s], bv, acc, 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < K / 16; ++s) {
-            const i16x4 bv = *reinterpret_cast<const i16x4 *>(Bt + r * ldb + 16 * s + 4 * g);
-            acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(f.v4[s], bv, acc, 0, 0, 0);
-        }
-    }
-    return acc;
-}
-template <int K>
-__device__ __forceinline__ f32x4 mma_nt_fa(f32x4 acc, const RowFrags<float, K> &f,
-                                           const float *Bt, int ldb) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-#pragma unroll
-    for (int s = 0; s < K / 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f.v[s], Bt[r * ldb + 4 * s + g], acc, 0, 0, 0);
-    return acc;
-}
 
-// A BR x BR block of 16x16 tiles: acc[x][y] += A[16x..][0:K] * Bt[16y..][0:K]^T,
-// each operand row loaded once per k step (halves LDS reads at BR = 2).
-template <int BR, int K>
-__device__ __forceinline__ void mma_nt_blk(f32x4 (&acc)[BR][BR], const bf16 *A, int lda,
-                                           const bf16 *Bt, int ldb) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-    if constexpr (K % 32 == 0) {
-#pragma unroll
-        for (int k = 0; k < K; k += 32) {
-            bf16x8 a[BR], b[BR];
-#pragma unroll
-            for (int x = 0; x < BR; ++x) {
-                a[x] = *reinterpret_cast<const bf16x8 *>(A + (16 * x + r) * lda + k + 8 * g);
-                b[x] = *reinterpret_cast<const bf16x8 *>(Bt + (16 * x + r) * ldb + k + 8 * g);
-            }
-#pragma unroll
-            for (int x = 0; x < BR; ++x)
-#pragma unroll
-                for (int y = 0; y < BR; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < K; k += 16) {
-            i16x4 a[BR], b[BR];
-#pragma unroll
-            for (int x = 0; x < BR; ++x) {
-                a[x] = *reinterpret_cast<const i16x4 *>(A + (16 * x + r) * lda + k + 4 * g);
-                b[x] = *reinterpret_cast<const i16x4 *>(Bt + (16 * x + r) * ldb + k + 4 * g);
-            }
-#pragma unroll
-            for (int x = 0; x < BR; ++x)
-#pragma unroll
-                for (int y = 0; y < BR; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[x], b[y], acc[x][y], 0, 0, 0);
-        }
-    }
-}
-template <int BR, int K>
-__device__ __forceinline__ void mma_nt_blk(f32x4 (&acc)[BR][BR], const float *A, int lda,
-                                           const float *Bt, int ldb) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-#pragma unroll 4
-    for (int k = 0; k < K; k += 4) {
-        float a[BR], b[BR];
-#pragma unroll
-        for (int x = 0; x < BR; ++x) {
-            a[x] = A[(16 * x + r) * lda + k + g];
-            b[x] = Bt[(16 * x + r) * ldb + k + g];
-        }
-#pragma unroll
-        for (int x = 0; x < BR; ++x)
-#pragma unroll
-            for (int y = 0; y < BR; ++y)
-                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
-    }
-}
 
 // Ownership of the tiles of an (nTR x nTC)-tile matrix by NW waves, in
 // BR x BR blocks (BR = 2 when that still gives every wave a block).
@@ -368,7 +203,7 @@ struct TileBlocks {
 // V_MFMA_F32_16X16X4_F32, instruction m pairing slot m of every lane group
 // (k = 4g + m) on both sides.  A chain of mma16 steps starts from its own
 // zero accumulator and is added to any 16x16x32 partial sum with VALU adds
-// (see mma_nt).
+// (see the note on MFMA shapes above).
 template <typename T> struct Frag16;
 template <> struct Frag16<bf16> { i16x4 v; };
 template <> struct Frag16<float> { f32x4 v; };
@@ -426,33 +261,11 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const bf16 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(const_cast<bf16 *>(p)));
 }
 
-// Operand fragment of rows m0..m0+15, k = k0..k0+15 of M[k][m]; M points at
-// M[k0][m0].  Lane l gets M[k0 + 4g + e][m0 + l%16] in slot e.
-__device__ __forceinline__ Frag16<bf16> ld_frag_t(const bf16 *M, int ld) {
-    const int l = lane_id(), g = l >> 4, s = l & 15;
-    return Frag16<bf16>{ds_read_tr16(M + (4 * g + (s >> 2)) * ld + 4 * (s & 3))};
-}
-__device__ __forceinline__ Frag16<float> ld_frag_t(const float *M, int ld) {
-    const int l = lane_id(), g = l >> 4, c = l & 15;
-    f32x4 v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = M[(4 * g + i) * ld + c];
-    return Frag16<float>{v};
-}
-
-// 16x16x32 operand from M[k][m]: slot j holds k = k0 + 8g + j (the slot
-// order of a contiguous 16-byte load, so it pairs with either kind).
-__device__ __forceinline__ bf16x8 ld_op8_t(const bf16 *M, int ld) {
-    const int l = lane_id(), g = l >> 4, s = l & 15;
-    const bf16 *p = M + (8 * g + (s >> 2)) * ld + 4 * (s & 3);
-    const i16x4 lo = ds_read_tr16(p), hi = ds_read_tr16(p + 4 * ld);
-    const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, both);
-}
-
-// The same operand reads from an LdsTile matrix M (its base), for the
-// sub-tile whose first row (k) is row0 and first column col0, both multiples
-// of 16.
+// Operand fragments from an LdsTile matrix M (its base) for the sub-tile whose
+// first row (k) is row0 and first column col0, both multiples of 16: the
+// 16-deep fragment (ld_frag_tt: slot e holds k = row0 + 4g + e) and the
+// 32-deep operand of a 16x16x32 step (ld_op8_tt: slot j holds k = row0 + 8g
+// + j, two transposing reads four rows apart).
 template <typename TL>
 __device__ __forceinline__ Frag16<bf16> ld_frag_tt(const bf16 *M, int row0, int col0) {
     const int l = lane_id(), g = l >> 4, s = l & 15;
@@ -492,62 +305,6 @@ __device__ __forceinline__ bf16x8 ones_op8() {
     return __builtin_bit_cast(bf16x8, i16x8{one, one, one, one, one, one, one, one});
 }
 
-// A BR x BR block of 16x16 tiles contracting over the rows of two k-major
-// LDS matrices: acc[x][y] += sum_k A[k][16x + i] * B[k][16y + j], k = 0..K.
-template <int BR, int K>
-__device__ __forceinline__ void mma_tn_blk(f32x4 (&acc)[BR][BR], const bf16 *A, int lda,
-                                           const bf16 *B, int ldb) {
-    if constexpr (K % 32 == 0) {
-#pragma unroll
-        for (int k = 0; k < K; k += 32) {
-            bf16x8 a[BR], b[BR];
-#pragma unroll
-            for (int x = 0; x < BR; ++x) {
-                a[x] = ld_op8_t(A + k * lda + 16 * x, lda);
-                b[x] = ld_op8_t(B + k * ldb + 16 * x, ldb);
-            }
-#pragma unroll
-            for (int x = 0; x < BR; ++x)
-#pragma unroll
-                for (int y = 0; y < BR; ++y)
-                    acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < K; k += 16) {
-            Frag16<bf16> a[BR], b[BR];
-#pragma unroll
-            for (int x = 0; x < BR; ++x) {
-                a[x] = ld_frag_t(A + k * lda + 16 * x, lda);
-                b[x] = ld_frag_t(B + k * ldb + 16 * x, ldb);
-            }
-#pragma unroll
-            for (int x = 0; x < BR; ++x)
-#pragma unroll
-                for (int y = 0; y < BR; ++y) acc[x][y] = mma16(acc[x][y], a[x], b[y]);
-        }
-    }
-}
-template <int BR, int K>
-__device__ __forceinline__ void mma_tn_blk(f32x4 (&acc)[BR][BR], const float *A, int lda,
-                                           const float *B, int ldb) {
-    const int l = lane_id(), r = l & 15, g = l >> 4;
-#pragma unroll 4
-    for (int k = 0; k < K; k += 4) {
-        float a[BR], b[BR];
-#pragma unroll
-        for (int x = 0; x < BR; ++x) {
-            a[x] = A[(k + g) * lda + 16 * x + r];
-            b[x] = B[(k + g) * ldb + 16 * x + r];
-        }
-#pragma unroll
-        for (int x = 0; x < BR; ++x)
-#pragma unroll
-            for (int y = 0; y < BR; ++y)
-                acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
-    }
-}
-
 // Store four consecutive T values (one accumulator's slots, converted).
 __device__ __forceinline__ void store4(bf16 *p, f32x4 a) {
     union { bf16 h[4]; uint2 v; } u;
@@ -556,21 +313,6 @@ __device__ __forceinline__ void store4(bf16 *p, f32x4 a) {
     *reinterpret_cast<uint2 *>(p) = u.v;
 }
 __device__ __forceinline__ void store4(float *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
-
-// Sum over the 16 lanes of each lane group (same g, all c).
-__device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
-    return x;
-}
-// Sum over the 4 lane groups (same c, all g).
-__device__ __forceinline__ float sum_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
-}
 
 // Row / column of accumulator element r held by this lane within its tile.
 __device__ __forceinline__ int acc_row(int r) { return ((lane_id() >> 4) << 2) + r; }

@@ -113,13 +113,6 @@ __device__ __forceinline__ void for_stripe(int w, F f) {
     }
 }
 
-// acc += A^T B over the C token rows for one 16x16 tile (k-major operands)
-template <int C, typename T>
-__device__ __forceinline__ f32x4 mma_tn_tile(f32x4 acc, const T *A, int lda, const T *B, int ldb) {
-    f32x4 a[1][1] = {{acc}};
-    mma_tn_blk<1, C>(a, A, lda, B, ldb);
-    return a[0][0];
-}
 
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2FwdSmem {
