@@ -85,29 +85,33 @@ def test_support_matrix(case):
     assert err < TOL[dtype]
 
 
+@pytest.mark.parametrize("shape", [(32, 32, 2, 3), (64, 64, 2, 1)], ids=["d32c32", "d64c64"])
 @pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_state_out_and_resume(variant, dtype):
+def test_state_out_and_resume(variant, dtype, shape):
     """forward(n1) -> state_out -> forward(n2, state_in) equals forward(n1+n2),
-    and state_out equals the oracle's state."""
-    say(f"[resume] {variant} {dtype}")
-    B, H, n1, n2, d = 1, 2, 230, 181, 32
+    and state_out equals the oracle's state.  d = chunk = 64 runs the kernels'
+    per-row-tile state layout; its second call has three segments, so the
+    caller's state is folded with the up-sweep nodes' cross terms."""
+    d, chunk, seg1, seg2 = shape
+    say(f"[resume] {variant} {dtype} d={d} chunk={chunk}")
+    B, H, n1, n2 = 1, 2, 230, 181
     dist = "uniform_pos" if variant.endswith("ratio") else "normal_scaled"
     decay = variant.startswith("hla2")
-    x = _inputs(B, H, n1 + n2, d, dtype, dist, seed=77, decay=decay)
+    x = _inputs(B, H, n1 + n2, d, dtype, dist, seed=77 + d, decay=decay)
     g = x["gamma"]
     x1 = {kk: x[kk][:, :n1] for kk in ("q", "k", "v")}
     x2 = {kk: x[kk][:, n1:] for kk in ("q", "k", "v")}
-    o1, st = gpu_forward(x1, variant, B, H, dtype, 32, 2, gamma=g, want_state=True)
+    o1, st = gpu_forward(x1, variant, B, H, dtype, chunk, seg1, gamma=g, want_state=True)
     w1, wst = oracle_forward(x1, variant, H, gamma=g, want_state=True)
     assert rel_l2(st, wst) < 10 * TOL[dtype]
-    o2 = gpu_forward(x2, variant, B, H, dtype, 32, 3, gamma=g, state_in=st)
+    o2 = gpu_forward(x2, variant, B, H, dtype, chunk, seg2, gamma=g, state_in=st)
     whole = oracle_forward(x, variant, H, gamma=g)
     err = rel_l2(np.concatenate([o1, o2], axis=1), whole)
     say(f"   rel_l2 {err:.3e}")
     assert err < TOL[dtype]
     # one segment path (no scan) from the same state
-    o2b = gpu_forward(x2, variant, B, H, dtype, 32, 1000, gamma=g, state_in=st)
+    o2b = gpu_forward(x2, variant, B, H, dtype, chunk, 1000, gamma=g, state_in=st)
     assert rel_l2(np.concatenate([o1, o2b], axis=1), whole) < TOL[dtype]
 
 

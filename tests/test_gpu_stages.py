@@ -57,6 +57,8 @@ def _nodes(nreal):
 @pytest.mark.parametrize("dtype,variant,d,chunk,seg,decay", [
     ("f32", "hla2", 32, 16, 2, False),
     ("bf16", "hla2", 64, 64, 1, False),
+    ("bf16", "hla2", 64, 64, 2, True),
+    ("f32", "hla2", 64, 64, 2, True),
     ("bf16", "hla2", 64, 32, 2, False),
     ("bf16", "hla2", 64, 16, 4, True),
     ("bf16", "hla2", 128, 32, 2, True),
