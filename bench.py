@@ -11,13 +11,22 @@ to stderr.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 
-Timing: K steps between two synchronisations, one library call per step,
+Timing: first untimed steps for at least --settle-ms (300 ms: the GPU's
+clocks ramp over the first few hundred ms of load, and steps timed before
+that run up to 15% slower), then W warm-up steps; then
+K steps between two synchronisations, one library call per step,
 with HIP events only at the two ends, on the stream the library launches on
 (torch's current stream): that gives ms_per_step and the throughput.  A
 second pass of K steps brackets every stage with events on the same stream,
-which splits the time per kernel for the roofline figure (the markers add
-small gaps, so that pass is not the throughput).  The CPU baseline is the
-fp64 oracle on the same inputs (all heads), on the host's cores.
+which splits the step by stage (the markers add small gaps, so that pass is
+not the throughput).  A third pass launches each stage K times back to back
+between two events: the per-kernel times, which the roofline figure uses.  Then: K steps with an
+event between consecutive steps (median, p10, p90 per step); K cold steps,
+each after a 1 GiB buffer (more than the Infinity Cache) has been written;
+and K replays of the step captured in a HIP graph.  Decode is timed as the
+mean over 1024 plain calls and over replays of 64 captured steps (a spread
+per call would time the host: a 3.5 us step is shorter than one submission).  The CPU baseline is the fp64
+oracle on the same inputs (all heads), on the host's cores.
 """
 from __future__ import annotations
 
@@ -68,6 +77,35 @@ def stored_traffic(kernel: str):
     return ent.get("hbm_bytes_per_launch")
 
 
+def trace_summary(trace_csv: str, bench_json: str) -> None:
+    """Per-pass kernel durations from a rocprofv3 kernel trace of one bench.py
+    run (`--kernel-trace`, csv) and that run's JSON line: each stage kernel's
+    dispatches in launch order, past the settle and warm-up steps, split into
+    the timed pass, the stage pass and the back-to-back pass (K each)."""
+    import csv
+    import statistics
+    with open(bench_json) as fh:
+        rec = json.loads(fh.read().strip().splitlines()[-1])
+    skip, K = rec["settle"]["steps"] + rec["warmup"], rec["steps"]
+    with open(trace_csv) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    for r in rows:
+        per.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"settle + warm-up steps skipped: {skip}; K = {K}")
+    for name, us in per.items():
+        if not any(x in name for x in ("summary_kernel", "up_sweep_kernel", "forward_kernel")):
+            continue
+        parts = {"timed": us[skip:skip + K], "stages": us[skip + K:skip + 2 * K],
+                 "back-to-back": us[skip + 2 * K:skip + 3 * K]}
+        print(name)
+        for label, v in parts.items():
+            if v:
+                print(f"    {label:13s} n={len(v):5d} avg {statistics.fmean(v):8.2f} us"
+                      f"  min {min(v):8.2f}  max {max(v):8.2f}")
+
+
 def flops_per_token(c, d, dv):
     # dense products of the chunked method per token: scores 2cd, Q S0 2d^2,
     # L K 2cd, Q Z^T 2cd, P V 2c dv, Q W0 2d dv, S update 2d^2, W update 2d dv
@@ -77,19 +115,28 @@ def flops_per_token(c, d, dv):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps for at least this long before the warm-up steps, so "
+                         "the GPU is at its steady clocks when timing starts")
     ap.add_argument("--chunk", type=int, default=64)
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle over the workload until this much wall time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the workload, run a plain elementwise copy (torch.neg) of "
                          "this many MiB in and out, whose HBM counters scale the kernel's")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
+                    help="print per-pass kernel durations from a rocprofv3 kernel trace of a "
+                         "bench.py run and that run's JSON line, then exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
     if args.print_source_hash:
         print(kernel_source_hash())
         return
@@ -141,6 +188,19 @@ def main():
     def step():
         plan.run()
 
+    # ---- settle: untimed steps until the GPU has run them for settle_ms (its
+    # clocks ramp over the first few hundred ms of load), then W warm-up steps
+    settle_steps, settle_ms = 0, 0.0
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while settle_ms < args.settle_ms and settle_steps < 100000:
+        e_a.record()
+        for _ in range(100):
+            step()
+        e_b.record()
+        torch.cuda.synchronize()
+        settle_ms += e_a.elapsed_time(e_b)
+        settle_steps += 100
+    log(f"[bench] settle: {settle_steps} untimed steps, {settle_ms:.0f} ms")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -170,10 +230,78 @@ def main():
     torch.cuda.synchronize()
     stage_ms = [float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(K)]))
                 for i in range(3)]
+    # ---- per-kernel time: each stage launched K times back to back between two
+    # events (each stage is idempotent given the previous one's output), so no
+    # dependency gap of the step sits inside the figure
+    kern_ms = []
+    for stage in (1, 2, 3):
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(K):
+            plan.stage(stage)
+        t_end.record()
+        torch.cuda.synchronize()
+        kern_ms.append(t_start.elapsed_time(t_end) / K)
     tokens = B * H * n
     tok_s = tokens / (ms_per_step * 1e-3)
     log(f"[bench] {ms_per_step:.4f} ms/step, {tok_s / 1e9:.3f} G tokens/s; stages (ms) "
-        f"summary {stage_ms[0]:.4f} up-sweep {stage_ms[1]:.4f} forward {stage_ms[2]:.4f}")
+        f"summary {stage_ms[0]:.4f} up-sweep {stage_ms[1]:.4f} forward {stage_ms[2]:.4f}; "
+        f"back-to-back launches (ms) {kern_ms[0]:.4f} {kern_ms[1]:.4f} {kern_ms[2]:.4f}")
+
+    def pct(a):
+        a = np.asarray(a, np.float64)
+        return {"median_ms": round(float(np.median(a)), 5), "p10_ms": round(float(np.percentile(a, 10)), 5),
+                "p90_ms": round(float(np.percentile(a, 90)), 5)}
+
+    # ---- per-step spread: K more steps with an event between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for s in range(K):
+        step()
+        evs[s + 1].record()
+    torch.cuda.synchronize()
+    warm = pct([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
+
+    # ---- cold steps: a 1 GiB buffer (more than the 256 MB Infinity Cache) is
+    # written before each step, outside the step's own events
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        scrub.fill_(s & 0xFF)
+        evc[s][0].record()
+        step()
+        evc[s][1].record()
+    torch.cuda.synchronize()
+    cold = pct([a.elapsed_time(b) for a, b in evc])
+    del scrub
+    log(f"[bench] per step: warm median {warm['median_ms']:.4f} ms, cold median "
+        f"{cold['median_ms']:.4f} ms")
+
+    # ---- the same step captured once in a HIP graph and replayed K times
+    gstream = torch.cuda.Stream()
+    gplan = hla.ForwardPlan(q, k, v, variant=variant, chunk=chunk, seg_chunks=seg, out=o,
+                            workspace=ws, staged=True, stream=gstream)
+    graph = torch.cuda.CUDAGraph()
+    gstream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gstream):
+        gplan.run()
+    torch.cuda.current_stream().wait_stream(gstream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gstream):
+        gplan.run()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(K):
+        graph.replay()
+    t_end.record()
+    torch.cuda.synchronize()
+    graph_ms = t_start.elapsed_time(t_end) / K
+    log(f"[bench] graph replay: {graph_ms:.4f} ms/step")
 
     # ---- spot parity of the benchmarked output on two heads
     import oracle
@@ -185,7 +313,7 @@ def main():
 
     # ---- roofline of the dominant kernel (largest measured stage)
     names = ["hla2_summary_kernel", "up_sweep_kernel", "hla2_forward_kernel"]
-    dom = int(np.argmax(stage_ms))
+    dom = int(np.argmax(kern_ms))
     esz = 2  # bf16
     per_token_bytes = (2 * d + 2 * dv) * esz          # q, k, v in, o out
     sumf = d * d + 2 * d * dv + 2 * d
@@ -197,15 +325,15 @@ def main():
     else:   # each up-sweep combine reads two summaries and writes one
         ncomb = sum(max(0, (nseg - 1) >> b) for b in range(1, 32))
         alg_bytes = B * H * ncomb * 3 * sumf * 4
-    achieved = alg_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms[dom] * 1e-3) / 1e9
     traffic = stored_traffic(names[dom])
     fl_tok = flops_per_token(chunk, d, dv)
-    mfma_tflops_fwd = tokens * fl_tok / (stage_ms[2] * 1e-3) / 1e12
+    mfma_tflops_fwd = tokens * fl_tok / (kern_ms[2] * 1e-3) / 1e12
     mfma_tflops_step = tokens * fl_tok / (ms_per_step * 1e-3) / 1e12
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": names[dom],
-                "kernel_ms": round(stage_ms[dom], 5), "alg_bytes_per_launch": int(alg_bytes)}
+                "kernel_ms": round(kern_ms[dom], 5), "alg_bytes_per_launch": int(alg_bytes)}
 
     # ---- decode step (one token per head, AHLA state of 32 heads, d = 64)
     decode = None
@@ -229,12 +357,34 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        # the same steps captured in a HIP graph (64 steps per replay)
+        per_graph = 64
+        gsp = hla.StepPlan(qd, kd, vd, state, variant="ahla", out=od, stream=gstream)
+        dgraph = torch.cuda.CUDAGraph()
+        gstream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gstream):
+            gsp.run()
+        torch.cuda.current_stream().wait_stream(gstream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(dgraph, stream=gstream):
+            for _ in range(per_graph):
+                gsp.run()
+        dgraph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.decode_steps // per_graph)
+        e0.record()
+        for _ in range(reps):
+            dgraph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us_graph = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
         st_bytes = 2 * BHd * stf * 4 + BHd * (2 * dw.d + 2 * dw.dv) * 2
         decode = {"workload": "AHLA decode step, B=1 H=32 d=dv=64 bf16, fp32 state",
                   "us_per_step": round(us, 3), "tokens_per_s": round(BHd / (us * 1e-6), 1),
+                  "us_per_step_graph": round(us_graph, 3),
                   "state_bytes_per_step": st_bytes,
                   "achieved_GBs": round(st_bytes / (us * 1e-6) / 1e9, 2)}
-        log(f"[bench] decode: {us:.2f} us/step")
+        log(f"[bench] decode: {us:.2f} us/step, {us_graph:.2f} us/step under graph replay")
 
     # ---- CPU baseline: the oracle on the same inputs, all heads
     cpu = None
@@ -257,6 +407,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1)},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "variant": variant, "B": B, "H": H, "n": n, "d": d,
@@ -270,6 +421,11 @@ def main():
                  "whole_step_frac": round(mfma_tflops_step / BF16_MFMA_PEAK_TFLOPS, 4)},
         "stages_ms": {"summary": round(stage_ms[0], 5), "up_sweep": round(stage_ms[1], 5),
                       "prefix_and_forward": round(stage_ms[2], 5)},
+        "kernel_ms": {"summary": round(kern_ms[0], 5), "up_sweep": round(kern_ms[1], 5),
+                      "prefix_and_forward": round(kern_ms[2], 5)},
+        "per_step_warm": warm,
+        "per_step_cold": cold,
+        "graph_ms_per_step": round(graph_ms, 5),
         "parity_spot_rel_l2": rel,
         "decode": decode,
         "cpu_baseline": cpu,
