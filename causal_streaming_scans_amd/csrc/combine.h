@@ -216,17 +216,33 @@ __device__ void combine_slice(const float *eA, const float *eB, float *eD, float
     if (first && threadIdx.x < D) eD[O::y + threadIdx.x] = lin * vya + vyb;
 }
 
-// One level of the up-sweep of the exclusive Blelloch scan: workgroup
-// (m * CS + cs, bh) forms column slice cs of node (b+1, m) of head bh from
-// its children (b, 2m) and (b, 2m+1).  The host launches the levels in
-// order, one launch each, over the nodes that end below nreal (a node ending
-// at or past it would only feed prefixes no segment needs).
+// Workgroups of one up-sweep level: the CS column slices of a combine are
+// 8 workgroup ids apart, so they run on one XCD (ids are dealt to the XCDs
+// in turn) and the left factor they all read is fetched into its L2 once.
+// Combine c = bh * npair + m; ids past the last combine exit at once.
+template <int CS>
+__host__ __device__ inline int up_sweep_groups(int ncomb) { return ((ncomb + 7) / 8) * 8 * CS; }
+template <int CS>
+__device__ inline void up_sweep_slot(int id, int *comb, int *cs) {
+    *comb = (id / (8 * CS)) * 8 + id % 8;
+    *cs = (id / 8) % CS;
+}
+
+// One level of the up-sweep of the exclusive Blelloch scan: a workgroup forms
+// column slice cs of node (b+1, m) of head bh from its children (b, 2m) and
+// (b, 2m+1).  The host launches the levels in order, one launch each, over
+// the nodes that end below nreal (a node ending at or past it would only feed
+// prefixes no segment needs).
 template <bool HLA2, int D, int DV, int NT>
 __global__ __launch_bounds__(NT) void up_sweep_kernel(FwdParams p, int b) {
     constexpr int SUMF = summary_floats(D, DV);
     constexpr int CS = combine_slices<DV>();
     __shared__ alignas(16) float lds[CrossLds<D, DV / CS>::FLOATS];
-    const int m = blockIdx.x / CS, cs = blockIdx.x % CS, bh = blockIdx.y;
+    const int npair = p.nreal >> (b + 1);
+    int comb, cs;
+    up_sweep_slot<CS>(blockIdx.x, &comb, &cs);
+    if (comb >= npair * p.BH) return;
+    const int bh = comb / npair, m = comb - bh * npair;
     const float g = HLA2 ? p.gamma[bh % p.H] : 1.f;
     const float a = HLA2 ? pow_int(g, (long)p.seg_len << b) : 1.f;   // g^(tokens of a child)
     combine_slice<HLA2, D, DV, NT, CS>(p.ws + node_offset(bh, b, 2 * m, p.BH, p.nreal, SUMF),

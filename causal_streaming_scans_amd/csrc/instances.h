@@ -55,8 +55,8 @@ hipError_t launch_up_sweep(const FwdParams &p, hipStream_t s) {
     constexpr int NT = 256, CS = combine_slices<D>();
     for (int b = 0; (p.nreal >> (b + 1)) > 0; ++b) {
         const int npair = p.nreal >> (b + 1);
-        hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(npair * CS, p.BH), dim3(NT), 0, s,
-                           p, b);
+        hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(up_sweep_groups<CS>(npair * p.BH)),
+                           dim3(NT), 0, s, p, b);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

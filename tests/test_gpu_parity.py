@@ -45,6 +45,12 @@ CASES = [
     ("bf16", "ahla_ratio", 1, 2, 517, 64, 64, 2, False, "uniform_pos"),
     ("bf16", "ahla", 1, 2, 300, 128, 32, 2, False, "l2norm"),
     ("bf16", "ahla", 1, 2, 300, 16, 16, 4, False, "l2norm"),
+    # four segments (three summaries, one internal node): the benchmark's layout
+    ("f32", "hla2", 1, 2, 203, 16, 16, 4, True, "normal_scaled"),
+    ("f32", "ahla_ratio", 1, 2, 203, 16, 16, 4, False, "uniform_pos"),
+    ("bf16", "hla2_ratio", 2, 2, 1000, 64, 64, 4, False, "uniform_pos"),
+    ("bf16", "hla2", 1, 3, 1000, 64, 64, 4, True, "l2norm"),
+    ("bf16", "ahla", 1, 2, 1000, 64, 64, 4, False, "l2norm"),
 ]
 
 
@@ -85,14 +91,16 @@ def test_support_matrix(case):
     assert err < TOL[dtype]
 
 
-@pytest.mark.parametrize("shape", [(32, 32, 2, 3), (64, 64, 2, 1)], ids=["d32c32", "d64c64"])
+@pytest.mark.parametrize("shape", [(32, 32, 2, 3), (64, 64, 2, 1), (32, 16, 4, 3)],
+                         ids=["d32c32", "d64c64", "d32c16"])
 @pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_state_out_and_resume(variant, dtype, shape):
     """forward(n1) -> state_out -> forward(n2, state_in) equals forward(n1+n2),
     and state_out equals the oracle's state.  d = chunk = 64 runs the kernels'
     per-row-tile state layout; its second call has three segments, so the
-    caller's state is folded with the up-sweep nodes' cross terms."""
+    caller's state is folded with the up-sweep nodes' cross terms.  At chunk
+    16 both calls have four segments."""
     d, chunk, seg1, seg2 = shape
     say(f"[resume] {variant} {dtype} d={d} chunk={chunk}")
     B, H, n1, n2 = 1, 2, 230, 181
