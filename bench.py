@@ -106,6 +106,54 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
                       f"  min {min(v):8.2f}  max {max(v):8.2f}")
 
 
+def counters_summary(fetch_csv: str, write_csv: str) -> None:
+    """HBM bytes per launch of each stage kernel from two `rocprofv3 --pmc` runs
+    of bench.py with --copy-calibration-mib (FETCH_SIZE, then WRITE_SIZE; csv).
+    Each counter's KiB per dispatch is scaled by what it reads for the torch.neg
+    copy of known size.  Prints the JSON record bench.py reads back."""
+    import csv
+    import re
+    import statistics
+
+    def per_kernel(path, counter):
+        per = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        out = {}
+        for (name, _), val in per.items():
+            out.setdefault(name, []).append(val)
+        return {name: statistics.fmean(v) for name, v in out.items()}
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    neg = [n for n in fetch if "neg" in n]
+    if not neg:
+        raise SystemExit("no torch.neg calibration dispatches in the counter csv")
+    cal_f, cal_w = fetch[neg[0]], write[[n for n in write if "neg" in n][0]]
+    mib = round(cal_w / 1024)            # KiB written by the copy -> its size in MiB
+    fs, ws = mib * 1024 / cal_f, mib * 1024 / cal_w
+    rec = {"source_hash": kernel_source_hash(),
+           "workload": "HLA-2 ratio B=8 H=16 n=4096 d=dv=64 bf16, default launch configuration",
+           "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+           "copy_calibration": {"kernel": f"torch.neg over {mib} MiB bf16 ({mib} MiB read, "
+                                          f"{mib} MiB written)",
+                                "FETCH_SIZE_KiB": round(cal_f, 1), "WRITE_SIZE_KiB": round(cal_w, 1)}}
+    for short in ("summary_kernel", "up_sweep_kernel", "forward_kernel"):
+        names = [n for n in fetch if short in n and n in write]
+        for name in names:
+            key = re.search(r"(?:hla2_|ahla_)?" + short, name).group(0)
+            fb, wb = fetch[name] * 1024 * fs, write[name] * 1024 * ws
+            rec[key] = {"FETCH_SIZE_KiB": round(fetch[name], 1),
+                        "WRITE_SIZE_KiB": round(write[name], 1),
+                        "fetch_bytes": int(fb), "write_bytes": int(wb),
+                        "hbm_bytes_per_launch": int(fb + wb)}
+    print(json.dumps(rec, indent=1))
+
+
 def flops_per_token(c, d, dv):
     # dense products of the chunked method per token: scores 2cd, Q S0 2d^2,
     # L K 2cd, Q Z^T 2cd, P V 2c dv, Q W0 2d dv, S update 2d^2, W update 2d dv
@@ -130,12 +178,18 @@ def main():
                     help="before the workload, run a plain elementwise copy (torch.neg) of "
                          "this many MiB in and out, whose HBM counters scale the kernel's")
     ap.add_argument("--print-source-hash", action="store_true")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM-traffic record from two rocprofv3 --pmc counter csv "
+                         "files of a bench.py run (FETCH_SIZE, then WRITE_SIZE), then exit")
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
                     help="print per-pass kernel durations from a rocprofv3 kernel trace of a "
                          "bench.py run and that run's JSON line, then exit")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(*args.trace_summary)
+        return
+    if args.counters_summary:
+        counters_summary(*args.counters_summary)
         return
     if args.print_source_hash:
         print(kernel_source_hash())
