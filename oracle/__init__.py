@@ -13,6 +13,8 @@ Contents
 ``definition.py``  brute-force masked-matrix definitions (n x n), fp64.
 ``chunk_scan.py``  the chunk-parallel algebra (segment summaries, semidirect
                    combine, exclusive Blelloch scan) written out in fp64 NumPy.
+``backward.py``    gradients (dq, dk, dv) of the masked operators: the chain
+                   rule applied to the n x n matrix form, fp64 NumPy.
 
 Source for every formula: "Resumen Tecnico: Atencion Lineal de Orden Superior
 (HLA)", gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",
