@@ -172,6 +172,9 @@ def main():
     ap.add_argument("--seg-chunks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--backward-steps", type=int, default=200,
+                    help="time this many hla_backward calls (HLA-2 gradients at the benchmark "
+                         "shape); 0 skips the backward leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle over the workload until this much wall time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -440,6 +443,39 @@ def main():
                   "achieved_GBs": round(st_bytes / (us * 1e-6) / 1e9, 2)}
         log(f"[bench] decode: {us:.2f} us/step, {us_graph:.2f} us/step under graph replay")
 
+    # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
+    # unnormalised HLA-2 (the variant the backward supports), q, k L2-normalised
+    # Gaussian rows, v and the upstream gradient ~ N(0, 1), bf16
+    backward = None
+    if args.backward_steps > 0:
+        xb = I.make_inputs(B, H, n, d, dv, dtype="bf16", dist="l2norm", seed=w.seed + 500)
+        gb = I.make_upstream_grad(B * H, n, dv, "bf16", seed=w.seed + 501)
+        qb, kb, vb = (to_dev(xb[key], (B, H, n, d)) for key in ("q", "k", "v"))
+        dob = to_dev(gb, (B, H, n, dv))
+        del xb, gb
+        bplan = hla.BackwardPlan(qb, kb, vb, dob, variant="hla2")
+        for _ in range(10):
+            bplan.run()
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.backward_steps):
+            bplan.run()
+        t_end.record()
+        torch.cuda.synchronize()
+        bms = t_start.elapsed_time(t_end) / args.backward_steps
+        # lean HBM floor: q, k, v, do read once and dq, dk, dv written once
+        b_bytes = tokens * 7 * d * 2
+        backward = {"workload": f"HLA-2 backward (dq, dk, dv), B={B} H={H} n={n} d=dv={d} bf16, "
+                                "q,k L2-normalised Gaussian, v and do ~ N(0,1)",
+                    "passes": "7 chunked linear-attention passes (chunk 64), each a segment-state "
+                              "launch and a main launch",
+                    "seg_chunks": hla.backward_default_seg_chunks(B, H, n),
+                    "ms_per_step": round(bms, 5), "tokens_per_s": round(tokens / (bms * 1e-3), 1),
+                    "lean_bytes_per_step": b_bytes,
+                    "lean_hbm_frac": round(b_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] backward: {bms:.4f} ms/step, {tokens / (bms * 1e-3) / 1e9:.3f} G tokens/s")
+        del qb, kb, vb, dob, bplan
+
     # ---- CPU baseline: the oracle on the same inputs, all heads
     cpu = None
     if not args.no_cpu_baseline:
@@ -482,6 +518,7 @@ def main():
         "graph_ms_per_step": round(graph_ms, 5),
         "parity_spot_rel_l2": rel,
         "decode": decode,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -21,8 +21,8 @@ import ctypes
 import os
 
 __all__ = ["HLAError", "VARIANTS", "load", "library_path", "ForwardPlan", "StepPlan",
-           "hla_forward", "hla_forward_stage",
-           "hla_step",
+           "BackwardPlan", "hla_forward", "hla_forward_stage", "hla_backward",
+           "hla_step", "backward_workspace_bytes", "backward_default_seg_chunks",
            "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,12 @@ def load():
     lib.hla_forward_stage.restype = I
     lib.hla_step.argtypes = [P, P, P, P, I, I, I, I, I, I, FP, P, P]
     lib.hla_step.restype = I
+    lib.hla_backward_default_seg_chunks.argtypes = [I, I, I]
+    lib.hla_backward_default_seg_chunks.restype = I
+    lib.hla_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.hla_backward_workspace_bytes.restype = Z
+    lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, I, P, Z, P]
+    lib.hla_backward.restype = I
     lib.hla_status_str.argtypes = [I]
     lib.hla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -94,6 +100,15 @@ def default_seg_chunks(variant, B, H, n, chunk) -> int:
 
 def workspace_bytes(variant, B, H, n, d, dv, chunk, seg_chunks=0) -> int:
     return int(load().hla_workspace_bytes(_variant(variant), B, H, n, d, dv, chunk, seg_chunks))
+
+
+def backward_default_seg_chunks(B, H, n) -> int:
+    return int(load().hla_backward_default_seg_chunks(B, H, n))
+
+
+def backward_workspace_bytes(variant, B, H, n, d, dv, dtype="bf16", seg_chunks=0) -> int:
+    return int(load().hla_backward_workspace_bytes(_variant(variant), B, H, n, d, dv,
+                                                   _DTYPES[dtype], seg_chunks))
 
 
 def _dtype_code(t) -> int:
@@ -279,3 +294,67 @@ def hla_step(q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):
     """One decode step.  q, k: [B, H, d]; v: [B, H, dv]; state: fp32 device
     tensor with B*H*state_floats elements, updated in place.  Returns o."""
     return StepPlan(q, k, v, state, variant, gamma, out, stream).run()
+
+
+class BackwardPlan:
+    """The arguments of one backward pass (hla_backward), checked and
+    marshalled once; ``run()`` enqueues it as a single library call and
+    returns (dq, dk, dv)."""
+
+    def __init__(self, q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0,
+                 dq=None, dk=None, dv=None, workspace=None, stream=None):
+        import torch
+        lib = load()
+        for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
+            _check_device_tensor(name, t)
+        if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
+            raise HLAError("expected q, k, v, do of one shape [B, H, n, d] (d == dv)")
+        if not (q.dtype == k.dtype == v.dtype == do.dtype):
+            raise HLAError("q, k, v, do must share one dtype")
+        B, H, n, d = q.shape
+        vid = _variant(variant)
+        grads = []
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if t is None:
+                t = torch.empty_like(q)
+            else:
+                _check_device_tensor(name, t)
+                if t.shape != q.shape or t.dtype != q.dtype:
+                    raise HLAError(f"{name} has the wrong shape or dtype")
+            grads.append(t)
+        dtc = _dtype_code(q)
+        need = int(lib.hla_backward_workspace_bytes(vid, B, H, n, d, d, dtc, seg_chunks))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        self.grads = tuple(grads)
+        self._keep = (q, k, v, do, *grads, workspace)
+        self._gamma, g_ptr = _gamma_arg(gamma, H)
+        VP, CI = ctypes.c_void_p, ctypes.c_int
+        self._args = (VP(q.data_ptr()), VP(k.data_ptr()), VP(v.data_ptr()), VP(do.data_ptr()),
+                      VP(grads[0].data_ptr()), VP(grads[1].data_ptr()), VP(grads[2].data_ptr()),
+                      CI(B), CI(H), CI(n), CI(d), CI(d), CI(dtc), CI(vid), g_ptr, CI(seg_chunks),
+                      VP(workspace.data_ptr()),
+                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                      _stream_ptr(stream, q.device))
+        self._dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+        self._lib = lib
+
+    def run(self):
+        import torch
+        if torch.cuda.current_device() == self._dev:
+            rc = self._lib.hla_backward(*self._args)
+        else:
+            with torch.cuda.device(self._dev):
+                rc = self._lib.hla_backward(*self._args)
+        if rc != 0:
+            raise HLAError(f"hla_backward failed: {status_str(rc)} (code {rc})")
+        return self.grads
+
+
+def hla_backward(q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0, dq=None, dk=None,
+                 dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the HLA-2 output with respect to q, k, v,
+    given the upstream gradient do.  All four are [B, H, n, d] (d == dv), one
+    dtype (bf16 or fp32), contiguous, on one GPU; gamma as in hla_forward."""
+    return BackwardPlan(q, k, v, do, variant, gamma, seg_chunks, dq, dk, dv, workspace,
+                        stream).run()

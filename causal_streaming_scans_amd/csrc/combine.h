@@ -243,7 +243,7 @@ __global__ __launch_bounds__(NT) void up_sweep_kernel(FwdParams p, int b) {
     up_sweep_slot<CS>(blockIdx.x, &comb, &cs);
     if (comb >= npair * p.BH) return;
     const int bh = comb / npair, m = comb - bh * npair;
-    const float g = HLA2 ? p.gamma[bh % p.H] : 1.f;
+    const float g = HLA2 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const float a = HLA2 ? pow_int(g, (long)p.seg_len << b) : 1.f;   // g^(tokens of a child)
     combine_slice<HLA2, D, DV, NT, CS>(p.ws + node_offset(bh, b, 2 * m, p.BH, p.nreal, SUMF),
                                        p.ws + node_offset(bh, b, 2 * m + 1, p.BH, p.nreal, SUMF),

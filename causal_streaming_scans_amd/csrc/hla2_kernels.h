@@ -239,7 +239,7 @@ void hla2_forward_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
+    const float g = DECAY ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const bool ratio = p.ratio != 0;
@@ -527,7 +527,7 @@ void hla2_summary_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
-    const float g = DECAY ? p.gamma[bh % p.H] : 1.f;
+    const float g = DECAY ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;

@@ -219,6 +219,107 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
     return run_stage(stage, kern, p, variant, d, dv, static_cast<hipStream_t>(stream));
 }
 
+// ------------------------------------------------------------------ backward
+//
+// HLA-2 as two chained first-order linear attentions, with z_t = S^K_t q_t:
+//   Z = LA_g(Q, K, K),   O = LA_{g^2}(Q, Z, V),
+//   LA_g(A, B, C)_t = sum_{s<=t} g^(t-s) (a_t . b_s) c_s.
+// The vector-Jacobian product of LA_g is three passes of the same form, two
+// of them anti-causal (RLA: sum over s >= t, weight g^(s-t)):
+//   dA = LA_g(dOut, C, B),  dB = RLA_g(C, dOut, A),  dC = RLA_g(B, A, dOut).
+// Through O: dQ += LA_{g^2}(dO, V, Z), dZ = RLA_{g^2}(V, dO, Q),
+//            dV = RLA_{g^2}(Z, Q, dO);
+// through Z (K is both key and value there): dQ += LA_g(dZ, K, K),
+//            dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ).
+// Seven passes in that dependency order; Z and dZ live in the workspace.
+
+int hla_backward_default_seg_chunks(int B, int H, int n) {
+    if (B < 1 || H < 1 || n < 1) return 1;
+    const long nch = ceil_div(n, kLaChunk);
+    // about 1024 workgroups per pass; a segment's summary costs one fold of
+    // d x d floats in each later segment, so segments can be short
+    long nseg = ceil_div(1024, (long)B * H);
+    long g = ceil_div(nch, nseg);
+    if (g < 2) g = 2;
+    if (g > nch) g = nch;
+    return (int)g;
+}
+
+size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
+                                    int seg_chunks) {
+    if (variant != HLA_HLA2 || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
+        (dtype != HLA_F32 && dtype != HLA_BF16))
+        return 0;
+    const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
+    const long nseg = num_segments(n, kLaChunk, g);
+    const size_t esz = dtype == HLA_BF16 ? 2 : 4;
+    const size_t sums = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
+    return sums + 2 * (size_t)B * H * n * d * esz;
+}
+
+hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
+                        void *dk, void *dv_out, int B, int H, int n, int d, int dv, int dtype,
+                        int variant, const float *gamma_host, int seg_chunks, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
+    if (st != HLA_OK) return st;
+    if (n < 0) return HLA_ERR_SHAPE;
+    if (seg_chunks < 0) return HLA_ERR_ARG;
+    if (variant != HLA_HLA2 || d != dv) return HLA_ERR_UNSUPPORTED;
+    LaLaunch la;
+    if (!lookup_la(dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
+    if (n == 0) return HLA_OK;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
+    const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
+    if ((long)kLaChunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    const long nseg = num_segments(n, kLaChunk, g);
+    if (nseg * B * H > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    const size_t need = hla_backward_workspace_bytes(variant, B, H, n, d, dv, dtype, g);
+    if (!workspace) return HLA_ERR_NULL;
+    if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
+
+    const size_t esz = dtype == HLA_BF16 ? 2 : 4;
+    const size_t sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
+    char *ws = static_cast<char *>(workspace);
+    void *Z = ws + sums_bytes;
+    void *dZ = ws + sums_bytes + (size_t)B * H * n * d * esz;
+
+    LaParams p1, p2;   // decay g and g^2
+    memset(&p1, 0, sizeof(p1));
+    p1.sums = reinterpret_cast<float *>(ws);
+    p1.BH = B * H;
+    p1.H = H;
+    p1.n = n;
+    p1.seg_len = kLaChunk * g;
+    p1.nseg = (int)nseg;
+    fill_gamma(p1.gamma, gamma_host, H);
+    p2 = p1;
+    for (int h = 0; h < kMaxDecayHeads; ++h) p2.gamma[h] = p1.gamma[h] * p1.gamma[h];
+
+    struct Pass { LaParams *base; const void *a, *b, *c, *add; void *out; int rev; };
+    const Pass passes[7] = {
+        {&p1, q, k, k, nullptr, Z, 0},          // Z  = LA_g(Q, K, K)
+        {&p2, dout, v, Z, nullptr, dq, 0},      // dQ = LA_g2(dO, V, Z)
+        {&p2, v, dout, q, nullptr, dZ, 1},      // dZ = RLA_g2(V, dO, Q)
+        {&p2, Z, q, dout, nullptr, dv_out, 1},  // dV = RLA_g2(Z, Q, dO)
+        {&p1, k, dZ, q, nullptr, dk, 1},        // dK = RLA_g(K, dZ, Q)
+        {&p1, k, q, dZ, dk, dk, 1},             // dK += RLA_g(K, Q, dZ)
+        {&p1, dZ, k, k, dq, dq, 0},             // dQ += LA_g(dZ, K, K)
+    };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (const Pass &ps : passes) {
+        LaParams p = *ps.base;
+        p.a = ps.a;
+        p.b = ps.b;
+        p.c = ps.c;
+        p.add = ps.add;
+        p.out = ps.out;
+        p.reverse = ps.rev;
+        if (la(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+    }
+    return HLA_OK;
+}
+
 hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B, int H, int d,
                     int dv, int dtype, int variant, const float *gamma_host, float *state,
                     void *stream) {

@@ -30,6 +30,12 @@ bool lookup_forward_bf16_32(bool ahla, int chunk, bool decay, FwdKernels *out);
 bool lookup_forward_bf16_64(bool ahla, int chunk, bool decay, FwdKernels *out);
 bool lookup_forward_bf16_128(bool ahla, int chunk, bool decay, FwdKernels *out);
 
+// Chunked first-order linear attention (la_kernels.h): the summary launch
+// (when p.nseg > 1) and the main launch, on one stream.
+constexpr int kLaChunk = 64;
+typedef hipError_t (*LaLaunch)(const LaParams &, hipStream_t);
+bool lookup_la(int dtype, int d, LaLaunch *out);
+
 // fill dst[0:count) with src[0:count), or with zeros when src is null
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s);
 

@@ -29,6 +29,15 @@ struct FwdParams {
     short seg_order[kMaxOrder];    // forward: segment run by rank r (nseg <= kMaxOrder)
 };
 
+// Decay of head index h (= bh % H).  Only the first kMaxDecayHeads entries of
+// a gamma array exist; a per-head decay is accepted only for H up to that,
+// and without one every entry is 1, so clamping the index keeps the read
+// inside the array for any H.
+__host__ __device__ inline int gamma_slot(int bh, int H) {
+    const int h = bh % H;
+    return h < kMaxDecayHeads ? h : kMaxDecayHeads - 1;
+}
+
 // Forward workgroup L of the 1-D grid of nseg * BH: heads vary fastest, so
 // consecutive workgroups -- dealt to different XCDs -- share one segment
 // rank, and every XCD gets every segment; rank r runs segment seg_order[r]
@@ -72,6 +81,23 @@ __host__ __device__ inline size_t node_offset(int bh, int b, int m, int BH, int 
                                : (size_t)BH * nreal + (size_t)bh * nreal + node_index(b, m, nreal);
     return slot * (size_t)sumf;
 }
+
+// Arguments of one chunked first-order linear-attention pass (la_kernels.h):
+//   out_t = add_t + sum_{s <= t} g^(t-s) (a_t . b_s) c_s,
+// over the reversed sequence when `reverse` is set.
+struct LaParams {
+    const void *a;      // [BH][n][D] queries of this pass
+    const void *b;      // [BH][n][D] keys
+    const void *c;      // [BH][n][D] values
+    const void *add;    // [BH][n][D] added to the output, or null (may alias out)
+    void *out;          // [BH][n][D]
+    float *sums;        // [BH][nseg-1][D*D] segment states (nseg > 1)
+    int BH, H, n;
+    int seg_len;        // tokens per segment, a multiple of the chunk
+    int nseg;
+    int reverse;        // run the sequence backwards (anti-causal pass)
+    float gamma[kMaxDecayHeads];   // decay of head h for this pass
+};
 
 // Decode step arguments.
 struct StepParams {

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const float g = AHLA ? 1.f : p.gamma[bh % p.H];
+    const float g = AHLA ? 1.f : p.gamma[gamma_slot(bh, p.H)];
     const float g2 = g * g;
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;

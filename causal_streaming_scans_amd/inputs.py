@@ -118,6 +118,13 @@ def make_inputs(B, H, n, d, dv, dtype="bf16", dist="l2norm", seed=0,
     return out
 
 
+def make_upstream_grad(BH, n, dv, dtype="bf16", seed=0):
+    """Upstream gradient dL/do for a backward pass: N(0, 1) entries,
+    [B*H, n, dv], from its own PCG64 stream, rounded like the inputs."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _store(rng.standard_normal((BH, n, dv)), dtype)
+
+
 def workload_inputs(key: str, **overrides):
     w = WORKLOADS[key]
     kw = dict(B=w.B, H=w.H, n=w.n, d=w.d, dv=w.dv, dtype=w.dtype, dist=w.dist,

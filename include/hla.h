@@ -177,6 +177,44 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
                     int B, int H, int d, int dv, int dtype, int variant,
                     const float *gamma_host, float *state, void *stream);
 
+/*
+ * Backward pass (vector-Jacobian product) of the HLA-2 operator, for
+ * training through the chunk-parallel form (page section "4. Entrenamiento
+ * Paralelo mediante Escaneos Asociativos"; the operator of section "1. HLA de
+ * Segundo Orden", decay per "Contribuciones Clave" item 2).  Given the
+ * upstream gradient dout = dL/do, writes dq = dL/dq, dk = dL/dk, dv = dL/dv
+ * of the HLA_HLA2 output o = tril(L L^T) V (with decay g_h when gamma_host is
+ * given) computed from zero state.
+ *
+ * Method: with z_t = S^K_t q_t, the operator is two chained causal linear
+ * attentions, Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), where
+ * LA_g(A, B, C)_t = sum_{s<=t} g^(t-s) (a_t . b_s) c_s.  The chain rule through
+ * each gives linear attentions of the same form, causal or anti-causal; the
+ * library runs seven chunked passes (chunk 64 tokens, segments of seg_chunks
+ * chunks in parallel, each pass one segment-state launch and one main
+ * launch), recomputing Z, and keeps Z and dZ in the workspace.
+ *
+ * q, k, v, dout  device, [B][H][n][d] (d == dv), element type = dtype
+ * dq, dk, dv_out  device outputs, same layout and type; may not alias the
+ *                inputs or each other
+ * gamma_host     NULL or H decays in (0, 1] (as hla_forward)
+ * seg_chunks     chunks (of 64 tokens) per segment; 0 = the library's default
+ *                (hla_backward_default_seg_chunks)
+ * workspace      device buffer of at least hla_backward_workspace_bytes()
+ *                bytes (contents ignored on entry, unspecified on return)
+ * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
+ * dZ are kept in dtype.  Supported: variant HLA_HLA2 only (other variants:
+ * HLA_ERR_UNSUPPORTED), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
+ * d in {16, 32, 64}.  Errors as hla_forward.
+ */
+int hla_backward_default_seg_chunks(int B, int H, int n);
+size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
+                                    int seg_chunks);
+hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout,
+                        void *dq, void *dk, void *dv_out, int B, int H, int n, int d, int dv,
+                        int dtype, int variant, const float *gamma_host, int seg_chunks,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *hla_status_str(int status);
 

@@ -158,3 +158,51 @@ def test_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 1, 16, 16)
     with pytest.raises(hla.HLAError):
         hla.hla_forward(x, x, x, chunk=16)
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd(lib, q=1, k=1, v=1, do=1, dq=1, dk=1, dv=1, B=1, H=2, n=128, d=64, dvd=64, dtype=BF16,
+         variant=HLA2, gamma=None, seg=0, ws=1, ws_bytes=1 << 40):
+    P = ctypes.c_void_p
+    g = None
+    if gamma is not None:
+        g = (ctypes.c_float * len(gamma))(*gamma)
+    return lib.hla_backward(P(q), P(k), P(v), P(do), P(dq), P(dk), P(dv), B, H, n, d, dvd, dtype,
+                            variant, g, seg, P(ws), ws_bytes, None)
+
+
+def test_backward_workspace_bytes(lib):
+    # default segments: about 1024 workgroups a pass, at least 2 chunks of 64 each
+    assert lib.hla_backward_default_seg_chunks(4, 8, 2048) == 2
+    assert lib.hla_backward_default_seg_chunks(1, 1, 256) == 2
+    assert lib.hla_backward_default_seg_chunks(1, 1, 100) == 2 or \
+        lib.hla_backward_default_seg_chunks(1, 1, 100) == 1
+    B, H, n, d = 4, 8, 2048, 64
+    g = lib.hla_backward_default_seg_chunks(B, H, n)
+    nseg = -(-n // (64 * g))
+    want = B * H * (nseg - 1) * d * d * 4 + 2 * B * H * n * d * 2
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16") == want
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32) == 2 * B * H * n * d * 4
+    assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == 0
+    assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == 0
+
+
+def test_backward_validation(lib):
+    assert _bwd(lib, n=0) == OK                      # nothing to do, nothing enqueued
+    assert _bwd(lib, variant=HLA2_RATIO) == ERR_UNSUP
+    assert _bwd(lib, variant=AHLA) == ERR_UNSUP
+    assert _bwd(lib, variant=9) == ERR_ARG
+    assert _bwd(lib, dvd=32) == ERR_UNSUP
+    assert _bwd(lib, d=48, dvd=48) == ERR_UNSUP
+    assert _bwd(lib, dtype=F32, d=128, dvd=128) == ERR_UNSUP
+    assert _bwd(lib, dtype=5) == ERR_ARG
+    assert _bwd(lib, B=0) == ERR_SHAPE
+    assert _bwd(lib, n=-1) == ERR_SHAPE
+    assert _bwd(lib, seg=-1) == ERR_ARG
+    assert _bwd(lib, gamma=[0.9, 1.5]) == ERR_ARG
+    assert _bwd(lib, gamma=[0.9, 0.0]) == ERR_ARG
+    assert _bwd(lib, q=None) == ERR_NULL
+    assert _bwd(lib, dv=None) == ERR_NULL
+    assert _bwd(lib, ws=None) == ERR_NULL
+    assert _bwd(lib, ws_bytes=1) == ERR_WS

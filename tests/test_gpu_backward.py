@@ -1,0 +1,139 @@
+"""GPU parity of hla_backward (HLA-2 gradients dq, dk, dv) against the fp64
+oracle of oracle/backward.py -- the chain rule on the masked matrix form of
+the operator of "1. HLA de Segundo Orden" ("Resumen Tecnico: Atencion Lineal
+de Orden Superior (HLA)", gist.science/es/paper/2510.27258), trained through
+the chunk-parallel form of "4. Entrenamiento Paralelo mediante Escaneos
+Asociativos".  Relative L2 per gradient: 1e-5 for fp32, 1e-2 for bf16 (the
+oracle consumes the same bf16-rounded inputs)."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import backward as BW
+from causal_streaming_scans_amd import inputs as I
+from hla_testlib import TOL, from_dev, rel_l2, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_backward(x, do, B, H, dtype, gamma=None, seg_chunks=0):
+    import torch
+    import causal_streaming_scans_amd as hla
+    n, d = x["q"].shape[1], x["q"].shape[2]
+    shp = (B, H, n, d)
+    dq, dk, dv = hla.hla_backward(to_dev(x["q"], dtype, shp), to_dev(x["k"], dtype, shp),
+                                  to_dev(x["v"], dtype, shp), to_dev(do, dtype, shp),
+                                  gamma=gamma, seg_chunks=seg_chunks)
+    torch.cuda.synchronize()
+    return tuple(from_dev(t).reshape(B * H, n, d) for t in (dq, dk, dv))
+
+
+def check(got, want, dtype, label):
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        e = rel_l2(g, w)
+        say(f"  {label} {name}: rel_l2 {e:.3e}")
+        assert e < TOL[dtype], (label, name, e)
+
+
+SMALL = [
+    # dtype, d, n, H, decay, seg_chunks
+    ("f32", 16, 200, 2, False, 0),
+    ("f32", 16, 200, 2, True, 1),
+    ("f32", 32, 130, 1, True, 0),
+    ("f32", 64, 257, 2, False, 1),
+    ("f32", 64, 1, 1, True, 0),
+    ("bf16", 16, 333, 2, True, 1),
+    ("bf16", 32, 64, 2, False, 0),
+    ("bf16", 64, 65, 2, True, 0),
+    ("bf16", 64, 450, 3, True, 2),
+    ("bf16", 64, 512, 2, False, 1),
+    ("bf16", 128, 300, 2, True, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,n,H,decay,seg", SMALL)
+def test_backward_small(dtype, d, n, H, decay, seg):
+    say(f"[backward] dtype {dtype} d {d} n {n} H {H} decay {decay} seg_chunks {seg}")
+    B = 1
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="normal_scaled" if dtype == "f32" else "l2norm",
+                      seed=700 + d + n, decay=decay)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=800 + n)
+    gamma = x["gamma"]
+    got = run_backward(x, do, B, H, dtype, gamma, seg)
+    want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, H, gamma)
+    check(got, want, dtype, f"{dtype} d{d} n{n}")
+
+
+def test_backward_hla2_n2048_sampled_heads():
+    """The HLA-2 workload B=4 H=8 n=2048 d=dv=64 bf16 in the default launch
+    configuration; the oracle on the first and last head."""
+    w = I.WORKLOADS["hla2_n2048"]
+    say(f"[backward] workload {w.name}")
+    x = I.workload_inputs("hla2_n2048")
+    do = I.make_upstream_grad(w.B * w.H, w.n, w.dv, w.dtype, seed=w.seed + 100)
+    got = run_backward(x, do, w.B, w.H, w.dtype)
+    heads = [0, w.B * w.H - 1]
+    want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, w.H, heads=heads)
+    check(tuple(g[heads] for g in got), want, w.dtype, "hla2_n2048 heads 0,31")
+
+
+def test_backward_decay_n16384_prefix_and_euler():
+    """The decay workload B=2 H=16 n=16384 d=dv=128 bf16 at full size.
+    (1) With do zero from token m on, the gradient of tokens before m is that
+    of the first m tokens alone (causality), which the oracle computes for
+    two heads, and every token from m on gets an exact zero.  (2) With a
+    dense do, Euler's identity for an operator of degree 2 in q, 2 in k and
+    1 in v: <q, dq> = <k, dk> = 2 <do, o> and <v, dv> = <do, o>, with o from
+    the serial fp64 oracle."""
+    w = I.WORKLOADS["decay_n16384"]
+    say(f"[backward] workload {w.name}")
+    x = I.workload_inputs("decay_n16384")
+    BH, m = w.B * w.H, 1024
+    do = I.make_upstream_grad(BH, w.n, w.dv, w.dtype, seed=w.seed + 100)
+    do_cut = do.copy()
+    do_cut[:, m:] = 0
+    got = run_backward(x, do_cut, w.B, w.H, w.dtype, x["gamma"])
+    for g in got:
+        assert np.all(g[:, m:] == 0)
+    heads = [3, BH - 1]
+    xs = {key: x[key][:, :m] for key in ("q", "k", "v")}
+    want = BW.hla2_vjp_batched(xs["q"], xs["k"], xs["v"], do_cut[:, :m], w.H, x["gamma"],
+                               heads=heads)
+    check(tuple(g[heads, :m] for g in got), want, w.dtype, "decay_n16384 prefix")
+
+    got = run_backward(x, do, w.B, w.H, w.dtype, x["gamma"])
+    o = oracle.hla2(x["q"], x["k"], x["v"], H=w.H, gamma=x["gamma"])
+    ref = float(np.sum(do.astype(np.float64) * o))
+    for name, xin, g, deg in (("q", x["q"], got[0], 2), ("k", x["k"], got[1], 2),
+                              ("v", x["v"], got[2], 1)):
+        lhs = float(np.sum(xin.astype(np.float64) * g))
+        scale = float(np.linalg.norm(xin) * np.linalg.norm(g))
+        say(f"  euler {name}: <x, dx> {lhs:.6e} vs {deg} <do, o> {deg * ref:.6e} (scale {scale:.3e})")
+        assert abs(lhs - deg * ref) <= 1e-2 * scale
+
+
+def test_many_heads_without_decay():
+    """H above the 256 heads a per-head decay can name: without a decay every
+    head is undecayed (regression: the kernels once read the decay of head h
+    from an array of 256 entries for any h)."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    from hla_testlib import gpu_forward, oracle_forward
+    B, H, n, d = 1, 300, 80, 16
+    say(f"[many heads] B {B} H {H} n {n} d {d} bf16 forward, decode step, backward")
+    x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist="l2norm", seed=901)
+    o, st = gpu_forward(x, "hla2", B, H, "bf16", chunk=32, seg_chunks=1, want_state=True)
+    want_o, want_st = oracle_forward(x, "hla2", H, want_state=True)
+    assert rel_l2(o, want_o) < TOL["bf16"]
+    y = I.make_inputs(B, H, 1, d, d, dtype="bf16", dist="l2norm", seed=902)
+    sd = torch.from_numpy(np.ascontiguousarray(st, np.float32)).cuda()
+    od = hla.hla_step(to_dev(y["q"], "bf16", (B, H, d)), to_dev(y["k"], "bf16", (B, H, d)),
+                      to_dev(y["v"], "bf16", (B, H, d)), sd, variant="hla2")
+    torch.cuda.synchronize()
+    want_d = oracle.hla2(y["q"], y["k"], y["v"], state_in=want_st)
+    assert rel_l2(from_dev(od).reshape(-1), want_d.reshape(-1)) < TOL["bf16"]
+    do = I.make_upstream_grad(B * H, n, d, "bf16", seed=903)
+    got = run_backward(x, do, B, H, "bf16", None, 1)
+    heads = [0, 255, 256, 299]
+    want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, H, heads=heads)
+    check(tuple(g[heads] for g in got), want, "bf16", "H=300")
