@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--backward-steps", type=int, default=200,
                     help="time this many hla_backward calls (HLA-2 gradients at the benchmark "
                          "shape); 0 skips the backward leg")
+    ap.add_argument("--backward-seg-chunks", type=int, default=0,
+                    help="chunks per segment of the backward passes (0 = the library default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the CPU oracle over the workload until this much wall time")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -453,7 +455,8 @@ def main():
         qb, kb, vb = (to_dev(xb[key], (B, H, n, d)) for key in ("q", "k", "v"))
         dob = to_dev(gb, (B, H, n, dv))
         del xb, gb
-        bplan = hla.BackwardPlan(qb, kb, vb, dob, variant="hla2")
+        bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
+        bplan = hla.BackwardPlan(qb, kb, vb, dob, variant="hla2", seg_chunks=bseg)
         for _ in range(10):
             bplan.run()
         torch.cuda.synchronize()
@@ -469,7 +472,7 @@ def main():
                                 "q,k L2-normalised Gaussian, v and do ~ N(0,1)",
                     "passes": "7 chunked linear-attention passes (chunk 64), each a segment-state "
                               "launch and a main launch",
-                    "seg_chunks": hla.backward_default_seg_chunks(B, H, n),
+                    "seg_chunks": bseg,
                     "ms_per_step": round(bms, 5), "tokens_per_s": round(tokens / (bms * 1e-3), 1),
                     "lean_bytes_per_step": b_bytes,
                     "lean_hbm_frac": round(b_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -230,15 +230,20 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
 // Through O: dQ += LA_{g^2}(dO, V, Z), dZ = RLA_{g^2}(V, dO, Q),
 //            dV = RLA_{g^2}(Z, Q, dO);
 // through Z (K is both key and value there): dQ += LA_g(dZ, K, K),
-//            dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ).
-// Seven passes in that dependency order; Z and dZ live in the workspace.
+//            dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ), the two slots in one
+//            pass with one state (the kernels' SYM form).
+// Six passes in that dependency order; Z and dZ live in the workspace.  The
+// first and last passes share b = c = K and the decay g, so the segment
+// states of the first are kept and reused by the last.
 
 int hla_backward_default_seg_chunks(int B, int H, int n) {
     if (B < 1 || H < 1 || n < 1) return 1;
     const long nch = ceil_div(n, kLaChunk);
-    // about 1024 workgroups per pass; a segment's summary costs one fold of
-    // d x d floats in each later segment, so segments can be short
-    long nseg = ceil_div(1024, (long)B * H);
+    // about 768 workgroups per pass, three per compute unit at d = 64 (the
+    // main kernel's LDS allows three): one full round, no ragged second one.
+    // Measured at B*H = 128, n = 4096: 6 segments 0.79 ms per backward,
+    // 8 segments 0.84, 4 segments 0.92
+    long nseg = ceil_div(768, (long)B * H);
     long g = ceil_div(nch, nseg);
     if (g < 2) g = 2;
     if (g > nch) g = nch;
@@ -254,7 +259,7 @@ size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int
     const long nseg = num_segments(n, kLaChunk, g);
     const size_t esz = dtype == HLA_BF16 ? 2 : 4;
     const size_t sums = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    return sums + 2 * (size_t)B * H * n * d * esz;
+    return 2 * sums + 2 * (size_t)B * H * n * d * esz;
 }
 
 hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
@@ -266,8 +271,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (variant != HLA_HLA2 || d != dv) return HLA_ERR_UNSUPPORTED;
-    LaLaunch la;
-    if (!lookup_la(dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
+    LaLaunch la, la_sym;
+    if (!lookup_la(dtype, d, &la, &la_sym)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
     if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
@@ -281,12 +286,14 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     const size_t esz = dtype == HLA_BF16 ? 2 : 4;
     const size_t sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
     char *ws = static_cast<char *>(workspace);
-    void *Z = ws + sums_bytes;
-    void *dZ = ws + sums_bytes + (size_t)B * H * n * d * esz;
+    float *sums_kk = reinterpret_cast<float *>(ws);               // states of K K^T (g)
+    float *sums = reinterpret_cast<float *>(ws + sums_bytes);     // the other passes'
+    void *Z = ws + 2 * sums_bytes;
+    void *dZ = ws + 2 * sums_bytes + (size_t)B * H * n * d * esz;
 
     LaParams p1, p2;   // decay g and g^2
     memset(&p1, 0, sizeof(p1));
-    p1.sums = reinterpret_cast<float *>(ws);
+    p1.sums = sums;
     p1.BH = B * H;
     p1.H = H;
     p1.n = n;
@@ -296,15 +303,17 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     p2 = p1;
     for (int h = 0; h < kMaxDecayHeads; ++h) p2.gamma[h] = p1.gamma[h] * p1.gamma[h];
 
-    struct Pass { LaParams *base; const void *a, *b, *c, *add; void *out; int rev; };
-    const Pass passes[7] = {
-        {&p1, q, k, k, nullptr, Z, 0},          // Z  = LA_g(Q, K, K)
-        {&p2, dout, v, Z, nullptr, dq, 0},      // dQ = LA_g2(dO, V, Z)
-        {&p2, v, dout, q, nullptr, dZ, 1},      // dZ = RLA_g2(V, dO, Q)
-        {&p2, Z, q, dout, nullptr, dv_out, 1},  // dV = RLA_g2(Z, Q, dO)
-        {&p1, k, dZ, q, nullptr, dk, 1},        // dK = RLA_g(K, dZ, Q)
-        {&p1, k, q, dZ, dk, dk, 1},             // dK += RLA_g(K, Q, dZ)
-        {&p1, dZ, k, k, dq, dq, 0},             // dQ += LA_g(dZ, K, K)
+    struct Pass {
+        LaParams *base; const void *a, *b, *c, *add; void *out; int rev; bool sym;
+        float *sums; bool summaries;
+    };
+    const Pass passes[6] = {
+        {&p1, q, k, k, nullptr, Z, 0, false, sums_kk, true},        // Z  = LA_g(Q, K, K)
+        {&p2, dout, v, Z, nullptr, dq, 0, false, sums, true},       // dQ = LA_g2(dO, V, Z)
+        {&p2, v, dout, q, nullptr, dZ, 1, false, sums, true},       // dZ = RLA_g2(V, dO, Q)
+        {&p2, Z, q, dout, nullptr, dv_out, 1, false, sums, true},   // dV = RLA_g2(Z, Q, dO)
+        {&p1, k, dZ, q, nullptr, dk, 1, true, sums, true},          // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+        {&p1, dZ, k, k, dq, dq, 0, false, sums_kk, false},          // dQ += LA_g(dZ, K, K)
     };
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (const Pass &ps : passes) {
@@ -315,7 +324,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         p.add = ps.add;
         p.out = ps.out;
         p.reverse = ps.rev;
-        if (la(p, s) != hipSuccess) return HLA_ERR_DEVICE;
+        p.sums = ps.sums;
+        if ((ps.sym ? la_sym : la)(p, s, ps.summaries) != hipSuccess) return HLA_ERR_DEVICE;
     }
     return HLA_OK;
 }

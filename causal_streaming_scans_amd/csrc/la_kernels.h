@@ -1,17 +1,20 @@
 // la_kernels.h -- chunked first-order causal linear attention on gfx950, the
 // building block of the HLA-2 backward pass.
 //
-//   out_t = add_t + sum_{s <= t} g^(t-s) (a_t . b_s) c_s           (forward time)
+//   out_t = add_t + sum_{s <= t} g^(t-s) (a_t . b_s) c_s                 (plain)
+//   out_t = add_t + sum_{s <= t} g^(t-s) [(a_t . b_s) c_s + (a_t . c_s) b_s]  (SYM)
 //
 // and the same over the reversed sequence (s >= t, weight g^(s-t)) when
 // `reverse` is set: logical token l is physical row n-1-l, so an anti-causal
-// pass is the causal pass run backwards through memory.
+// pass is the causal pass run backwards through memory.  SYM is the
+// gradient of a pass whose key and value are one tensor (K in Z = LA(Q, K, K)):
+// both slots in one pass, with one state S = sum w (b c^T + c b^T).
 //
 // The gradient of HLA-2 is a chain of such passes.  With z_t = S^K_t q_t =
 // sum_{i<=t} g^(t-i) (q_t . k_i) k_i (the key read-out of page section "1. HLA
 // de Segundo Orden"), the masked operator is two chained linear attentions,
 // Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), and the chain rule through each
-// one gives three more of the same form (see hla_api.cpp).
+// one gives more of the same form (see hla_api.cpp).
 //
 // Parallel form (page section "4. Entrenamiento Paralelo mediante Escaneos
 // Asociativos", first order): the state S = sum_s g^(.) b_s c_s^T is additive,
@@ -23,9 +26,10 @@
 //   P     = D_g * tril(A_c B_c^T)                           (C x C, in LDS)
 //   out^T = C_c^T P^T + S^T A_c^T diag(g^(tau+1)) [+ add]   (written from registers)
 //   S     = g^C S + (B_c^T diag(g^(C-1-sigma))) C_c         (fp32, in registers)
-// Products use the "NT" MFMA form of device_common.h with both operands
-// row-major along k in LDS: c and the weighted b are staged transposed
-// ([feature][token]) next to the row-major a and b.
+// Every chunk tile is stored row-major ([token][feature]) once; products that
+// contract over the tokens read their operands with the transposing LDS read
+// (bf16) of device_common.h, so no transposed copy is ever written.  The
+// next chunk's rows are loaded into registers while the current one computes.
 #pragma once
 
 #include "device_common.h"
@@ -33,105 +37,176 @@
 
 namespace hla {
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool SYM>
 struct LaLds {
-    using TR = PadTile<T, D>;    // [C][D] a, b rows; [D][D] state copy St[j][i] = S[i][j]
-    using TT = PadTile<T, C>;    // [D][C] transposed c and weighted b; [C][C] scores
+    using TR = LdsTile<T, D>;    // [C][D] chunk rows; [D][D] state copy St[j][i] = S[i][j]
+    using TP = LdsTile<T, C>;    // [C][C] scores
     T a[C * TR::LD];
     T b[C * TR::LD];
-    T ct[D * TT::LD];
-    T btw[D * TT::LD];
-    T p[C * TT::LD];
+    T c[C * TR::LD];
+    T bw[C * TR::LD];            // g^(C-1-sigma) b_sigma
+    T cw[SYM ? C * TR::LD : 1];  // g^(C-1-sigma) c_sigma (SYM)
+    T p[C * TP::LD];
+    T p2[SYM ? C * TP::LD : 1];  // D_g * tril(A C^T) (SYM)
     T st[D * TR::LD];
     float pw[C + 1];             // g^e, e = 0..C
 };
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool SYM>
 struct LaCfg {
     static constexpr int NW = 4, NT = NW * kWave;
     static constexpr int TR = C / 16;          // token tiles per chunk
     static constexpr int TD = D / 16;          // feature tiles
     static constexpr int NS = TD * TD;         // state tiles
     static constexpr int SPW = (NS + NW - 1) / NW;   // state tiles per wave
+    static constexpr int NTRI = TR * (TR + 1) / 2;   // lower-triangular score tiles
+    static constexpr int NOUT = TR * TD;             // output tiles
     static constexpr int blocks() {
-        constexpr size_t lds = sizeof(LaLds<T, D, C>);
-        return lds <= 40 * 1024 ? 3 : (lds <= 80 * 1024 ? 2 : 1);
+        constexpr size_t lds = sizeof(LaLds<T, D, C, SYM>);
+        return lds <= 52 * 1024 ? 3 : (lds <= 78 * 1024 ? 2 : 1);
     }
 };
 
-// Stage the chunk whose first logical token is l0: a, b row-major, c and
-// g^(C-1-sigma) b transposed.  Rows past the end of the sequence are zeros.
-template <typename T, int D, int C>
-__device__ __forceinline__ void la_stage(const LaParams &p, size_t head_row, int l0,
-                                         LaLds<T, D, C> &s) {
-    using L = LaLds<T, D, C>;
-    constexpr int VE = Vec16<T>::N, VPR = D / VE, NV = C * VPR;
-    constexpr int NT = LaCfg<T, D, C>::NT;
-    const T *A = static_cast<const T *>(p.a);
-    const T *B = static_cast<const T *>(p.b);
-    const T *Cv = static_cast<const T *>(p.c);
-    for (int idx = threadIdx.x; idx < NV; idx += NT) {
-        const int r = idx / VPR, col = (idx % VPR) * VE;
-        const int l = l0 + r;
-        Vec16<T> xa, xb, xc;
-        if (l < p.n) {
-            const size_t row = head_row + (size_t)(p.reverse ? p.n - 1 - l : l);
-            xa = load16(A + row * D + col);
-            xb = load16(B + row * D + col);
-            xc = load16(Cv + row * D + col);
-        } else {
+// One thread's share of the a, b, c rows of a chunk, held in registers from
+// the global load (a chunk ahead) to the LDS store.  Lanes run along the
+// columns of a row, so one load instruction covers whole rows.  Rows past
+// the end of the sequence load row 0 of the head (in bounds) and are stored
+// as zeros.
+template <typename T, int D, int C, int NT>
+struct LaRegs {
+    static constexpr int VE = Vec16<T>::N, VPR = D / VE, NVEC = C * VPR;
+    static constexpr int NV = (NVEC + NT - 1) / NT;
+    uint4 ra[NV], rb[NV], rc[NV];
+    int l0;
+
+    __device__ __forceinline__ void load(const LaParams &p, size_t head_row, int first) {
+        l0 = first;
+        const T *A = static_cast<const T *>(p.a);
+        const T *B = static_cast<const T *>(p.b);
+        const T *Cv = static_cast<const T *>(p.c);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) xa.v[e] = xb.v[e] = xc.v[e] = from_f<T>(0.f);
-        }
-        store16(s.a + L::TR::off(r, col), xa);
-        store16(s.b + L::TR::off(r, col), xb);
-        const float w = s.pw[C - 1 - r];
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            s.ct[L::TT::off(col + e, r)] = xc.v[e];
-            s.btw[L::TT::off(col + e, r)] = from_f<T>(to_f(xb.v[e]) * w);
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            const int r = idx / VPR, col = (idx % VPR) * VE;
+            const int l = l0 + r;
+            size_t row = head_row;
+            if (idx < NVEC && l < p.n) row += (size_t)(p.reverse ? p.n - 1 - l : l);
+            const size_t off = row * D + (idx < NVEC ? col : 0);
+            ra[i] = *reinterpret_cast<const uint4 *>(A + off);
+            rb[i] = *reinterpret_cast<const uint4 *>(B + off);
+            rc[i] = *reinterpret_cast<const uint4 *>(Cv + off);
         }
     }
+
+    template <bool SYM>
+    __device__ __forceinline__ void store(LaLds<T, D, C, SYM> &s, int n) const {
+        using TL = typename LaLds<T, D, C, SYM>::TR;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int idx = threadIdx.x + i * NT;
+            if (idx < NVEC) {
+                const int r = idx / VPR, col = (idx % VPR) * VE;
+                const bool ok = l0 + r < n;
+                Vec16<T> xa, xb, xc;
+                // rows past the end become zeros by masking the words: a
+                // select between two uint4 values kept the prefetch arrays in
+                // scratch memory instead of registers
+                const unsigned m = ok ? 0xffffffffu : 0u;
+                uint4 ua = ra[i], ub = rb[i], uc = rc[i];
+                ua.x &= m; ua.y &= m; ua.z &= m; ua.w &= m;
+                ub.x &= m; ub.y &= m; ub.z &= m; ub.w &= m;
+                uc.x &= m; uc.y &= m; uc.z &= m; uc.w &= m;
+                *reinterpret_cast<uint4 *>(xa.v) = ua;
+                *reinterpret_cast<uint4 *>(xb.v) = ub;
+                *reinterpret_cast<uint4 *>(xc.v) = uc;
+                const int o = TL::off(r, col);
+                store16(s.a + o, xa);
+                store16(s.b + o, xb);
+                store16(s.c + o, xc);
+                const float w = s.pw[C - 1 - r];
+                Vec16<T> yb;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) yb.v[e] = from_f<T>(to_f(xb.v[e]) * w);
+                store16(s.bw + o, yb);
+                if constexpr (SYM) {
+                    Vec16<T> yc;
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) yc.v[e] = from_f<T>(to_f(xc.v[e]) * w);
+                    store16(s.cw + o, yc);
+                }
+            }
+        }
+    }
+};
+
+// acc[i][j] += sum_{k < K} M1[k][c1 + i] M2[k][c2 + j] for two row-major
+// [token][feature] LDS tiles: a product over the tokens, operands read with
+// the transposing LDS read (bf16) or per element (fp32).
+template <typename TL, int K>
+__device__ __forceinline__ f32x4 mma_tt(f32x4 acc, const bf16 *M1, int c1, const bf16 *M2, int c2) {
+#pragma unroll
+    for (int k = 0; k < K; k += 32)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_op8_tt<TL>(M1, k, c1), ld_op8_tt<TL>(M2, k, c2),
+                                                      acc, 0, 0, 0);
+    return acc;
+}
+template <typename TL, int K>
+__device__ __forceinline__ f32x4 mma_tt(f32x4 acc, const float *M1, int c1, const float *M2, int c2) {
+#pragma unroll
+    for (int k = 0; k < K; k += 16) acc = mma16(acc, ld_frag_tt<TL>(M1, k, c1), ld_frag_tt<TL>(M2, k, c2));
+    return acc;
+}
+
+// 16-deep operand whose four k-values are consecutive in a row of an LdsTile
+// matrix: lane l reads row row0 + l%16, columns col0 + 4g .. +3.
+template <typename TL>
+__device__ __forceinline__ Frag16<bf16> ld_frag_row(const bf16 *M, int row0, int col0) {
+    const int l = lane_id();
+    return Frag16<bf16>{*reinterpret_cast<const i16x4 *>(M + TL::off(row0 + (l & 15), col0 + 4 * (l >> 4)))};
+}
+template <typename TL>
+__device__ __forceinline__ Frag16<float> ld_frag_row(const float *M, int row0, int col0) {
+    const int l = lane_id();
+    return Frag16<float>{*reinterpret_cast<const f32x4 *>(M + TL::off(row0 + (l & 15), col0 + 4 * (l >> 4)))};
 }
 
 // The state tiles of this wave: tile m = wave + NW*i covers S rows
 // 16*(m / TD) .., columns 16*(m % TD) ..
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool SYM>
 struct LaState {
-    using Cfg = LaCfg<T, D, C>;
+    using Cfg = LaCfg<T, D, C, SYM>;
+    using TL = typename LaLds<T, D, C, SYM>::TR;
     f32x4 acc[Cfg::SPW];
 
     __device__ __forceinline__ void zero() {
 #pragma unroll
         for (int i = 0; i < Cfg::SPW; ++i) acc[i] = zero4();
     }
-    // S <- g^C S + Btw Ct^T (products of the staged chunk)
-    __device__ __forceinline__ void advance(const LaLds<T, D, C> &s, float gC, int w) {
-        using L = LaLds<T, D, C>;
+    // S <- g^C S + Bw^T C (+ Cw^T B): products of the staged chunk
+    __device__ __forceinline__ void advance(const LaLds<T, D, C, SYM> &s, float gC, int w) {
 #pragma unroll
         for (int i = 0; i < Cfg::SPW; ++i) {
             const int m = w + Cfg::NW * i;
             if (m < Cfg::NS) {
                 const int si = m / Cfg::TD, sj = m % Cfg::TD;
-                RowFrags<T, C> fc;
-                fc.template load_t<typename L::TT>(s.ct + L::TT::off(16 * sj, 0));
                 f32x4 a = acc[i];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] *= gC;
-                acc[i] = mma_nt_ft<typename L::TT, C>(a, s.btw + L::TT::off(16 * si, 0), fc);
+                a = mma_tt<TL, C>(a, s.bw, 16 * si, s.c, 16 * sj);
+                if constexpr (SYM) a = mma_tt<TL, C>(a, s.cw, 16 * si, s.b, 16 * sj);
+                acc[i] = a;
             }
         }
     }
     // St[j][i] = S[i][j], rounded to T
-    __device__ __forceinline__ void store_copy(LaLds<T, D, C> &s, int w) const {
-        using L = LaLds<T, D, C>;
+    __device__ __forceinline__ void store_copy(LaLds<T, D, C, SYM> &s, int w) const {
         const int l = lane_id(), g = l >> 4;
 #pragma unroll
         for (int i = 0; i < Cfg::SPW; ++i) {
             const int m = w + Cfg::NW * i;
             if (m < Cfg::NS) {
                 const int si = m / Cfg::TD, sj = m % Cfg::TD;
-                store4(s.st + L::TR::off(16 * sj + (l & 15), 16 * si + 4 * g), acc[i]);
+                store4(s.st + TL::off(16 * sj + (l & 15), 16 * si + 4 * g), acc[i]);
             }
         }
     }
@@ -139,25 +214,28 @@ struct LaState {
 
 // Summary of segment seg (< nseg-1): its state from zero, decayed to its end,
 // into p.sums.  Grid: (nseg-1) * BH workgroups, heads fastest.
-template <typename T, int D, int C>
-__global__ __launch_bounds__((LaCfg<T, D, C>::NT), (LaCfg<T, D, C>::blocks()))
+template <typename T, int D, int C, bool SYM>
+__global__ __launch_bounds__((LaCfg<T, D, C, SYM>::NT), (LaCfg<T, D, C, SYM>::blocks()))
 void la_summary_kernel(LaParams p) {
-    using Cfg = LaCfg<T, D, C>;
-    __shared__ LaLds<T, D, C> s;
+    using Cfg = LaCfg<T, D, C, SYM>;
+    __shared__ LaLds<T, D, C, SYM> s;
     const int L = blockIdx.x;
     const int bh = L % p.BH, seg = L / p.BH;
     const int w = wave_id();
     const float g = p.gamma[gamma_slot(bh, p.H)];
-    fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
-    __syncthreads();
-    const float gC = s.pw[C];
     const size_t head_row = (size_t)bh * p.n;
     const int l_begin = seg * p.seg_len;
     const int l_end = min(p.n, l_begin + p.seg_len);
-    LaState<T, D, C> S;
+    LaRegs<T, D, C, Cfg::NT> regs;
+    regs.load(p, head_row, l_begin);
+    fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
+    __syncthreads();
+    const float gC = s.pw[C];
+    LaState<T, D, C, SYM> S;
     S.zero();
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
-        la_stage<T, D, C>(p, head_row, l0, s);
+        regs.store(s, p.n);
+        if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
         __syncthreads();
         S.advance(s, gC, w);
         __syncthreads();
@@ -177,24 +255,28 @@ void la_summary_kernel(LaParams p) {
 }
 
 // Main pass over segment seg.  Grid: nseg * BH workgroups, heads fastest.
-template <typename T, int D, int C>
-__global__ __launch_bounds__((LaCfg<T, D, C>::NT), (LaCfg<T, D, C>::blocks()))
+template <typename T, int D, int C, bool SYM>
+__global__ __launch_bounds__((LaCfg<T, D, C, SYM>::NT), (LaCfg<T, D, C, SYM>::blocks()))
 void la_forward_kernel(LaParams p) {
-    using Cfg = LaCfg<T, D, C>;
-    using Ls = LaLds<T, D, C>;
+    using Cfg = LaCfg<T, D, C, SYM>;
+    using Ls = LaLds<T, D, C, SYM>;
+    using TR = typename Ls::TR;
+    using TP = typename Ls::TP;
     __shared__ Ls s;
     const int L = blockIdx.x;
     const int bh = L % p.BH, seg = L / p.BH;
     const int w = wave_id();
     const int l = lane_id(), gq = l >> 4, cl = l & 15;
     const float g = p.gamma[gamma_slot(bh, p.H)];
-    fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
     const size_t head_row = (size_t)bh * p.n;
     const int l_begin = seg * p.seg_len;
     const int l_end = min(p.n, l_begin + p.seg_len);
+    LaRegs<T, D, C, Cfg::NT> regs;
+    regs.load(p, head_row, l_begin);
+    fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
 
     // carried state: the summaries of the segments before this one, in order
-    LaState<T, D, C> S;
+    LaState<T, D, C, SYM> S;
     S.zero();
     if (seg > 0) {
         const float gL = pow_int(g, p.seg_len);
@@ -218,40 +300,52 @@ void la_forward_kernel(LaParams p) {
 
     const T *Add = static_cast<const T *>(p.add);
     T *Out = static_cast<T *>(p.out);
-    constexpr int NTRI = Cfg::TR * (Cfg::TR + 1) / 2;
-    constexpr int NOUT = Cfg::TR * Cfg::TD;
 
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
-        la_stage<T, D, C>(p, head_row, l0, s);
+        regs.store(s, p.n);
+        if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
         __syncthreads();
-        // scores: lower-triangular tiles (ti >= tj) of D_g * (A B^T)
-        for (int t = w; t < NTRI; t += Cfg::NW) {
+        // scores, transposed in registers so each lane holds four consecutive
+        // sigma of one tau: lower-triangular tiles (ti >= tj) of D_g * (A B^T)
+        for (int t = w; t < Cfg::NTRI; t += Cfg::NW) {
             int ti = 0;
             while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
             const int tj = t - ti * (ti + 1) / 2;
-            RowFrags<T, D> fb;
-            fb.template load_t<typename Ls::TR>(s.b + Ls::TR::off(16 * tj, 0));
-            f32x4 acc = mma_nt_ft<typename Ls::TR, D>(zero4(), s.a + Ls::TR::off(16 * ti, 0), fb);
-            const int sg = 16 * tj + cl;
+            RowFrags<T, D> fa;
+            fa.template load_t<TR>(s.a + 16 * ti * TR::LD);
+            const int tau = 16 * ti + cl;
+            f32x4 acc = mma_nt_ft<TR, D>(zero4(), s.b + 16 * tj * TR::LD, fa);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tau = 16 * ti + 4 * gq + r;
-                const float v = tau >= sg ? acc[r] * s.pw[tau - sg] : 0.f;
-                s.p[Ls::TT::off(tau, sg)] = from_f<T>(v);
+                const int sg = 16 * tj + 4 * gq + r;
+                acc[r] = tau >= sg ? acc[r] * s.pw[tau - sg] : 0.f;
+            }
+            store4(s.p + TP::off(tau, 16 * tj + 4 * gq), acc);
+            if constexpr (SYM) {
+                f32x4 acc2 = mma_nt_ft<TR, D>(zero4(), s.c + 16 * tj * TR::LD, fa);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int sg = 16 * tj + 4 * gq + r;
+                    acc2[r] = tau >= sg ? acc2[r] * s.pw[tau - sg] : 0.f;
+                }
+                store4(s.p2 + TP::off(tau, 16 * tj + 4 * gq), acc2);
             }
         }
         __syncthreads();
         // outputs, transposed: lane holds features 4gq..4gq+3 of token cl
-        for (int t = w; t < NOUT; t += Cfg::NW) {
+        for (int t = w; t < Cfg::NOUT; t += Cfg::NW) {
             const int tj = t % Cfg::TD, ti = t / Cfg::TD;   // feature tile, token tile
             f32x4 acc1 = zero4();
-            for (int ks = 0; ks <= ti; ++ks)
-                acc1 = mma16(acc1, ld_frag(s.ct + Ls::TT::off(16 * tj, 16 * ks), Ls::TT::LD),
-                             ld_frag(s.p + Ls::TT::off(16 * ti, 16 * ks), Ls::TT::LD));
+            for (int ks = 0; ks <= ti; ++ks) {
+                acc1 = mma16(acc1, ld_frag_tt<TR>(s.c, 16 * ks, 16 * tj),
+                             ld_frag_row<TP>(s.p, 16 * ti, 16 * ks));
+                if constexpr (SYM)
+                    acc1 = mma16(acc1, ld_frag_tt<TR>(s.b, 16 * ks, 16 * tj),
+                                 ld_frag_row<TP>(s.p2, 16 * ti, 16 * ks));
+            }
             RowFrags<T, D> fa;
-            fa.template load_t<typename Ls::TR>(s.a + Ls::TR::off(16 * ti, 0));
-            const f32x4 acc2 =
-                mma_nt_ft<typename Ls::TR, D>(zero4(), s.st + Ls::TR::off(16 * tj, 0), fa);
+            fa.template load_t<TR>(s.a + 16 * ti * TR::LD);
+            const f32x4 acc2 = mma_nt_ft<TR, D>(zero4(), s.st + 16 * tj * TR::LD, fa);
             const int tau = 16 * ti + cl;
             const int lt = l0 + tau;
             if (lt < l_end) {

@@ -173,15 +173,16 @@ def _bwd(lib, q=1, k=1, v=1, do=1, dq=1, dk=1, dv=1, B=1, H=2, n=128, d=64, dvd=
 
 
 def test_backward_workspace_bytes(lib):
-    # default segments: about 1024 workgroups a pass, at least 2 chunks of 64 each
+    # default segments: about 768 workgroups a pass, at least 2 chunks of 64 each
     assert lib.hla_backward_default_seg_chunks(4, 8, 2048) == 2
+    assert lib.hla_backward_default_seg_chunks(8, 16, 4096) == 11
     assert lib.hla_backward_default_seg_chunks(1, 1, 256) == 2
     assert lib.hla_backward_default_seg_chunks(1, 1, 100) == 2 or \
         lib.hla_backward_default_seg_chunks(1, 1, 100) == 1
     B, H, n, d = 4, 8, 2048, 64
     g = lib.hla_backward_default_seg_chunks(B, H, n)
     nseg = -(-n // (64 * g))
-    want = B * H * (nseg - 1) * d * d * 4 + 2 * B * H * n * d * 2
+    want = 2 * B * H * (nseg - 1) * d * d * 4 + 2 * B * H * n * d * 2
     assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16") == want
     assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32) == 2 * B * H * n * d * 4
     assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == 0
