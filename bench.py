@@ -94,8 +94,14 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
         per.setdefault(r["Kernel_Name"], []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     print(f"settle + warm-up steps skipped: {skip}; K = {K}")
+    # backward leg: its last `backward_steps` passes of la_ launches, by
+    # position within a pass (the pass order of hla_backward)
+    bwd = [r for r in rows if "la_" in r["Kernel_Name"]]
+    nb = (rec.get("backward") or {}).get("launches_per_step", 0)
+    Kb = (rec.get("backward") or {}).get("steps", 0)
     for name, us in per.items():
-        if not any(x in name for x in ("summary_kernel", "up_sweep_kernel", "forward_kernel")):
+        if "la_" in name or not any(x in name for x in ("summary_kernel", "up_sweep_kernel",
+                                                        "forward_kernel")):
             continue
         parts = {"timed": us[skip:skip + K], "stages": us[skip + K:skip + 2 * K],
                  "back-to-back": us[skip + 2 * K:skip + 3 * K]}
@@ -104,6 +110,28 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
             if v:
                 print(f"    {label:13s} n={len(v):5d} avg {statistics.fmean(v):8.2f} us"
                       f"  min {min(v):8.2f}  max {max(v):8.2f}")
+    if nb and Kb and len(bwd) >= nb * Kb:
+        last = bwd[-nb * Kb:]
+        print(f"backward: last {Kb} steps, {nb} launches each")
+        total = 0.0
+        for i in range(nb):
+            v = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last[i::nb]]
+            total += statistics.fmean(v)
+            print(f"    {i:2d} {kernel_key(last[i]['Kernel_Name']):20s} grid {last[i]['Grid_Size_X']:>8s}"
+                  f"  avg {statistics.fmean(v):8.2f} us")
+        print(f"    sum of averages {total:8.2f} us")
+
+
+def kernel_key(name: str) -> str:
+    """Short key of a stage kernel from its (mangled or demangled) name: the
+    forward path's hla2_/ahla_ kernels and the up-sweep, and the backward's
+    la_ kernels, whose two-slot (SYM) instances get a _sym suffix."""
+    import re
+    m = re.search(r"(hla2_|ahla_|la_)?(summary_kernel|up_sweep_kernel|forward_kernel)", name)
+    key = m.group(0)
+    if key.startswith("la_") and ("Lb1E" in name or "true>" in name):
+        key += "_sym"
+    return key
 
 
 def counters_summary(fetch_csv: str, write_csv: str) -> None:
@@ -145,7 +173,7 @@ def counters_summary(fetch_csv: str, write_csv: str) -> None:
     for short in ("summary_kernel", "up_sweep_kernel", "forward_kernel"):
         names = [n for n in fetch if short in n and n in write]
         for name in names:
-            key = re.search(r"(?:hla2_|ahla_)?" + short, name).group(0)
+            key = kernel_key(name)
             fb, wb = fetch[name] * 1024 * fs, write[name] * 1024 * ws
             rec[key] = {"FETCH_SIZE_KiB": round(fetch[name], 1),
                         "WRITE_SIZE_KiB": round(write[name], 1),
@@ -468,10 +496,14 @@ def main():
         bms = t_start.elapsed_time(t_end) / args.backward_steps
         # lean HBM floor: q, k, v, do read once and dq, dk, dv written once
         b_bytes = tokens * 7 * d * 2
-        backward = {"workload": f"HLA-2 backward (dq, dk, dv), B={B} H={H} n={n} d=dv={d} bf16, "
+        bnseg = -(-n // (64 * bseg))
+        backward = {"steps": args.backward_steps,
+                    "launches_per_step": 6 + 5 * (bnseg > 1),
+                    "workload": f"HLA-2 backward (dq, dk, dv), B={B} H={H} n={n} d=dv={d} bf16, "
                                 "q,k L2-normalised Gaussian, v and do ~ N(0,1)",
-                    "passes": "7 chunked linear-attention passes (chunk 64), each a segment-state "
-                              "launch and a main launch",
+                    "passes": "6 chunked linear-attention passes (chunk 64), each a main launch "
+                              "after a segment-state launch (the last pass reuses the first's "
+                              "states)",
                     "seg_chunks": bseg,
                     "ms_per_step": round(bms, 5), "tokens_per_s": round(tokens / (bms * 1e-3), 1),
                     "lean_bytes_per_step": b_bytes,

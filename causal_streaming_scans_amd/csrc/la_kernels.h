@@ -79,6 +79,9 @@ struct LaRegs {
     uint4 ra[NV], rb[NV], rc[NV];
     int l0;
 
+    // WITH_A = false (segment states) skips the a rows, which only the
+    // outputs read
+    template <bool WITH_A = true>
     __device__ __forceinline__ void load(const LaParams &p, size_t head_row, int first) {
         l0 = first;
         const T *A = static_cast<const T *>(p.a);
@@ -92,13 +95,13 @@ struct LaRegs {
             size_t row = head_row;
             if (idx < NVEC && l < p.n) row += (size_t)(p.reverse ? p.n - 1 - l : l);
             const size_t off = row * D + (idx < NVEC ? col : 0);
-            ra[i] = *reinterpret_cast<const uint4 *>(A + off);
+            if constexpr (WITH_A) ra[i] = *reinterpret_cast<const uint4 *>(A + off);
             rb[i] = *reinterpret_cast<const uint4 *>(B + off);
             rc[i] = *reinterpret_cast<const uint4 *>(Cv + off);
         }
     }
 
-    template <bool SYM>
+    template <bool WITH_A = true, bool SYM>
     __device__ __forceinline__ void store(LaLds<T, D, C, SYM> &s, int n) const {
         using TL = typename LaLds<T, D, C, SYM>::TR;
 #pragma unroll
@@ -112,15 +115,18 @@ struct LaRegs {
                 // select between two uint4 values kept the prefetch arrays in
                 // scratch memory instead of registers
                 const unsigned m = ok ? 0xffffffffu : 0u;
-                uint4 ua = ra[i], ub = rb[i], uc = rc[i];
-                ua.x &= m; ua.y &= m; ua.z &= m; ua.w &= m;
+                uint4 ub = rb[i], uc = rc[i];
                 ub.x &= m; ub.y &= m; ub.z &= m; ub.w &= m;
                 uc.x &= m; uc.y &= m; uc.z &= m; uc.w &= m;
-                *reinterpret_cast<uint4 *>(xa.v) = ua;
                 *reinterpret_cast<uint4 *>(xb.v) = ub;
                 *reinterpret_cast<uint4 *>(xc.v) = uc;
                 const int o = TL::off(r, col);
-                store16(s.a + o, xa);
+                if constexpr (WITH_A) {
+                    uint4 ua = ra[i];
+                    ua.x &= m; ua.y &= m; ua.z &= m; ua.w &= m;
+                    *reinterpret_cast<uint4 *>(xa.v) = ua;
+                    store16(s.a + o, xa);
+                }
                 store16(s.b + o, xb);
                 store16(s.c + o, xc);
                 const float w = s.pw[C - 1 - r];
@@ -138,6 +144,14 @@ struct LaRegs {
         }
     }
 };
+
+// four consecutive values of T from global memory, as floats
+__device__ __forceinline__ f32x4 load4f(const bf16 *p) {
+    union { uint2 u; bf16 h[4]; } x;
+    x.u = *reinterpret_cast<const uint2 *>(p);
+    return f32x4{(float)x.h[0], (float)x.h[1], (float)x.h[2], (float)x.h[3]};
+}
+__device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
 // acc[i][j] += sum_{k < K} M1[k][c1 + i] M2[k][c2 + j] for two row-major
 // [token][feature] LDS tiles: a product over the tokens, operands read with
@@ -227,15 +241,15 @@ void la_summary_kernel(LaParams p) {
     const int l_begin = seg * p.seg_len;
     const int l_end = min(p.n, l_begin + p.seg_len);
     LaRegs<T, D, C, Cfg::NT> regs;
-    regs.load(p, head_row, l_begin);
+    regs.template load<false>(p, head_row, l_begin);
     fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
     __syncthreads();
     const float gC = s.pw[C];
     LaState<T, D, C, SYM> S;
     S.zero();
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
-        regs.store(s, p.n);
-        if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
+        regs.template store<false>(s, p.n);
+        if (l0 + C < l_end) regs.template load<false>(p, head_row, l0 + C);
         __syncthreads();
         S.advance(s, gC, w);
         __syncthreads();
@@ -356,8 +370,9 @@ void la_forward_kernel(LaParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = acc1[r] + sc * acc2[r];
                 if (Add) {
+                    const f32x4 ad = load4f(Add + off);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] += to_f(Add[off + r]);
+                    for (int r = 0; r < 4; ++r) o[r] += ad[r];
                 }
                 store4(Out + off, o);
             }
