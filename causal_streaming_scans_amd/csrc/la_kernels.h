@@ -23,7 +23,7 @@
 // before its own (S <- g^len S + S_seg) and then runs its chunks.
 //
 // Per chunk of C tokens (one workgroup, NW = 4 waves):
-//   P     = D_g * tril(A_c B_c^T)                           (C x C, in LDS)
+//   P     = D_g * tril(A_c B_c^T)                           (C x C, in LDS, zeros above)
 //   out^T = C_c^T P^T + S^T A_c^T diag(g^(tau+1)) [+ add]   (written from registers)
 //   S     = g^C S + (B_c^T diag(g^(C-1-sigma))) C_c         (fp32, in registers)
 // Every chunk tile is stored row-major ([token][feature]) once; products that
@@ -32,35 +32,44 @@
 // next chunk's rows are loaded into registers while the current one computes.
 #pragma once
 
+#include <stddef.h>
+
 #include "device_common.h"
 #include "params.h"
 
 namespace hla {
 
+// Every array starts 16-byte aligned (the 8- and 16-byte LDS accesses need
+// it; the placeholders of the arrays only SYM uses would otherwise shift
+// everything after them by a few bytes, and misaligned LDS accesses cost
+// several times their aligned form).
 template <typename T, int D, int C, bool SYM>
 struct LaLds {
     using TR = LdsTile<T, D>;    // [C][D] chunk rows; [D][D] state copy St[j][i] = S[i][j]
     using TP = LdsTile<T, C>;    // [C][C] scores
-    T a[C * TR::LD];
-    T b[C * TR::LD];
-    T c[C * TR::LD];
-    T bw[C * TR::LD];            // g^(C-1-sigma) b_sigma
-    T cw[SYM ? C * TR::LD : 1];  // g^(C-1-sigma) c_sigma (SYM)
-    T p[C * TP::LD];
-    T p2[SYM ? C * TP::LD : 1];  // D_g * tril(A C^T) (SYM)
-    T st[D * TR::LD];
-    float pw[C + 1];             // g^e, e = 0..C
+    alignas(16) T a[C * TR::LD];
+    alignas(16) T b[C * TR::LD];
+    alignas(16) T c[C * TR::LD];
+    alignas(16) T bw[C * TR::LD];            // g^(C-1-sigma) b_sigma
+    alignas(16) T cw[SYM ? C * TR::LD : 1];  // g^(C-1-sigma) c_sigma (SYM)
+    alignas(16) T p[C * TP::LD];
+    alignas(16) T p2[SYM ? C * TP::LD : 1];  // D_g * tril(A C^T) (SYM)
+    alignas(16) T st[D * TR::LD];
+    alignas(16) float pw[C + 1];             // g^e, e = 0..C
 };
 
 template <typename T, int D, int C, bool SYM>
 struct LaCfg {
+    using Lds = LaLds<T, D, C, SYM>;
+    static_assert(offsetof(Lds, p) % 16 == 0 && offsetof(Lds, st) % 16 == 0, "LDS tiles 16-byte aligned");
     static constexpr int NW = 4, NT = NW * kWave;
     static constexpr int TR = C / 16;          // token tiles per chunk
     static constexpr int TD = D / 16;          // feature tiles
     static constexpr int NS = TD * TD;         // state tiles
     static constexpr int SPW = (NS + NW - 1) / NW;   // state tiles per wave
-    static constexpr int NTRI = TR * (TR + 1) / 2;   // lower-triangular score tiles
+    static constexpr int NSC = TR * TR;              // score tiles
     static constexpr int NOUT = TR * TD;             // output tiles
+    static_assert(NSC % NW == 0 && NOUT % NW == 0, "tiles dealt evenly to the waves");
     static constexpr int blocks() {
         constexpr size_t lds = sizeof(LaLds<T, D, C, SYM>);
         return lds <= 52 * 1024 ? 3 : (lds <= 78 * 1024 ? 2 : 1);
@@ -171,6 +180,22 @@ __device__ __forceinline__ f32x4 mma_tt(f32x4 acc, const float *M1, int c1, cons
     return acc;
 }
 
+// acc[i][j] += sum_{sigma < K} M[sigma][c1 + i] P[r2 + j][sigma]: M a
+// row-major [token][feature] tile read with the transposing LDS read, P a
+// row-major [token][token] score tile read along its rows.
+template <typename TL, typename TPL, int K>
+__device__ __forceinline__ f32x4 mma_cp(f32x4 acc, const bf16 *M, int c1, const bf16 *P, int r2) {
+    const int l = lane_id();
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+        const bf16x8 pv = *reinterpret_cast<const bf16x8 *>(P + TPL::off(r2 + (l & 15), k + 8 * (l >> 4)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_op8_tt<TL>(M, k, c1), pv, acc, 0, 0, 0);
+    }
+    return acc;
+}
+template <typename TL, typename TPL, int K>
+__device__ __forceinline__ f32x4 mma_cp(f32x4 acc, const float *M, int c1, const float *P, int r2);
+
 // 16-deep operand whose four k-values are consecutive in a row of an LdsTile
 // matrix: lane l reads row row0 + l%16, columns col0 + 4g .. +3.
 template <typename TL>
@@ -182,6 +207,13 @@ template <typename TL>
 __device__ __forceinline__ Frag16<float> ld_frag_row(const float *M, int row0, int col0) {
     const int l = lane_id();
     return Frag16<float>{*reinterpret_cast<const f32x4 *>(M + TL::off(row0 + (l & 15), col0 + 4 * (l >> 4)))};
+}
+
+template <typename TL, typename TPL, int K>
+__device__ __forceinline__ f32x4 mma_cp(f32x4 acc, const float *M, int c1, const float *P, int r2) {
+#pragma unroll
+    for (int k = 0; k < K; k += 16) acc = mma16(acc, ld_frag_tt<TL>(M, k, c1), ld_frag_row<TPL>(P, r2, k));
+    return acc;
 }
 
 // The state tiles of this wave: tile m = wave + NW*i covers S rows
@@ -320,43 +352,38 @@ void la_forward_kernel(LaParams p) {
         if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
         __syncthreads();
         // scores, transposed in registers so each lane holds four consecutive
-        // sigma of one tau: lower-triangular tiles (ti >= tj) of D_g * (A B^T)
-        for (int t = w; t < Cfg::NTRI; t += Cfg::NW) {
-            int ti = 0;
-            while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-            const int tj = t - ti * (ti + 1) / 2;
+        // sigma of one tau: every tile of D_g * (A B^T), the ones above the
+        // diagonal masked to zero, so the output products below run over
+        // the whole chunk with no per-tile bounds and every loop has
+        // compile-time trip counts
+#pragma unroll
+        for (int i = 0; i < Cfg::NSC / Cfg::NW; ++i) {
+            const int t = w + Cfg::NW * i;
+            const int ti = t / Cfg::TR, tj = t % Cfg::TR;
             RowFrags<T, D> fa;
             fa.template load_t<TR>(s.a + 16 * ti * TR::LD);
             const int tau = 16 * ti + cl;
             f32x4 acc = mma_nt_ft<TR, D>(zero4(), s.b + 16 * tj * TR::LD, fa);
+            f32x4 acc2;
+            if constexpr (SYM) acc2 = mma_nt_ft<TR, D>(zero4(), s.c + 16 * tj * TR::LD, fa);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int sg = 16 * tj + 4 * gq + r;
-                acc[r] = tau >= sg ? acc[r] * s.pw[tau - sg] : 0.f;
+                const float wt = tau >= sg ? s.pw[tau >= sg ? tau - sg : 0] : 0.f;
+                acc[r] *= wt;
+                if constexpr (SYM) acc2[r] *= wt;
             }
             store4(s.p + TP::off(tau, 16 * tj + 4 * gq), acc);
-            if constexpr (SYM) {
-                f32x4 acc2 = mma_nt_ft<TR, D>(zero4(), s.c + 16 * tj * TR::LD, fa);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int sg = 16 * tj + 4 * gq + r;
-                    acc2[r] = tau >= sg ? acc2[r] * s.pw[tau - sg] : 0.f;
-                }
-                store4(s.p2 + TP::off(tau, 16 * tj + 4 * gq), acc2);
-            }
+            if constexpr (SYM) store4(s.p2 + TP::off(tau, 16 * tj + 4 * gq), acc2);
         }
         __syncthreads();
         // outputs, transposed: lane holds features 4gq..4gq+3 of token cl
-        for (int t = w; t < Cfg::NOUT; t += Cfg::NW) {
+#pragma unroll
+        for (int i = 0; i < Cfg::NOUT / Cfg::NW; ++i) {
+            const int t = w + Cfg::NW * i;
             const int tj = t % Cfg::TD, ti = t / Cfg::TD;   // feature tile, token tile
-            f32x4 acc1 = zero4();
-            for (int ks = 0; ks <= ti; ++ks) {
-                acc1 = mma16(acc1, ld_frag_tt<TR>(s.c, 16 * ks, 16 * tj),
-                             ld_frag_row<TP>(s.p, 16 * ti, 16 * ks));
-                if constexpr (SYM)
-                    acc1 = mma16(acc1, ld_frag_tt<TR>(s.b, 16 * ks, 16 * tj),
-                                 ld_frag_row<TP>(s.p2, 16 * ti, 16 * ks));
-            }
+            f32x4 acc1 = mma_cp<TR, TP, C>(zero4(), s.c, 16 * tj, s.p, 16 * ti);
+            if constexpr (SYM) acc1 = mma_cp<TR, TP, C>(acc1, s.b, 16 * tj, s.p2, 16 * ti);
             RowFrags<T, D> fa;
             fa.template load_t<TR>(s.a + 16 * ti * TR::LD);
             const f32x4 acc2 = mma_nt_ft<TR, D>(zero4(), s.st + 16 * tj * TR::LD, fa);
