@@ -232,9 +232,11 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
 // through Z (K is both key and value there): dQ += LA_g(dZ, K, K),
 //            dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ), the two slots in one
 //            pass with one state (the kernels' SYM form).
-// Six passes in that dependency order; Z and dZ live in the workspace.  The
-// first and last passes share b = c = K and the decay g, so the segment
-// states of the first are kept and reused by the last.
+// dZ and dV read one state (sum dO Q^T and its transpose) and share two
+// inputs, so they run as one pass (the kernels' DUAL form): five passes in
+// dependency order; Z and dZ live in the workspace.  The first and last
+// passes share b = c = K and the decay g, so the segment states of the first
+// are kept and reused by the last.
 
 int hla_backward_default_seg_chunks(int B, int H, int n) {
     if (B < 1 || H < 1 || n < 1) return 1;
@@ -271,8 +273,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (variant != HLA_HLA2 || d != dv) return HLA_ERR_UNSUPPORTED;
-    LaLaunch la, la_sym;
-    if (!lookup_la(dtype, d, &la, &la_sym)) return HLA_ERR_UNSUPPORTED;
+    LaLaunches la;
+    if (!lookup_la(dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
     if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
@@ -303,17 +305,22 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     p2 = p1;
     for (int h = 0; h < kMaxDecayHeads; ++h) p2.gamma[h] = p1.gamma[h] * p1.gamma[h];
 
+    enum Form { PLAIN, SYM, DUAL };
     struct Pass {
-        LaParams *base; const void *a, *b, *c, *add; void *out; int rev; bool sym;
-        float *sums; bool summaries;
+        LaParams *base; const void *a, *b, *c, *add; void *out; int rev; Form form;
+        float *sums; bool summaries; const void *a2; void *out2;
     };
-    const Pass passes[6] = {
-        {&p1, q, k, k, nullptr, Z, 0, false, sums_kk, true},        // Z  = LA_g(Q, K, K)
-        {&p2, dout, v, Z, nullptr, dq, 0, false, sums, true},       // dQ = LA_g2(dO, V, Z)
-        {&p2, v, dout, q, nullptr, dZ, 1, false, sums, true},       // dZ = RLA_g2(V, dO, Q)
-        {&p2, Z, q, dout, nullptr, dv_out, 1, false, sums, true},   // dV = RLA_g2(Z, Q, dO)
-        {&p1, k, dZ, q, nullptr, dk, 1, true, sums, true},          // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
-        {&p1, dZ, k, k, dq, dq, 0, false, sums_kk, false},          // dQ += LA_g(dZ, K, K)
+    const Pass passes[5] = {
+        // Z  = LA_g(Q, K, K)
+        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr},
+        // dQ = LA_g2(dO, V, Z)
+        {&p2, dout, v, Z, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr},
+        // dZ = RLA_g2(V, dO, Q) and dV = RLA_g2(Z, Q, dO): one state, sum dO Q^T
+        {&p2, v, dout, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out},
+        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr},
+        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
+        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr},
     };
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (const Pass &ps : passes) {
@@ -323,9 +330,12 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         p.c = ps.c;
         p.add = ps.add;
         p.out = ps.out;
+        p.a2 = ps.a2;
+        p.out2 = ps.out2;
         p.reverse = ps.rev;
         p.sums = ps.sums;
-        if ((ps.sym ? la_sym : la)(p, s, ps.summaries) != hipSuccess) return HLA_ERR_DEVICE;
+        const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
+        if (fn(p, s, ps.summaries) != hipSuccess) return HLA_ERR_DEVICE;
     }
     return HLA_OK;
 }

@@ -5,42 +5,65 @@
 
 namespace hla {
 
-template <typename T, int D, bool SYM>
+template <typename T, int D, bool SYM, bool DUAL>
 hipError_t launch_la(const LaParams &p, hipStream_t s, bool summaries) {
     constexpr int C = kLaChunk;
-    using Cfg = LaCfg<T, D, C, SYM>;
+    using Cfg = LaCfg<T, D, C, SYM, DUAL>;
     if (summaries && p.nseg > 1) {
-        hipLaunchKernelGGL((la_summary_kernel<T, D, C, SYM>), dim3((p.nseg - 1) * p.BH),
+        // a DUAL pass's state is the plain state of its b, c
+        hipLaunchKernelGGL((la_summary_kernel<T, D, C, SYM, false>), dim3((p.nseg - 1) * p.BH),
                            dim3(Cfg::NT), 0, s, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((la_forward_kernel<T, D, C, SYM>), dim3(p.nseg * p.BH), dim3(Cfg::NT), 0, s, p);
+    hipLaunchKernelGGL((la_forward_kernel<T, D, C, SYM, DUAL>), dim3(p.nseg * p.BH), dim3(Cfg::NT),
+                       0, s, p);
     return hipGetLastError();
 }
 
+// The DUAL form as two plain passes, for shapes whose fused LDS layout does
+// not fit: LA(a, b, c) into out, then LA(a2, c, b) into out2.
 template <typename T, int D>
-bool la_pair(LaLaunch *plain, LaLaunch *sym) {
-    static_assert(sizeof(LaLds<T, D, kLaChunk, true>) <= 160 * 1024, "LDS");
-    *plain = launch_la<T, D, false>;
-    *sym = launch_la<T, D, true>;
+hipError_t launch_la_dual_split(const LaParams &p, hipStream_t s, bool summaries) {
+    hipError_t e = launch_la<T, D, false, false>(p, s, summaries);
+    if (e != hipSuccess) return e;
+    LaParams q = p;
+    q.a = p.a2;
+    q.b = p.c;
+    q.c = p.b;
+    q.add = nullptr;
+    q.out = p.out2;
+    q.a2 = nullptr;
+    q.out2 = nullptr;
+    return launch_la<T, D, false, false>(q, s, true);
+}
+
+template <typename T, int D>
+bool la_set(LaLaunches *out) {
+    static_assert(sizeof(LaLds<T, D, kLaChunk, true, false>) <= 160 * 1024, "LDS");
+    out->plain = launch_la<T, D, false, false>;
+    out->sym = launch_la<T, D, true, false>;
+    if constexpr (sizeof(LaLds<T, D, kLaChunk, false, true>) <= 160 * 1024)
+        out->dual = launch_la<T, D, false, true>;
+    else
+        out->dual = launch_la_dual_split<T, D>;
     return true;
 }
 
-bool lookup_la(int dtype, int d, LaLaunch *plain, LaLaunch *sym) {
+bool lookup_la(int dtype, int d, LaLaunches *out) {
     if (dtype == 0) {
         switch (d) {
-            case 16: return la_pair<float, 16>(plain, sym);
-            case 32: return la_pair<float, 32>(plain, sym);
-            case 64: return la_pair<float, 64>(plain, sym);
+            case 16: return la_set<float, 16>(out);
+            case 32: return la_set<float, 32>(out);
+            case 64: return la_set<float, 64>(out);
             default: return false;
         }
     }
     switch (d) {
-        case 16: return la_pair<bf16, 16>(plain, sym);
-        case 32: return la_pair<bf16, 32>(plain, sym);
-        case 64: return la_pair<bf16, 64>(plain, sym);
-        case 128: return la_pair<bf16, 128>(plain, sym);
+        case 16: return la_set<bf16, 16>(out);
+        case 32: return la_set<bf16, 32>(out);
+        case 64: return la_set<bf16, 64>(out);
+        case 128: return la_set<bf16, 128>(out);
         default: return false;
     }
 }

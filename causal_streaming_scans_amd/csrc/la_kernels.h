@@ -3,12 +3,15 @@
 //
 //   out_t = add_t + sum_{s <= t} g^(t-s) (a_t . b_s) c_s                 (plain)
 //   out_t = add_t + sum_{s <= t} g^(t-s) [(a_t . b_s) c_s + (a_t . c_s) b_s]  (SYM)
+//   out_t as plain, and out2_t = sum_{s <= t} g^(t-s) (a2_t . c_s) b_s       (DUAL)
 //
 // and the same over the reversed sequence (s >= t, weight g^(s-t)) when
 // `reverse` is set: logical token l is physical row n-1-l, so an anti-causal
 // pass is the causal pass run backwards through memory.  SYM is the
 // gradient of a pass whose key and value are one tensor (K in Z = LA(Q, K, K)):
-// both slots in one pass, with one state S = sum w (b c^T + c b^T).
+// both slots in one pass, with one state S = sum w (b c^T + c b^T).  DUAL is
+// two passes whose states are transposes of each other (keys and values
+// swapped), which share the staged b, c and the state.
 //
 // The gradient of HLA-2 is a chain of such passes.  With z_t = S^K_t q_t =
 // sum_{i<=t} g^(t-i) (q_t . k_i) k_i (the key read-out of page section "1. HLA
@@ -43,24 +46,26 @@ namespace hla {
 // it; the placeholders of the arrays only SYM uses would otherwise shift
 // everything after them by a few bytes, and misaligned LDS accesses cost
 // several times their aligned form).
-template <typename T, int D, int C, bool SYM>
+template <typename T, int D, int C, bool SYM, bool DUAL>
 struct LaLds {
     using TR = LdsTile<T, D>;    // [C][D] chunk rows; [D][D] state copy St[j][i] = S[i][j]
     using TP = LdsTile<T, C>;    // [C][C] scores
     alignas(16) T a[C * TR::LD];
+    alignas(16) T a2[DUAL ? C * TR::LD : 8];  // second queries (DUAL)
     alignas(16) T b[C * TR::LD];
     alignas(16) T c[C * TR::LD];
     alignas(16) T bw[C * TR::LD];            // g^(C-1-sigma) b_sigma
-    alignas(16) T cw[SYM ? C * TR::LD : 1];  // g^(C-1-sigma) c_sigma (SYM)
+    alignas(16) T cw[SYM ? C * TR::LD : 8];  // g^(C-1-sigma) c_sigma (SYM)
     alignas(16) T p[C * TP::LD];
-    alignas(16) T p2[SYM ? C * TP::LD : 1];  // D_g * tril(A C^T) (SYM)
+    alignas(16) T p2[SYM || DUAL ? C * TP::LD : 8];  // D_g * tril(A C^T) (SYM), D_g * tril(A2 C^T) (DUAL)
     alignas(16) T st[D * TR::LD];
+    alignas(16) T ss[DUAL ? D * TR::LD : 8];  // the state itself, Ss[i][j] = S[i][j] (DUAL)
     alignas(16) float pw[C + 1];             // g^e, e = 0..C
 };
 
-template <typename T, int D, int C, bool SYM>
+template <typename T, int D, int C, bool SYM, bool DUAL>
 struct LaCfg {
-    using Lds = LaLds<T, D, C, SYM>;
+    using Lds = LaLds<T, D, C, SYM, DUAL>;
     static_assert(offsetof(Lds, p) % 16 == 0 && offsetof(Lds, st) % 16 == 0, "LDS tiles 16-byte aligned");
     static constexpr int NW = 4, NT = NW * kWave;
     static constexpr int TR = C / 16;          // token tiles per chunk
@@ -71,7 +76,7 @@ struct LaCfg {
     static constexpr int NOUT = TR * TD;             // output tiles
     static_assert(NSC % NW == 0 && NOUT % NW == 0, "tiles dealt evenly to the waves");
     static constexpr int blocks() {
-        constexpr size_t lds = sizeof(LaLds<T, D, C, SYM>);
+        constexpr size_t lds = sizeof(LaLds<T, D, C, SYM, DUAL>);
         return lds <= 52 * 1024 ? 3 : (lds <= 78 * 1024 ? 2 : 1);
     }
 };
@@ -81,11 +86,12 @@ struct LaCfg {
 // columns of a row, so one load instruction covers whole rows.  Rows past
 // the end of the sequence load row 0 of the head (in bounds) and are stored
 // as zeros.
-template <typename T, int D, int C, int NT>
+template <typename T, int D, int C, int NT, bool A2>
 struct LaRegs {
     static constexpr int VE = Vec16<T>::N, VPR = D / VE, NVEC = C * VPR;
     static constexpr int NV = (NVEC + NT - 1) / NT;
     uint4 ra[NV], rb[NV], rc[NV];
+    uint4 ra2[A2 ? NV : 1];
     int l0;
 
     // WITH_A = false (segment states) skips the a rows, which only the
@@ -96,6 +102,7 @@ struct LaRegs {
         const T *A = static_cast<const T *>(p.a);
         const T *B = static_cast<const T *>(p.b);
         const T *Cv = static_cast<const T *>(p.c);
+        const T *A2p = static_cast<const T *>(p.a2);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
@@ -105,14 +112,15 @@ struct LaRegs {
             if (idx < NVEC && l < p.n) row += (size_t)(p.reverse ? p.n - 1 - l : l);
             const size_t off = row * D + (idx < NVEC ? col : 0);
             if constexpr (WITH_A) ra[i] = *reinterpret_cast<const uint4 *>(A + off);
+            if constexpr (WITH_A && A2) ra2[i] = *reinterpret_cast<const uint4 *>(A2p + off);
             rb[i] = *reinterpret_cast<const uint4 *>(B + off);
             rc[i] = *reinterpret_cast<const uint4 *>(Cv + off);
         }
     }
 
-    template <bool WITH_A = true, bool SYM>
-    __device__ __forceinline__ void store(LaLds<T, D, C, SYM> &s, int n) const {
-        using TL = typename LaLds<T, D, C, SYM>::TR;
+    template <bool WITH_A = true, bool SYM, bool DUAL>
+    __device__ __forceinline__ void store(LaLds<T, D, C, SYM, DUAL> &s, int n) const {
+        using TL = typename LaLds<T, D, C, SYM, DUAL>::TR;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int idx = threadIdx.x + i * NT;
@@ -135,6 +143,14 @@ struct LaRegs {
                     ua.x &= m; ua.y &= m; ua.z &= m; ua.w &= m;
                     *reinterpret_cast<uint4 *>(xa.v) = ua;
                     store16(s.a + o, xa);
+                }
+                if constexpr (WITH_A && A2) {
+                    static_assert(!A2 || DUAL, "second queries only in the DUAL layout");
+                    uint4 ua = ra2[i];
+                    ua.x &= m; ua.y &= m; ua.z &= m; ua.w &= m;
+                    Vec16<T> x2;
+                    *reinterpret_cast<uint4 *>(x2.v) = ua;
+                    store16(s.a2 + o, x2);
                 }
                 store16(s.b + o, xb);
                 store16(s.c + o, xc);
@@ -218,10 +234,10 @@ __device__ __forceinline__ f32x4 mma_cp(f32x4 acc, const float *M, int c1, const
 
 // The state tiles of this wave: tile m = wave + NW*i covers S rows
 // 16*(m / TD) .., columns 16*(m % TD) ..
-template <typename T, int D, int C, bool SYM>
+template <typename T, int D, int C, bool SYM, bool DUAL>
 struct LaState {
-    using Cfg = LaCfg<T, D, C, SYM>;
-    using TL = typename LaLds<T, D, C, SYM>::TR;
+    using Cfg = LaCfg<T, D, C, SYM, DUAL>;
+    using TL = typename LaLds<T, D, C, SYM, DUAL>::TR;
     f32x4 acc[Cfg::SPW];
 
     __device__ __forceinline__ void zero() {
@@ -229,7 +245,7 @@ struct LaState {
         for (int i = 0; i < Cfg::SPW; ++i) acc[i] = zero4();
     }
     // S <- g^C S + Bw^T C (+ Cw^T B): products of the staged chunk
-    __device__ __forceinline__ void advance(const LaLds<T, D, C, SYM> &s, float gC, int w) {
+    __device__ __forceinline__ void advance(const LaLds<T, D, C, SYM, DUAL> &s, float gC, int w) {
 #pragma unroll
         for (int i = 0; i < Cfg::SPW; ++i) {
             const int m = w + Cfg::NW * i;
@@ -245,7 +261,7 @@ struct LaState {
         }
     }
     // St[j][i] = S[i][j], rounded to T
-    __device__ __forceinline__ void store_copy(LaLds<T, D, C, SYM> &s, int w) const {
+    __device__ __forceinline__ void store_copy(LaLds<T, D, C, SYM, DUAL> &s, int w) const {
         const int l = lane_id(), g = l >> 4;
 #pragma unroll
         for (int i = 0; i < Cfg::SPW; ++i) {
@@ -253,6 +269,11 @@ struct LaState {
             if (m < Cfg::NS) {
                 const int si = m / Cfg::TD, sj = m % Cfg::TD;
                 store4(s.st + TL::off(16 * sj + (l & 15), 16 * si + 4 * g), acc[i]);
+                if constexpr (DUAL) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        s.ss[TL::off(16 * si + 4 * g + r, 16 * sj + (l & 15))] = from_f<T>(acc[i][r]);
+                }
             }
         }
     }
@@ -260,11 +281,11 @@ struct LaState {
 
 // Summary of segment seg (< nseg-1): its state from zero, decayed to its end,
 // into p.sums.  Grid: (nseg-1) * BH workgroups, heads fastest.
-template <typename T, int D, int C, bool SYM>
-__global__ __launch_bounds__((LaCfg<T, D, C, SYM>::NT), (LaCfg<T, D, C, SYM>::blocks()))
+template <typename T, int D, int C, bool SYM, bool DUAL>
+__global__ __launch_bounds__((LaCfg<T, D, C, SYM, DUAL>::NT), (LaCfg<T, D, C, SYM, DUAL>::blocks()))
 void la_summary_kernel(LaParams p) {
-    using Cfg = LaCfg<T, D, C, SYM>;
-    __shared__ LaLds<T, D, C, SYM> s;
+    using Cfg = LaCfg<T, D, C, SYM, DUAL>;
+    __shared__ LaLds<T, D, C, SYM, DUAL> s;
     const int L = blockIdx.x;
     const int bh = L % p.BH, seg = L / p.BH;
     const int w = wave_id();
@@ -272,12 +293,12 @@ void la_summary_kernel(LaParams p) {
     const size_t head_row = (size_t)bh * p.n;
     const int l_begin = seg * p.seg_len;
     const int l_end = min(p.n, l_begin + p.seg_len);
-    LaRegs<T, D, C, Cfg::NT> regs;
+    LaRegs<T, D, C, Cfg::NT, DUAL> regs;
     regs.template load<false>(p, head_row, l_begin);
     fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
     __syncthreads();
     const float gC = s.pw[C];
-    LaState<T, D, C, SYM> S;
+    LaState<T, D, C, SYM, DUAL> S;
     S.zero();
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
         regs.template store<false>(s, p.n);
@@ -301,11 +322,11 @@ void la_summary_kernel(LaParams p) {
 }
 
 // Main pass over segment seg.  Grid: nseg * BH workgroups, heads fastest.
-template <typename T, int D, int C, bool SYM>
-__global__ __launch_bounds__((LaCfg<T, D, C, SYM>::NT), (LaCfg<T, D, C, SYM>::blocks()))
+template <typename T, int D, int C, bool SYM, bool DUAL>
+__global__ __launch_bounds__((LaCfg<T, D, C, SYM, DUAL>::NT), (LaCfg<T, D, C, SYM, DUAL>::blocks()))
 void la_forward_kernel(LaParams p) {
-    using Cfg = LaCfg<T, D, C, SYM>;
-    using Ls = LaLds<T, D, C, SYM>;
+    using Cfg = LaCfg<T, D, C, SYM, DUAL>;
+    using Ls = LaLds<T, D, C, SYM, DUAL>;
     using TR = typename Ls::TR;
     using TP = typename Ls::TP;
     __shared__ Ls s;
@@ -317,12 +338,12 @@ void la_forward_kernel(LaParams p) {
     const size_t head_row = (size_t)bh * p.n;
     const int l_begin = seg * p.seg_len;
     const int l_end = min(p.n, l_begin + p.seg_len);
-    LaRegs<T, D, C, Cfg::NT> regs;
+    LaRegs<T, D, C, Cfg::NT, DUAL> regs;
     regs.load(p, head_row, l_begin);
     fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
 
     // carried state: the summaries of the segments before this one, in order
-    LaState<T, D, C, SYM> S;
+    LaState<T, D, C, SYM, DUAL> S;
     S.zero();
     if (seg > 0) {
         const float gL = pow_int(g, p.seg_len);
@@ -366,15 +387,20 @@ void la_forward_kernel(LaParams p) {
             f32x4 acc = mma_nt_ft<TR, D>(zero4(), s.b + 16 * tj * TR::LD, fa);
             f32x4 acc2;
             if constexpr (SYM) acc2 = mma_nt_ft<TR, D>(zero4(), s.c + 16 * tj * TR::LD, fa);
+            if constexpr (DUAL) {
+                RowFrags<T, D> fa2;
+                fa2.template load_t<TR>(s.a2 + 16 * ti * TR::LD);
+                acc2 = mma_nt_ft<TR, D>(zero4(), s.c + 16 * tj * TR::LD, fa2);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int sg = 16 * tj + 4 * gq + r;
                 const float wt = tau >= sg ? s.pw[tau >= sg ? tau - sg : 0] : 0.f;
                 acc[r] *= wt;
-                if constexpr (SYM) acc2[r] *= wt;
+                if constexpr (SYM || DUAL) acc2[r] *= wt;
             }
             store4(s.p + TP::off(tau, 16 * tj + 4 * gq), acc);
-            if constexpr (SYM) store4(s.p2 + TP::off(tau, 16 * tj + 4 * gq), acc2);
+            if constexpr (SYM || DUAL) store4(s.p2 + TP::off(tau, 16 * tj + 4 * gq), acc2);
         }
         __syncthreads();
         // outputs, transposed: lane holds features 4gq..4gq+3 of token cl
@@ -402,6 +428,21 @@ void la_forward_kernel(LaParams p) {
                     for (int r = 0; r < 4; ++r) o[r] += ad[r];
                 }
                 store4(Out + off, o);
+            }
+            if constexpr (DUAL) {
+                // out2 = LA(a2, c, b): scores A2 C^T, values b, state S^T
+                const f32x4 b1 = mma_cp<TR, TP, C>(zero4(), s.b, 16 * tj, s.p2, 16 * ti);
+                RowFrags<T, D> fa2;
+                fa2.template load_t<TR>(s.a2 + 16 * ti * TR::LD);
+                const f32x4 b2 = mma_nt_ft<TR, D>(zero4(), s.ss + 16 * tj * TR::LD, fa2);
+                if (lt < l_end) {
+                    const float sc = s.pw[tau + 1];
+                    const size_t row = head_row + (size_t)(p.reverse ? p.n - 1 - lt : lt);
+                    f32x4 o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = b1[r] + sc * b2[r];
+                    store4(static_cast<T *>(p.out2) + row * D + 16 * tj + 4 * gq, o);
+                }
             }
         }
         S.advance(s, gC, w);

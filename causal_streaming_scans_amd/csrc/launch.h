@@ -33,10 +33,14 @@ bool lookup_forward_bf16_128(bool ahla, int chunk, bool decay, FwdKernels *out);
 // Chunked first-order linear attention (la_kernels.h): the segment-state
 // launch (when p.nseg > 1 and `summaries`; otherwise p.sums must already hold
 // the states of these b, c and decay) and the main launch, on one stream;
-// `plain` runs LA(a, b, c), `sym` the two-slot form LA(a, b, c) + LA(a, c, b).
+// `plain` runs LA(a, b, c), `sym` the two-slot form LA(a, b, c) + LA(a, c, b),
+// `dual` LA(a, b, c) into out and LA(a2, c, b) into out2.
 constexpr int kLaChunk = 64;
 typedef hipError_t (*LaLaunch)(const LaParams &, hipStream_t, bool summaries);
-bool lookup_la(int dtype, int d, LaLaunch *plain, LaLaunch *sym);
+struct LaLaunches {
+    LaLaunch plain, sym, dual;
+};
+bool lookup_la(int dtype, int d, LaLaunches *out);
 
 // fill dst[0:count) with src[0:count), or with zeros when src is null
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s);

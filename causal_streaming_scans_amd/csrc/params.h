@@ -91,6 +91,8 @@ struct LaParams {
     const void *c;      // [BH][n][D] values
     const void *add;    // [BH][n][D] added to the output, or null (may alias out)
     void *out;          // [BH][n][D]
+    const void *a2;     // [BH][n][D] queries of the second output (DUAL form), else null
+    void *out2;         // [BH][n][D] second output (DUAL form), else null
     float *sums;        // [BH][nseg-1][D*D] segment states (nseg > 1)
     int BH, H, n;
     int seg_len;        // tokens per segment, a multiple of the chunk
