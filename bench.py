@@ -498,12 +498,12 @@ def main():
         b_bytes = tokens * 7 * d * 2
         bnseg = -(-n // (64 * bseg))
         backward = {"steps": args.backward_steps,
-                    "launches_per_step": 6 + 5 * (bnseg > 1),
+                    "launches_per_step": 5 + 4 * (bnseg > 1),
                     "workload": f"HLA-2 backward (dq, dk, dv), B={B} H={H} n={n} d=dv={d} bf16, "
                                 "q,k L2-normalised Gaussian, v and do ~ N(0,1)",
-                    "passes": "6 chunked linear-attention passes (chunk 64), each a main launch "
+                    "passes": "5 chunked linear-attention passes (chunk 64), each a main launch "
                               "after a segment-state launch (the last pass reuses the first's "
-                              "states)",
+                              "states); dZ and dV share one pass, dK's two slots another",
                     "seg_chunks": bseg,
                     "ms_per_step": round(bms, 5), "tokens_per_s": round(tokens / (bms * 1e-3), 1),
                     "lean_bytes_per_step": b_bytes,

@@ -190,9 +190,10 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * attentions, Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), where
  * LA_g(A, B, C)_t = sum_{s<=t} g^(t-s) (a_t . b_s) c_s.  The chain rule through
  * each gives linear attentions of the same form, causal or anti-causal; the
- * library runs six chunked passes (chunk 64 tokens, segments of seg_chunks
- * chunks in parallel, each pass one segment-state launch and one main
- * launch), recomputing Z, and keeps Z and dZ in the workspace.
+ * library runs five chunked passes (chunk 64 tokens, segments of seg_chunks
+ * chunks in parallel, each pass a segment-state launch and a main launch;
+ * the last pass reuses the first one's segment states), recomputing Z, and
+ * keeps Z and dZ in the workspace.
  *
  * q, k, v, dout  device, [B][H][n][d] (d == dv), element type = dtype
  * dq, dk, dv_out  device outputs, same layout and type; may not alias the
