@@ -237,6 +237,12 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
 // dependency order; Z and dZ live in the workspace.  The first and last
 // passes share b = c = K and the decay g, so the segment states of the first
 // are kept and reused by the last.
+//
+// AHLA is LA(Q, K, LA(Q, K, V)) without decay: Y = LA(Q, K, V), O = LA(Q, K, Y).
+// Its gradient: dQ = LA(dO, Y, K) + LA(dY, V, K), dY = RLA(K, Q, dO),
+// dK = RLA(Y, dO, Q) + RLA(V, dY, Q), dV = RLA(K, Q, dY); the pairs
+// (dY, first dK term) and (dV, second dK term) each share one state and run
+// as DUAL passes.
 
 int hla_backward_default_seg_chunks(int B, int H, int n) {
     if (B < 1 || H < 1 || n < 1) return 1;
@@ -254,7 +260,7 @@ int hla_backward_default_seg_chunks(int B, int H, int n) {
 
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
                                     int seg_chunks) {
-    if (variant != HLA_HLA2 || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
+    if ((variant != HLA_HLA2 && variant != HLA_AHLA) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
         (dtype != HLA_F32 && dtype != HLA_BF16))
         return 0;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
@@ -272,7 +278,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
-    if (variant != HLA_HLA2 || d != dv) return HLA_ERR_UNSUPPORTED;
+    if ((variant != HLA_HLA2 && variant != HLA_AHLA) || d != dv) return HLA_ERR_UNSUPPORTED;
     LaLaunches la;
     if (!lookup_la(dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
@@ -308,22 +314,38 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     enum Form { PLAIN, SYM, DUAL };
     struct Pass {
         LaParams *base; const void *a, *b, *c, *add; void *out; int rev; Form form;
-        float *sums; bool summaries; const void *a2; void *out2;
+        float *sums; bool summaries; const void *a2; void *out2; const void *add2;
     };
-    const Pass passes[5] = {
+    // HLA-2 (Z in the workspace's first tensor, dZ in the second)
+    const Pass hla2_passes[5] = {
         // Z  = LA_g(Q, K, K)
-        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr},
+        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
         // dQ = LA_g2(dO, V, Z)
-        {&p2, dout, v, Z, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr},
+        {&p2, dout, v, Z, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
         // dZ = RLA_g2(V, dO, Q) and dV = RLA_g2(Z, Q, dO): one state, sum dO Q^T
-        {&p2, v, dout, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out},
+        {&p2, v, dout, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
         // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
-        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr},
+        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
         // dQ += LA_g(dZ, K, K), with the segment states of the first pass
-        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr},
+        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
     };
+    // AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y and dY in the workspace)
+    const Pass ahla_passes[5] = {
+        // Y  = LA(Q, K, V)
+        {&p1, q, k, v, nullptr, Z, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        // dQ = LA(dO, Y, K)
+        {&p1, dout, Z, k, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        // dY = RLA(K, Q, dO) and dK = RLA(Y, dO, Q): one state, sum Q dO^T
+        {&p1, k, q, dout, nullptr, dZ, 1, DUAL, sums, true, Z, dk, nullptr},
+        // dV = RLA(K, Q, dY) and dK += RLA(V, dY, Q): one state, sum Q dY^T
+        {&p1, k, q, dZ, nullptr, dv_out, 1, DUAL, sums, true, v, dk, dk},
+        // dQ += LA(dY, V, K)
+        {&p1, dZ, v, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+    };
+    const Pass *passes = variant == HLA_AHLA ? ahla_passes : hla2_passes;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (const Pass &ps : passes) {
+    for (int i = 0; i < 5; ++i) {
+        const Pass &ps = passes[i];
         LaParams p = *ps.base;
         p.a = ps.a;
         p.b = ps.b;
@@ -332,6 +354,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         p.out = ps.out;
         p.a2 = ps.a2;
         p.out2 = ps.out2;
+        p.add2 = ps.add2;
         p.reverse = ps.rev;
         p.sums = ps.sums;
         const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;

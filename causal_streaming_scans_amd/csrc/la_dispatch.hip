@@ -31,10 +31,11 @@ hipError_t launch_la_dual_split(const LaParams &p, hipStream_t s, bool summaries
     q.a = p.a2;
     q.b = p.c;
     q.c = p.b;
-    q.add = nullptr;
+    q.add = p.add2;
     q.out = p.out2;
     q.a2 = nullptr;
     q.out2 = nullptr;
+    q.add2 = nullptr;
     return launch_la<T, D, false, false>(q, s, true);
 }
 

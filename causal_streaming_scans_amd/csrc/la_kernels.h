@@ -3,7 +3,7 @@
 //
 //   out_t = add_t + sum_{s <= t} g^(t-s) (a_t . b_s) c_s                 (plain)
 //   out_t = add_t + sum_{s <= t} g^(t-s) [(a_t . b_s) c_s + (a_t . c_s) b_s]  (SYM)
-//   out_t as plain, and out2_t = sum_{s <= t} g^(t-s) (a2_t . c_s) b_s       (DUAL)
+//   out_t as plain, and out2_t = add2_t + sum_{s <= t} g^(t-s) (a2_t . c_s) b_s  (DUAL)
 //
 // and the same over the reversed sequence (s >= t, weight g^(s-t)) when
 // `reverse` is set: logical token l is physical row n-1-l, so an anti-causal
@@ -441,7 +441,13 @@ void la_forward_kernel(LaParams p) {
                     f32x4 o;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) o[r] = b1[r] + sc * b2[r];
-                    store4(static_cast<T *>(p.out2) + row * D + 16 * tj + 4 * gq, o);
+                    const size_t off = row * D + 16 * tj + 4 * gq;
+                    if (p.add2) {
+                        const f32x4 ad = load4f(static_cast<const T *>(p.add2) + off);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) o[r] += ad[r];
+                    }
+                    store4(static_cast<T *>(p.out2) + off, o);
                 }
             }
         }

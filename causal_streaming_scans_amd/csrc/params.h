@@ -93,6 +93,7 @@ struct LaParams {
     void *out;          // [BH][n][D]
     const void *a2;     // [BH][n][D] queries of the second output (DUAL form), else null
     void *out2;         // [BH][n][D] second output (DUAL form), else null
+    const void *add2;   // [BH][n][D] added to out2, or null (may alias out2)
     float *sums;        // [BH][nseg-1][D*D] segment states (nseg > 1)
     int BH, H, n;
     int seg_len;        // tokens per segment, a multiple of the chunk

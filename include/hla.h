@@ -178,13 +178,14 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
                     const float *gamma_host, float *state, void *stream);
 
 /*
- * Backward pass (vector-Jacobian product) of the HLA-2 operator, for
- * training through the chunk-parallel form (page section "4. Entrenamiento
- * Paralelo mediante Escaneos Asociativos"; the operator of section "1. HLA de
- * Segundo Orden", decay per "Contribuciones Clave" item 2).  Given the
- * upstream gradient dout = dL/do, writes dq = dL/dq, dk = dL/dk, dv = dL/dv
- * of the HLA_HLA2 output o = tril(L L^T) V (with decay g_h when gamma_host is
- * given) computed from zero state.
+ * Backward pass (vector-Jacobian product) of the HLA-2 and AHLA operators,
+ * for training through the chunk-parallel form (page section "4.
+ * Entrenamiento Paralelo mediante Escaneos Asociativos"; the operators of
+ * sections "1. HLA de Segundo Orden" and "2. ... (AHLA)", decay per
+ * "Contribuciones Clave" item 2).  Given the upstream gradient dout = dL/do,
+ * writes dq = dL/dq, dk = dL/dk, dv = dL/dv of the HLA_HLA2 output
+ * o = tril(L L^T) V (with decay g_h when gamma_host is given) or of the
+ * HLA_AHLA output o = (L L) V, computed from zero state.
  *
  * Method: with z_t = S^K_t q_t, the operator is two chained causal linear
  * attentions, Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), where
@@ -193,7 +194,8 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * library runs five chunked passes (chunk 64 tokens, segments of seg_chunks
  * chunks in parallel, each pass a segment-state launch and a main launch;
  * the last pass reuses the first one's segment states), recomputing Z, and
- * keeps Z and dZ in the workspace.
+ * keeps Z and dZ in the workspace.  AHLA is LA(Q, K, LA(Q, K, V)): five
+ * passes likewise, with Y = LA(Q, K, V) and dY in the workspace.
  *
  * q, k, v, dout  device, [B][H][n][d] (d == dv), element type = dtype
  * dq, dk, dv_out  device outputs, same layout and type; may not alias the
@@ -204,8 +206,8 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * workspace      device buffer of at least hla_backward_workspace_bytes()
  *                bytes (contents ignored on entry, unspecified on return)
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
- * dZ are kept in dtype.  Supported: variant HLA_HLA2 only (other variants:
- * HLA_ERR_UNSUPPORTED), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
+ * dZ are kept in dtype.  Supported: variants HLA_HLA2 and HLA_AHLA (the
+ * ratio variants: HLA_ERR_UNSUPPORTED; AHLA with a decay: likewise), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
  * d in {16, 32, 64}.  Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);

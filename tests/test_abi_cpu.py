@@ -186,13 +186,16 @@ def test_backward_workspace_bytes(lib):
     assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16") == want
     assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32) == 2 * B * H * n * d * 4
     assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == 0
-    assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == 0
+    assert hla.backward_workspace_bytes("ahla_ratio", B, H, n, d, d) == 0
+    assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == want
 
 
 def test_backward_validation(lib):
     assert _bwd(lib, n=0) == OK                      # nothing to do, nothing enqueued
     assert _bwd(lib, variant=HLA2_RATIO) == ERR_UNSUP
-    assert _bwd(lib, variant=AHLA) == ERR_UNSUP
+    assert _bwd(lib, variant=AHLA_RATIO) == ERR_UNSUP
+    assert _bwd(lib, variant=AHLA, gamma=[0.9, 0.9]) == ERR_UNSUP   # AHLA has no decay
+    assert _bwd(lib, variant=AHLA, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=9) == ERR_ARG
     assert _bwd(lib, dvd=32) == ERR_UNSUP
     assert _bwd(lib, d=48, dvd=48) == ERR_UNSUP

@@ -16,14 +16,14 @@ from hla_testlib import TOL, from_dev, rel_l2, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_backward(x, do, B, H, dtype, gamma=None, seg_chunks=0):
+def run_backward(x, do, B, H, dtype, gamma=None, seg_chunks=0, variant="hla2"):
     import torch
     import causal_streaming_scans_amd as hla
     n, d = x["q"].shape[1], x["q"].shape[2]
     shp = (B, H, n, d)
     dq, dk, dv = hla.hla_backward(to_dev(x["q"], dtype, shp), to_dev(x["k"], dtype, shp),
                                   to_dev(x["v"], dtype, shp), to_dev(do, dtype, shp),
-                                  gamma=gamma, seg_chunks=seg_chunks)
+                                  variant=variant, gamma=gamma, seg_chunks=seg_chunks)
     torch.cuda.synchronize()
     return tuple(from_dev(t).reshape(B * H, n, d) for t in (dq, dk, dv))
 
@@ -109,7 +109,9 @@ def test_backward_decay_n16384_prefix_and_euler():
         lhs = float(np.sum(xin.astype(np.float64) * g))
         scale = float(np.linalg.norm(xin) * np.linalg.norm(g))
         say(f"  euler {name}: <x, dx> {lhs:.6e} vs {deg} <do, o> {deg * ref:.6e} (scale {scale:.3e})")
-        assert abs(lhs - deg * ref) <= 1e-2 * scale
+        # bf16 operands leave the inner product within a few tenths of a
+        # percent; a dropped or mis-signed term moves it by its own size
+        assert abs(lhs - deg * ref) <= 3e-2 * abs(deg * ref) + 1e-6 * scale
 
 
 def test_many_heads_without_decay():
@@ -137,3 +139,62 @@ def test_many_heads_without_decay():
     heads = [0, 255, 256, 299]
     want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, H, heads=heads)
     check(tuple(g[heads] for g in got), want, "bf16", "H=300")
+
+
+AHLA_SMALL = [
+    # dtype, d, n, H, seg_chunks
+    ("f32", 16, 200, 2, 0),
+    ("f32", 32, 130, 1, 1),
+    ("f32", 64, 257, 2, 1),
+    ("bf16", 16, 333, 2, 1),
+    ("bf16", 64, 65, 2, 0),
+    ("bf16", 64, 450, 3, 2),
+    ("bf16", 128, 300, 2, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,n,H,seg", AHLA_SMALL)
+def test_ahla_backward_small(dtype, d, n, H, seg):
+    """AHLA gradients (o = tril(QK^T) tril(QK^T) V, page section "2. ...
+    (AHLA)") against the oracle's chain rule on the matrix form."""
+    say(f"[ahla backward] dtype {dtype} d {d} n {n} H {H} seg_chunks {seg}")
+    B = 1
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="normal_scaled" if dtype == "f32" else "l2norm",
+                      seed=750 + d + n)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=850 + n)
+    got = run_backward(x, do, B, H, dtype, None, seg, variant="ahla")
+    want = BW.ahla_vjp_batched(x["q"], x["k"], x["v"], do)
+    check(got, want, dtype, f"ahla {dtype} d{d} n{n}")
+
+
+def test_ahla_backward_n65536_prefix_and_euler():
+    """The AHLA workload B=1 H=32 n=65536 d=dv=64 bf16 at full size, in the
+    default launch configuration: (1) do zero from token m on, the first m
+    tokens against the oracle of the prefix on two heads, exact zeros after
+    it; (2) a dense do, Euler's identity for degree 2 in q, 2 in k, 1 in v,
+    with o from the serial fp64 oracle."""
+    w = I.WORKLOADS["ahla_n65536"]
+    say(f"[ahla backward] workload {w.name}")
+    x = I.workload_inputs("ahla_n65536", decode_tokens=0)
+    BH, m = w.B * w.H, 1024
+    do = I.make_upstream_grad(BH, w.n, w.dv, w.dtype, seed=w.seed + 100)
+    do_cut = do.copy()
+    do_cut[:, m:] = 0
+    got = run_backward(x, do_cut, w.B, w.H, w.dtype, variant="ahla")
+    for g in got:
+        assert np.all(g[:, m:] == 0)
+    heads = [0, BH - 1]
+    want = BW.ahla_vjp_batched(x["q"][:, :m], x["k"][:, :m], x["v"][:, :m], do_cut[:, :m],
+                               heads=heads)
+    check(tuple(g[heads, :m] for g in got), want, w.dtype, "ahla_n65536 prefix")
+    got = run_backward(x, do, w.B, w.H, w.dtype, variant="ahla")
+    o = oracle.ahla(x["q"], x["k"], x["v"])
+    ref = float(np.sum(do.astype(np.float64) * o))
+    for name, xin, g, deg in (("q", x["q"], got[0], 2), ("k", x["k"], got[1], 2),
+                              ("v", x["v"], got[2], 1)):
+        lhs = float(np.sum(xin.astype(np.float64) * g))
+        scale = float(np.linalg.norm(xin) * np.linalg.norm(g))
+        say(f"  euler {name}: <x, dx> {lhs:.6e} vs {deg} <do, o> {deg * ref:.6e} (scale {scale:.3e})")
+        # bf16 operands leave the inner product within a few tenths of a
+        # percent; a dropped or mis-signed term moves it by its own size
+        assert abs(lhs - deg * ref) <= 3e-2 * abs(deg * ref) + 1e-6 * scale
