@@ -110,9 +110,10 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
             if v:
                 print(f"    {label:13s} n={len(v):5d} avg {statistics.fmean(v):8.2f} us"
                       f"  min {min(v):8.2f}  max {max(v):8.2f}")
-    if nb and Kb and len(bwd) >= nb * Kb:
-        last = bwd[-nb * Kb:]
-        print(f"backward: last {Kb} steps, {nb} launches each")
+    if nb and Kb and len(bwd) >= nb * (10 + Kb):
+        # the HLA-2 leg: 10 untimed calls, then Kb timed ones (the ratio leg follows)
+        last = bwd[10 * nb:(10 + Kb) * nb]
+        print(f"backward: the {Kb} timed HLA-2 backward calls, {nb} launches each")
         total = 0.0
         for i in range(nb):
             v = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last[i::nb]]
@@ -476,27 +477,31 @@ def main():
     # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
     # unnormalised HLA-2 (the variant the backward supports), q, k L2-normalised
     # Gaussian rows, v and the upstream gradient ~ N(0, 1), bf16
-    backward = None
+    backward = backward_ratio = None
     if args.backward_steps > 0:
+        bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
+        bnseg = -(-n // (64 * bseg))
+
+        def time_backward(variant, qb, kb, vb, dob):
+            bplan = hla.BackwardPlan(qb, kb, vb, dob, variant=variant, seg_chunks=bseg)
+            for _ in range(10):
+                bplan.run()
+            torch.cuda.synchronize()
+            t_start.record()
+            for _ in range(args.backward_steps):
+                bplan.run()
+            t_end.record()
+            torch.cuda.synchronize()
+            return t_start.elapsed_time(t_end) / args.backward_steps
+
+        # lean HBM floor: q, k, v, do read once and dq, dk, dv written once
+        b_bytes = tokens * 7 * d * 2
         xb = I.make_inputs(B, H, n, d, dv, dtype="bf16", dist="l2norm", seed=w.seed + 500)
         gb = I.make_upstream_grad(B * H, n, dv, "bf16", seed=w.seed + 501)
         qb, kb, vb = (to_dev(xb[key], (B, H, n, d)) for key in ("q", "k", "v"))
         dob = to_dev(gb, (B, H, n, dv))
         del xb, gb
-        bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
-        bplan = hla.BackwardPlan(qb, kb, vb, dob, variant="hla2", seg_chunks=bseg)
-        for _ in range(10):
-            bplan.run()
-        torch.cuda.synchronize()
-        t_start.record()
-        for _ in range(args.backward_steps):
-            bplan.run()
-        t_end.record()
-        torch.cuda.synchronize()
-        bms = t_start.elapsed_time(t_end) / args.backward_steps
-        # lean HBM floor: q, k, v, do read once and dq, dk, dv written once
-        b_bytes = tokens * 7 * d * 2
-        bnseg = -(-n // (64 * bseg))
+        bms = time_backward("hla2", qb, kb, vb, dob)
         backward = {"steps": args.backward_steps,
                     "launches_per_step": 5 + 4 * (bnseg > 1),
                     "workload": f"HLA-2 backward (dq, dk, dv), B={B} H={H} n={n} d=dv={d} bf16, "
@@ -509,7 +514,21 @@ def main():
                     "lean_bytes_per_step": b_bytes,
                     "lean_hbm_frac": round(b_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] backward: {bms:.4f} ms/step, {tokens / (bms * 1e-3) / 1e9:.3f} G tokens/s")
-        del qb, kb, vb, dob, bplan
+        del qb, kb, vb
+        # the benchmark's own variant and inputs: ratio HLA-2 on q, k, v above
+        rms = time_backward("hla2_ratio", q, k, v, dob)
+        backward_ratio = {"steps": args.backward_steps,
+                          "workload": f"ratio HLA-2 backward, the forward's inputs (B={B} H={H} "
+                                      f"n={n} d=dv={d} bf16), do ~ N(0,1)",
+                          "passes": "8 chunked linear-attention passes and a row-wise kernel: "
+                                    "num and den recomputed, then the HLA-2 passes with "
+                                    "upstream do/den and one pass for den's term",
+                          "seg_chunks": bseg,
+                          "ms_per_step": round(rms, 5),
+                          "tokens_per_s": round(tokens / (rms * 1e-3), 1),
+                          "lean_hbm_frac": round(b_bytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] ratio backward: {rms:.4f} ms/step, {tokens / (rms * 1e-3) / 1e9:.3f} G tokens/s")
+        del dob
 
     # ---- CPU baseline: the oracle on the same inputs, all heads
     cpu = None
@@ -554,6 +573,7 @@ def main():
         "parity_spot_rel_l2": rel,
         "decode": decode,
         "backward": backward,
+        "backward_ratio": backward_ratio,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

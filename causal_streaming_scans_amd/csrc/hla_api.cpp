@@ -258,16 +258,28 @@ int hla_backward_default_seg_chunks(int B, int H, int n) {
     return (int)g;
 }
 
+// tensors of [B][H][n][d] the backward keeps in its workspace: Z and dZ (Y
+// and dY for AHLA); the ratio form adds dO / den, the rows (e, 0, ..., 0)
+// and the unit rows (1, 0, ..., 0), and with bf16 inputs runs in fp32 on
+// widened copies of q, k, v, dO and fp32 gradients (seven more)
+static int backward_tensors(int variant, int dtype) {
+    if (variant != HLA_HLA2_RATIO) return 2;
+    return dtype == HLA_BF16 ? 12 : 5;
+}
+static size_t backward_elem_bytes(int variant, int dtype) {
+    return (variant == HLA_HLA2_RATIO || dtype == HLA_F32) ? 4 : 2;
+}
+
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
                                     int seg_chunks) {
-    if ((variant != HLA_HLA2 && variant != HLA_AHLA) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
+    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
         (dtype != HLA_F32 && dtype != HLA_BF16))
         return 0;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
     const long nseg = num_segments(n, kLaChunk, g);
-    const size_t esz = dtype == HLA_BF16 ? 2 : 4;
+    const size_t esz = backward_elem_bytes(variant, dtype);
     const size_t sums = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    return 2 * sums + 2 * (size_t)B * H * n * d * esz;
+    return 2 * sums + (size_t)backward_tensors(variant, dtype) * B * H * n * d * esz;
 }
 
 hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
@@ -278,26 +290,33 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
-    if ((variant != HLA_HLA2 && variant != HLA_AHLA) || d != dv) return HLA_ERR_UNSUPPORTED;
+    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || d != dv)
+        return HLA_ERR_UNSUPPORTED;
+    // the ratio form runs its passes in fp32 (its gradient with respect to q
+    // and k is a small difference of large terms, which bf16 intermediates
+    // do not resolve)
+    const int run_dtype = variant == HLA_HLA2_RATIO ? HLA_F32 : dtype;
     LaLaunches la;
-    if (!lookup_la(dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
+    if (!lookup_la(run_dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
     if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
     if ((long)kLaChunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, kLaChunk, g);
     if (nseg * B * H > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    if ((long)B * H * n / 4 > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;   // row-wise grid
     const size_t need = hla_backward_workspace_bytes(variant, B, H, n, d, dv, dtype, g);
     if (!workspace) return HLA_ERR_NULL;
     if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
 
-    const size_t esz = dtype == HLA_BF16 ? 2 : 4;
+    const size_t esz = backward_elem_bytes(variant, dtype);
     const size_t sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
     char *ws = static_cast<char *>(workspace);
     float *sums_kk = reinterpret_cast<float *>(ws);               // states of K K^T (g)
     float *sums = reinterpret_cast<float *>(ws + sums_bytes);     // the other passes'
+    const size_t tensor_bytes = (size_t)B * H * n * d * esz;
     void *Z = ws + 2 * sums_bytes;
-    void *dZ = ws + 2 * sums_bytes + (size_t)B * H * n * d * esz;
+    void *dZ = ws + 2 * sums_bytes + tensor_bytes;
 
     LaParams p1, p2;   // decay g and g^2
     memset(&p1, 0, sizeof(p1));
@@ -342,10 +361,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         // dQ += LA(dY, V, K)
         {&p1, dZ, v, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
     };
-    const Pass *passes = variant == HLA_AHLA ? ahla_passes : hla2_passes;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int i = 0; i < 5; ++i) {
-        const Pass &ps = passes[i];
+    auto run = [&](const Pass &ps) {
         LaParams p = *ps.base;
         p.a = ps.a;
         p.b = ps.b;
@@ -358,7 +375,83 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         p.reverse = ps.rev;
         p.sums = ps.sums;
         const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
-        if (fn(p, s, ps.summaries) != hipSuccess) return HLA_ERR_DEVICE;
+        return fn(p, s, ps.summaries) == hipSuccess;
+    };
+    if (variant != HLA_HLA2_RATIO) {
+        const Pass *passes = variant == HLA_AHLA ? ahla_passes : hla2_passes;
+        for (int i = 0; i < 5; ++i)
+            if (!run(passes[i])) return HLA_ERR_DEVICE;
+        return HLA_OK;
+    }
+
+    // Ratio form, o = num / den with den the v == 1 sum.  With G = dO / den and
+    // e = -(dO . o) / den per row, the gradient is that of num with upstream
+    // G, plus den's: dq += e_t u_t, u = LA_g2(ONE1, ONE1, Z) (u_t = sum_j
+    // g^(2(t-j)) z_j), and dZ += RLA_g2(ONE1, E1, Q) (sum_{t>=j} g^(2(t-j)) e_t q_t),
+    // where ONE1 has rows (1, 0, ..., 0) and E1 rows (e_t, 0, ..., 0).  den
+    // itself is q_t . u_t and num = LA_g2(Q, Z, V).  u lives in dv_out and num
+    // in dZ's buffer until the passes that overwrite them.
+    void *G = ws + 2 * sums_bytes + 2 * tensor_bytes;
+    void *E1 = ws + 2 * sums_bytes + 3 * tensor_bytes;
+    void *ONE1 = ws + 2 * sums_bytes + 4 * tensor_bytes;
+    const long rows = (long)B * H * n;
+    const long count = rows * d;
+    // bf16 inputs: every pass below reads and writes fp32 copies
+    void *dq_out = dq, *dk_out = dk, *dv_user = dv_out;
+    if (dtype == HLA_BF16) {
+        void *w32[7];
+        for (int i = 0; i < 7; ++i) w32[i] = ws + 2 * sums_bytes + (5 + i) * tensor_bytes;
+        const void *src[4] = {q, k, v, dout};
+        for (int i = 0; i < 4; ++i)
+            if (launch_convert(src[i], w32[i], count, true, s) != hipSuccess) return HLA_ERR_DEVICE;
+        q = w32[0];
+        k = w32[1];
+        v = w32[2];
+        dout = w32[3];
+        dq = w32[4];
+        dk = w32[5];
+        dv_out = w32[6];
+    }
+    if (la.unit_column(ONE1, rows, s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass pre[3] = {
+        // Z  = LA_g(Q, K, K)
+        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
+        // u  = LA_g2(ONE1, ONE1, Z)
+        {&p2, ONE1, ONE1, Z, nullptr, dv_out, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        // num = LA_g2(Q, Z, V)
+        {&p2, q, Z, v, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+    };
+    for (const Pass &ps : pre)
+        if (!run(ps)) return HLA_ERR_DEVICE;
+    RatioPrepParams rp;
+    rp.q = q;
+    rp.u = dv_out;
+    rp.num = dZ;
+    rp.dout = dout;
+    rp.g = G;
+    rp.e1 = E1;
+    rp.dq = dq;
+    rp.rows = rows;
+    if (la.ratio_prep(rp, s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass post[5] = {
+        // dQ = e u + LA_g2(G, V, Z)
+        {&p2, G, v, Z, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        // dZ = RLA_g2(V, G, Q) and dV = RLA_g2(Z, Q, G)
+        {&p2, v, G, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
+        // dZ += RLA_g2(ONE1, E1, Q)
+        {&p2, ONE1, E1, q, dZ, dZ, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
+        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
+        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
+    };
+    for (const Pass &ps : post)
+        if (!run(ps)) return HLA_ERR_DEVICE;
+    if (dtype == HLA_BF16) {
+        void *dst[3] = {dq_out, dk_out, dv_user};
+        const void *src[3] = {dq, dk, dv_out};
+        for (int i = 0; i < 3; ++i)
+            if (launch_convert(src[i], dst[i], count, false, s) != hipSuccess) return HLA_ERR_DEVICE;
     }
     return HLA_OK;
 }

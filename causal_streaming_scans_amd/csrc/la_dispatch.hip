@@ -40,7 +40,25 @@ hipError_t launch_la_dual_split(const LaParams &p, hipStream_t s, bool summaries
 }
 
 template <typename T, int D>
+hipError_t launch_unit_column(void *out, long rows, hipStream_t s) {
+    long blocks = (rows * D + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL((unit_column_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<T *>(out), rows);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_ratio_prep(const RatioPrepParams &p, hipStream_t s) {
+    const long blocks = (p.rows + 3) / 4;   // one wave per row, four waves per block
+    hipLaunchKernelGGL((ratio_prep_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
 bool la_set(LaLaunches *out) {
+    out->unit_column = launch_unit_column<T, D>;
+    out->ratio_prep = launch_ratio_prep<T, D>;
     static_assert(sizeof(LaLds<T, D, kLaChunk, true, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
     out->sym = launch_la<T, D, true, false>;
@@ -49,6 +67,20 @@ bool la_set(LaLaunches *out) {
     else
         out->dual = launch_la_dual_split<T, D>;
     return true;
+}
+
+hipError_t launch_convert(const void *src, void *dst, long count, bool to_f32, hipStream_t s) {
+    const long count4 = count / 4;
+    long blocks = (count4 + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) return hipSuccess;
+    if (to_f32)
+        hipLaunchKernelGGL(widen_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const bf16 *>(src), static_cast<float *>(dst), count4);
+    else
+        hipLaunchKernelGGL(narrow_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const float *>(src), static_cast<bf16 *>(dst), count4);
+    return hipGetLastError();
 }
 
 bool lookup_la(int dtype, int d, LaLaunches *out) {

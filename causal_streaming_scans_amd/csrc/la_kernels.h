@@ -458,3 +458,95 @@ void la_forward_kernel(LaParams p) {
 }
 
 }  // namespace hla
+
+namespace hla {
+
+// ------------------------------------------------ ratio form of the backward
+//
+// With o = num / den (num = LA_{g^2}(Q, Z, V), den its v == 1 sum), the
+// gradient is that of num with the upstream gradient dO / den, plus the
+// terms of den with e_t = -(dO_t . o_t) / den_t.  The ones column of den is
+// carried by a tensor whose rows are the unit vector (1, 0, ..., 0) (ONE1),
+// and e by one whose rows are (e_t, 0, ..., 0) (E1), so that LA passes of
+// the same kernels form u_t = sum_j g^(2(t-j)) z_j = LA(ONE1, ONE1, Z)_t and
+// r_j = sum_{t>=j} g^(2(t-j)) e_t q_t = RLA(ONE1, E1, Q)_j.
+
+// rows of ONE1 (a unit first column) into out: [rows][D]
+template <typename T, int D>
+__global__ __launch_bounds__(256) void unit_column_kernel(T *out, long rows) {
+    const long total = rows * D;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
+        out[i] = from_f<T>(i % D == 0 ? 1.f : 0.f);
+}
+
+// One wave per row t:
+//   den = q . u,  o = num / den,  g = dO / den,  e = -(dO . o) / den;
+//   writes g into G, (e, 0, ..., 0) into E1, and e u into dq.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void ratio_prep_kernel(RatioPrepParams p) {
+    constexpr int PER = (D + kWave - 1) / kWave;
+    const long row = (long)blockIdx.x * (256 / kWave) + wave_id();
+    if (row >= p.rows) return;
+    const int l = lane_id();
+    const size_t base = (size_t)row * D;
+    const T *q = static_cast<const T *>(p.q) + base;
+    const T *u = static_cast<const T *>(p.u) + base;
+    const T *num = static_cast<const T *>(p.num) + base;
+    const T *dout = static_cast<const T *>(p.dout) + base;
+    float qv[PER], uv[PER], nv[PER], dv[PER];
+    float den = 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int c = l + kWave * j;
+        const bool ok = c < D;
+        qv[j] = ok ? to_f(q[c]) : 0.f;
+        uv[j] = ok ? to_f(u[c]) : 0.f;
+        nv[j] = ok ? to_f(num[c]) : 0.f;
+        dv[j] = ok ? to_f(dout[c]) : 0.f;
+        den += qv[j] * uv[j];
+    }
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) den += __shfl_xor(den, m, kWave);
+    const float inv = 1.f / den;
+    float dot = 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) dot += dv[j] * nv[j] * inv;
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) dot += __shfl_xor(dot, m, kWave);
+    const float e = -dot * inv;
+    T *G = static_cast<T *>(p.g) + base;
+    T *E1 = static_cast<T *>(p.e1) + base;
+    T *dq = static_cast<T *>(p.dq) + base;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int c = l + kWave * j;
+        if (c < D) {
+            G[c] = from_f<T>(dv[j] * inv);
+            E1[c] = from_f<T>(c == 0 ? e : 0.f);
+            dq[c] = from_f<T>(e * uv[j]);
+        }
+    }
+}
+
+}  // namespace hla
+
+namespace hla {
+
+// bf16 <-> fp32 copies of whole tensors (the ratio backward keeps its passes
+// in fp32, see hla_api.cpp); count is a multiple of 4
+__global__ __launch_bounds__(256) void widen_kernel(const bf16 *src, float *dst, long count4) {
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count4; i += stride) {
+        union { uint2 u; bf16 h[4]; } x;
+        x.u = reinterpret_cast<const uint2 *>(src)[i];
+        reinterpret_cast<f32x4 *>(dst)[i] = f32x4{(float)x.h[0], (float)x.h[1], (float)x.h[2], (float)x.h[3]};
+    }
+}
+__global__ __launch_bounds__(256) void narrow_kernel(const float *src, bf16 *dst, long count4) {
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < count4; i += stride)
+        store4(dst + 4 * i, reinterpret_cast<const f32x4 *>(src)[i]);
+}
+
+}  // namespace hla

@@ -39,8 +39,12 @@ constexpr int kLaChunk = 64;
 typedef hipError_t (*LaLaunch)(const LaParams &, hipStream_t, bool summaries);
 struct LaLaunches {
     LaLaunch plain, sym, dual;
+    hipError_t (*unit_column)(void *out, long rows, hipStream_t);   // rows (1, 0, ..., 0)
+    hipError_t (*ratio_prep)(const RatioPrepParams &, hipStream_t);
 };
 bool lookup_la(int dtype, int d, LaLaunches *out);
+// bf16 -> fp32 (to_f32) or fp32 -> bf16 copy of count values (a multiple of 4)
+hipError_t launch_convert(const void *src, void *dst, long count, bool to_f32, hipStream_t s);
 
 // fill dst[0:count) with src[0:count), or with zeros when src is null
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s);

@@ -102,6 +102,13 @@ struct LaParams {
     float gamma[kMaxDecayHeads];   // decay of head h for this pass
 };
 
+// Row-wise step of the ratio backward (la_kernels.h, ratio_prep_kernel).
+struct RatioPrepParams {
+    const void *q, *u, *num, *dout;   // [rows][D]
+    void *g, *e1, *dq;                // [rows][D]
+    long rows;
+};
+
 // Decode step arguments.
 struct StepParams {
     const void *q;   // [BH][D]

@@ -184,8 +184,9 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * sections "1. HLA de Segundo Orden" and "2. ... (AHLA)", decay per
  * "Contribuciones Clave" item 2).  Given the upstream gradient dout = dL/do,
  * writes dq = dL/dq, dk = dL/dk, dv = dL/dv of the HLA_HLA2 output
- * o = tril(L L^T) V (with decay g_h when gamma_host is given) or of the
- * HLA_AHLA output o = (L L) V, computed from zero state.
+ * o = tril(L L^T) V (with decay g_h when gamma_host is given), of its ratio
+ * form HLA_HLA2_RATIO, or of the HLA_AHLA output o = (L L) V, computed from
+ * zero state.
  *
  * Method: with z_t = S^K_t q_t, the operator is two chained causal linear
  * attentions, Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), where
@@ -195,7 +196,10 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * chunks in parallel, each pass a segment-state launch and a main launch;
  * the last pass reuses the first one's segment states), recomputing Z, and
  * keeps Z and dZ in the workspace.  AHLA is LA(Q, K, LA(Q, K, V)): five
- * passes likewise, with Y = LA(Q, K, V) and dY in the workspace.
+ * passes likewise, with Y = LA(Q, K, V) and dY in the workspace.  The ratio
+ * form recomputes num and den (two more passes and a row-wise kernel), runs
+ * the passes with dO / den as upstream gradient, and adds the denominator's
+ * terms through one more pass; it keeps three more tensors in the workspace.
  *
  * q, k, v, dout  device, [B][H][n][d] (d == dv), element type = dtype
  * dq, dk, dv_out  device outputs, same layout and type; may not alias the
@@ -206,8 +210,9 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * workspace      device buffer of at least hla_backward_workspace_bytes()
  *                bytes (contents ignored on entry, unspecified on return)
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
- * dZ are kept in dtype.  Supported: variants HLA_HLA2 and HLA_AHLA (the
- * ratio variants: HLA_ERR_UNSUPPORTED; AHLA with a decay: likewise), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
+ * dZ are kept in dtype.  Supported: variants HLA_HLA2, HLA_HLA2_RATIO and
+ * HLA_AHLA (HLA_AHLA_RATIO and AHLA with a decay: HLA_ERR_UNSUPPORTED; the
+ * ratio form needs nonzero denominators, as the forward), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
  * d in {16, 32, 64}.  Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);

@@ -198,3 +198,44 @@ def test_ahla_backward_n65536_prefix_and_euler():
         # bf16 operands leave the inner product within a few tenths of a
         # percent; a dropped or mis-signed term moves it by its own size
         assert abs(lhs - deg * ref) <= 3e-2 * abs(deg * ref) + 1e-6 * scale
+
+
+RATIO_SMALL = [
+    # dtype, d, n, H, decay, seg_chunks
+    ("f32", 16, 200, 2, False, 0),
+    ("f32", 16, 200, 2, True, 1),
+    ("f32", 64, 257, 2, True, 1),
+    ("bf16", 32, 130, 2, False, 1),
+    ("bf16", 64, 450, 3, True, 2),
+    ("bf16", 16, 200, 1, False, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,n,H,decay,seg", RATIO_SMALL)
+def test_ratio_backward_small(dtype, d, n, H, decay, seg):
+    """Gradients of the ratio-normalised HLA-2 (numerator over the v == 1
+    denominator, page section "1. HLA de Segundo Orden"); positive q, k keep
+    the denominators away from zero.  With bf16 inputs the library runs these
+    passes in fp32 (the gradient is a small difference of large terms)."""
+    say(f"[ratio backward] dtype {dtype} d {d} n {n} H {H} decay {decay} seg_chunks {seg}")
+    B = 1
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos", seed=770 + d + n,
+                      decay=decay)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=870 + n)
+    got = run_backward(x, do, B, H, dtype, x["gamma"], seg, variant="hla2_ratio")
+    want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, H, x["gamma"], ratio=True)
+    check(got, want, dtype, f"ratio {dtype} d{d} n{n}")
+
+
+def test_ratio_backward_n4096_sampled_heads():
+    """The benchmark workload -- ratio HLA-2, B=8 H=16 n=4096 d=dv=64 bf16 --
+    in the default launch configuration; the oracle's chain rule on the
+    first and last head, element by element."""
+    w = I.WORKLOADS["ratio_n4096"]
+    say(f"[ratio backward] workload {w.name}")
+    x = I.workload_inputs("ratio_n4096")
+    do = I.make_upstream_grad(w.B * w.H, w.n, w.dv, w.dtype, seed=w.seed + 100)
+    got = run_backward(x, do, w.B, w.H, w.dtype, variant="hla2_ratio")
+    heads = [0, w.B * w.H - 1]
+    want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, w.H, ratio=True, heads=heads)
+    check(tuple(g[heads] for g in got), want, w.dtype, "ratio_n4096 heads 0,127")
