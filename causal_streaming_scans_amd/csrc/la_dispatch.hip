@@ -5,9 +5,15 @@
 
 namespace hla {
 
+// Chunk of the kernels: 64 tokens, or 32 for fp32 at d >= 32, whose 64-token
+// tiles would leave room for one workgroup per compute unit.  Segments are
+// multiples of kLaChunk tokens either way.
+template <typename T, int D>
+constexpr int la_chunk() { return (sizeof(T) == 4 && D >= 32) ? 32 : kLaChunk; }
+
 template <typename T, int D, bool SYM, bool DUAL>
 hipError_t launch_la(const LaParams &p, hipStream_t s, bool summaries) {
-    constexpr int C = kLaChunk;
+    constexpr int C = la_chunk<T, D>();
     using Cfg = LaCfg<T, D, C, SYM, DUAL>;
     if (summaries && p.nseg > 1) {
         // a DUAL pass's state is the plain state of its b, c
@@ -59,10 +65,10 @@ template <typename T, int D>
 bool la_set(LaLaunches *out) {
     out->unit_column = launch_unit_column<T, D>;
     out->ratio_prep = launch_ratio_prep<T, D>;
-    static_assert(sizeof(LaLds<T, D, kLaChunk, true, false>) <= 160 * 1024, "LDS");
+    static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
     out->sym = launch_la<T, D, true, false>;
-    if constexpr (sizeof(LaLds<T, D, kLaChunk, false, true>) <= 160 * 1024)
+    if constexpr (sizeof(LaLds<T, D, la_chunk<T, D>(), false, true>) <= 160 * 1024)
         out->dual = launch_la<T, D, false, true>;
     else
         out->dual = launch_la_dual_split<T, D>;
