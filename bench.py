@@ -130,8 +130,18 @@ def kernel_key(name: str) -> str:
     import re
     m = re.search(r"(hla2_|ahla_|la_)?(summary_kernel|up_sweep_kernel|forward_kernel)", name)
     key = m.group(0)
-    if key.startswith("la_") and ("Lb1E" in name or "true>" in name):
-        key += "_sym"
+    if key.startswith("la_"):
+        # template flags (SYM, DUAL): mangled ...Lb<0|1>ELb<0|1>E, or demangled
+        mm = re.search(r"Lb([01])ELb([01])E", name)
+        md = re.search(r"(true|false), (true|false)>", name)
+        flags = (mm.group(1) == "1", mm.group(2) == "1") if mm else \
+            ((md.group(1) == "true", md.group(2) == "true") if md else (False, False))
+        if flags[0]:
+            key += "_sym"
+        if flags[1]:
+            key += "_dual"
+        if "<float" in name or re.search(r"kernelIf", name):
+            key += "_f32"
     return key
 
 
