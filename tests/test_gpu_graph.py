@@ -97,3 +97,38 @@ def test_step_graph_replay():
         assert torch.equal(state, st_e), f"replay {r}: state differs from {T} eager steps"
         for t in range(T):
             assert torch.equal(outs[t], outs_e[t]), f"replay {r}: output of step {t} differs"
+
+
+@pytest.mark.parametrize("variant,decay", [("hla2", True), ("hla2_ratio", False), ("ahla", False)])
+def test_backward_graph_replay(variant, decay):
+    """hla_backward captured once and replayed: every replay equals the eager
+    gradients bit for bit, with the workspace and outputs overwritten between
+    replays (the backward fills its unit rows with a kernel, not a memset)."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    B, H, n, d, seg = 1, 3, 900, 64, 3           # 5 segments, ragged tail
+    say(f"[graph] backward {variant} decay={decay} B={B} H={H} n={n} d={d}")
+    dist = "uniform_pos" if variant.endswith("ratio") else "l2norm"
+    x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist=dist, seed=903, decay=decay)
+    q, k, v = (to_dev(x[key], "bf16", (B, H, n, d)) for key in ("q", "k", "v"))
+    do = to_dev(I.make_upstream_grad(B * H, n, d, "bf16", seed=904), "bf16", (B, H, n, d))
+    eager = [t.clone() for t in hla.hla_backward(q, k, v, do, variant=variant, gamma=x["gamma"],
+                                                 seg_chunks=seg)]
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(max(1, hla.backward_workspace_bytes(variant, B, H, n, d, d, "bf16", seg)),
+                     dtype=torch.uint8, device="cuda")
+    plan = hla.BackwardPlan(q, k, v, do, variant=variant, gamma=x["gamma"], seg_chunks=seg,
+                            dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws, stream=s)
+    g = _capture(plan.run, s)
+    for r in range(3):
+        for t in grads:
+            t.fill_(float("nan"))          # eager work between replays
+        ws.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("dq", "dk", "dv"), grads, eager):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager backward"
