@@ -15,6 +15,8 @@ Contents
                    combine, exclusive Blelloch scan) written out in fp64 NumPy.
 ``backward.py``    gradients (dq, dk, dv) of the masked operators: the chain
                    rule applied to the n x n matrix form, fp64 NumPy.
+``third_order.py`` the masked third-order operator tril(L L^T) L V: loops,
+                   matrix form and a serial recurrence, fp64 NumPy.
 
 Source for every formula: "Resumen Tecnico: Atencion Lineal de Orden Superior
 (HLA)", gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",
