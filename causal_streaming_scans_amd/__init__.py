@@ -14,6 +14,8 @@ gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",
     hla2_ratio  the same over its v == 1 denominator
     ahla        o = tril(QK^T) tril(QK^T) V
     ahla_ratio  the same over its v == 1 denominator
+    hla3        o = tril(L L^T) L V, L = tril(QK^T)  (third order, section "3.
+                HLA de Tercer Orden"; no decay, no streaming state)
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhla.so")
 _lib = None
 
-VARIANTS = {"hla2": 0, "hla2_ratio": 1, "ahla": 2, "ahla_ratio": 3}
+VARIANTS = {"hla2": 0, "hla2_ratio": 1, "ahla": 2, "ahla_ratio": 3, "hla3": 4}
 _DTYPES = {"f32": 0, "bf16": 1}
 MAX_DECAY_HEADS = 256
 

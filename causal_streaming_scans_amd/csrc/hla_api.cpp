@@ -24,7 +24,8 @@ using namespace hla;
 
 namespace {
 
-bool valid_variant(int v) { return v >= HLA_HLA2 && v <= HLA_AHLA_RATIO; }
+bool valid_variant(int v) { return v >= HLA_HLA2 && v <= HLA_HLA3; }
+bool is_hla3(int v) { return v == HLA_HLA3; }
 bool is_ahla(int v) { return v == HLA_AHLA || v == HLA_AHLA_RATIO; }
 bool is_ratio(int v) { return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO; }
 
@@ -46,7 +47,7 @@ hla_status check_common(int B, int H, int d, int dv, int dtype, int variant, con
     if (B < 1 || H < 1 || d < 1 || dv < 1) return HLA_ERR_SHAPE;
     if ((long)B * H > 65535) return HLA_ERR_UNSUPPORTED;
     if (gamma) {
-        if (is_ahla(variant)) return HLA_ERR_UNSUPPORTED;
+        if (is_ahla(variant) || is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
         if (H > HLA_MAX_DECAY_HEADS) return HLA_ERR_UNSUPPORTED;
         for (int h = 0; h < H; ++h)
             if (!(gamma[h] > 0.f && gamma[h] <= 1.f)) return HLA_ERR_ARG;  // also rejects NaN
@@ -86,7 +87,7 @@ void fill_gamma(float *dst, const float *gamma, int H) {
 extern "C" {
 
 size_t hla_state_floats(int variant, int d, int dv) {
-    if (!valid_variant(variant) || d < 1 || dv < 1) return 0;
+    if (!valid_variant(variant) || is_hla3(variant) || d < 1 || dv < 1) return 0;
     return is_ahla(variant) ? (size_t)ahla_state_floats(d, dv) : (size_t)hla2_state_floats(d, dv);
 }
 
@@ -114,11 +115,22 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
         return 0;
     const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
     const long nseg = num_segments(n, chunk, g);
-    if (nseg <= 1) return 0;
-    const size_t nreal = (size_t)(nseg - 1);
     // leaves, then internal nodes of the up-sweep (fewer than nreal per head)
-    return 2 * (size_t)B * H * nreal * (size_t)summary_floats(d, dv) * sizeof(float);
+    const size_t scan = nseg <= 1 ? 0
+        : 2 * (size_t)B * H * (size_t)(nseg - 1) * (size_t)summary_floats(d, dv) * sizeof(float);
+    if (!is_hla3(variant)) return scan;
+    // third order: Y = LA(Q, K, V) (sized for fp32) and its pass's segment states
+    const long nseg_la = num_segments(n, kLaChunk, hla_backward_default_seg_chunks(B, H, n));
+    return scan + (size_t)B * H * n * dv * sizeof(float) +
+           (size_t)B * H * (size_t)(nseg_la - 1) * d * dv * sizeof(float);
 }
+
+// The first-order pass of the third-order variant, Y = LA(Q, K, V), run
+// before the second-order stages consume (Q, K, Y).
+struct Hla3Pass {
+    LaLaunches la;
+    LaParams lp;
+};
 
 // Validate, pick the kernels and fill the argument block; shared by
 // hla_forward and hla_forward_stage.
@@ -126,7 +138,8 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
                                   int H, int n, int d, int dv, int dtype, int variant,
                                   const float *gamma_host, int chunk, int seg_chunks,
                                   const float *state_in, float *state_out, void *workspace,
-                                  size_t workspace_bytes, FwdKernels *kern, FwdParams *p) {
+                                  size_t workspace_bytes, FwdKernels *kern, FwdParams *p,
+                                  Hla3Pass *x3) {
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
@@ -134,6 +147,10 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     if (n > 0 && (!q || !k || !v || !o)) return HLA_ERR_NULL;
     if (state_in && state_out && state_in == state_out) return HLA_ERR_ARG;
     if (!lookup_forward(dtype, is_ahla(variant), d, dv, chunk, gamma_host != nullptr, kern))
+        return HLA_ERR_UNSUPPORTED;
+    // the third-order variant keeps no streaming state (its carried state
+    // would add P^KV to the second-order one)
+    if (is_hla3(variant) && (state_in || state_out || d != dv || !lookup_la(dtype, d, &x3->la)))
         return HLA_ERR_UNSUPPORTED;
     const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
@@ -164,12 +181,34 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     p->state_out = state_out;
     fill_gamma(p->gamma, gamma_host, H);
     fill_order(p);
+    if (is_hla3(variant)) {
+        // Y after the scan's part of the workspace; the second-order stages
+        // read it as their values
+        const size_t scan = nseg <= 1 ? 0
+            : 2 * (size_t)B * H * (size_t)(nseg - 1) * (size_t)summary_floats(d, dv) * sizeof(float);
+        char *Y = static_cast<char *>(workspace) + scan;
+        const int g_la = hla_backward_default_seg_chunks(B, H, n);
+        LaParams &lp = x3->lp;
+        memset(&lp, 0, sizeof(lp));
+        lp.a = q;
+        lp.b = k;
+        lp.c = v;
+        lp.out = Y;
+        lp.sums = reinterpret_cast<float *>(Y + (size_t)B * H * n * dv * sizeof(float));
+        lp.BH = B * H;
+        lp.H = H;
+        lp.n = n;
+        lp.seg_len = kLaChunk * g_la;
+        lp.nseg = (int)num_segments(n, kLaChunk, g_la);
+        fill_gamma(lp.gamma, nullptr, H);
+        p->v = Y;
+    }
     return HLA_OK;
 }
 
 // one stage of the forward pass (1 = summaries, 2 = up-sweep, 3 = chunked forward)
 static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &p, int variant,
-                            int d, int dv, hipStream_t s) {
+                            int d, int dv, const Hla3Pass &x3, hipStream_t s) {
     if (p.n == 0) {
         // no tokens: the state passes through unchanged (done by the last stage)
         if (stage == 3 && p.state_out) {
@@ -180,6 +219,10 @@ static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &
         return HLA_OK;
     }
     hipError_t e = hipSuccess;
+    if (stage == 1 && is_hla3(variant)) {
+        e = x3.la.plain(x3.lp, s, true);
+        if (e != hipSuccess) return HLA_ERR_DEVICE;
+    }
     if (stage == 1 && p.nseg > 1) e = kern.summary(p, s);
     if (stage == 2 && p.nseg > 2) e = kern.up_sweep(p, s);
     if (stage == 3) e = kern.forward(p, s);
@@ -192,13 +235,14 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int
                        size_t workspace_bytes, void *stream) {
     FwdKernels kern;
     FwdParams p;
+    Hla3Pass x3;
     hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
                                     seg_chunks, state_in, state_out, workspace, workspace_bytes,
-                                    &kern, &p);
+                                    &kern, &p, &x3);
     if (st != HLA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int stage = 1; stage <= 3; ++stage) {
-        st = run_stage(stage, kern, p, variant, d, dv, s);
+        st = run_stage(stage, kern, p, variant, d, dv, x3, s);
         if (st != HLA_OK) return st;
     }
     return HLA_OK;
@@ -212,11 +256,12 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
     if (stage < 1 || stage > 3) return HLA_ERR_ARG;
     FwdKernels kern;
     FwdParams p;
+    Hla3Pass x3;
     hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
                                     seg_chunks, state_in, state_out, workspace, workspace_bytes,
-                                    &kern, &p);
+                                    &kern, &p, &x3);
     if (st != HLA_OK) return st;
-    return run_stage(stage, kern, p, variant, d, dv, static_cast<hipStream_t>(stream));
+    return run_stage(stage, kern, p, variant, d, dv, x3, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ backward
@@ -462,6 +507,7 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B,
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (!q || !k || !v || !o || !state) return HLA_ERR_NULL;
+    if (is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
     StepLaunch fn;
     if (!lookup_step(dtype, is_ahla(variant), d, dv, &fn)) return HLA_ERR_UNSUPPORTED;
     StepParams p;

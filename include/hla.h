@@ -23,6 +23,13 @@
  *                   gives IEEE inf/NaN in that row)
  *   HLA_AHLA        o = (L L) V,  o_t = sum_{i<=t} sum_{j<=i} A[t,i] A[i,j] v_j
  *   HLA_AHLA_RATIO  the AHLA numerator over the same sum with v == 1
+ *   HLA_HLA3        third order (section "3. HLA de Tercer Orden": the product
+ *                   A A^T A made strictly causal), read as o = tril(L L^T) L V:
+ *                   o_t = sum_{m<=t} sum_{i<=m} sum_{j<=m} A[t,i] A[m,i] A[m,j] v_j.
+ *                   Computed as the second-order operator on the values
+ *                   Y = L V (one chunked first-order pass into the workspace);
+ *                   no decay, no streaming state (state_in / state_out must be
+ *                   NULL, hla_step and hla_state_floats do not apply)
  * g is the per-head decay (1 when gamma is NULL).  No 1/sqrt(d) or other
  * scaling is applied inside.
  *
@@ -72,7 +79,8 @@ typedef enum {
     HLA_HLA2 = 0,
     HLA_HLA2_RATIO = 1,
     HLA_AHLA = 2,
-    HLA_AHLA_RATIO = 3
+    HLA_AHLA_RATIO = 3,
+    HLA_HLA3 = 4
 } hla_variant;
 
 /* Largest H for which a per-head decay can be given (it travels in the kernel
@@ -89,7 +97,8 @@ int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk);
 /* Bytes of device workspace hla_forward needs for these arguments
  * (seg_chunks == 0 means the default): 2*B*H*(nseg-1) fp32 summaries of
  * d*d + 2*d*dv + 2*d floats (the segment summaries and the nodes of the
- * scan's up-sweep).  0 when the sequence is one segment. */
+ * scan's up-sweep).  0 when the sequence is one segment.  HLA_HLA3 adds
+ * B*H*n*dv fp32 for Y and the segment states of its first-order pass. */
 size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
                            int chunk, int seg_chunks);
 

@@ -214,3 +214,29 @@ def test_backward_validation(lib):
     assert _bwd(lib, dv=None) == ERR_NULL
     assert _bwd(lib, ws=None) == ERR_NULL
     assert _bwd(lib, ws_bytes=1) == ERR_WS
+
+
+# ---------------------------------------------------------------- third order
+
+HLA3 = 4
+
+
+def test_hla3_sizes_and_validation(lib):
+    assert lib.hla_state_floats(HLA3, 64, 64) == 0          # no streaming state
+    B, H, n, d, chunk, seg = 2, 4, 1000, 64, 64, 4
+    nseg = -(-n // (chunk * seg))
+    scan = 2 * B * H * (nseg - 1) * (d * d + 2 * d * d + 2 * d) * 4
+    g = lib.hla_backward_default_seg_chunks(B, H, n)
+    nseg_la = -(-n // (64 * g))
+    want = scan + B * H * n * d * 4 + B * H * (nseg_la - 1) * d * d * 4
+    assert hla.workspace_bytes("hla3", B, H, n, d, d, chunk, seg) == want
+    P = ctypes.c_void_p
+    g2 = (ctypes.c_float * H)(*([0.9] * H))
+    fwd = lambda **kw: lib.hla_forward(P(1), P(1), P(1), P(1), B, H, n, d, d, BF16, HLA3,
+                                       kw.get("gamma"), chunk, seg, kw.get("si"), kw.get("so"),
+                                       P(1), kw.get("ws", 1), None)
+    assert fwd(gamma=g2) == ERR_UNSUP                       # no decay for third order
+    assert fwd(si=P(8)) == ERR_UNSUP                        # no streaming state
+    assert fwd(so=ctypes.cast(P(8), ctypes.POINTER(ctypes.c_float))) == ERR_UNSUP
+    assert fwd(ws=16) == ERR_WS
+    assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, None, P(1), None) == ERR_UNSUP

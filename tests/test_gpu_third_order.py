@@ -1,0 +1,62 @@
+"""GPU parity of the third-order variant (hla_forward, variant "hla3") against
+the fp64 oracle of oracle/third_order.py: o = tril(L L^T) L V, the strictly
+causal reading of the product A A^T A of section "3. HLA de Tercer Orden"
+("Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)",
+gist.science/es/paper/2510.27258).  Relative L2: 1e-5 fp32, 1e-2 bf16."""
+import pytest
+
+from causal_streaming_scans_amd import inputs as I
+from oracle import third_order as T3
+from hla_testlib import TOL, from_dev, rel_l2, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, d, n, H, chunk, seg_chunks
+    ("f32", 16, 200, 2, 32, 2),
+    ("f32", 32, 130, 1, 16, 0),
+    ("f32", 64, 257, 2, 64, 1),
+    ("bf16", 16, 333, 2, 32, 3),
+    ("bf16", 64, 65, 2, 64, 0),
+    ("bf16", 64, 450, 3, 64, 2),
+    ("bf16", 128, 300, 2, 32, 2),
+]
+
+
+def run(x, B, H, dtype, chunk, seg):
+    import torch
+    import causal_streaming_scans_amd as hla
+    n, d = x["q"].shape[1], x["q"].shape[2]
+    shp = (B, H, n, d)
+    o = hla.hla_forward(to_dev(x["q"], dtype, shp), to_dev(x["k"], dtype, shp),
+                        to_dev(x["v"], dtype, shp), variant="hla3", chunk=chunk, seg_chunks=seg)
+    torch.cuda.synchronize()
+    return from_dev(o).reshape(B * H, n, d)
+
+
+@pytest.mark.parametrize("dtype,d,n,H,chunk,seg", CASES)
+def test_hla3_small(dtype, d, n, H, chunk, seg):
+    say(f"[third order] dtype {dtype} d {d} n {n} H {H} chunk {chunk} seg_chunks {seg}")
+    B = 1
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="normal_scaled" if dtype == "f32" else "l2norm",
+                      seed=990 + d + n)
+    got = run(x, B, H, dtype, chunk, seg)
+    want = T3.hla3_batched(x["q"], x["k"], x["v"])
+    e = rel_l2(got, want)
+    say(f"  rel_l2 {e:.3e}")
+    assert e < TOL[dtype]
+
+
+def test_hla3_n2048_sampled_heads():
+    """The HLA-2 workload's inputs (B=4 H=8 n=2048 d=dv=64 bf16) through the
+    third-order variant in the default launch configuration; the oracle on
+    the first and last head."""
+    w = I.WORKLOADS["hla2_n2048"]
+    say(f"[third order] inputs of {w.name}")
+    x = I.workload_inputs("hla2_n2048")
+    got = run(x, w.B, w.H, w.dtype, 64, 0)
+    heads = [0, w.B * w.H - 1]
+    want = T3.hla3_batched(x["q"], x["k"], x["v"], heads=heads)
+    e = rel_l2(got[heads], want)
+    say(f"  rel_l2 {e:.3e}")
+    assert e < TOL[w.dtype]
