@@ -25,7 +25,10 @@ event between consecutive steps (median, p10, p90 per step); K cold steps,
 each after a 1 GiB buffer (more than the Infinity Cache) has been written;
 and K replays of the step captured in a HIP graph.  Decode is timed as the
 mean over 1024 plain calls and over replays of 64 captured steps (a spread
-per call would time the host: a 3.5 us step is shorter than one submission).  The CPU baseline is the fp64
+per call would time the host: a 3.5 us step is shorter than one submission).  Then the
+backward (HLA-2 gradients at the same shape, and the ratio gradients on the
+benchmark's own inputs) and the third-order forward, each as calls between two
+events.  The CPU baseline is the fp64
 oracle on the same inputs (all heads), on the host's cores.
 """
 from __future__ import annotations
@@ -212,8 +215,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--backward-steps", type=int, default=200,
-                    help="time this many hla_backward calls (HLA-2 gradients at the benchmark "
-                         "shape); 0 skips the backward leg")
+                    help="time this many hla_backward calls (HLA-2 and ratio gradients at the "
+                         "benchmark shape) and third-order forwards; 0 skips these legs")
     ap.add_argument("--backward-seg-chunks", type=int, default=0,
                     help="chunks per segment of the backward passes (0 = the library default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -487,7 +490,7 @@ def main():
     # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
     # unnormalised HLA-2 (the variant the backward supports), q, k L2-normalised
     # Gaussian rows, v and the upstream gradient ~ N(0, 1), bf16
-    backward = backward_ratio = None
+    backward = backward_ratio = third_order = None
     if args.backward_steps > 0:
         bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
         bnseg = -(-n // (64 * bseg))
@@ -524,7 +527,24 @@ def main():
                     "lean_bytes_per_step": b_bytes,
                     "lean_hbm_frac": round(b_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] backward: {bms:.4f} ms/step, {tokens / (bms * 1e-3) / 1e9:.3f} G tokens/s")
-        del qb, kb, vb
+        # third-order forward (variant hla3) on the same inputs: the LA pass
+        # into the workspace, then the three second-order stages
+        t3plan = hla.ForwardPlan(qb, kb, vb, variant="hla3", chunk=chunk, seg_chunks=seg)
+        for _ in range(10):
+            t3plan.run()
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.backward_steps):
+            t3plan.run()
+        t_end.record()
+        torch.cuda.synchronize()
+        t3ms = t_start.elapsed_time(t_end) / args.backward_steps
+        third_order = {"workload": f"third-order HLA forward, B={B} H={H} n={n} d=dv={d} bf16, "
+                                   "q,k L2-normalised Gaussian, v ~ N(0,1)",
+                       "ms_per_step": round(t3ms, 5),
+                       "tokens_per_s": round(tokens / (t3ms * 1e-3), 1)}
+        log(f"[bench] third-order forward: {t3ms:.4f} ms/step")
+        del qb, kb, vb, t3plan
         # the benchmark's own variant and inputs: ratio HLA-2 on q, k, v above
         rms = time_backward("hla2_ratio", q, k, v, dob)
         backward_ratio = {"steps": args.backward_steps,
@@ -584,6 +604,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "backward_ratio": backward_ratio,
+        "third_order": third_order,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
