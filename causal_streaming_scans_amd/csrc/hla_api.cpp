@@ -292,11 +292,11 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
 int hla_backward_default_seg_chunks(int B, int H, int n) {
     if (B < 1 || H < 1 || n < 1) return 1;
     const long nch = ceil_div(n, kLaChunk);
-    // about 768 workgroups per pass, three per compute unit at d = 64 (the
-    // main kernel's LDS allows three): one full round, no ragged second one.
-    // Measured at B*H = 128, n = 4096: 6 segments 0.79 ms per backward,
-    // 8 segments 0.84, 4 segments 0.92
-    long nseg = ceil_div(768, (long)B * H);
+    // about 512 workgroups per pass, two per compute unit: the fused (SYM,
+    // DUAL) and fp32 kernels hold two, the plain bf16 kernel three.  Measured
+    // at B*H = 128, n = 4096 (bf16 backward / ratio backward, ms): 16 chunks
+    // per segment 0.442 / 2.40, 11 chunks 0.450 / 2.72, 8 chunks 0.494 / 2.50
+    long nseg = ceil_div(512, (long)B * H);
     long g = ceil_div(nch, nseg);
     if (g < 2) g = 2;
     if (g > nch) g = nch;
@@ -317,7 +317,8 @@ static size_t backward_elem_bytes(int variant, int dtype) {
 
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
                                     int seg_chunks) {
-    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
+    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || B < 1 ||
+        H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
         (dtype != HLA_F32 && dtype != HLA_BF16))
         return 0;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
