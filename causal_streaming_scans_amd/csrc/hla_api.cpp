@@ -308,16 +308,21 @@ int hla_backward_default_seg_chunks(int B, int H, int n) {
 // and the unit rows (1, 0, ..., 0), and with bf16 inputs runs in fp32 on
 // widened copies of q, k, v, dO and fp32 gradients (seven more)
 static int backward_tensors(int variant, int dtype) {
-    if (variant != HLA_HLA2_RATIO) return 2;
-    return dtype == HLA_BF16 ? 12 : 5;
+    if (!is_ratio(variant)) return 2;
+    const int own = variant == HLA_AHLA_RATIO ? 7 : 5;   // AHLA adds Y1 and dY1
+    return dtype == HLA_BF16 ? own + 7 : own;
 }
 static size_t backward_elem_bytes(int variant, int dtype) {
-    return (variant == HLA_HLA2_RATIO || dtype == HLA_F32) ? 4 : 2;
+    return (is_ratio(variant) || dtype == HLA_F32) ? 4 : 2;
+}
+static bool has_backward(int variant) {
+    return variant == HLA_HLA2 || variant == HLA_HLA2_RATIO || variant == HLA_AHLA ||
+           variant == HLA_AHLA_RATIO;
 }
 
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
                                     int seg_chunks) {
-    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || B < 1 ||
+    if (!has_backward(variant) || B < 1 ||
         H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
         (dtype != HLA_F32 && dtype != HLA_BF16))
         return 0;
@@ -336,12 +341,11 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
-    if ((variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA) || d != dv)
-        return HLA_ERR_UNSUPPORTED;
+    if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
     // the ratio form runs its passes in fp32 (its gradient with respect to q
     // and k is a small difference of large terms, which bf16 intermediates
     // do not resolve)
-    const int run_dtype = variant == HLA_HLA2_RATIO ? HLA_F32 : dtype;
+    const int run_dtype = is_ratio(variant) ? HLA_F32 : dtype;
     LaLaunches la;
     if (!lookup_la(run_dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
@@ -423,7 +427,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
         return fn(p, s, ps.summaries) == hipSuccess;
     };
-    if (variant != HLA_HLA2_RATIO) {
+    if (!is_ratio(variant)) {
         const Pass *passes = variant == HLA_AHLA ? ahla_passes : hla2_passes;
         for (int i = 0; i < 5; ++i)
             if (!run(passes[i])) return HLA_ERR_DEVICE;
@@ -440,13 +444,14 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     void *G = ws + 2 * sums_bytes + 2 * tensor_bytes;
     void *E1 = ws + 2 * sums_bytes + 3 * tensor_bytes;
     void *ONE1 = ws + 2 * sums_bytes + 4 * tensor_bytes;
+    const int own = variant == HLA_AHLA_RATIO ? 7 : 5;
     const long rows = (long)B * H * n;
     const long count = rows * d;
     // bf16 inputs: every pass below reads and writes fp32 copies
     void *dq_out = dq, *dk_out = dk, *dv_user = dv_out;
     if (dtype == HLA_BF16) {
         void *w32[7];
-        for (int i = 0; i < 7; ++i) w32[i] = ws + 2 * sums_bytes + (5 + i) * tensor_bytes;
+        for (int i = 0; i < 7; ++i) w32[i] = ws + 2 * sums_bytes + (own + i) * tensor_bytes;
         const void *src[4] = {q, k, v, dout};
         for (int i = 0; i < 4; ++i)
             if (launch_convert(src[i], w32[i], count, true, s) != hipSuccess) return HLA_ERR_DEVICE;
@@ -459,40 +464,81 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         dv_out = w32[6];
     }
     if (la.unit_column(ONE1, rows, s) != hipSuccess) return HLA_ERR_DEVICE;
-    const Pass pre[3] = {
-        // Z  = LA_g(Q, K, K)
-        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
-        // u  = LA_g2(ONE1, ONE1, Z)
-        {&p2, ONE1, ONE1, Z, nullptr, dv_out, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // num = LA_g2(Q, Z, V)
-        {&p2, q, Z, v, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-    };
-    for (const Pass &ps : pre)
-        if (!run(ps)) return HLA_ERR_DEVICE;
-    RatioPrepParams rp;
-    rp.q = q;
-    rp.u = dv_out;
-    rp.num = dZ;
-    rp.dout = dout;
-    rp.g = G;
-    rp.e1 = E1;
-    rp.dq = dq;
-    rp.rows = rows;
-    if (la.ratio_prep(rp, s) != hipSuccess) return HLA_ERR_DEVICE;
-    const Pass post[5] = {
-        // dQ = e u + LA_g2(G, V, Z)
-        {&p2, G, v, Z, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // dZ = RLA_g2(V, G, Q) and dV = RLA_g2(Z, Q, G)
-        {&p2, v, G, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
-        // dZ += RLA_g2(ONE1, E1, Q)
-        {&p2, ONE1, E1, q, dZ, dZ, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
-        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
-        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
-        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
-    };
-    for (const Pass &ps : post)
-        if (!run(ps)) return HLA_ERR_DEVICE;
+    if (variant == HLA_AHLA_RATIO) {
+        // AHLA: num = LA(Q, K, Y), den = first column of LA(Q, K, Y1) with
+        // Y = LA(Q, K, V), Y1 = LA(Q, K, ONE1).  The gradient is the AHLA
+        // chain with upstream G on values V plus the AHLA chain with
+        // upstream E1 on values ONE1 (whose value gradient is dropped).
+        void *Y1 = ws + 2 * sums_bytes + 5 * tensor_bytes;
+        void *dY1 = ws + 2 * sums_bytes + 6 * tensor_bytes;
+        const Pass apre[4] = {
+            {&p1, q, k, v, nullptr, Z, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},       // Y
+            {&p1, q, k, ONE1, nullptr, Y1, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},   // Y1
+            {&p1, q, k, Z, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},      // num
+            {&p1, q, k, Y1, nullptr, dY1, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},    // den
+        };
+        for (const Pass &ps : apre)
+            if (!run(ps)) return HLA_ERR_DEVICE;
+        RatioPrepParams ap;
+        ap.q = ONE1;      // den = ONE1_t . DEN_t, the first column
+        ap.u = dY1;
+        ap.num = dZ;
+        ap.dout = dout;
+        ap.g = G;
+        ap.e1 = E1;
+        ap.dq = dv_out;   // unused here; dv_out is written by a later pass
+        ap.rows = rows;
+        if (la.ratio_prep(ap, s) != hipSuccess) return HLA_ERR_DEVICE;
+        const Pass apost[8] = {
+            // upstream G, values V
+            {&p1, G, Z, k, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            {&p1, k, q, G, nullptr, dZ, 1, DUAL, sums, true, Z, dk, nullptr},
+            {&p1, k, q, dZ, nullptr, dv_out, 1, DUAL, sums, true, v, dk, dk},
+            {&p1, dZ, v, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            // upstream E1, values ONE1
+            {&p1, E1, Y1, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            {&p1, k, q, E1, nullptr, dY1, 1, DUAL, sums, true, Y1, dk, dk},
+            {&p1, ONE1, dY1, q, dk, dk, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            {&p1, dY1, ONE1, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        };
+        for (const Pass &ps : apost)
+            if (!run(ps)) return HLA_ERR_DEVICE;
+    } else {
+        const Pass pre[3] = {
+            // Z  = LA_g(Q, K, K)
+            {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
+            // u  = LA_g2(ONE1, ONE1, Z)
+            {&p2, ONE1, ONE1, Z, nullptr, dv_out, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            // num = LA_g2(Q, Z, V)
+            {&p2, q, Z, v, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+        };
+        for (const Pass &ps : pre)
+            if (!run(ps)) return HLA_ERR_DEVICE;
+        RatioPrepParams rp;
+        rp.q = q;
+        rp.u = dv_out;
+        rp.num = dZ;
+        rp.dout = dout;
+        rp.g = G;
+        rp.e1 = E1;
+        rp.dq = dq;
+        rp.rows = rows;
+        if (la.ratio_prep(rp, s) != hipSuccess) return HLA_ERR_DEVICE;
+        const Pass post[5] = {
+            // dQ = e u + LA_g2(G, V, Z)
+            {&p2, G, v, Z, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            // dZ = RLA_g2(V, G, Q) and dV = RLA_g2(Z, Q, G)
+            {&p2, v, G, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
+            // dZ += RLA_g2(ONE1, E1, Q)
+            {&p2, ONE1, E1, q, dZ, dZ, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
+            // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+            {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
+            // dQ += LA_g(dZ, K, K), with the segment states of the first pass
+            {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
+        };
+        for (const Pass &ps : post)
+            if (!run(ps)) return HLA_ERR_DEVICE;
+    }
     if (dtype == HLA_BF16) {
         void *dst[3] = {dq_out, dk_out, dv_user};
         const void *src[3] = {dq, dk, dv_out};

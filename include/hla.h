@@ -193,9 +193,9 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * sections "1. HLA de Segundo Orden" and "2. ... (AHLA)", decay per
  * "Contribuciones Clave" item 2).  Given the upstream gradient dout = dL/do,
  * writes dq = dL/dq, dk = dL/dk, dv = dL/dv of the HLA_HLA2 output
- * o = tril(L L^T) V (with decay g_h when gamma_host is given), of its ratio
- * form HLA_HLA2_RATIO, or of the HLA_AHLA output o = (L L) V, computed from
- * zero state.
+ * o = tril(L L^T) V (with decay g_h when gamma_host is given), of the
+ * HLA_AHLA output o = (L L) V, or of either ratio form (HLA_HLA2_RATIO,
+ * HLA_AHLA_RATIO), computed from zero state.
  *
  * Method: with z_t = S^K_t q_t, the operator is two chained causal linear
  * attentions, Z = LA_g(Q, K, K) and O = LA_{g^2}(Q, Z, V), where
@@ -209,6 +209,8 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * form recomputes num and den (two more passes and a row-wise kernel), runs
  * the passes with dO / den as upstream gradient, and adds the denominator's
  * terms through one more pass; it keeps three more tensors in the workspace.
+ * The AHLA ratio form runs the AHLA chain twice (upstream dO / den on V, and
+ * the denominator's upstream on unit rows), with two more tensors.
  *
  * q, k, v, dout  device, [B][H][n][d] (d == dv), element type = dtype
  * dq, dk, dv_out  device outputs, same layout and type; may not alias the
@@ -219,9 +221,11 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * workspace      device buffer of at least hla_backward_workspace_bytes()
  *                bytes (contents ignored on entry, unspecified on return)
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
- * dZ are kept in dtype.  Supported: variants HLA_HLA2, HLA_HLA2_RATIO and
- * HLA_AHLA (HLA_AHLA_RATIO and AHLA with a decay: HLA_ERR_UNSUPPORTED; the
- * ratio form needs nonzero denominators, as the forward), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
+ * dZ are kept in dtype; the ratio forms run every pass in fp32 (for bf16
+ * inputs on widened copies, d <= 64).  Supported: HLA_HLA2, HLA_HLA2_RATIO,
+ * HLA_AHLA, HLA_AHLA_RATIO (AHLA with a decay and HLA_HLA3:
+ * HLA_ERR_UNSUPPORTED; the ratio forms need nonzero denominators, as the
+ * forward), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
  * d in {16, 32, 64}.  Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);

@@ -189,7 +189,9 @@ def test_backward_workspace_bytes(lib):
     # (fp32 copies of q, k, v, dO and fp32 gradients)
     want_ratio = want - 2 * B * H * n * d * 2 + 12 * B * H * n * d * 4
     assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == want_ratio
-    assert hla.backward_workspace_bytes("ahla_ratio", B, H, n, d, d) == 0
+    assert hla.backward_workspace_bytes("ahla_ratio", B, H, n, d, d) == \
+        want_ratio + 2 * B * H * n * d * 4                   # Y1 and its gradient
+    assert hla.backward_workspace_bytes("hla3", B, H, n, d, d) == 0
     assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == want
 
 
@@ -197,7 +199,9 @@ def test_backward_validation(lib):
     assert _bwd(lib, n=0) == OK                      # nothing to do, nothing enqueued
     assert _bwd(lib, variant=HLA2_RATIO, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=HLA2_RATIO, d=128, dvd=128) == ERR_UNSUP   # fp32 passes: d <= 64
-    assert _bwd(lib, variant=AHLA_RATIO) == ERR_UNSUP
+    assert _bwd(lib, variant=AHLA_RATIO, ws_bytes=1) == ERR_WS
+    assert _bwd(lib, variant=AHLA_RATIO, d=128, dvd=128) == ERR_UNSUP   # fp32 passes: d <= 64
+    assert _bwd(lib, variant=4) == ERR_UNSUP                              # third order: forward only
     assert _bwd(lib, variant=AHLA, gamma=[0.9, 0.9]) == ERR_UNSUP   # AHLA has no decay
     assert _bwd(lib, variant=AHLA, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=9) == ERR_ARG

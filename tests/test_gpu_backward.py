@@ -239,3 +239,40 @@ def test_ratio_backward_n4096_sampled_heads():
     heads = [0, w.B * w.H - 1]
     want = BW.hla2_vjp_batched(x["q"], x["k"], x["v"], do, w.H, ratio=True, heads=heads)
     check(tuple(g[heads] for g in got), want, w.dtype, "ratio_n4096 heads 0,127")
+
+
+AHLA_RATIO_SMALL = [
+    # dtype, d, n, H, seg_chunks
+    ("f32", 16, 200, 2, 1),
+    ("f32", 64, 257, 2, 0),
+    ("bf16", 32, 130, 2, 1),
+    ("bf16", 64, 450, 3, 2),
+    ("bf16", 16, 200, 1, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,d,n,H,seg", AHLA_RATIO_SMALL)
+def test_ahla_ratio_backward_small(dtype, d, n, H, seg):
+    """Gradients of the ratio-normalised AHLA (numerator over the v == 1
+    denominator); positive q, k keep the denominators positive.  Run with
+    fp32 passes for bf16 inputs, as the HLA-2 ratio form."""
+    say(f"[ahla ratio backward] dtype {dtype} d {d} n {n} H {H} seg_chunks {seg}")
+    B = 1
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos", seed=1110 + d + n)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=1210 + n)
+    got = run_backward(x, do, B, H, dtype, None, seg, variant="ahla_ratio")
+    want = BW.ahla_vjp_batched(x["q"], x["k"], x["v"], do, ratio=True)
+    check(got, want, dtype, f"ahla ratio {dtype} d{d} n{n}")
+
+
+def test_ahla_ratio_backward_n4096():
+    """Ratio AHLA at B=1 H=4 n=4096 d=dv=64 bf16 in the default launch
+    configuration, q, k ~ U[0,1)/sqrt(d); the oracle on two heads."""
+    B, H, n, d = 1, 4, 4096, 64
+    say(f"[ahla ratio backward] B={B} H={H} n={n} d={d} bf16")
+    x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist="uniform_pos", seed=1301)
+    do = I.make_upstream_grad(B * H, n, d, "bf16", seed=1302)
+    got = run_backward(x, do, B, H, "bf16", variant="ahla_ratio")
+    heads = [0, 3]
+    want = BW.ahla_vjp_batched(x["q"], x["k"], x["v"], do, ratio=True, heads=heads)
+    check(tuple(g[heads] for g in got), want, "bf16", "ahla ratio n4096 heads 0,3")
