@@ -244,3 +244,25 @@ def test_hla3_sizes_and_validation(lib):
     assert fwd(so=ctypes.cast(P(8), ctypes.POINTER(ctypes.c_float))) == ERR_UNSUP
     assert fwd(ws=16) == ERR_WS
     assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, None, P(1), None) == ERR_UNSUP
+
+
+def test_binding_fails_loudly_without_the_library():
+    """No CPU fallback: with libhla.so absent, every entry point raises."""
+    import subprocess
+    import sys
+    code = ("import causal_streaming_scans_amd as h\n"
+            "h._LIB_PATH = '/nonexistent/libhla.so'\n"
+            "h._lib = None\n"
+            "try:\n"
+            "    h.load()\n"
+            "except h.HLAError as e:\n"
+            "    print('HLAError', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "HLAError" in r.stdout, r.stdout + r.stderr
+
+
+def test_backward_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 64, 16)
+    with pytest.raises(hla.HLAError):
+        hla.hla_backward(x, x, x, x)
