@@ -15,7 +15,7 @@ gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",
     ahla        o = tril(QK^T) tril(QK^T) V
     ahla_ratio  the same over its v == 1 denominator
     hla3        o = tril(L L^T) L V, L = tril(QK^T)  (third order, section "3.
-                HLA de Tercer Orden"; no decay, no streaming state)
+                HLA de Tercer Orden"; no decay, no ratio form)
 """
 from __future__ import annotations
 

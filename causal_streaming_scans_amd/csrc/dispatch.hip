@@ -19,26 +19,32 @@ hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipSt
     return hipGetLastError();
 }
 
-template <typename T, int D, bool AHLA>
+template <typename T, int D, int MODE>
 hipError_t launch_step(const StepParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((step_kernel<T, D, D, AHLA, 256>), dim3(p.BH), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((step_kernel<T, D, D, MODE, 256>), dim3(p.BH), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
+template <typename T, int D>
+static StepLaunch step_mode(int mode) {
+    return mode == kStepAhla ? launch_step<T, D, kStepAhla>
+         : mode == kStepHla3 ? launch_step<T, D, kStepHla3> : launch_step<T, D, kStepHla2>;
+}
+
 template <typename T>
-static bool step_for(bool ahla, int d, StepLaunch *out) {
+static bool step_for(int mode, int d, StepLaunch *out) {
     switch (d) {
-        case 16: *out = ahla ? launch_step<T, 16, true> : launch_step<T, 16, false>; return true;
-        case 32: *out = ahla ? launch_step<T, 32, true> : launch_step<T, 32, false>; return true;
-        case 64: *out = ahla ? launch_step<T, 64, true> : launch_step<T, 64, false>; return true;
-        case 128: *out = ahla ? launch_step<T, 128, true> : launch_step<T, 128, false>; return true;
+        case 16: *out = step_mode<T, 16>(mode); return true;
+        case 32: *out = step_mode<T, 32>(mode); return true;
+        case 64: *out = step_mode<T, 64>(mode); return true;
+        case 128: *out = step_mode<T, 128>(mode); return true;
         default: return false;
     }
 }
 
-bool lookup_step(int dtype, bool ahla, int d, int dv, StepLaunch *out) {
+bool lookup_step(int dtype, int mode, int d, int dv, StepLaunch *out) {
     if (d != dv) return false;
-    return dtype == 0 ? step_for<float>(ahla, d, out) : step_for<bf16>(ahla, d, out);
+    return dtype == 0 ? step_for<float>(mode, d, out) : step_for<bf16>(mode, d, out);
 }
 
 bool lookup_forward(int dtype, bool ahla, int d, int dv, int chunk, bool decay, FwdKernels *out) {

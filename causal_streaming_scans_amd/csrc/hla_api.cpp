@@ -87,7 +87,8 @@ void fill_gamma(float *dst, const float *gamma, int H) {
 extern "C" {
 
 size_t hla_state_floats(int variant, int d, int dv) {
-    if (!valid_variant(variant) || is_hla3(variant) || d < 1 || dv < 1) return 0;
+    if (!valid_variant(variant) || d < 1 || dv < 1) return 0;
+    if (is_hla3(variant)) return (size_t)hla3_state_floats(d, dv);
     return is_ahla(variant) ? (size_t)ahla_state_floats(d, dv) : (size_t)hla2_state_floats(d, dv);
 }
 
@@ -148,10 +149,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     if (state_in && state_out && state_in == state_out) return HLA_ERR_ARG;
     if (!lookup_forward(dtype, is_ahla(variant), d, dv, chunk, gamma_host != nullptr, kern))
         return HLA_ERR_UNSUPPORTED;
-    // the third-order variant keeps no streaming state (its carried state
-    // would add P^KV to the second-order one)
-    if (is_hla3(variant) && (state_in || state_out || d != dv || !lookup_la(dtype, d, &x3->la)))
-        return HLA_ERR_UNSUPPORTED;
+    if (is_hla3(variant) && (d != dv || !lookup_la(dtype, d, &x3->la))) return HLA_ERR_UNSUPPORTED;
     const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, chunk, g);
@@ -202,6 +200,12 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
         lp.nseg = (int)num_segments(n, kLaChunk, g_la);
         fill_gamma(lp.gamma, nullptr, H);
         p->v = Y;
+        // state: the P^KV blocks of all heads, then the second-order states
+        const size_t pkv = (size_t)B * H * d * dv;
+        lp.state_in = state_in;
+        lp.state_out = state_out;
+        p->state_in = state_in ? state_in + pkv : nullptr;
+        p->state_out = state_out ? state_out + pkv : nullptr;
     }
     return HLA_OK;
 }
@@ -554,9 +558,9 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B,
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (!q || !k || !v || !o || !state) return HLA_ERR_NULL;
-    if (is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
     StepLaunch fn;
-    if (!lookup_step(dtype, is_ahla(variant), d, dv, &fn)) return HLA_ERR_UNSUPPORTED;
+    const int mode = is_hla3(variant) ? kStepHla3 : is_ahla(variant) ? kStepAhla : kStepHla2;
+    if (!lookup_step(dtype, mode, d, dv, &fn)) return HLA_ERR_UNSUPPORTED;
     StepParams p;
     memset(&p, 0, sizeof(p));
     p.q = q;

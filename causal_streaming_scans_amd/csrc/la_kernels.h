@@ -361,6 +361,19 @@ void la_forward_kernel(LaParams p) {
             }
         }
     }
+    if (p.state_in) {
+        // the caller's state before token 0 (passes without decay only)
+        const float *src = p.state_in + (size_t)bh * (D * D);
+#pragma unroll
+        for (int i = 0; i < Cfg::SPW; ++i) {
+            const int m = w + Cfg::NW * i;
+            if (m < Cfg::NS) {
+                const int si = m / Cfg::TD, sj = m % Cfg::TD;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S.acc[i][r] += src[(16 * si + 4 * gq + r) * D + 16 * sj + cl];
+            }
+        }
+    }
     S.store_copy(s, w);
     __syncthreads();
     const float gC = s.pw[C];
@@ -454,6 +467,20 @@ void la_forward_kernel(LaParams p) {
         S.advance(s, gC, w);
         __syncthreads();
         S.store_copy(s, w);
+    }
+    if (p.state_out && seg == p.nseg - 1) {
+        // the state after token n-1 (passes without decay only)
+        float *dst = p.state_out + (size_t)bh * (D * D);
+#pragma unroll
+        for (int i = 0; i < Cfg::SPW; ++i) {
+            const int m = w + Cfg::NW * i;
+            if (m < Cfg::NS) {
+                const int si = m / Cfg::TD, sj = m % Cfg::TD;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(16 * si + 4 * gq + r) * D + 16 * sj + cl] = S.acc[i][r];
+            }
+        }
     }
 }
 

@@ -19,7 +19,8 @@ struct FwdKernels {
 // dtype: 0 = fp32, 1 = bf16.  ahla: AHLA family (else HLA-2).  Returns false
 // when no instance exists for these compile-time parameters.
 bool lookup_forward(int dtype, bool ahla, int d, int dv, int chunk, bool decay, FwdKernels *out);
-bool lookup_step(int dtype, bool ahla, int d, int dv, StepLaunch *out);
+// mode: StepMode (HLA-2, AHLA, third order)
+bool lookup_step(int dtype, int mode, int d, int dv, StepLaunch *out);
 
 // per-(dtype, d) tables, one translation unit each
 bool lookup_forward_f32_16(bool ahla, int chunk, bool decay, FwdKernels *out);

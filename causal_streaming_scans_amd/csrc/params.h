@@ -63,6 +63,9 @@ __device__ inline void forward_slot(const FwdParams &p, int L, int *seg, int *bh
 __host__ __device__ constexpr int summary_floats(int D, int DV) { return D * D + 2 * D * DV + 2 * D; }
 __host__ __device__ constexpr int hla2_state_floats(int D, int DV) { return D * D + D * DV + D; }
 __host__ __device__ constexpr int ahla_state_floats(int D, int DV) { return 2 * D * DV + 2 * D; }
+// third order: [B*H][D*DV] P^KV blocks, then [B*H][hla2_state_floats] the
+// second-order state of (q, k, y), y = P^T q
+__host__ __device__ constexpr int hla3_state_floats(int D, int DV) { return D * DV + hla2_state_floats(D, DV); }
 
 template <int D, int DV>
 struct SumOfs {
@@ -99,6 +102,8 @@ struct LaParams {
     int seg_len;        // tokens per segment, a multiple of the chunk
     int nseg;
     int reverse;        // run the sequence backwards (anti-causal pass)
+    const float *state_in;   // [BH][D*D] state before token 0 (forward passes, decay 1), or null
+    float *state_out;        // [BH][D*D] state after token n-1 (forward passes, decay 1), or null
     float gamma[kMaxDecayHeads];   // decay of head h for this pass
 };
 
@@ -120,5 +125,8 @@ struct StepParams {
     int ratio;
     float gamma[kMaxDecayHeads];
 };
+
+// StepParams' mode of the decode kernel
+enum StepMode { kStepHla2 = 0, kStepAhla = 1, kStepHla3 = 2 };
 
 }  // namespace hla

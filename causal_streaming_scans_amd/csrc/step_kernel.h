@@ -10,6 +10,9 @@
 //        o = q^T W  (ratio: / q^T u)
 // AHLA : P <- P + k v^T ; y = P^T q ; E <- E + k y^T ; mK <- mK + k ;
 //        nk <- nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
+// HLA3 : P <- P + k v^T ; y = P^T q ; then the HLA-2 step on (q, k, y)
+//        without decay (section "3. HLA de Tercer Orden": the third-order
+//        operator read as tril(L L^T) L V; P^KV is the moment it adds)
 //
 // One workgroup of NT threads per (b,h).  The state is read once and written
 // once (fp32, row-major), with consecutive threads on consecutive columns so
@@ -22,8 +25,9 @@
 
 namespace hla {
 
-template <typename T, int D, int DV, bool AHLA, int NT>
+template <typename T, int D, int DV, int MODE, int NT>
 __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
+    constexpr bool AHLA = MODE == kStepAhla, HLA3 = MODE == kStepHla3;
     constexpr int RG = NT / DV;     // row groups of the column-parallel passes
     constexpr int RPT = D / RG;     // rows per thread in those passes
     constexpr int TPR = NT / D;     // threads per row of the S pass (HLA-2)
@@ -35,14 +39,16 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const float g = AHLA ? 1.f : p.gamma[gamma_slot(bh, p.H)];
+    const float g = MODE == kStepHla2 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const float g2 = g * g;
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
     constexpr int STF = AHLA ? ahla_state_floats(D, DV) : hla2_state_floats(D, DV);
-    float *st = p.state + (size_t)bh * STF;
+    // third order: the P^KV blocks of all heads, then their second-order states
+    float *st = HLA3 ? p.state + (size_t)p.BH * D * DV + (size_t)bh * STF
+                     : p.state + (size_t)bh * STF;
     const int col = tid % DV, rg = tid / DV;
 
     auto block_sum = [&](float x) -> float {
@@ -59,15 +65,42 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     if (!AHLA) {
         float *S = st, *W = st + D * D, *u = st + D * D + D * DV;
         const int row = tid / TPR, sub = tid % TPR;
-        float sv_[CPT], wv[RPT], uv = 0.f;
+        float sv_[CPT], wv[RPT], uv = 0.f, pv[HLA3 ? RPT : 1];
+        float *P = p.state + (size_t)bh * D * DV;   // HLA3 only
 #pragma unroll
         for (int i = 0; i < CPT; ++i) sv_[i] = S[row * D + sub + i * TPR];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) wv[i] = W[(rg + i * RG) * DV + col];
+        if constexpr (HLA3) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) pv[i] = P[(rg + i * RG) * DV + col];
+        }
         if (tid < D) uv = u[tid];
         for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
         for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
         __syncthreads();
+        if constexpr (HLA3) {
+            // P <- P + k v^T ; y = P^T q, which then stands in for v
+            float yp = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rg + i * RG;
+                const float pn = pv[i] + sk[r] * sv[col];
+                P[r * DV + col] = pn;
+                yp += sq[r] * pn;
+            }
+            part[rg][col] = yp;
+            __syncthreads();
+            if (tid < DV) {
+                float y = 0.f;
+#pragma unroll
+                for (int i = 0; i < RG; ++i) y += part[i][tid];
+                sy[tid] = y;
+            }
+            __syncthreads();
+            for (int j = tid; j < DV; j += NT) sv[j] = sy[j];
+            __syncthreads();
+        }
         // S <- g S + k k^T ; z = S q
         float zp = 0.f;
 #pragma unroll

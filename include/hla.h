@@ -28,8 +28,7 @@
  *                   o_t = sum_{m<=t} sum_{i<=m} sum_{j<=m} A[t,i] A[m,i] A[m,j] v_j.
  *                   Computed as the second-order operator on the values
  *                   Y = L V (one chunked first-order pass into the workspace);
- *                   no decay, no streaming state (state_in / state_out must be
- *                   NULL, hla_step and hla_state_floats do not apply)
+ *                   no decay, no ratio form
  * g is the per-head decay (1 when gamma is NULL).  No 1/sqrt(d) or other
  * scaling is applied inside.
  *
@@ -40,6 +39,9 @@
  *             W = S^K C^QV - G, u = S^K m^Q - h  (the page's five summaries
  *             folded into the three that a continuation needs)
  *     AHLA  : [ P (d*dv) | E (d*dv) | mK (d) | nk (d) ]  the page's P^KV, E, m^K, n
+ *     HLA3  : not per (b,h) blocks: first the P^KV (d*dv) of every (b,h), then
+ *             every (b,h)'s HLA-2 block [ S | W | u ] of (q, k, y), y = P^T q
+ *             (hla_state_floats() = d*dv + d*d + d*dv + d per (b,h))
  *
  * Ownership: the caller allocates and owns every buffer, including the
  * workspace.  The library allocates no memory, keeps no mutable global state,
@@ -180,6 +182,7 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
  *          o = q^T W  (ratio: / q^T u)
  *   AHLA : P <- P + k v^T; y = P^T q; E <- E + k y^T; mK <- mK + k;
  *          nk <- nk + k (q . mK); o = q^T E  (ratio: / q^T nk)
+ *   HLA3 : P <- P + k v^T; y = P^T q; then the HLA-2 step on (q, k, y)
  * state is device fp32 [B*H][hla_state_floats()], never NULL.
  */
 hla_status hla_step(const void *q, const void *k, const void *v, void *o,

@@ -226,7 +226,8 @@ HLA3 = 4
 
 
 def test_hla3_sizes_and_validation(lib):
-    assert lib.hla_state_floats(HLA3, 64, 64) == 0          # no streaming state
+    # P^KV per head, then the second-order state of (q, k, y)
+    assert lib.hla_state_floats(HLA3, 64, 64) == 64 * 64 + (64 * 64 + 64 * 64 + 64)
     B, H, n, d, chunk, seg = 2, 4, 1000, 64, 64, 4
     nseg = -(-n // (chunk * seg))
     scan = 2 * B * H * (nseg - 1) * (d * d + 2 * d * d + 2 * d) * 4
@@ -240,10 +241,8 @@ def test_hla3_sizes_and_validation(lib):
                                        kw.get("gamma"), chunk, seg, kw.get("si"), kw.get("so"),
                                        P(1), kw.get("ws", 1), None)
     assert fwd(gamma=g2) == ERR_UNSUP                       # no decay for third order
-    assert fwd(si=P(8)) == ERR_UNSUP                        # no streaming state
-    assert fwd(so=ctypes.cast(P(8), ctypes.POINTER(ctypes.c_float))) == ERR_UNSUP
     assert fwd(ws=16) == ERR_WS
-    assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, None, P(1), None) == ERR_UNSUP
+    assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, g2, P(1), None) == ERR_UNSUP
 
 
 def test_binding_fails_loudly_without_the_library():

@@ -60,3 +60,45 @@ def test_hla3_n2048_sampled_heads():
     e = rel_l2(got[heads], want)
     say(f"  rel_l2 {e:.3e}")
     assert e < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64), ("bf16", 128)])
+def test_hla3_resume_and_decode(dtype, d):
+    """Streaming state of the third-order variant: a forward over the first
+    n1 tokens with state_out, a forward over the next n2 tokens continuing
+    from it (state_in), then decode steps (hla_step) continuing from that;
+    every output against the oracle on the whole sequence."""
+    import numpy as np
+    import torch
+    import causal_streaming_scans_amd as hla
+    B, H, n1, n2, T = 1, 3, 190, 150, 4
+    n = n1 + n2 + T
+    say(f"[third order] resume + decode dtype {dtype} d {d} n1 {n1} n2 {n2} steps {T}")
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="normal_scaled" if dtype == "f32" else "l2norm",
+                      seed=1400 + d)
+    want = T3.hla3_batched(x["q"], x["k"], x["v"])
+    stf = hla.state_floats("hla3", d, d)
+    st1 = torch.empty(B * H * stf, dtype=torch.float32, device="cuda")
+    st2 = torch.empty_like(st1)
+
+    def part(a, b):
+        return tuple(to_dev(np.ascontiguousarray(x[key][:, a:b]), dtype, (B, H, b - a, d))
+                     for key in ("q", "k", "v"))
+
+    o1 = hla.hla_forward(*part(0, n1), variant="hla3", chunk=32, seg_chunks=2, state_out=st1)
+    o2 = hla.hla_forward(*part(n1, n1 + n2), variant="hla3", chunk=64, seg_chunks=1, state_in=st1,
+                         state_out=st2)
+    outs = []
+    for t in range(n1 + n2, n):
+        qt, kt, vt = (to_dev(np.ascontiguousarray(x[key][:, t]), dtype, (B, H, d))
+                      for key in ("q", "k", "v"))
+        outs.append(hla.hla_step(qt, kt, vt, st2, variant="hla3"))
+    torch.cuda.synchronize()
+    got1 = from_dev(o1).reshape(B * H, n1, d)
+    got2 = from_dev(o2).reshape(B * H, n2, d)
+    got3 = np.stack([from_dev(o).reshape(B * H, d) for o in outs], axis=1)
+    for label, g, w in (("first", got1, want[:, :n1]), ("resumed", got2, want[:, n1:n1 + n2]),
+                        ("decode", got3, want[:, n1 + n2:])):
+        e = rel_l2(g, w)
+        say(f"  {label}: rel_l2 {e:.3e}")
+        assert e < TOL[dtype], (label, e)
