@@ -102,3 +102,23 @@ def test_hla3_resume_and_decode(dtype, d):
         e = rel_l2(g, w)
         say(f"  {label}: rel_l2 {e:.3e}")
         assert e < TOL[dtype], (label, e)
+
+
+def test_hla3_stages_equal_whole():
+    """hla_forward_stage 1, 2, 3 in order (stage 1 also runs the first-order
+    pass into the workspace) give exactly hla_forward's output."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    B, H, n, d, chunk, seg = 1, 2, 700, 64, 64, 2
+    say(f"[third order] stages vs whole B={B} H={H} n={n} d={d}")
+    x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist="l2norm", seed=1501)
+    q, k, v = (to_dev(x[key], "bf16", (B, H, n, d)) for key in ("q", "k", "v"))
+    whole = hla.hla_forward(q, k, v, variant="hla3", chunk=chunk, seg_chunks=seg)
+    ws = torch.empty(hla.workspace_bytes("hla3", B, H, n, d, d, chunk, seg), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(whole)
+    for stage in (1, 2, 3):
+        hla.hla_forward_stage(stage, q, k, v, variant="hla3", chunk=chunk, seg_chunks=seg,
+                              out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, whole)
