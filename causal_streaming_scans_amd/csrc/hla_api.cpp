@@ -82,6 +82,178 @@ void fill_gamma(float *dst, const float *gamma, int H) {
     for (int h = 0; h < kMaxDecayHeads; ++h) dst[h] = (gamma && h < H) ? gamma[h] : 1.f;
 }
 
+// ------------------------------------------------------------ backward passes
+//
+// Each pass is one chunked linear-attention launch pair (la_kernels.h): a
+// segment-state launch (unless `summaries` is false and `sums` already holds
+// the states of the same b, c and decay) and the main launch, in the plain,
+// SYM or DUAL form.  The pass lists below are in dependency order.
+
+enum Form { PLAIN, SYM, DUAL };
+
+struct Pass {
+    const LaParams *base;   // sizes and decay (g or g^2)
+    const void *a, *b, *c, *add;
+    void *out;
+    int rev;                // anti-causal: run backwards through memory
+    Form form;
+    float *sums;
+    bool summaries;
+    const void *a2;         // DUAL: second queries, output and addend
+    void *out2;
+    const void *add2;
+};
+
+// Inputs and gradients of one backward call.
+struct Grads {
+    const void *q, *k, *v, *dout;
+    void *dq, *dk, *dv;
+};
+
+struct BwdCtx {
+    LaLaunches la;
+    LaParams p1, p2;        // decay g and g^2
+    float *sums_kk, *sums;  // K K^T states (first and last pass), the rest
+    char *ws;
+    size_t sums_bytes, tensor_bytes;
+    long rows;
+    hipStream_t s;
+
+    // workspace tensor i of [B*H*n*d] after the segment states
+    void *tensor(int i) const { return ws + 2 * sums_bytes + (size_t)i * tensor_bytes; }
+
+    bool run(const Pass &ps) const {
+        LaParams p = *ps.base;
+        p.a = ps.a;
+        p.b = ps.b;
+        p.c = ps.c;
+        p.add = ps.add;
+        p.out = ps.out;
+        p.a2 = ps.a2;
+        p.out2 = ps.out2;
+        p.add2 = ps.add2;
+        p.reverse = ps.rev;
+        p.sums = ps.sums;
+        const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
+        return fn(p, s, ps.summaries) == hipSuccess;
+    }
+    hla_status run_all(const Pass *ps, int count) const {
+        for (int i = 0; i < count; ++i)
+            if (!run(ps[i])) return HLA_ERR_DEVICE;
+        return HLA_OK;
+    }
+};
+
+// HLA-2: Z = LA_g(Q, K, K), O = LA_{g^2}(Q, Z, V) (Z, dZ in tensors 0, 1).
+hla_status backward_hla2(const BwdCtx &c, const Grads &x) {
+    void *Z = c.tensor(0), *dZ = c.tensor(1);
+    const Pass passes[5] = {
+        // Z  = LA_g(Q, K, K)
+        {&c.p1, x.q, x.k, x.k, nullptr, Z, 0, PLAIN, c.sums_kk, true, nullptr, nullptr, nullptr},
+        // dQ = LA_g2(dO, V, Z)
+        {&c.p2, x.dout, x.v, Z, nullptr, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dZ = RLA_g2(V, dO, Q) and dV = RLA_g2(Z, Q, dO): one state, sum dO Q^T
+        {&c.p2, x.v, x.dout, x.q, nullptr, dZ, 1, DUAL, c.sums, true, Z, x.dv, nullptr},
+        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+        {&c.p1, x.k, dZ, x.q, nullptr, x.dk, 1, SYM, c.sums, true, nullptr, nullptr, nullptr},
+        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
+        {&c.p1, dZ, x.k, x.k, x.dq, x.dq, 0, PLAIN, c.sums_kk, false, nullptr, nullptr, nullptr},
+    };
+    return c.run_all(passes, 5);
+}
+
+// AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y, dY in tensors 0, 1).
+hla_status backward_ahla(const BwdCtx &c, const Grads &x) {
+    void *Y = c.tensor(0), *dY = c.tensor(1);
+    const Pass passes[5] = {
+        // Y  = LA(Q, K, V)
+        {&c.p1, x.q, x.k, x.v, nullptr, Y, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dQ = LA(dO, Y, K)
+        {&c.p1, x.dout, Y, x.k, nullptr, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dY = RLA(K, Q, dO) and dK = RLA(Y, dO, Q): one state, sum Q dO^T
+        {&c.p1, x.k, x.q, x.dout, nullptr, dY, 1, DUAL, c.sums, true, Y, x.dk, nullptr},
+        // dV = RLA(K, Q, dY) and dK += RLA(V, dY, Q): one state, sum Q dY^T
+        {&c.p1, x.k, x.q, dY, nullptr, x.dv, 1, DUAL, c.sums, true, x.v, x.dk, x.dk},
+        // dQ += LA(dY, V, K)
+        {&c.p1, dY, x.v, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+    };
+    return c.run_all(passes, 5);
+}
+
+// Ratio HLA-2, o = num / den with den the v == 1 sum.  With G = dO / den and
+// e = -(dO . o) / den per row, the gradient is that of num with upstream G,
+// plus den's: dq += e_t u_t, u = LA_g2(ONE1, ONE1, Z) (u_t = sum_j
+// g^(2(t-j)) z_j), and dZ += RLA_g2(ONE1, E1, Q) (sum_{t>=j} g^(2(t-j)) e_t q_t),
+// where ONE1 has rows (1, 0, ..., 0) and E1 rows (e_t, 0, ..., 0).  den is
+// q_t . u_t and num = LA_g2(Q, Z, V); u lives in dv and num in dZ's buffer
+// until the passes that overwrite them.  Tensors: Z, dZ, G, E1, ONE1.
+hla_status backward_hla2_ratio(const BwdCtx &c, const Grads &x) {
+    void *Z = c.tensor(0), *dZ = c.tensor(1), *G = c.tensor(2), *E1 = c.tensor(3),
+         *ONE1 = c.tensor(4);
+    if (c.la.unit_column(ONE1, c.rows, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass pre[3] = {
+        // Z  = LA_g(Q, K, K)
+        {&c.p1, x.q, x.k, x.k, nullptr, Z, 0, PLAIN, c.sums_kk, true, nullptr, nullptr, nullptr},
+        // u  = LA_g2(ONE1, ONE1, Z)
+        {&c.p2, ONE1, ONE1, Z, nullptr, x.dv, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // num = LA_g2(Q, Z, V)
+        {&c.p2, x.q, Z, x.v, nullptr, dZ, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+    };
+    hla_status st = c.run_all(pre, 3);
+    if (st != HLA_OK) return st;
+    const RatioPrepParams rp{x.q, x.dv, dZ, x.dout, G, E1, x.dq, c.rows};
+    if (c.la.ratio_prep(rp, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass post[5] = {
+        // dQ = e u + LA_g2(G, V, Z)
+        {&c.p2, G, x.v, Z, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dZ = RLA_g2(V, G, Q) and dV = RLA_g2(Z, Q, G)
+        {&c.p2, x.v, G, x.q, nullptr, dZ, 1, DUAL, c.sums, true, Z, x.dv, nullptr},
+        // dZ += RLA_g2(ONE1, E1, Q)
+        {&c.p2, ONE1, E1, x.q, dZ, dZ, 1, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
+        {&c.p1, x.k, dZ, x.q, nullptr, x.dk, 1, SYM, c.sums, true, nullptr, nullptr, nullptr},
+        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
+        {&c.p1, dZ, x.k, x.k, x.dq, x.dq, 0, PLAIN, c.sums_kk, false, nullptr, nullptr, nullptr},
+    };
+    return c.run_all(post, 5);
+}
+
+// Ratio AHLA: num = LA(Q, K, Y), den = first column of LA(Q, K, Y1) with
+// Y = LA(Q, K, V), Y1 = LA(Q, K, ONE1).  The gradient is the AHLA chain with
+// upstream G on values V plus the AHLA chain with upstream E1 on values ONE1
+// (whose value gradient is dropped).  Tensors: Y, dY, G, E1, ONE1, Y1, dY1;
+// num lives in dY's buffer and den in dY1's until those are written.
+hla_status backward_ahla_ratio(const BwdCtx &c, const Grads &x) {
+    void *Y = c.tensor(0), *dY = c.tensor(1), *G = c.tensor(2), *E1 = c.tensor(3),
+         *ONE1 = c.tensor(4), *Y1 = c.tensor(5), *dY1 = c.tensor(6);
+    if (c.la.unit_column(ONE1, c.rows, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass pre[4] = {
+        {&c.p1, x.q, x.k, x.v, nullptr, Y, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},    // Y
+        {&c.p1, x.q, x.k, ONE1, nullptr, Y1, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},  // Y1
+        {&c.p1, x.q, x.k, Y, nullptr, dY, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},     // num
+        {&c.p1, x.q, x.k, Y1, nullptr, dY1, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},   // den
+    };
+    hla_status st = c.run_all(pre, 4);
+    if (st != HLA_OK) return st;
+    // den = ONE1_t . DEN_t, the first column; the row kernel's e u output is
+    // not used here and goes to dv, which a later pass writes
+    const RatioPrepParams rp{ONE1, dY1, dY, x.dout, G, E1, x.dv, c.rows};
+    if (c.la.ratio_prep(rp, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+    const Pass post[8] = {
+        // upstream G, values V
+        {&c.p1, G, Y, x.k, nullptr, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        {&c.p1, x.k, x.q, G, nullptr, dY, 1, DUAL, c.sums, true, Y, x.dk, nullptr},
+        {&c.p1, x.k, x.q, dY, nullptr, x.dv, 1, DUAL, c.sums, true, x.v, x.dk, x.dk},
+        {&c.p1, dY, x.v, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // upstream E1, values ONE1
+        {&c.p1, E1, Y1, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        {&c.p1, x.k, x.q, E1, nullptr, dY1, 1, DUAL, c.sums, true, Y1, x.dk, x.dk},
+        {&c.p1, ONE1, dY1, x.q, x.dk, x.dk, 1, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        {&c.p1, dY1, ONE1, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+    };
+    return c.run_all(post, 8);
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,12 +518,12 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
-    // the ratio form runs its passes in fp32 (its gradient with respect to q
-    // and k is a small difference of large terms, which bf16 intermediates
-    // do not resolve)
+    // the ratio forms run their passes in fp32 (their gradient with respect
+    // to q and k is a small difference of large terms, which bf16
+    // intermediates do not resolve)
     const int run_dtype = is_ratio(variant) ? HLA_F32 : dtype;
-    LaLaunches la;
-    if (!lookup_la(run_dtype, d, &la)) return HLA_ERR_UNSUPPORTED;
+    BwdCtx c;
+    if (!lookup_la(run_dtype, d, &c.la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) return HLA_OK;
     if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
@@ -363,192 +535,51 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (!workspace) return HLA_ERR_NULL;
     if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
 
-    const size_t esz = backward_elem_bytes(variant, dtype);
-    const size_t sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    char *ws = static_cast<char *>(workspace);
-    float *sums_kk = reinterpret_cast<float *>(ws);               // states of K K^T (g)
-    float *sums = reinterpret_cast<float *>(ws + sums_bytes);     // the other passes'
-    const size_t tensor_bytes = (size_t)B * H * n * d * esz;
-    void *Z = ws + 2 * sums_bytes;
-    void *dZ = ws + 2 * sums_bytes + tensor_bytes;
+    // workspace: the K K^T segment states (kept from the first pass to the
+    // last), the other passes' segment states, then [B*H*n*d] tensors
+    c.ws = static_cast<char *>(workspace);
+    c.sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
+    c.tensor_bytes = (size_t)B * H * n * d * backward_elem_bytes(variant, dtype);
+    c.sums_kk = reinterpret_cast<float *>(c.ws);
+    c.sums = reinterpret_cast<float *>(c.ws + c.sums_bytes);
+    c.rows = (long)B * H * n;
+    c.s = static_cast<hipStream_t>(stream);
+    memset(&c.p1, 0, sizeof(c.p1));   // decay g
+    c.p1.BH = B * H;
+    c.p1.H = H;
+    c.p1.n = n;
+    c.p1.seg_len = kLaChunk * g;
+    c.p1.nseg = (int)nseg;
+    fill_gamma(c.p1.gamma, gamma_host, H);
+    c.p2 = c.p1;                      // decay g^2
+    for (int h = 0; h < kMaxDecayHeads; ++h) c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h];
 
-    LaParams p1, p2;   // decay g and g^2
-    memset(&p1, 0, sizeof(p1));
-    p1.sums = sums;
-    p1.BH = B * H;
-    p1.H = H;
-    p1.n = n;
-    p1.seg_len = kLaChunk * g;
-    p1.nseg = (int)nseg;
-    fill_gamma(p1.gamma, gamma_host, H);
-    p2 = p1;
-    for (int h = 0; h < kMaxDecayHeads; ++h) p2.gamma[h] = p1.gamma[h] * p1.gamma[h];
-
-    enum Form { PLAIN, SYM, DUAL };
-    struct Pass {
-        LaParams *base; const void *a, *b, *c, *add; void *out; int rev; Form form;
-        float *sums; bool summaries; const void *a2; void *out2; const void *add2;
-    };
-    // HLA-2 (Z in the workspace's first tensor, dZ in the second)
-    const Pass hla2_passes[5] = {
-        // Z  = LA_g(Q, K, K)
-        {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
-        // dQ = LA_g2(dO, V, Z)
-        {&p2, dout, v, Z, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // dZ = RLA_g2(V, dO, Q) and dV = RLA_g2(Z, Q, dO): one state, sum dO Q^T
-        {&p2, v, dout, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
-        // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
-        {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
-        // dQ += LA_g(dZ, K, K), with the segment states of the first pass
-        {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
-    };
-    // AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y and dY in the workspace)
-    const Pass ahla_passes[5] = {
-        // Y  = LA(Q, K, V)
-        {&p1, q, k, v, nullptr, Z, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // dQ = LA(dO, Y, K)
-        {&p1, dout, Z, k, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        // dY = RLA(K, Q, dO) and dK = RLA(Y, dO, Q): one state, sum Q dO^T
-        {&p1, k, q, dout, nullptr, dZ, 1, DUAL, sums, true, Z, dk, nullptr},
-        // dV = RLA(K, Q, dY) and dK += RLA(V, dY, Q): one state, sum Q dY^T
-        {&p1, k, q, dZ, nullptr, dv_out, 1, DUAL, sums, true, v, dk, dk},
-        // dQ += LA(dY, V, K)
-        {&p1, dZ, v, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-    };
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto run = [&](const Pass &ps) {
-        LaParams p = *ps.base;
-        p.a = ps.a;
-        p.b = ps.b;
-        p.c = ps.c;
-        p.add = ps.add;
-        p.out = ps.out;
-        p.a2 = ps.a2;
-        p.out2 = ps.out2;
-        p.add2 = ps.add2;
-        p.reverse = ps.rev;
-        p.sums = ps.sums;
-        const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
-        return fn(p, s, ps.summaries) == hipSuccess;
-    };
-    if (!is_ratio(variant)) {
-        const Pass *passes = variant == HLA_AHLA ? ahla_passes : hla2_passes;
-        for (int i = 0; i < 5; ++i)
-            if (!run(passes[i])) return HLA_ERR_DEVICE;
-        return HLA_OK;
-    }
-
-    // Ratio form, o = num / den with den the v == 1 sum.  With G = dO / den and
-    // e = -(dO . o) / den per row, the gradient is that of num with upstream
-    // G, plus den's: dq += e_t u_t, u = LA_g2(ONE1, ONE1, Z) (u_t = sum_j
-    // g^(2(t-j)) z_j), and dZ += RLA_g2(ONE1, E1, Q) (sum_{t>=j} g^(2(t-j)) e_t q_t),
-    // where ONE1 has rows (1, 0, ..., 0) and E1 rows (e_t, 0, ..., 0).  den
-    // itself is q_t . u_t and num = LA_g2(Q, Z, V).  u lives in dv_out and num
-    // in dZ's buffer until the passes that overwrite them.
-    void *G = ws + 2 * sums_bytes + 2 * tensor_bytes;
-    void *E1 = ws + 2 * sums_bytes + 3 * tensor_bytes;
-    void *ONE1 = ws + 2 * sums_bytes + 4 * tensor_bytes;
-    const int own = variant == HLA_AHLA_RATIO ? 7 : 5;
-    const long rows = (long)B * H * n;
-    const long count = rows * d;
-    // bf16 inputs: every pass below reads and writes fp32 copies
-    void *dq_out = dq, *dk_out = dk, *dv_user = dv_out;
+    Grads io{q, k, v, dout, dq, dk, dv_out};
+    if (variant == HLA_HLA2) return backward_hla2(c, io);
+    if (variant == HLA_AHLA) return backward_ahla(c, io);
+    // ratio forms: with bf16 inputs every pass reads and writes fp32 copies
+    // (after the variant's own tensors in the workspace)
+    Grads run = io;
+    const int own = backward_tensors(variant, HLA_F32);
+    const long count = c.rows * d;
     if (dtype == HLA_BF16) {
-        void *w32[7];
-        for (int i = 0; i < 7; ++i) w32[i] = ws + 2 * sums_bytes + (own + i) * tensor_bytes;
         const void *src[4] = {q, k, v, dout};
-        for (int i = 0; i < 4; ++i)
-            if (launch_convert(src[i], w32[i], count, true, s) != hipSuccess) return HLA_ERR_DEVICE;
-        q = w32[0];
-        k = w32[1];
-        v = w32[2];
-        dout = w32[3];
-        dq = w32[4];
-        dk = w32[5];
-        dv_out = w32[6];
+        const void **dst_in[4] = {&run.q, &run.k, &run.v, &run.dout};
+        for (int i = 0; i < 4; ++i) {
+            *dst_in[i] = c.tensor(own + i);
+            if (launch_convert(src[i], c.tensor(own + i), count, true, c.s) != hipSuccess)
+                return HLA_ERR_DEVICE;
+        }
+        run.dq = c.tensor(own + 4);
+        run.dk = c.tensor(own + 5);
+        run.dv = c.tensor(own + 6);
     }
-    if (la.unit_column(ONE1, rows, s) != hipSuccess) return HLA_ERR_DEVICE;
-    if (variant == HLA_AHLA_RATIO) {
-        // AHLA: num = LA(Q, K, Y), den = first column of LA(Q, K, Y1) with
-        // Y = LA(Q, K, V), Y1 = LA(Q, K, ONE1).  The gradient is the AHLA
-        // chain with upstream G on values V plus the AHLA chain with
-        // upstream E1 on values ONE1 (whose value gradient is dropped).
-        void *Y1 = ws + 2 * sums_bytes + 5 * tensor_bytes;
-        void *dY1 = ws + 2 * sums_bytes + 6 * tensor_bytes;
-        const Pass apre[4] = {
-            {&p1, q, k, v, nullptr, Z, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},       // Y
-            {&p1, q, k, ONE1, nullptr, Y1, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},   // Y1
-            {&p1, q, k, Z, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},      // num
-            {&p1, q, k, Y1, nullptr, dY1, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},    // den
-        };
-        for (const Pass &ps : apre)
-            if (!run(ps)) return HLA_ERR_DEVICE;
-        RatioPrepParams ap;
-        ap.q = ONE1;      // den = ONE1_t . DEN_t, the first column
-        ap.u = dY1;
-        ap.num = dZ;
-        ap.dout = dout;
-        ap.g = G;
-        ap.e1 = E1;
-        ap.dq = dv_out;   // unused here; dv_out is written by a later pass
-        ap.rows = rows;
-        if (la.ratio_prep(ap, s) != hipSuccess) return HLA_ERR_DEVICE;
-        const Pass apost[8] = {
-            // upstream G, values V
-            {&p1, G, Z, k, nullptr, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            {&p1, k, q, G, nullptr, dZ, 1, DUAL, sums, true, Z, dk, nullptr},
-            {&p1, k, q, dZ, nullptr, dv_out, 1, DUAL, sums, true, v, dk, dk},
-            {&p1, dZ, v, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            // upstream E1, values ONE1
-            {&p1, E1, Y1, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            {&p1, k, q, E1, nullptr, dY1, 1, DUAL, sums, true, Y1, dk, dk},
-            {&p1, ONE1, dY1, q, dk, dk, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            {&p1, dY1, ONE1, k, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        };
-        for (const Pass &ps : apost)
-            if (!run(ps)) return HLA_ERR_DEVICE;
-    } else {
-        const Pass pre[3] = {
-            // Z  = LA_g(Q, K, K)
-            {&p1, q, k, k, nullptr, Z, 0, PLAIN, sums_kk, true, nullptr, nullptr, nullptr},
-            // u  = LA_g2(ONE1, ONE1, Z)
-            {&p2, ONE1, ONE1, Z, nullptr, dv_out, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            // num = LA_g2(Q, Z, V)
-            {&p2, q, Z, v, nullptr, dZ, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-        };
-        for (const Pass &ps : pre)
-            if (!run(ps)) return HLA_ERR_DEVICE;
-        RatioPrepParams rp;
-        rp.q = q;
-        rp.u = dv_out;
-        rp.num = dZ;
-        rp.dout = dout;
-        rp.g = G;
-        rp.e1 = E1;
-        rp.dq = dq;
-        rp.rows = rows;
-        if (la.ratio_prep(rp, s) != hipSuccess) return HLA_ERR_DEVICE;
-        const Pass post[5] = {
-            // dQ = e u + LA_g2(G, V, Z)
-            {&p2, G, v, Z, dq, dq, 0, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            // dZ = RLA_g2(V, G, Q) and dV = RLA_g2(Z, Q, G)
-            {&p2, v, G, q, nullptr, dZ, 1, DUAL, sums, true, Z, dv_out, nullptr},
-            // dZ += RLA_g2(ONE1, E1, Q)
-            {&p2, ONE1, E1, q, dZ, dZ, 1, PLAIN, sums, true, nullptr, nullptr, nullptr},
-            // dK = RLA_g(K, dZ, Q) + RLA_g(K, Q, dZ)
-            {&p1, k, dZ, q, nullptr, dk, 1, SYM, sums, true, nullptr, nullptr, nullptr},
-            // dQ += LA_g(dZ, K, K), with the segment states of the first pass
-            {&p1, dZ, k, k, dq, dq, 0, PLAIN, sums_kk, false, nullptr, nullptr, nullptr},
-        };
-        for (const Pass &ps : post)
-            if (!run(ps)) return HLA_ERR_DEVICE;
-    }
-    if (dtype == HLA_BF16) {
-        void *dst[3] = {dq_out, dk_out, dv_user};
-        const void *src[3] = {dq, dk, dv_out};
-        for (int i = 0; i < 3; ++i)
-            if (launch_convert(src[i], dst[i], count, false, s) != hipSuccess) return HLA_ERR_DEVICE;
-    }
+    st = variant == HLA_HLA2_RATIO ? backward_hla2_ratio(c, run) : backward_ahla_ratio(c, run);
+    if (st != HLA_OK || dtype != HLA_BF16) return st;
+    void *dst[3] = {dq, dk, dv_out};
+    const void *src[3] = {run.dq, run.dk, run.dv};
+    for (int i = 0; i < 3; ++i)
+        if (launch_convert(src[i], dst[i], count, false, c.s) != hipSuccess) return HLA_ERR_DEVICE;
     return HLA_OK;
 }
 
