@@ -99,12 +99,12 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
     print(f"settle + warm-up steps skipped: {skip}; K = {K}")
     # backward leg: its last `backward_steps` passes of la_ launches, by
     # position within a pass (the pass order of hla_backward)
-    bwd = [r for r in rows if "la_" in r["Kernel_Name"]]
+    bwd = [r for r in rows if is_la_kernel(r["Kernel_Name"])]
     nb = (rec.get("backward") or {}).get("launches_per_step", 0)
     Kb = (rec.get("backward") or {}).get("steps", 0)
     for name, us in per.items():
-        if "la_" in name or not any(x in name for x in ("summary_kernel", "up_sweep_kernel",
-                                                        "forward_kernel")):
+        if is_la_kernel(name) or not any(x in name for x in ("summary_kernel", "up_sweep_kernel",
+                                                             "forward_kernel")):
             continue
         parts = {"timed": us[skip:skip + K], "stages": us[skip + K:skip + 2 * K],
                  "back-to-back": us[skip + 2 * K:skip + 3 * K]}
@@ -124,6 +124,13 @@ def trace_summary(trace_csv: str, bench_json: str) -> None:
             print(f"    {i:2d} {kernel_key(last[i]['Kernel_Name']):20s} grid {last[i]['Grid_Size_X']:>8s}"
                   f"  avg {statistics.fmean(v):8.2f} us")
         print(f"    sum of averages {total:8.2f} us")
+
+
+def is_la_kernel(name: str) -> bool:
+    """A first-order linear-attention kernel (backward passes, third order's
+    Y), not an AHLA kernel whose name also contains "la_"."""
+    import re
+    return re.search(r"(?<![a-z])la_(summary|forward)_kernel", name) is not None
 
 
 def kernel_key(name: str) -> str:

@@ -207,3 +207,99 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 }
 
 }  // namespace hla
+
+namespace hla {
+
+// The unnormalised AHLA step split over column slices of 16 value columns:
+// workgroup (bh, slice) owns columns [16 slice, 16 slice + 16) of P and E.
+// y_j = P[:, j]^T q and E's column j need only column j, so the slices are
+// independent.  mK and nk feed only the ratio form's denominator: slice 0
+// alone reads and updates them, so no two workgroups touch the same state
+// word.  (The ratio form needs q . nk in every slice and keeps the
+// one-workgroup kernel above.)  At d = 64 that is four workgroups per head
+// instead of one, so a decode step of few heads reaches more of the chip.
+template <typename T, int D, int DV, int NT>
+__global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
+    constexpr int SW = 16;              // columns per slice
+    constexpr int RG = NT / SW;         // row groups
+    constexpr int RPT = D / RG;         // rows per thread
+    static_assert(DV % SW == 0 && NT % SW == 0 && D % RG == 0, "block shape");
+    __shared__ float sq[D], sk[D], sv[SW], sy[SW];
+    __shared__ float part[RG][SW];
+
+    const int nsl = DV / SW;
+    const int bh = blockIdx.x / nsl, slice = blockIdx.x % nsl;
+    const int tid = threadIdx.x;
+    const int col = tid % SW, rg = tid / SW;
+    const int j = slice * SW + col;     // this thread's value column
+    const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
+    const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
+    const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
+    T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
+    float *st = p.state + (size_t)bh * ahla_state_floats(D, DV);
+    float *P = st, *E = st + D * DV, *mK = st + 2 * D * DV, *nk = mK + D;
+
+    float pv[RPT], ev[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        pv[i] = P[(rg + i * RG) * DV + j];
+        ev[i] = E[(rg + i * RG) * DV + j];
+    }
+    for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
+    if (tid < SW) sv[tid] = to_f(v[slice * SW + tid]);
+    __syncthreads();
+    if (slice == 0) {
+        // mK <- mK + k ; nk <- nk + k (q . mK), owned by this workgroup alone
+        __shared__ float red[NT / kWave];
+        float mkv = 0.f, sp = 0.f;
+        if (tid < D) {
+            mkv = mK[tid] + sk[tid];
+            mK[tid] = mkv;
+            sp = sq[tid] * mkv;
+        }
+        for (int m = kWave / 2; m >= 1; m >>= 1) sp += __shfl_xor(sp, m);
+        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sp;
+        __syncthreads();
+        float s_all = 0.f;
+#pragma unroll
+        for (int i = 0; i < NT / kWave; ++i) s_all += red[i];
+        if (tid < D) nk[tid] += sk[tid] * s_all;
+    }
+    // P <- P + k v^T ; partial y = P^T q
+    float yp = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        const float pn = pv[i] + sk[r] * sv[col];
+        P[r * DV + j] = pn;
+        yp += sq[r] * pn;
+    }
+    part[rg][col] = yp;
+    __syncthreads();
+    if (tid < SW) {
+        float y = 0.f;
+#pragma unroll
+        for (int i = 0; i < RG; ++i) y += part[i][tid];
+        sy[tid] = y;
+    }
+    __syncthreads();
+    // E <- E + k y^T ; partial o = q^T E
+    float op = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        const float en = ev[i] + sk[r] * sy[col];
+        E[r * DV + j] = en;
+        op += sq[r] * en;
+    }
+    part[rg][col] = op;
+    __syncthreads();
+    if (tid < SW) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < RG; ++i) s += part[i][tid];
+        o[slice * SW + tid] = from_f<T>(s);
+    }
+}
+
+}  // namespace hla

@@ -29,6 +29,14 @@ def test_kernel_keys():
         "la_forward_kernel_f32"
 
 
+def test_la_kernel_filter():
+    assert bench.is_la_kernel("_ZN3hla17la_forward_kernelIDF16bLi64ELi64ELb0ELb0EEEvNS_8LaParamsE")
+    assert bench.is_la_kernel("void hla::la_summary_kernel<float, 64, 32, true, false>(hla::LaParams)")
+    assert not bench.is_la_kernel("_ZN3hla23ahla_step_sliced_kernelIDF16bLi64ELi64ELi256EEEvNS_10StepParamsE")
+    assert not bench.is_la_kernel("_ZN3hla19ahla_forward_kernelIDF16bLi64ELi64ELi64EEEvNS_9FwdParamsE")
+    assert not bench.is_la_kernel("_ZN3hla19hla2_forward_kernelIDF16bLi64ELi64ELi64ELb0EEEvNS_9FwdParamsE")
+
+
 def _csv(path, counter, rows):
     cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     with open(path, "w", newline="") as fh:
