@@ -203,6 +203,48 @@ def counters_summary(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def all_configs(args, hla, I, torch, dev):
+    """Forward time of every named workload in its default launch
+    configuration (each one library call between two events, after a settle
+    phase); one JSON line.  Only the forward is timed: the AHLA workload's
+    decode tokens are timed by the default run."""
+    rows = []
+    for key, w in I.WORKLOADS.items():
+        x = I.workload_inputs(key, decode_tokens=0)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        shp = (w.B, w.H, w.n, w.d)
+        q, k, v = (torch.from_numpy(x[n]).reshape(shp).to(dev, tdt).contiguous() for n in "qkv")
+        gamma = x["gamma"]
+        del x
+        plan = hla.ForwardPlan(q, k, v, variant=w.variant, gamma=gamma, chunk=w.chunk)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        settle = 0.0
+        while settle < 200.0:
+            e0.record()
+            for _ in range(20):
+                plan.run()
+            e1.record()
+            torch.cuda.synchronize()
+            settle += e0.elapsed_time(e1)
+        K = max(20, args.steps // 10)
+        e0.record()
+        for _ in range(K):
+            plan.run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        tokens = w.B * w.H * w.n
+        esz = 2 if w.dtype == "bf16" else 4
+        lean = tokens * (2 * w.d + 2 * w.dv) * esz
+        rows.append({"workload": w.name, "timed": "forward", "variant": w.variant, "chunk": w.chunk,
+                     "seg_chunks": hla.default_seg_chunks(w.variant, w.B, w.H, w.n, w.d, w.chunk),
+                     "ms": round(ms, 5), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+                     "lean_hbm_frac": round(lean / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"[bench] {w.name}: {ms:.4f} ms, {tokens / (ms * 1e-3) / 1e9:.3f} G tokens/s")
+        del q, k, v, plan
+    print(json.dumps({"forward_per_workload": rows}), flush=True)
+
+
 def flops_per_token(c, d, dv):
     # dense products of the chunked method per token: scores 2cd, Q S0 2d^2,
     # L K 2cd, Q Z^T 2cd, P V 2c dv, Q W0 2d dv, S update 2d^2, W update 2d dv
@@ -231,6 +273,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the workload, run a plain elementwise copy (torch.neg) of "
                          "this many MiB in and out, whose HBM counters scale the kernel's")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="time the forward of every named workload (and the AHLA decode), "
+                         "print one JSON line, then exit")
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic record from two rocprofv3 --pmc counter csv "
@@ -262,6 +307,9 @@ def main():
     hla.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.all_configs:
+        all_configs(args, hla, I, torch, dev)
+        return
     if args.copy_calibration_mib > 0:
         nel = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.ones(nel, dtype=torch.bfloat16, device=dev)
@@ -274,7 +322,7 @@ def main():
     w = I.WORKLOADS["ratio_n4096"]
     B, H, n, d, dv, chunk = w.B, w.H, w.n, w.d, w.dv, args.chunk
     variant = w.variant
-    seg = args.seg_chunks or hla.default_seg_chunks(variant, B, H, n, chunk)
+    seg = args.seg_chunks or hla.default_seg_chunks(variant, B, H, n, d, chunk)
     nseg = -(-n // (chunk * seg))
     log(f"[bench] workload {w.name}: chunk {chunk}, {seg} chunks/segment, {nseg} segments")
 

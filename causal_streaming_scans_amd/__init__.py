@@ -58,7 +58,7 @@ def load():
     FP = ctypes.POINTER(ctypes.c_float)
     lib.hla_state_floats.argtypes = [I, I, I]
     lib.hla_state_floats.restype = Z
-    lib.hla_default_seg_chunks.argtypes = [I, I, I, I, I]
+    lib.hla_default_seg_chunks.argtypes = [I, I, I, I, I, I]
     lib.hla_default_seg_chunks.restype = I
     lib.hla_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.hla_workspace_bytes.restype = Z
@@ -96,8 +96,8 @@ def state_floats(variant, d: int, dv: int) -> int:
     return int(load().hla_state_floats(_variant(variant), d, dv))
 
 
-def default_seg_chunks(variant, B, H, n, chunk) -> int:
-    return int(load().hla_default_seg_chunks(_variant(variant), B, H, n, chunk))
+def default_seg_chunks(variant, B, H, n, d, chunk) -> int:
+    return int(load().hla_default_seg_chunks(_variant(variant), B, H, n, d, chunk))
 
 
 def workspace_bytes(variant, B, H, n, d, dv, chunk, seg_chunks=0) -> int:

@@ -31,8 +31,8 @@ bool is_ratio(int v) { return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO; }
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
-int effective_seg_chunks(int variant, int B, int H, int n, int chunk, int seg_chunks) {
-    return seg_chunks > 0 ? seg_chunks : hla_default_seg_chunks(variant, B, H, n, chunk);
+int effective_seg_chunks(int variant, int B, int H, int n, int d, int chunk, int seg_chunks) {
+    return seg_chunks > 0 ? seg_chunks : hla_default_seg_chunks(variant, B, H, n, d, chunk);
 }
 
 long num_segments(int n, int chunk, int seg_chunks) {
@@ -264,15 +264,18 @@ size_t hla_state_floats(int variant, int d, int dv) {
     return is_ahla(variant) ? (size_t)ahla_state_floats(d, dv) : (size_t)hla2_state_floats(d, dv);
 }
 
-int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk) {
+int hla_default_seg_chunks(int variant, int B, int H, int n, int d, int chunk) {
     (void)variant;
-    if (B < 1 || H < 1 || n < 1 || chunk < 1) return 1;
+    if (B < 1 || H < 1 || n < 1 || d < 1 || chunk < 1) return 1;
     const long nch = ceil_div(n, chunk);
     const long bh = (long)B * H;
     // Enough segments to give the 256 compute units about two workgroups
     // each, but no segment shorter than 8 chunks: short segments add summary
-    // work and scan depth without adding useful parallelism.
-    const long target_wg = 512;
+    // work and scan depth without adding useful parallelism.  At d >= 128 a
+    // summary (and each combine of the up-sweep) is O(d^2 dv) and costs as
+    // much as several chunks of the forward, so one workgroup per compute
+    // unit is the better trade.
+    const long target_wg = d >= 128 ? 256 : 512;
     long nseg = ceil_div(target_wg, bh);
     if (nseg <= 1) return (int)nch;
     long g = ceil_div(nch, nseg);
@@ -286,7 +289,7 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
     if (!valid_variant(variant) || B < 1 || H < 1 || n < 1 || d < 1 || dv < 1 || chunk < 1 ||
         seg_chunks < 0)
         return 0;
-    const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
+    const int g = effective_seg_chunks(variant, B, H, n, d, chunk, seg_chunks);
     const long nseg = num_segments(n, chunk, g);
     // leaves, then internal nodes of the up-sweep (fewer than nreal per head)
     const size_t scan = nseg <= 1 ? 0
@@ -322,7 +325,7 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     if (!lookup_forward(dtype, is_ahla(variant), d, dv, chunk, gamma_host != nullptr, kern))
         return HLA_ERR_UNSUPPORTED;
     if (is_hla3(variant) && (d != dv || !lookup_la(dtype, d, &x3->la))) return HLA_ERR_UNSUPPORTED;
-    const int g = effective_seg_chunks(variant, B, H, n, chunk, seg_chunks);
+    const int g = effective_seg_chunks(variant, B, H, n, d, chunk, seg_chunks);
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, chunk, g);
     if (nseg > INT32_MAX / 4) return HLA_ERR_UNSUPPORTED;

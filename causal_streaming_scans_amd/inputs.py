@@ -64,7 +64,7 @@ WORKLOADS = {
     "ratio_n4096": Workload("HLA-2 ratio B=8 H=16 n=4096 d=dv=64 bf16", "hla2_ratio",
                             8, 16, 4096, 64, 64, "bf16", "uniform_pos", 64, seed=1003),
     "decay_n16384": Workload("HLA-2 decay B=2 H=16 n=16384 d=dv=128 bf16", "hla2",
-                             2, 16, 16384, 128, 128, "bf16", "l2norm", 32, decay=True,
+                             2, 16, 16384, 128, 128, "bf16", "l2norm", 64, decay=True,
                              seed=1004),
     "ahla_n65536": Workload("AHLA B=1 H=32 n=65536 d=dv=64 bf16 + 1024 decode", "ahla",
                             1, 32, 65536, 64, 64, "bf16", "l2norm", 64,

@@ -93,8 +93,10 @@ typedef enum {
  * 0 for an unknown variant. */
 size_t hla_state_floats(int variant, int d, int dv);
 
-/* Segment length, in chunks, that hla_forward uses when seg_chunks == 0. */
-int hla_default_seg_chunks(int variant, int B, int H, int n, int chunk);
+/* Segment length, in chunks, that hla_forward uses when seg_chunks == 0 (d is
+ * the q/k head dimension: the segment summaries and the scan's combines grow
+ * as d^2 dv, so at d >= 128 the default keeps half as many segments). */
+int hla_default_seg_chunks(int variant, int B, int H, int n, int d, int chunk);
 
 /* Bytes of device workspace hla_forward needs for these arguments
  * (seg_chunks == 0 means the default): 2*B*H*(nseg-1) fp32 summaries of

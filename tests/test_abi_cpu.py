@@ -67,11 +67,14 @@ def test_workspace_bytes(lib):
 
 def test_default_segments_fill_the_chip(lib):
     # 128 heads x 4096 tokens: 4 segments of 16 chunks
-    assert hla.default_seg_chunks("hla2_ratio", 8, 16, 4096, 64) == 16
+    assert hla.default_seg_chunks("hla2_ratio", 8, 16, 4096, 64, 64) == 16
     # 32 heads x 65536 tokens: 16 segments of 64 chunks
-    assert hla.default_seg_chunks("ahla", 1, 32, 65536, 64) == 64
+    assert hla.default_seg_chunks("ahla", 1, 32, 65536, 64, 64) == 64
     # short sequences are never split below 8 chunks
-    assert hla.default_seg_chunks("hla2", 1, 1, 256, 32) == 8
+    assert hla.default_seg_chunks("hla2", 1, 1, 256, 16, 32) == 8
+    # d = 128: one workgroup per compute unit, 32 heads x 16384 tokens -> 8 segments
+    assert hla.default_seg_chunks("hla2", 2, 16, 16384, 128, 64) == 32
+    assert hla.default_seg_chunks("hla2", 2, 16, 16384, 64, 64) == 16
 
 
 def _fwd(lib, q=1, k=1, v=1, o=1, B=1, H=1, n=64, d=64, dv=64, dtype=BF16, variant=HLA2,

@@ -38,6 +38,9 @@ CASES = [
     ("bf16", "hla2_ratio", 1, 2, 640, 64, 32, 3, True, "uniform_pos"),
     ("bf16", "hla2", 1, 2, 400, 128, 32, 2, True, "l2norm"),
     ("bf16", "hla2", 1, 2, 333, 128, 16, 4, False, "l2norm"),
+    # d = 128 at chunk 64 (the decay workload's launch), eight segments with a ragged last one
+    ("bf16", "hla2", 1, 2, 1000, 128, 64, 2, True, "l2norm"),
+    ("bf16", "hla2", 1, 2, 700, 128, 64, 1, False, "l2norm"),
     ("bf16", "hla2", 1, 2, 200, 32, 32, 2, False, "l2norm"),
     ("bf16", "hla2", 1, 2, 200, 16, 16, 3, True, "l2norm"),
     ("bf16", "ahla", 1, 2, 1000, 64, 64, 3, False, "l2norm"),
