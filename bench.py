@@ -545,13 +545,14 @@ def main():
     # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
     # unnormalised HLA-2 (the variant the backward supports), q, k L2-normalised
     # Gaussian rows, v and the upstream gradient ~ N(0, 1), bf16
-    backward = backward_ratio = third_order = None
+    backward = backward_ratio = backward_decay = third_order = None
     if args.backward_steps > 0:
         bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
         bnseg = -(-n // (64 * bseg))
 
-        def time_backward(variant, qb, kb, vb, dob):
-            bplan = hla.BackwardPlan(qb, kb, vb, dob, variant=variant, seg_chunks=bseg)
+        def time_backward(variant, qb, kb, vb, dob, gamma=None, dgamma=None):
+            bplan = hla.BackwardPlan(qb, kb, vb, dob, variant=variant, gamma=gamma,
+                                     seg_chunks=bseg, dgamma=dgamma)
             for _ in range(10):
                 bplan.run()
             torch.cuda.synchronize()
@@ -613,6 +614,19 @@ def main():
                           "tokens_per_s": round(tokens / (rms * 1e-3), 1),
                           "lean_hbm_frac": round(b_bytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] ratio backward: {rms:.4f} ms/step, {tokens / (rms * 1e-3) / 1e9:.3f} G tokens/s")
+        # HLA-2 with per-head decays on the same inputs, without and with the
+        # decay gradient (two more launches over q, k, Z, dq, dk, dZ)
+        gam = np.random.default_rng(w.seed + 502).uniform(0.95, 0.999, H).astype(np.float32)
+        dms = time_backward("hla2", q, k, v, dob, gamma=gam)
+        dgms = time_backward("hla2", q, k, v, dob, gamma=gam, dgamma=True)
+        backward_decay = {"steps": args.backward_steps,
+                          "workload": f"HLA-2 backward with decays g_h ~ U[0.95, 0.999], the "
+                                      f"forward's inputs (B={B} H={H} n={n} d=dv={d} bf16), "
+                                      "do ~ N(0,1)",
+                          "ms_per_step": round(dms, 5),
+                          "ms_per_step_with_dgamma": round(dgms, 5),
+                          "dgamma_bytes": tokens * 6 * d * 2}
+        log(f"[bench] decay backward: {dms:.4f} ms/step, with dL/dgamma {dgms:.4f} ms/step")
         del dob
 
     # ---- CPU baseline: the oracle on the same inputs, all heads
@@ -659,6 +673,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "backward_ratio": backward_ratio,
+        "backward_decay": backward_decay,
         "third_order": third_order,
         "cpu_baseline": cpu,
     }

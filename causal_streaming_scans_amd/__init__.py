@@ -72,7 +72,7 @@ def load():
     lib.hla_backward_default_seg_chunks.restype = I
     lib.hla_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.hla_backward_workspace_bytes.restype = Z
-    lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, I, P, Z, P]
+    lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, P, I, P, Z, P]
     lib.hla_backward.restype = I
     lib.hla_status_str.argtypes = [I]
     lib.hla_status_str.restype = ctypes.c_char_p
@@ -301,10 +301,12 @@ def hla_step(q, k, v, state, variant="hla2", gamma=None, out=None, stream=None):
 class BackwardPlan:
     """The arguments of one backward pass (hla_backward), checked and
     marshalled once; ``run()`` enqueues it as a single library call and
-    returns (dq, dk, dv)."""
+    returns (dq, dk, dv), or (dq, dk, dv, dgamma) when ``dgamma`` is True or
+    an fp32 [H] device tensor (HLA-2 forms: dL/dgamma_h summed over the
+    batch, at the given decays, 1 when gamma is None)."""
 
     def __init__(self, q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0,
-                 dq=None, dk=None, dv=None, workspace=None, stream=None):
+                 dq=None, dk=None, dv=None, workspace=None, stream=None, dgamma=None):
         import torch
         lib = load()
         for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
@@ -324,17 +326,28 @@ class BackwardPlan:
                 if t.shape != q.shape or t.dtype != q.dtype:
                     raise HLAError(f"{name} has the wrong shape or dtype")
             grads.append(t)
+        if dgamma is True:
+            dgamma = torch.empty(H, dtype=torch.float32, device=q.device)
+        elif dgamma is not None and dgamma is not False:
+            _check_device_tensor("dgamma", dgamma)
+            if dgamma.dtype != torch.float32 or dgamma.numel() != H:
+                raise HLAError("dgamma must be an fp32 device tensor of H elements")
+        else:
+            dgamma = None
+        self.dgamma = dgamma
         dtc = _dtype_code(q)
         need = int(lib.hla_backward_workspace_bytes(vid, B, H, n, d, d, dtc, seg_chunks))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.grads = tuple(grads)
-        self._keep = (q, k, v, do, *grads, workspace)
+        self._keep = (q, k, v, do, *grads, workspace, dgamma)
         self._gamma, g_ptr = _gamma_arg(gamma, H)
         VP, CI = ctypes.c_void_p, ctypes.c_int
+        dg_ptr = VP(dgamma.data_ptr() if dgamma is not None else None)
         self._args = (VP(q.data_ptr()), VP(k.data_ptr()), VP(v.data_ptr()), VP(do.data_ptr()),
                       VP(grads[0].data_ptr()), VP(grads[1].data_ptr()), VP(grads[2].data_ptr()),
-                      CI(B), CI(H), CI(n), CI(d), CI(d), CI(dtc), CI(vid), g_ptr, CI(seg_chunks),
+                      CI(B), CI(H), CI(n), CI(d), CI(d), CI(dtc), CI(vid), g_ptr, dg_ptr,
+                      CI(seg_chunks),
                       VP(workspace.data_ptr()),
                       ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                       _stream_ptr(stream, q.device))
@@ -350,13 +363,14 @@ class BackwardPlan:
                 rc = self._lib.hla_backward(*self._args)
         if rc != 0:
             raise HLAError(f"hla_backward failed: {status_str(rc)} (code {rc})")
-        return self.grads
+        return self.grads if self.dgamma is None else (*self.grads, self.dgamma)
 
 
 def hla_backward(q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0, dq=None, dk=None,
-                 dv=None, workspace=None, stream=None):
+                 dv=None, workspace=None, stream=None, dgamma=None):
     """Gradients (dq, dk, dv) of the HLA-2 output with respect to q, k, v,
     given the upstream gradient do.  All four are [B, H, n, d] (d == dv), one
-    dtype (bf16 or fp32), contiguous, on one GPU; gamma as in hla_forward."""
+    dtype (bf16 or fp32), contiguous, on one GPU; gamma as in hla_forward.
+    With ``dgamma`` (True or an fp32 [H] tensor) also returns dL/dgamma."""
     return BackwardPlan(q, k, v, do, variant, gamma, seg_chunks, dq, dk, dv, workspace,
-                        stream).run()
+                        stream, dgamma).run()

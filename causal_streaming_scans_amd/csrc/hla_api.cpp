@@ -254,6 +254,34 @@ hla_status backward_ahla_ratio(const BwdCtx &c, const Grads &x) {
     return c.run_all(post, 8);
 }
 
+// dL/dg_h from the tensors the HLA-2 passes leave behind (DecayGradParams):
+// x's q, k, dq, dk in the pass dtype, Z and dZ in workspace tensors 0 and 1.
+hla_status decay_gradient(const BwdCtx &c, const Grads &x, int H, int n, int d, float *dgamma,
+                          void *partial) {
+    DecayGradParams p;
+    memset(&p, 0, sizeof(p));
+    p.q = x.q;
+    p.k = x.k;
+    p.z = c.tensor(0);
+    p.dq = x.dq;
+    p.dk = x.dk;
+    p.dz = c.tensor(1);
+    p.partial = static_cast<double *>(partial);
+    p.dgamma = dgamma;
+    p.n = n;
+    p.BH = c.p1.BH;
+    p.H = H;
+    // rows per workgroup step: 4 waves of 64 / (d / 4) rows; about 1024
+    // workgroups in all, at most kDecayGradBlocks per head
+    const long rpb = 4L * (64 / (d / 4));
+    long nblk = ceil_div(1024, p.BH);
+    if (nblk > kDecayGradBlocks) nblk = kDecayGradBlocks;
+    if (nblk > ceil_div(n, rpb)) nblk = ceil_div(n, rpb);
+    p.nblk = (int)nblk;
+    memcpy(p.gamma, c.p1.gamma, sizeof(p.gamma));
+    return c.la.decay_grad(p, c.s) == hipSuccess ? HLA_OK : HLA_ERR_DEVICE;
+}
+
 }  // namespace
 
 extern "C" {
@@ -498,6 +526,11 @@ static bool has_backward(int variant) {
     return variant == HLA_HLA2 || variant == HLA_HLA2_RATIO || variant == HLA_AHLA ||
            variant == HLA_AHLA_RATIO;
 }
+// fp64 partial sums of the decay gradient, after the tensors (HLA-2 forms)
+static size_t decay_grad_bytes(int variant, int B, int H) {
+    const bool hla2 = variant == HLA_HLA2 || variant == HLA_HLA2_RATIO;
+    return hla2 ? (size_t)B * H * kDecayGradBlocks * sizeof(double) : 0;
+}
 
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
                                     int seg_chunks) {
@@ -509,25 +542,39 @@ size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int
     const long nseg = num_segments(n, kLaChunk, g);
     const size_t esz = backward_elem_bytes(variant, dtype);
     const size_t sums = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    return 2 * sums + (size_t)backward_tensors(variant, dtype) * B * H * n * d * esz;
+    return 2 * sums + (size_t)backward_tensors(variant, dtype) * B * H * n * d * esz +
+           decay_grad_bytes(variant, B, H);
 }
+
 
 hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
                         void *dk, void *dv_out, int B, int H, int n, int d, int dv, int dtype,
-                        int variant, const float *gamma_host, int seg_chunks, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        int variant, const float *gamma_host, float *dgamma, int seg_chunks,
+                        void *workspace, size_t workspace_bytes, void *stream) {
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
+    if (dgamma && is_ahla(variant)) return HLA_ERR_UNSUPPORTED;   // AHLA has no decay
     // the ratio forms run their passes in fp32 (their gradient with respect
     // to q and k is a small difference of large terms, which bf16
     // intermediates do not resolve)
     const int run_dtype = is_ratio(variant) ? HLA_F32 : dtype;
     BwdCtx c;
     if (!lookup_la(run_dtype, d, &c.la)) return HLA_ERR_UNSUPPORTED;
-    if (n == 0) return HLA_OK;
+    if (n == 0) {
+        if (!dgamma) return HLA_OK;
+        // no rows: dgamma = 0 (the second step of the decay gradient alone)
+        DecayGradParams p;
+        memset(&p, 0, sizeof(p));
+        p.dgamma = dgamma;
+        p.BH = B * H;
+        p.H = H;
+        for (int h = 0; h < kMaxDecayHeads; ++h) p.gamma[h] = 1.f;
+        return c.la.decay_grad(p, static_cast<hipStream_t>(stream)) == hipSuccess
+                   ? HLA_OK : HLA_ERR_DEVICE;
+    }
     if (!q || !k || !v || !dout || !dq || !dk || !dv_out) return HLA_ERR_NULL;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
     if ((long)kLaChunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
@@ -558,7 +605,12 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     for (int h = 0; h < kMaxDecayHeads; ++h) c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h];
 
     Grads io{q, k, v, dout, dq, dk, dv_out};
-    if (variant == HLA_HLA2) return backward_hla2(c, io);
+    void *partial = c.tensor(backward_tensors(variant, dtype));
+    if (variant == HLA_HLA2) {
+        st = backward_hla2(c, io);
+        if (st != HLA_OK || !dgamma) return st;
+        return decay_gradient(c, io, H, n, d, dgamma, partial);
+    }
     if (variant == HLA_AHLA) return backward_ahla(c, io);
     // ratio forms: with bf16 inputs every pass reads and writes fp32 copies
     // (after the variant's own tensors in the workspace)
@@ -578,6 +630,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         run.dv = c.tensor(own + 6);
     }
     st = variant == HLA_HLA2_RATIO ? backward_hla2_ratio(c, run) : backward_ahla_ratio(c, run);
+    if (st == HLA_OK && dgamma) st = decay_gradient(c, run, H, n, d, dgamma, partial);
     if (st != HLA_OK || dtype != HLA_BF16) return st;
     void *dst[3] = {dq, dk, dv_out};
     const void *src[3] = {run.dq, run.dk, run.dv};

@@ -62,9 +62,25 @@ hipError_t launch_ratio_prep(const RatioPrepParams &p, hipStream_t s) {
 }
 
 template <typename T, int D>
+hipError_t launch_decay_grad(const DecayGradParams &p, hipStream_t s) {
+    // nblk == 0 (no rows): the second step alone writes zeros
+    if (p.nblk < 0 || p.nblk > kDecayGradBlocks || p.BH < 1 || p.H < 1 || p.BH % p.H != 0)
+        return hipErrorInvalidValue;
+    if (p.nblk > 0) {
+        hipLaunchKernelGGL((decay_grad_rows_kernel<T, D>), dim3((unsigned)p.nblk, (unsigned)p.BH),
+                           dim3(256), 0, s, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(decay_grad_final_kernel, dim3(1), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
 bool la_set(LaLaunches *out) {
     out->unit_column = launch_unit_column<T, D>;
     out->ratio_prep = launch_ratio_prep<T, D>;
+    out->decay_grad = launch_decay_grad<T, D>;
     static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
     out->sym = launch_la<T, D, true, false>;

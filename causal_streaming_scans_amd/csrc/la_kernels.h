@@ -556,6 +556,68 @@ __global__ __launch_bounds__(256) void ratio_prep_kernel(RatioPrepParams p) {
     }
 }
 
+// Decay gradient, first step: workgroup (x, bh) sums the weighted row terms
+// of DecayGradParams over rows x*RPB + i*nblk*RPB + ...  Each row is read by
+// D/4 lanes (four elements each); the row term is formed in fp32 and
+// weighted and summed in fp64.  One partial per workgroup, no atomics.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decay_grad_rows_kernel(DecayGradParams p) {
+    constexpr int LPR = D / 4;              // lanes per row
+    constexpr int RPW = kWave / LPR;        // rows per wave and step
+    constexpr int RPB = RPW * (256 / kWave);
+    static_assert(D % 4 == 0 && kWave % LPR == 0, "row split");
+    const int bh = blockIdx.y;
+    const int l = lane_id(), w = wave_id();
+    const int sub = l / LPR, part = l % LPR;
+    const double mid = 0.5 * (double)(p.n - 1);
+    const size_t head = (size_t)bh * p.n * D;
+    const T *Q = static_cast<const T *>(p.q) + head, *K = static_cast<const T *>(p.k) + head;
+    const T *Zt = static_cast<const T *>(p.z) + head, *dQ = static_cast<const T *>(p.dq) + head;
+    const T *dK = static_cast<const T *>(p.dk) + head, *dZ = static_cast<const T *>(p.dz) + head;
+    double acc = 0.0;
+    // the loop bound is uniform over the wave; rows past n contribute zero
+    for (long t0 = (long)blockIdx.x * RPB + w * RPW; t0 < p.n; t0 += (long)p.nblk * RPB) {
+        const long t = t0 + sub;
+        float s = 0.f;
+        if (t < p.n) {
+            const size_t off = (size_t)t * D + part * 4;
+            const f32x4 q = load4f(Q + off), dq = load4f(dQ + off);
+            const f32x4 z = load4f(Zt + off), dz = load4f(dZ + off);
+            const f32x4 k = load4f(K + off), dk = load4f(dK + off);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s += 2.f * q[j] * dq[j] - 3.f * z[j] * dz[j] - 0.5f * k[j] * dk[j];
+        }
+#pragma unroll
+        for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, kWave);
+        if (part == 0 && t < p.n) acc += ((double)t - mid) * (double)s;
+    }
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, kWave);
+    __shared__ double wsum[256 / kWave];
+    if (l == 0) wsum[w] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double tot = 0.0;
+#pragma unroll
+        for (int i = 0; i < 256 / kWave; ++i) tot += wsum[i];
+        p.partial[(size_t)bh * p.nblk + blockIdx.x] = tot;
+    }
+}
+
+// Decay gradient, second step: dgamma[h] = (sum over b and the row
+// workgroups of head b*H + h, in a fixed order) / g_h.
+__global__ __launch_bounds__(256) void decay_grad_final_kernel(DecayGradParams p) {
+    const int B = p.BH / p.H;
+    for (int h = threadIdx.x; h < p.H; h += blockDim.x) {
+        double tot = 0.0;
+        for (int b = 0; b < B; ++b) {
+            const double *row = p.partial + (size_t)(b * p.H + h) * p.nblk;
+            for (int x = 0; x < p.nblk; ++x) tot += row[x];
+        }
+        p.dgamma[h] = (float)(tot / (double)p.gamma[gamma_slot(h, p.H)]);
+    }
+}
+
 }  // namespace hla
 
 namespace hla {

@@ -42,6 +42,8 @@ struct LaLaunches {
     LaLaunch plain, sym, dual;
     hipError_t (*unit_column)(void *out, long rows, hipStream_t);   // rows (1, 0, ..., 0)
     hipError_t (*ratio_prep)(const RatioPrepParams &, hipStream_t);
+    // both steps of the decay gradient; p.nblk is set by the host
+    hipError_t (*decay_grad)(const DecayGradParams &, hipStream_t);
 };
 bool lookup_la(int dtype, int d, LaLaunches *out);
 // bf16 -> fp32 (to_f32) or fp32 -> bf16 copy of count values (a multiple of 4)

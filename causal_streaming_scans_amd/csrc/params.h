@@ -107,6 +107,23 @@ struct LaParams {
     float gamma[kMaxDecayHeads];   // decay of head h for this pass
 };
 
+// Gradient of the per-head decays of HLA-2 (la_kernels.h,
+// decay_grad_rows_kernel and decay_grad_final_kernel).  With Z = LA_g(Q, K, K)
+// and dZ the full gradient reaching Z, differentiating every g^(t-s) factor of
+// the two chained passes gives
+//     g_h dL/dg_h = sum_{b, t} (t - c) (2 q_t . dq_t - 3 z_t . dz_t - k_t . dk_t / 2)
+// for any constant c (the sum without the weight is zero); c = (n - 1) / 2
+// keeps the terms small.  The same sum holds for the ratio form.
+constexpr int kDecayGradBlocks = 64;   // most row workgroups per head
+struct DecayGradParams {
+    const void *q, *k, *z, *dq, *dk, *dz;   // [BH][n][D]
+    double *partial;                        // [BH][nblk]
+    float *dgamma;                          // [H] out
+    long n;
+    int BH, H, nblk;
+    float gamma[kMaxDecayHeads];            // decay of head h (1 when none)
+};
+
 // Row-wise step of the ratio backward (la_kernels.h, ratio_prep_kernel).
 struct RatioPrepParams {
     const void *q, *u, *num, *dout;   // [rows][D]

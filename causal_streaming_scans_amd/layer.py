@@ -14,7 +14,10 @@ into PyTorch autograd:
   BLAS libraries); every step of the operator itself runs in the library.
 
 Variants with a backward: "hla2" (optional per-head decay), "hla2_ratio",
-"ahla".  Inputs are bf16 or fp32 GPU tensors; d == dv.
+"ahla".  Inputs are bf16 or fp32 GPU tensors; d == dv.  A decay given as a
+tensor that requires grad receives dL/dgamma (HLA-2 forms; the library's
+decay gradient, summed over the batch); the library accepts decays in
+(0, 1] only, so a learned decay must be kept in that range by its owner.
 """
 from __future__ import annotations
 
@@ -32,15 +35,28 @@ class HLAFunction(torch.autograd.Function):
     def forward(ctx, q, k, v, variant, gamma, chunk):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         o = hla_forward(q, k, v, variant=variant, gamma=gamma, chunk=chunk)
-        ctx.save_for_backward(q, k, v)
-        ctx.variant, ctx.gamma = variant, gamma
+        ctx.gamma_is_tensor = isinstance(gamma, torch.Tensor)
+        if ctx.gamma_is_tensor:
+            ctx.save_for_backward(q, k, v, gamma)
+        else:
+            ctx.save_for_backward(q, k, v)
+            ctx.gamma = gamma
+        ctx.variant = variant
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v = ctx.saved_tensors
-        dq, dk, dv = hla_backward(q, k, v, do.contiguous(), variant=ctx.variant, gamma=ctx.gamma)
-        return dq, dk, dv, None, None, None
+        if ctx.gamma_is_tensor:
+            q, k, v, gamma = ctx.saved_tensors
+        else:
+            (q, k, v), gamma = ctx.saved_tensors, ctx.gamma
+        want_dg = ctx.gamma_is_tensor and ctx.needs_input_grad[4]
+        res = hla_backward(q, k, v, do.contiguous(), variant=ctx.variant, gamma=gamma,
+                           dgamma=True if want_dg else None)
+        dgamma = None
+        if want_dg:
+            dgamma = res[3].to(gamma.device, gamma.dtype).reshape(gamma.shape)
+        return res[0], res[1], res[2], None, dgamma, None
 
 
 def hla(q, k, v, variant: str = "hla2", gamma=None, chunk: int = 64):
@@ -56,16 +72,23 @@ class HLAAttention(torch.nn.Module):
     x: [B, n, d_model] -> [B, n, d_model].  Weights are bias-free linear maps
     (d_model -> heads * head_dim for q, k, v; heads * head_dim -> d_model for
     the output), initialised by torch's default; ``gamma`` is None or one
-    decay per head (variant "hla2" only)."""
+    decay per head (variant "hla2" only).  With ``learn_gamma`` the decays
+    are an fp32 parameter trained through the library's decay gradient
+    (its owner keeps them in (0, 1])."""
 
     def __init__(self, d_model: int, heads: int, head_dim: int, variant: str = "hla2",
-                 gamma=None, chunk: int = 64, device=None, dtype=None):
+                 gamma=None, chunk: int = 64, device=None, dtype=None, learn_gamma: bool = False):
         super().__init__()
         if variant not in _BACKWARD_VARIANTS:
             raise ValueError(f"variant {variant!r} has no backward; one of {_BACKWARD_VARIANTS}")
         kw = dict(bias=False, device=device, dtype=dtype)
         self.heads, self.head_dim = heads, head_dim
-        self.variant, self.gamma, self.chunk = variant, gamma, chunk
+        self.variant, self.chunk = variant, chunk
+        if learn_gamma:
+            if gamma is None:
+                raise ValueError("learn_gamma needs initial decays")
+            gamma = torch.nn.Parameter(torch.as_tensor(gamma, dtype=torch.float32).reshape(heads).clone())
+        self.gamma = gamma
         self.wq = torch.nn.Linear(d_model, heads * head_dim, **kw)
         self.wk = torch.nn.Linear(d_model, heads * head_dim, **kw)
         self.wv = torch.nn.Linear(d_model, heads * head_dim, **kw)

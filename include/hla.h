@@ -221,6 +221,16 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * dq, dk, dv_out  device outputs, same layout and type; may not alias the
  *                inputs or each other
  * gamma_host     NULL or H decays in (0, 1] (as hla_forward)
+ * dgamma         NULL, or device [H] fp32 output (HLA_HLA2, HLA_HLA2_RATIO):
+ *                dL/dg_h, summed over the batch, at the decays given (1 for
+ *                every head when gamma_host is NULL).  Differentiating each
+ *                g^(t-s) factor of the two chained passes gives
+ *                g_h dL/dg_h = sum_{b,t} (t - c)(2 q_t.dq_t - 3 z_t.dz_t
+ *                - k_t.dk_t / 2) for any constant c, with Z and dZ as kept
+ *                in the workspace; two more launches form it (fp32 row terms
+ *                summed in fp64 in a fixed order, so repeat calls agree
+ *                bit for bit).  n == 0 writes zeros.  Non-NULL with an
+ *                AHLA form: HLA_ERR_UNSUPPORTED.
  * seg_chunks     chunks (of 64 tokens) per segment; 0 = the library's default
  *                (hla_backward_default_seg_chunks)
  * workspace      device buffer of at least hla_backward_workspace_bytes()
@@ -238,8 +248,8 @@ size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int
                                     int seg_chunks);
 hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout,
                         void *dq, void *dk, void *dv_out, int B, int H, int n, int d, int dv,
-                        int dtype, int variant, const float *gamma_host, int seg_chunks,
-                        void *workspace, size_t workspace_bytes, void *stream);
+                        int dtype, int variant, const float *gamma_host, float *dgamma,
+                        int seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *hla_status_str(int status);

@@ -22,6 +22,11 @@ by g per token):
 AHLA ("2. ... (AHLA)"):
     M = L L,  num = M V,  den = M 1
 
+Gradient of the decay g (HLA-2): D_g enters twice, through F and through M.
+With D'[t, i] = (t - i) g^(t-i-1) for i <= t (else 0), the derivative of
+D_g, and dF, dM the gradients of F and M below,
+    dL/dg = sum(dF * A * D') + sum(dM * N * D') .
+
 Backward, in the order the chain rule visits the factors:
     ratio:  dnum = dO / den,  dden = -rowsum(dO * o) / den ;  else dnum = dO
     dV = M^T dnum
@@ -68,6 +73,39 @@ def hla2_vjp(q, k, v, do, gamma: float = 1.0, ratio: bool = False):
     dL = dN.T @ F
     dA = Dg * dF + np.tril(dL)
     return dA @ k, dA.T @ q, dv
+
+
+def hla2_dgamma(q, k, v, do, gamma: float = 1.0, ratio: bool = False) -> float:
+    """dL/dg of HLA-2 for one head (L = sum(dO * o)), by the chain rule through
+    the two decay masks of the matrix form."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n = q.shape[0]
+    A = q @ k.T
+    Dg = decay_mask(n, gamma)
+    lag = np.arange(n)[:, None] - np.arange(n)[None, :]
+    dD = np.where(lag >= 1, lag * float(gamma) ** np.maximum(lag - 1, 0), 0.0)
+    L = np.tril(A)
+    F = Dg * A
+    N = F @ L.T
+    M = Dg * N
+    if ratio:
+        den = M.sum(axis=1, keepdims=True)
+        o = (M @ v) / den
+        dM = (do / den) @ v.T - (do * o).sum(axis=1, keepdims=True) / den
+    else:
+        dM = do @ v.T
+    dF = (Dg * dM) @ L
+    return float((dF * A * dD).sum() + (dM * N * dD).sum())
+
+
+def hla2_dgamma_batched(q, k, v, do, H: int, gamma=None, ratio: bool = False):
+    """dL/dg_h over [BH, n, *] arrays: the per-(b, h) derivatives summed over
+    the batch (bh = b * H + h).  Returns fp64 [H]."""
+    out = np.zeros(H)
+    for bh in range(q.shape[0]):
+        g = 1.0 if gamma is None else float(gamma[bh % H])
+        out[bh % H] += hla2_dgamma(q[bh], k[bh], v[bh], do[bh], g, ratio)
+    return out
 
 
 def ahla_vjp(q, k, v, do, ratio: bool = False):

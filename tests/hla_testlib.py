@@ -90,3 +90,33 @@ def gpu_forward(x, variant, B, H, dtype, chunk, seg_chunks=0, gamma=None, state_
     if want_state:
         return out, so.cpu().numpy().astype(np.float64).reshape(B * H, -1)
     return out
+
+
+def dgamma_scale(x, do, H, gamma, ratio):
+    """Size of the terms of the decay gradient, per head h, from fp64 oracle
+    tensors: (1/g_h) sum_{b,t} |t - c| (2|q.dq| + 3|z.dz| + |k.dk|/2), with
+    Z = LA_g(Q, K, K), dz its full gradient, c = (n - 1)/2.  The terms sum to
+    zero without the weight, so errors are judged against this size."""
+    from oracle import backward as BW
+    from oracle import definition as D
+    BH, n, _ = x["q"].shape
+    c = 0.5 * (n - 1)
+    w = np.abs(np.arange(n) - c)
+    out = np.zeros(H)
+    for bh in range(BH):
+        q, k, v = (np.asarray(x[a][bh], np.float64) for a in "qkv")
+        dob = np.asarray(do[bh], np.float64)
+        g = 1.0 if gamma is None else float(gamma[bh % H])
+        dq, dk, _ = BW.hla2_vjp(q, k, v, dob, g, ratio)
+        z = (D.decay_mask(n, g) * (q @ k.T)) @ k
+        D2 = D.decay_mask(n, g * g)
+        up = dob @ v.T
+        if ratio:
+            M = D2 * (q @ z.T)
+            den = M.sum(axis=1, keepdims=True)
+            o = (M @ v) / den
+            up = (dob / den) @ v.T - (dob * o).sum(axis=1, keepdims=True) / den
+        dz = (D2 * up).T @ q
+        terms = 2 * np.abs((q * dq).sum(1)) + 3 * np.abs((z * dz).sum(1)) + 0.5 * np.abs((k * dk).sum(1))
+        out[bh % H] += (w * terms).sum() / g
+    return out

@@ -166,13 +166,13 @@ def test_binding_refuses_cpu_tensors(lib):
 # ------------------------------------------------------------------ backward
 
 def _bwd(lib, q=1, k=1, v=1, do=1, dq=1, dk=1, dv=1, B=1, H=2, n=128, d=64, dvd=64, dtype=BF16,
-         variant=HLA2, gamma=None, seg=0, ws=1, ws_bytes=1 << 40):
+         variant=HLA2, gamma=None, dgamma=None, seg=0, ws=1, ws_bytes=1 << 40):
     P = ctypes.c_void_p
     g = None
     if gamma is not None:
         g = (ctypes.c_float * len(gamma))(*gamma)
     return lib.hla_backward(P(q), P(k), P(v), P(do), P(dq), P(dk), P(dv), B, H, n, d, dvd, dtype,
-                            variant, g, seg, P(ws), ws_bytes, None)
+                            variant, g, P(dgamma), seg, P(ws), ws_bytes, None)
 
 
 def test_backward_workspace_bytes(lib):
@@ -186,12 +186,14 @@ def test_backward_workspace_bytes(lib):
     g = lib.hla_backward_default_seg_chunks(B, H, n)
     nseg = -(-n // (64 * g))
     want = 2 * B * H * (nseg - 1) * d * d * 4 + 2 * B * H * n * d * 2
-    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16") == want
-    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32) == 2 * B * H * n * d * 4
+    dg = B * H * 64 * 8                    # fp64 partials of the decay gradient (HLA-2 forms)
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16") == want + dg
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32) == \
+        2 * B * H * n * d * 4 + dg
     # the ratio form runs in fp32: 5 tensors, and with bf16 inputs 7 more
     # (fp32 copies of q, k, v, dO and fp32 gradients)
     want_ratio = want - 2 * B * H * n * d * 2 + 12 * B * H * n * d * 4
-    assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == want_ratio
+    assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == want_ratio + dg
     assert hla.backward_workspace_bytes("ahla_ratio", B, H, n, d, d) == \
         want_ratio + 2 * B * H * n * d * 4                   # Y1 and its gradient
     assert hla.backward_workspace_bytes("hla3", B, H, n, d, d) == 0
@@ -206,6 +208,8 @@ def test_backward_validation(lib):
     assert _bwd(lib, variant=AHLA_RATIO, d=128, dvd=128) == ERR_UNSUP   # fp32 passes: d <= 64
     assert _bwd(lib, variant=4) == ERR_UNSUP                              # third order: forward only
     assert _bwd(lib, variant=AHLA, gamma=[0.9, 0.9]) == ERR_UNSUP   # AHLA has no decay
+    assert _bwd(lib, variant=AHLA, dgamma=1) == ERR_UNSUP           # nor a decay gradient
+    assert _bwd(lib, variant=AHLA_RATIO, dgamma=1) == ERR_UNSUP
     assert _bwd(lib, variant=AHLA, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=9) == ERR_ARG
     assert _bwd(lib, dvd=32) == ERR_UNSUP

@@ -1,0 +1,89 @@
+"""GPU parity of the decay gradient of hla_backward (dL/dg_h, HLA-2 and its
+ratio form) against the fp64 oracle's chain rule through the two decay masks
+(oracle/backward.py, hla2_dgamma), on the decay reading of "1. HLA de Segundo
+Orden" ("Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)",
+gist.science/es/paper/2510.27258) trained through "4. Entrenamiento Paralelo
+mediante Escaneos Asociativos".
+
+dL/dg_h is a sum over tokens of position-weighted terms whose unweighted sum
+is zero, so its error is measured against the size of those terms:
+scale_h = (1/g_h) sum_{b,t} |t - c| (2|q.dq| + 3|z.dz| + |k.dk|/2) from fp64
+oracle tensors, and |got - want| must stay under BAR * scale_h.  fp32: the
+fp32 bar, 1e-5.  bf16: every row term is a product of two factors that each
+carry at most one bf16 rounding (the stored dq, dk, Z, dZ; relative 2^-9),
+so no term is off by more than 2^-8 of its size, and BAR = 2^-8.  (Measured
+err/scale: about 1e-8 fp32, 5e-5 bf16; relative to dL/dg itself bf16 is
+0.1-4% off, the conditioning of a sum of large terms that nearly cancel.)"""
+import numpy as np
+import pytest
+
+from oracle import backward as BW
+from causal_streaming_scans_amd import inputs as I
+from hla_testlib import TOL, dgamma_scale, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run(x, do, B, H, dtype, gamma, variant, seg=0):
+    import torch
+    import causal_streaming_scans_amd as hla
+    n, d = x["q"].shape[1], x["q"].shape[2]
+    shp = (B, H, n, d)
+    res = hla.hla_backward(*(to_dev(x[a], dtype, shp) for a in "qkv"), to_dev(do, dtype, shp),
+                           variant=variant, gamma=gamma, seg_chunks=seg, dgamma=True)
+    torch.cuda.synchronize()
+    return res
+
+
+CASES = [
+    # dtype, variant, B, H, n, d, decay, seg_chunks
+    ("f32", "hla2", 2, 2, 300, 32, True, 0),
+    ("f32", "hla2", 1, 3, 257, 16, True, 1),
+    ("f32", "hla2", 1, 2, 200, 64, False, 0),
+    ("f32", "hla2_ratio", 2, 2, 203, 32, True, 1),
+    ("bf16", "hla2", 2, 2, 450, 64, True, 2),
+    ("bf16", "hla2", 1, 2, 700, 128, True, 1),
+    ("bf16", "hla2", 1, 2, 333, 16, True, 0),
+    ("bf16", "hla2_ratio", 1, 2, 400, 64, True, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(v) for v in c))
+def test_dgamma_matches_oracle(case):
+    dtype, variant, B, H, n, d, decay, seg = case
+    say(f"[dgamma] {case}")
+    ratio = variant == "hla2_ratio"
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos" if ratio else "l2norm",
+                      seed=900 + n + d, decay=decay)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=950 + n)
+    gamma = x["gamma"]
+    got = run(x, do, B, H, dtype, gamma, variant, seg)[3].cpu().double().numpy()
+    want = BW.hla2_dgamma_batched(x["q"], x["k"], x["v"], do, H, gamma, ratio)
+    scale = dgamma_scale(x, do, H, gamma, ratio)
+    err = np.abs(got - want)
+    say(f"  got {got} want {want} err/scale {err / scale} rel {err / np.abs(want)}")
+    bar = TOL["f32"] if dtype == "f32" else 2.0 ** -8
+    assert np.all(err <= bar * scale), (case, got, want, scale)
+
+
+def test_dgamma_repeatable_and_no_rows():
+    """Two calls agree bit for bit (fixed-order sums); n = 0 gives zeros; the
+    gradients dq, dk, dv are the same with or without dgamma."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    B, H, n, d = 2, 4, 500, 64
+    x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist="l2norm", seed=977, decay=True)
+    do = I.make_upstream_grad(B * H, n, d, "bf16", seed=978)
+    a = run(x, do, B, H, "bf16", x["gamma"], "hla2")
+    b = run(x, do, B, H, "bf16", x["gamma"], "hla2")
+    assert torch.equal(a[3], b[3])
+    shp = (B, H, n, d)
+    plain = hla.hla_backward(*(to_dev(x[s], "bf16", shp) for s in "qkv"), to_dev(do, "bf16", shp),
+                             gamma=x["gamma"])
+    for g1, g2 in zip(plain, a[:3]):
+        assert torch.equal(g1, g2)
+    z = torch.zeros(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
+    dg = torch.full((H,), 7.0, device="cuda")
+    hla.hla_backward(z, z, z, z, gamma=x["gamma"], dgamma=dg)
+    torch.cuda.synchronize()
+    assert torch.equal(dg, torch.zeros_like(dg))

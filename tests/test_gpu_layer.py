@@ -107,3 +107,26 @@ def test_sublayer(dtype, variant):
         e = rel_l2(t.detach().float().cpu().numpy(), ref)
         say(f"  {name}: rel_l2 {e:.3e}")
         assert e < tol, (name, e)
+
+
+def test_learned_decay_gradient():
+    """A decay tensor that requires grad receives dL/dgamma through autograd:
+    the library's decay gradient against the oracle's chain rule, judged
+    against the size of its terms (fp32)."""
+    import torch
+    from causal_streaming_scans_amd.layer import hla
+    from hla_testlib import dgamma_scale
+    B, H, n, d = 2, 3, 257, 32
+    say(f"[autograd] learned decay B={B} H={H} n={n} d={d} fp32")
+    x = I.make_inputs(B, H, n, d, d, dtype="f32", dist="l2norm", seed=1211, decay=True)
+    q, k, v = (to_dev(x[key], "f32", (B, H, n, d)) for key in ("q", "k", "v"))
+    gamma = torch.tensor(x["gamma"], dtype=torch.float32, requires_grad=True)
+    w = I.make_upstream_grad(B * H, n, d, "f32", seed=1212)
+    o = hla(q, k, v, "hla2", gamma)
+    (o * torch.from_numpy(w).reshape(B, H, n, d).cuda()).sum().backward()
+    torch.cuda.synchronize()
+    want = BW.hla2_dgamma_batched(x["q"], x["k"], x["v"], w, H, x["gamma"])
+    got = gamma.grad.double().numpy()
+    scale = dgamma_scale(x, w, H, x["gamma"], False)
+    say(f"  dgamma {got} want {want} err/scale {np.abs(got - want) / scale}")
+    assert np.all(np.abs(got - want) <= TOL["f32"] * scale)

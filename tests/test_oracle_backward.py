@@ -165,3 +165,69 @@ def test_planted_mistakes_are_caught():
     variants.append((Dg * (dN @ L) + np.tril(F.T @ dN)) @ k)  # transposed
     for wrong in variants:
         assert rel(wrong, dq) > 1e-3
+
+
+# ---------------------------------------------------------- decay gradient
+
+def _fd_gamma(fwd, q, k, v, do, g, h=1e-6):
+    return float(((fwd(g + h) - fwd(g - h)) * do).sum() / (2 * h))
+
+
+@pytest.mark.parametrize("ratio", [False, True])
+@pytest.mark.parametrize("gamma", [0.7, 0.95, 1.0])
+def test_dgamma_finite_differences(gamma, ratio):
+    """dL/dg by the chain rule against a central difference of the masked
+    matrix definition (L = sum(dO * o)); at g = 1 the difference straddles
+    the page's undecayed operator."""
+    rng = np.random.default_rng(31 + int(100 * gamma) + ratio)
+    n, d, dv = 23, 4, 3
+    q, k, v, do = inputs(rng, n, d, dv, pos=ratio)
+    fd = _fd_gamma(lambda g: D.hla2_matrix(q, k, v, g, ratio), q, k, v, do, gamma)
+    got = BW.hla2_dgamma(q, k, v, do, gamma, ratio)
+    assert abs(got - fd) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_dgamma_loops_definition():
+    """The same derivative against a central difference of the explicit
+    double sum (a second, loop-based forward)."""
+    rng = np.random.default_rng(37)
+    n, d, dv, g = 7, 3, 2, 0.85
+    q, k, v, do = inputs(rng, n, d, dv)
+    fd = _fd_gamma(lambda gg: D.hla2_loops(q, k, v, gg), q, k, v, do, g)
+    assert abs(BW.hla2_dgamma(q, k, v, do, g) - fd) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_dgamma_special_cases():
+    """One token: no pair (t, i) with i < t, so the decay never acts and
+    dL/dg = 0.  Batched: per-(b, h) derivatives summed over b."""
+    rng = np.random.default_rng(41)
+    q, k, v, do = inputs(rng, 1, 4, 4)
+    assert BW.hla2_dgamma(q, k, v, do, 0.9) == 0.0
+    H, B, n, d = 2, 3, 6, 3
+    x = [rng.standard_normal((B * H, n, d)) for _ in range(4)]
+    gam = np.array([0.8, 0.95])
+    got = BW.hla2_dgamma_batched(*x, H, gam)
+    for h in range(H):
+        want = sum(BW.hla2_dgamma(x[0][b * H + h], x[1][b * H + h], x[2][b * H + h],
+                                  x[3][b * H + h], gam[h]) for b in range(B))
+        assert got[h] == pytest.approx(want, rel=1e-12)
+
+
+def test_dgamma_planted_mistakes_are_caught():
+    """Dropping either mask's term, or using g^(t-i) in place of its
+    derivative, moves dL/dg far from the finite difference."""
+    rng = np.random.default_rng(43)
+    n, d, dv, g = 11, 3, 2, 0.8
+    q, k, v, do = inputs(rng, n, d, dv)
+    fd = _fd_gamma(lambda gg: D.hla2_matrix(q, k, v, gg), q, k, v, do, g)
+    A = q @ k.T
+    Dg = D.decay_mask(n, g)
+    lag = np.arange(n)[:, None] - np.arange(n)[None, :]
+    dD = np.where(lag >= 1, lag * g ** np.maximum(lag - 1, 0), 0.0)
+    L, F = np.tril(A), Dg * A
+    N = F @ L.T
+    dM = do @ v.T
+    dF = (Dg * dM) @ L
+    for wrong in ((dF * A * dD).sum(), (dM * N * dD).sum(),
+                  (dF * A * Dg).sum() + (dM * N * Dg).sum()):
+        assert abs(wrong - fd) > 1e-3 * abs(fd)
