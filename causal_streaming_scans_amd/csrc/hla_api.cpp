@@ -271,9 +271,11 @@ hla_status decay_gradient(const BwdCtx &c, const Grads &x, int H, int n, int d, 
     p.n = n;
     p.BH = c.p1.BH;
     p.H = H;
-    // rows per workgroup step: 4 waves of 64 / (d / 4) rows; about 1024
-    // workgroups in all, at most kDecayGradBlocks per head
-    const long rpb = 4L * (64 / (d / 4));
+    // rows per workgroup step: 4 waves of 64 / (d / N) rows, N = the values
+    // in 16 bytes; about 1024 workgroups in all, at most kDecayGradBlocks
+    // per head
+    const int per16 = 16 / (int)(c.tensor_bytes / ((size_t)c.rows * d));
+    const long rpb = 4L * (64 / (d / per16));
     long nblk = ceil_div(1024, p.BH);
     if (nblk > kDecayGradBlocks) nblk = kDecayGradBlocks;
     if (nblk > ceil_div(n, rpb)) nblk = ceil_div(n, rpb);

@@ -72,7 +72,7 @@ hipError_t launch_decay_grad(const DecayGradParams &p, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(decay_grad_final_kernel, dim3(1), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(decay_grad_final_kernel, dim3((unsigned)p.H), dim3(kWave), 0, s, p);
     return hipGetLastError();
 }
 

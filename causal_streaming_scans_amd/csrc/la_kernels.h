@@ -556,16 +556,39 @@ __global__ __launch_bounds__(256) void ratio_prep_kernel(RatioPrepParams p) {
     }
 }
 
+// 16 bytes of a row as floats: 8 bf16 or 4 fp32 values.
+template <typename T> struct Row16;
+template <> struct Row16<bf16> {
+    static constexpr int N = 8;
+    float x[8];
+    __device__ __forceinline__ void load(const bf16 *p) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = (float)v[j];
+    }
+};
+template <> struct Row16<float> {
+    static constexpr int N = 4;
+    float x[4];
+    __device__ __forceinline__ void load(const float *p) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = v[j];
+    }
+};
+
 // Decay gradient, first step: workgroup (x, bh) sums the weighted row terms
 // of DecayGradParams over rows x*RPB + i*nblk*RPB + ...  Each row is read by
-// D/4 lanes (four elements each); the row term is formed in fp32 and
-// weighted and summed in fp64.  One partial per workgroup, no atomics.
+// D/N lanes with one 16-byte load per tensor (N values each); the row term is
+// formed in fp32 and weighted and summed in fp64.  One partial per
+// workgroup, no atomics.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decay_grad_rows_kernel(DecayGradParams p) {
-    constexpr int LPR = D / 4;              // lanes per row
+    using R = Row16<T>;
+    constexpr int LPR = D / R::N;           // lanes per row
     constexpr int RPW = kWave / LPR;        // rows per wave and step
     constexpr int RPB = RPW * (256 / kWave);
-    static_assert(D % 4 == 0 && kWave % LPR == 0, "row split");
+    static_assert(D % R::N == 0 && kWave % LPR == 0, "row split");
     const int bh = blockIdx.y;
     const int l = lane_id(), w = wave_id();
     const int sub = l / LPR, part = l % LPR;
@@ -580,12 +603,17 @@ __global__ __launch_bounds__(256) void decay_grad_rows_kernel(DecayGradParams p)
         const long t = t0 + sub;
         float s = 0.f;
         if (t < p.n) {
-            const size_t off = (size_t)t * D + part * 4;
-            const f32x4 q = load4f(Q + off), dq = load4f(dQ + off);
-            const f32x4 z = load4f(Zt + off), dz = load4f(dZ + off);
-            const f32x4 k = load4f(K + off), dk = load4f(dK + off);
+            const size_t off = (size_t)t * D + part * R::N;
+            R q, dq, z, dz, k, dk;
+            q.load(Q + off);
+            dq.load(dQ + off);
+            z.load(Zt + off);
+            dz.load(dZ + off);
+            k.load(K + off);
+            dk.load(dK + off);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s += 2.f * q[j] * dq[j] - 3.f * z[j] * dz[j] - 0.5f * k[j] * dk[j];
+            for (int j = 0; j < R::N; ++j)
+                s += 2.f * q.x[j] * dq.x[j] - 3.f * z.x[j] * dz.x[j] - 0.5f * k.x[j] * dk.x[j];
         }
 #pragma unroll
         for (int m = LPR / 2; m > 0; m >>= 1) s += __shfl_xor(s, m, kWave);
@@ -604,18 +632,20 @@ __global__ __launch_bounds__(256) void decay_grad_rows_kernel(DecayGradParams p)
     }
 }
 
-// Decay gradient, second step: dgamma[h] = (sum over b and the row
-// workgroups of head b*H + h, in a fixed order) / g_h.
-__global__ __launch_bounds__(256) void decay_grad_final_kernel(DecayGradParams p) {
+// Decay gradient, second step: one wave per head h.  Lane i sums the
+// partials i, i + 64, ... of heads b*H + h (b in order), the lanes are then
+// combined by a fixed butterfly, and dgamma[h] = sum / g_h.
+__global__ __launch_bounds__(kWave) void decay_grad_final_kernel(DecayGradParams p) {
+    const int h = blockIdx.x, l = lane_id();
     const int B = p.BH / p.H;
-    for (int h = threadIdx.x; h < p.H; h += blockDim.x) {
-        double tot = 0.0;
-        for (int b = 0; b < B; ++b) {
-            const double *row = p.partial + (size_t)(b * p.H + h) * p.nblk;
-            for (int x = 0; x < p.nblk; ++x) tot += row[x];
-        }
-        p.dgamma[h] = (float)(tot / (double)p.gamma[gamma_slot(h, p.H)]);
+    double tot = 0.0;
+    for (int b = 0; b < B; ++b) {
+        const double *row = p.partial + (size_t)(b * p.H + h) * p.nblk;
+        for (int x = l; x < p.nblk; x += kWave) tot += row[x];
     }
+#pragma unroll
+    for (int m = kWave / 2; m > 0; m >>= 1) tot += __shfl_xor(tot, m, kWave);
+    if (l == 0) p.dgamma[h] = (float)(tot / (double)p.gamma[gamma_slot(h, p.H)]);
 }
 
 }  // namespace hla

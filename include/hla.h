@@ -48,7 +48,9 @@
  * never prints and never aborts.  All work is enqueued on `stream` (a
  * hipStream_t passed as void*, NULL = the null stream); the call returns
  * after enqueueing.  Concurrent calls on different streams are safe if they
- * use different workspaces and outputs.
+ * use different workspaces and outputs.  Every device buffer must start on
+ * a 16-byte boundary (the kernels move rows in 16-byte pieces; allocations
+ * from hipMalloc or torch are 256-byte aligned); this is not checked.
  *
  * Errors: arguments are validated first, on the host, with no HIP call; on a
  * validation error nothing is enqueued.  A failed launch returns
