@@ -545,7 +545,7 @@ def main():
     # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
     # unnormalised HLA-2 (the variant the backward supports), q, k L2-normalised
     # Gaussian rows, v and the upstream gradient ~ N(0, 1), bf16
-    backward = backward_ratio = backward_decay = third_order = None
+    backward = backward_ratio = backward_decay = third_order = unmasked = None
     if args.backward_steps > 0:
         bseg = args.backward_seg_chunks or hla.backward_default_seg_chunks(B, H, n)
         bnseg = -(-n // (64 * bseg))
@@ -627,6 +627,24 @@ def main():
                           "ms_per_step_with_dgamma": round(dgms, 5),
                           "dgamma_bytes": tokens * 6 * d * 2}
         log(f"[bench] decay backward: {dms:.4f} ms/step, with dL/dgamma {dgms:.4f} ms/step")
+        # unmasked (non-causal) operators on the forward's inputs
+        unmasked = {}
+        for uv in ("hla2", "ahla"):
+            uo = torch.empty_like(q)
+            uws = torch.empty(max(hla.unmasked_workspace_bytes(B, H, n, d), 1), dtype=torch.uint8,
+                              device=dev)
+            for _ in range(10):
+                hla.hla_unmasked_forward(q, k, v, uv, out=uo, workspace=uws)
+            torch.cuda.synchronize()
+            t_start.record()
+            for _ in range(args.backward_steps):
+                hla.hla_unmasked_forward(q, k, v, uv, out=uo, workspace=uws)
+            t_end.record()
+            torch.cuda.synchronize()
+            ums = t_start.elapsed_time(t_end) / args.backward_steps
+            unmasked[uv] = {"ms_per_step": round(ums, 5), "tokens_per_s": round(tokens / (ums * 1e-3), 1)}
+            log(f"[bench] unmasked {uv}: {ums:.4f} ms/step")
+            del uo, uws
         del dob
 
     # ---- CPU baseline: the oracle on the same inputs, all heads
@@ -674,6 +692,7 @@ def main():
         "backward": backward,
         "backward_ratio": backward_ratio,
         "backward_decay": backward_decay,
+        "unmasked": unmasked,
         "third_order": third_order,
         "cpu_baseline": cpu,
     }

@@ -24,7 +24,8 @@ import os
 
 __all__ = ["HLAError", "VARIANTS", "load", "library_path", "ForwardPlan", "StepPlan",
            "BackwardPlan", "hla_forward", "hla_forward_stage", "hla_backward",
-           "hla_step", "backward_workspace_bytes", "backward_default_seg_chunks",
+           "hla_step", "hla_unmasked_forward", "backward_workspace_bytes",
+           "backward_default_seg_chunks", "unmasked_workspace_bytes",
            "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,10 @@ def load():
     lib.hla_backward_workspace_bytes.restype = Z
     lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, P, I, P, Z, P]
     lib.hla_backward.restype = I
+    lib.hla_unmasked_workspace_bytes.argtypes = [I, I, I, I]
+    lib.hla_unmasked_workspace_bytes.restype = Z
+    lib.hla_unmasked_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.hla_unmasked_forward.restype = I
     lib.hla_status_str.argtypes = [I]
     lib.hla_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -374,3 +379,42 @@ def hla_backward(q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0, d
     With ``dgamma`` (True or an fp32 [H] tensor) also returns dL/dgamma."""
     return BackwardPlan(q, k, v, do, variant, gamma, seg_chunks, dq, dk, dv, workspace,
                         stream, dgamma).run()
+
+
+def unmasked_workspace_bytes(B, H, n, d) -> int:
+    return int(load().hla_unmasked_workspace_bytes(B, H, n, d))
+
+
+def hla_unmasked_forward(q, k, v, variant="hla2", out=None, workspace=None, stream=None):
+    """Unmasked (non-causal) operator over [B, H, n, d] tensors (d == dv, one
+    dtype): "hla2" gives Q (K^T K)(Q^T V), "ahla" gives Q (K^T Q)(K^T V).
+    Returns o [B, H, n, d] (``out`` if given)."""
+    import torch
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_device_tensor(name, t)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise HLAError("expected q, k, v of one shape [B, H, n, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise HLAError("q, k, v must share one dtype")
+    B, H, n, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_device_tensor("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise HLAError("out has the wrong shape or dtype")
+    need = int(lib.hla_unmasked_workspace_bytes(B, H, n, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    VP, CI = ctypes.c_void_p, ctypes.c_int
+    with torch.cuda.device(q.device):
+        rc = lib.hla_unmasked_forward(VP(q.data_ptr()), VP(k.data_ptr()), VP(v.data_ptr()),
+                                      VP(out.data_ptr()), CI(B), CI(H), CI(n), CI(d),
+                                      CI(_dtype_code(q)), CI(_variant(variant)),
+                                      VP(workspace.data_ptr()),
+                                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                      _stream_ptr(stream, q.device))
+    if rc != 0:
+        raise HLAError(f"hla_unmasked_forward failed: {status_str(rc)} (code {rc})")
+    return out

@@ -1,0 +1,274 @@
+// unmasked.hip -- the unmasked (non-causal) second-order operators, and their
+// C entry points (declared in include/hla.h).
+//
+// Page: "Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)"
+// (gist.science/es/paper/2510.27258).  Without the causal masks the
+// second-order operator of "1. HLA de Segundo Orden" is the product of the
+// prefix moments taken over the whole sequence, and the asymmetric operator
+// of "2. ... (AHLA)" likewise:
+//     HLA-2:  o = (Q K^T)(K Q^T) V = Q (K^T K)(Q^T V)
+//     AHLA :  o = (Q K^T)(Q K^T) V = Q (K^T Q)(K^T V)
+// Both are o_t = T^T q_t with one d x d matrix T = G1 G2 per head, where G1,
+// G2 are token sums of outer products (G1 = X^T Y, G2 = U^T W).  Three
+// launches: per-block partial sums of G1 and G2, their fixed-order sum and
+// product T, and the per-row read-out.  All arithmetic is fp32.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/hla.h"
+#include "device_common.h"
+
+namespace hla {
+namespace {
+
+struct UnmaskedParams {
+    const void *x, *y, *u, *w;   // [BH][n][D] operands of G1 = X^T Y, G2 = U^T W
+    const void *q;               // [BH][n][D] queries of the read-out
+    void *o;                     // [BH][n][D] output
+    float *partial;              // [BH][nblk][2][D][D]
+    float *tmat;                 // [BH][D][D]
+    long n;
+    int BH, nblk;
+};
+
+constexpr int kUnmaskedMaxBlocks = 64;   // partial-sum workgroups per head, at most
+
+// Workgroups per head of the partial-sum launch: about 512 in all, each over
+// at least 32 tokens.
+long unmasked_blocks(long BH, long n) {
+    long nb = (512 + BH - 1) / BH;
+    const long by_len = (n + 31) / 32;
+    if (nb > by_len) nb = by_len;
+    if (nb > kUnmaskedMaxBlocks) nb = kUnmaskedMaxBlocks;
+    return nb < 1 ? 1 : nb;
+}
+
+template <typename T> __device__ __forceinline__ f32x4 ld4(const T *p);
+template <> __device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
+    union { uint2 u; bf16 h[4]; } x;
+    x.u = *reinterpret_cast<const uint2 *>(p);
+    return f32x4{(float)x.h[0], (float)x.h[1], (float)x.h[2], (float)x.h[3]};
+}
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+
+// Step 1: workgroup (x, bh) sums x_t y_t^T and u_t w_t^T over its token range
+// (32-token tiles staged in LDS as fp32).  Thread i owns the 4 x 4 blocks
+// i, i + 256, ... of both matrices.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void unmasked_gram_kernel(UnmaskedParams p) {
+    constexpr int TT = 32, NBD = D / 4, NB = NBD * NBD, BPT = (NB + 255) / 256;
+    __shared__ alignas(16) float sx[TT][D], sy[TT][D], su[TT][D], sw[TT][D];
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const long per = (p.n + p.nblk - 1) / p.nblk;
+    const long t_begin = (long)blockIdx.x * per;
+    const long t_end = min(p.n, t_begin + per);
+    const size_t head = (size_t)bh * p.n * D;
+    const T *X = static_cast<const T *>(p.x) + head, *Y = static_cast<const T *>(p.y) + head;
+    const T *U = static_cast<const T *>(p.u) + head, *W = static_cast<const T *>(p.w) + head;
+    float a1[BPT][4][4], a2[BPT][4][4];
+#pragma unroll
+    for (int m = 0; m < BPT; ++m)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) a1[m][a][b] = a2[m][a][b] = 0.f;
+    for (long t0 = t_begin; t0 < t_end; t0 += TT) {
+        for (int e = tid; e < TT * NBD; e += 256) {
+            const int r = e / NBD, c = 4 * (e % NBD);
+            const long t = t0 + r;
+            const bool ok = t < t_end;
+            const size_t off = (size_t)t * D + c;
+            *reinterpret_cast<f32x4 *>(&sx[r][c]) = ok ? ld4(X + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4 *>(&sy[r][c]) = ok ? ld4(Y + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4 *>(&su[r][c]) = ok ? ld4(U + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4 *>(&sw[r][c]) = ok ? ld4(W + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        __syncthreads();
+        for (int r = 0; r < TT; ++r) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m) {
+                const int bidx = tid + 256 * m;
+                if (bidx < NB) {
+                    const int bi = 4 * (bidx / NBD), bj = 4 * (bidx % NBD);
+                    const f32x4 xv = *reinterpret_cast<const f32x4 *>(&sx[r][bi]);
+                    const f32x4 yv = *reinterpret_cast<const f32x4 *>(&sy[r][bj]);
+                    const f32x4 uv = *reinterpret_cast<const f32x4 *>(&su[r][bi]);
+                    const f32x4 wv = *reinterpret_cast<const f32x4 *>(&sw[r][bj]);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            a1[m][a][b] += xv[a] * yv[b];
+                            a2[m][a][b] += uv[a] * wv[b];
+                        }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float *out = p.partial + ((size_t)bh * p.nblk + blockIdx.x) * 2 * D * D;
+#pragma unroll
+    for (int m = 0; m < BPT; ++m) {
+        const int bidx = tid + 256 * m;
+        if (bidx < NB) {
+            const int bi = 4 * (bidx / NBD), bj = 4 * (bidx % NBD);
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                *reinterpret_cast<f32x4 *>(out + (bi + a) * D + bj) =
+                    f32x4{a1[m][a][0], a1[m][a][1], a1[m][a][2], a1[m][a][3]};
+                *reinterpret_cast<f32x4 *>(out + D * D + (bi + a) * D + bj) =
+                    f32x4{a2[m][a][0], a2[m][a][1], a2[m][a][2], a2[m][a][3]};
+            }
+        }
+    }
+}
+
+// Step 2: workgroup bh sums its partials in block order and forms T = G1 G2.
+template <int D>
+__global__ __launch_bounds__(256) void unmasked_product_kernel(UnmaskedParams p) {
+    __shared__ alignas(16) float g1[D * D], g2[D * D];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const float *part = p.partial + (size_t)bh * p.nblk * 2 * D * D;
+    for (int e = tid; e < D * D; e += 256) {
+        float s1 = 0.f, s2 = 0.f;
+        for (int x = 0; x < p.nblk; ++x) {
+            s1 += part[(size_t)x * 2 * D * D + e];
+            s2 += part[(size_t)x * 2 * D * D + D * D + e];
+        }
+        g1[e] = s1;
+        g2[e] = s2;
+    }
+    __syncthreads();
+    float *Tm = p.tmat + (size_t)bh * D * D;
+    for (int e = tid; e < D * D; e += 256) {
+        const int i = e / D, j = e % D;
+        float acc = 0.f;
+        for (int m = 0; m < D; ++m) acc += g1[i * D + m] * g2[m * D + j];
+        Tm[e] = acc;
+    }
+}
+
+// Step 3: workgroup (x, bh) writes o_t = T^T q_t for 64 tokens; thread
+// (r, c) forms columns c*D/4 .. of token r.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void unmasked_apply_kernel(UnmaskedParams p) {
+    constexpr int QC = D / 4;
+    __shared__ alignas(16) float tm[D * D];
+    __shared__ float sq[64][D + 1];
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const long t0 = (long)blockIdx.x * 64;
+    const float *Tm = p.tmat + (size_t)bh * D * D;
+    for (int e = tid; e < D * D / 4; e += 256)
+        *reinterpret_cast<f32x4 *>(&tm[4 * e]) = *reinterpret_cast<const f32x4 *>(Tm + 4 * e);
+    const T *Q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
+    for (int e = tid; e < 64 * (D / 4); e += 256) {
+        const int r = e / (D / 4), c = 4 * (e % (D / 4));
+        const long t = t0 + r;
+        const f32x4 v = t < p.n ? ld4(Q + (size_t)t * D + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sq[r][c + j] = v[j];
+    }
+    __syncthreads();
+    const int r = tid / 4, c = tid % 4;
+    float acc[QC];
+#pragma unroll
+    for (int j = 0; j < QC; ++j) acc[j] = 0.f;
+    for (int i = 0; i < D; ++i) {
+        const float qi = sq[r][i];
+#pragma unroll
+        for (int j = 0; j < QC; ++j) acc[j] += qi * tm[i * D + c * QC + j];
+    }
+    const long t = t0 + r;
+    if (t < p.n) {
+        T *O = static_cast<T *>(p.o) + ((size_t)bh * p.n + t) * D + c * QC;
+#pragma unroll
+        for (int j = 0; j < QC; ++j) O[j] = from_f<T>(acc[j]);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_unmasked(const UnmaskedParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((unmasked_gram_kernel<T, D>), dim3((unsigned)p.nblk, (unsigned)p.BH),
+                       dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((unmasked_product_kernel<D>), dim3((unsigned)p.BH), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((unmasked_apply_kernel<T, D>), dim3((unsigned)((p.n + 63) / 64), (unsigned)p.BH),
+                       dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*UnmaskedLaunch)(const UnmaskedParams &, hipStream_t);
+
+UnmaskedLaunch lookup_unmasked(int dtype, int d) {
+    if (dtype == HLA_F32) {
+        switch (d) {
+            case 16: return launch_unmasked<float, 16>;
+            case 32: return launch_unmasked<float, 32>;
+            case 64: return launch_unmasked<float, 64>;
+            case 128: return launch_unmasked<float, 128>;
+        }
+        return nullptr;
+    }
+    switch (d) {
+        case 16: return launch_unmasked<bf16, 16>;
+        case 32: return launch_unmasked<bf16, 32>;
+        case 64: return launch_unmasked<bf16, 64>;
+        case 128: return launch_unmasked<bf16, 128>;
+    }
+    return nullptr;
+}
+
+}  // namespace
+}  // namespace hla
+
+using namespace hla;
+
+extern "C" {
+
+size_t hla_unmasked_workspace_bytes(int B, int H, int n, int d) {
+    if (B < 1 || H < 1 || n < 1 || d < 1) return 0;
+    const long BH = (long)B * H;
+    const long nb = unmasked_blocks(BH, n);
+    return (size_t)BH * (size_t)(2 * nb + 1) * d * d * sizeof(float);
+}
+
+hla_status hla_unmasked_forward(const void *q, const void *k, const void *v, void *o, int B,
+                                int H, int n, int d, int dtype, int variant, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+    if (dtype != HLA_F32 && dtype != HLA_BF16) return HLA_ERR_ARG;
+    if (variant < HLA_HLA2 || variant > HLA_HLA3) return HLA_ERR_ARG;
+    if (B < 1 || H < 1 || d < 1 || n < 0) return HLA_ERR_SHAPE;
+    if (variant != HLA_HLA2 && variant != HLA_AHLA) return HLA_ERR_UNSUPPORTED;
+    if ((long)B * H > 65535) return HLA_ERR_UNSUPPORTED;
+    const UnmaskedLaunch fn = lookup_unmasked(dtype, d);
+    if (!fn) return HLA_ERR_UNSUPPORTED;
+    if ((n + 63L) / 64 > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    if (n == 0) return HLA_OK;
+    if (!q || !k || !v || !o) return HLA_ERR_NULL;
+    if (!workspace) return HLA_ERR_NULL;
+    if (workspace_bytes < hla_unmasked_workspace_bytes(B, H, n, d)) return HLA_ERR_WORKSPACE;
+    UnmaskedParams p;
+    memset(&p, 0, sizeof(p));
+    const bool hla2 = variant == HLA_HLA2;
+    p.x = k;                      // G1 = K^T K (HLA-2) or K^T Q (AHLA)
+    p.y = hla2 ? k : q;
+    p.u = hla2 ? q : k;           // G2 = Q^T V (HLA-2) or K^T V (AHLA)
+    p.w = v;
+    p.q = q;
+    p.o = o;
+    p.BH = B * H;
+    p.n = n;
+    p.nblk = (int)unmasked_blocks(p.BH, n);
+    p.partial = static_cast<float *>(workspace);
+    p.tmat = p.partial + (size_t)p.BH * p.nblk * 2 * d * d;
+    return fn(p, static_cast<hipStream_t>(stream)) == hipSuccess ? HLA_OK : HLA_ERR_DEVICE;
+}
+
+}  // extern "C"

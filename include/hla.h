@@ -253,6 +253,27 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
                         int dtype, int variant, const float *gamma_host, float *dgamma,
                         int seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Unmasked (non-causal) second-order operators: the operators of sections
+ * "1. HLA de Segundo Orden" and "2. ... (AHLA)" without the causal masks,
+ * i.e. the products of the moments over the whole sequence:
+ *     variant HLA_HLA2:  o = (Q K^T)(K Q^T) V = Q (K^T K)(Q^T V)
+ *     variant HLA_AHLA:  o = (Q K^T)(Q K^T) V = Q (K^T Q)(K^T V)
+ * Every output row sees every token, so there is no streaming state, decay
+ * or decode step.  Three launches on `stream`: per-block fp32 partial sums of
+ * the two d x d moments, their sum (in a fixed order) and product T, then
+ * o_t = T^T q_t.  fp32 arithmetic throughout (bf16 inputs are widened).
+ *
+ * q, k, v, o  device, [B][H][n][d] (dv == d), element type = dtype
+ * workspace   device buffer of at least hla_unmasked_workspace_bytes() bytes
+ *             (B*H*(2*nblk + 1)*d*d fp32, nblk <= 64 partial blocks per head)
+ * Supported: HLA_HLA2 and HLA_AHLA only (the ratio forms and
+ * HLA_HLA3: HLA_ERR_UNSUPPORTED), d in {16, 32, 64, 128} for both dtypes.
+ * n == 0: nothing to do, HLA_OK.  Errors as hla_forward. */
+size_t hla_unmasked_workspace_bytes(int B, int H, int n, int d);
+hla_status hla_unmasked_forward(const void *q, const void *k, const void *v, void *o, int B,
+                                int H, int n, int d, int dtype, int variant, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *hla_status_str(int status);
 

@@ -17,6 +17,8 @@ Contents
                    rule applied to the n x n matrix form, fp64 NumPy.
 ``third_order.py`` the masked third-order operator tril(L L^T) L V: loops,
                    matrix form and a serial recurrence, fp64 NumPy.
+``unmasked.py``    the unmasked operators (A A^T) V and (A A) V: loops and
+                   the matrix product, fp64 NumPy.
 
 Source for every formula: "Resumen Tecnico: Atencion Lineal de Orden Superior
 (HLA)", gist.science/es/paper/2510.27258, sections "1. HLA de Segundo Orden",

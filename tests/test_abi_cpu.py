@@ -272,3 +272,31 @@ def test_backward_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 1, 64, 16)
     with pytest.raises(hla.HLAError):
         hla.hla_backward(x, x, x, x)
+
+
+# ------------------------------------------------------------------ unmasked
+
+def test_unmasked_sizes_and_validation(lib):
+    P = ctypes.c_void_p
+    B, H, n, d = 2, 4, 1000, 64
+    nb = min(-(-512 // (B * H)), -(-n // 32), 64)
+    assert lib.hla_unmasked_workspace_bytes(B, H, n, d) == B * H * (2 * nb + 1) * d * d * 4
+    assert hla.unmasked_workspace_bytes(1, 1, 10, 16) == 1 * (2 * 1 + 1) * 16 * 16 * 4
+    assert lib.hla_unmasked_workspace_bytes(B, H, 0, d) == 0
+
+    def fwd(q=1, k=1, v=1, o=1, B=B, H=H, n=n, d=d, dtype=BF16, variant=HLA2, ws=1,
+            wsb=1 << 40):
+        return lib.hla_unmasked_forward(P(q), P(k), P(v), P(o), B, H, n, d, dtype, variant,
+                                        P(ws), wsb, None)
+    assert fwd(n=0) == OK
+    assert fwd(dtype=5) == ERR_ARG
+    assert fwd(variant=9) == ERR_ARG
+    assert fwd(variant=HLA2_RATIO) == ERR_UNSUP
+    assert fwd(variant=AHLA_RATIO) == ERR_UNSUP
+    assert fwd(variant=4) == ERR_UNSUP
+    assert fwd(d=48) == ERR_UNSUP
+    assert fwd(B=0) == ERR_SHAPE
+    assert fwd(n=-1) == ERR_SHAPE
+    assert fwd(q=None) == ERR_NULL
+    assert fwd(ws=None) == ERR_NULL
+    assert fwd(wsb=16) == ERR_WS
