@@ -127,6 +127,72 @@ __global__ __launch_bounds__(256) void unmasked_gram_kernel(UnmaskedParams p) {
     }
 }
 
+// Step 1 for bf16 inputs, on the matrix cores: the same sums as
+// unmasked_gram_kernel, G[i][j] += sum_t x_t[i] y_t[j], as 16 x 16 tiles of
+// mfma_f32_16x16x32_bf16 over 32-token tiles.  The tile is staged
+// feature-major (xT[feature][token], rows padded to 40 tokens), so a lane's
+// operand (8 consecutive tokens of one feature) is one 16-byte LDS read, for
+// both operands.  Wave w owns tiles w, w + 4, ... of [G1 tiles | G2 tiles];
+// accumulator element r of lane l is G[16 ti + 4 (l / 16) + r][16 tj + l % 16].
+template <int D>
+__global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams p) {
+    constexpr int TT = 32, LD = TT + 8, NTD = D / 16, NT1 = NTD * NTD, NT = 2 * NT1;
+    constexpr int TPW = (NT + 3) / 4;
+    __shared__ alignas(16) bf16 xT[D][LD], yT[D][LD], uT[D][LD], wT[D][LD];
+    const int bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const long per = (p.n + p.nblk - 1) / p.nblk;
+    const long t_begin = (long)blockIdx.x * per;
+    const long t_end = min(p.n, t_begin + per);
+    const size_t head = (size_t)bh * p.n * D;
+    const bf16 *src[4] = {static_cast<const bf16 *>(p.x) + head, static_cast<const bf16 *>(p.y) + head,
+                          static_cast<const bf16 *>(p.u) + head, static_cast<const bf16 *>(p.w) + head};
+    bf16 (*dst[4])[LD] = {xT, yT, uT, wT};
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (long t0 = t_begin; t0 < t_end; t0 += TT) {
+        // stage: 8 features of one token per thread and tensor, transposed
+        for (int e = tid; e < TT * (D / 8); e += 256) {
+            const int r = e / (D / 8), f = 8 * (e % (D / 8));
+            const long t = t0 + r;
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const bf16x8 v = t < t_end ? *reinterpret_cast<const bf16x8 *>(src[a] + (size_t)t * D + f)
+                                           : bf16x8{};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dst[a][f + j][r] = v[j];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < TPW; ++m) {
+            const int tau = w + 4 * m;
+            if (tau < NT) {
+                const int mat = tau / NT1, rem = tau % NT1;
+                const int ti = rem / NTD, tj = rem % NTD;
+                const bf16 (*A)[LD] = mat == 0 ? xT : uT;
+                const bf16 (*Bm)[LD] = mat == 0 ? yT : wT;
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&A[16 * ti + (l & 15)][8 * (l >> 4)]);
+                const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&Bm[16 * tj + (l & 15)][8 * (l >> 4)]);
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[m], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+    float *out = p.partial + ((size_t)bh * p.nblk + blockIdx.x) * 2 * D * D;
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+        const int tau = w + 4 * m;
+        if (tau < NT) {
+            const int mat = tau / NT1, rem = tau % NT1;
+            const int ti = rem / NTD, tj = rem % NTD;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                out[mat * D * D + (16 * ti + 4 * (l >> 4) + r) * D + 16 * tj + (l & 15)] = acc[m][r];
+        }
+    }
+}
+
 // Step 2: workgroup bh sums its partials in block order and forms T = G1 G2.
 template <int D>
 __global__ __launch_bounds__(256) void unmasked_product_kernel(UnmaskedParams p) {
@@ -192,8 +258,12 @@ __global__ __launch_bounds__(256) void unmasked_apply_kernel(UnmaskedParams p) {
 
 template <typename T, int D>
 hipError_t launch_unmasked(const UnmaskedParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((unmasked_gram_kernel<T, D>), dim3((unsigned)p.nblk, (unsigned)p.BH),
-                       dim3(256), 0, s, p);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((unmasked_gram_mfma_kernel<D>), dim3((unsigned)p.nblk, (unsigned)p.BH),
+                           dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((unmasked_gram_kernel<T, D>), dim3((unsigned)p.nblk, (unsigned)p.BH),
+                           dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((unmasked_product_kernel<D>), dim3((unsigned)p.BH), dim3(256), 0, s, p);
