@@ -11,7 +11,9 @@
 // Both are o_t = T^T q_t with one d x d matrix T = G1 G2 per head, where G1,
 // G2 are token sums of outer products (G1 = X^T Y, G2 = U^T W).  Three
 // launches: per-block partial sums of G1 and G2, their fixed-order sum and
-// product T, and the per-row read-out.  All arithmetic is fp32.
+// product T, and the per-row read-out.  fp32 arithmetic, except that for
+// bf16 inputs the moment sums and (d >= 32) the read-out run on bf16 MFMA
+// with fp32 accumulation, the read-out with T rounded to bf16.
 #include <stdint.h>
 #include <string.h>
 
@@ -29,6 +31,7 @@ struct UnmaskedParams {
     void *o;                     // [BH][n][D] output
     float *partial;              // [BH][nblk][2][D][D]
     float *tmat;                 // [BH][D][D]
+    bf16 *tmat_t;                // [BH][D][D] T transposed, bf16 (MFMA read-out)
     long n;
     int BH, nblk;
 };
@@ -215,6 +218,51 @@ __global__ __launch_bounds__(256) void unmasked_product_kernel(UnmaskedParams p)
         float acc = 0.f;
         for (int m = 0; m < D; ++m) acc += g1[i * D + m] * g2[m * D + j];
         Tm[e] = acc;
+        p.tmat_t[(size_t)bh * D * D + j * D + i] = (bf16)acc;
+    }
+}
+
+// Step 3 for bf16 inputs and D >= 32, on the matrix cores: o = Q T with T
+// rounded to bf16.  Wave w forms tokens t0 + 16 w .. + 15, all D columns, as
+// D/16 tiles of mfma_f32_16x16x32_bf16: lane l's A operand is 8 consecutive
+// features of token 16 w + l % 16 (one 16-byte load from HBM), its B operand
+// 8 consecutive rows of column 16 tj + l % 16 of T, i.e. a 16-byte piece of
+// a row of T^T (staged in LDS); accumulator r is o[16 w + 4 (l / 16) + r].
+template <int D>
+__global__ __launch_bounds__(256) void unmasked_apply_mfma_kernel(UnmaskedParams p) {
+    constexpr int NTD = D / 16, LD = D + 8;
+    __shared__ alignas(16) bf16 tt[D][LD];
+    const int bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const bf16 *Tt = p.tmat_t + (size_t)bh * D * D;
+    for (int e = tid; e < D * D / 8; e += 256) {
+        const int r = e / (D / 8), c = 8 * (e % (D / 8));
+        *reinterpret_cast<bf16x8 *>(&tt[r][c]) = *reinterpret_cast<const bf16x8 *>(Tt + r * D + c);
+    }
+    __syncthreads();
+    const long t0 = (long)blockIdx.x * 64 + 16 * w;
+    const long ta = t0 + (l & 15);
+    const bf16 *Q = static_cast<const bf16 *>(p.q) + (size_t)bh * p.n * D;
+    f32x4 acc[NTD];
+#pragma unroll
+    for (int j = 0; j < NTD; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D; ks += 32) {
+        const bf16x8 a = ta < p.n ? *reinterpret_cast<const bf16x8 *>(Q + (size_t)ta * D + ks + 8 * (l >> 4))
+                                  : bf16x8{};
+#pragma unroll
+        for (int j = 0; j < NTD; ++j) {
+            const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&tt[16 * j + (l & 15)][ks + 8 * (l >> 4)]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        }
+    }
+    bf16 *O = static_cast<bf16 *>(p.o) + (size_t)bh * p.n * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const long t = t0 + 4 * (l >> 4) + r;
+        if (t < p.n) {
+#pragma unroll
+            for (int j = 0; j < NTD; ++j) O[(size_t)t * D + 16 * j + (l & 15)] = (bf16)acc[j][r];
+        }
     }
 }
 
@@ -269,8 +317,11 @@ hipError_t launch_unmasked(const UnmaskedParams &p, hipStream_t s) {
     hipLaunchKernelGGL((unmasked_product_kernel<D>), dim3((unsigned)p.BH), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((unmasked_apply_kernel<T, D>), dim3((unsigned)((p.n + 63) / 64), (unsigned)p.BH),
-                       dim3(256), 0, s, p);
+    const dim3 grid((unsigned)((p.n + 63) / 64), (unsigned)p.BH);
+    if constexpr (sizeof(T) == 2 && D >= 32)
+        hipLaunchKernelGGL((unmasked_apply_mfma_kernel<D>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((unmasked_apply_kernel<T, D>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -306,7 +357,8 @@ size_t hla_unmasked_workspace_bytes(int B, int H, int n, int d) {
     if (B < 1 || H < 1 || n < 1 || d < 1) return 0;
     const long BH = (long)B * H;
     const long nb = unmasked_blocks(BH, n);
-    return (size_t)BH * (size_t)(2 * nb + 1) * d * d * sizeof(float);
+    return (size_t)BH * (size_t)(2 * nb + 1) * d * d * sizeof(float) +
+           (size_t)BH * d * d * sizeof(bf16);
 }
 
 hla_status hla_unmasked_forward(const void *q, const void *k, const void *v, void *o, int B,
@@ -338,6 +390,7 @@ hla_status hla_unmasked_forward(const void *q, const void *k, const void *v, voi
     p.nblk = (int)unmasked_blocks(p.BH, n);
     p.partial = static_cast<float *>(workspace);
     p.tmat = p.partial + (size_t)p.BH * p.nblk * 2 * d * d;
+    p.tmat_t = reinterpret_cast<bf16 *>(p.tmat + (size_t)p.BH * d * d);
     return fn(p, static_cast<hipStream_t>(stream)) == hipSuccess ? HLA_OK : HLA_ERR_DEVICE;
 }
 

@@ -261,11 +261,14 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
  * Every output row sees every token, so there is no streaming state, decay
  * or decode step.  Three launches on `stream`: per-block fp32 partial sums of
  * the two d x d moments, their sum (in a fixed order) and product T, then
- * o_t = T^T q_t.  fp32 arithmetic throughout (bf16 inputs are widened).
+ * o_t = T^T q_t.  fp32 inputs: fp32 arithmetic throughout.  bf16 inputs:
+ * the moment sums on bf16 MFMA with fp32 accumulation, T in fp32, and for
+ * d >= 32 the read-out on bf16 MFMA with T rounded to bf16.
  *
  * q, k, v, o  device, [B][H][n][d] (dv == d), element type = dtype
  * workspace   device buffer of at least hla_unmasked_workspace_bytes() bytes
- *             (B*H*(2*nblk + 1)*d*d fp32, nblk <= 64 partial blocks per head)
+ *             (B*H*(2*nblk + 1)*d*d fp32 and B*H*d*d bf16, nblk <= 64
+ *             partial blocks per head)
  * Supported: HLA_HLA2 and HLA_AHLA only (the ratio forms and
  * HLA_HLA3: HLA_ERR_UNSUPPORTED), d in {16, 32, 64, 128} for both dtypes.
  * n == 0: nothing to do, HLA_OK.  Errors as hla_forward. */

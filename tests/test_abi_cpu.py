@@ -280,8 +280,9 @@ def test_unmasked_sizes_and_validation(lib):
     P = ctypes.c_void_p
     B, H, n, d = 2, 4, 1000, 64
     nb = min(-(-512 // (B * H)), -(-n // 32), 64)
-    assert lib.hla_unmasked_workspace_bytes(B, H, n, d) == B * H * (2 * nb + 1) * d * d * 4
-    assert hla.unmasked_workspace_bytes(1, 1, 10, 16) == 1 * (2 * 1 + 1) * 16 * 16 * 4
+    assert lib.hla_unmasked_workspace_bytes(B, H, n, d) == \
+        B * H * (2 * nb + 1) * d * d * 4 + B * H * d * d * 2
+    assert hla.unmasked_workspace_bytes(1, 1, 10, 16) == (2 * 1 + 1) * 16 * 16 * 4 + 16 * 16 * 2
     assert lib.hla_unmasked_workspace_bytes(B, H, 0, d) == 0
 
     def fwd(q=1, k=1, v=1, o=1, B=B, H=H, n=n, d=d, dtype=BF16, variant=HLA2, ws=1,
