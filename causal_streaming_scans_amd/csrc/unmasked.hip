@@ -132,16 +132,18 @@ __global__ __launch_bounds__(256) void unmasked_gram_kernel(UnmaskedParams p) {
 
 // Step 1 for bf16 inputs, on the matrix cores: the same sums as
 // unmasked_gram_kernel, G[i][j] += sum_t x_t[i] y_t[j], as 16 x 16 tiles of
-// mfma_f32_16x16x32_bf16 over 32-token tiles.  The tile is staged
-// feature-major (xT[feature][token], rows padded to 40 tokens), so a lane's
-// operand (8 consecutive tokens of one feature) is one 16-byte LDS read, for
-// both operands.  Wave w owns tiles w, w + 4, ... of [G1 tiles | G2 tiles];
-// accumulator element r of lane l is G[16 ti + 4 (l / 16) + r][16 tj + l % 16].
+// mfma_f32_16x16x32_bf16 over 32-token tiles.  Each tile is staged
+// row-major ([token][feature], LdsTile layout) with 16-byte copies, and both
+// operands (8 consecutive tokens of one feature per lane) come from the
+// transposing LDS read.  Wave w owns tiles w, w + 4, ... of [G1 tiles | G2
+// tiles]; accumulator element r of lane l is
+// G[16 ti + 4 (l / 16) + r][16 tj + l % 16].
 template <int D>
 __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams p) {
-    constexpr int TT = 32, LD = TT + 8, NTD = D / 16, NT1 = NTD * NTD, NT = 2 * NT1;
+    using TL = LdsTile<bf16, D>;
+    constexpr int TT = 32, NTD = D / 16, NT1 = NTD * NTD, NT = 2 * NT1;
     constexpr int TPW = (NT + 3) / 4;
-    __shared__ alignas(16) bf16 xT[D][LD], yT[D][LD], uT[D][LD], wT[D][LD];
+    __shared__ alignas(16) bf16 tiles[4][TT * TL::LD];
     const int bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = wave_id();
     const long per = (p.n + p.nblk - 1) / p.nblk;
     const long t_begin = (long)blockIdx.x * per;
@@ -149,21 +151,18 @@ __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams 
     const size_t head = (size_t)bh * p.n * D;
     const bf16 *src[4] = {static_cast<const bf16 *>(p.x) + head, static_cast<const bf16 *>(p.y) + head,
                           static_cast<const bf16 *>(p.u) + head, static_cast<const bf16 *>(p.w) + head};
-    bf16 (*dst[4])[LD] = {xT, yT, uT, wT};
     f32x4 acc[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (long t0 = t_begin; t0 < t_end; t0 += TT) {
-        // stage: 8 features of one token per thread and tensor, transposed
         for (int e = tid; e < TT * (D / 8); e += 256) {
-            const int r = e / (D / 8), f = 8 * (e % (D / 8));
+            const int r = e / (D / 8), c = 8 * (e % (D / 8));
             const long t = t0 + r;
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const bf16x8 v = t < t_end ? *reinterpret_cast<const bf16x8 *>(src[a] + (size_t)t * D + f)
+                const bf16x8 v = t < t_end ? *reinterpret_cast<const bf16x8 *>(src[a] + (size_t)t * D + c)
                                            : bf16x8{};
-#pragma unroll
-                for (int j = 0; j < 8; ++j) dst[a][f + j][r] = v[j];
+                *reinterpret_cast<bf16x8 *>(&tiles[a][TL::off(r, c)]) = v;
             }
         }
         __syncthreads();
@@ -173,11 +172,9 @@ __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams 
             if (tau < NT) {
                 const int mat = tau / NT1, rem = tau % NT1;
                 const int ti = rem / NTD, tj = rem % NTD;
-                const bf16 (*A)[LD] = mat == 0 ? xT : uT;
-                const bf16 (*Bm)[LD] = mat == 0 ? yT : wT;
-                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&A[16 * ti + (l & 15)][8 * (l >> 4)]);
-                const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&Bm[16 * tj + (l & 15)][8 * (l >> 4)]);
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[m], 0, 0, 0);
+                const bf16 *A = tiles[mat == 0 ? 0 : 2], *Bm = tiles[mat == 0 ? 1 : 3];
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_op8_tt<TL>(A, 0, 16 * ti),
+                                                                 ld_op8_tt<TL>(Bm, 0, 16 * tj), acc[m], 0, 0, 0);
             }
         }
         __syncthreads();
