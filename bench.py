@@ -660,7 +660,7 @@ def main():
             if dt >= args.cpu_seconds or reps >= 1000:
                 break
         cpu = {"value": round(reps * tokens / dt, 1), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
                "sample": f"the whole workload ({B * H} heads x {n} tokens) {reps} times over, "
                          f"fp64 serial recurrence, one head per thread, {dt:.2f} s wall"}
         log(f"[bench] cpu oracle: {reps} passes in {dt:.2f} s on {threads} threads")
@@ -697,6 +697,18 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (Linux)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -40,4 +40,4 @@ def test_decode_continues_forward(variant, dtype, d):
     say(f"   decode rel_l2 {err:.3e}  state rel_l2 {serr:.3e}")
     assert np.isfinite(got).all()
     assert err < TOL[dtype]
-    assert serr < 10 * TOL[dtype]
+    assert serr < TOL[dtype]

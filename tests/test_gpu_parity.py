@@ -115,7 +115,9 @@ def test_state_out_and_resume(variant, dtype, shape):
     x2 = {kk: x[kk][:, n1:] for kk in ("q", "k", "v")}
     o1, st = gpu_forward(x1, variant, B, H, dtype, chunk, seg1, gamma=g, want_state=True)
     w1, wst = oracle_forward(x1, variant, H, gamma=g, want_state=True)
-    assert rel_l2(st, wst) < 10 * TOL[dtype]
+    serr = rel_l2(st, wst)
+    say(f"   state_out rel_l2 {serr:.3e}")
+    assert serr < TOL[dtype]
     o2 = gpu_forward(x2, variant, B, H, dtype, chunk, seg2, gamma=g, state_in=st)
     whole = oracle_forward(x, variant, H, gamma=g)
     err = rel_l2(np.concatenate([o1, o2], axis=1), whole)

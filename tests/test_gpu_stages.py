@@ -83,7 +83,8 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
     nseg = -(-n // seg_len)
     nreal = nseg - 1
     sumf = d * d + 2 * d * d + 2 * d
-    tol = 10 * TOL[dtype]
+    tol = TOL[dtype]
+    worst = 0.0
 
     def slots():
         torch.cuda.synchronize()
@@ -109,6 +110,7 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
                 for name, a, b in zip(("X", "Y", "N", "y", "nv"), _unpack(stage_ws[bh, s_], d, d),
                                       parts(items[s_])):
                     err = rel_l2(a, b)
+                    worst = max(worst, err)
                     assert err < tol, f"head {bh} summary {s_} part {name}: {err:.3e}"
         for (lev, m, lo, hi, idx) in _nodes(nreal):
             node = items[lo]
@@ -117,5 +119,6 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
             got = _unpack(e[B * H + bh, idx], d, d)
             for name, a, b in zip(("X", "Y", "N", "y", "nv"), got, parts(node)):
                 err = rel_l2(a, b)
+                worst = max(worst, err)
                 assert err < tol, f"head {bh} node ({lev},{m}) [{lo}..{hi}] part {name}: {err:.3e}"
-    say(f"   {nreal} slots per head match")
+    say(f"   {nreal} slots per head match, worst part rel_l2 {worst:.3e}")
