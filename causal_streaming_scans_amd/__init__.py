@@ -22,11 +22,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["HLAError", "VARIANTS", "load", "library_path", "ForwardPlan", "StepPlan",
+__all__ = ["HLAError", "VARIANTS", "NOALLOC_SCRATCH_BYTES", "load", "library_path", "ForwardPlan", "StepPlan",
            "BackwardPlan", "hla_forward", "hla_forward_stage", "hla_backward",
-           "hla_step", "hla_unmasked_forward", "backward_workspace_bytes",
+           "hla_step", "hla_unmasked_forward", "hla_forward_noalloc", "backward_workspace_bytes",
            "backward_default_seg_chunks", "unmasked_workspace_bytes",
            "state_floats", "workspace_bytes", "default_seg_chunks", "status_str"]
+
+# bytes of the library's fixed workspace array behind hla_forward_noalloc
+# (HLA_NOALLOC_SCRATCH_BYTES in include/hla.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhla.so")
@@ -65,6 +69,8 @@ def load():
     lib.hla_workspace_bytes.restype = Z
     lib.hla_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P, Z, P]
     lib.hla_forward.restype = I
+    lib.hla_forward_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P]
+    lib.hla_forward_noalloc.restype = I
     lib.hla_forward_stage.argtypes = [I] + lib.hla_forward.argtypes
     lib.hla_forward_stage.restype = I
     lib.hla_step.argtypes = [P, P, P, P, I, I, I, I, I, I, FP, P, P]
@@ -255,6 +261,26 @@ def hla_forward_stage(stage, q, k, v, variant="hla2", gamma=None, chunk: int = 6
     same arguments (and the same workspace and out) equal hla_forward."""
     return _forward_call(stage, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out,
                          out, workspace, stream)
+
+
+def hla_forward_noalloc(q, k, v, variant="hla2", gamma=None, chunk: int = 64,
+                        seg_chunks: int = 0, state_in=None, state_out=None, out=None,
+                        stream=None):
+    """hla_forward with the library's fixed workspace array (no device
+    allocation inside the call; see include/hla.h).  Same arguments as
+    hla_forward, less ``workspace``.  Raises HLAError with
+    HLA_ERR_WORKSPACE when the call needs more than that array holds."""
+    import torch
+    plan = ForwardPlan(q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
+                       workspace=torch.empty(0, dtype=torch.uint8, device=q.device),
+                       stream=stream)
+    # the plan's arguments less the workspace pointer and size
+    args = plan._args[:16] + plan._args[18:]
+    with torch.cuda.device(plan._dev):
+        rc = plan._lib.hla_forward_noalloc(*args)
+    if rc != 0:
+        raise HLAError(f"hla_forward_noalloc failed: {status_str(rc)} (code {rc})")
+    return plan.out
 
 
 class StepPlan:

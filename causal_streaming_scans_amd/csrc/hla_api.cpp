@@ -679,3 +679,25 @@ const char *hla_status_str(int status) {
 }
 
 }  // extern "C"
+
+// Validation of hla_forward's arguments without a caller workspace: every
+// check of prepare_forward except the workspace's own, and the workspace
+// size the call needs.  No HIP call.
+hla_status hla::forward_validate(const void *q, const void *k, const void *v, void *o, int B,
+                                 int H, int n, int d, int dv, int dtype, int variant,
+                                 const float *gamma_host, int chunk, int seg_chunks,
+                                 const float *state_in, float *state_out, size_t *need) {
+    FwdKernels kern;
+    FwdParams p;
+    Hla3Pass x3;
+    // a stand-in address that passes the workspace checks; prepare_forward
+    // only stores it, and it never reaches a kernel
+    static char stand_in;
+    hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
+                                    seg_chunks, state_in, state_out, &stand_in, SIZE_MAX, &kern,
+                                    &p, &x3);
+    if (st != HLA_OK) return st;
+    const int g = effective_seg_chunks(variant, B, H, n, d, chunk, seg_chunks);
+    *need = n > 0 ? hla_workspace_bytes(variant, B, H, n, d, dv, chunk, g) : 0;
+    return HLA_OK;
+}

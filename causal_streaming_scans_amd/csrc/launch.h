@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "params.h"
+#include "../../include/hla.h"
 
 namespace hla {
 
@@ -48,6 +49,13 @@ struct LaLaunches {
 bool lookup_la(int dtype, int d, LaLaunches *out);
 // bf16 -> fp32 (to_f32) or fp32 -> bf16 copy of count values (a multiple of 4)
 hipError_t launch_convert(const void *src, void *dst, long count, bool to_f32, hipStream_t s);
+
+// hla_forward's argument checks, except the workspace's, with no HIP call;
+// on HLA_OK *need holds the workspace bytes the call needs (hla_api.cpp)
+hla_status forward_validate(const void *q, const void *k, const void *v, void *o, int B, int H,
+                            int n, int d, int dv, int dtype, int variant, const float *gamma_host,
+                            int chunk, int seg_chunks, const float *state_in, float *state_out,
+                            size_t *need);
 
 // fill dst[0:count) with src[0:count), or with zeros when src is null
 hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipStream_t s);

@@ -177,6 +177,36 @@ hla_status hla_forward_stage(int stage, const void *q, const void *k, const void
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * hla_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as hla_forward, without the workspace
+ * arguments: the workspace is a fixed array of HLA_NOALLOC_SCRATCH_BYTES
+ * inside the library, one copy per device, held by each device the library
+ * runs on until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine); the caller still passes q, k, v, o and the
+ * states.  The first call on a device looks up the array's address there
+ * (one hipGetSymbolAddress).
+ *
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: every part a call reads it
+ * writes first).  Calls that overlap in time on one device -- on different
+ * streams or from different threads without ordering -- race on the array and
+ * give wrong results; calls on one stream are ordered and safe.
+ *
+ * Errors: as hla_forward, plus HLA_ERR_WORKSPACE when the call needs more
+ * than HLA_NOALLOC_SCRATCH_BYTES of workspace (hla_workspace_bytes() with
+ * the same arguments; a larger seg_chunks means fewer segments and a smaller
+ * workspace), and HLA_ERR_DEVICE when the array's address cannot be found.
+ * 64 MiB covers, e.g., B*H = 128, n = 4096, d = dv = 64 with the default
+ * segments (38 MB).
+ */
+#define HLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hla_status hla_forward_noalloc(const void *q, const void *k, const void *v, void *o,
+                               int B, int H, int n, int d, int dv, int dtype, int variant,
+                               const float *gamma_host, int chunk, int seg_chunks,
+                               const float *state_in, float *state_out, void *stream);
+
+/*
  * One streaming (decode) step: for every (b,h) take the single token
  * q, k : [B][H][d], v : [B][H][dv], update `state` in place and write
  * o : [B][H][dv].  The update is the same recurrence the forward pass

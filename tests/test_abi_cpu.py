@@ -301,3 +301,25 @@ def test_unmasked_sizes_and_validation(lib):
     assert fwd(q=None) == ERR_NULL
     assert fwd(ws=None) == ERR_NULL
     assert fwd(wsb=16) == ERR_WS
+
+
+def test_noalloc_limit_and_validation(lib):
+    """hla_forward_noalloc: the binding's size constant is the header's, a
+    call needing more workspace than the fixed array holds is refused with
+    HLA_ERR_WORKSPACE, and argument errors come first, as in hla_forward --
+    all before any HIP call (the pointers here are never dereferenced)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define HLA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == hla.NOALLOC_SCRATCH_BYTES
+    P = ctypes.c_void_p
+    big = (64, 16, 8192, 128)
+    assert hla.workspace_bytes("hla2", *big, 128, 16, 1) > hla.NOALLOC_SCRATCH_BYTES
+    call = lambda B, H, n, d, dtype=BF16, variant=HLA2, chunk=16, seg=1: lib.hla_forward_noalloc(
+        P(16), P(16), P(16), P(16), B, H, n, d, d, dtype, variant, None, chunk, seg, None, None,
+        None)
+    assert call(*big) == ERR_WS
+    assert call(*big, dtype=7) == ERR_ARG
+    assert call(64, 16, 8192, 0) == ERR_SHAPE
+    assert call(1, 1, 100, 64, chunk=48) == ERR_UNSUP
+    # no tokens: nothing to do, no workspace, no device work
+    assert call(1, 1, 0, 64) == OK
