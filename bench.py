@@ -203,10 +203,87 @@ def counters_summary(fetch_csv: str, write_csv: str) -> None:
     print(json.dumps(rec, indent=1))
 
 
+def short_kernel_name(name: str) -> str:
+    """hla::<kernel><template arguments> from a mangled or demangled kernel name,
+    e.g. hla2_forward_kernel<bf16,64,64,64,0>."""
+    import re
+    m = re.search(r"_ZN3hla\d+(\w+?)I(.*?)EEvNS_", name)
+    if m:
+        parts = []
+        for tok in re.finditer(r"DF16b|Lb[01]|Li\d+|f(?=L|E)", m.group(2)):
+            t = tok.group(0)
+            parts.append("bf16" if t == "DF16b" else "float" if t == "f" else
+                         t[2:] if t.startswith("Li") else t[2:])
+        return f"{m.group(1)}<{','.join(parts)}>"
+    m = re.search(r"hla::(\w+)", name)
+    return m.group(1) if m else name[:80]
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+SIMD_COUNT = 256 * 4     # MI355X: 256 compute units of 4 SIMDs
+XCD_COUNT = 8            # GRBM_GUI_ACTIVE arrives summed over the 8 XCDs
+NOMINAL_CLOCK_HZ = 2.4e9  # MI355X peak engine clock
+
+
+def mfma_summary(csv_path: str) -> None:
+    """Counter-measured matrix-core use per kernel and launch shape, from one
+    `rocprofv3 --pmc` run with the four MFMA_COUNTERS (csv).  Per dispatch:
+    MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES (summed over every SIMD) /
+    (GRBM_GUI_ACTIVE / XCD_COUNT x SIMD_COUNT) (rocprof's MfmaUtil), and
+    the same over the dispatch's timestamp span at 2.4 GHz (short dispatches
+    count more GUI_ACTIVE cycles than their span, so the first reads low); executed bf16 / fp32 MFMA flops =
+    SQ_INSTS_VALU_MFMA_MOPS_* x 512; TFLOP/s over the dispatch's own
+    timestamps.  GRBM_GUI_ACTIVE arrives summed over the XCDs, so one XCD's
+    busy cycles (the dispatch's length in GPU clocks) are that over XCD_COUNT.
+    Averages over the dispatches of each (kernel, grid) pair;
+    prints one JSON record."""
+    import csv
+    import statistics
+
+    per = {}
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), r["Dispatch_Id"])
+            d = per.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            c, val = r["Counter_Name"], float(r["Counter_Value"])
+            # GRBM_GUI_ACTIVE may be listed twice for one dispatch (same value)
+            d[c] = max(d.get(c, 0.0), val) if c == "GRBM_GUI_ACTIVE" else d.get(c, 0.0) + val
+    groups = {}
+    for (name, grid, _), d in per.items():
+        if not all(c in d for c in MFMA_COUNTERS):
+            continue
+        groups.setdefault((name, grid), []).append(d)
+    rows = []
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        mean = lambda f: statistics.fmean(f(d) for d in ds)
+        busy = mean(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"]
+                    / (d["GRBM_GUI_ACTIVE"] / XCD_COUNT * SIMD_COUNT))
+        mhz = mean(lambda d: d["GRBM_GUI_ACTIVE"] / XCD_COUNT / (d["ns"] * 1e-3))
+        busy_ts = mean(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"]
+                       / (SIMD_COUNT * d["ns"] * 1e-9 * NOMINAL_CLOCK_HZ))
+        fl_bf16 = mean(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512)
+        fl_f32 = mean(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512)
+        us = mean(lambda d: d["ns"]) * 1e-3
+        if fl_bf16 + fl_f32 == 0:
+            continue
+        rows.append({"kernel": short_kernel_name(name), "grid_threads": grid, "dispatches": len(ds),
+                     "us": round(us, 2), "gpu_clock_mhz": round(mhz),
+                     "mfma_busy_pct": round(100 * busy, 2),
+                     "mfma_busy_pct_of_span": round(100 * busy_ts, 2),
+                     "bf16_mfma_gflop": round(fl_bf16 * 1e-9, 3),
+                     "f32_mfma_gflop": round(fl_f32 * 1e-9, 3),
+                     "bf16_tflops": round(fl_bf16 / (us * 1e-6) * 1e-12, 1) if us > 0 else None,
+                     "bf16_peak_frac": round(fl_bf16 / (us * 1e-6) * 1e-12 / BF16_MFMA_PEAK_TFLOPS, 4)
+                     if us > 0 else None})
+    print(json.dumps({"source_hash": kernel_source_hash(), "counters": list(MFMA_COUNTERS),
+                      "kernels": rows}, indent=1))
+
+
 def all_configs(args, hla, I, torch, dev):
     """Forward time of every named workload in its default launch
     configuration (each one library call between two events, after a settle
-    phase); one JSON line.  Only the forward is timed: the AHLA workload's
+    phase of --settle-ms); one JSON line.  Only the forward is timed: the AHLA workload's
     decode tokens are timed by the default run."""
     rows = []
     for key, w in I.WORKLOADS.items():
@@ -219,7 +296,7 @@ def all_configs(args, hla, I, torch, dev):
         plan = hla.ForwardPlan(q, k, v, variant=w.variant, gamma=gamma, chunk=w.chunk)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         settle = 0.0
-        while settle < 200.0:
+        while settle < args.settle_ms:
             e0.record()
             for _ in range(20):
                 plan.run()
@@ -280,6 +357,9 @@ def main():
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM-traffic record from two rocprofv3 --pmc counter csv "
                          "files of a bench.py run (FETCH_SIZE, then WRITE_SIZE), then exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_CSV",
+                    help="per-kernel MFMA busy %% and executed MFMA flops from a rocprofv3 --pmc "
+                         "run with the counters " + " ".join(MFMA_COUNTERS))
     ap.add_argument("--trace-summary", nargs=2, metavar=("KERNEL_TRACE_CSV", "BENCH_JSON"),
                     help="print per-pass kernel durations from a rocprofv3 kernel trace of a "
                          "bench.py run and that run's JSON line, then exit")
@@ -289,6 +369,9 @@ def main():
         return
     if args.counters_summary:
         counters_summary(*args.counters_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.print_source_hash:
         print(kernel_source_hash())
@@ -625,7 +708,8 @@ def main():
                                       "do ~ N(0,1)",
                           "ms_per_step": round(dms, 5),
                           "ms_per_step_with_dgamma": round(dgms, 5),
-                          "dgamma_bytes": tokens * 6 * d * 2}
+                          "dgamma_passes": "fp32 (widened copies of the bf16 inputs)",
+                          "dgamma_bytes": tokens * 6 * d * 4}
         log(f"[bench] decay backward: {dms:.4f} ms/step, with dL/dgamma {dgms:.4f} ms/step")
         # unmasked (non-causal) operators on the forward's inputs
         unmasked = {}

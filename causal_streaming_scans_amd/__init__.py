@@ -77,7 +77,7 @@ def load():
     lib.hla_step.restype = I
     lib.hla_backward_default_seg_chunks.argtypes = [I, I, I]
     lib.hla_backward_default_seg_chunks.restype = I
-    lib.hla_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.hla_backward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
     lib.hla_backward_workspace_bytes.restype = Z
     lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, P, I, P, Z, P]
     lib.hla_backward.restype = I
@@ -119,9 +119,10 @@ def backward_default_seg_chunks(B, H, n) -> int:
     return int(load().hla_backward_default_seg_chunks(B, H, n))
 
 
-def backward_workspace_bytes(variant, B, H, n, d, dv, dtype="bf16", seg_chunks=0) -> int:
+def backward_workspace_bytes(variant, B, H, n, d, dv, dtype="bf16", seg_chunks=0,
+                             dgamma=False) -> int:
     return int(load().hla_backward_workspace_bytes(_variant(variant), B, H, n, d, dv,
-                                                   _DTYPES[dtype], seg_chunks))
+                                                   _DTYPES[dtype], seg_chunks, int(bool(dgamma))))
 
 
 def _dtype_code(t) -> int:
@@ -367,7 +368,8 @@ class BackwardPlan:
             dgamma = None
         self.dgamma = dgamma
         dtc = _dtype_code(q)
-        need = int(lib.hla_backward_workspace_bytes(vid, B, H, n, d, d, dtc, seg_chunks))
+        need = int(lib.hla_backward_workspace_bytes(vid, B, H, n, d, d, dtc, seg_chunks,
+                                                    int(dgamma is not None)))
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.grads = tuple(grads)

@@ -512,17 +512,27 @@ int hla_backward_default_seg_chunks(int B, int H, int n) {
     return (int)g;
 }
 
+// The passes run in fp32 for the ratio forms (their q, k gradient is a small
+// difference of large terms, which bf16 intermediates do not resolve) and
+// whenever the decay gradient is asked for (dL/dg is a sum of position-
+// weighted row terms that nearly cancel: with bf16 Z, dZ and gradients it is
+// off by a few percent, with fp32 passes by about 1e-6 of itself).
+static bool fp32_passes(int variant, bool with_dgamma) {
+    return is_ratio(variant) || with_dgamma;
+}
 // tensors of [B][H][n][d] the backward keeps in its workspace: Z and dZ (Y
 // and dY for AHLA); the ratio form adds dO / den, the rows (e, 0, ..., 0)
-// and the unit rows (1, 0, ..., 0), and with bf16 inputs runs in fp32 on
+// and the unit rows (1, 0, ..., 0); fp32 passes on bf16 inputs run on
 // widened copies of q, k, v, dO and fp32 gradients (seven more)
-static int backward_tensors(int variant, int dtype) {
-    if (!is_ratio(variant)) return 2;
-    const int own = variant == HLA_AHLA_RATIO ? 7 : 5;   // AHLA adds Y1 and dY1
-    return dtype == HLA_BF16 ? own + 7 : own;
+static int own_tensors(int variant) {
+    return variant == HLA_AHLA_RATIO ? 7 : is_ratio(variant) ? 5 : 2;   // AHLA adds Y1, dY1
 }
-static size_t backward_elem_bytes(int variant, int dtype) {
-    return (is_ratio(variant) || dtype == HLA_F32) ? 4 : 2;
+static int backward_tensors(int variant, int dtype, bool with_dgamma) {
+    const int own = own_tensors(variant);
+    return (fp32_passes(variant, with_dgamma) && dtype == HLA_BF16) ? own + 7 : own;
+}
+static size_t backward_elem_bytes(int variant, int dtype, bool with_dgamma) {
+    return (fp32_passes(variant, with_dgamma) || dtype == HLA_F32) ? 4 : 2;
 }
 static bool has_backward(int variant) {
     return variant == HLA_HLA2 || variant == HLA_HLA2_RATIO || variant == HLA_AHLA ||
@@ -535,16 +545,17 @@ static size_t decay_grad_bytes(int variant, int B, int H) {
 }
 
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
-                                    int seg_chunks) {
+                                    int seg_chunks, int with_dgamma) {
     if (!has_backward(variant) || B < 1 ||
         H < 1 || n < 1 || d < 1 || dv < 1 || seg_chunks < 0 ||
         (dtype != HLA_F32 && dtype != HLA_BF16))
         return 0;
+    const bool dg = with_dgamma != 0;
     const int g = seg_chunks > 0 ? seg_chunks : hla_backward_default_seg_chunks(B, H, n);
     const long nseg = num_segments(n, kLaChunk, g);
-    const size_t esz = backward_elem_bytes(variant, dtype);
+    const size_t esz = backward_elem_bytes(variant, dtype, dg);
     const size_t sums = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    return 2 * sums + (size_t)backward_tensors(variant, dtype) * B * H * n * d * esz +
+    return 2 * sums + (size_t)backward_tensors(variant, dtype, dg) * B * H * n * d * esz +
            decay_grad_bytes(variant, B, H);
 }
 
@@ -559,10 +570,9 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
     if (dgamma && is_ahla(variant)) return HLA_ERR_UNSUPPORTED;   // AHLA has no decay
-    // the ratio forms run their passes in fp32 (their gradient with respect
-    // to q and k is a small difference of large terms, which bf16
-    // intermediates do not resolve)
-    const int run_dtype = is_ratio(variant) ? HLA_F32 : dtype;
+    const bool dg = dgamma != nullptr;
+    const bool fp32run = fp32_passes(variant, dg);
+    const int run_dtype = fp32run ? HLA_F32 : dtype;
     BwdCtx c;
     if (!lookup_la(run_dtype, d, &c.la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) {
@@ -583,7 +593,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     const long nseg = num_segments(n, kLaChunk, g);
     if (nseg * B * H > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     if ((long)B * H * n / 4 > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;   // row-wise grid
-    const size_t need = hla_backward_workspace_bytes(variant, B, H, n, d, dv, dtype, g);
+    const size_t need = hla_backward_workspace_bytes(variant, B, H, n, d, dv, dtype, g, dg);
     if (!workspace) return HLA_ERR_NULL;
     if (workspace_bytes < need) return HLA_ERR_WORKSPACE;
 
@@ -591,7 +601,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     // last), the other passes' segment states, then [B*H*n*d] tensors
     c.ws = static_cast<char *>(workspace);
     c.sums_bytes = (size_t)B * H * (size_t)(nseg - 1) * d * d * sizeof(float);
-    c.tensor_bytes = (size_t)B * H * n * d * backward_elem_bytes(variant, dtype);
+    c.tensor_bytes = (size_t)B * H * n * d * backward_elem_bytes(variant, dtype, dg);
     c.sums_kk = reinterpret_cast<float *>(c.ws);
     c.sums = reinterpret_cast<float *>(c.ws + c.sums_bytes);
     c.rows = (long)B * H * n;
@@ -607,19 +617,14 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     for (int h = 0; h < kMaxDecayHeads; ++h) c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h];
 
     Grads io{q, k, v, dout, dq, dk, dv_out};
-    void *partial = c.tensor(backward_tensors(variant, dtype));
-    if (variant == HLA_HLA2) {
-        st = backward_hla2(c, io);
-        if (st != HLA_OK || !dgamma) return st;
-        return decay_gradient(c, io, H, n, d, dgamma, partial);
-    }
-    if (variant == HLA_AHLA) return backward_ahla(c, io);
-    // ratio forms: with bf16 inputs every pass reads and writes fp32 copies
-    // (after the variant's own tensors in the workspace)
+    void *partial = c.tensor(backward_tensors(variant, dtype, dg));
+    // fp32 passes on bf16 inputs read and write fp32 copies (after the
+    // variant's own tensors in the workspace)
     Grads run = io;
-    const int own = backward_tensors(variant, HLA_F32);
+    const int own = own_tensors(variant);
     const long count = c.rows * d;
-    if (dtype == HLA_BF16) {
+    const bool widen = fp32run && dtype == HLA_BF16;
+    if (widen) {
         const void *src[4] = {q, k, v, dout};
         const void **dst_in[4] = {&run.q, &run.k, &run.v, &run.dout};
         for (int i = 0; i < 4; ++i) {
@@ -631,9 +636,14 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         run.dk = c.tensor(own + 5);
         run.dv = c.tensor(own + 6);
     }
-    st = variant == HLA_HLA2_RATIO ? backward_hla2_ratio(c, run) : backward_ahla_ratio(c, run);
+    switch (variant) {
+        case HLA_HLA2: st = backward_hla2(c, run); break;
+        case HLA_AHLA: st = backward_ahla(c, run); break;
+        case HLA_HLA2_RATIO: st = backward_hla2_ratio(c, run); break;
+        default: st = backward_ahla_ratio(c, run); break;
+    }
     if (st == HLA_OK && dgamma) st = decay_gradient(c, run, H, n, d, dgamma, partial);
-    if (st != HLA_OK || dtype != HLA_BF16) return st;
+    if (st != HLA_OK || !widen) return st;
     void *dst[3] = {dq, dk, dv_out};
     const void *src[3] = {run.dq, run.dk, run.dv};
     for (int i = 0; i < 3; ++i)

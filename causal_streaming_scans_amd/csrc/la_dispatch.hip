@@ -45,6 +45,19 @@ hipError_t launch_la_dual_split(const LaParams &p, hipStream_t s, bool summaries
     return launch_la<T, D, false, false>(q, s, true);
 }
 
+// The SYM form as two plain passes, for shapes whose fused LDS layout does
+// not fit: LA(a, b, c) into out (after add), then LA(a, c, b) added to it.
+template <typename T, int D>
+hipError_t launch_la_sym_split(const LaParams &p, hipStream_t s, bool summaries) {
+    hipError_t e = launch_la<T, D, false, false>(p, s, summaries);
+    if (e != hipSuccess) return e;
+    LaParams q = p;
+    q.b = p.c;
+    q.c = p.b;
+    q.add = p.out;
+    return launch_la<T, D, false, false>(q, s, true);
+}
+
 template <typename T, int D>
 hipError_t launch_unit_column(void *out, long rows, hipStream_t s) {
     long blocks = (rows * D + 255) / 256;
@@ -81,9 +94,12 @@ bool la_set(LaLaunches *out) {
     out->unit_column = launch_unit_column<T, D>;
     out->ratio_prep = launch_ratio_prep<T, D>;
     out->decay_grad = launch_decay_grad<T, D>;
-    static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024, "LDS");
+    static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), false, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
-    out->sym = launch_la<T, D, true, false>;
+    if constexpr (sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024)
+        out->sym = launch_la<T, D, true, false>;
+    else
+        out->sym = launch_la_sym_split<T, D>;
     if constexpr (sizeof(LaLds<T, D, la_chunk<T, D>(), false, true>) <= 160 * 1024)
         out->dual = launch_la<T, D, false, true>;
     else
@@ -111,6 +127,7 @@ bool lookup_la(int dtype, int d, LaLaunches *out) {
             case 16: return la_set<float, 16>(out);
             case 32: return la_set<float, 32>(out);
             case 64: return la_set<float, 64>(out);
+            case 128: return la_set<float, 128>(out);
             default: return false;
         }
     }

@@ -261,23 +261,27 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  *                - k_t.dk_t / 2) for any constant c, with Z and dZ as kept
  *                in the workspace; two more launches form it (fp32 row terms
  *                summed in fp64 in a fixed order, so repeat calls agree
- *                bit for bit).  n == 0 writes zeros.  Non-NULL with an
- *                AHLA form: HLA_ERR_UNSUPPORTED.
+ *                bit for bit).  Those terms nearly cancel, so with dgamma
+ *                every pass runs in fp32 (bf16 inputs on widened copies):
+ *                bf16 intermediates would leave dL/dg a few percent off.
+ *                n == 0 writes zeros.  Non-NULL with an AHLA form:
+ *                HLA_ERR_UNSUPPORTED.
  * seg_chunks     chunks (of 64 tokens) per segment; 0 = the library's default
  *                (hla_backward_default_seg_chunks)
  * workspace      device buffer of at least hla_backward_workspace_bytes()
- *                bytes (contents ignored on entry, unspecified on return)
+ *                bytes, with_dgamma = (dgamma != NULL) (contents ignored on
+ *                entry, unspecified on return)
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
- * dZ are kept in dtype; the ratio forms run every pass in fp32 (for bf16
- * inputs on widened copies, d <= 64).  Supported: HLA_HLA2, HLA_HLA2_RATIO,
- * HLA_AHLA, HLA_AHLA_RATIO (AHLA with a decay and HLA_HLA3:
- * HLA_ERR_UNSUPPORTED; the ratio forms need nonzero denominators, as the
- * forward), d == dv, HLA_BF16: d in {16, 32, 64, 128}, HLA_F32:
- * d in {16, 32, 64}.  Errors as hla_forward.
+ * dZ are kept in dtype; the ratio forms, and every form when dgamma is
+ * given, run every pass in fp32 (for bf16 inputs on widened copies).
+ * Supported: HLA_HLA2, HLA_HLA2_RATIO, HLA_AHLA, HLA_AHLA_RATIO (AHLA with a
+ * decay and HLA_HLA3: HLA_ERR_UNSUPPORTED; the ratio forms need nonzero
+ * denominators, as the forward), d == dv in {16, 32, 64, 128}, both dtypes.
+ * Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,
-                                    int seg_chunks);
+                                    int seg_chunks, int with_dgamma);
 hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout,
                         void *dq, void *dk, void *dv_out, int B, int H, int n, int d, int dv,
                         int dtype, int variant, const float *gamma_host, float *dgamma,

@@ -198,14 +198,19 @@ def test_backward_workspace_bytes(lib):
         want_ratio + 2 * B * H * n * d * 4                   # Y1 and its gradient
     assert hla.backward_workspace_bytes("hla3", B, H, n, d, d) == 0
     assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == want
+    # with the decay gradient every pass runs in fp32: the two tensors in fp32
+    # and, for bf16 inputs, the seven widened copies and gradients
+    want_dg = want - 2 * B * H * n * d * 2 + 9 * B * H * n * d * 4
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "bf16", dgamma=True) == want_dg + dg
+    assert hla.backward_workspace_bytes("hla2", B, H, n, d, d, "f32", 32, dgamma=True) == \
+        2 * B * H * n * d * 4 + dg
+    assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d, dgamma=True) == want_ratio + dg
 
 
 def test_backward_validation(lib):
     assert _bwd(lib, n=0) == OK                      # nothing to do, nothing enqueued
     assert _bwd(lib, variant=HLA2_RATIO, ws_bytes=1) == ERR_WS
-    assert _bwd(lib, variant=HLA2_RATIO, d=128, dvd=128) == ERR_UNSUP   # fp32 passes: d <= 64
     assert _bwd(lib, variant=AHLA_RATIO, ws_bytes=1) == ERR_WS
-    assert _bwd(lib, variant=AHLA_RATIO, d=128, dvd=128) == ERR_UNSUP   # fp32 passes: d <= 64
     assert _bwd(lib, variant=4) == ERR_UNSUP                              # third order: forward only
     assert _bwd(lib, variant=AHLA, gamma=[0.9, 0.9]) == ERR_UNSUP   # AHLA has no decay
     assert _bwd(lib, variant=AHLA, dgamma=1) == ERR_UNSUP           # nor a decay gradient
@@ -214,7 +219,7 @@ def test_backward_validation(lib):
     assert _bwd(lib, variant=9) == ERR_ARG
     assert _bwd(lib, dvd=32) == ERR_UNSUP
     assert _bwd(lib, d=48, dvd=48) == ERR_UNSUP
-    assert _bwd(lib, dtype=F32, d=128, dvd=128) == ERR_UNSUP
+    assert _bwd(lib, d=256, dvd=256) == ERR_UNSUP
     assert _bwd(lib, dtype=5) == ERR_ARG
     assert _bwd(lib, B=0) == ERR_SHAPE
     assert _bwd(lib, n=-1) == ERR_SHAPE

@@ -48,6 +48,7 @@ SMALL = [
     ("bf16", 64, 450, 3, True, 2),
     ("bf16", 64, 512, 2, False, 1),
     ("bf16", 128, 300, 2, True, 1),
+    ("f32", 128, 200, 2, True, 1),
 ]
 
 
@@ -208,6 +209,8 @@ RATIO_SMALL = [
     ("bf16", 32, 130, 2, False, 1),
     ("bf16", 64, 450, 3, True, 2),
     ("bf16", 16, 200, 1, False, 1),
+    ("bf16", 128, 300, 2, True, 1),
+    ("f32", 128, 150, 1, False, 0),
 ]
 
 
@@ -248,6 +251,7 @@ AHLA_RATIO_SMALL = [
     ("bf16", 32, 130, 2, 1),
     ("bf16", 64, 450, 3, 2),
     ("bf16", 16, 200, 1, 1),
+    ("bf16", 128, 260, 2, 1),
 ]
 
 

@@ -5,15 +5,13 @@ Orden" ("Resumen Tecnico: Atencion Lineal de Orden Superior (HLA)",
 gist.science/es/paper/2510.27258) trained through "4. Entrenamiento Paralelo
 mediante Escaneos Asociativos".
 
-dL/dg_h is a sum over tokens of position-weighted terms whose unweighted sum
-is zero, so its error is measured against the size of those terms:
-scale_h = (1/g_h) sum_{b,t} |t - c| (2|q.dq| + 3|z.dz| + |k.dk|/2) from fp64
-oracle tensors, and |got - want| must stay under BAR * scale_h.  fp32: the
-fp32 bar, 1e-5.  bf16: every row term is a product of two factors that each
-carry at most one bf16 rounding (the stored dq, dk, Z, dZ; relative 2^-9),
-so no term is off by more than 2^-8 of its size, and BAR = 2^-8.  (Measured
-err/scale: about 1e-8 fp32, 5e-5 bf16; relative to dL/dg itself bf16 is
-0.1-4% off, the conditioning of a sum of large terms that nearly cancel.)"""
+The bar is the stated one, relative to dL/dg_h itself: 1e-5 for fp32 inputs,
+1e-2 for bf16 inputs (the oracle runs on the same bf16-rounded values).
+dL/dg_h is a sum of position-weighted row terms that nearly cancel (their
+unweighted sum is zero), so the library runs every pass in fp32 when the
+decay gradient is asked for; the error is also reported against the size of
+those terms, scale_h = (1/g_h) sum_{b,t} |t - c| (2|q.dq| + 3|z.dz| +
+|k.dk|/2), and must stay under 1e-5 of it for either dtype."""
 import numpy as np
 import pytest
 
@@ -45,6 +43,8 @@ CASES = [
     ("bf16", "hla2", 1, 2, 700, 128, True, 1),
     ("bf16", "hla2", 1, 2, 333, 16, True, 0),
     ("bf16", "hla2_ratio", 1, 2, 400, 64, True, 0),
+    ("bf16", "hla2", 1, 4, 2048, 64, True, 0),
+    ("bf16", "hla2_ratio", 1, 2, 300, 128, True, 1),
 ]
 
 
@@ -61,27 +61,32 @@ def test_dgamma_matches_oracle(case):
     want = BW.hla2_dgamma_batched(x["q"], x["k"], x["v"], do, H, gamma, ratio)
     scale = dgamma_scale(x, do, H, gamma, ratio)
     err = np.abs(got - want)
-    say(f"  got {got} want {want} err/scale {err / scale} rel {err / np.abs(want)}")
-    bar = TOL["f32"] if dtype == "f32" else 2.0 ** -8
-    assert np.all(err <= bar * scale), (case, got, want, scale)
+    rel = err / np.abs(want)
+    say(f"  got {got} want {want} rel {rel} err/scale {err / scale}")
+    assert np.all(rel < TOL[dtype]), (case, got, want)
+    assert np.all(err <= 1e-5 * scale), (case, got, want, scale)
 
 
 def test_dgamma_repeatable_and_no_rows():
     """Two calls agree bit for bit (fixed-order sums); n = 0 gives zeros; the
-    gradients dq, dk, dv are the same with or without dgamma."""
+    gradients dq, dk, dv with dgamma (fp32 passes) match those without it
+    (bf16 passes) to the stated bf16 bar."""
     import torch
     import causal_streaming_scans_amd as hla
+    from hla_testlib import rel_l2
     B, H, n, d = 2, 4, 500, 64
     x = I.make_inputs(B, H, n, d, d, dtype="bf16", dist="l2norm", seed=977, decay=True)
     do = I.make_upstream_grad(B * H, n, d, "bf16", seed=978)
     a = run(x, do, B, H, "bf16", x["gamma"], "hla2")
     b = run(x, do, B, H, "bf16", x["gamma"], "hla2")
     assert torch.equal(a[3], b[3])
+    for g1, g2 in zip(a[:3], b[:3]):
+        assert torch.equal(g1, g2)
     shp = (B, H, n, d)
     plain = hla.hla_backward(*(to_dev(x[s], "bf16", shp) for s in "qkv"), to_dev(do, "bf16", shp),
                              gamma=x["gamma"])
     for g1, g2 in zip(plain, a[:3]):
-        assert torch.equal(g1, g2)
+        assert rel_l2(g1.float().cpu().numpy(), g2.float().cpu().numpy()) < TOL["bf16"]
     z = torch.zeros(B, H, 0, d, dtype=torch.bfloat16, device="cuda")
     dg = torch.full((H,), 7.0, device="cuda")
     hla.hla_backward(z, z, z, z, gamma=x["gamma"], dgamma=dg)
