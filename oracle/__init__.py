@@ -69,7 +69,7 @@ def _load():
     P, L, I = ctypes.c_void_p, ctypes.c_long, ctypes.c_int
     lib.oracle_hla2.argtypes = [P, P, P, P, L, L, L, L, L, P, I, P, P, I]
     lib.oracle_hla2.restype = I
-    lib.oracle_ahla.argtypes = [P, P, P, P, L, L, L, L, I, P, P, I]
+    lib.oracle_ahla.argtypes = [P, P, P, P, L, L, L, L, L, P, I, P, P, I]
     lib.oracle_ahla.restype = I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = I
@@ -120,15 +120,20 @@ def hla2(q, k, v, H=None, gamma=None, ratio=False, state_in=None,
     return (o, so) if want_state else o
 
 
-def ahla(q, k, v, ratio=False, state_in=None, want_state=False, threads=0):
-    """Serial fp64 AHLA; state layout [BH, 2*d*dv + 2*d] = (P, E, m^K, n)."""
+def ahla(q, k, v, ratio=False, state_in=None, want_state=False, threads=0, H=None,
+         gamma=None):
+    """Serial fp64 AHLA; state layout [BH, 2*d*dv + 2*d] = (P, E, m^K, n).
+    gamma: None or length-H decay per head index h = bh % H (every summary
+    decays by gamma per token)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     BH, n, d = q.shape
     dv = v.shape[2]
+    H = H or BH
     o = np.empty((BH, n, dv), dtype=np.float64)
+    g = None if gamma is None else np.ascontiguousarray(np.asarray(gamma, np.float64))
     si = None if state_in is None else np.ascontiguousarray(np.asarray(state_in, np.float64))
     so = np.empty((BH, ahla_state_size(d, dv))) if want_state else None
-    rc = _load().oracle_ahla(_ptr(q), _ptr(k), _ptr(v), _ptr(o), BH, n, d, dv,
+    rc = _load().oracle_ahla(_ptr(q), _ptr(k), _ptr(v), _ptr(o), BH, H, n, d, dv, _ptr(g),
                              int(bool(ratio)), _ptr(si), _ptr(so), int(threads))
     if rc:
         raise RuntimeError(f"oracle_ahla failed ({rc})")

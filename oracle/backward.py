@@ -19,8 +19,9 @@ by g per token):
     F = D_g * A,   N = F L^T,   M = D_g * N,   num = M V
     plain:  o = num
     ratio:  o = num / den,  den = M 1      (row sums)
-AHLA ("2. ... (AHLA)"):
-    M = L L,  num = M V,  den = M 1
+AHLA ("2. ... (AHLA)"; with a decay every summary decays by g per token,
+F = D_g * L):
+    M = F F,  num = M V,  den = M 1
 
 Gradient of the decay g (HLA-2): D_g enters twice, through F and through M.
 With D'[t, i] = (t - i) g^(t-i-1) for i <= t (else 0), the derivative of
@@ -33,7 +34,7 @@ Backward, in the order the chain rule visits the factors:
     dM = dnum V^T (+ dden 1^T)
     HLA-2:  dN = D_g * dM;  dF = dN L;  dL = dN^T F;  dA = D_g * dF + tril(dL)
     AHLA :  dM restricted to the lower triangle (M is lower-triangular);
-            dL = dM L^T + L^T dM;  dA = tril(dL)
+            dF = dM F^T + F^T dM;  dA = D_g * dF
     dQ = dA K,  dK = dA^T Q
 """
 from __future__ import annotations
@@ -108,10 +109,12 @@ def hla2_dgamma_batched(q, k, v, do, H: int, gamma=None, ratio: bool = False):
     return out
 
 
-def ahla_vjp(q, k, v, do, ratio: bool = False):
-    """(dq, dk, dv) of AHLA for one head."""
+def ahla_vjp(q, k, v, do, ratio: bool = False, gamma: float = 1.0):
+    """(dq, dk, dv) of AHLA for one head; with a decay, L below is the decayed
+    lower-triangular factor F = D_g * tril(A) and M = F F."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    L = np.tril(q @ k.T)
+    Dg = decay_mask(q.shape[0], gamma)
+    L = Dg * (q @ k.T)
     M = L @ L
     num = M @ v
     if ratio:
@@ -125,7 +128,7 @@ def ahla_vjp(q, k, v, do, ratio: bool = False):
         dM = np.tril(do @ v.T)
     dv = M.T @ dnum
     dL = dM @ L.T + L.T @ dM
-    dA = np.tril(dL)
+    dA = Dg * dL
     return dA @ k, dA.T @ q, dv
 
 
@@ -138,7 +141,8 @@ def hla2_vjp_batched(q, k, v, do, H: int, gamma=None, ratio: bool = False, heads
     return tuple(np.stack([r[i] for r in res]) for i in range(3))
 
 
-def ahla_vjp_batched(q, k, v, do, ratio: bool = False, heads=None):
+def ahla_vjp_batched(q, k, v, do, ratio: bool = False, heads=None, H: int = 1, gamma=None):
     bhs = range(q.shape[0]) if heads is None else heads
-    res = [ahla_vjp(q[bh], k[bh], v[bh], do[bh], ratio) for bh in bhs]
+    res = [ahla_vjp(q[bh], k[bh], v[bh], do[bh], ratio,
+                    1.0 if gamma is None else float(gamma[bh % H])) for bh in bhs]
     return tuple(np.stack([r[i] for r in res]) for i in range(3))

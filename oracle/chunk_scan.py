@@ -27,11 +27,17 @@ Combine, segment A before segment B (the semidirect product):
 (W = S^K C^QV - G and u = S^K m^Q - h in the page's notation; the cross term
 S_A C_B is the page's S^K_B C^QV_A written for W instead of G.)
 
-AHLA segment summary from zero: P = sum k v^T, M = sum k q^T, mK = sum k,
-E = sum_i k_i y_i^T with y_i = sum_{j<=i in segment} (q_i . k_j) v_j,
-nk = sum_i k_i (q_i . mK_i).  Combine:
-    P = P_A + P_B ; M = M_A + M_B ; mK = mK_A + mK_B
-    E = E_A + E_B + M_B P_A ;  nk = nk_A + nk_B + M_B mK_A
+AHLA segment summary from zero (every summary decays by g per token, as
+for HLA-2; g = 1 is the undecayed operator): P = sum g^(e-j) k_j v_j^T,
+mK = sum g^(e-j) k_j, E = sum_i g^(e-i) k_i y_i^T with
+y_i = sum_{j<=i in segment} g^(i-j) (q_i . k_j) v_j,
+nk = sum_i g^(e-i) k_i (q_i . mK_i), and the undecayed M = sum k q^T.
+Combine, a = g^lB:
+    P = a P_A + P_B ; mK = a mK_A + mK_B ; M = M_A + M_B
+    E = a E_A + E_B + a M_B P_A ;  nk = a nk_A + nk_B + a M_B mK_A
+(the cross term: a token i of B reads A's P decayed by g^(i - e_A), and its
+row of E decays by g^(e - i) to the end, so the product is g^(e - e_A) = a
+for every i: M_B is the plain sum).
 
 Chunked forward inside a segment, carried state (S0, W0, u0), chunk tokens
 tau = 0..c-1:
@@ -40,8 +46,9 @@ tau = 0..c-1:
     O = diag(g^(2(tau+1))) Q W0 + P V ,  den = diag(g^(2(tau+1))) Q u0 + P 1
     S0 <- g^c S0 + K^T diag(g^(c-1-tau)) K
     W0 <- g^(2c) W0 + Z^T diag(g^(2(c-1-tau))) V ,  u0 likewise with 1
-AHLA: Y = Q P0 + tril(QK^T) V ; O = Q E0 + tril(QK^T) Y ; P0 += K^T V ;
-      E0 += K^T Y (and the v == 1 column for mK, nk).
+AHLA (F = D_g * tril(QK^T)): Y = diag(g^(tau+1)) Q P0 + F V ;
+      O = diag(g^(tau+1)) Q E0 + F Y ; P0 <- g^c P0 + K^T diag(g^(c-1-tau)) V ;
+      E0 <- g^c E0 + K^T diag(g^(c-1-tau)) Y (and the v == 1 column for mK, nk).
 """
 from __future__ import annotations
 
@@ -165,56 +172,64 @@ def hla2_scan_forward(q, k, v, chunk, seg_chunks, gamma=1.0, ratio=False,
 
 def ahla_zero(d, dv):
     return dict(P=np.zeros((d, dv)), E=np.zeros((d, dv)), M=np.zeros((d, d)),
-                mK=np.zeros(d), nk=np.zeros(d))
+                mK=np.zeros(d), nk=np.zeros(d), l=0)
 
 
-def ahla_combine(A, B):
-    """A earlier, B later."""
-    return dict(P=A["P"] + B["P"], M=A["M"] + B["M"], mK=A["mK"] + B["mK"],
-                E=A["E"] + B["E"] + B["M"] @ A["P"],
-                nk=A["nk"] + B["nk"] + B["M"] @ A["mK"])
+def ahla_combine(A, B, g=1.0):
+    """A earlier, B later; a = g^(tokens of B)."""
+    a = 1.0 if g == 1.0 else float(g) ** B["l"]
+    return dict(P=a * A["P"] + B["P"], M=A["M"] + B["M"], mK=a * A["mK"] + B["mK"],
+                E=a * A["E"] + B["E"] + a * (B["M"] @ A["P"]),
+                nk=a * A["nk"] + B["nk"] + a * (B["M"] @ A["mK"]),
+                l=A.get("l", 0) + B.get("l", 0))
 
 
-def _ahla_chunk(q, k, v, P0, E0, mK0, nk0):
-    L = np.tril(q @ k.T)
-    Y = q @ P0 + L @ v
-    y1 = q @ mK0 + L.sum(axis=1)
-    num = q @ E0 + L @ Y
-    den = q @ nk0 + L @ y1
-    return (num, den, P0 + k.T @ v, E0 + k.T @ Y, mK0 + k.sum(axis=0),
-            nk0 + k.T @ y1)
+def _ahla_chunk(q, k, v, P0, E0, mK0, nk0, g=1.0):
+    c = q.shape[0]
+    tau = np.arange(c)
+    F = np.tril(q @ k.T) * _pw(g, np.maximum(tau[:, None] - tau[None, :], 0))
+    gt = _pw(g, tau + 1)
+    Y = gt[:, None] * (q @ P0) + F @ v
+    y1 = gt * (q @ mK0) + F.sum(axis=1)
+    num = gt[:, None] * (q @ E0) + F @ Y
+    den = gt * (q @ nk0) + F @ y1
+    kw = _pw(g, c - 1 - tau)[:, None] * k
+    gc = float(g) ** c
+    return (num, den, gc * P0 + kw.T @ v, gc * E0 + kw.T @ Y, gc * mK0 + kw.sum(axis=0),
+            gc * nk0 + kw.T @ y1)
 
 
-def ahla_segment_summary(q, k, v, chunk):
+def ahla_segment_summary(q, k, v, chunk, g=1.0):
     n, d = q.shape
     dv = v.shape[1]
     s = ahla_zero(d, dv)
     P, E, mK, nk = s["P"], s["E"], s["mK"], s["nk"]
     for c0 in range(0, n, chunk):
         qc, kc, vc = q[c0:c0 + chunk], k[c0:c0 + chunk], v[c0:c0 + chunk]
-        _, _, P, E, mK, nk = _ahla_chunk(qc, kc, vc, P, E, mK, nk)
-    return dict(P=P, E=E, M=k.T @ q, mK=mK, nk=nk)
+        _, _, P, E, mK, nk = _ahla_chunk(qc, kc, vc, P, E, mK, nk, g)
+    return dict(P=P, E=E, M=k.T @ q, mK=mK, nk=nk, l=n)
 
 
-def ahla_scan_forward(q, k, v, chunk, seg_chunks, ratio=False, state_in=None):
+def ahla_scan_forward(q, k, v, chunk, seg_chunks, ratio=False, state_in=None, gamma=1.0):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     n, d = q.shape
     dv = v.shape[1]
     seg = chunk * seg_chunks
     bounds = [(s, min(s + seg, n)) for s in range(0, n, seg)] or [(0, 0)]
-    sums = [ahla_segment_summary(q[a:b], k[a:b], v[a:b], chunk) for a, b in bounds]
-    pref = blelloch_exclusive(sums, ahla_combine, lambda: ahla_zero(d, dv))
+    sums = [ahla_segment_summary(q[a:b], k[a:b], v[a:b], chunk, gamma) for a, b in bounds]
+    comb = lambda A, B: ahla_combine(A, B, gamma)
+    pref = blelloch_exclusive(sums, comb, lambda: ahla_zero(d, dv))
     if state_in is not None:
         P_in, E_in, mK_in, nk_in = state_in
-        init = dict(P=P_in, E=E_in, M=np.zeros((d, d)), mK=mK_in, nk=nk_in)
-        pref = [ahla_combine(init, p) for p in pref]
+        init = dict(P=P_in, E=E_in, M=np.zeros((d, d)), mK=mK_in, nk=nk_in, l=0)
+        pref = [comb(init, p) for p in pref]
     o = np.zeros((n, dv))
     st = None
     for (a, b), p in zip(bounds, pref):
         st = (p["P"], p["E"], p["mK"], p["nk"])
         for c0 in range(a, b, chunk):
             c1 = min(c0 + chunk, b)
-            num, den, *st = _ahla_chunk(q[c0:c1], k[c0:c1], v[c0:c1], *st)
+            num, den, *st = _ahla_chunk(q[c0:c1], k[c0:c1], v[c0:c1], *st, g=gamma)
             o[c0:c1] = num / den[:, None] if ratio else num
     if st is None:
         st = (np.zeros((d, dv)), np.zeros((d, dv)), np.zeros(d), np.zeros(d))

@@ -19,8 +19,12 @@ D_g[t, i] = g^(t - i) if i <= t else 0.
     HLA-2          o_t = sum_{j<=t} sum_{i<=j} g^((t-i)+(t-j)) A[t,i] A[j,i] v_j
                    i.e.  o = (D_g * ((D_g * A) L^T)) V
     ratio HLA-2    the same with v == 1 as denominator
-    AHLA           o_t = sum_{i<=t} sum_{j<=i} A[t,i] A[i,j] v_j ,  o = (L L) V
+    AHLA           o_t = sum_{i<=t} sum_{j<=i} g^(t-j) A[t,i] A[i,j] v_j
+                   i.e.  o = ((D_g * L)(D_g * L)) V = (D_g * (L L)) V
     ratio AHLA     the same with v == 1 as denominator
+
+Decay (both families) is the reading in which every streaming summary decays
+by g per token; g = 1 is the undecayed operator.
 
 Two forms are given: explicit loops (``*_loops``, tiny inputs only) and the
 equivalent matrix expressions (``hla2_matrix``, ``ahla_matrix``).
@@ -51,7 +55,7 @@ def hla2_loops(q, k, v, gamma: float = 1.0, ratio: bool = False):
     return o
 
 
-def ahla_loops(q, k, v, ratio: bool = False):
+def ahla_loops(q, k, v, ratio: bool = False, gamma: float = 1.0):
     """Direct double sum for one head; q, k: [n, d], v: [n, dv]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     n, dv = v.shape
@@ -61,7 +65,7 @@ def ahla_loops(q, k, v, ratio: bool = False):
         den = 0.0
         for i in range(t + 1):
             for j in range(i + 1):
-                w = float(q[t] @ k[i]) * float(q[i] @ k[j])
+                w = gamma ** (t - j) * float(q[t] @ k[i]) * float(q[i] @ k[j])
                 num += w * v[j]
                 den += w
         o[t] = num / den if ratio else num
@@ -89,11 +93,11 @@ def hla2_matrix(q, k, v, gamma: float = 1.0, ratio: bool = False):
     return num
 
 
-def ahla_matrix(q, k, v, ratio: bool = False):
+def ahla_matrix(q, k, v, ratio: bool = False, gamma: float = 1.0):
     """Matrix form for one head (materialises n x n)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
-    L = np.tril(q @ k.T)
-    M = L @ L
+    F = decay_mask(q.shape[0], gamma) * (q @ k.T)     # D_g * L (the mask zeroes i > t)
+    M = F @ F
     num = M @ v
     if ratio:
         return num / M.sum(axis=1, keepdims=True)
@@ -110,9 +114,11 @@ def hla2_batched(q, k, v, H: int, gamma=None, ratio: bool = False):
     return out
 
 
-def ahla_batched(q, k, v, ratio: bool = False):
+def ahla_batched(q, k, v, ratio: bool = False, H: int = 1, gamma=None):
+    """Matrix form over [BH, n, d] inputs; gamma is None or a length-H array."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     out = np.empty(v.shape)
     for bh in range(q.shape[0]):
-        out[bh] = ahla_matrix(q[bh], k[bh], v[bh], ratio)
+        g = 1.0 if gamma is None else float(gamma[bh % H])
+        out[bh] = ahla_matrix(q[bh], k[bh], v[bh], ratio, g)
     return out

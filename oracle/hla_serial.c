@@ -31,6 +31,9 @@
  * key-after-value part of the decayed product, so the output formula is
  * unchanged and the pair (i, j) of a term in o_t carries weight
  * gamma^((t-i)+(t-j)).  gamma = 1 is the undecayed operator.
+ * AHLA under the same reading: every summary decays by gamma per token
+ * (P <- g P + k v^T, E <- g E + k y^T, m^K <- g m^K + k, n <- g n + ...), so
+ * the term A[t,i] A[i,j] v_j of o_t carries weight gamma^(t-j).
  *
  * All arithmetic is fp64.  Inputs are fp32 arrays (bf16-rounded inputs are
  * exactly representable in fp32); every value is upcast before use.
@@ -135,7 +138,7 @@ static void hla2_head(const float *q, const float *k, const float *v, double *o,
 
 /* one (b,h) sequence of AHLA in the page's summary form */
 static void ahla_head(const float *q, const float *k, const float *v, double *o,
-                      long n, long d, long dv, int ratio,
+                      long n, long d, long dv, double g, int ratio,
                       const double *st_in, double *st_out, double *work)
 {
     double *P = work;            /* d x dv  P^KV = sum k v^T              */
@@ -151,17 +154,17 @@ static void ahla_head(const float *q, const float *k, const float *v, double *o,
         for (a = 0; a < d; ++a) { kt[a] = k[t * d + a]; qt[a] = q[t * d + a]; }
         for (j = 0; j < dv; ++j) vt[j] = v[t * dv + j];
         for (a = 0; a < d; ++a)
-            for (j = 0; j < dv; ++j) P[a * dv + j] += kt[a] * vt[j];
+            for (j = 0; j < dv; ++j) P[a * dv + j] = g * P[a * dv + j] + kt[a] * vt[j];
         /* y_t = P_t^T q_t : first-order read-out routed through key index */
         for (j = 0; j < dv; ++j) y[j] = 0.0;
         for (a = 0; a < d; ++a)
             for (j = 0; j < dv; ++j) y[j] += qt[a] * P[a * dv + j];
         for (a = 0; a < d; ++a)
-            for (j = 0; j < dv; ++j) E[a * dv + j] += kt[a] * y[j];
+            for (j = 0; j < dv; ++j) E[a * dv + j] = g * E[a * dv + j] + kt[a] * y[j];
         double s = 0.0;
-        for (a = 0; a < d; ++a) { mK[a] += kt[a]; }
+        for (a = 0; a < d; ++a) { mK[a] = g * mK[a] + kt[a]; }
         for (a = 0; a < d; ++a) s += qt[a] * mK[a];
-        for (a = 0; a < d; ++a) nk[a] += kt[a] * s;
+        for (a = 0; a < d; ++a) nk[a] = g * nk[a] + kt[a] * s;
         for (j = 0; j < dv; ++j) {
             double acc = 0.0;
             for (a = 0; a < d; ++a) acc += qt[a] * E[a * dv + j];
@@ -211,10 +214,11 @@ int oracle_hla2(const float *q, const float *k, const float *v, double *o,
 }
 
 int oracle_ahla(const float *q, const float *k, const float *v, double *o,
-                long BH, long n, long d, long dv, int ratio,
+                long BH, long H, long n, long d, long dv,
+                const double *gamma, int ratio,
                 const double *state_in, double *state_out, int threads)
 {
-    if (bad_dims(BH, n, d, dv) || (n > 0 && (!q || !k || !v || !o))) return 1;
+    if (bad_dims(BH, n, d, dv) || H < 1 || (n > 0 && (!q || !k || !v || !o))) return 1;
     const long st = 2 * d * dv + 2 * d;
     const long wsz = 2 * d * dv + 2 * d + 2 * d + 2 * dv;
     int rc = 0;
@@ -226,8 +230,9 @@ int oracle_ahla(const float *q, const float *k, const float *v, double *o,
     for (bh = 0; bh < BH; ++bh) {
         double *work = (double *)malloc(sizeof(double) * (size_t)wsz);
         if (!work) { rc |= 2; continue; }
+        const double g = gamma ? gamma[bh % H] : 1.0;
         ahla_head(q + bh * n * d, k + bh * n * d, v + bh * n * dv, o + bh * n * dv,
-                  n, d, dv, ratio,
+                  n, d, dv, g, ratio,
                   state_in ? state_in + bh * st : NULL,
                   state_out ? state_out + bh * st : NULL, work);
         free(work);
