@@ -7,14 +7,18 @@
 // streaming summaries P^KV, m^K, E and n.
 //
 // Chunk form (derived from those summaries): y_t = P_t^T q_t is causal linear
-// attention, and o_t = q_t^T E_t with E_t = E_{t-1} + k_t y_t^T.  For a chunk
-// with carried (P0, E0, mK0, nk0) and L = tril(Q K^T):
-//     Y  = Q P0 + L V              y1 = Q mK0 + L 1      (v == 1 column)
-//     O  = Q E0 + L Y              den = Q nk0 + L y1    (ratio form)
-//     P0 += K^T V ; E0 += K^T Y ; mK0 += K^T 1 ; nk0 += K^T y1
+// attention, and o_t = q_t^T E_t with E_t = g E_{t-1} + k_t y_t^T.  With a
+// decay g every summary decays by g per token ("Contribuciones Clave", item
+// 2: masked operators with exponential decay; g = 1 without), so the term
+// A[t,i] A[i,j] v_j of o_t carries g^(t-j).  For a chunk with carried
+// (P0, E0, mK0, nk0), in-chunk positions tau and L = D_g * tril(Q K^T):
+//     Y  = diag(g^(tau+1)) Q P0 + L V       y1 = diag(g^(tau+1)) Q mK0 + L 1
+//     O  = diag(g^(tau+1)) Q E0 + L Y       den = diag(g^(tau+1)) Q nk0 + L y1
+//     P0 <- g^c P0 + K^T diag(g^(c-1-tau)) V ; E0 likewise with Y;
+//     mK0, nk0 likewise with the v == 1 column and y1
 // The summary kernel runs this from zero over one segment and also forms
-// M = sum_t k_t q_t^T, the factor the segment combine's cross term M_B P_A
-// needs.
+// M = sum_t k_t q_t^T (undecayed), the factor of the segment combine's cross
+// term a M_B P_A (a = g^(tokens of B)).
 //
 // Work split and LDS layout as for HLA-2: wave (r, cg) owns row tile r and
 // column tiles cg, cg + NCG, ...; chunk tiles sit in LDS row-major and every
@@ -37,6 +41,7 @@ namespace hla {
 
 template <typename T, int D, int DV, int C>
 struct AhlaCfg {
+    static constexpr int NPOW = C + 2;        // g^e, e = 0 .. C+1
     using WS = WaveShape<C, D>;
     static constexpr int RT = WS::RT, NCG = WS::NCG, NW = WS::NW, NT = WS::NT;
     static constexpr int DVX = DV + 16;       // P, E widened by the mK / nk column tile
@@ -54,50 +59,55 @@ struct AhlaCfg {
     static_assert(D % 16 == 0 && DV % 16 == 0 && C % 16 == 0, "tile multiples");
 };
 
-template <typename T, int D, int DV, int C>
+template <typename T, int D, int DV, int C, bool DECAY>
 struct AhlaFwdSmem {
     using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T K[C * G::TK::LD];
+    alignas(16) T Kw[DECAY ? C * G::TK::LD : 8];   // rows weighted by g^(c-1-tau)
     alignas(16) T V[C * G::TV::LD];
     alignas(16) T Y[C * G::TV::LD];
     alignas(16) T Y1[C * G::TY1::LD];      // column 0 = y1
     alignas(16) T Pt[G::DVX * G::TK::LD];  // Pt[j][i] = P0[i][j]; row DV = mK0
     alignas(16) T Et[G::DVX * G::TK::LD];  // Et[j][i] = E0[i][j]; row DV = nk0
+    float gp[DECAY ? G::NPOW : 1];
 };
 
-template <typename T, int D, int DV, int C>
-using AhlaFwdLds = LdsWithScratch<AhlaFwdSmem<T, D, DV, C>, CrossLds<D, DV>::FLOATS>;
+template <typename T, int D, int DV, int C, bool DECAY>
+using AhlaFwdLds = LdsWithScratch<AhlaFwdSmem<T, D, DV, C, DECAY>, CrossLds<D, DV>::FLOATS>;
 
-template <typename T, int D, int DV, int C>
+template <typename T, int D, int DV, int C, bool DECAY>
 struct AhlaSumSmem {
     using G = AhlaCfg<T, D, DV, C>;
     alignas(16) T Q[C * G::TK::LD];
     alignas(16) T K[C * G::TK::LD];
+    alignas(16) T Kw[DECAY ? C * G::TK::LD : 8];
     alignas(16) T V[C * G::TV::LD];
     alignas(16) T Y[C * G::TV::LD];
     alignas(16) T Y1[C * G::TY1::LD];
     alignas(16) T Pt[G::DVX * G::TK::LD];
+    float gp[DECAY ? G::NPOW : 1];
 };
 
 // Built for at most two workgroups per CU: the register budget of a third
 // (168 VGPRs) makes both kernels spill at chunk 64.
-template <typename T, int D, int DV, int C>
+template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int ahla_fwd_blocks() {
-    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdLds<T, D, DV, C>)>();
+    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaFwdLds<T, D, DV, C, DECAY>)>();
     return b > 2 ? 2 : b;
 }
-template <typename T, int D, int DV, int C>
+template <typename T, int D, int DV, int C, bool DECAY>
 constexpr int ahla_sum_blocks() {
-    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C>)>();
+    const int b = hla_min_blocks<AhlaCfg<T, D, DV, C>::NT, (int)sizeof(AhlaSumSmem<T, D, DV, C, DECAY>)>();
     return C >= 64 && b > 2 ? 2 : b;
 }
 
-// Y^T tiles of row tile R: Y = Q P0 + L V, and the y1 tile (Q mK0 + L 1, in
-// Y1) when `wide`; stored row-major after every product.
-template <typename T, int D, int DV, int R, int NCG, int YJ, typename G>
+// Y^T tiles of row tile R: Y = diag(g^(tau+1)) Q P0 + L V, and the y1 tile
+// (the same with mK0 and the v == 1 column, in Y1) when `wide`; stored
+// row-major after every product.
+template <typename T, int D, int DV, int R, int NCG, int YJ, typename G, bool DECAY>
 __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Frag16<T> (&Lf)[R + 1],
                                              const T *Pt, const T *V, T *Y, T *Y1, int cg, int tau,
-                                             bool wide) {
+                                             bool wide, const float *gp) {
     using TK = typename G::TK;
     using TV = typename G::TV;
     constexpr int nTV = DV / 16;
@@ -108,7 +118,8 @@ __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Fra
         const int jv = cg + jj * NCG;
         y[jj] = zero4();
         if (jv < nTV || (wide && jv == nTV)) {
-            const f32x4 yq = mma_nt_ft<TK>(zero4(), Pt + 16 * jv * TK::LD, qf);
+            f32x4 yq = mma_nt_ft<TK>(zero4(), Pt + 16 * jv * TK::LD, qf);
+            if (DECAY) yq *= gp[tau + 1];
             f32x4 yc = zero4();
 #pragma unroll
             for (int s = 0; s <= R; ++s)
@@ -124,8 +135,8 @@ __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Fra
     }
 }
 
-template <typename T, int D, int DV, int C>
-__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_fwd_blocks<T, D, DV, C>()))
+template <typename T, int D, int DV, int C, bool DECAY>
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_fwd_blocks<T, D, DV, C, DECAY>()))
 void ahla_forward_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
@@ -133,7 +144,7 @@ void ahla_forward_kernel(FwdParams p) {
     using TK = typename G::TK;
     using TV = typename G::TV;
     using TY1 = typename G::TY1;
-    __shared__ AhlaFwdLds<T, D, DV, C> lds;
+    __shared__ AhlaFwdLds<T, D, DV, C, DECAY> lds;
     auto &sm = lds.s;
 
     int seg, bh;
@@ -141,6 +152,7 @@ void ahla_forward_kernel(FwdParams p) {
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    const float g = DECAY ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const int t_begin = seg * p.seg_len;
     const int t_end = min(p.n, t_begin + p.seg_len);
     const bool ratio = p.ratio != 0;
@@ -193,15 +205,17 @@ void ahla_forward_kernel(FwdParams p) {
         }
     });
     if (seg > 0) {
-        // fold node B (later) into the running state A: E <- E + E_B + M_B P,
-        // nk <- nk + nk_B + M_B mK, P <- P + P_B, mK <- mK + mK_B; the node's
-        // M and the old widened [P | mK] are staged in LDS (fp32)
+        // fold node B (later) into the running state A, a = g^(tokens of B):
+        // E <- a E + E_B + a M_B P, nk <- a nk + nk_B + a M_B mK,
+        // P <- a P + P_B, mK <- a mK + mK_B; the node's M and the old widened
+        // [P | mK] are staged in LDS (fp32)
         using L = CrossLds<D, DV>;  // fold: whole right factor
         float *Ms = lds.f, *Ps = lds.f + D * L::LDA;
         int done = 0;
         for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
             if (!((seg >> b) & 1)) continue;
             const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
+            const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
             // with no caller state the first node folds into zero: no cross terms
             const bool cross = p.state_in != nullptr || done > 0;
             // The node's linear parts: with d <= 64 they are loaded into
@@ -245,24 +259,24 @@ void ahla_forward_kernel(FwdParams p) {
             for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    accE[pb][x][y][i] += PRE ? ne[pb][x][y][PRE ? i : 0] : ev(O::N, ti, tv, i);
-                    accP[pb][x][y][i] += PRE ? np[pb][x][y][PRE ? i : 0] : ev(O::Y, ti, tv, i);
+                    accE[pb][x][y][i] = a * accE[pb][x][y][i] + (PRE ? ne[pb][x][y][PRE ? i : 0] : ev(O::N, ti, tv, i));
+                    accP[pb][x][y][i] = a * accP[pb][x][y][i] + (PRE ? np[pb][x][y][PRE ? i : 0] : ev(O::Y, ti, tv, i));
                 }
             });
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    accNK[j][i] += PRE ? nn[j][PRE ? i : 0] : vv(O::nv, ti, i);
-                    accMK[j][i] += PRE ? nm[j][PRE ? i : 0] : vv(O::y, ti, i);
+                    accNK[j][i] = a * accNK[j][i] + (PRE ? nn[j][PRE ? i : 0] : vv(O::nv, ti, i));
+                    accMK[j][i] = a * accMK[j][i] + (PRE ? nm[j][PRE ? i : 0] : vv(O::y, ti, i));
                 }
             });
             if (cross) {
                 __syncthreads();
                 for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
-                    accE[pb][x][y] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + 16 * tv, L::LDB);
+                    accE[pb][x][y] += a * tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + 16 * tv, L::LDB);
                 });
                 for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                    accNK[j] += tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + DV, L::LDB);
+                    accNK[j] += a * tile_ab_f32<D>(Ms + 16 * ti * L::LDA, L::LDA, Ps + DV, L::LDB);
                 });
                 __syncthreads();
             }
@@ -277,6 +291,7 @@ void ahla_forward_kernel(FwdParams p) {
         store4(sm.Pt + TK::off(DV + col, 16 * ti + g4), accMK[j]);
         store4(sm.Et + TK::off(DV + col, 16 * ti + g4), accNK[j]);
     });
+    if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
 
     int c0 = t_begin;
     int cv = min(C, t_end - c0);
@@ -285,6 +300,7 @@ void ahla_forward_kernel(FwdParams p) {
     while (c0 < t_end) {
         __syncthreads();
         rk.template store_tile<TK>(sm.K);
+        if (DECAY) rk.template store_tile_w<TK>(sm.Kw, sm.gp, cv - 1);
         rv.template store_tile<TV>(sm.V);
         RowFrags<T, D> qf = qn;
         qf.mask_rows(cv - 16 * r);
@@ -297,18 +313,25 @@ void ahla_forward_kernel(FwdParams p) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, TK, false>(Lf, sm.K, qf, tau, nullptr, 1);
-            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau, need_u);
+            scores_t<T, D, R, TK, DECAY>(Lf, sm.K, qf, tau, DECAY ? sm.gp : nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G, DECAY>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau,
+                                                            need_u, DECAY ? sm.gp : nullptr);
             // carried part of the output and of its denominator (row DV)
             f32x4 accO[G::OJ];
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
                 const int jv = cg + jj * NCG;
                 accO[jj] = zero4();
-                if (jv < nTV) accO[jj] = mma_nt_ft<TK>(zero4(), sm.Et + 16 * jv * TK::LD, qf);
+                if (jv < nTV) {
+                    accO[jj] = mma_nt_ft<TK>(zero4(), sm.Et + 16 * jv * TK::LD, qf);
+                    if (DECAY) accO[jj] *= sm.gp[tau + 1];
+                }
             }
             f32x4 accD = zero4();
-            if (ratio) accD = mma_nt_ft<TK>(zero4(), sm.Et + DV * TK::LD, qf);
+            if (ratio) {
+                accD = mma_nt_ft<TK>(zero4(), sm.Et + DV * TK::LD, qf);
+                if (DECAY) accD *= sm.gp[tau + 1];
+            }
             __syncthreads();
 
             // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
@@ -333,16 +356,30 @@ void ahla_forward_kernel(FwdParams p) {
                 }
             }
         });
-        // advance the state: P0 += K^T V, E0 += K^T Y, mK0 += K^T 1, nk0 += K^T y1
-        // all products first, then the T-typed copies
+        // advance the state: P0 <- g^c P0 + Kw^T V, E0 likewise with Y, mK0
+        // with the ones column, nk0 with y1 (Kw: K rows weighted by
+        // g^(c-1-tau)); all products first, then the T-typed copies
+        const T *KA = DECAY ? sm.Kw : sm.K;
+        const float gc = DECAY ? sm.gp[cv] : 1.f;
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], sm.K, 16 * ti0, sm.V, 16 * tv0);
-            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], sm.K, 16 * ti0, sm.Y, 16 * tv0);
+            if (DECAY) {
+#pragma unroll
+                for (int x = 0; x < PBk::BR * PBk::BR; ++x) {
+                    (&accP[pb][0][0])[x] *= gc;
+                    (&accE[pb][0][0])[x] *= gc;
+                }
+            }
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], KA, 16 * ti0, sm.V, 16 * tv0);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], KA, 16 * ti0, sm.Y, 16 * tv0);
         });
         if (need_u) {
             for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-                mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], sm.K, 16 * ti, sm.V, 0);
-                mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], sm.K, 16 * ti, sm.Y1, 0);
+                if (DECAY) {
+                    accMK[j] *= gc;
+                    accNK[j] *= gc;
+                }
+                mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], KA, 16 * ti, sm.V, 0);
+                mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], KA, 16 * ti, sm.Y1, 0);
             });
         }
         for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {
@@ -382,8 +419,8 @@ void ahla_forward_kernel(FwdParams p) {
     }
 }
 
-template <typename T, int D, int DV, int C>
-__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_sum_blocks<T, D, DV, C>()))
+template <typename T, int D, int DV, int C, bool DECAY>
+__global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_sum_blocks<T, D, DV, C, DECAY>()))
 void ahla_summary_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
     constexpr int NT = G::NT, NW = G::NW, NCG = G::NCG, RT = G::RT;
@@ -391,9 +428,10 @@ void ahla_summary_kernel(FwdParams p) {
     using TK = typename G::TK;
     using TV = typename G::TV;
     using TY1 = typename G::TY1;
-    __shared__ AhlaSumSmem<T, D, DV, C> sm;
+    __shared__ AhlaSumSmem<T, D, DV, C, DECAY> sm;
 
     const int seg = blockIdx.x, bh = blockIdx.y;
+    const float g = DECAY ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const int w = wave_id();
     const int r = w / NCG, cg = w % NCG;
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
@@ -428,6 +466,7 @@ void ahla_summary_kernel(FwdParams p) {
         accNK[j] = zero4();
     }
     for (int i = threadIdx.x; i < G::DVX * TK::LD; i += NT) sm.Pt[i] = from_f<T>(0.f);
+    if (DECAY) fill_pow_table<NT>(sm.gp, G::NPOW, g);
 
     ChunkRegs<T, C, D, NT> rq, rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -441,6 +480,7 @@ void ahla_summary_kernel(FwdParams p) {
         __syncthreads();
         rq.template store_tile<TK>(sm.Q);
         rk.template store_tile<TK>(sm.K);
+        if (DECAY) rk.template store_tile_w<TK>(sm.Kw, sm.gp, cv - 1);
         rv.template store_tile<TV>(sm.V);
         const int n0 = c0 + C;
         const int ncv = min(C, t_end - n0);
@@ -457,21 +497,37 @@ void ahla_summary_kernel(FwdParams p) {
             constexpr int R = decltype(rt)::value;
             const int tau = 16 * R + col;
             Frag16<T> Lf[R + 1];
-            scores_t<T, D, R, TK, false>(Lf, sm.K, qf, tau, nullptr, 1);
-            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau, true);
+            scores_t<T, D, R, TK, DECAY>(Lf, sm.K, qf, tau, DECAY ? sm.gp : nullptr, 1);
+            ahla_y_tiles<T, D, DV, R, NCG, G::YJ, G, DECAY>(qf, Lf, sm.Pt, sm.V, sm.Y, sm.Y1, cg, tau,
+                                                            true, DECAY ? sm.gp : nullptr);
         });
         __syncthreads();
 
+        // P <- g^c P + Kw^T V, E likewise with Y, mK, nk with the ones column
+        // and y1; M += K^T Q undecayed
+        const T *KA = DECAY ? sm.Kw : sm.K;
+        const float gc = DECAY ? sm.gp[cv] : 1.f;
         for_blocks<PBk, NW>(w, [&](int pb, int ti0, int tv0) {
-            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], sm.K, 16 * ti0, sm.V, 16 * tv0);
-            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], sm.K, 16 * ti0, sm.Y, 16 * tv0);
+            if (DECAY) {
+#pragma unroll
+                for (int x = 0; x < PBk::BR * PBk::BR; ++x) {
+                    (&accP[pb][0][0])[x] *= gc;
+                    (&accE[pb][0][0])[x] *= gc;
+                }
+            }
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accP[pb][0][0], KA, 16 * ti0, sm.V, 16 * tv0);
+            mma_tn_grp<PBk::BR, PBk::BR, C, TK, TV, false>(&accE[pb][0][0], KA, 16 * ti0, sm.Y, 16 * tv0);
         });
         for_blocks<MBk, NW>(w, [&](int pb, int ti0, int tj0) {
             mma_tn_grp<MBk::BR, MBk::BR, C, TK, TK, false>(&accM[pb][0][0], sm.K, 16 * ti0, sm.Q, 16 * tj0);
         });
         for_stripe<G::UJ, NW, nTD>(w, [&](int j, int ti) {
-            mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], sm.K, 16 * ti, sm.V, 0);
-            mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], sm.K, 16 * ti, sm.Y1, 0);
+            if (DECAY) {
+                accMK[j] *= gc;
+                accNK[j] *= gc;
+            }
+            mma_tn_grp<1, 1, C, TK, TV, true>(&accMK[j], KA, 16 * ti, sm.V, 0);
+            mma_tn_grp<1, 1, C, TK, TY1, false>(&accNK[j], KA, 16 * ti, sm.Y1, 0);
         });
         // the running widened P's T-typed copy after every product of the chunk
         for_owned<PBk, NW>(w, [&](int pb, int x, int y, int ti, int tv) {

@@ -9,11 +9,11 @@
 // the segment summaries reproduces the serial recurrence exactly.
 //
 // Summary = (X, Y, N, y, nv) (layout in params.h).  Combine, A earlier than B,
-// a = g^(tokens in B) (1 for AHLA):
+// a = g^(tokens in B) (1 without a decay):
 //   HLA-2: X = a X_A + X_B, Y = a Y_A + Y_B, y = a y_A + y_B,
 //          N = a^2 N_A + N_B + a X_A Y_B,  nv = a^2 nv_A + nv_B + a X_A y_B
-//   AHLA : X = X_A + X_B, Y = Y_A + Y_B, y = y_A + y_B,
-//          N = N_A + N_B + X_B Y_A,        nv = nv_A + nv_B + X_B y_A
+//   AHLA : X = X_A + X_B (undecayed M), Y = a Y_A + Y_B, y = a y_A + y_B,
+//          N = a N_A + N_B + a X_B Y_A,    nv = a nv_A + nv_B + a X_B y_A
 //
 // The scan's up-sweep runs over the stored summaries level by level, one
 // launch per level and a few workgroups per combine (column slices): node
@@ -132,7 +132,8 @@ __device__ void combine_slice(const float *eA, const float *eB, float *eD, float
     const float *Xc = HLA2 ? eA + O::X : eB + O::X;
     const float *Yc = HLA2 ? eB + O::Y : eA + O::Y;
     const float *yc = HLA2 ? eB + O::y : eA + O::y;
-    const float lin = HLA2 ? a : 1.f, quad = HLA2 ? a * a : 1.f;
+    // scales of X, of Y and y, of N and nv, and of the cross term
+    const float xs = HLA2 ? a : 1.f, ys = a, quad = HLA2 ? a * a : a, lin = a;
     float *As = lds, *Bs = lds + D * L::LDA;
     // which of this wave's tiles exist: the nv column only in slice 0
     auto tile_ok = [&](int t) { return t < nTD * nTW || (first && t < NTILE); };
@@ -203,17 +204,17 @@ __device__ void combine_slice(const float *eA, const float *eB, float *eD, float
 #pragma unroll
     for (int u = 0; u < UX; ++u) {
         const int v = threadIdx.x + u * NT;
-        if (v < NX4) *reinterpret_cast<f32x4 *>(eD + O::X + r0 * D + 4 * v) = lin * xa[u] + xb[u];
+        if (v < NX4) *reinterpret_cast<f32x4 *>(eD + O::X + r0 * D + 4 * v) = xs * xa[u] + xb[u];
     }
 #pragma unroll
     for (int u = 0; u < UY; ++u) {
         const int v = threadIdx.x + u * NT;
         if (v < NY4) {
             const int off = O::Y + (v / (CW / 4)) * DV + c0 + 4 * (v % (CW / 4));
-            *reinterpret_cast<f32x4 *>(eD + off) = lin * ya[u] + yb[u];
+            *reinterpret_cast<f32x4 *>(eD + off) = ys * ya[u] + yb[u];
         }
     }
-    if (first && threadIdx.x < D) eD[O::y + threadIdx.x] = lin * vya + vyb;
+    if (first && threadIdx.x < D) eD[O::y + threadIdx.x] = ys * vya + vyb;
 }
 
 // Workgroups of one up-sweep level: the CS column slices of a combine are
@@ -243,8 +244,9 @@ __global__ __launch_bounds__(NT) void up_sweep_kernel(FwdParams p, int b) {
     up_sweep_slot<CS>(blockIdx.x, &comb, &cs);
     if (comb >= npair * p.BH) return;
     const int bh = comb / npair, m = comb - bh * npair;
-    const float g = HLA2 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
-    const float a = HLA2 ? pow_int(g, (long)p.seg_len << b) : 1.f;   // g^(tokens of a child)
+    // every entry is 1 without a decay, so a is exactly 1 then
+    const float g = p.gamma[gamma_slot(bh, p.H)];
+    const float a = pow_int(g, (long)p.seg_len << b);   // g^(tokens of a child)
     combine_slice<HLA2, D, DV, NT, CS>(p.ws + node_offset(bh, b, 2 * m, p.BH, p.nreal, SUMF),
                                        p.ws + node_offset(bh, b, 2 * m + 1, p.BH, p.nreal, SUMF),
                                        p.ws + node_offset(bh, b + 1, m, p.BH, p.nreal, SUMF), a, cs,

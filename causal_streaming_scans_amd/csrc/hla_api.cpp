@@ -47,7 +47,7 @@ hla_status check_common(int B, int H, int d, int dv, int dtype, int variant, con
     if (B < 1 || H < 1 || d < 1 || dv < 1) return HLA_ERR_SHAPE;
     if ((long)B * H > 65535) return HLA_ERR_UNSUPPORTED;
     if (gamma) {
-        if (is_ahla(variant) || is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
+        if (is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
         if (H > HLA_MAX_DECAY_HEADS) return HLA_ERR_UNSUPPORTED;
         for (int h = 0; h < H; ++h)
             if (!(gamma[h] > 0.f && gamma[h] <= 1.f)) return HLA_ERR_ARG;  // also rejects NaN
@@ -569,7 +569,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (n < 0) return HLA_ERR_SHAPE;
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
-    if (dgamma && is_ahla(variant)) return HLA_ERR_UNSUPPORTED;   // AHLA has no decay
+    // the decay gradient's identity is written for the HLA-2 chain
+    if (dgamma && is_ahla(variant)) return HLA_ERR_UNSUPPORTED;
     const bool dg = dgamma != nullptr;
     const bool fp32run = fp32_passes(variant, dg);
     const int run_dtype = fp32run ? HLA_F32 : dtype;

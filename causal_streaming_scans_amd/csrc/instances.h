@@ -16,10 +16,10 @@ constexpr bool hla2_fits() {
            sizeof(Hla2SumSmem<T, D, D, C, DECAY>) <= kLdsBytes;
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool DECAY>
 constexpr bool ahla_fits() {
-    return sizeof(AhlaFwdLds<T, D, D, C>) <= kLdsBytes &&
-           sizeof(AhlaSumSmem<T, D, D, C>) <= kLdsBytes;
+    return sizeof(AhlaFwdLds<T, D, D, C, DECAY>) <= kLdsBytes &&
+           sizeof(AhlaSumSmem<T, D, D, C, DECAY>) <= kLdsBytes;
 }
 
 template <typename T, int D, int C, bool DECAY>
@@ -36,16 +36,16 @@ hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool DECAY>
 hipError_t launch_ahla_summary(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((ahla_summary_kernel<T, D, D, C>), dim3(p.nseg - 1, p.BH),
+    hipLaunchKernelGGL((ahla_summary_kernel<T, D, D, C, DECAY>), dim3(p.nseg - 1, p.BH),
                        dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool DECAY>
 hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C>), dim3(p.nseg * p.BH),
+    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg * p.BH),
                        dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -66,10 +66,17 @@ hipError_t launch_up_sweep(const FwdParams &p, hipStream_t s) {
 template <typename T, int D, int C>
 bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
     if (ahla) {
-        if (decay) return false;
-        if constexpr (ahla_fits<T, D, C>()) {
-            *out = {launch_ahla_summary<T, D, C>, launch_up_sweep<T, D, false>,
-                    launch_ahla_forward<T, D, C>};
+        if (decay) {
+            if constexpr (ahla_fits<T, D, C, true>()) {
+                *out = {launch_ahla_summary<T, D, C, true>, launch_up_sweep<T, D, false>,
+                        launch_ahla_forward<T, D, C, true>};
+                return true;
+            }
+            return false;
+        }
+        if constexpr (ahla_fits<T, D, C, false>()) {
+            *out = {launch_ahla_summary<T, D, C, false>, launch_up_sweep<T, D, false>,
+                    launch_ahla_forward<T, D, C, false>};
             return true;
         }
         return false;

@@ -8,8 +8,9 @@
 //
 // HLA-2: S <- g S + k k^T ; z = S q ; W <- g^2 W + z v^T ; u <- g^2 u + z ;
 //        o = q^T W  (ratio: / q^T u)
-// AHLA : P <- P + k v^T ; y = P^T q ; E <- E + k y^T ; mK <- mK + k ;
-//        nk <- nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
+// AHLA : P <- g P + k v^T ; y = P^T q ; E <- g E + k y^T ; mK <- g mK + k ;
+//        nk <- g nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
+//        (every summary decays by g per token; g = 1 without a decay)
 // HLA3 : P <- P + k v^T ; y = P^T q ; then the HLA-2 step on (q, k, y)
 //        without decay (section "3. HLA de Tercer Orden": the third-order
 //        operator read as tril(L L^T) L V; P^KV is the moment it adds)
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const float g = MODE == kStepHla2 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
+    const float g = MODE != kStepHla3 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
     const float g2 = g * g;
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
@@ -153,20 +154,20 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
         for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
         for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
         __syncthreads();
-        // P <- P + k v^T ; partial y = P^T q
+        // P <- g P + k v^T ; partial y = P^T q
         float yp = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int r = rg + i * RG;
-            const float pn = pv[i] + sk[r] * sv[col];
+            const float pn = g * pv[i] + sk[r] * sv[col];
             P[r * DV + col] = pn;
             yp += sq[r] * pn;
         }
         part[rg][col] = yp;
-        // mK <- mK + k ; s = q . mK
+        // mK <- g mK + k ; s = q . mK
         float sp = 0.f;
         if (tid < D) {
-            mkv += sk[tid];
+            mkv = g * mkv + sk[tid];
             mK[tid] = mkv;
             sp = sq[tid] * mkv;
         }
@@ -178,20 +179,20 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
             sy[tid] = s;
         }
         __syncthreads();
-        // E <- E + k y^T ; partial o = q^T E
+        // E <- g E + k y^T ; partial o = q^T E
         float op = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int r = rg + i * RG;
-            const float en = ev[i] + sk[r] * sy[col];
+            const float en = g * ev[i] + sk[r] * sy[col];
             E[r * DV + col] = en;
             op += sq[r] * en;
         }
         part[rg][col] = op;
-        // nk <- nk + k s ; den = q . nk
+        // nk <- g nk + k s ; den = q . nk
         float dp = 0.f;
         if (tid < D) {
-            nkv += sk[tid] * s_all;
+            nkv = g * nkv + sk[tid] * s_all;
             nk[tid] = nkv;
             dp = sq[tid] * nkv;
         }
@@ -232,6 +233,7 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
     const int tid = threadIdx.x;
     const int col = tid % SW, rg = tid / SW;
     const int j = slice * SW + col;     // this thread's value column
+    const float g = p.gamma[gamma_slot(bh, p.H)];
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
@@ -249,11 +251,11 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
     if (tid < SW) sv[tid] = to_f(v[slice * SW + tid]);
     __syncthreads();
     if (slice == 0) {
-        // mK <- mK + k ; nk <- nk + k (q . mK), owned by this workgroup alone
+        // mK <- g mK + k ; nk <- g nk + k (q . mK), owned by this workgroup alone
         __shared__ float red[NT / kWave];
         float mkv = 0.f, sp = 0.f;
         if (tid < D) {
-            mkv = mK[tid] + sk[tid];
+            mkv = g * mK[tid] + sk[tid];
             mK[tid] = mkv;
             sp = sq[tid] * mkv;
         }
@@ -263,14 +265,14 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
         float s_all = 0.f;
 #pragma unroll
         for (int i = 0; i < NT / kWave; ++i) s_all += red[i];
-        if (tid < D) nk[tid] += sk[tid] * s_all;
+        if (tid < D) nk[tid] = g * nk[tid] + sk[tid] * s_all;
     }
-    // P <- P + k v^T ; partial y = P^T q
+    // P <- g P + k v^T ; partial y = P^T q
     float yp = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + i * RG;
-        const float pn = pv[i] + sk[r] * sv[col];
+        const float pn = g * pv[i] + sk[r] * sv[col];
         P[r * DV + j] = pn;
         yp += sq[r] * pn;
     }
@@ -283,12 +285,12 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
         sy[tid] = y;
     }
     __syncthreads();
-    // E <- E + k y^T ; partial o = q^T E
+    // E <- g E + k y^T ; partial o = q^T E
     float op = 0.f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = rg + i * RG;
-        const float en = ev[i] + sk[r] * sy[col];
+        const float en = g * ev[i] + sk[r] * sy[col];
         E[r * DV + j] = en;
         op += sq[r] * en;
     }

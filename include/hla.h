@@ -21,7 +21,7 @@
  *   HLA_HLA2_RATIO  the HLA_HLA2 numerator divided, row by row, by the same
  *                   double sum with v == 1 (no epsilon; a zero denominator
  *                   gives IEEE inf/NaN in that row)
- *   HLA_AHLA        o = (L L) V,  o_t = sum_{i<=t} sum_{j<=i} A[t,i] A[i,j] v_j
+ *   HLA_AHLA        o = (L L) V,  o_t = sum_{i<=t} sum_{j<=i} g^(t-j) A[t,i] A[i,j] v_j
  *   HLA_AHLA_RATIO  the AHLA numerator over the same sum with v == 1
  *   HLA_HLA3        third order (section "3. HLA de Tercer Orden": the product
  *                   A A^T A made strictly causal), read as o = tril(L L^T) L V:
@@ -29,8 +29,11 @@
  *                   Computed as the second-order operator on the values
  *                   Y = L V (one chunked first-order pass into the workspace);
  *                   no decay, no ratio form
- * g is the per-head decay (1 when gamma is NULL).  No 1/sqrt(d) or other
- * scaling is applied inside.
+ * g is the per-head decay (1 when gamma is NULL).  Decay reading ("Contribuciones
+ * Clave", item 2, names masked operators with and without exponential decay):
+ * every streaming summary of the variant decays by g per token, hence the
+ * weights g^((t-i)+(t-j)) for HLA-2 and g^(t-j) for AHLA.  No 1/sqrt(d) or
+ * other scaling is applied inside.
  *
  * Layout (all row-major, contiguous, device memory):
  *   q, k : [B][H][n][d]     v, o : [B][H][n][dv]    element type = dtype
@@ -119,8 +122,8 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  *                accumulation and fp32 state)
  * variant        hla_variant
  * gamma_host     NULL (no decay) or host array of H floats in (0, 1]: decay of
- *                head h, shared by every batch index; HLA-2 variants only,
- *                H <= HLA_MAX_DECAY_HEADS
+ *                head h, shared by every batch index; HLA-2 and AHLA
+ *                variants (not HLA_HLA3), H <= HLA_MAX_DECAY_HEADS
  * chunk          tokens per intra-chunk tile: 16, 32 or 64 (see Supported)
  * seg_chunks     chunks per segment of the scan; 0 = hla_default_seg_chunks().
  *                The sequence is split into ceil(n / (chunk*seg_chunks))
@@ -274,10 +277,11 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
  * dZ are kept in dtype; the ratio forms, and every form when dgamma is
  * given, run every pass in fp32 (for bf16 inputs on widened copies).
- * Supported: HLA_HLA2, HLA_HLA2_RATIO, HLA_AHLA, HLA_AHLA_RATIO (AHLA with a
- * decay and HLA_HLA3: HLA_ERR_UNSUPPORTED; the ratio forms need nonzero
- * denominators, as the forward), d == dv in {16, 32, 64, 128}, both dtypes.
- * Errors as hla_forward.
+ * Supported: HLA_HLA2, HLA_HLA2_RATIO, HLA_AHLA, HLA_AHLA_RATIO, each with or
+ * without a decay (HLA_HLA3: HLA_ERR_UNSUPPORTED; the ratio forms need
+ * nonzero denominators, as the forward), d == dv in {16, 32, 64, 128}, both
+ * dtypes.  With a decay, AHLA is LA_g(Q, K, LA_g(Q, K, V)) and its passes
+ * carry g.  Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,

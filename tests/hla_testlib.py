@@ -65,7 +65,16 @@ def oracle_forward(x, variant, H, gamma=None, state_in=None, want_state=False, h
             return np.concatenate(res)
         return oracle.hla2(q, k, v, H=(1 if heads is not None else H), gamma=gamma, ratio=ratio,
                            state_in=state_in, want_state=want_state)
-    return oracle.ahla(q, k, v, ratio=ratio, state_in=state_in, want_state=want_state)
+    if heads is not None and gamma is not None:
+        gsel = [float(gamma[h % H]) for h in heads]
+        res = [oracle.ahla(q[i:i + 1], k[i:i + 1], v[i:i + 1], ratio=ratio, H=1, gamma=[gsel[i]],
+                           state_in=None if state_in is None else state_in[i:i + 1],
+                           want_state=want_state) for i in range(len(heads))]
+        if want_state:
+            return (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]))
+        return np.concatenate(res)
+    return oracle.ahla(q, k, v, ratio=ratio, state_in=state_in, want_state=want_state,
+                       H=(1 if heads is not None else H), gamma=gamma)
 
 
 def gpu_forward(x, variant, B, H, dtype, chunk, seg_chunks=0, gamma=None, state_in=None,

@@ -104,8 +104,9 @@ def test_forward_validation_errors(lib):
     assert _fwd(lib, fake, fake, fake, fake, d=128, dv=128, dtype=0) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, chunk=128) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, dtype=F32, d=128, dv=128, chunk=16) == ERR_UNSUP
-    # decay: AHLA has none; gamma must lie in (0, 1]; H bounded
-    assert _fwd(lib, fake, fake, fake, fake, variant=AHLA, gamma=[0.9]) == ERR_UNSUP
+    # decay: not for third order; gamma must lie in (0, 1]; H bounded
+    assert _fwd(lib, fake, fake, fake, fake, variant=4, gamma=[0.9]) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, variant=AHLA, gamma=[1.5]) == ERR_ARG
     assert _fwd(lib, fake, fake, fake, fake, gamma=[0.0]) == ERR_ARG
     assert _fwd(lib, fake, fake, fake, fake, gamma=[1.5]) == ERR_ARG
     assert _fwd(lib, fake, fake, fake, fake, gamma=[float("nan")]) == ERR_ARG
@@ -151,7 +152,8 @@ def test_step_validation_errors(lib):
     assert step(st=None) == ERR_NULL
     assert step(B=0) == ERR_SHAPE
     assert step(d=24, dv=24) == ERR_UNSUP
-    assert step(variant=AHLA_RATIO, gamma=[0.5]) == ERR_UNSUP
+    assert step(variant=4, gamma=[0.5]) == ERR_UNSUP
+    assert step(variant=AHLA_RATIO, gamma=[1.5]) == ERR_ARG
     assert step(gamma=[-0.5]) == ERR_ARG
     assert step(dtype=3) == ERR_ARG
 
@@ -212,8 +214,7 @@ def test_backward_validation(lib):
     assert _bwd(lib, variant=HLA2_RATIO, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=AHLA_RATIO, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=4) == ERR_UNSUP                              # third order: forward only
-    assert _bwd(lib, variant=AHLA, gamma=[0.9, 0.9]) == ERR_UNSUP   # AHLA has no decay
-    assert _bwd(lib, variant=AHLA, dgamma=1) == ERR_UNSUP           # nor a decay gradient
+    assert _bwd(lib, variant=AHLA, dgamma=1) == ERR_UNSUP           # no AHLA decay gradient
     assert _bwd(lib, variant=AHLA_RATIO, dgamma=1) == ERR_UNSUP
     assert _bwd(lib, variant=AHLA, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=9) == ERR_ARG

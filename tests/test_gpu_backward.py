@@ -244,6 +244,32 @@ def test_ratio_backward_n4096_sampled_heads():
     check(tuple(g[heads] for g in got), want, w.dtype, "ratio_n4096 heads 0,127")
 
 
+AHLA_DECAY_SMALL = [
+    # dtype, variant, d, n, H, seg_chunks
+    ("f32", "ahla", 16, 200, 2, 1),
+    ("f32", "ahla", 64, 257, 2, 0),
+    ("f32", "ahla_ratio", 32, 130, 2, 1),
+    ("bf16", "ahla", 64, 450, 3, 2),
+    ("bf16", "ahla", 128, 300, 2, 1),
+    ("bf16", "ahla_ratio", 64, 300, 2, 1),
+]
+
+
+@pytest.mark.parametrize("dtype,variant,d,n,H,seg", AHLA_DECAY_SMALL)
+def test_ahla_decay_backward_small(dtype, variant, d, n, H, seg):
+    """Gradients of AHLA with a per-head decay, LA_g(Q, K, LA_g(Q, K, V)),
+    against the oracle's chain rule through the decayed factors."""
+    say(f"[ahla decay backward] {variant} dtype {dtype} d {d} n {n} H {H} seg_chunks {seg}")
+    B = 1
+    ratio = variant == "ahla_ratio"
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos" if ratio else "l2norm",
+                      seed=1410 + d + n, decay=True)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=1510 + n)
+    got = run_backward(x, do, B, H, dtype, x["gamma"], seg, variant=variant)
+    want = BW.ahla_vjp_batched(x["q"], x["k"], x["v"], do, ratio=ratio, H=H, gamma=x["gamma"])
+    check(got, want, dtype, f"ahla decay {variant} {dtype} d{d} n{n}")
+
+
 AHLA_RATIO_SMALL = [
     # dtype, d, n, H, seg_chunks
     ("f32", 16, 200, 2, 1),

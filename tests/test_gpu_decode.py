@@ -11,15 +11,16 @@ from hla_testlib import TOL, from_dev, gpu_forward, oracle_forward, rel_l2, say,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
+@pytest.mark.parametrize("variant,decay", [("hla2", True), ("hla2_ratio", True), ("ahla", False),
+                                           ("ahla_ratio", False), ("ahla", True),
+                                           ("ahla_ratio", True)])
 @pytest.mark.parametrize("dtype,d", [("f32", 16), ("f32", 32), ("bf16", 64), ("bf16", 128)])
-def test_decode_continues_forward(variant, dtype, d):
+def test_decode_continues_forward(variant, decay, dtype, d):
     import torch
     import causal_streaming_scans_amd as hla
     B, H, n, T = 2, 2, 100, 20
     ratio = variant.endswith("ratio")
-    decay = variant.startswith("hla2")
-    say(f"[decode] {variant} {dtype} d={d} n={n} T={T}")
+    say(f"[decode] {variant} decay={decay} {dtype} d={d} n={n} T={T}")
     x = I.make_inputs(B, H, n + T, d, d, dtype=dtype,
                       dist="uniform_pos" if ratio else "normal_scaled", seed=900 + d, decay=decay)
     g = x["gamma"]

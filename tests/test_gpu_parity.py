@@ -54,6 +54,15 @@ CASES = [
     ("bf16", "hla2_ratio", 2, 2, 1000, 64, 64, 4, False, "uniform_pos"),
     ("bf16", "hla2", 1, 3, 1000, 64, 64, 4, True, "l2norm"),
     ("bf16", "ahla", 1, 2, 1000, 64, 64, 4, False, "l2norm"),
+    # AHLA with a per-head decay (every summary decays by g per token)
+    ("f32", "ahla", 1, 2, 203, 16, 32, 2, True, "normal_scaled"),
+    ("f32", "ahla_ratio", 2, 2, 203, 32, 16, 3, True, "uniform_pos"),
+    ("f32", "ahla", 1, 2, 150, 64, 64, 1, True, "normal_scaled"),
+    ("bf16", "ahla", 1, 3, 1000, 64, 64, 3, True, "l2norm"),
+    ("bf16", "ahla", 1, 2, 1000, 64, 64, 4, True, "l2norm"),
+    ("bf16", "ahla_ratio", 1, 2, 517, 64, 32, 2, True, "uniform_pos"),
+    ("bf16", "ahla", 1, 2, 400, 128, 64, 2, True, "l2norm"),
+    ("bf16", "ahla", 1, 2, 333, 32, 16, 5, True, "l2norm"),
 ]
 
 
@@ -77,15 +86,16 @@ SUPPORT = [(dt, d, c, fam)
 
 
 @pytest.mark.parametrize("case", SUPPORT, ids=lambda c: "-".join(str(x) for x in c))
-def test_support_matrix(case):
-    """One small ragged, multi-segment case per kernel instance: HLA-2 with a
-    per-head decay and the ratio form, AHLA with the ratio form."""
+@pytest.mark.parametrize("decay", [False, True])
+def test_support_matrix(case, decay):
+    """One small ragged, multi-segment case per kernel instance, ratio form,
+    with and without a per-head decay."""
     dtype, d, chunk, fam = case
     variant = fam + "_ratio"
     B, H, seg = 1, 2, 2
     n = 2 * chunk * seg + chunk // 2 + 3
-    say(f"[support] {case} n={n}")
-    x = _inputs(B, H, n, d, dtype, "uniform_pos", seed=5000 + d + chunk, decay=fam == "hla2")
+    say(f"[support] {case} decay={decay} n={n}")
+    x = _inputs(B, H, n, d, dtype, "uniform_pos", seed=5000 + d + chunk, decay=decay)
     got = gpu_forward(x, variant, B, H, dtype, chunk, seg, gamma=x["gamma"])
     want = oracle_forward(x, variant, H, gamma=x["gamma"])
     err = rel_l2(got, want)
@@ -96,9 +106,11 @@ def test_support_matrix(case):
 
 @pytest.mark.parametrize("shape", [(32, 32, 2, 3), (64, 64, 2, 1), (32, 16, 4, 3)],
                          ids=["d32c32", "d64c64", "d32c16"])
-@pytest.mark.parametrize("variant", ["hla2", "hla2_ratio", "ahla", "ahla_ratio"])
+@pytest.mark.parametrize("variant,decay", [("hla2", True), ("hla2_ratio", True), ("ahla", False),
+                                           ("ahla_ratio", False), ("ahla", True),
+                                           ("ahla_ratio", True)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_state_out_and_resume(variant, dtype, shape):
+def test_state_out_and_resume(variant, decay, dtype, shape):
     """forward(n1) -> state_out -> forward(n2, state_in) equals forward(n1+n2),
     and state_out equals the oracle's state.  d = chunk = 64 runs the kernels'
     per-row-tile state layout; its second call has three segments, so the
@@ -108,7 +120,6 @@ def test_state_out_and_resume(variant, dtype, shape):
     say(f"[resume] {variant} {dtype} d={d} chunk={chunk}")
     B, H, n1, n2 = 1, 2, 230, 181
     dist = "uniform_pos" if variant.endswith("ratio") else "normal_scaled"
-    decay = variant.startswith("hla2")
     x = _inputs(B, H, n1 + n2, d, dtype, dist, seed=77 + d, decay=decay)
     g = x["gamma"]
     x1 = {kk: x[kk][:, :n1] for kk in ("q", "k", "v")}

@@ -37,7 +37,7 @@ def _ref_summaries(x, bh, variant, chunk, seg_len, nseg, g):
             sm = CS.hla2_segment_summary(q[a:b], k[a:b], v[a:b], chunk, g)
             sums.append((sm["S"], sm["C"], sm["W"], sm["m"], sm["u"]))
         else:
-            sm = CS.ahla_segment_summary(q[a:b], k[a:b], v[a:b], chunk)
+            sm = CS.ahla_segment_summary(q[a:b], k[a:b], v[a:b], chunk, g)
             sums.append((sm["M"], sm["P"], sm["E"], sm["mK"], sm["nk"]))
     return sums
 
@@ -65,6 +65,8 @@ def _nodes(nreal):
     ("bf16", "ahla", 64, 64, 1, False),
     ("bf16", "ahla", 64, 32, 2, False),
     ("f32", "ahla", 32, 16, 1, False),
+    ("bf16", "ahla", 64, 64, 1, True),
+    ("f32", "ahla", 32, 16, 2, True),
 ])
 def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
     import torch
@@ -102,8 +104,8 @@ def test_summaries_and_up_sweep(dtype, variant, d, chunk, seg, decay):
             comb = lambda A, Bq: CS.hla2_combine(A, Bq, g)
             parts = lambda it: (it["S"], it["C"], it["W"], it["m"], it["u"])
         else:
-            items = [dict(M=r[0], P=r[1], E=r[2], mK=r[3], nk=r[4]) for r in ref]
-            comb = CS.ahla_combine
+            items = [dict(M=r[0], P=r[1], E=r[2], mK=r[3], nk=r[4], l=seg_len) for r in ref]
+            comb = lambda A, Bq: CS.ahla_combine(A, Bq, g)
             parts = lambda it: (it["M"], it["P"], it["E"], it["mK"], it["nk"])
         for s_ in range(nreal):
             for stage_ws in (e1, e):      # the leaves are not touched by stage 2

@@ -92,3 +92,46 @@ def test_ahla_n65536_sampled_heads_and_decode():
     derr = rel_l2(got_dec, want_dec)
     say(f"   decode rel_l2 {derr:.3e}")
     assert np.isfinite(got_dec).all() and derr < TOL[w.dtype]
+
+
+def test_ahla_decay_n65536_sampled_heads_and_decode():
+    """The AHLA workload's shape (B=1 H=32 n=65536 d=dv=64 bf16) with per-head
+    decays g_h ~ U[0.95, 0.999] (drawn after q, k, v from the same stream),
+    default launch configuration, then 64 decode steps with the same decays;
+    sampled heads against the oracle."""
+    import torch
+    import oracle
+    import causal_streaming_scans_amd as hla
+    from hla_testlib import to_dev
+    key = "ahla_n65536"
+    w = I.WORKLOADS[key]
+    rng = np.random.default_rng(6)
+    heads = sorted(rng.choice(w.B * w.H, size=3, replace=False).tolist())
+    T = 64
+    say(f"[workload] {key} with decay, forward + {T} decode steps, heads {heads}")
+    x = I.workload_inputs(key, decay=True)
+    g = x["gamma"]
+    got, st = gpu_forward(x, w.variant, w.B, w.H, w.dtype, w.chunk, 0, gamma=g, want_state=True)
+    want, wst = oracle_forward(x, w.variant, w.H, gamma=g, heads=heads, want_state=True)
+    err = rel_l2(got[heads], want)
+    say(f"   forward rel_l2 {err:.3e}")
+    assert np.isfinite(got).all() and err < TOL[w.dtype]
+    st_err = rel_l2(st[heads], wst)
+    say(f"   state rel_l2 {st_err:.3e}")
+    assert st_err < TOL[w.dtype]
+
+    state = torch.from_numpy(st.astype(np.float32).reshape(-1)).cuda()
+    qd = to_dev(x["q_dec"][:T], "bf16", (T, w.B, w.H, w.d))
+    kd = to_dev(x["k_dec"][:T], "bf16", (T, w.B, w.H, w.d))
+    vd = to_dev(x["v_dec"][:T], "bf16", (T, w.B, w.H, w.dv))
+    outs = [hla.hla_step(qd[t], kd[t], vd[t], state, variant=w.variant, gamma=g) for t in range(T)]
+    torch.cuda.synchronize()
+    got_dec = torch.stack(outs).float().cpu().numpy().reshape(T, w.B * w.H, w.dv)
+    got_dec = got_dec.transpose(1, 0, 2)[heads]
+    want_dec = np.concatenate([
+        oracle.ahla(*(np.ascontiguousarray(x[kk + "_dec"][:T, hd][None]) for kk in "qkv"),
+                    state_in=wst[i:i + 1], H=1, gamma=[float(g[hd % w.H])])
+        for i, hd in enumerate(heads)])
+    derr = rel_l2(got_dec, want_dec)
+    say(f"   decode rel_l2 {derr:.3e}")
+    assert np.isfinite(got_dec).all() and derr < TOL[w.dtype]
