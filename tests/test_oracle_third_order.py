@@ -88,3 +88,130 @@ def test_other_mask_placements_are_not_causal():
     q2[15] += 1.0
     assert not np.allclose(no_inner(q2, k, v)[:10], no_inner(q, k, v)[:10])
     assert np.allclose(T3.hla3_matrix(q2, k, v)[:15], T3.hla3_matrix(q, k, v)[:15], rtol=1e-14)
+
+
+# ------------------------------------------------- decay and the ratio form
+
+def _la(q, k, v, g=1.0):
+    """Textbook causal linear attention with decay, by its own recurrence:
+    M <- g M + k v^T, out_t = M^T q_t."""
+    M = np.zeros((q.shape[1], v.shape[1]))
+    out = np.empty((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        M = g * M + np.outer(k[t], v[t])
+        out[t] = q[t] @ M
+    return out
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.8, 0.95])
+@pytest.mark.parametrize("ratio", [False, True])
+def test_decay_and_ratio_forms_agree(gamma, ratio):
+    rng = np.random.default_rng(41)
+    q, k, v = rng.random((9, 3)), rng.random((9, 3)), rng.standard_normal((9, 2))
+    a = T3.hla3_loops(q, k, v, gamma, ratio)
+    assert rel(T3.hla3_matrix(q, k, v, gamma, ratio), a) < 1e-13
+    assert rel(T3.hla3_serial(q, k, v, gamma, ratio), a) < 1e-13
+    q, k, v = rng.random((120, 6)) / 6, rng.random((120, 6)) / 6, rng.standard_normal((120, 4))
+    assert rel(T3.hla3_serial(q, k, v, gamma, ratio), T3.hla3_matrix(q, k, v, gamma, ratio)) < 1e-12
+
+
+@pytest.mark.parametrize("gamma", [0.5, 0.9])
+def test_decay_all_ones_closed_form(gamma):
+    """q = k = v = 1 (d = dv = 1): the weight of (i, m, j) is
+    g^((t-i)+(t-m)+(t-j)), so o_t = sum_{m<=t} g^(3(t-m)) (sum_{i<=m} g^(m-i))^2
+    = sum_{m<=t} g^(3(t-m)) ((1 - g^(m+1)) / (1 - g))^2."""
+    n = 30
+    one = np.ones((n, 1))
+    want = [sum(gamma ** (3 * (t - m)) * ((1 - gamma ** (m + 1)) / (1 - gamma)) ** 2
+                for m in range(t + 1)) for t in range(n)]
+    np.testing.assert_allclose(T3.hla3_serial(one, one, one, gamma)[:, 0], want, rtol=1e-13)
+    np.testing.assert_allclose(T3.hla3_loops(one[:7], one[:7], one[:7], gamma)[:, 0], want[:7],
+                               rtol=1e-13)
+
+
+@pytest.mark.parametrize("gamma", [1.0, 0.9])
+def test_decay_is_chained_linear_attention(gamma):
+    """o = LA_{g^3}(Q, LA_g(Q, K, K), LA_g(Q, K, V)): keys z_m = S_m q_m and
+    values y_m = P_m^T q_m, each decayed to m, meet with g^(3(t-m))."""
+    q, k, v = rnd(42, 60, 5, 3)
+    want = _la(q, _la(q, k, k, gamma), _la(q, k, v, gamma), gamma ** 3)
+    assert rel(T3.hla3_serial(q, k, v, gamma), want) < 1e-12
+
+
+def test_decay_zero_and_ratio_invariants():
+    q, k, v = rnd(43, 25, 4, 3)
+    # g = 0 keeps i = m = j = t only: o_t = (q_t . k_t)^3 v_t
+    want = ((q * k).sum(1) ** 3)[:, None] * v
+    assert rel(T3.hla3_serial(q, k, v, 0.0), want) < 1e-13
+    rng = np.random.default_rng(44)
+    qp, kp = rng.random((30, 4)), rng.random((30, 4))
+    c = np.ones((30, 3)) * np.array([0.5, -1.0, 3.0])
+    assert rel(T3.hla3_serial(qp, kp, c, 0.9, ratio=True), c) < 1e-13
+    # the ratio form is homogeneous of degree 0 in q and in k
+    vp = rng.standard_normal((30, 3))
+    base = T3.hla3_serial(qp, kp, vp, 0.9, ratio=True)
+    assert rel(T3.hla3_serial(2.5 * qp, 0.3 * kp, vp, 0.9, ratio=True), base) < 1e-13
+
+
+def test_decay_causality_and_resume():
+    q, k, v = rnd(45, 50, 4, 3)
+    o1 = T3.hla3_serial(q, k, v, 0.9, ratio=False)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[30:] += 1.0
+    v2[30:] *= -2.0
+    o2 = T3.hla3_serial(q2, k2, v2, 0.9)
+    assert np.array_equal(o1[:30], o2[:30])
+    for ratio in (False, True):
+        qq, kk = (np.abs(q), np.abs(k)) if ratio else (q, k)
+        whole = T3.hla3_serial(qq, kk, v, 0.93, ratio)
+        a, st = T3.hla3_serial_state(qq[:21], kk[:21], v[:21], 0.93, ratio)
+        b, _ = T3.hla3_serial_state(qq[21:], kk[21:], v[21:], 0.93, ratio, state=st)
+        assert rel(np.concatenate([a, b]), whole) < 1e-13
+
+
+def test_decay_law_rejects_plausible_mistakes():
+    """The second-order weight law g^((t-i)+(t-j)) (no term for m), and g^2
+    instead of g^3 between the keys' and values' chains, each differ from the
+    reading far beyond the tolerances above."""
+    q, k, v = rnd(46, 20, 4, 3)
+    g = 0.85
+    good = T3.hla3_serial(q, k, v, g)
+    assert rel(_la(q, _la(q, k, k, g), _la(q, k, v, g), g ** 2), good) > 1e-2
+    n = q.shape[0]
+    A = q @ k.T
+    bad = np.zeros_like(good)
+    for t in range(n):
+        for m in range(t + 1):
+            for i in range(m + 1):
+                for j in range(m + 1):
+                    bad[t] += g ** ((t - i) + (t - j)) * A[t, i] * A[m, i] * A[m, j] * v[j]
+    assert rel(bad, good) > 1e-2
+
+
+@pytest.mark.parametrize("gamma,ratio", [(1.0, False), (0.8, False), (0.9, True)])
+def test_backward_by_central_differences_and_euler(gamma, ratio):
+    rng = np.random.default_rng(47)
+    n, d, dv = 8, 3, 2
+    q, k = (rng.random((n, d)), rng.random((n, d))) if ratio else \
+        (rng.standard_normal((n, d)), rng.standard_normal((n, d)))
+    v = rng.standard_normal((n, dv))
+    do = rng.standard_normal((n, dv))
+    dq, dk, dv_ = T3.hla3_vjp(q, k, v, do, gamma, ratio)
+    h = 1e-6
+    for x, dx in ((q, dq), (k, dk), (v, dv_)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + h
+            fp = (T3.hla3_matrix(q, k, v, gamma, ratio) * do).sum()
+            x[idx] = x0 - h
+            fm = (T3.hla3_matrix(q, k, v, gamma, ratio) * do).sum()
+            x[idx] = x0
+            num[idx] = (fp - fm) / (2 * h)
+        assert rel(dx, num) < 1e-6
+    # Euler: o has degree 3 in q, 3 in k, 1 in v (ratio: 0, 0, 1)
+    o = T3.hla3_matrix(q, k, v, gamma, ratio)
+    ref = float((do * o).sum())
+    dq_deg = 0 if ratio else 3
+    np.testing.assert_allclose(float((q * dq).sum()), dq_deg * ref, atol=1e-9 * abs(ref) + 1e-12)
+    np.testing.assert_allclose(float((v * dv_).sum()), ref, rtol=1e-10)
