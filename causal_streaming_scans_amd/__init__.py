@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libhla.so")
 _lib = None
 
-VARIANTS = {"hla2": 0, "hla2_ratio": 1, "ahla": 2, "ahla_ratio": 3, "hla3": 4}
+VARIANTS = {"hla2": 0, "hla2_ratio": 1, "ahla": 2, "ahla_ratio": 3, "hla3": 4, "hla3_ratio": 5}
 _DTYPES = {"f32": 0, "bf16": 1}
 MAX_DECAY_HEADS = 256
 

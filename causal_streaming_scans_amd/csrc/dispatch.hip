@@ -21,7 +21,9 @@ hipError_t launch_copy_or_zero(const float *src, float *dst, size_t count, hipSt
 
 template <typename T, int D, int MODE>
 hipError_t launch_step(const StepParams &p, hipStream_t s) {
-    if (MODE == kStepAhla && !p.ratio) {
+    if constexpr (MODE == kStepHla3) {
+        hipLaunchKernelGGL((hla3_step_kernel<T, D, D, 256>), dim3(p.BH), dim3(256), 0, s, p);
+    } else if (MODE == kStepAhla && !p.ratio) {
         // unnormalised AHLA: one workgroup per 16 value columns of each head
         hipLaunchKernelGGL((ahla_step_sliced_kernel<T, D, D, 256>), dim3(p.BH * (D / 16)), dim3(256),
                            0, s, p);

@@ -24,10 +24,16 @@ using namespace hla;
 
 namespace {
 
-bool valid_variant(int v) { return v >= HLA_HLA2 && v <= HLA_HLA3; }
-bool is_hla3(int v) { return v == HLA_HLA3; }
+bool valid_variant(int v) { return v >= HLA_HLA2 && v <= HLA_HLA3_RATIO; }
+bool is_hla3(int v) { return v == HLA_HLA3 || v == HLA_HLA3_RATIO; }
 bool is_ahla(int v) { return v == HLA_AHLA || v == HLA_AHLA_RATIO; }
-bool is_ratio(int v) { return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO; }
+bool is_ratio(int v) {
+    return v == HLA_HLA2_RATIO || v == HLA_AHLA_RATIO || v == HLA_HLA3_RATIO;
+}
+// third order as chained first-order passes: with a decay, or the ratio form
+bool hla3_chain(int v, const float *gamma) {
+    return v == HLA_HLA3_RATIO || (v == HLA_HLA3 && gamma != nullptr);
+}
 
 long ceil_div(long a, long b) { return (a + b - 1) / b; }
 
@@ -47,7 +53,6 @@ hla_status check_common(int B, int H, int d, int dv, int dtype, int variant, con
     if (B < 1 || H < 1 || d < 1 || dv < 1) return HLA_ERR_SHAPE;
     if ((long)B * H > 65535) return HLA_ERR_UNSUPPORTED;
     if (gamma) {
-        if (is_hla3(variant)) return HLA_ERR_UNSUPPORTED;
         if (H > HLA_MAX_DECAY_HEADS) return HLA_ERR_UNSUPPORTED;
         for (int h = 0; h < H; ++h)
             if (!(gamma[h] > 0.f && gamma[h] <= 1.f)) return HLA_ERR_ARG;  // also rejects NaN
@@ -290,6 +295,7 @@ extern "C" {
 
 size_t hla_state_floats(int variant, int d, int dv) {
     if (!valid_variant(variant) || d < 1 || dv < 1) return 0;
+    if (variant == HLA_HLA3_RATIO) return 2 * (size_t)hla3_state_floats(d, dv);
     if (is_hla3(variant)) return (size_t)hla3_state_floats(d, dv);
     return is_ahla(variant) ? (size_t)ahla_state_floats(d, dv) : (size_t)hla2_state_floats(d, dv);
 }
@@ -325,10 +331,14 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
     const size_t scan = nseg <= 1 ? 0
         : 2 * (size_t)B * H * (size_t)(nseg - 1) * (size_t)summary_floats(d, dv) * sizeof(float);
     if (!is_hla3(variant)) return scan;
-    // third order: Y = LA(Q, K, V) (sized for fp32) and its pass's segment states
+    // third order: the segment states of its first-order passes, then
+    // [B*H][n][d] fp32 tensors: Y and Z of the decayed chain (the undecayed
+    // form uses the first for Y); the ratio form also widened q, k, v, the
+    // unit rows, Y1, the numerator and the denominator
     const long nseg_la = num_segments(n, kLaChunk, hla_backward_default_seg_chunks(B, H, n));
-    return scan + (size_t)B * H * n * dv * sizeof(float) +
-           (size_t)B * H * (size_t)(nseg_la - 1) * d * dv * sizeof(float);
+    const size_t sums = (size_t)B * H * (size_t)(nseg_la - 1) * d * dv * sizeof(float);
+    const size_t tensor = (size_t)B * H * n * dv * sizeof(float);
+    return scan + sums + (variant == HLA_HLA3_RATIO ? 9 : 2) * tensor;
 }
 
 // The first-order pass of the third-order variant, Y = LA(Q, K, V), run
@@ -336,7 +346,91 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int 
 struct Hla3Pass {
     LaLaunches la;
     LaParams lp;
+    // the chained form (a decay, or the ratio form): passes of decay g (p1)
+    // and g^3 (p3) over the tensors in the workspace
+    bool chain, ratio, widen;
+    LaLaunches lac;
+    LaParams p1, p3;
+    const void *q, *k, *v;
+    void *o;
+    char *tensors;
+    size_t tensor_bytes;
+    long rows;
+    int d;
+    const float *state_in;
+    float *state_out;
+    size_t state_count;     // floats of state_out
 };
+
+// State views of the third-order layout (per head bh): the P^KV block at
+// base + bh*d*dv, then the second-order block [S | W | u] at
+// base + BH*d*dv + bh*(d*d + d*dv + d); the ratio form's unit-value chain
+// repeats that layout after it.
+static const float *hla3_view(const float *base, int BH, int d, int part, int chain) {
+    if (!base) return nullptr;
+    const size_t one = (size_t)BH * hla3_state_floats(d, d);
+    const float *b = base + (size_t)chain * one;
+    if (part == 0) return b;                                  // P
+    b += (size_t)BH * d * d;
+    return part == 1 ? b : b + (size_t)d * d;                 // S, W
+}
+static float *hla3_view(float *base, int BH, int d, int part, int chain) {
+    return const_cast<float *>(hla3_view(static_cast<const float *>(base), BH, d, part, chain));
+}
+
+// Third order with a decay or in the ratio form:
+//   Y = LA_g(Q, K, V),  Z = LA_g(Q, K, K),  O = LA_{g^3}(Q, Z, Y)
+// (keys z_m = S_m q_m and values y_m = P_m^T q_m, each decayed to m, meet
+// with g^(3(t-m))); the ratio form runs the value chain again on unit rows
+// ONE1, Y1 = LA_g(Q, K, ONE1), DEN = LA_{g^3}(Q, Z, Y1), in fp32, and
+// divides.  Tensors: [qw, kw, vw (widened bf16 inputs),] Y, Z[, ONE1, Y1,
+// O, DEN].
+static hla_status run_hla3_chain(const Hla3Pass &x, hipStream_t s) {
+    const LaLaunches &la = x.lac;
+    auto t = [&](int i) { return static_cast<void *>(x.tensors + (size_t)i * x.tensor_bytes); };
+    const void *q = x.q, *k = x.k, *v = x.v;
+    const long count = x.rows * x.d;
+    if (x.widen) {
+        const void *src[3] = {x.q, x.k, x.v};
+        for (int i = 0; i < 3; ++i)
+            if (launch_convert(src[i], t(i), count, true, s) != hipSuccess) return HLA_ERR_DEVICE;
+        q = t(0);
+        k = t(1);
+        v = t(2);
+    }
+    const int base = x.ratio ? 3 : 0;
+    void *Y = t(base), *Z = t(base + 1);
+    void *O = x.ratio ? t(base + 4) : x.o;
+    const int BH = x.p1.BH, d = x.d;
+    const long hla2_stride = hla2_state_floats(d, d);
+    // the u slots are not used by third order: the whole state starts at zero
+    if (x.state_out && launch_copy_or_zero(nullptr, x.state_out, x.state_count, s) != hipSuccess)
+        return HLA_ERR_DEVICE;
+    auto pass = [&](const LaParams &base_p, const void *a, const void *b, const void *c, void *out,
+                    int part, int chain, bool second_copy) {
+        LaParams p = base_p;
+        p.a = a;
+        p.b = b;
+        p.c = c;
+        p.out = out;
+        p.state_stride = part == 0 ? 0 : hla2_stride;
+        p.state_in = hla3_view(x.state_in, BH, d, part, chain);
+        p.state_out = hla3_view(x.state_out, BH, d, part, chain);
+        p.state_out2 = second_copy ? hla3_view(x.state_out, BH, d, part, 1) : nullptr;
+        return la.plain(p, s, true) == hipSuccess;
+    };
+    if (!pass(x.p1, q, k, v, Y, 0, 0, false)) return HLA_ERR_DEVICE;           // Y, P
+    if (!pass(x.p1, q, k, k, Z, 1, 0, x.ratio)) return HLA_ERR_DEVICE;         // Z, S
+    if (!pass(x.p3, q, Z, Y, O, 2, 0, false)) return HLA_ERR_DEVICE;           // O, W
+    if (!x.ratio) return HLA_OK;
+    void *ONE1 = t(base + 2), *Y1 = t(base + 3), *DEN = t(base + 5);
+    if (la.unit_column(ONE1, x.rows, s) != hipSuccess) return HLA_ERR_DEVICE;
+    if (!pass(x.p1, q, k, ONE1, Y1, 0, 1, false)) return HLA_ERR_DEVICE;       // Y1, P of ONE1
+    if (!pass(x.p3, q, Z, Y1, DEN, 2, 1, false)) return HLA_ERR_DEVICE;        // DEN, its W
+    return launch_divide_rows(static_cast<const float *>(O), static_cast<const float *>(DEN),
+                              x.o, x.rows, d, !x.widen ? false : true, s) == hipSuccess
+               ? HLA_OK : HLA_ERR_DEVICE;
+}
 
 // Validate, pick the kernels and fill the argument block; shared by
 // hla_forward and hla_forward_stage.
@@ -355,6 +449,9 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     if (!lookup_forward(dtype, is_ahla(variant), d, dv, chunk, gamma_host != nullptr, kern))
         return HLA_ERR_UNSUPPORTED;
     if (is_hla3(variant) && (d != dv || !lookup_la(dtype, d, &x3->la))) return HLA_ERR_UNSUPPORTED;
+    x3->chain = hla3_chain(variant, gamma_host);
+    if (x3->chain && !lookup_la(variant == HLA_HLA3_RATIO ? HLA_F32 : dtype, d, &x3->lac))
+        return HLA_ERR_UNSUPPORTED;
     const int g = effective_seg_chunks(variant, B, H, n, d, chunk, seg_chunks);
     if ((long)chunk * g > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
     const long nseg = num_segments(n, chunk, g);
@@ -385,25 +482,50 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     fill_gamma(p->gamma, gamma_host, H);
     fill_order(p);
     if (is_hla3(variant)) {
-        // Y after the scan's part of the workspace; the second-order stages
-        // read it as their values
+        // after the scan's part of the workspace: the first-order passes'
+        // segment states, then the tensors (Y first, which the second-order
+        // stages of the undecayed form read as their values)
         const size_t scan = nseg <= 1 ? 0
             : 2 * (size_t)B * H * (size_t)(nseg - 1) * (size_t)summary_floats(d, dv) * sizeof(float);
-        char *Y = static_cast<char *>(workspace) + scan;
         const int g_la = hla_backward_default_seg_chunks(B, H, n);
+        const long nseg_la = num_segments(n, kLaChunk, g_la);
+        char *sums = static_cast<char *>(workspace) + scan;
+        char *tensors = sums + (size_t)B * H * (size_t)(nseg_la > 0 ? nseg_la - 1 : 0) * d * dv * sizeof(float);
+        char *Y = tensors;
         LaParams &lp = x3->lp;
         memset(&lp, 0, sizeof(lp));
         lp.a = q;
         lp.b = k;
         lp.c = v;
         lp.out = Y;
-        lp.sums = reinterpret_cast<float *>(Y + (size_t)B * H * n * dv * sizeof(float));
+        lp.sums = reinterpret_cast<float *>(sums);
         lp.BH = B * H;
         lp.H = H;
         lp.n = n;
         lp.seg_len = kLaChunk * g_la;
-        lp.nseg = (int)num_segments(n, kLaChunk, g_la);
+        lp.nseg = (int)nseg_la;
         fill_gamma(lp.gamma, nullptr, H);
+        if (x3->chain) {
+            x3->ratio = variant == HLA_HLA3_RATIO;
+            x3->widen = x3->ratio && dtype == HLA_BF16;
+            x3->p1 = lp;
+            fill_gamma(x3->p1.gamma, gamma_host, H);
+            x3->p3 = x3->p1;
+            for (int h = 0; h < kMaxDecayHeads; ++h)
+                x3->p3.gamma[h] = x3->p1.gamma[h] * x3->p1.gamma[h] * x3->p1.gamma[h];
+            x3->q = q;
+            x3->k = k;
+            x3->v = v;
+            x3->o = o;
+            x3->tensors = tensors;
+            x3->tensor_bytes = (size_t)B * H * n * dv * sizeof(float);
+            x3->rows = (long)B * H * n;
+            x3->d = d;
+            x3->state_in = state_in;
+            x3->state_out = state_out;
+            x3->state_count = (size_t)B * H * hla_state_floats(variant, d, dv);
+            return HLA_OK;
+        }
         p->v = Y;
         // state: the P^KV blocks of all heads, then the second-order states
         const size_t pkv = (size_t)B * H * d * dv;
@@ -428,6 +550,7 @@ static hla_status run_stage(int stage, const FwdKernels &kern, const FwdParams &
         return HLA_OK;
     }
     hipError_t e = hipSuccess;
+    if (is_hla3(variant) && x3.chain) return stage == 3 ? run_hla3_chain(x3, s) : HLA_OK;
     if (stage == 1 && is_hla3(variant)) {
         e = x3.la.plain(x3.lp, s, true);
         if (e != hipSuccess) return HLA_ERR_DEVICE;

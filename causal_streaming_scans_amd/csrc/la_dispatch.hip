@@ -107,6 +107,32 @@ bool la_set(LaLaunches *out) {
     return true;
 }
 
+template <int D>
+hipError_t launch_divide_rows_d(const float *num, const float *den, void *out, long rows,
+                                bool to_bf16, hipStream_t s) {
+    long blocks = (rows * (D / 4) + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) return hipSuccess;
+    if (to_bf16)
+        hipLaunchKernelGGL((divide_rows_kernel<bf16, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           num, den, static_cast<bf16 *>(out), rows);
+    else
+        hipLaunchKernelGGL((divide_rows_kernel<float, D>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           num, den, static_cast<float *>(out), rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_divide_rows(const float *num, const float *den, void *out, long rows, int d,
+                              bool to_bf16, hipStream_t s) {
+    switch (d) {
+        case 16: return launch_divide_rows_d<16>(num, den, out, rows, to_bf16, s);
+        case 32: return launch_divide_rows_d<32>(num, den, out, rows, to_bf16, s);
+        case 64: return launch_divide_rows_d<64>(num, den, out, rows, to_bf16, s);
+        case 128: return launch_divide_rows_d<128>(num, den, out, rows, to_bf16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_convert(const void *src, void *dst, long count, bool to_f32, hipStream_t s) {
     const long count4 = count / 4;
     long blocks = (count4 + 255) / 256;

@@ -118,8 +118,12 @@ struct LaRegs {
         }
     }
 
+    // The rows' weights for the state advance are g^(cv-1-r), cv = the
+    // chunk's valid rows (its last row gets g^0), so that the advance by
+    // g^cv leaves the state exact after a partial last chunk too.
     template <bool WITH_A = true, bool SYM, bool DUAL>
     __device__ __forceinline__ void store(LaLds<T, D, C, SYM, DUAL> &s, int n) const {
+        const int cv = n - l0 < C ? n - l0 : C;
         using TL = typename LaLds<T, D, C, SYM, DUAL>::TR;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
@@ -154,7 +158,7 @@ struct LaRegs {
                 }
                 store16(s.b + o, xb);
                 store16(s.c + o, xc);
-                const float w = s.pw[C - 1 - r];
+                const float w = r < cv ? s.pw[cv - 1 - r] : 0.f;
                 Vec16<T> yb;
 #pragma unroll
                 for (int e = 0; e < VE; ++e) yb.v[e] = from_f<T>(to_f(xb.v[e]) * w);
@@ -342,9 +346,24 @@ void la_forward_kernel(LaParams p) {
     regs.load(p, head_row, l_begin);
     fill_pow_table<Cfg::NT>(s.pw, C + 1, g);
 
-    // carried state: the summaries of the segments before this one, in order
+    // carried state: the caller's state before token 0, then the summaries
+    // of the segments before this one, in order (each fold decays what is
+    // already there by g^(segment length))
     LaState<T, D, C, SYM, DUAL> S;
     S.zero();
+    const size_t st_stride = p.state_stride > 0 ? (size_t)p.state_stride : (size_t)(D * D);
+    if (p.state_in) {
+        const float *src = p.state_in + (size_t)bh * st_stride;
+#pragma unroll
+        for (int i = 0; i < Cfg::SPW; ++i) {
+            const int m = w + Cfg::NW * i;
+            if (m < Cfg::NS) {
+                const int si = m / Cfg::TD, sj = m % Cfg::TD;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S.acc[i][r] = src[(16 * si + 4 * gq + r) * D + 16 * sj + cl];
+            }
+        }
+    }
     if (seg > 0) {
         const float gL = pow_int(g, p.seg_len);
         for (int s2 = 0; s2 < seg; ++s2) {
@@ -361,19 +380,6 @@ void la_forward_kernel(LaParams p) {
             }
         }
     }
-    if (p.state_in) {
-        // the caller's state before token 0 (passes without decay only)
-        const float *src = p.state_in + (size_t)bh * (D * D);
-#pragma unroll
-        for (int i = 0; i < Cfg::SPW; ++i) {
-            const int m = w + Cfg::NW * i;
-            if (m < Cfg::NS) {
-                const int si = m / Cfg::TD, sj = m % Cfg::TD;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) S.acc[i][r] += src[(16 * si + 4 * gq + r) * D + 16 * sj + cl];
-            }
-        }
-    }
     S.store_copy(s, w);
     __syncthreads();
     const float gC = s.pw[C];
@@ -382,6 +388,7 @@ void la_forward_kernel(LaParams p) {
     T *Out = static_cast<T *>(p.out);
 
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
+        const int cv = min(C, l_end - l0);   // valid rows of this chunk
         regs.store(s, p.n);
         if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
         __syncthreads();
@@ -464,21 +471,24 @@ void la_forward_kernel(LaParams p) {
                 }
             }
         }
-        S.advance(s, gC, w);
+        S.advance(s, cv == C ? gC : s.pw[cv], w);
         __syncthreads();
         S.store_copy(s, w);
     }
-    if (p.state_out && seg == p.nseg - 1) {
-        // the state after token n-1 (passes without decay only)
-        float *dst = p.state_out + (size_t)bh * (D * D);
+    if (seg == p.nseg - 1) {
+        // the state after token n-1
+        for (float *base : {p.state_out, p.state_out2}) {
+            if (!base) continue;
+            float *dst = base + (size_t)bh * st_stride;
 #pragma unroll
-        for (int i = 0; i < Cfg::SPW; ++i) {
-            const int m = w + Cfg::NW * i;
-            if (m < Cfg::NS) {
-                const int si = m / Cfg::TD, sj = m % Cfg::TD;
+            for (int i = 0; i < Cfg::SPW; ++i) {
+                const int m = w + Cfg::NW * i;
+                if (m < Cfg::NS) {
+                    const int si = m / Cfg::TD, sj = m % Cfg::TD;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dst[(16 * si + 4 * gq + r) * D + 16 * sj + cl] = S.acc[i][r];
+                    for (int r = 0; r < 4; ++r)
+                        dst[(16 * si + 4 * gq + r) * D + 16 * sj + cl] = S.acc[i][r];
+                }
             }
         }
     }
@@ -505,6 +515,23 @@ __global__ __launch_bounds__(256) void unit_column_kernel(T *out, long rows) {
     const long stride = (long)gridDim.x * blockDim.x;
     for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
         out[i] = from_f<T>(i % D == 0 ? 1.f : 0.f);
+}
+
+// Row-wise division of the third-order ratio form: out[t][:] = num[t][:] /
+// den[t][0], with num and den fp32 [rows][D] and out of element type TO.
+// Four consecutive values per thread; a zero den gives IEEE inf / NaN.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void divide_rows_kernel(const float *num, const float *den,
+                                                          TO *out, long rows) {
+    constexpr int Q4 = D / 4;
+    const long total = rows * Q4;
+    const long stride = (long)gridDim.x * blockDim.x;
+    for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const long row = i / Q4;
+        const f32x4 x = reinterpret_cast<const f32x4 *>(num)[i];
+        const float dn = den[(size_t)row * D];
+        store4(out + 4 * i, f32x4{x[0] / dn, x[1] / dn, x[2] / dn, x[3] / dn});
+    }
 }
 
 // One wave per row t:

@@ -47,6 +47,10 @@ struct LaLaunches {
     hipError_t (*decay_grad)(const DecayGradParams &, hipStream_t);
 };
 bool lookup_la(int dtype, int d, LaLaunches *out);
+// out[t][:] = num[t][:] / den[t][0] over rows of d fp32 values; out is bf16
+// (to_bf16) or fp32
+hipError_t launch_divide_rows(const float *num, const float *den, void *out, long rows, int d,
+                              bool to_bf16, hipStream_t s);
 // bf16 -> fp32 (to_f32) or fp32 -> bf16 copy of count values (a multiple of 4)
 hipError_t launch_convert(const void *src, void *dst, long count, bool to_f32, hipStream_t s);
 

@@ -102,8 +102,10 @@ struct LaParams {
     int seg_len;        // tokens per segment, a multiple of the chunk
     int nseg;
     int reverse;        // run the sequence backwards (anti-causal pass)
-    const float *state_in;   // [BH][D*D] state before token 0 (forward passes, decay 1), or null
-    float *state_out;        // [BH][D*D] state after token n-1 (forward passes, decay 1), or null
+    const float *state_in;   // head bh's D*D state before token 0 at state_in + bh*state_stride, or null
+    float *state_out;        // the state after token n-1, same layout, or null
+    float *state_out2;       // a second copy of it, same layout, or null
+    long state_stride;       // floats between heads' states (0: D*D)
     float gamma[kMaxDecayHeads];   // decay of head h for this pass
 };
 

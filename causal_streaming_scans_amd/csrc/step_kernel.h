@@ -11,9 +11,11 @@
 // AHLA : P <- g P + k v^T ; y = P^T q ; E <- g E + k y^T ; mK <- g mK + k ;
 //        nk <- g nk + k (q . mK) ; o = q^T E  (ratio: / q^T nk)
 //        (every summary decays by g per token; g = 1 without a decay)
-// HLA3 : P <- P + k v^T ; y = P^T q ; then the HLA-2 step on (q, k, y)
-//        without decay (section "3. HLA de Tercer Orden": the third-order
-//        operator read as tril(L L^T) L V; P^KV is the moment it adds)
+// HLA3 : P <- g P + k v^T ; y = P^T q ; S <- g S + k k^T ; z = S q ;
+//        W <- g^3 W + z y^T ; o = q^T W  (hla3_step_kernel; section "3. HLA de
+//        Tercer Orden": the third-order operator read as tril(L L^T) L V, every
+//        moment decayed by g per token; the ratio form runs the same step on
+//        unit values (1, 0, ..., 0) in its second state block and divides)
 //
 // One workgroup of NT threads per (b,h).  The state is read once and written
 // once (fp32, row-major), with consecutive threads on consecutive columns so
@@ -28,7 +30,8 @@ namespace hla {
 
 template <typename T, int D, int DV, int MODE, int NT>
 __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
-    constexpr bool AHLA = MODE == kStepAhla, HLA3 = MODE == kStepHla3;
+    constexpr bool AHLA = MODE == kStepAhla;
+    static_assert(MODE != kStepHla3, "third order: hla3_step_kernel");
     constexpr int RG = NT / DV;     // row groups of the column-parallel passes
     constexpr int RPT = D / RG;     // rows per thread in those passes
     constexpr int TPR = NT / D;     // threads per row of the S pass (HLA-2)
@@ -40,16 +43,14 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
 
     const int bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const float g = MODE != kStepHla3 ? p.gamma[gamma_slot(bh, p.H)] : 1.f;
+    const float g = p.gamma[gamma_slot(bh, p.H)];
     const float g2 = g * g;
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
     constexpr int STF = AHLA ? ahla_state_floats(D, DV) : hla2_state_floats(D, DV);
-    // third order: the P^KV blocks of all heads, then their second-order states
-    float *st = HLA3 ? p.state + (size_t)p.BH * D * DV + (size_t)bh * STF
-                     : p.state + (size_t)bh * STF;
+    float *st = p.state + (size_t)bh * STF;
     const int col = tid % DV, rg = tid / DV;
 
     auto block_sum = [&](float x) -> float {
@@ -66,42 +67,15 @@ __global__ __launch_bounds__(NT) void step_kernel(StepParams p) {
     if (!AHLA) {
         float *S = st, *W = st + D * D, *u = st + D * D + D * DV;
         const int row = tid / TPR, sub = tid % TPR;
-        float sv_[CPT], wv[RPT], uv = 0.f, pv[HLA3 ? RPT : 1];
-        float *P = p.state + (size_t)bh * D * DV;   // HLA3 only
+        float sv_[CPT], wv[RPT], uv = 0.f;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) sv_[i] = S[row * D + sub + i * TPR];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) wv[i] = W[(rg + i * RG) * DV + col];
-        if constexpr (HLA3) {
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) pv[i] = P[(rg + i * RG) * DV + col];
-        }
         if (tid < D) uv = u[tid];
         for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
         for (int j = tid; j < DV; j += NT) sv[j] = to_f(v[j]);
         __syncthreads();
-        if constexpr (HLA3) {
-            // P <- P + k v^T ; y = P^T q, which then stands in for v
-            float yp = 0.f;
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const int r = rg + i * RG;
-                const float pn = pv[i] + sk[r] * sv[col];
-                P[r * DV + col] = pn;
-                yp += sq[r] * pn;
-            }
-            part[rg][col] = yp;
-            __syncthreads();
-            if (tid < DV) {
-                float y = 0.f;
-#pragma unroll
-                for (int i = 0; i < RG; ++i) y += part[i][tid];
-                sy[tid] = y;
-            }
-            __syncthreads();
-            for (int j = tid; j < DV; j += NT) sv[j] = sy[j];
-            __syncthreads();
-        }
         // S <- g S + k k^T ; z = S q
         float zp = 0.f;
 #pragma unroll
@@ -302,6 +276,110 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
         for (int i = 0; i < RG; ++i) s += part[i][tid];
         o[slice * SW + tid] = from_f<T>(s);
     }
+}
+
+}  // namespace hla
+
+namespace hla {
+
+// Third-order step, one workgroup per (b,h): for each chain (the values v;
+// for the ratio form also the unit values (1, 0, ..., 0), whose state block
+// follows the first one)
+//   P <- g P + k v^T ; y = P^T q ; S <- g S + k k^T ; z = S q ;
+//   W <- g^3 W + z y^T ; o = q^T W
+// and the ratio form divides the first chain's o by the second's o[0].  The
+// u part of each second-order block is not used by third order.
+template <typename T, int D, int DV, int NT>
+__global__ __launch_bounds__(NT) void hla3_step_kernel(StepParams p) {
+    constexpr int RG = NT / DV;     // row groups of the column-parallel passes
+    constexpr int RPT = D / RG;     // rows per thread in those passes
+    constexpr int TPR = NT / D;     // threads per row of the S pass
+    constexpr int CPT = D / TPR;    // S columns per thread
+    static_assert(NT % DV == 0 && NT % D == 0 && D % RG == 0 && D % TPR == 0, "block shape");
+    __shared__ float sq[D], sk[D], sv[DV], sz[D], sy[DV];
+    __shared__ float part[RG][DV];
+    __shared__ float sden;
+
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float g = p.gamma[gamma_slot(bh, p.H)];
+    const float g3 = g * g * g;
+    const T *q = static_cast<const T *>(p.q) + (size_t)bh * D;
+    const T *k = static_cast<const T *>(p.k) + (size_t)bh * D;
+    const T *v = static_cast<const T *>(p.v) + (size_t)bh * DV;
+    T *o = static_cast<T *>(p.o) + (size_t)bh * DV;
+    const size_t chain_floats = (size_t)p.BH * hla3_state_floats(D, DV);
+    const int col = tid % DV, rg = tid / DV;
+    const int row = tid / TPR, sub = tid % TPR;
+
+    for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
+    float onum = 0.f;
+    const int nchain = p.ratio ? 2 : 1;
+    for (int chain = 0; chain < nchain; ++chain) {
+        float *P = p.state + chain * chain_floats + (size_t)bh * D * DV;
+        float *S = p.state + chain * chain_floats + (size_t)p.BH * D * DV +
+                   (size_t)bh * hla2_state_floats(D, DV);
+        float *W = S + D * D;
+        float pv[RPT], wv[RPT], svv[CPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            pv[i] = P[(rg + i * RG) * DV + col];
+            wv[i] = W[(rg + i * RG) * DV + col];
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) svv[i] = S[row * D + sub + i * TPR];
+        for (int j = tid; j < DV; j += NT) sv[j] = chain == 0 ? to_f(v[j]) : (j == 0 ? 1.f : 0.f);
+        __syncthreads();
+        // P <- g P + k v^T ; partial y = P^T q
+        float yp = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float pn = g * pv[i] + sk[r] * sv[col];
+            P[r * DV + col] = pn;
+            yp += sq[r] * pn;
+        }
+        part[rg][col] = yp;
+        // S <- g S + k k^T ; z = S q
+        float zp = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = sub + i * TPR;
+            const float sn = g * svv[i] + sk[row] * sk[c];
+            S[row * D + c] = sn;
+            zp += sn * sq[c];
+        }
+        for (int m = TPR / 2; m >= 1; m >>= 1) zp += __shfl_xor(zp, m, TPR);
+        if (sub == 0) sz[row] = zp;
+        __syncthreads();
+        if (tid < DV) {
+            float y = 0.f;
+#pragma unroll
+            for (int i = 0; i < RG; ++i) y += part[i][tid];
+            sy[tid] = y;
+        }
+        __syncthreads();
+        // W <- g^3 W + z y^T ; partial o = q^T W
+        float op = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            const float wn = g3 * wv[i] + sz[r] * sy[col];
+            W[r * DV + col] = wn;
+            op += sq[r] * wn;
+        }
+        part[rg][col] = op;
+        __syncthreads();
+        if (tid < DV) {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < RG; ++i) s += part[i][tid];
+            if (chain == 0) onum = s;
+            else if (tid == 0) sden = s;
+        }
+        __syncthreads();   // part, sv reused by the next chain; sden published
+    }
+    if (tid < DV) o[tid] = from_f<T>(p.ratio ? onum / sden : onum);
 }
 
 }  // namespace hla

@@ -25,10 +25,16 @@
  *   HLA_AHLA_RATIO  the AHLA numerator over the same sum with v == 1
  *   HLA_HLA3        third order (section "3. HLA de Tercer Orden": the product
  *                   A A^T A made strictly causal), read as o = tril(L L^T) L V:
- *                   o_t = sum_{m<=t} sum_{i<=m} sum_{j<=m} A[t,i] A[m,i] A[m,j] v_j.
- *                   Computed as the second-order operator on the values
- *                   Y = L V (one chunked first-order pass into the workspace);
- *                   no decay, no ratio form
+ *                   o_t = sum_{m<=t} sum_{i<=m} sum_{j<=m}
+ *                         g^((t-i)+(t-m)+(t-j)) A[t,i] A[m,i] A[m,j] v_j.
+ *                   Without a decay: the second-order operator on the values
+ *                   Y = L V (one chunked first-order pass into the workspace,
+ *                   then the three second-order stages).  With a decay: three
+ *                   chained first-order passes, Y = LA_g(Q, K, V),
+ *                   Z = LA_g(Q, K, K), o = LA_{g^3}(Q, Z, Y), all in stage 3
+ *   HLA_HLA3_RATIO  the HLA_HLA3 numerator over the same sum with v == 1: the
+ *                   chain above and its twin on unit values, in fp32 (bf16
+ *                   inputs on widened copies), divided row by row
  * g is the per-head decay (1 when gamma is NULL).  Decay reading ("Contribuciones
  * Clave", item 2, names masked operators with and without exponential decay):
  * every streaming summary of the variant decays by g per token, hence the
@@ -44,7 +50,10 @@
  *     AHLA  : [ P (d*dv) | E (d*dv) | mK (d) | nk (d) ]  the page's P^KV, E, m^K, n
  *     HLA3  : not per (b,h) blocks: first the P^KV (d*dv) of every (b,h), then
  *             every (b,h)'s HLA-2 block [ S | W | u ] of (q, k, y), y = P^T q
- *             (hla_state_floats() = d*dv + d*d + d*dv + d per (b,h))
+ *             (hla_state_floats() = d*dv + d*d + d*dv + d per (b,h)); with a
+ *             decay W = sum g^(3(t-m)) z_m y_m^T, and u is unused (written 0)
+ *     HLA3_RATIO: the HLA3 layout twice: the chain on v, then the chain on
+ *             unit values (1, 0, ..., 0) (hla_state_floats() = 2 x HLA3's)
  *
  * Ownership: the caller allocates and owns every buffer, including the
  * workspace.  The library allocates no memory, keeps no mutable global state,
@@ -87,7 +96,8 @@ typedef enum {
     HLA_HLA2_RATIO = 1,
     HLA_AHLA = 2,
     HLA_AHLA_RATIO = 3,
-    HLA_HLA3 = 4
+    HLA_HLA3 = 4,
+    HLA_HLA3_RATIO = 5
 } hla_variant;
 
 /* Largest H for which a per-head decay can be given (it travels in the kernel

@@ -105,7 +105,6 @@ def test_forward_validation_errors(lib):
     assert _fwd(lib, fake, fake, fake, fake, chunk=128) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, dtype=F32, d=128, dv=128, chunk=16) == ERR_UNSUP
     # decay: not for third order; gamma must lie in (0, 1]; H bounded
-    assert _fwd(lib, fake, fake, fake, fake, variant=4, gamma=[0.9]) == ERR_UNSUP
     assert _fwd(lib, fake, fake, fake, fake, variant=AHLA, gamma=[1.5]) == ERR_ARG
     assert _fwd(lib, fake, fake, fake, fake, gamma=[0.0]) == ERR_ARG
     assert _fwd(lib, fake, fake, fake, fake, gamma=[1.5]) == ERR_ARG
@@ -152,7 +151,6 @@ def test_step_validation_errors(lib):
     assert step(st=None) == ERR_NULL
     assert step(B=0) == ERR_SHAPE
     assert step(d=24, dv=24) == ERR_UNSUP
-    assert step(variant=4, gamma=[0.5]) == ERR_UNSUP
     assert step(variant=AHLA_RATIO, gamma=[1.5]) == ERR_ARG
     assert step(gamma=[-0.5]) == ERR_ARG
     assert step(dtype=3) == ERR_ARG
@@ -235,27 +233,35 @@ def test_backward_validation(lib):
 
 # ---------------------------------------------------------------- third order
 
-HLA3 = 4
+HLA3, HLA3_RATIO = 4, 5
 
 
 def test_hla3_sizes_and_validation(lib):
-    # P^KV per head, then the second-order state of (q, k, y)
-    assert lib.hla_state_floats(HLA3, 64, 64) == 64 * 64 + (64 * 64 + 64 * 64 + 64)
+    # P^KV per head, then the second-order state of (q, k, y); the ratio form
+    # has that layout twice (the chain on v, then on unit values)
+    one = 64 * 64 + (64 * 64 + 64 * 64 + 64)
+    assert lib.hla_state_floats(HLA3, 64, 64) == one
+    assert lib.hla_state_floats(HLA3_RATIO, 64, 64) == 2 * one
     B, H, n, d, chunk, seg = 2, 4, 1000, 64, 64, 4
     nseg = -(-n // (chunk * seg))
     scan = 2 * B * H * (nseg - 1) * (d * d + 2 * d * d + 2 * d) * 4
     g = lib.hla_backward_default_seg_chunks(B, H, n)
     nseg_la = -(-n // (64 * g))
-    want = scan + B * H * n * d * 4 + B * H * (nseg_la - 1) * d * d * 4
-    assert hla.workspace_bytes("hla3", B, H, n, d, d, chunk, seg) == want
+    sums = B * H * (nseg_la - 1) * d * d * 4
+    tensor = B * H * n * d * 4
+    assert hla.workspace_bytes("hla3", B, H, n, d, d, chunk, seg) == scan + sums + 2 * tensor
+    assert hla.workspace_bytes("hla3_ratio", B, H, n, d, d, chunk, seg) == scan + sums + 9 * tensor
     P = ctypes.c_void_p
     g2 = (ctypes.c_float * H)(*([0.9] * H))
-    fwd = lambda **kw: lib.hla_forward(P(1), P(1), P(1), P(1), B, H, n, d, d, BF16, HLA3,
-                                       kw.get("gamma"), chunk, seg, kw.get("si"), kw.get("so"),
-                                       P(1), kw.get("ws", 1), None)
-    assert fwd(gamma=g2) == ERR_UNSUP                       # no decay for third order
+    fwd = lambda **kw: lib.hla_forward(P(1), P(1), P(1), P(1), B, H, n, d, d, BF16,
+                                       kw.get("variant", HLA3), kw.get("gamma"), chunk, seg,
+                                       kw.get("si"), kw.get("so"), P(1), kw.get("ws", 1), None)
     assert fwd(ws=16) == ERR_WS
-    assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, g2, P(1), None) == ERR_UNSUP
+    assert fwd(gamma=g2, ws=16) == ERR_WS
+    assert fwd(variant=HLA3_RATIO, ws=16) == ERR_WS
+    bad = (ctypes.c_float * H)(*([1.5] * H))
+    assert fwd(gamma=bad) == ERR_ARG
+    assert lib.hla_step(P(1), P(1), P(1), P(1), B, H, d, d, BF16, HLA3, bad, P(1), None) == ERR_ARG
 
 
 def test_binding_fails_loudly_without_the_library():

@@ -122,3 +122,103 @@ def test_hla3_stages_equal_whole():
                               out=out, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out, whole)
+
+
+# ------------------------------------------------- decay and the ratio form
+
+CHAIN_CASES = [
+    # dtype, variant, d, n, H, decay
+    ("f32", "hla3", 16, 200, 2, True),
+    ("f32", "hla3_ratio", 32, 130, 2, False),
+    ("f32", "hla3_ratio", 64, 257, 2, True),
+    ("bf16", "hla3", 64, 450, 3, True),
+    ("bf16", "hla3", 128, 300, 2, True),
+    ("bf16", "hla3_ratio", 64, 333, 2, False),
+    ("bf16", "hla3_ratio", 64, 700, 2, True),
+    ("bf16", "hla3_ratio", 128, 200, 2, True),
+    ("bf16", "hla3", 32, 65, 2, True),
+]
+
+
+def run_chain(x, B, H, dtype, variant, gamma, state_in=None, state_out=None):
+    import torch
+    import causal_streaming_scans_amd as hla
+    n, d = x["q"].shape[1], x["q"].shape[2]
+    shp = (B, H, n, d)
+    o = hla.hla_forward(*(to_dev(x[a], dtype, shp) for a in "qkv"), variant=variant, gamma=gamma,
+                        state_in=state_in, state_out=state_out)
+    torch.cuda.synchronize()
+    return from_dev(o).reshape(B * H, n, d)
+
+
+@pytest.mark.parametrize("dtype,variant,d,n,H,decay", CHAIN_CASES)
+def test_hla3_decay_and_ratio(dtype, variant, d, n, H, decay):
+    """Third order with per-head decays (every moment decays by g per token)
+    and its ratio form, through the chained first-order passes."""
+    say(f"[third order] {variant} dtype {dtype} d {d} n {n} H {H} decay {decay}")
+    B = 2
+    ratio = variant == "hla3_ratio"
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos" if ratio else "l2norm",
+                      seed=1600 + d + n, decay=decay)
+    got = run_chain(x, B, H, dtype, variant, x["gamma"])
+    want = T3.hla3_batched(x["q"], x["k"], x["v"], H=H, gamma=x["gamma"], ratio=ratio)
+    e = rel_l2(got, want)
+    say(f"  rel_l2 {e:.3e}")
+    assert e < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,variant,d", [("f32", "hla3", 32), ("bf16", "hla3", 64),
+                                             ("bf16", "hla3_ratio", 64), ("f32", "hla3_ratio", 16),
+                                             ("bf16", "hla3", 128)])
+def test_hla3_decay_resume_and_decode(dtype, variant, d):
+    """With a decay: forward over n1 tokens with state_out, a resumed forward
+    over n2 tokens, then decode steps, each against the oracle on the whole
+    sequence (the state carries P, S and W for each chain)."""
+    import numpy as np
+    import torch
+    import causal_streaming_scans_amd as hla
+    B, H, n1, n2, T = 1, 3, 190, 141, 4
+    n = n1 + n2 + T
+    ratio = variant == "hla3_ratio"
+    say(f"[third order] resume + decode {variant} {dtype} d {d} n1 {n1} n2 {n2} steps {T}")
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos" if ratio else "l2norm",
+                      seed=1700 + d, decay=True)
+    g = x["gamma"]
+    want = T3.hla3_batched(x["q"], x["k"], x["v"], H=H, gamma=g, ratio=ratio)
+    stf = hla.state_floats(variant, d, d)
+    st1 = torch.empty(B * H * stf, dtype=torch.float32, device="cuda")
+    st2 = torch.empty_like(st1)
+
+    def part(a, b):
+        return {key: np.ascontiguousarray(x[key][:, a:b]) for key in ("q", "k", "v")}
+
+    got1 = run_chain(part(0, n1), B, H, dtype, variant, g, state_out=st1)
+    got2 = run_chain(part(n1, n1 + n2), B, H, dtype, variant, g, state_in=st1, state_out=st2)
+    outs = []
+    for t in range(n1 + n2, n):
+        qt, kt, vt = (to_dev(np.ascontiguousarray(x[key][:, t]), dtype, (B, H, d))
+                      for key in ("q", "k", "v"))
+        outs.append(hla.hla_step(qt, kt, vt, st2, variant=variant, gamma=g))
+    torch.cuda.synchronize()
+    got3 = np.stack([from_dev(o).reshape(B * H, d) for o in outs], axis=1)
+    for label, gg, w in (("first", got1, want[:, :n1]), ("resumed", got2, want[:, n1:n1 + n2]),
+                         ("decode", got3, want[:, n1 + n2:])):
+        e = rel_l2(gg, w)
+        say(f"  {label}: rel_l2 {e:.3e}")
+        assert e < TOL[dtype], (label, e)
+
+
+def test_hla3_ratio_n2048_sampled_heads():
+    """The ratio form with decays g_h ~ U[0.95, 0.999] at the HLA-2 workload's
+    shape (B=4 H=8 n=2048 d=dv=64 bf16, q, k ~ U[0,1)/sqrt(d)); the oracle on
+    the first and last head."""
+    w = I.WORKLOADS["hla2_n2048"]
+    say("[third order] ratio with decay, B=4 H=8 n=2048 d=64 bf16")
+    x = I.make_inputs(w.B, w.H, w.n, w.d, w.dv, dtype="bf16", dist="uniform_pos", seed=1801,
+                      decay=True)
+    got = run_chain(x, w.B, w.H, "bf16", "hla3_ratio", x["gamma"])
+    heads = [0, w.B * w.H - 1]
+    want = T3.hla3_batched(x["q"], x["k"], x["v"], heads=heads, H=w.H, gamma=x["gamma"], ratio=True)
+    e = rel_l2(got[heads], want)
+    say(f"  rel_l2 {e:.3e}")
+    assert e < TOL["bf16"]
