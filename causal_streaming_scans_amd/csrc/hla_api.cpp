@@ -117,7 +117,8 @@ struct Grads {
 
 struct BwdCtx {
     LaLaunches la;
-    LaParams p1, p2;        // decay g and g^2
+    LaParams p1, p2;        // decay g and g^2 (third order: g^3)
+    bool p3_cube;
     float *sums_kk, *sums;  // K K^T states (first and last pass), the rest
     char *ws;
     size_t sums_bytes, tensor_bytes;
@@ -257,6 +258,82 @@ hla_status backward_ahla_ratio(const BwdCtx &c, const Grads &x) {
         {&c.p1, dY1, ONE1, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
     };
     return c.run_all(post, 8);
+}
+
+// Third order: Y = LA_g(Q, K, V), Z = LA_g(Q, K, K), O = LA_{g^3}(Q, Z, Y)
+// (p1 carries g, p2 here g^3).  The ratio form adds the unit-value chain
+// Y1 = LA_g(Q, K, ONE1), DEN = LA_{g^3}(Q, Z, Y1), o = O / DEN[:, 0]: its
+// upstream is G = dO / den on O and E1 = (e, 0, ..., 0) on DEN.  Through O:
+// dQ = LA(G, Y, Z), dZ = RLA(Y, G, Q), dY = RLA(Z, Q, G) (dZ and dY one DUAL
+// pass), and the same with E1 and Y1 for DEN; through Z: dK = RLA(K, dZ, Q) +
+// RLA(K, Q, dZ) (SYM), dQ += LA(dZ, K, K); through Y: dQ += LA(dY, V, K),
+// dV = RLA(K, Q, dY) and dK += RLA(V, dY, Q) (DUAL); through Y1:
+// dQ += LA(dY1, ONE1, K), dK += RLA(ONE1, dY1, Q).  Tensors: Y, Z, dZ, dY
+// and for the ratio form G, E1, ONE1, Y1, dY1, NUM, DEN, a spare.
+hla_status backward_hla3(const BwdCtx &c, const Grads &x, bool ratio) {
+    void *Y = c.tensor(0), *Z = c.tensor(1), *dZ = c.tensor(2), *dY = c.tensor(3);
+    const Pass fwd[2] = {
+        {&c.p1, x.q, x.k, x.v, nullptr, Y, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        {&c.p1, x.q, x.k, x.k, nullptr, Z, 0, PLAIN, c.sums_kk, true, nullptr, nullptr, nullptr},
+    };
+    hla_status st = c.run_all(fwd, 2);
+    if (st != HLA_OK) return st;
+    const void *up = x.dout;
+    void *G = nullptr, *E1 = nullptr, *ONE1 = nullptr, *Y1 = nullptr, *dY1 = nullptr;
+    if (ratio) {
+        G = c.tensor(4);
+        E1 = c.tensor(5);
+        ONE1 = c.tensor(6);
+        Y1 = c.tensor(7);
+        dY1 = c.tensor(8);
+        void *NUM = c.tensor(9), *DEN = c.tensor(10), *spare = c.tensor(11);
+        if (c.la.unit_column(ONE1, c.rows, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+        const Pass pre[3] = {
+            {&c.p1, x.q, x.k, ONE1, nullptr, Y1, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+            {&c.p2, x.q, Z, Y, nullptr, NUM, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+            {&c.p2, x.q, Z, Y1, nullptr, DEN, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        };
+        st = c.run_all(pre, 3);
+        if (st != HLA_OK) return st;
+        // den = ONE1 . DEN (its first column); the e u output is not used here
+        const RatioPrepParams rp{ONE1, DEN, NUM, x.dout, G, E1, spare, c.rows};
+        if (c.la.ratio_prep(rp, c.s) != hipSuccess) return HLA_ERR_DEVICE;
+        up = G;
+    }
+    const Pass through_o[2] = {
+        // dQ = LA(G, Y, Z)
+        {&c.p2, up, Y, Z, nullptr, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dZ = RLA(Y, G, Q) and dY = RLA(Z, Q, G)
+        {&c.p2, Y, up, x.q, nullptr, dZ, 1, DUAL, c.sums, true, Z, dY, nullptr},
+    };
+    st = c.run_all(through_o, 2);
+    if (st != HLA_OK) return st;
+    if (ratio) {
+        const Pass through_den[2] = {
+            {&c.p2, E1, Y1, Z, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+            {&c.p2, Y1, E1, x.q, dZ, dZ, 1, DUAL, c.sums, true, Z, dY1, nullptr},
+        };
+        st = c.run_all(through_den, 2);
+        if (st != HLA_OK) return st;
+    }
+    const Pass rest[4] = {
+        // dK = RLA(K, dZ, Q) + RLA(K, Q, dZ)
+        {&c.p1, x.k, dZ, x.q, nullptr, x.dk, 1, SYM, c.sums, true, nullptr, nullptr, nullptr},
+        // dQ += LA(dZ, K, K), with the segment states of the Z pass
+        {&c.p1, dZ, x.k, x.k, x.dq, x.dq, 0, PLAIN, c.sums_kk, false, nullptr, nullptr, nullptr},
+        // dQ += LA(dY, V, K)
+        {&c.p1, dY, x.v, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        // dV = RLA(K, Q, dY) and dK += RLA(V, dY, Q)
+        {&c.p1, x.k, x.q, dY, nullptr, x.dv, 1, DUAL, c.sums, true, x.v, x.dk, x.dk},
+    };
+    st = c.run_all(rest, 4);
+    if (st != HLA_OK || !ratio) return st;
+    const Pass unit[2] = {
+        // dQ += LA(dY1, ONE1, K) ; dK += RLA(ONE1, dY1, Q)
+        {&c.p1, dY1, ONE1, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+        {&c.p1, ONE1, dY1, x.q, x.dk, x.dk, 1, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
+    };
+    return c.run_all(unit, 2);
 }
 
 // dL/dg_h from the tensors the HLA-2 passes leave behind (DecayGradParams):
@@ -648,7 +725,13 @@ static bool fp32_passes(int variant, bool with_dgamma) {
 // and the unit rows (1, 0, ..., 0); fp32 passes on bf16 inputs run on
 // widened copies of q, k, v, dO and fp32 gradients (seven more)
 static int own_tensors(int variant) {
-    return variant == HLA_AHLA_RATIO ? 7 : is_ratio(variant) ? 5 : 2;   // AHLA adds Y1, dY1
+    switch (variant) {
+        case HLA_HLA2_RATIO: return 5;
+        case HLA_AHLA_RATIO: return 7;    // AHLA adds Y1, dY1
+        case HLA_HLA3: return 4;
+        case HLA_HLA3_RATIO: return 12;
+        default: return 2;
+    }
 }
 static int backward_tensors(int variant, int dtype, bool with_dgamma) {
     const int own = own_tensors(variant);
@@ -657,10 +740,7 @@ static int backward_tensors(int variant, int dtype, bool with_dgamma) {
 static size_t backward_elem_bytes(int variant, int dtype, bool with_dgamma) {
     return (fp32_passes(variant, with_dgamma) || dtype == HLA_F32) ? 4 : 2;
 }
-static bool has_backward(int variant) {
-    return variant == HLA_HLA2 || variant == HLA_HLA2_RATIO || variant == HLA_AHLA ||
-           variant == HLA_AHLA_RATIO;
-}
+static bool has_backward(int variant) { return valid_variant(variant); }
 // fp64 partial sums of the decay gradient, after the tensors (HLA-2 forms)
 static size_t decay_grad_bytes(int variant, int B, int H) {
     const bool hla2 = variant == HLA_HLA2 || variant == HLA_HLA2_RATIO;
@@ -693,11 +773,12 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     if (seg_chunks < 0) return HLA_ERR_ARG;
     if (!has_backward(variant) || d != dv) return HLA_ERR_UNSUPPORTED;
     // the decay gradient's identity is written for the HLA-2 chain
-    if (dgamma && is_ahla(variant)) return HLA_ERR_UNSUPPORTED;
+    if (dgamma && (is_ahla(variant) || is_hla3(variant))) return HLA_ERR_UNSUPPORTED;
     const bool dg = dgamma != nullptr;
     const bool fp32run = fp32_passes(variant, dg);
     const int run_dtype = fp32run ? HLA_F32 : dtype;
     BwdCtx c;
+    c.p3_cube = is_hla3(variant);
     if (!lookup_la(run_dtype, d, &c.la)) return HLA_ERR_UNSUPPORTED;
     if (n == 0) {
         if (!dgamma) return HLA_OK;
@@ -737,8 +818,9 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     c.p1.seg_len = kLaChunk * g;
     c.p1.nseg = (int)nseg;
     fill_gamma(c.p1.gamma, gamma_host, H);
-    c.p2 = c.p1;                      // decay g^2
-    for (int h = 0; h < kMaxDecayHeads; ++h) c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h];
+    c.p2 = c.p1;                      // decay g^2 (third order: g^3)
+    for (int h = 0; h < kMaxDecayHeads; ++h)
+        c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h] * (c.p3_cube ? c.p1.gamma[h] : 1.f);
 
     Grads io{q, k, v, dout, dq, dk, dv_out};
     void *partial = c.tensor(backward_tensors(variant, dtype, dg));
@@ -764,7 +846,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
         case HLA_HLA2: st = backward_hla2(c, run); break;
         case HLA_AHLA: st = backward_ahla(c, run); break;
         case HLA_HLA2_RATIO: st = backward_hla2_ratio(c, run); break;
-        default: st = backward_ahla_ratio(c, run); break;
+        case HLA_AHLA_RATIO: st = backward_ahla_ratio(c, run); break;
+        default: st = backward_hla3(c, run, variant == HLA_HLA3_RATIO); break;
     }
     if (st == HLA_OK && dgamma) st = decay_gradient(c, run, H, n, d, dgamma, partial);
     if (st != HLA_OK || !widen) return st;

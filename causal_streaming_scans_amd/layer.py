@@ -13,11 +13,12 @@ into PyTorch autograd:
   projection.  The four projections are plain GEMMs (torch, i.e. the ROCm
   BLAS libraries); every step of the operator itself runs in the library.
 
-Variants with a backward: "hla2" (optional per-head decay), "hla2_ratio",
-"ahla".  Inputs are bf16 or fp32 GPU tensors; d == dv.  A decay given as a
-tensor that requires grad receives dL/dgamma (HLA-2 forms; the library's
-decay gradient, summed over the batch); the library accepts decays in
-(0, 1] only, so a learned decay must be kept in that range by its owner.
+Every variant has a backward ("hla2", "hla2_ratio", "ahla", "ahla_ratio",
+"hla3", "hla3_ratio"), each with an optional per-head decay.  Inputs are
+bf16 or fp32 GPU tensors; d == dv.  A decay given as a tensor that requires
+grad receives dL/dgamma (HLA-2 forms only; the library's decay gradient,
+summed over the batch); the library accepts decays in (0, 1] only, so a
+learned decay must be kept in that range by its owner.
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ import torch
 
 from . import hla_backward, hla_forward
 
-_BACKWARD_VARIANTS = ("hla2", "hla2_ratio", "ahla")
+_BACKWARD_VARIANTS = ("hla2", "hla2_ratio", "ahla", "ahla_ratio", "hla3", "hla3_ratio")
 
 
 class HLAFunction(torch.autograd.Function):

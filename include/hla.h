@@ -287,11 +287,13 @@ hla_status hla_step(const void *q, const void *k, const void *v, void *o,
  * Precision: bf16 operands, fp32 accumulation and fp32 carried states; Z and
  * dZ are kept in dtype; the ratio forms, and every form when dgamma is
  * given, run every pass in fp32 (for bf16 inputs on widened copies).
- * Supported: HLA_HLA2, HLA_HLA2_RATIO, HLA_AHLA, HLA_AHLA_RATIO, each with or
- * without a decay (HLA_HLA3: HLA_ERR_UNSUPPORTED; the ratio forms need
+ * Supported: every variant, with or without a decay (the ratio forms need
  * nonzero denominators, as the forward), d == dv in {16, 32, 64, 128}, both
  * dtypes.  With a decay, AHLA is LA_g(Q, K, LA_g(Q, K, V)) and its passes
- * carry g.  Errors as hla_forward.
+ * carry g.  Third order is Y = LA_g(Q, K, V), Z = LA_g(Q, K, K),
+ * O = LA_{g^3}(Q, Z, Y): its gradient is eight passes (the ratio form, run
+ * in fp32, thirteen: the unit-value chain as well).  dgamma is for the HLA-2
+ * forms only.  Errors as hla_forward.
  */
 int hla_backward_default_seg_chunks(int B, int H, int n);
 size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int dv, int dtype,

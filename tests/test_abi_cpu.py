@@ -196,7 +196,11 @@ def test_backward_workspace_bytes(lib):
     assert hla.backward_workspace_bytes("hla2_ratio", B, H, n, d, d) == want_ratio + dg
     assert hla.backward_workspace_bytes("ahla_ratio", B, H, n, d, d) == \
         want_ratio + 2 * B * H * n * d * 4                   # Y1 and its gradient
-    assert hla.backward_workspace_bytes("hla3", B, H, n, d, d) == 0
+    # third order keeps Y, Z, dZ, dY; its ratio form twelve fp32 tensors, plus
+    # the seven widened copies and gradients for bf16 inputs
+    assert hla.backward_workspace_bytes("hla3", B, H, n, d, d) == want + 2 * B * H * n * d * 2
+    assert hla.backward_workspace_bytes("hla3_ratio", B, H, n, d, d) == \
+        want - 2 * B * H * n * d * 2 + 19 * B * H * n * d * 4
     assert hla.backward_workspace_bytes("ahla", B, H, n, d, d) == want
     # with the decay gradient every pass runs in fp32: the two tensors in fp32
     # and, for bf16 inputs, the seven widened copies and gradients
@@ -211,7 +215,8 @@ def test_backward_validation(lib):
     assert _bwd(lib, n=0) == OK                      # nothing to do, nothing enqueued
     assert _bwd(lib, variant=HLA2_RATIO, ws_bytes=1) == ERR_WS
     assert _bwd(lib, variant=AHLA_RATIO, ws_bytes=1) == ERR_WS
-    assert _bwd(lib, variant=4) == ERR_UNSUP                              # third order: forward only
+    assert _bwd(lib, variant=4, dgamma=1) == ERR_UNSUP                    # no third-order decay gradient
+    assert _bwd(lib, variant=6) == ERR_ARG
     assert _bwd(lib, variant=AHLA, dgamma=1) == ERR_UNSUP           # no AHLA decay gradient
     assert _bwd(lib, variant=AHLA_RATIO, dgamma=1) == ERR_UNSUP
     assert _bwd(lib, variant=AHLA, ws_bytes=1) == ERR_WS

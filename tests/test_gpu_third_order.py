@@ -222,3 +222,43 @@ def test_hla3_ratio_n2048_sampled_heads():
     e = rel_l2(got[heads], want)
     say(f"  rel_l2 {e:.3e}")
     assert e < TOL["bf16"]
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_CASES = [
+    # dtype, variant, d, n, H, decay, seg_chunks
+    ("f32", "hla3", 16, 200, 2, False, 1),
+    ("f32", "hla3", 32, 130, 2, True, 0),
+    ("f32", "hla3_ratio", 32, 150, 2, True, 1),
+    ("bf16", "hla3", 64, 450, 3, False, 2),
+    ("bf16", "hla3", 64, 333, 2, True, 1),
+    ("bf16", "hla3", 128, 300, 2, True, 1),
+    ("bf16", "hla3_ratio", 64, 300, 2, False, 1),
+    ("bf16", "hla3_ratio", 16, 257, 2, True, 0),
+    ("bf16", "hla3", 16, 65, 2, True, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,variant,d,n,H,decay,seg", BWD_CASES)
+def test_hla3_backward(dtype, variant, d, n, H, decay, seg):
+    """Gradients of the third-order operator (and its ratio form, with and
+    without decays) against the oracle's chain rule through its matrix form."""
+    import torch
+    import causal_streaming_scans_amd as hla
+    from oracle import third_order as T
+    say(f"[third order backward] {variant} {dtype} d {d} n {n} H {H} decay {decay} seg {seg}")
+    B = 1
+    ratio = variant == "hla3_ratio"
+    x = I.make_inputs(B, H, n, d, d, dtype=dtype, dist="uniform_pos" if ratio else "l2norm",
+                      seed=1900 + d + n, decay=decay)
+    do = I.make_upstream_grad(B * H, n, d, dtype, seed=1950 + n)
+    shp = (B, H, n, d)
+    got = hla.hla_backward(*(to_dev(x[a], dtype, shp) for a in "qkv"), to_dev(do, dtype, shp),
+                           variant=variant, gamma=x["gamma"], seg_chunks=seg)
+    torch.cuda.synchronize()
+    want = T.hla3_vjp_batched(x["q"], x["k"], x["v"], do, H=H, gamma=x["gamma"], ratio=ratio)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        e = rel_l2(from_dev(g).reshape(w.shape), w)
+        say(f"  {name}: rel_l2 {e:.3e}")
+        assert e < TOL[dtype], (name, e)
