@@ -443,16 +443,15 @@ struct Hla3Pass {
 // base + bh*d*dv, then the second-order block [S | W | u] at
 // base + BH*d*dv + bh*(d*d + d*dv + d); the ratio form's unit-value chain
 // repeats that layout after it.
-static const float *hla3_view(const float *base, int BH, int d, int part, int chain) {
+// (one function for both the input and the output state: the result is
+// handed back as writable, the caller keeps the input's constness)
+static float *hla3_view(const float *base, int BH, int d, int part, int chain) {
     if (!base) return nullptr;
     const size_t one = (size_t)BH * hla3_state_floats(d, d);
-    const float *b = base + (size_t)chain * one;
+    float *b = const_cast<float *>(base) + (size_t)chain * one;
     if (part == 0) return b;                                  // P
     b += (size_t)BH * d * d;
     return part == 1 ? b : b + (size_t)d * d;                 // S, W
-}
-static float *hla3_view(float *base, int BH, int d, int part, int chain) {
-    return const_cast<float *>(hla3_view(static_cast<const float *>(base), BH, d, part, chain));
 }
 
 // Third order with a decay or in the ratio form:
