@@ -15,6 +15,9 @@ Contents
                    combine, exclusive Blelloch scan) written out in fp64 NumPy.
 ``backward.py``    gradients (dq, dk, dv) of the masked operators: the chain
                    rule applied to the n x n matrix form, fp64 NumPy.
+``streaming_grad.py`` the same gradients as chains of causal linear
+                   attention and their token-by-token recurrences, O(n d^2)
+                   per head, for the long workloads; fp64 NumPy.
 ``third_order.py`` the masked third-order operator tril(L L^T) L V: loops,
                    matrix form and a serial recurrence, fp64 NumPy.
 ``unmasked.py``    the unmasked operators (A A^T) V and (A A) V: loops and

@@ -1,6 +1,7 @@
 """GPU parity of hla_backward (HLA-2 gradients dq, dk, dv) against the fp64
 oracle of oracle/backward.py -- the chain rule on the masked matrix form of
-the operator of "1. HLA de Segundo Orden" ("Resumen Tecnico: Atencion Lineal
+the operator (at n >= 16384 the same gradients in linear time,
+oracle/streaming_grad.py) of "1. HLA de Segundo Orden" ("Resumen Tecnico: Atencion Lineal
 de Orden Superior (HLA)", gist.science/es/paper/2510.27258), trained through
 the chunk-parallel form of "4. Entrenamiento Paralelo mediante Escaneos
 Asociativos".  Relative L2 per gradient: 1e-5 for fp32, 1e-2 for bf16 (the
@@ -10,6 +11,7 @@ import pytest
 
 import oracle
 from oracle import backward as BW
+from oracle import streaming_grad as SG
 from causal_streaming_scans_amd import inputs as I
 from hla_testlib import TOL, from_dev, rel_l2, say, to_dev
 
@@ -78,14 +80,16 @@ def test_backward_hla2_n2048_sampled_heads():
     check(tuple(g[heads] for g in got), want, w.dtype, "hla2_n2048 heads 0,31")
 
 
-def test_backward_decay_n16384_prefix_and_euler():
+def test_backward_decay_n16384_full_heads_prefix_and_euler():
     """The decay workload B=2 H=16 n=16384 d=dv=128 bf16 at full size.
     (1) With do zero from token m on, the gradient of tokens before m is that
     of the first m tokens alone (causality), which the oracle computes for
     two heads, and every token from m on gets an exact zero.  (2) With a
-    dense do, Euler's identity for an operator of degree 2 in q, 2 in k and
-    1 in v: <q, dq> = <k, dk> = 2 <do, o> and <v, dv> = <do, o>, with o from
-    the serial fp64 oracle."""
+    dense do, two whole heads (all 16384 tokens) element by element against
+    the oracle's linear-time chain rule, and Euler's identity for an
+    operator of degree 2 in q, 2 in k and 1 in v over every head:
+    <q, dq> = <k, dk> = 2 <do, o> and <v, dv> = <do, o>, with o from the
+    serial fp64 oracle."""
     w = I.WORKLOADS["decay_n16384"]
     say(f"[backward] workload {w.name}")
     x = I.workload_inputs("decay_n16384")
@@ -103,6 +107,9 @@ def test_backward_decay_n16384_prefix_and_euler():
     check(tuple(g[heads, :m] for g in got), want, w.dtype, "decay_n16384 prefix")
 
     got = run_backward(x, do, w.B, w.H, w.dtype, x["gamma"])
+    want = SG.hla2_vjp_streaming(*(x[key][heads] for key in ("q", "k", "v")), do[heads],
+                                 gamma=[x["gamma"][bh % w.H] for bh in heads], H=len(heads))
+    check(tuple(g[heads] for g in got), want, w.dtype, "decay_n16384 whole heads")
     o = oracle.hla2(x["q"], x["k"], x["v"], H=w.H, gamma=x["gamma"])
     ref = float(np.sum(do.astype(np.float64) * o))
     for name, xin, g, deg in (("q", x["q"], got[0], 2), ("k", x["k"], got[1], 2),
@@ -168,12 +175,14 @@ def test_ahla_backward_small(dtype, d, n, H, seg):
     check(got, want, dtype, f"ahla {dtype} d{d} n{n}")
 
 
-def test_ahla_backward_n65536_prefix_and_euler():
+def test_ahla_backward_n65536_full_heads_prefix_and_euler():
     """The AHLA workload B=1 H=32 n=65536 d=dv=64 bf16 at full size, in the
     default launch configuration: (1) do zero from token m on, the first m
     tokens against the oracle of the prefix on two heads, exact zeros after
-    it; (2) a dense do, Euler's identity for degree 2 in q, 2 in k, 1 in v,
-    with o from the serial fp64 oracle."""
+    it; (2) a dense do, two whole heads (all 65536 tokens) element by element
+    against the oracle's linear-time chain rule, and Euler's identity for
+    degree 2 in q, 2 in k, 1 in v over every head, with o from the serial
+    fp64 oracle."""
     w = I.WORKLOADS["ahla_n65536"]
     say(f"[ahla backward] workload {w.name}")
     x = I.workload_inputs("ahla_n65536", decode_tokens=0)
@@ -189,6 +198,8 @@ def test_ahla_backward_n65536_prefix_and_euler():
                                heads=heads)
     check(tuple(g[heads, :m] for g in got), want, w.dtype, "ahla_n65536 prefix")
     got = run_backward(x, do, w.B, w.H, w.dtype, variant="ahla")
+    want = SG.ahla_vjp_streaming(*(x[key][heads] for key in ("q", "k", "v")), do[heads])
+    check(tuple(g[heads] for g in got), want, w.dtype, "ahla_n65536 whole heads")
     o = oracle.ahla(x["q"], x["k"], x["v"])
     ref = float(np.sum(do.astype(np.float64) * o))
     for name, xin, g, deg in (("q", x["q"], got[0], 2), ("k", x["k"], got[1], 2),
