@@ -4,6 +4,7 @@
 
 #include "ahla_kernels.h"
 #include "hla2_kernels.h"
+#include "hla2_pipe.h"
 #include "launch.h"
 
 namespace hla {
@@ -33,6 +34,13 @@ template <typename T, int D, int C, bool DECAY>
 hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
     hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg * p.BH),
                        dim3(Hla2Cfg<T, D, D, C, DECAY>::NT), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int D, int C>
+hipError_t launch_hla2_forward_pipe(const FwdParams &p, hipStream_t s) {
+    hipLaunchKernelGGL((hla2_forward_pipe_kernel<T, D, D, C>), dim3(p.nseg * p.BH),
+                       dim3(Hla2Cfg<T, D, D, C, false>::NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -90,8 +98,12 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
         return false;
     }
     if constexpr (hla2_fits<T, D, C, false>()) {
-        *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
-                launch_hla2_forward<T, D, C, false>};
+        if constexpr (hla2_pipe_ok<T, D, D, C>())
+            *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
+                    launch_hla2_forward_pipe<T, D, C>};
+        else
+            *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
+                    launch_hla2_forward<T, D, C, false>};
         return true;
     }
     return false;
