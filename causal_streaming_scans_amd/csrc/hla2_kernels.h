@@ -222,10 +222,12 @@ __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T
 
 // a-6: fold the up-sweep nodes covering segments 0 .. seg-1 (seg > 0) into
 // the state tiles acc that plan P gives wave w; lds_f is the fp32 staging
-// area of the cross factors.  Shared by the forward kernels.
+// area of the cross factors.  The same steps as the fold written out in
+// hla2_forward_kernel (kept inline there: at d = 128 the compiler allocates
+// registers for the call form with more spills).
 template <typename T, int D, int DV, int C, bool DECAY, typename P>
 __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int seg, float g, int w,
-                                                 f32x4 *acc, float *lds_f) {
+                                                 f32x4 (&acc)[P::NA], float *lds_f) {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     constexpr int NT = G::NT;
     using O = SumOfs<D, DV>;
@@ -377,7 +379,80 @@ void hla2_forward_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[j][i] = (u0 && col == 0) ? u0[16 * ti + g4 + i] : 0.f;
         });
-        if (seg > 0) hla2_fold_prefix<T, D, DV, C, DECAY, P>(p, bh, seg, g, w, acc, lds.f);
+        if (seg > 0) {
+            // fold node B (later) into the running state A: W <- a^2 W + N_B +
+            // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
+            // the node's [Y | y] are staged in LDS (fp32) as the cross factors
+            using L = CrossLds<D, DV>;  // fold: whole right factor
+            float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
+            int done = 0;
+            for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
+                if (!((seg >> b) & 1)) continue;
+                const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
+                const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
+                // with no caller state the first node folds into zero: no cross terms
+                const bool cross = p.state_in != nullptr || done > 0;
+                // The node's linear parts: with d <= 64 they are loaded into
+                // registers ahead of the staging, so every global load of the
+                // node is in flight at once (larger heads have no registers to
+                // spare)
+                constexpr bool PRE = D <= 64;
+                f32x4 nl[PRE ? P::NA : 1];
+                auto w_lin = [&](int ti, int tv, int i) {
+                    return e[O::N + (16 * ti + g4 + i) * DV + 16 * tv + col];
+                };
+                auto u_lin = [&](int ti, int i) { return col == 0 ? e[O::nv + 16 * ti + g4 + i] : 0.f; };
+                auto s_lin = [&](int ti, int tj, int i) { return e[O::X + (16 * ti + g4 + i) * D + 16 * tj + col]; };
+                if constexpr (PRE) {
+                    for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nl[j][i] = w_lin(ti, tv, i);
+                    });
+                    for_tiles<P, kU>(w, [&](int j, int ti, int) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nl[j][i] = u_lin(ti, i);
+                    });
+                    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) nl[j][i] = s_lin(ti, tj, i);
+                    });
+                }
+                if (cross) {
+                    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
+                    });
+                    stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                }
+                // the linear terms (the old S is already staged); the cross
+                // terms once the staging has landed
+                for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[j][i] = a * a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : w_lin(ti, tv, i));
+                });
+                for_tiles<P, kU>(w, [&](int j, int ti, int) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[j][i] = a * a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : u_lin(ti, i));
+                });
+                for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[j][i] = a * acc[j][i] + (PRE ? nl[PRE ? j : 0][i] : s_lin(ti, tj, i));
+                });
+                if (cross) {
+                    __syncthreads();
+                    for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+                    });
+                    for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+                    });
+                    __syncthreads();
+                }
+                done += 1 << b;
+            }
+        }
         // T-typed transposed copies: the operands of Q S0 and Q W0 (row DV of Wt = u)
         auto store_copies = [&](bool with_u) {
             for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
