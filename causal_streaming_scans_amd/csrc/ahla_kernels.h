@@ -69,6 +69,8 @@ struct AhlaFwdSmem {
     alignas(16) T Y1[C * G::TY1::LD];      // column 0 = y1
     alignas(16) T Pt[G::DVX * G::TK::LD];  // Pt[j][i] = P0[i][j]; row DV = mK0
     alignas(16) T Et[G::DVX * G::TK::LD];  // Et[j][i] = E0[i][j]; row DV = nk0
+    // each wave's 16 output rows on their way out (one wave per row tile)
+    alignas(16) T Ot[G::NCG == 1 && sizeof(T) == 2 ? G::RT * 16 * G::TV::LD : 8];
     float gp[DECAY ? G::NPOW : 1];
 };
 
@@ -162,6 +164,9 @@ void ahla_forward_kernel(FwdParams p) {
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
+    // one wave per row tile: output rows staged in LDS, stored whole
+    constexpr bool ROWS_OUT = NCG == 1 && sizeof(T) == 2;
+    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
 
     // the next chunk's data in registers: K, V for LDS; this wave's Q rows
     ChunkRegs<T, C, D, NT> rk;
@@ -352,9 +357,12 @@ void ahla_forward_kernel(FwdParams p) {
                         oc = mma16(oc, ld_frag_tt<TV>(sm.Y, 16 * s, 16 * jv), Lf[s]);
                     f32x4 ov = accO[jj] + oc;
                     if (ratio) ov *= rden;
-                    if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                    if constexpr (ROWS_OUT) store4(sm.Ot + (R * 16) * TV::LD + TV::off(col, 16 * jv + g4), ov);
+                    else if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
                 }
             }
+            if constexpr (ROWS_OUT)
+                store_rows_out<T, TV, DV>(sm.Ot + (R * 16) * TV::LD, orsrc, c0 - t_begin + 16 * R);
         });
         // advance the state: P0 <- g^c P0 + Kw^T V, E0 likewise with Y, mK0
         // with the ones column, nk0 with y1 (Kw: K rows weighted by

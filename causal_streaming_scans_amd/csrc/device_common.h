@@ -314,6 +314,51 @@ __device__ __forceinline__ void store4(bf16 *p, f32x4 a) {
 }
 __device__ __forceinline__ void store4(float *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
 
+// ------------------------------------------------------------ output rows
+//
+// A kernel's final output goes through a raw buffer resource over the
+// segment's rows: stores past the last valid row are dropped by the
+// resource's range check, so no branch per tile is needed.  Word 3 selects
+// the 32-bit data format, under which untyped accesses are range-checked
+// (gfx9 family).
+constexpr int kBufWord3 = 0x00020000;
+// Cache policy of those stores: non-temporal.  The output is written once
+// and never read back by the kernel; for whole 128-byte rows this measured
+// faster than the default policy (3 us of 55 per HLA-2 forward at B=8 H=16
+// n=4096 d=64), while for 8-byte pieces of rows (one accumulator's slots)
+// it was much slower, and non-temporal loads of q, k, v were slower too.
+constexpr int kCpolNT = 2;
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(T *base, int rows, int cols) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, rows * cols * (int)sizeof(T), kBufWord3);
+}
+
+__device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t rs, int byte_off, uint4 x) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, rs, byte_off, 0, kCpolNT);
+}
+
+// Write the 16 rows x COLS of a wave's LDS tile ot (layout TL) to rows
+// row0 .. row0+15 of the output behind rs, 16 bytes a lane: each global
+// store covers whole rows.  The rows were written to ot by this wave's own
+// lanes; LDS operations of one wave complete in order, so no barrier.
+template <typename T, typename TL, int COLS>
+__device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc_t rs, int row0) {
+    constexpr int VE = 16 / (int)sizeof(T);
+    constexpr int VPR = COLS / VE;      // 16-byte pieces per row
+    constexpr int NP = 16 * VPR;        // pieces of the tile
+#pragma unroll
+    for (int h = 0; h < (NP + kWave - 1) / kWave; ++h) {
+        const int idx = h * kWave + lane_id();
+        const int rr = idx / VPR, cc = (idx % VPR) * VE;
+        if (NP % kWave == 0 || idx < NP) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(ot + TL::off(rr, cc));
+            store16_buf(rs, ((row0 + rr) * COLS + cc) * (int)sizeof(T), x);
+        }
+    }
+}
+
 // Row / column of accumulator element r held by this lane within its tile.
 __device__ __forceinline__ int acc_row(int r) { return ((lane_id() >> 4) << 2) + r; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }

@@ -34,22 +34,6 @@
 
 namespace hla {
 
-// Third word of a raw buffer resource on gfx9-family chips: 32-bit data
-// format, so untyped loads and stores are range-checked against the record
-// count and not dropped as "invalid format".
-constexpr int kBufWord3 = 0x00020000;
-
-// Cache policy of the output stores: non-temporal.  o is written once and
-// never read back by the kernel; streaming it past the caches' normal
-// allocation measured 3 us faster per forward at B=8 H=16 n=4096 d=64 than
-// the default policy (and non-temporal loads of q, k, v 4 us slower).
-constexpr int kCpolNT = 2;
-
-__device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t rs, int byte_off, uint4 x) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, rs, byte_off, 0, kCpolNT);
-}
-
 template <typename T, int D, int DV, int C>
 struct Hla2PipeSmem {
     using G = Hla2Cfg<T, D, DV, C, false>;
@@ -97,8 +81,7 @@ void hla2_forward_pipe_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
     // this segment's rows of o; stores past its last valid row are dropped
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        o + (size_t)t_begin * DV, 0, (t_end - t_begin) * DV * (int)sizeof(T), kBufWord3);
+    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
 
     ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -193,8 +176,7 @@ void hla2_forward_pipe_kernel(FwdParams p) {
             for (int s = 0; s <= R; ++s) dc = mma16(dc, ones, Pf[s]);
             const float den = __shfl(accD[0] + dc[0], col);
             const float rden = ratio ? 1.f / den : 1.f;
-            // the tile's rows go through the wave's own LDS rows, so each
-            // global store writes whole 128-byte lines (8 lanes a row)
+            // the tile goes out through the wave's own LDS rows, whole rows at a time
             T *ot = sm.Ot[R];
 #pragma unroll
             for (int jv = 0; jv < nTV; ++jv) {
@@ -203,17 +185,7 @@ void hla2_forward_pipe_kernel(FwdParams p) {
                 for (int s = 0; s <= R; ++s) oc = mma16(oc, ld_frag_tt<TV>(sm.V[b], 16 * s, 16 * jv), Pf[s]);
                 store4(ot + TV::off(col, 16 * jv + g4), (accO[jv] + oc) * rden);
             }
-            constexpr int VPR = DV * (int)sizeof(T) / 16;   // 16-byte pieces per row
-            constexpr int NP = 16 * VPR;                       // pieces of the tile
-#pragma unroll
-            for (int h = 0; h < (NP + kWave - 1) / kWave; ++h) {
-                const int idx = h * kWave + lane_id();
-                const int rr = idx / VPR, cc = (idx % VPR) * (16 / (int)sizeof(T));
-                if (NP % kWave == 0 || idx < NP) {
-                    const uint4 x = *reinterpret_cast<const uint4 *>(ot + TV::off(rr, cc));
-                    store16_buf(orsrc, ((C * c + 16 * R + rr) * DV + cc) * (int)sizeof(T), x);
-                }
-            }
+            store_rows_out<T, TV, DV>(ot, orsrc, C * c + 16 * R);
         };
 
         store_s();
