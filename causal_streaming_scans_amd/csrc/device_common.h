@@ -340,11 +340,13 @@ __device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t rs, int byte_
 }
 
 // Write the 16 rows x COLS of a wave's LDS tile ot (layout TL) to rows
-// row0 .. row0+15 of the output behind rs, 16 bytes a lane: each global
-// store covers whole rows.  The rows were written to ot by this wave's own
-// lanes; LDS operations of one wave complete in order, so no barrier.
-template <typename T, typename TL, int COLS>
-__device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc_t rs, int row0) {
+// row0 .. row0+15, columns col0 .. col0+COLS-1 of the [rows][LDG] output
+// behind rs, 16 bytes a lane: each global store covers whole row pieces of
+// COLS columns.  The rows were written to ot by this wave's own lanes; LDS
+// operations of one wave complete in order, so no barrier.
+template <typename T, typename TL, int COLS, int LDG = COLS>
+__device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc_t rs, int row0,
+                                               int col0 = 0) {
     constexpr int VE = 16 / (int)sizeof(T);
     constexpr int VPR = COLS / VE;      // 16-byte pieces per row
     constexpr int NP = 16 * VPR;        // pieces of the tile
@@ -354,7 +356,7 @@ __device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc
         const int rr = idx / VPR, cc = (idx % VPR) * VE;
         if (NP % kWave == 0 || idx < NP) {
             const uint4 x = *reinterpret_cast<const uint4 *>(ot + TL::off(rr, cc));
-            store16_buf(rs, ((row0 + rr) * COLS + cc) * (int)sizeof(T), x);
+            store16_buf(rs, ((row0 + rr) * LDG + col0 + cc) * (int)sizeof(T), x);
         }
     }
 }

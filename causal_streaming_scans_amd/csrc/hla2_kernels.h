@@ -75,6 +75,11 @@ struct Hla2Cfg {
     static constexpr int SUMF = summary_floats(D, DV);
     static constexpr int STF = hla2_state_floats(D, DV);
     static constexpr int NPOW = 2 * C + 2;
+    // Output rows staged in LDS and stored whole (bf16, where the LDS has
+    // room for the staging rows): wave (r, cg) holds the contiguous column
+    // tiles cg*OJ .. cg*OJ+OJ-1 of its row tile, a [16][DV/NCG] tile TO.
+    static constexpr bool ROWS_OUT_SHAPE = sizeof(T) == 2 && OJ * NCG == nTV;
+    using TO = LdsTile<T, (ROWS_OUT_SHAPE ? DV / NCG : 16)>;
     static_assert(D % 16 == 0 && DV % 16 == 0 && C % 16 == 0, "tile multiples");
 };
 
@@ -114,7 +119,7 @@ __device__ __forceinline__ void for_stripe(int w, F f) {
 }
 
 
-template <typename T, int D, int DV, int C, bool DECAY>
+template <typename T, int D, int DV, int C, bool DECAY, bool RO = false>
 struct Hla2FwdSmem {
     using G = Hla2Cfg<T, D, DV, C, DECAY>;
     alignas(16) T K[C * G::TK::LD];
@@ -124,11 +129,22 @@ struct Hla2FwdSmem {
     alignas(16) T Zw[DECAY ? C * G::TK::LD : 8];    // rows weighted by g^(2(c-1-tau))
     alignas(16) T St[D * G::TS::LD];             // St[j][i] = S0[i][j]
     alignas(16) T Wt[G::DVX * G::TS::LD];        // Wt[j][i] = W0[i][j]; row DV = u0
+    alignas(16) T Ot[RO ? G::NW * 16 * G::TO::LD : 8];   // output rows on their way out
     float gp[G::NPOW];
 };
 
+// whether the forward stages its output rows (the shape allows it and the
+// LDS holds the staging rows as well)
 template <typename T, int D, int DV, int C, bool DECAY>
-using Hla2FwdLds = LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY>, CrossLds<D, DV>::FLOATS>;
+constexpr bool hla2_rows_out() {
+    return Hla2Cfg<T, D, DV, C, DECAY>::ROWS_OUT_SHAPE &&
+           sizeof(LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY, true>, CrossLds<D, DV>::FLOATS>) <=
+               160 * 1024;
+}
+
+template <typename T, int D, int DV, int C, bool DECAY>
+using Hla2FwdLds = LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY, hla2_rows_out<T, D, DV, C, DECAY>()>,
+                                  CrossLds<D, DV>::FLOATS>;
 
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
@@ -335,6 +351,10 @@ void hla2_forward_kernel(FwdParams p) {
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
+    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
+    using TO = typename G::TO;
+    constexpr bool RO = hla2_rows_out<T, D, DV, C, DECAY>();
+    T *const ot = sm.Ot + (RO ? w * 16 * TO::LD : 0);   // this wave's staging rows
 
     // the next chunk's data in registers: K, V for LDS; this wave's Q rows
     ChunkRegs<T, C, D, NT> rk;
@@ -525,7 +545,7 @@ void hla2_forward_kernel(FwdParams p) {
             f32x4 accO[G::OJ];
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
-                const int jv = cg + jj * NCG;
+                const int jv = RO ? cg * G::OJ + jj : cg + jj * NCG;
                 accO[jj] = zero4();
                 if (jv < nTV) {
                     accO[jj] = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + 16 * jv * G::TS::LD, qf);
@@ -557,7 +577,7 @@ void hla2_forward_kernel(FwdParams p) {
             }
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
-                const int jv = cg + jj * NCG;
+                const int jv = RO ? cg * G::OJ + jj : cg + jj * NCG;
                 if (jv < nTV) {
                     f32x4 oc = zero4();
 #pragma unroll
@@ -565,9 +585,12 @@ void hla2_forward_kernel(FwdParams p) {
                         oc = mma16(oc, ld_frag_tt<TV>(sm.V, 16 * s, 16 * jv), Pf[s]);
                     f32x4 ov = accO[jj] + oc;
                     if (ratio) ov *= rden;
-                    if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                    if constexpr (RO) store4(ot + TO::off(col, 16 * jj + g4), ov);
+                    else if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
                 }
             }
+            if constexpr (RO)
+                store_rows_out<T, TO, DV / NCG, DV>(ot, orsrc, c0 - t_begin + 16 * R, cg * (DV / NCG));
 
             // the rest of the state (W, u: products of Z) after every product,
             // then the T-typed copies, so no operand load waits behind a store
