@@ -18,6 +18,11 @@ def test_kernel_keys():
     k = bench.kernel_key
     assert k("_ZN3hla19hla2_forward_kernelIDF16bLi64ELi64ELi64ELb0EEEvNS_9FwdParamsE") == \
         "hla2_forward_kernel"
+    # the pipelined forward is stage 3's kernel
+    assert k("_ZN3hla24hla2_forward_pipe_kernelIDF16bLi64ELi64ELi64EEEvNS_9FwdParamsE") == \
+        "hla2_forward_kernel"
+    assert bench.is_stage_kernel("_ZN3hla24hla2_forward_pipe_kernelIDF16bLi64ELi64ELi64EEEvNS_9FwdParamsE")
+    assert not bench.is_stage_kernel("__amd_rocclr_copyBuffer")
     assert k("void hla::up_sweep_kernel<true, 64, 64, 256>(hla::FwdParams, int)") == "up_sweep_kernel"
     assert k("_ZN3hla17la_forward_kernelIDF16bLi64ELi64ELb0ELb1EEEvNS_8LaParamsE") == \
         "la_forward_kernel_dual"
