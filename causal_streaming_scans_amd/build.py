@@ -3,7 +3,11 @@
 Every translation unit under ``csrc/`` is compiled by hipcc in parallel into
 ``_build/`` and linked into ``causal_streaming_scans_amd/libhla.so``.
 Packed-fp32 instructions are disabled for all device code (the compiler
-otherwise forms them from plain float code).
+otherwise forms them from plain float code).  The kernels move bf16 data
+through LDS and registers as 8- and 16-byte words of other types; with
+-fno-strict-aliasing the compiler keeps every such access in program order
+against the others (type-based alias analysis once let it hoist a wave's
+16-byte LDS reads above its own 8-byte writes of the same rows).
 """
 from __future__ import annotations
 
@@ -23,6 +27,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-strict-aliasing",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -159,7 +159,10 @@ void ahla_forward_kernel(FwdParams p) {
     const int t_end = min(p.n, t_begin + p.seg_len);
     const bool ratio = p.ratio != 0;
     const bool last = seg == p.nseg - 1;
-    const bool need_u = ratio || (p.state_out != nullptr && last);
+    // u-type summaries always carried and the ratio's products always
+    // formed, so the chunk loop has no wave-uniform branches (as in the
+    // HLA-2 forward, where such branches gave run-to-run errors)
+    constexpr bool need_u = true;
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
@@ -332,21 +335,16 @@ void ahla_forward_kernel(FwdParams p) {
                     if (DECAY) accO[jj] *= sm.gp[tau + 1];
                 }
             }
-            f32x4 accD = zero4();
-            if (ratio) {
-                accD = mma_nt_ft<TK>(zero4(), sm.Et + DV * TK::LD, qf);
-                if (DECAY) accD *= sm.gp[tau + 1];
-            }
+            f32x4 accD = mma_nt_ft<TK>(zero4(), sm.Et + DV * TK::LD, qf);
+            if (DECAY) accD *= sm.gp[tau + 1];
             __syncthreads();
 
             // O^T += Y^T L^T ; den = q . nk0 + sum_sigma L[tau][sigma] y1[sigma]
-            float rden = 1.f;
-            if (ratio) {
-                f32x4 dc = zero4();
+            f32x4 dc = zero4();
 #pragma unroll
-                for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_tt<TY1>(sm.Y1, 16 * s, 0), Lf[s]);
-                rden = 1.f / __shfl(accD[0] + dc[0], col);
-            }
+            for (int s = 0; s <= R; ++s) dc = mma16(dc, ld_frag_tt<TY1>(sm.Y1, 16 * s, 0), Lf[s]);
+            const float den = __shfl(accD[0] + dc[0], col);
+            const float rden = ratio ? 1.f / den : 1.f;
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
                 const int jv = cg + jj * NCG;
@@ -355,10 +353,9 @@ void ahla_forward_kernel(FwdParams p) {
 #pragma unroll
                     for (int s = 0; s <= R; ++s)
                         oc = mma16(oc, ld_frag_tt<TV>(sm.Y, 16 * s, 16 * jv), Lf[s]);
-                    f32x4 ov = accO[jj] + oc;
-                    if (ratio) ov *= rden;
+                    const f32x4 ov = (accO[jj] + oc) * rden;
                     if constexpr (ROWS_OUT) store4(sm.Ot + (R * 16) * TV::LD + TV::off(col, 16 * jv + g4), ov);
-                    else if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                    else store4_row<T>(orsrc, ((c0 - t_begin + tau) * DV + 16 * jv + g4) * (int)sizeof(T), ov);
                 }
             }
             if constexpr (ROWS_OUT)

@@ -339,14 +339,38 @@ __device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t rs, int byte_
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, rs, byte_off, 0, kCpolNT);
 }
 
+// One accumulator's four slots (consecutive columns of one output row) at
+// byte offset byte_off behind rs, with the default cache policy: a store
+// past the resource's last row is dropped, so no per-lane branch is needed.
+__device__ __forceinline__ void store4_rows(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4 a) {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    union { bf16 h[4]; u32x2 v; } u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u.h[i] = (bf16)a[i];
+    __builtin_amdgcn_raw_buffer_store_b64(u.v, rs, byte_off, 0, 0);
+}
+__device__ __forceinline__ void store4_rows(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4 a, float) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, a), rs, byte_off, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ void store4_row(__amdgpu_buffer_rsrc_t rs, int byte_off, f32x4 a) {
+    if constexpr (sizeof(T) == 2) store4_rows(rs, byte_off, a);
+    else store4_rows(rs, byte_off, a, 0.f);
+}
+
 // Write the 16 rows x COLS of a wave's LDS tile ot (layout TL) to rows
 // row0 .. row0+15, columns col0 .. col0+COLS-1 of the [rows][LDG] output
 // behind rs, 16 bytes a lane: each global store covers whole row pieces of
 // COLS columns.  The rows were written to ot by this wave's own lanes; LDS
-// operations of one wave complete in order, so no barrier.
+// operations of one wave complete in order, so no barrier.  The compiler,
+// though, may not move the 16-byte reads above those writes: they are 8-byte
+// stores of another type, which type-based alias analysis would let it treat
+// as independent -- hence the compiler-only memory fence first.
 template <typename T, typename TL, int COLS, int LDG = COLS>
 __device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc_t rs, int row0,
                                                int col0 = 0) {
+    __asm__ __volatile__("" ::: "memory");
     constexpr int VE = 16 / (int)sizeof(T);
     constexpr int VPR = COLS / VE;      // 16-byte pieces per row
     constexpr int NP = 16 * VPR;        // pieces of the tile

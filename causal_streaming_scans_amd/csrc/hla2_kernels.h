@@ -346,7 +346,12 @@ void hla2_forward_kernel(FwdParams p) {
     const int t_end = min(p.n, t_begin + p.seg_len);
     const bool ratio = p.ratio != 0;
     const bool last = seg == p.nseg - 1;
-    const bool need_u = ratio || (p.state_out != nullptr && last);
+    // Every wave-uniform choice inside the chunk loop is made without a
+    // branch: u (the denominator's state) is always carried and the ratio's
+    // products always formed, the division selected at the end.  With a
+    // branch skipping those blocks, a non-ratio instance (d = 32, decay)
+    // gave wrong state copies from its second chunk on, varying from run
+    // to run; the branch-free loop is exact.
     const T *q = static_cast<const T *>(p.q) + (size_t)bh * p.n * D;
     const T *k = static_cast<const T *>(p.k) + (size_t)bh * p.n * D;
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
@@ -522,7 +527,7 @@ void hla2_forward_kernel(FwdParams p) {
                             for (int x = 0; x < gr.nr * gr.nc; ++x) a[x] *= gc;
                         }
                         mma_tn_grp<gr.nr, gr.nc, C, TK, TK, false>(a, KA, 16 * ti0, sm.K, 16 * tj0);
-                    } else if (gr.mat == kW || need_u) {
+                    } else {
                         if (DECAY) {
 #pragma unroll
                             for (int x = 0; x < gr.nr * gr.nc; ++x) a[x] *= gc2;
@@ -552,11 +557,8 @@ void hla2_forward_kernel(FwdParams p) {
                     if (DECAY) accO[jj] *= sm.gp[2 * (tau + 1)];
                 }
             }
-            f32x4 accD = zero4();
-            if (ratio) {
-                accD = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + DV * G::TS::LD, qf);
-                if (DECAY) accD *= sm.gp[2 * (tau + 1)];
-            }
+            f32x4 accD = mma_nt_ft<typename G::TS>(zero4(), sm.Wt + DV * G::TS::LD, qf);
+            if (DECAY) accD *= sm.gp[2 * (tau + 1)];
             // products of the staged chunk alone (S += K^T K), while the waves
             // of later row tiles finish Z
             advance(std::integral_constant<int, 0>{});
@@ -565,16 +567,14 @@ void hla2_forward_kernel(FwdParams p) {
             // ---- a-4: P^T = (D_{g^2} * tril(Q Z^T))^T ; O^T += V^T P^T
             Frag16<T> Pf[R + 1];
             scores_t<T, D, R, TK, DECAY>(Pf, sm.Z, qf, tau, sm.gp, 2);
-            float rden = 1.f;
-            if (ratio) {
-                // den = q . u0 + P 1: the product with a ones column tile puts
-                // P 1 in slot 0 of the token's lane in group 0
-                f32x4 dc = zero4();
-                const Frag16<T> ones = ones_frag<T>();
+            // den = q . u0 + P 1: the product with a ones column tile puts
+            // P 1 in slot 0 of the token's lane in group 0
+            f32x4 dc = zero4();
+            const Frag16<T> ones = ones_frag<T>();
 #pragma unroll
-                for (int s = 0; s <= R; ++s) dc = mma16(dc, ones, Pf[s]);
-                rden = 1.f / __shfl(accD[0] + dc[0], col);
-            }
+            for (int s = 0; s <= R; ++s) dc = mma16(dc, ones, Pf[s]);
+            const float den = __shfl(accD[0] + dc[0], col);
+            const float rden = ratio ? 1.f / den : 1.f;
 #pragma unroll
             for (int jj = 0; jj < G::OJ; ++jj) {
                 const int jv = RO ? cg * G::OJ + jj : cg + jj * NCG;
@@ -583,10 +583,9 @@ void hla2_forward_kernel(FwdParams p) {
 #pragma unroll
                     for (int s = 0; s <= R; ++s)
                         oc = mma16(oc, ld_frag_tt<TV>(sm.V, 16 * s, 16 * jv), Pf[s]);
-                    f32x4 ov = accO[jj] + oc;
-                    if (ratio) ov *= rden;
+                    const f32x4 ov = (accO[jj] + oc) * rden;
                     if constexpr (RO) store4(ot + TO::off(col, 16 * jj + g4), ov);
-                    else if (tau < cv) store4(o + (size_t)(c0 + tau) * DV + 16 * jv + g4, ov);
+                    else store4_row<T>(orsrc, ((c0 - t_begin + tau) * DV + 16 * jv + g4) * (int)sizeof(T), ov);
                 }
             }
             if constexpr (RO)
@@ -595,7 +594,7 @@ void hla2_forward_kernel(FwdParams p) {
             // the rest of the state (W, u: products of Z) after every product,
             // then the T-typed copies, so no operand load waits behind a store
             advance(std::integral_constant<int, 1>{});
-            store_copies(need_u);
+            store_copies(true);
             c0 = n0;
             cv = ncv;
         }
