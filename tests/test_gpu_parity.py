@@ -87,11 +87,12 @@ SUPPORT = [(dt, d, c, fam)
 
 @pytest.mark.parametrize("case", SUPPORT, ids=lambda c: "-".join(str(x) for x in c))
 @pytest.mark.parametrize("decay", [False, True])
-def test_support_matrix(case, decay):
-    """One small ragged, multi-segment case per kernel instance, ratio form,
-    with and without a per-head decay."""
+@pytest.mark.parametrize("ratio", [True, False])
+def test_support_matrix(case, decay, ratio):
+    """One small ragged, multi-segment case per kernel instance, with and
+    without the ratio and a per-head decay."""
     dtype, d, chunk, fam = case
-    variant = fam + "_ratio"
+    variant = fam + ("_ratio" if ratio else "")
     B, H, seg = 1, 2, 2
     n = 2 * chunk * seg + chunk // 2 + 3
     say(f"[support] {case} decay={decay} n={n}")
@@ -102,6 +103,9 @@ def test_support_matrix(case, decay):
     say(f"   rel_l2 {err:.3e}")
     assert np.isfinite(got).all()
     assert err < TOL[dtype]
+    # the same call again, bit for bit (every instance's chunk loop is
+    # deterministic; a run-to-run difference means a race or hazard)
+    assert np.array_equal(gpu_forward(x, variant, B, H, dtype, chunk, seg, gamma=x["gamma"]), got)
 
 
 @pytest.mark.parametrize("shape", [(32, 32, 2, 3), (64, 64, 2, 1), (32, 16, 4, 3)],
