@@ -187,20 +187,27 @@ namespace hla {
 
 // The unnormalised AHLA step split over column slices of 16 value columns:
 // workgroup (bh, slice) owns columns [16 slice, 16 slice + 16) of P and E.
-// y_j = P[:, j]^T q and E's column j need only column j, so the slices are
-// independent.  mK and nk feed only the ratio form's denominator: slice 0
-// alone reads and updates them, so no two workgroups touch the same state
-// word.  (The ratio form needs q . nk in every slice and keeps the
-// one-workgroup kernel above.)  At d = 64 that is four workgroups per head
-// instead of one, so a decode step of few heads reaches more of the chip.
+// With the old state, every quantity the step needs is one dot product with
+// q (or k):
+//     y_j = (g P + k v^T)[:, j] . q = g (P[:, j] . q) + (k . q) v_j
+//     o_j = (g E + k y^T)[:, j] . q = g (E[:, j] . q) + (k . q) y_j
+// so the workgroup forms the column sums P.q, E.q, k.q (and q.mK for the
+// slice that owns mK, nk) in one reduction -- one barrier -- and writes
+// P' = g P + k v^T (which needs no sum) before it, E' = g E + k y^T after.
+// mK <- g mK + k, nk <- g nk + k (q . mK') belong to slice 0 alone, so no
+// two workgroups touch the same state word.  (The ratio form needs q . nk in
+// every slice and keeps the one-workgroup kernel above.)  At d = 64 that is
+// four workgroups per head, so a decode step of few heads reaches more of
+// the chip, and every state load is issued at the kernel's start.
 template <typename T, int D, int DV, int NT>
 __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
     constexpr int SW = 16;              // columns per slice
     constexpr int RG = NT / SW;         // row groups
     constexpr int RPT = D / RG;         // rows per thread
-    static_assert(DV % SW == 0 && NT % SW == 0 && D % RG == 0, "block shape");
-    __shared__ float sq[D], sk[D], sv[SW], sy[SW];
-    __shared__ float part[RG][SW];
+    constexpr int NWV = NT / kWave;     // waves
+    constexpr int RGW = kWave / SW;     // row groups per wave
+    static_assert(DV % SW == 0 && NT % SW == 0 && D % RG == 0 && kWave % SW == 0, "block shape");
+    __shared__ float red[NWV][4][SW];
 
     const int nsl = DV / SW;
     const int bh = blockIdx.x / nsl, slice = blockIdx.x % nsl;
@@ -215,66 +222,66 @@ __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
     float *st = p.state + (size_t)bh * ahla_state_floats(D, DV);
     float *P = st, *E = st + D * DV, *mK = st + 2 * D * DV, *nk = mK + D;
 
-    float pv[RPT], ev[RPT];
+    // every load first: this thread's rows r = rg + i RG of column j
+    float pv[RPT], ev[RPT], qv[RPT], kv[RPT], mv[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        pv[i] = P[(rg + i * RG) * DV + j];
-        ev[i] = E[(rg + i * RG) * DV + j];
+        const int r = rg + i * RG;
+        pv[i] = P[r * DV + j];
+        ev[i] = E[r * DV + j];
+        qv[i] = to_f(q[r]);
+        kv[i] = to_f(k[r]);
+        mv[i] = slice == 0 ? mK[r] : 0.f;   // only slice 0 reads or writes mK
     }
-    for (int i = tid; i < D; i += NT) { sq[i] = to_f(q[i]); sk[i] = to_f(k[i]); }
-    if (tid < SW) sv[tid] = to_f(v[slice * SW + tid]);
+    const float vj = to_f(v[j]);
+
+    // P' = g P + k v^T needs no sum
+    float sums[4] = {0.f, 0.f, 0.f, 0.f};   // P.q, E.q, k.q, q.mK over this thread's rows
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        P[r * DV + j] = g * pv[i] + kv[i] * vj;
+        sums[0] += qv[i] * pv[i];
+        sums[1] += qv[i] * ev[i];
+        sums[2] += qv[i] * kv[i];
+        sums[3] += qv[i] * mv[i];
+    }
+    // over the row groups of this wave (lanes 16 apart share the column),
+    // then over the waves through LDS
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+        for (int m = SW; m < kWave; m <<= 1) sums[x] += __shfl_xor(sums[x], m);
+    }
+    const int wv = tid / kWave;
+    if ((tid % kWave) < SW) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) red[wv][x][col] = sums[x];
+    }
     __syncthreads();
-    if (slice == 0) {
-        // mK <- g mK + k ; nk <- g nk + k (q . mK), owned by this workgroup alone
-        __shared__ float red[NT / kWave];
-        float mkv = 0.f, sp = 0.f;
-        if (tid < D) {
-            mkv = g * mK[tid] + sk[tid];
-            mK[tid] = mkv;
-            sp = sq[tid] * mkv;
+    float tot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWV; ++w)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) tot[x] += red[w][x][col];
+    const float kq = tot[2];
+    const float yj = g * tot[0] + kq * vj;
+    // E' = g E + k y^T ; o_j
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + i * RG;
+        E[r * DV + j] = g * ev[i] + kv[i] * yj;
+    }
+    if (rg == 0) o[j] = from_f<T>(g * tot[1] + kq * yj);
+    if (slice == 0 && col == 0) {
+        // mK' = g mK + k ; nk' = g nk + k (q . mK'), q . mK' = g (q . mK) + k . q
+        const float qm = g * tot[3] + kq;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + i * RG;
+            mK[r] = g * mv[i] + kv[i];
+            nk[r] = g * nk[r] + kv[i] * qm;
         }
-        for (int m = kWave / 2; m >= 1; m >>= 1) sp += __shfl_xor(sp, m);
-        if ((tid & (kWave - 1)) == 0) red[tid / kWave] = sp;
-        __syncthreads();
-        float s_all = 0.f;
-#pragma unroll
-        for (int i = 0; i < NT / kWave; ++i) s_all += red[i];
-        if (tid < D) nk[tid] = g * nk[tid] + sk[tid] * s_all;
-    }
-    // P <- g P + k v^T ; partial y = P^T q
-    float yp = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float pn = g * pv[i] + sk[r] * sv[col];
-        P[r * DV + j] = pn;
-        yp += sq[r] * pn;
-    }
-    part[rg][col] = yp;
-    __syncthreads();
-    if (tid < SW) {
-        float y = 0.f;
-#pragma unroll
-        for (int i = 0; i < RG; ++i) y += part[i][tid];
-        sy[tid] = y;
-    }
-    __syncthreads();
-    // E <- g E + k y^T ; partial o = q^T E
-    float op = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + i * RG;
-        const float en = g * ev[i] + sk[r] * sy[col];
-        E[r * DV + j] = en;
-        op += sq[r] * en;
-    }
-    part[rg][col] = op;
-    __syncthreads();
-    if (tid < SW) {
-        float s = 0.f;
-#pragma unroll
-        for (int i = 0; i < RG; ++i) s += part[i][tid];
-        o[slice * SW + tid] = from_f<T>(s);
     }
 }
 
