@@ -54,27 +54,19 @@ struct ChunkRegs {
     static constexpr int NV = (NVEC + NT - 1) / NT;
     static_assert(COLS % VE == 0, "rows of whole 16-byte groups");
     uint4 raw[NV];
-    int rows_valid;
 
+    // rows at or past rv read as zeros: the loads go through a buffer
+    // resource that covers the rv valid rows only, whose range check returns
+    // zeros past its end, so neither the loads nor the staging stores need a
+    // per-row select (each 16-byte piece lies wholly inside or outside)
     __device__ __forceinline__ void load(const T *__restrict__ src, int rv) {
-        rows_valid = rv;
+        const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src, rv, COLS);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int idx = threadIdx.x + i * NT;
-            int r = idx / VPR;
-            const int c = (idx % VPR) * VE;
-            if (!(idx < NVEC && r < rv)) r = 0;
-            raw[i] = *reinterpret_cast<const uint4 *>(src + (size_t)r * COLS + c);
-        }
-    }
-    __device__ __forceinline__ bool ok(int i) const {
-        const int idx = threadIdx.x + i * NT;
-        return idx < NVEC && idx / VPR < rows_valid;
+        for (int i = 0; i < NV; ++i) raw[i] = load16_buf(rs, (threadIdx.x + i * NT) * 16);
     }
     __device__ __forceinline__ Vec16<T> get(int i) const {
         Vec16<T> x;
-        const uint4 z = ok(i) ? raw[i] : make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4 *>(x.v) = z;
+        *reinterpret_cast<uint4 *>(x.v) = raw[i];
         return x;
     }
     // the same into an LdsTile matrix

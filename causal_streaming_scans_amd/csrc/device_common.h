@@ -314,13 +314,14 @@ __device__ __forceinline__ void store4(bf16 *p, f32x4 a) {
 }
 __device__ __forceinline__ void store4(float *p, f32x4 a) { *reinterpret_cast<f32x4 *>(p) = a; }
 
-// ------------------------------------------------------------ output rows
+// ------------------------------------------------------- row buffers
 //
 // A kernel's final output goes through a raw buffer resource over the
 // segment's rows: stores past the last valid row are dropped by the
-// resource's range check, so no branch per tile is needed.  Word 3 selects
-// the 32-bit data format, under which untyped accesses are range-checked
-// (gfx9 family).
+// resource's range check, so no branch per tile is needed; the chunk loads
+// read through such a resource too, and read zeros past its end.  Word 3
+// selects the 32-bit data format, under which untyped accesses are
+// range-checked (gfx9 family).
 constexpr int kBufWord3 = 0x00020000;
 // Cache policy of those stores: non-temporal.  The output is written once
 // and never read back by the kernel; for whole 128-byte rows this measured
@@ -332,6 +333,18 @@ constexpr int kCpolNT = 2;
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(T *base, int rows, int cols) {
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, rows * cols * (int)sizeof(T), kBufWord3);
+}
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T *base, int rows, int cols) {
+    return rows_rsrc(const_cast<T *>(base), rows, cols);
+}
+
+// 16 bytes at byte offset byte_off behind rs; zeros past the resource's end
+__device__ __forceinline__ uint4 load16_buf(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
 __device__ __forceinline__ void store16_buf(__amdgpu_buffer_rsrc_t rs, int byte_off, uint4 x) {
