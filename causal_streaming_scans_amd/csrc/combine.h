@@ -107,9 +107,15 @@ __device__ __forceinline__ f32x4 tile_ab_f32(const float *A, int lda, const floa
     return acc;
 }
 
-// Column slices a combine is split into (each a multiple of 16 columns).
+// Column slices a combine is split into (each a multiple of 16 columns).  At
+// dv >= 128 a slice workgroup stages the whole d x d left factor (one per
+// CU) and its products are fp32 MFMA chains over k = d, so eight slices of
+// 1024 threads -- one tile per wave -- finish a level sooner than four of
+// 256 (up-sweep of the d = 128 decay workload 39 -> 29 us).
 template <int DV>
-constexpr int combine_slices() { return DV / 16 < 4 ? DV / 16 : 4; }
+constexpr int combine_slices() { return DV / 16 < 4 ? DV / 16 : (DV >= 128 ? 8 : 4); }
+template <int DV>
+constexpr int combine_threads() { return DV >= 128 ? 1024 : 256; }
 
 // Slice cs of eD = eA (+) eB, by all NT threads of the workgroup, eD a
 // separate node (nothing is read that any slice writes).  The slice owns the

@@ -533,8 +533,8 @@ static hla_status prepare_forward(const void *q, const void *k, const void *v, v
     const long nseg = num_segments(n, chunk, g);
     if (nseg > INT32_MAX / 4) return HLA_ERR_UNSUPPORTED;
     // one-dimensional grids: the forward's nseg*B*H workgroups, the up-sweep's
-    // four column slices of (nseg-1)/2*B*H combines
-    if (nseg * B * H > INT32_MAX / 2) return HLA_ERR_UNSUPPORTED;
+    // four (dv >= 128: eight) column slices of (nseg-1)/2*B*H combines
+    if (nseg * B * H > (dv >= 128 ? INT32_MAX / 4 : INT32_MAX / 2)) return HLA_ERR_UNSUPPORTED;
     const size_t need = hla_workspace_bytes(variant, B, H, n, d, dv, chunk, g);
     if (need > 0) {
         if (!workspace) return HLA_ERR_NULL;

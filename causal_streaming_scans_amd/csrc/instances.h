@@ -60,7 +60,7 @@ hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
 
 template <typename T, int D, bool HLA2>
 hipError_t launch_up_sweep(const FwdParams &p, hipStream_t s) {
-    constexpr int NT = 256, CS = combine_slices<D>();
+    constexpr int NT = combine_threads<D>(), CS = combine_slices<D>();
     for (int b = 0; (p.nreal >> (b + 1)) > 0; ++b) {
         const int npair = p.nreal >> (b + 1);
         hipLaunchKernelGGL((up_sweep_kernel<HLA2, D, D, NT>), dim3(up_sweep_groups<CS>(npair * p.BH)),

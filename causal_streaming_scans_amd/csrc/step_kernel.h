@@ -199,9 +199,8 @@ namespace hla {
 // every slice and keeps the one-workgroup kernel above.)  At d = 64 that is
 // four workgroups per head, so a decode step of few heads reaches more of
 // the chip, and every state load is issued at the kernel's start.
-template <typename T, int D, int DV, int NT>
+template <typename T, int D, int DV, int NT, int SW = 16>   // SW: columns per slice
 __global__ __launch_bounds__(NT) void ahla_step_sliced_kernel(StepParams p) {
-    constexpr int SW = 16;              // columns per slice
     constexpr int RG = NT / SW;         // row groups
     constexpr int RPT = D / RG;         // rows per thread
     constexpr int NWV = NT / kWave;     // waves

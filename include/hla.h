@@ -153,7 +153,8 @@ size_t hla_workspace_bytes(int variant, int B, int H, int n, int d, int dv,
  * Supported (otherwise HLA_ERR_UNSUPPORTED): d == dv, chunk 16, 32 or 64;
  *   HLA_BF16: d in {16, 32, 64, 128};
  *   HLA_F32:  d in {16, 32, 64};
- *   B*H <= 65535, and nseg*B*H <= 2^30 - 1 (nseg = ceil(n / (chunk*seg_chunks)),
+ *   B*H <= 65535, and nseg*B*H <= 2^30 - 1, or 2^29 - 1 at dv >= 128
+ *   (nseg = ceil(n / (chunk*seg_chunks)),
  *   one workgroup per segment and head).
  */
 hla_status hla_forward(const void *q, const void *k, const void *v, void *o,

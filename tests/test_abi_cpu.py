@@ -117,6 +117,11 @@ def test_forward_validation_errors(lib):
     assert _fwd(lib, fake, fake, fake, fake, n=1024, seg=2, ws=fake, wsb=need - 1) == ERR_WS
     # the forward grid has one workgroup per (segment, head): at most 2^31 - 1
     assert _fwd(lib, fake, fake, fake, fake, B=64, H=1000, n=1 << 21, chunk=16, seg=1) == ERR_UNSUP
+    # at dv = 128 the up-sweep has eight column slices per combine: nseg*B*H
+    # up to 2^29 - 1 there (here 8389 * 64000 > 2^29), 2^30 - 1 otherwise
+    big = dict(B=64, H=1000, n=8389 * 16, chunk=16, seg=1)
+    assert _fwd(lib, fake, fake, fake, fake, d=128, dv=128, **big) == ERR_UNSUP
+    assert _fwd(lib, fake, fake, fake, fake, **big) == ERR_NULL   # within the limit; no workspace
     # state_in may not alias state_out
     assert _fwd(lib, fake, fake, fake, fake, si=fake, so=fake) == ERR_ARG
 
