@@ -133,18 +133,96 @@ struct Hla2FwdSmem {
     float gp[G::NPOW];
 };
 
+// The prefix fold's cross terms on bf16 MFMA (bf16 kernels, d >= 64).  Each
+// fp32 factor is split into a bf16 high part and a bf16 low part, x = h + l
+// with |x - h - l| <= 2^-17 |x|, and S Y is formed as Sh Yh + Sh Yl + Sl Yh:
+// the dropped Sl Yl and the rounding of the low parts leave about 2^-16 of
+// each product, far inside the bf16 path's bar, and three bf16 MFMA steps
+// replace eight fp32 steps per 32 k-values (with fp32 MFMA the fold cost the
+// d = 128 decay forward 39 us of 250).  The old S is staged transposed (the
+// layout of St) and the node's [a Y | a y | 0] row-major, each as a high and
+// a low copy; fp32 kernels keep exact fp32 products for their tighter bar.
+template <typename T, int D, int DV>
+struct FoldX3 {
+    static constexpr bool ON = sizeof(T) == 2 && D >= 64;
+    using TS = LdsTile<bf16, D>;
+    using TY = LdsTile<bf16, DV + 16>;
+    static constexpr int S_EL = D * TS::LD, Y_EL = D * TY::LD;   // bf16 elements of one copy
+    static constexpr int FLOATS = (2 * S_EL + 2 * Y_EL + 1) / 2;
+};
+// floats of the fold's staging area, overlaid on the chunk buffers
+template <typename T, int D, int DV>
+constexpr int fold_scratch_floats() {
+    using X = FoldX3<T, D, DV>;
+    return X::ON && X::FLOATS > CrossLds<D, DV>::FLOATS ? X::FLOATS : CrossLds<D, DV>::FLOATS;
+}
+
+// x minus its bf16 rounding (exact in fp32)
+__device__ __forceinline__ f32x4 bf16_low(f32x4 x) {
+    f32x4 l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l[i] = x[i] - static_cast<float>(static_cast<bf16>(x[i]));
+    return l;
+}
+
+// [a Y | a y | 0] of a node (fp32 rows Y [D][DV], column y [D]) into the
+// high and low [D][DV+16] copies, by all NT threads
+template <int D, int DV, int NT>
+__device__ __forceinline__ void fold_x3_stage_y(bf16 *Yh, bf16 *Yl, const float *Y, const float *y,
+                                                float a) {
+    using TY = LdsTile<bf16, DV + 16>;
+    constexpr int Q4 = (DV + 16) / 4, N = D * Q4;
+    for (int idx = threadIdx.x; idx < N; idx += NT) {
+        const int k = idx / Q4, v = 4 * (idx - k * Q4);
+        f32x4 x = zero4();
+        if (v < DV) x = a * *reinterpret_cast<const f32x4 *>(Y + k * DV + v);
+        else if (v == DV) x[0] = a * y[k];
+        store4(Yh + TY::off(k, v), x);
+        store4(Yl + TY::off(k, v), bf16_low(x));
+    }
+}
+
+// this wave's tiles of the old S into the high and low copies of S^T
+template <typename P, int D>
+__device__ __forceinline__ void fold_x3_stage_s(const f32x4 *acc, int w, bf16 *Sh, bf16 *Sl) {
+    using TS = LdsTile<bf16, D>;
+    const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
+    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+        store4(Sh + TS::off(16 * tj + col, 16 * ti + g4), acc[j]);
+        store4(Sl + TS::off(16 * tj + col, 16 * ti + g4), bf16_low(acc[j]));
+    });
+}
+
+// W += (a S) Y, u += S (a y) for this wave's W and u groups, from the staged
+// copies (the factor a travels in the staged Y)
+template <typename P, int D, int DV>
+__device__ __forceinline__ void fold_x3_products(f32x4 *acc, int w, const bf16 *Sh, const bf16 *Sl,
+                                                 const bf16 *Yh, const bf16 *Yl) {
+    using TS = LdsTile<bf16, D>;
+    using TY = LdsTile<bf16, DV + 16>;
+    for_groups<P, -1, -1>(w, [&](auto gi, int ti0, int tj0) {
+        constexpr Grp gr = P::grp(decltype(gi)::value);
+        if constexpr (gr.mat == kW || gr.mat == kU) {
+            f32x4 *c = acc + gr.first;
+            mma_tn_grp<gr.nr, gr.nc, D, TS, TY, false>(c, Sl, 16 * ti0, Yh, 16 * tj0);
+            mma_tn_grp<gr.nr, gr.nc, D, TS, TY, false>(c, Sh, 16 * ti0, Yl, 16 * tj0);
+            mma_tn_grp<gr.nr, gr.nc, D, TS, TY, false>(c, Sh, 16 * ti0, Yh, 16 * tj0);
+        }
+    });
+}
+
 // whether the forward stages its output rows (the shape allows it and the
 // LDS holds the staging rows as well)
 template <typename T, int D, int DV, int C, bool DECAY>
 constexpr bool hla2_rows_out() {
     return Hla2Cfg<T, D, DV, C, DECAY>::ROWS_OUT_SHAPE &&
-           sizeof(LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY, true>, CrossLds<D, DV>::FLOATS>) <=
+           sizeof(LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY, true>, fold_scratch_floats<T, D, DV>()>) <=
                160 * 1024;
 }
 
 template <typename T, int D, int DV, int C, bool DECAY>
 using Hla2FwdLds = LdsWithScratch<Hla2FwdSmem<T, D, DV, C, DECAY, hla2_rows_out<T, D, DV, C, DECAY>()>,
-                                  CrossLds<D, DV>::FLOATS>;
+                                  fold_scratch_floats<T, D, DV>()>;
 
 template <typename T, int D, int DV, int C, bool DECAY>
 struct Hla2SumSmem {
@@ -250,9 +328,12 @@ __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int
     const int col = acc_col(), g4 = (lane_id() >> 4) << 2;
     // fold node B (later) into the running state A: W <- a^2 W + N_B +
     // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
-    // the node's [Y | y] are staged in LDS (fp32) as the cross factors
+    // the node's [Y | y] are staged in LDS as the cross factors (fp32, or
+    // split bf16 for the bf16 kernels at d >= 64)
     using L = CrossLds<D, DV>;  // fold: whole right factor
+    using X3 = FoldX3<T, D, DV>;
     float *Ss = lds_f, *Bs = lds_f + D * L::LDA;
+    bf16 *Sh = reinterpret_cast<bf16 *>(lds_f), *Sl = Sh + X3::S_EL, *Yh = Sl + X3::S_EL, *Yl = Yh + X3::Y_EL;
     int done = 0;
     for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
         if (!((seg >> b) & 1)) continue;
@@ -286,11 +367,16 @@ __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int
             });
         }
         if (cross) {
-            for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+            if constexpr (X3::ON) {
+                fold_x3_stage_s<P, D>(acc, w, Sh, Sl);
+                fold_x3_stage_y<D, DV, NT>(Yh, Yl, e + O::Y, e + O::y, a);
+            } else {
+                for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
-            });
-            stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                    for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
+                });
+                stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+            }
         }
         // the linear terms (the old S is already staged); the cross
         // terms once the staging has landed
@@ -310,12 +396,16 @@ __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int
         });
         if (cross) {
             __syncthreads();
-            for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
-                acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
-            });
-            for_tiles<P, kU>(w, [&](int j, int ti, int) {
-                acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
-            });
+            if constexpr (X3::ON) {
+                fold_x3_products<P, D, DV>(acc, w, Sh, Sl, Yh, Yl);
+            } else {
+                for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+                    acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+                });
+                for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                    acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+                });
+            }
             __syncthreads();
         }
         done += 1 << b;
@@ -407,9 +497,13 @@ void hla2_forward_kernel(FwdParams p) {
         if (seg > 0) {
             // fold node B (later) into the running state A: W <- a^2 W + N_B +
             // a S Y_B, u <- a^2 u + nv_B + a S y_B, S <- a S + X_B; the old S and
-            // the node's [Y | y] are staged in LDS (fp32) as the cross factors
+            // the node's [Y | y] are staged in LDS as the cross factors (fp32,
+            // or split bf16 for the bf16 kernels at d >= 64)
             using L = CrossLds<D, DV>;  // fold: whole right factor
+            using X3 = FoldX3<T, D, DV>;
             float *Ss = lds.f, *Bs = lds.f + D * L::LDA;
+            bf16 *Sh = reinterpret_cast<bf16 *>(lds.f), *Sl = Sh + X3::S_EL, *Yh = Sl + X3::S_EL,
+                 *Yl = Yh + X3::Y_EL;
             int done = 0;
             for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
                 if (!((seg >> b) & 1)) continue;
@@ -443,11 +537,16 @@ void hla2_forward_kernel(FwdParams p) {
                     });
                 }
                 if (cross) {
-                    for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
+                    if constexpr (X3::ON) {
+                        fold_x3_stage_s<P, D>(acc, w, Sh, Sl);
+                        fold_x3_stage_y<D, DV, NT>(Yh, Yl, e + O::Y, e + O::y, a);
+                    } else {
+                        for_tiles<P, kS>(w, [&](int j, int ti, int tj) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
-                    });
-                    stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                            for (int i = 0; i < 4; ++i) Ss[(16 * ti + g4 + i) * L::LDA + 16 * tj + col] = acc[j][i];
+                        });
+                        stage_right_ext<D, DV, DV, NT>(Bs, e + O::Y, 0, e + O::y, true);
+                    }
                 }
                 // the linear terms (the old S is already staged); the cross
                 // terms once the staging has landed
@@ -467,12 +566,16 @@ void hla2_forward_kernel(FwdParams p) {
                 });
                 if (cross) {
                     __syncthreads();
-                    for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
-                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
-                    });
-                    for_tiles<P, kU>(w, [&](int j, int ti, int) {
-                        acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
-                    });
+                    if constexpr (X3::ON) {
+                        fold_x3_products<P, D, DV>(acc, w, Sh, Sl, Yh, Yl);
+                    } else {
+                        for_tiles<P, kW>(w, [&](int j, int ti, int tv) {
+                            acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + 16 * tv, L::LDB);
+                        });
+                        for_tiles<P, kU>(w, [&](int j, int ti, int) {
+                            acc[j] += a * tile_ab_f32<D>(Ss + 16 * ti * L::LDA, L::LDA, Bs + DV, L::LDB);
+                        });
+                    }
                     __syncthreads();
                 }
                 done += 1 << b;

@@ -46,7 +46,7 @@ struct Hla2PipeSmem {
 };
 
 template <typename T, int D, int DV, int C>
-using Hla2PipeLds = LdsWithScratch<Hla2PipeSmem<T, D, DV, C>, CrossLds<D, DV>::FLOATS>;
+using Hla2PipeLds = LdsWithScratch<Hla2PipeSmem<T, D, DV, C>, fold_scratch_floats<T, D, DV>()>;
 
 // the shapes the pipelined loop is built for: bf16, one wave per row tile
 template <typename T, int D, int DV, int C>
