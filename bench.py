@@ -205,16 +205,20 @@ def counters_summary(fetch_csv: str, write_csv: str) -> None:
            "copy_calibration": {"kernel": f"torch.neg over {mib} MiB bf16 ({mib} MiB read, "
                                           f"{mib} MiB written)",
                                 "FETCH_SIZE_KiB": round(cal_f, 1), "WRITE_SIZE_KiB": round(cal_w, 1)}}
+    def entry(name):
+        fb, wb = fetch[name] * 1024 * fs, write[name] * 1024 * ws
+        return {"FETCH_SIZE_KiB": round(fetch[name], 1), "WRITE_SIZE_KiB": round(write[name], 1),
+                "fetch_bytes": int(fb), "write_bytes": int(wb), "hbm_bytes_per_launch": int(fb + wb)}
+
     for short in ("summary_kernel", "up_sweep_kernel", "forward_kernel"):
         names = [n for n in fetch if is_stage_kernel(n) and kernel_key(n).endswith(short)
                  and n in write]
         for name in names:
-            key = kernel_key(name)
-            fb, wb = fetch[name] * 1024 * fs, write[name] * 1024 * ws
-            rec[key] = {"FETCH_SIZE_KiB": round(fetch[name], 1),
-                        "WRITE_SIZE_KiB": round(write[name], 1),
-                        "fetch_bytes": int(fb), "write_bytes": int(wb),
-                        "hbm_bytes_per_launch": int(fb + wb)}
+            rec[kernel_key(name)] = entry(name)
+    # the decode step (AHLA, 32 heads, d = 64) when the runs timed it
+    dec = [n for n in fetch if "ahla_step_sliced_kernel" in n and n in write]
+    if dec:
+        rec["ahla_step_sliced_kernel"] = entry(dec[0])
     print(json.dumps(rec, indent=1))
 
 
@@ -657,6 +661,7 @@ def main():
         us_graph = e0.elapsed_time(e1) * 1e3 / (reps * per_graph)
         st_bytes = 2 * BHd * stf * 4 + BHd * (2 * dw.d + 2 * dw.dv) * 2
         decode = {"workload": "AHLA decode step, B=1 H=32 d=dv=64 bf16, fp32 state",
+                  "traffic": stored_traffic("ahla_step_sliced_kernel"),
                   "us_per_step": round(us, 3), "tokens_per_s": round(BHd / (us * 1e-6), 1),
                   "us_per_step_graph": round(us_graph, 3),
                   "state_bytes_per_step": st_bytes,
