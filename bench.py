@@ -665,7 +665,8 @@ def main():
                   "us_per_step": round(us, 3), "tokens_per_s": round(BHd / (us * 1e-6), 1),
                   "us_per_step_graph": round(us_graph, 3),
                   "state_bytes_per_step": st_bytes,
-                  "achieved_GBs": round(st_bytes / (us * 1e-6) / 1e9, 2)}
+                  "achieved_GBs": round(st_bytes / (us * 1e-6) / 1e9, 2),
+                  "achieved_GBs_graph": round(st_bytes / (us_graph * 1e-6) / 1e9, 2)}
         log(f"[bench] decode: {us:.2f} us/step, {us_graph:.2f} us/step under graph replay")
 
     # ---- backward pass (HLA-2 gradients dq, dk, dv) at the benchmark shape:
