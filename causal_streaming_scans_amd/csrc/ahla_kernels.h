@@ -220,8 +220,9 @@ void ahla_forward_kernel(FwdParams p) {
         using L = CrossLds<D, DV>;  // fold: whole right factor
         float *Ms = lds.f, *Ps = lds.f + D * L::LDA;
         int done = 0;
-        for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
-            if (!((seg >> b) & 1)) continue;
+        while (done < seg) {
+            // the next node: a leaf, or the largest up-sweep node left
+            const int b = p.leaf_fold ? 0 : 31 - __builtin_clz(seg - done);
             const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
             const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
             // with no caller state the first node folds into zero: no cross terms

@@ -314,9 +314,9 @@ __device__ __forceinline__ void z_tiles(const RowFrags<T, D> &qf, const Frag16<T
     }
 }
 
-// a-6: fold the up-sweep nodes covering segments 0 .. seg-1 (seg > 0) into
-// the state tiles acc that plan P gives wave w; lds_f is the fp32 staging
-// area of the cross factors.  The same steps as the fold written out in
+// a-6: fold the up-sweep nodes covering segments 0 .. seg-1 (seg > 0), or
+// with p.leaf_fold the leaves 0 .. seg-1 themselves, into the state tiles acc
+// that plan P gives wave w; lds_f is the staging area of the cross factors.  The same steps as the fold written out in
 // hla2_forward_kernel (kept inline there: at d = 128 the compiler allocates
 // registers for the call form with more spills).
 template <typename T, int D, int DV, int C, bool DECAY, typename P>
@@ -335,8 +335,9 @@ __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int
     float *Ss = lds_f, *Bs = lds_f + D * L::LDA;
     bf16 *Sh = reinterpret_cast<bf16 *>(lds_f), *Sl = Sh + X3::S_EL, *Yh = Sl + X3::S_EL, *Yl = Yh + X3::Y_EL;
     int done = 0;
-    for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
-        if (!((seg >> b) & 1)) continue;
+    while (done < seg) {
+        // the next node: a leaf, or the largest up-sweep node left
+        const int b = p.leaf_fold ? 0 : 31 - __builtin_clz(seg - done);
         const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
         const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
         // with no caller state the first node folds into zero: no cross terms
@@ -505,8 +506,9 @@ void hla2_forward_kernel(FwdParams p) {
             bf16 *Sh = reinterpret_cast<bf16 *>(lds.f), *Sl = Sh + X3::S_EL, *Yh = Sl + X3::S_EL,
                  *Yl = Yh + X3::Y_EL;
             int done = 0;
-            for (int b = 31 - __builtin_clz(seg); b >= 0; --b) {
-                if (!((seg >> b) & 1)) continue;
+            while (done < seg) {
+                // the next node: a leaf, or the largest up-sweep node left
+                const int b = p.leaf_fold ? 0 : 31 - __builtin_clz(seg - done);
                 const float *e = p.ws + node_offset(bh, b, done >> b, p.BH, p.nreal, G::SUMF);
                 const float a = DECAY ? pow_int(g, (long)p.seg_len << b) : 1.f;
                 // with no caller state the first node folds into zero: no cross terms

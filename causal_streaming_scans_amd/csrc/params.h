@@ -21,6 +21,7 @@ struct FwdParams {
     int seg_len;      // tokens per segment (a multiple of the chunk)
     int nseg;         // segments per head
     int nreal;        // summarised segments per head: nseg - 1
+    int leaf_fold;    // no up-sweep: segment s folds leaves 0 .. s-1 one by one
     int ratio;        // divide by the masked denominator
     float *ws;        // workspace, see below (unused when nseg == 1)
     const float *state_in;   // [BH][state floats] or null

@@ -178,6 +178,10 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
  *            segments 0 .. s-1 (one per set bit of s) folded into its carried
  *            state (what the scan's down-sweep delivers), then the chunked
  *            forward from that state, and state_out.
+ * With R <= 3 (at most four segments) the scan has no up-sweep: stage 2
+ * enqueues nothing, the node slots stay unused, and stage 3 folds the leaves
+ * 0 .. s-1 of segment s one by one (at most three folds cost less than the
+ * up-sweep's launch).
  * Calling stages 1, 2, 3 in order on one stream with identical arguments is
  * exactly hla_forward.  With a single segment stages 1 and 2 enqueue nothing.
  * Meant for callers that time the stages or place them themselves (a caller
