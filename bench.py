@@ -710,6 +710,33 @@ def main():
                     "lean_bytes_per_step": b_bytes,
                     "lean_hbm_frac": round(b_bytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         log(f"[bench] backward: {bms:.4f} ms/step, {tokens / (bms * 1e-3) / 1e9:.3f} G tokens/s")
+        # a training step's pair: the forward that keeps its keyed queries
+        # z_t = S_t q_t (hla_forward_z) and the backward that takes them
+        # (hla_backward_z, four passes), against hla_forward + hla_backward
+        def time_plan(run):
+            for _ in range(10):
+                run()
+            torch.cuda.synchronize()
+            t_start.record()
+            for _ in range(args.backward_steps):
+                run()
+            t_end.record()
+            torch.cuda.synchronize()
+            return t_start.elapsed_time(t_end) / args.backward_steps
+
+        fplain = hla.ForwardPlan(qb, kb, vb, variant="hla2", chunk=chunk, seg_chunks=seg)
+        fz = hla.ForwardPlan(qb, kb, vb, variant="hla2", chunk=chunk, seg_chunks=seg, z=True)
+        fms, fzms = time_plan(fplain.run), time_plan(fz.run)
+        bzplan = hla.BackwardPlan(qb, kb, vb, dob, variant="hla2", seg_chunks=bseg, z=fz.z)
+        bzms = time_plan(bzplan.run)
+        backward["with_forward_z"] = {
+            "forward_ms": round(fms, 5), "forward_z_ms": round(fzms, 5),
+            "backward_z_ms": round(bzms, 5),
+            "forward_plus_backward_ms": round(fms + bms, 5),
+            "forward_z_plus_backward_z_ms": round(fzms + bzms, 5)}
+        log(f"[bench] forward + backward {fms + bms:.4f} ms; keeping z: forward {fzms:.4f} + "
+            f"backward {bzms:.4f} = {fzms + bzms:.4f} ms")
+        del fplain, fz, bzplan
         # third-order forward (variant hla3) on the same inputs: the LA pass
         # into the workspace, then the three second-order stages
         t3plan = hla.ForwardPlan(qb, kb, vb, variant="hla3", chunk=chunk, seg_chunks=seg)

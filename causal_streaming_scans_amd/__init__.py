@@ -71,6 +71,8 @@ def load():
     lib.hla_forward.restype = I
     lib.hla_forward_noalloc.argtypes = [P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P]
     lib.hla_forward_noalloc.restype = I
+    lib.hla_forward_z.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, FP, I, I, P, P, P, Z, P]
+    lib.hla_forward_z.restype = I
     lib.hla_forward_stage.argtypes = [I] + lib.hla_forward.argtypes
     lib.hla_forward_stage.restype = I
     lib.hla_step.argtypes = [P, P, P, P, I, I, I, I, I, I, FP, P, P]
@@ -81,6 +83,8 @@ def load():
     lib.hla_backward_workspace_bytes.restype = Z
     lib.hla_backward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, P, I, P, Z, P]
     lib.hla_backward.restype = I
+    lib.hla_backward_z.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, FP, I, P, Z, P]
+    lib.hla_backward_z.restype = I
     lib.hla_unmasked_workspace_bytes.argtypes = [I, I, I, I]
     lib.hla_unmasked_workspace_bytes.restype = Z
     lib.hla_unmasked_forward.argtypes = [P, P, P, P, I, I, I, I, I, I, P, Z, P]
@@ -173,7 +177,7 @@ class ForwardPlan:
 
     def __init__(self, q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
                  state_in=None, state_out=None, out=None, workspace=None, stream=None,
-                 staged=False):
+                 staged=False, z=None):
         import torch
         lib = load()
         for name, t in (("q", q), ("k", k), ("v", v)):
@@ -203,8 +207,17 @@ class ForwardPlan:
             if staged:
                 raise HLAError("hla_forward_stage needs the caller's workspace (shared by the stages)")
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if z is True:
+            z = torch.empty_like(q)
+        elif z is not None and z is not False:
+            _check_device_tensor("z", z)
+            if z.shape != q.shape or z.dtype != q.dtype:
+                raise HLAError("z must have the shape and dtype of q")
+        else:
+            z = None
         self.out = out
-        self._keep = (q, k, v, out, state_in, state_out, workspace)
+        self.z = z
+        self._keep = (q, k, v, out, state_in, state_out, workspace, z)
         self._gamma, g_ptr = _gamma_arg(gamma, H)
         VP, CI = ctypes.c_void_p, ctypes.c_int
         ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -230,7 +243,23 @@ class ForwardPlan:
         return self.out
 
     def run(self):
-        return self._call(self._lib.hla_forward)
+        """o, or (o, z) when the plan was made with ``z`` (hla_forward_z)."""
+        if self.z is None:
+            return self._call(self._lib.hla_forward)
+        self._call_z()
+        return self.out, self.z
+
+    def _call_z(self):
+        import torch
+        VP = ctypes.c_void_p
+        args = self._args[:4] + (VP(self.z.data_ptr()),) + self._args[4:]
+        if torch.cuda.current_device() == self._dev:
+            rc = self._lib.hla_forward_z(*args)
+        else:
+            with torch.cuda.device(self._dev):
+                rc = self._lib.hla_forward_z(*args)
+        if rc != 0:
+            raise HLAError(f"hla_forward_z failed: {status_str(rc)} (code {rc})")
 
     def stage(self, stage: int):
         return self._call(self._lib.hla_forward_stage, ctypes.c_int(int(stage)))
@@ -251,6 +280,16 @@ def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks
     Returns o [B, H, n, dv] (``out`` if given)."""
     return _forward_call(None, q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out,
                          out, workspace, stream)
+
+
+def hla_forward_z(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
+                  state_in=None, state_out=None, out=None, z=None, workspace=None, stream=None):
+    """hla_forward that also returns the keyed queries z_t = S_t q_t ([B, H,
+    n, d], q's dtype; into ``z`` if given) for hla_backward(..., z=z).
+    HLA-2 forms only.  Returns (o, z)."""
+    plan = ForwardPlan(q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
+                       workspace, stream, z=True if z is None else z)
+    return plan.run()
 
 
 def hla_forward_stage(stage, q, k, v, variant="hla2", gamma=None, chunk: int = 64,
@@ -338,11 +377,17 @@ class BackwardPlan:
     batch, at the given decays, 1 when gamma is None)."""
 
     def __init__(self, q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0,
-                 dq=None, dk=None, dv=None, workspace=None, stream=None, dgamma=None):
+                 dq=None, dk=None, dv=None, workspace=None, stream=None, dgamma=None, z=None):
         import torch
         lib = load()
         for name, t in (("q", q), ("k", k), ("v", v), ("do", do)):
             _check_device_tensor(name, t)
+        if z is not None:
+            _check_device_tensor("z", z)
+            if z.shape != q.shape or z.dtype != q.dtype:
+                raise HLAError("z must have the shape and dtype of q")
+            if dgamma is not None and dgamma is not False:
+                raise HLAError("dgamma is formed by hla_backward without z")
         if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or do.shape != q.shape:
             raise HLAError("expected q, k, v, do of one shape [B, H, n, d] (d == dv)")
         if not (q.dtype == k.dtype == v.dtype == do.dtype):
@@ -373,7 +418,7 @@ class BackwardPlan:
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         self.grads = tuple(grads)
-        self._keep = (q, k, v, do, *grads, workspace, dgamma)
+        self._keep = (q, k, v, do, *grads, workspace, dgamma, z)
         self._gamma, g_ptr = _gamma_arg(gamma, H)
         VP, CI = ctypes.c_void_p, ctypes.c_int
         dg_ptr = VP(dgamma.data_ptr() if dgamma is not None else None)
@@ -386,27 +431,35 @@ class BackwardPlan:
                       _stream_ptr(stream, q.device))
         self._dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
         self._lib = lib
+        self._fn = lib.hla_backward
+        if z is not None:
+            # hla_backward_z: z after v, no dgamma
+            self._args = self._args[:3] + (VP(z.data_ptr()),) + self._args[3:15] + self._args[16:]
+            self._fn = lib.hla_backward_z
 
     def run(self):
         import torch
         if torch.cuda.current_device() == self._dev:
-            rc = self._lib.hla_backward(*self._args)
+            rc = self._fn(*self._args)
         else:
             with torch.cuda.device(self._dev):
-                rc = self._lib.hla_backward(*self._args)
+                rc = self._fn(*self._args)
         if rc != 0:
-            raise HLAError(f"hla_backward failed: {status_str(rc)} (code {rc})")
+            raise HLAError(f"{self._fn.__name__} failed: {status_str(rc)} (code {rc})")
         return self.grads if self.dgamma is None else (*self.grads, self.dgamma)
 
 
 def hla_backward(q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0, dq=None, dk=None,
-                 dv=None, workspace=None, stream=None, dgamma=None):
+                 dv=None, workspace=None, stream=None, dgamma=None, z=None):
     """Gradients (dq, dk, dv) of the HLA-2 output with respect to q, k, v,
     given the upstream gradient do.  All four are [B, H, n, d] (d == dv), one
     dtype (bf16 or fp32), contiguous, on one GPU; gamma as in hla_forward.
-    With ``dgamma`` (True or an fp32 [H] tensor) also returns dL/dgamma."""
+    With ``dgamma`` (True or an fp32 [H] tensor) also returns dL/dgamma.
+    With ``z`` (variant "hla2", the keyed queries hla_forward_z returned for
+    the same q, k, gamma) the backward skips recomputing them
+    (hla_backward_z); not together with ``dgamma``."""
     return BackwardPlan(q, k, v, do, variant, gamma, seg_chunks, dq, dk, dv, workspace,
-                        stream, dgamma).run()
+                        stream, dgamma, z).run()
 
 
 def unmasked_workspace_bytes(B, H, n, d) -> int:

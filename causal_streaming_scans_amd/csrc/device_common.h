@@ -398,6 +398,28 @@ __device__ __forceinline__ void store_rows_out(const T *ot, __amdgpu_buffer_rsrc
     }
 }
 
+// Rows row0 .. row0+15, columns col0 .. col0+COLS-1 of an LdsTile matrix
+// (tile: its base) to global rows row0g .. (row0g+15) of LDG columns through
+// the buffer resource rs, in 16-byte pieces by the lanes of one wave.  The
+// rows may have been written by other waves: the caller orders those writes
+// before these reads with a barrier.
+template <typename T, typename TL, int COLS, int LDG>
+__device__ __forceinline__ void copy_rows_out(const T *tile, __amdgpu_buffer_rsrc_t rs, int row0,
+                                              int row0g, int col0) {
+    constexpr int VE = 16 / (int)sizeof(T);
+    constexpr int VPR = COLS / VE;
+    constexpr int NP = 16 * VPR;
+#pragma unroll
+    for (int h = 0; h < (NP + kWave - 1) / kWave; ++h) {
+        const int idx = h * kWave + lane_id();
+        const int rr = idx / VPR, cc = col0 + (idx % VPR) * VE;
+        if (NP % kWave == 0 || idx < NP) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(tile + TL::off(row0 + rr, cc));
+            store16_buf(rs, ((row0g + rr) * LDG + cc) * (int)sizeof(T), x);
+        }
+    }
+}
+
 // Row / column of accumulator element r held by this lane within its tile.
 __device__ __forceinline__ int acc_row(int r) { return ((lane_id() >> 4) << 2) + r; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }

@@ -415,7 +415,8 @@ __device__ __forceinline__ void hla2_fold_prefix(const FwdParams &p, int bh, int
 
 // ------------------------------------------------------------ forward kernel
 
-template <typename T, int D, int DV, int C, bool DECAY>
+// ZO: also write the keyed queries z_t = S_t q_t of every row to p.z_out.
+template <typename T, int D, int DV, int C, bool DECAY, bool ZO = false>
 __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, DECAY>::NT),
                              (hla2_fwd_blocks<T, D, DV, C, DECAY>()))
 void hla2_forward_kernel(FwdParams p) {
@@ -448,6 +449,8 @@ void hla2_forward_kernel(FwdParams p) {
     const T *v = static_cast<const T *>(p.v) + (size_t)bh * p.n * DV;
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
     const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
+    T *zo = ZO ? static_cast<T *>(p.z_out) + ((size_t)bh * p.n + t_begin) * D : nullptr;
+    const __amdgpu_buffer_rsrc_t zrsrc = rows_rsrc(zo, ZO ? t_end - t_begin : 0, D);
     using TO = typename G::TO;
     constexpr bool RO = hla2_rows_out<T, D, DV, C, DECAY>();
     T *const ot = sm.Ot + (RO ? w * 16 * TO::LD : 0);   // this wave's staging rows
@@ -695,6 +698,10 @@ void hla2_forward_kernel(FwdParams p) {
             }
             if constexpr (RO)
                 store_rows_out<T, TO, DV / NCG, DV>(ot, orsrc, c0 - t_begin + 16 * R, cg * (DV / NCG));
+            // the keyed queries, whole in Z since the barrier above: this
+            // wave's rows, its column group's share of them
+            if constexpr (ZO)
+                copy_rows_out<T, TK, D / NCG, D>(sm.Z, zrsrc, 16 * R, c0 - t_begin + 16 * R, cg * (D / NCG));
 
             // the rest of the state (W, u: products of Z) after every product,
             // then the T-typed copies, so no operand load waits behind a store

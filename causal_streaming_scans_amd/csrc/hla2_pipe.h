@@ -55,7 +55,8 @@ constexpr bool hla2_pipe_ok() {
            sizeof(Hla2PipeLds<T, D, DV, C>) <= 80 * 1024;
 }
 
-template <typename T, int D, int DV, int C>
+// ZO: also write the keyed queries z_t = S_t q_t of every row to p.z_out.
+template <typename T, int D, int DV, int C, bool ZO = false>
 __global__ __launch_bounds__((Hla2Cfg<T, D, DV, C, false>::NT), 2)
 void hla2_forward_pipe_kernel(FwdParams p) {
     using G = Hla2Cfg<T, D, DV, C, false>;
@@ -82,6 +83,8 @@ void hla2_forward_pipe_kernel(FwdParams p) {
     T *o = static_cast<T *>(p.o) + (size_t)bh * p.n * DV;
     // this segment's rows of o; stores past its last valid row are dropped
     const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
+    T *zo = ZO ? static_cast<T *>(p.z_out) + ((size_t)bh * p.n + t_begin) * D : nullptr;
+    const __amdgpu_buffer_rsrc_t zrsrc = rows_rsrc(zo, ZO ? t_end - t_begin : 0, D);
 
     ChunkRegs<T, C, D, NT> rk;
     ChunkRegs<T, C, DV, NT> rv;
@@ -154,12 +157,14 @@ void hla2_forward_pipe_kernel(FwdParams p) {
                 mma_tn_grp<gr.nr, gr.nc, C, TK, TV, true>(acc + gr.first, sm.Z[b], 16 * ti0, sm.V[b], 16 * tj0);
             });
         };
-        // Z of the staged chunk (queries qf) into Z[b]
-        auto keyed = [&](const RowFrags<T, D> &qf, int b) {
+        // Z of the staged chunk c (queries qf) into Z[b]; with ZO this
+        // wave's rows of it, which it wrote itself, also go out whole
+        auto keyed = [&](const RowFrags<T, D> &qf, int b, int c) {
             Frag16<T> Lf[R + 1];
             scores_t<T, D, R, TK, false>(Lf, sm.K, qf, tau, nullptr, 1);
             z_tiles<T, D, R, 1, G::ZJ, TK, false, TS>(qf, Lf, sm.St, sm.K, sm.Z[b], nullptr, 1.f,
                                                       nullptr, 0, tau);
+            if constexpr (ZO) store_rows_out<T, TK, D>(sm.Z[b] + 16 * R * TK::LD, zrsrc, C * c + 16 * R);
         };
         // o of chunk c (queries qf, keyed queries Z[b], values V[b]):
         // Q W0 + tril(Q Z^T) V, over Q u0 + tril(Q Z^T) 1 for the ratio form
@@ -200,7 +205,7 @@ void hla2_forward_pipe_kernel(FwdParams p) {
             qa.mask_rows(valid_of(0) - 16 * R);
             if (nch > 1) load_chunk(1);
             __syncthreads();
-            keyed(qa, 0);
+            keyed(qa, 0, 0);
             advance_s();
             __syncthreads();
             store_s();
@@ -216,7 +221,7 @@ void hla2_forward_pipe_kernel(FwdParams p) {
         int j = 0;
         for (; j + 1 < nch; ++j) {
             const int b = j & 1;
-            keyed(qb, b ^ 1);
+            keyed(qb, b ^ 1, j + 1);
             read_out(qa, b, j);
             advance_w(b);
             advance_s();

@@ -118,10 +118,12 @@ struct Pass {
     const void *add2;
 };
 
-// Inputs and gradients of one backward call.
+// Inputs and gradients of one backward call; z: the forward's keyed queries
+// (HLA-2 only), or null to recompute them.
 struct Grads {
     const void *q, *k, *v, *dout;
     void *dq, *dk, *dv;
+    const void *z = nullptr;
 };
 
 struct BwdCtx {
@@ -152,6 +154,15 @@ struct BwdCtx {
         const LaLaunch fn = ps.form == SYM ? la.sym : ps.form == DUAL ? la.dual : la.plain;
         return fn(p, s, ps.summaries) == hipSuccess;
     }
+    // the segment-state launch of a plain pass alone
+    bool states(const Pass &ps) const {
+        LaParams p = *ps.base;
+        p.b = ps.b;
+        p.c = ps.c;
+        p.reverse = ps.rev;
+        p.sums = ps.sums;
+        return la.states(p, s) == hipSuccess;
+    }
     hla_status run_all(const Pass *ps, int count) const {
         for (int i = 0; i < count; ++i)
             if (!run(ps[i])) return HLA_ERR_DEVICE;
@@ -159,9 +170,10 @@ struct BwdCtx {
     }
 };
 
-// HLA-2: Z = LA_g(Q, K, K), O = LA_{g^2}(Q, Z, V) (Z, dZ in tensors 0, 1).
+// HLA-2: Z = LA_g(Q, K, K), O = LA_{g^2}(Q, Z, V) (Z, dZ in tensors 0, 1;
+// Z is the caller's when x.z is given).
 hla_status backward_hla2(const BwdCtx &c, const Grads &x) {
-    void *Z = c.tensor(0), *dZ = c.tensor(1);
+    void *Z = x.z ? const_cast<void *>(x.z) : c.tensor(0), *dZ = c.tensor(1);
     const Pass passes[5] = {
         // Z  = LA_g(Q, K, K)
         {&c.p1, x.q, x.k, x.k, nullptr, Z, 0, PLAIN, c.sums_kk, true, nullptr, nullptr, nullptr},
@@ -174,7 +186,11 @@ hla_status backward_hla2(const BwdCtx &c, const Grads &x) {
         // dQ += LA_g(dZ, K, K), with the segment states of the first pass
         {&c.p1, dZ, x.k, x.k, x.dq, x.dq, 0, PLAIN, c.sums_kk, false, nullptr, nullptr, nullptr},
     };
-    return c.run_all(passes, 5);
+    if (!x.z) return c.run_all(passes, 5);
+    // Z from the forward: of the first pass only its segment states, which
+    // the last pass reads
+    if (!c.states(passes[0])) return HLA_ERR_DEVICE;
+    return c.run_all(passes + 1, 4);
 }
 
 // AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y, dY in tensors 0, 1).
@@ -666,6 +682,32 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o, int
     return HLA_OK;
 }
 
+hla_status hla_forward_z(const void *q, const void *k, const void *v, void *o, void *z, int B,
+                         int H, int n, int d, int dv, int dtype, int variant,
+                         const float *gamma_host, int chunk, int seg_chunks,
+                         const float *state_in, float *state_out, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+    FwdKernels kern;
+    FwdParams p;
+    Hla3Pass x3;
+    hla_status st = prepare_forward(q, k, v, o, B, H, n, d, dv, dtype, variant, gamma_host, chunk,
+                                    seg_chunks, state_in, state_out, workspace, workspace_bytes,
+                                    &kern, &p, &x3);
+    if (st != HLA_OK) return st;
+    if (variant != HLA_HLA2 && variant != HLA_HLA2_RATIO) return HLA_ERR_UNSUPPORTED;
+    if (n > 0 && !z) return HLA_ERR_NULL;
+    if (!kern.forward_z) return HLA_ERR_UNSUPPORTED;
+    if (z && (z == q || z == k || z == v || z == o)) return HLA_ERR_ARG;
+    p.z_out = z;
+    kern.forward = kern.forward_z;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int stage = 1; stage <= 3; ++stage) {
+        st = run_stage(stage, kern, p, variant, d, dv, x3, s);
+        if (st != HLA_OK) return st;
+    }
+    return HLA_OK;
+}
+
 hla_status hla_forward_stage(int stage, const void *q, const void *k, const void *v, void *o,
                              int B, int H, int n, int d, int dv, int dtype, int variant,
                              const float *gamma_host, int chunk, int seg_chunks,
@@ -772,10 +814,11 @@ size_t hla_backward_workspace_bytes(int variant, int B, int H, int n, int d, int
 }
 
 
-hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
-                        void *dk, void *dv_out, int B, int H, int n, int d, int dv, int dtype,
-                        int variant, const float *gamma_host, float *dgamma, int seg_chunks,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+static hla_status backward_impl(const void *q, const void *k, const void *v, const void *z,
+                                const void *dout, void *dq, void *dk, void *dv_out, int B, int H,
+                                int n, int d, int dv, int dtype, int variant,
+                                const float *gamma_host, float *dgamma, int seg_chunks,
+                                void *workspace, size_t workspace_bytes, void *stream) {
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
     if (n < 0) return HLA_ERR_SHAPE;
@@ -831,7 +874,7 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     for (int h = 0; h < kMaxDecayHeads; ++h)
         c.p2.gamma[h] = c.p1.gamma[h] * c.p1.gamma[h] * (c.p3_cube ? c.p1.gamma[h] : 1.f);
 
-    Grads io{q, k, v, dout, dq, dk, dv_out};
+    Grads io{q, k, v, dout, dq, dk, dv_out, z};
     void *partial = c.tensor(backward_tensors(variant, dtype, dg));
     // fp32 passes on bf16 inputs read and write fp32 copies (after the
     // variant's own tensors in the workspace)
@@ -865,6 +908,27 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
     for (int i = 0; i < 3; ++i)
         if (launch_convert(src[i], dst[i], count, false, c.s) != hipSuccess) return HLA_ERR_DEVICE;
     return HLA_OK;
+}
+
+hla_status hla_backward(const void *q, const void *k, const void *v, const void *dout, void *dq,
+                        void *dk, void *dv_out, int B, int H, int n, int d, int dv, int dtype,
+                        int variant, const float *gamma_host, float *dgamma, int seg_chunks,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    return backward_impl(q, k, v, nullptr, dout, dq, dk, dv_out, B, H, n, d, dv, dtype, variant,
+                         gamma_host, dgamma, seg_chunks, workspace, workspace_bytes, stream);
+}
+
+hla_status hla_backward_z(const void *q, const void *k, const void *v, const void *z,
+                          const void *dout, void *dq, void *dk, void *dv_out, int B, int H, int n,
+                          int d, int dv, int dtype, int variant, const float *gamma_host,
+                          int seg_chunks, void *workspace, size_t workspace_bytes, void *stream) {
+    hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
+    if (st != HLA_OK) return st;
+    if (variant != HLA_HLA2) return HLA_ERR_UNSUPPORTED;
+    if (n > 0 && !z) return HLA_ERR_NULL;
+    if (z && (z == dq || z == dk || z == dv_out)) return HLA_ERR_ARG;
+    return backward_impl(q, k, v, z, dout, dq, dk, dv_out, B, H, n, d, dv, dtype, variant,
+                         gamma_host, nullptr, seg_chunks, workspace, workspace_bytes, stream);
 }
 
 hla_status hla_step(const void *q, const void *k, const void *v, void *o, int B, int H, int d,

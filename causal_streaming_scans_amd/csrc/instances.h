@@ -30,16 +30,16 @@ hipError_t launch_hla2_summary(const FwdParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int C, bool DECAY>
+template <typename T, int D, int C, bool DECAY, bool ZO = false>
 hipError_t launch_hla2_forward(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg * p.BH),
+    hipLaunchKernelGGL((hla2_forward_kernel<T, D, D, C, DECAY, ZO>), dim3(p.nseg * p.BH),
                        dim3(Hla2Cfg<T, D, D, C, DECAY>::NT), 0, s, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int C>
+template <typename T, int D, int C, bool ZO = false>
 hipError_t launch_hla2_forward_pipe(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((hla2_forward_pipe_kernel<T, D, D, C>), dim3(p.nseg * p.BH),
+    hipLaunchKernelGGL((hla2_forward_pipe_kernel<T, D, D, C, ZO>), dim3(p.nseg * p.BH),
                        dim3(Hla2Cfg<T, D, D, C, false>::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -77,14 +77,14 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
         if (decay) {
             if constexpr (ahla_fits<T, D, C, true>()) {
                 *out = {launch_ahla_summary<T, D, C, true>, launch_up_sweep<T, D, false>,
-                        launch_ahla_forward<T, D, C, true>};
+                        launch_ahla_forward<T, D, C, true>, nullptr};
                 return true;
             }
             return false;
         }
         if constexpr (ahla_fits<T, D, C, false>()) {
             *out = {launch_ahla_summary<T, D, C, false>, launch_up_sweep<T, D, false>,
-                    launch_ahla_forward<T, D, C, false>};
+                    launch_ahla_forward<T, D, C, false>, nullptr};
             return true;
         }
         return false;
@@ -92,7 +92,7 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
     if (decay) {
         if constexpr (hla2_fits<T, D, C, true>()) {
             *out = {launch_hla2_summary<T, D, C, true>, launch_up_sweep<T, D, true>,
-                    launch_hla2_forward<T, D, C, true>};
+                    launch_hla2_forward<T, D, C, true>, launch_hla2_forward<T, D, C, true, true>};
             return true;
         }
         return false;
@@ -100,10 +100,10 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
     if constexpr (hla2_fits<T, D, C, false>()) {
         if constexpr (hla2_pipe_ok<T, D, D, C>())
             *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
-                    launch_hla2_forward_pipe<T, D, C>};
+                    launch_hla2_forward_pipe<T, D, C>, launch_hla2_forward_pipe<T, D, C, true>};
         else
             *out = {launch_hla2_summary<T, D, C, false>, launch_up_sweep<T, D, true>,
-                    launch_hla2_forward<T, D, C, false>};
+                    launch_hla2_forward<T, D, C, false>, launch_hla2_forward<T, D, C, false, true>};
         return true;
     }
     return false;

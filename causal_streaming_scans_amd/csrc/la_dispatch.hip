@@ -27,6 +27,15 @@ hipError_t launch_la(const LaParams &p, hipStream_t s, bool summaries) {
     return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t launch_la_states(const LaParams &p, hipStream_t s) {
+    constexpr int C = la_chunk<T, D>();
+    if (p.nseg <= 1) return hipSuccess;
+    hipLaunchKernelGGL((la_summary_kernel<T, D, C, false, false>), dim3((p.nseg - 1) * p.BH),
+                       dim3(LaCfg<T, D, C, false, false>::NT), 0, s, p);
+    return hipGetLastError();
+}
+
 // The DUAL form as two plain passes, for shapes whose fused LDS layout does
 // not fit: LA(a, b, c) into out, then LA(a2, c, b) into out2.
 template <typename T, int D>
@@ -96,6 +105,7 @@ bool la_set(LaLaunches *out) {
     out->decay_grad = launch_decay_grad<T, D>;
     static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), false, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
+    out->states = launch_la_states<T, D>;
     if constexpr (sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024)
         out->sym = launch_la<T, D, true, false>;
     else

@@ -174,13 +174,19 @@ struct LaRegs {
     }
 };
 
-// four consecutive values of T from global memory, as floats
-__device__ __forceinline__ f32x4 load4f(const bf16 *p) {
-    union { uint2 u; bf16 h[4]; } x;
-    x.u = *reinterpret_cast<const uint2 *>(p);
-    return f32x4{(float)x.h[0], (float)x.h[1], (float)x.h[2], (float)x.h[3]};
+// Four consecutive values held as loaded (bf16: 8 bytes) from an early load
+// to their use, converted to fp32 only there.
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> { uint2 u; };
+template <> struct Raw4<float> { f32x4 f; };
+__device__ __forceinline__ Raw4<bf16> load_raw4(const bf16 *p) { return {*reinterpret_cast<const uint2 *>(p)}; }
+__device__ __forceinline__ Raw4<float> load_raw4(const float *p) { return {*reinterpret_cast<const f32x4 *>(p)}; }
+__device__ __forceinline__ f32x4 raw4f(Raw4<bf16> x) {
+    union { uint2 u; bf16 h[4]; } y;
+    y.u = x.u;
+    return f32x4{(float)y.h[0], (float)y.h[1], (float)y.h[2], (float)y.h[3]};
 }
-__device__ __forceinline__ f32x4 load4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+__device__ __forceinline__ f32x4 raw4f(Raw4<float> x) { return x.f; }
 
 // acc[i][j] += sum_{k < K} M1[k][c1 + i] M2[k][c2 + j] for two row-major
 // [token][feature] LDS tiles: a product over the tokens, operands read with
@@ -387,10 +393,29 @@ void la_forward_kernel(LaParams p) {
     const T *Add = static_cast<const T *>(p.add);
     T *Out = static_cast<T *>(p.out);
 
+    constexpr int NO = Cfg::NOUT / Cfg::NW;   // output tiles per wave
     for (int l0 = l_begin; l0 < l_end; l0 += C) {
         const int cv = min(C, l_end - l0);   // valid rows of this chunk
         regs.store(s, p.n);
         if (l0 + C < l_end) regs.load(p, head_row, l0 + C);
+        // the addends of this wave's output tiles, loaded now so that their
+        // latency passes during the score phase (a row past the segment
+        // reads the chunk's first row instead, in bounds and never used);
+        // where Add is Out, each lane reads and later writes the same slots
+        Raw4<T> ad[NO], ad2[DUAL ? NO : 1];
+        if (Add || (DUAL && p.add2)) {
+#pragma unroll
+            for (int i = 0; i < NO; ++i) {
+                const int t = w + Cfg::NW * i;
+                const int tj = t % Cfg::TD, ti = t / Cfg::TD;
+                const int lt = l0 + 16 * ti + cl, lr = lt < l_end ? lt : l0;
+                const size_t row = head_row + (size_t)(p.reverse ? p.n - 1 - lr : lr);
+                const size_t off = row * D + 16 * tj + 4 * gq;
+                if (Add) ad[i] = load_raw4(Add + off);
+                if constexpr (DUAL)
+                    if (p.add2) ad2[i] = load_raw4(static_cast<const T *>(p.add2) + off);
+            }
+        }
         __syncthreads();
         // scores, transposed in registers so each lane holds four consecutive
         // sigma of one tau: every tile of D_g * (A B^T), the ones above the
@@ -425,7 +450,7 @@ void la_forward_kernel(LaParams p) {
         __syncthreads();
         // outputs, transposed: lane holds features 4gq..4gq+3 of token cl
 #pragma unroll
-        for (int i = 0; i < Cfg::NOUT / Cfg::NW; ++i) {
+        for (int i = 0; i < NO; ++i) {
             const int t = w + Cfg::NW * i;
             const int tj = t % Cfg::TD, ti = t / Cfg::TD;   // feature tile, token tile
             f32x4 acc1 = mma_cp<TR, TP, C>(zero4(), s.c, 16 * tj, s.p, 16 * ti);
@@ -443,9 +468,9 @@ void la_forward_kernel(LaParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = acc1[r] + sc * acc2[r];
                 if (Add) {
-                    const f32x4 ad = load4f(Add + off);
+                    const f32x4 a4 = raw4f(ad[i]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[r] += ad[r];
+                    for (int r = 0; r < 4; ++r) o[r] += a4[r];
                 }
                 store4(Out + off, o);
             }
@@ -463,9 +488,9 @@ void la_forward_kernel(LaParams p) {
                     for (int r = 0; r < 4; ++r) o[r] = b1[r] + sc * b2[r];
                     const size_t off = row * D + 16 * tj + 4 * gq;
                     if (p.add2) {
-                        const f32x4 ad = load4f(static_cast<const T *>(p.add2) + off);
+                        const f32x4 a4 = raw4f(ad2[i]);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) o[r] += ad[r];
+                        for (int r = 0; r < 4; ++r) o[r] += a4[r];
                     }
                     store4(static_cast<T *>(p.out2) + off, o);
                 }

@@ -15,6 +15,7 @@ struct FwdKernels {
     FwdLaunch summary;   // grid (nseg-1, BH): segment summaries from zero state
     FwdLaunch up_sweep;  // one launch per level, grid (pairs, BH): up-sweep of the scan
     FwdLaunch forward;   // grid (nseg, BH): prefix from the up-sweep nodes, chunked forward
+    FwdLaunch forward_z; // the same, also writing the keyed queries to p.z_out (HLA-2; else null)
 };
 
 // dtype: 0 = fp32, 1 = bf16.  ahla: AHLA family (else HLA-2).  Returns false
@@ -41,6 +42,8 @@ constexpr int kLaChunk = 64;
 typedef hipError_t (*LaLaunch)(const LaParams &, hipStream_t, bool summaries);
 struct LaLaunches {
     LaLaunch plain, sym, dual;
+    // the segment-state launch of the plain form alone (when p.nseg > 1)
+    hipError_t (*states)(const LaParams &, hipStream_t);
     hipError_t (*unit_column)(void *out, long rows, hipStream_t);   // rows (1, 0, ..., 0)
     hipError_t (*ratio_prep)(const RatioPrepParams &, hipStream_t);
     // both steps of the decay gradient; p.nblk is set by the host

@@ -8,6 +8,8 @@ into PyTorch autograd:
 
 * ``hla(q, k, v, variant, gamma)`` -- forward through ``hla_forward``,
   gradients through ``hla_backward``; both run in the library's HIP kernels;
+  for "hla2" the forward also keeps its keyed queries z_t = S_t q_t
+  (``hla_forward_z``), which the backward then does not recompute;
 * ``HLAAttention`` -- a sub-layer: bias-free q, k, v projections of the model
   dimension into heads, the HLA operator per head, heads merged, an output
   projection.  The four projections are plain GEMMs (torch, i.e. the ROCm
@@ -24,7 +26,7 @@ from __future__ import annotations
 
 import torch
 
-from . import hla_backward, hla_forward
+from . import hla_backward, hla_forward, hla_forward_z
 
 _BACKWARD_VARIANTS = ("hla2", "hla2_ratio", "ahla", "ahla_ratio", "hla3", "hla3_ratio")
 
@@ -35,12 +37,19 @@ class HLAFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q, k, v, variant, gamma, chunk):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-        o = hla_forward(q, k, v, variant=variant, gamma=gamma, chunk=chunk)
         ctx.gamma_is_tensor = isinstance(gamma, torch.Tensor)
-        if ctx.gamma_is_tensor:
-            ctx.save_for_backward(q, k, v, gamma)
+        want_dg = ctx.gamma_is_tensor and ctx.needs_input_grad[4]
+        # HLA-2 keeps the forward's keyed queries for the backward, which then
+        # skips recomputing them (the decay gradient's fp32 passes do not use them)
+        z = None
+        if variant == "hla2" and not want_dg:
+            o, z = hla_forward_z(q, k, v, variant=variant, gamma=gamma, chunk=chunk)
         else:
-            ctx.save_for_backward(q, k, v)
+            o = hla_forward(q, k, v, variant=variant, gamma=gamma, chunk=chunk)
+        if ctx.gamma_is_tensor:
+            ctx.save_for_backward(q, k, v, z, gamma)
+        else:
+            ctx.save_for_backward(q, k, v, z)
             ctx.gamma = gamma
         ctx.variant = variant
         return o
@@ -48,12 +57,12 @@ class HLAFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         if ctx.gamma_is_tensor:
-            q, k, v, gamma = ctx.saved_tensors
+            q, k, v, z, gamma = ctx.saved_tensors
         else:
-            (q, k, v), gamma = ctx.saved_tensors, ctx.gamma
+            (q, k, v, z), gamma = ctx.saved_tensors, ctx.gamma
         want_dg = ctx.gamma_is_tensor and ctx.needs_input_grad[4]
         res = hla_backward(q, k, v, do.contiguous(), variant=ctx.variant, gamma=gamma,
-                           dgamma=True if want_dg else None)
+                           dgamma=True if want_dg else None, z=None if want_dg else z)
         dgamma = None
         if want_dg:
             dgamma = res[3].to(gamma.device, gamma.dtype).reshape(gamma.shape)

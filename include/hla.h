@@ -164,6 +164,27 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * hla_forward that also writes the keyed queries z_t = S^K_t q_t (with a
+ * decay, S^K_t = sum_{s<=t} g^(t-s) k_s k_s^T) of every token to z, for a
+ * later hla_backward_z (page section "1. HLA de Segundo Orden": z_t is the
+ * query keyed by the running key moment; the backward's first pass would
+ * otherwise recompute it as Z = LA_g(Q, K, K)).
+ *
+ * z   device, [B][H][n][d], element type = dtype; not q, k, v or o.  Each
+ *     row is rounded once from its fp32 accumulation, as the forward stages
+ *     it for its own products.
+ * Other arguments, results and errors as hla_forward (o is bit for bit the
+ * same).  variant: HLA_HLA2 or HLA_HLA2_RATIO (z is the same for both),
+ * otherwise HLA_ERR_UNSUPPORTED; z NULL with n > 0: HLA_ERR_NULL; z equal
+ * to q, k, v or o: HLA_ERR_ARG.
+ */
+hla_status hla_forward_z(const void *q, const void *k, const void *v, void *o, void *z,
+                         int B, int H, int n, int d, int dv, int dtype, int variant,
+                         const float *gamma_host, int chunk, int seg_chunks,
+                         const float *state_in, float *state_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The three stages hla_forward runs, one at a time, on the same arguments
  * (page section "4. ... Escaneos Asociativos": segment summaries combined by
  * an exclusive Blelloch scan under the semidirect-product combine).  With
@@ -307,6 +328,27 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
                         void *dq, void *dk, void *dv_out, int B, int H, int n, int d, int dv,
                         int dtype, int variant, const float *gamma_host, float *dgamma,
                         int seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * hla_backward of the HLA_HLA2 output (with or without a decay) given the
+ * keyed queries Z that hla_forward_z wrote for the same q, k and decays:
+ * the first pass's main launch, Z = LA_g(Q, K, K), is skipped (its segment
+ * states of K K^T are still formed, for the last pass), four passes remain.
+ *
+ * z   device, [B][H][n][d], element type = dtype, as hla_forward_z wrote it;
+ *     not dq, dk or dv_out.
+ * Other arguments as hla_backward, without dgamma (the decay gradient's
+ * passes run in fp32 and recompute Z; use hla_backward for it); the same
+ * workspace size (hla_backward_workspace_bytes with with_dgamma = 0).
+ * Results: those of hla_backward up to the rounding of Z (the forward's
+ * row for row instead of the backward's own recomputation of it).
+ * Errors as hla_backward; variant other than HLA_HLA2: HLA_ERR_UNSUPPORTED;
+ * z NULL with n > 0: HLA_ERR_NULL; z equal to an output: HLA_ERR_ARG.
+ */
+hla_status hla_backward_z(const void *q, const void *k, const void *v, const void *z,
+                          const void *dout, void *dq, void *dk, void *dv_out, int B, int H,
+                          int n, int d, int dv, int dtype, int variant, const float *gamma_host,
+                          int seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Unmasked (non-causal) second-order operators: the operators of sections
  * "1. HLA de Segundo Orden" and "2. ... (AHLA)" without the causal masks,

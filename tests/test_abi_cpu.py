@@ -345,3 +345,52 @@ def test_noalloc_limit_and_validation(lib):
     assert call(1, 1, 100, 64, chunk=48) == ERR_UNSUP
     # no tokens: nothing to do, no workspace, no device work
     assert call(1, 1, 0, 64) == OK
+
+
+# ------------------------------------------- keyed queries kept for the backward
+
+def test_forward_z_validation(lib):
+    """hla_forward_z: hla_forward's checks first, then its own (HLA-2 forms
+    only, z needed for n > 0, z not one of q, k, v, o), all before any HIP
+    call."""
+    P = ctypes.c_void_p
+    fake, z = 0x1000, 0x2000
+    ws = hla.workspace_bytes("hla2", 1, 1, 4096, 64, 64, 64, 4)
+
+    def fz(zp=z, q=fake, variant=HLA2, n=4096, wsb=ws, B=1):
+        return lib.hla_forward_z(P(q), P(fake), P(fake), P(fake), P(zp), B, 1, n, 64, 64, BF16,
+                                 variant, None, 64, 4, None, None, P(fake), wsb, None)
+    assert fz(B=0) == ERR_SHAPE                 # the forward's own checks come first
+    assert fz(wsb=1) == ERR_WS
+    assert fz(variant=AHLA) == ERR_UNSUP
+    assert fz(variant=AHLA_RATIO) == ERR_UNSUP
+    assert fz(variant=4, wsb=1 << 40) == ERR_UNSUP   # third order
+    assert fz(zp=None) == ERR_NULL
+    assert fz(zp=fake) == ERR_ARG               # z is q (and k, v, o)
+    assert fz(zp=None, n=0) == OK               # no tokens, nothing enqueued
+
+
+def test_backward_z_validation(lib):
+    """hla_backward_z: HLA_HLA2 only, z needed for n > 0 and not an output."""
+    P = ctypes.c_void_p
+
+    def bz(z=5, variant=HLA2, n=128, dq=1, B=1):
+        return lib.hla_backward_z(P(1), P(1), P(1), P(z), P(1), P(dq), P(2), P(3), B, 2, n, 64,
+                                  64, BF16, variant, None, 0, P(1), 1 << 40, None)
+    assert bz(B=0) == ERR_SHAPE
+    assert bz(variant=HLA2_RATIO) == ERR_UNSUP
+    assert bz(variant=AHLA) == ERR_UNSUP
+    assert bz(variant=9) == ERR_ARG
+    assert bz(z=None) == ERR_NULL
+    assert bz(z=1) == ERR_ARG                   # z is dq
+    assert bz(z=None, n=0) == OK
+
+
+def test_binding_forward_z_and_backward_z_checks():
+    """The binding's own checks of z (no GPU call)."""
+    import torch
+    x = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(hla.HLAError):
+        hla.hla_forward_z(x, x, x)                 # CPU tensors are refused first
+    with pytest.raises(hla.HLAError):
+        hla.hla_backward(x, x, x, x, z=x)
