@@ -207,12 +207,14 @@ class ForwardPlan:
             if staged:
                 raise HLAError("hla_forward_stage needs the caller's workspace (shared by the stages)")
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # the first chained pass's rows: Z (HLA-2, rows of d) or Y (AHLA, rows of dv)
+        zlike = v if vid in (VARIANTS["ahla"], VARIANTS["ahla_ratio"]) else q
         if z is True:
-            z = torch.empty_like(q)
+            z = torch.empty_like(zlike)
         elif z is not None and z is not False:
             _check_device_tensor("z", z)
-            if z.shape != q.shape or z.dtype != q.dtype:
-                raise HLAError("z must have the shape and dtype of q")
+            if z.shape != zlike.shape or z.dtype != q.dtype:
+                raise HLAError("z must have the shape and dtype of q (HLA-2) or v (AHLA)")
         else:
             z = None
         self.out = out
@@ -284,9 +286,10 @@ def hla_forward(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks
 
 def hla_forward_z(q, k, v, variant="hla2", gamma=None, chunk: int = 64, seg_chunks: int = 0,
                   state_in=None, state_out=None, out=None, z=None, workspace=None, stream=None):
-    """hla_forward that also returns the keyed queries z_t = S_t q_t ([B, H,
-    n, d], q's dtype; into ``z`` if given) for hla_backward(..., z=z).
-    HLA-2 forms only.  Returns (o, z)."""
+    """hla_forward that also returns the rows of its first chained pass, for
+    hla_backward(..., z=z): HLA-2 forms the keyed queries z_t = S_t q_t
+    ([B, H, n, d]), AHLA forms y_t = P_t^T q_t ([B, H, n, dv]); q's dtype,
+    into ``z`` if given.  Returns (o, z)."""
     plan = ForwardPlan(q, k, v, variant, gamma, chunk, seg_chunks, state_in, state_out, out,
                        workspace, stream, z=True if z is None else z)
     return plan.run()
@@ -455,8 +458,8 @@ def hla_backward(q, k, v, do, variant="hla2", gamma=None, seg_chunks: int = 0, d
     given the upstream gradient do.  All four are [B, H, n, d] (d == dv), one
     dtype (bf16 or fp32), contiguous, on one GPU; gamma as in hla_forward.
     With ``dgamma`` (True or an fp32 [H] tensor) also returns dL/dgamma.
-    With ``z`` (variant "hla2", the keyed queries hla_forward_z returned for
-    the same q, k, gamma) the backward skips recomputing them
+    With ``z`` (variant "hla2" or "ahla": the rows hla_forward_z returned
+    for the same inputs and gamma) the backward skips recomputing them
     (hla_backward_z); not together with ``dgamma``."""
     return BackwardPlan(q, k, v, do, variant, gamma, seg_chunks, dq, dk, dv, workspace,
                         stream, dgamma, z).run()

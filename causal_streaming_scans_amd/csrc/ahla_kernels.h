@@ -137,7 +137,9 @@ __device__ __forceinline__ void ahla_y_tiles(const RowFrags<T, D> &qf, const Fra
     }
 }
 
-template <typename T, int D, int DV, int C, bool DECAY>
+// YO: also write the first pass's rows y_t = P_t^T q_t (Y = LA_g(Q, K, V))
+// to p.z_out.
+template <typename T, int D, int DV, int C, bool DECAY, bool YO = false>
 __global__ __launch_bounds__((AhlaCfg<T, D, DV, C>::NT), (ahla_fwd_blocks<T, D, DV, C, DECAY>()))
 void ahla_forward_kernel(FwdParams p) {
     using G = AhlaCfg<T, D, DV, C>;
@@ -170,6 +172,8 @@ void ahla_forward_kernel(FwdParams p) {
     // one wave per row tile: output rows staged in LDS, stored whole
     constexpr bool ROWS_OUT = NCG == 1 && sizeof(T) == 2;
     const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(o + (size_t)t_begin * DV, t_end - t_begin, DV);
+    T *yo = YO ? static_cast<T *>(p.z_out) + ((size_t)bh * p.n + t_begin) * DV : nullptr;
+    const __amdgpu_buffer_rsrc_t yrsrc = rows_rsrc(yo, YO ? t_end - t_begin : 0, DV);
 
     // the next chunk's data in registers: K, V for LDS; this wave's Q rows
     ChunkRegs<T, C, D, NT> rk;
@@ -361,6 +365,10 @@ void ahla_forward_kernel(FwdParams p) {
             }
             if constexpr (ROWS_OUT)
                 store_rows_out<T, TV, DV>(sm.Ot + (R * 16) * TV::LD, orsrc, c0 - t_begin + 16 * R);
+            // the rows of Y, whole since the barrier above: this wave's rows,
+            // its column group's share of them
+            if constexpr (YO)
+                copy_rows_out<T, TV, DV / NCG, DV>(sm.Y, yrsrc, 16 * R, c0 - t_begin + 16 * R, cg * (DV / NCG));
         });
         // advance the state: P0 <- g^c P0 + Kw^T V, E0 likewise with Y, mK0
         // with the ones column, nk0 with y1 (Kw: K rows weighted by

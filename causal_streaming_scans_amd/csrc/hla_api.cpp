@@ -193,9 +193,10 @@ hla_status backward_hla2(const BwdCtx &c, const Grads &x) {
     return c.run_all(passes + 1, 4);
 }
 
-// AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y, dY in tensors 0, 1).
+// AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y, dY in tensors 0, 1;
+// Y is the caller's when x.z is given).
 hla_status backward_ahla(const BwdCtx &c, const Grads &x) {
-    void *Y = c.tensor(0), *dY = c.tensor(1);
+    void *Y = x.z ? const_cast<void *>(x.z) : c.tensor(0), *dY = c.tensor(1);
     const Pass passes[5] = {
         // Y  = LA(Q, K, V)
         {&c.p1, x.q, x.k, x.v, nullptr, Y, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
@@ -208,7 +209,9 @@ hla_status backward_ahla(const BwdCtx &c, const Grads &x) {
         // dQ += LA(dY, V, K)
         {&c.p1, dY, x.v, x.k, x.dq, x.dq, 0, PLAIN, c.sums, true, nullptr, nullptr, nullptr},
     };
-    return c.run_all(passes, 5);
+    // Y from the forward: the first pass is not needed at all (no later
+    // pass reads its segment states)
+    return x.z ? c.run_all(passes + 1, 4) : c.run_all(passes, 5);
 }
 
 // Ratio HLA-2, o = num / den with den the v == 1 sum.  With G = dO / den and
@@ -694,7 +697,9 @@ hla_status hla_forward_z(const void *q, const void *k, const void *v, void *o, v
                                     seg_chunks, state_in, state_out, workspace, workspace_bytes,
                                     &kern, &p, &x3);
     if (st != HLA_OK) return st;
-    if (variant != HLA_HLA2 && variant != HLA_HLA2_RATIO) return HLA_ERR_UNSUPPORTED;
+    if (variant != HLA_HLA2 && variant != HLA_HLA2_RATIO && variant != HLA_AHLA &&
+        variant != HLA_AHLA_RATIO)
+        return HLA_ERR_UNSUPPORTED;
     if (n > 0 && !z) return HLA_ERR_NULL;
     if (!kern.forward_z) return HLA_ERR_UNSUPPORTED;
     if (z && (z == q || z == k || z == v || z == o)) return HLA_ERR_ARG;
@@ -924,7 +929,7 @@ hla_status hla_backward_z(const void *q, const void *k, const void *v, const voi
                           int seg_chunks, void *workspace, size_t workspace_bytes, void *stream) {
     hla_status st = check_common(B, H, d, dv, dtype, variant, gamma_host);
     if (st != HLA_OK) return st;
-    if (variant != HLA_HLA2) return HLA_ERR_UNSUPPORTED;
+    if (variant != HLA_HLA2 && variant != HLA_AHLA) return HLA_ERR_UNSUPPORTED;
     if (n > 0 && !z) return HLA_ERR_NULL;
     if (z && (z == dq || z == dk || z == dv_out)) return HLA_ERR_ARG;
     return backward_impl(q, k, v, z, dout, dq, dk, dv_out, B, H, n, d, dv, dtype, variant,

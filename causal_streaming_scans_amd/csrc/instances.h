@@ -51,9 +51,9 @@ hipError_t launch_ahla_summary(const FwdParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <typename T, int D, int C, bool DECAY>
+template <typename T, int D, int C, bool DECAY, bool YO = false>
 hipError_t launch_ahla_forward(const FwdParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C, DECAY>), dim3(p.nseg * p.BH),
+    hipLaunchKernelGGL((ahla_forward_kernel<T, D, D, C, DECAY, YO>), dim3(p.nseg * p.BH),
                        dim3(AhlaCfg<T, D, D, C>::NT), 0, s, p);
     return hipGetLastError();
 }
@@ -77,14 +77,14 @@ bool lookup_chunk(bool ahla, bool decay, FwdKernels *out) {
         if (decay) {
             if constexpr (ahla_fits<T, D, C, true>()) {
                 *out = {launch_ahla_summary<T, D, C, true>, launch_up_sweep<T, D, false>,
-                        launch_ahla_forward<T, D, C, true>, nullptr};
+                        launch_ahla_forward<T, D, C, true>, launch_ahla_forward<T, D, C, true, true>};
                 return true;
             }
             return false;
         }
         if constexpr (ahla_fits<T, D, C, false>()) {
             *out = {launch_ahla_summary<T, D, C, false>, launch_up_sweep<T, D, false>,
-                    launch_ahla_forward<T, D, C, false>, nullptr};
+                    launch_ahla_forward<T, D, C, false>, launch_ahla_forward<T, D, C, false, true>};
             return true;
         }
         return false;

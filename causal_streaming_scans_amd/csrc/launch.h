@@ -15,7 +15,7 @@ struct FwdKernels {
     FwdLaunch summary;   // grid (nseg-1, BH): segment summaries from zero state
     FwdLaunch up_sweep;  // one launch per level, grid (pairs, BH): up-sweep of the scan
     FwdLaunch forward;   // grid (nseg, BH): prefix from the up-sweep nodes, chunked forward
-    FwdLaunch forward_z; // the same, also writing the keyed queries to p.z_out (HLA-2; else null)
+    FwdLaunch forward_z; // the same, also writing the first pass's rows to p.z_out (HLA-2: Z, AHLA: Y)
 };
 
 // dtype: 0 = fp32, 1 = bf16.  ahla: AHLA family (else HLA-2).  Returns false

@@ -26,7 +26,8 @@ struct FwdParams {
     float *ws;        // workspace, see below (unused when nseg == 1)
     const float *state_in;   // [BH][state floats] or null
     float *state_out;        // [BH][state floats] or null
-    void *z_out;             // HLA-2: the keyed queries z_t = S_t q_t, [BH][n][D] rows of T, or null
+    void *z_out;             // rows of the first chained pass, or null: HLA-2 z_t = S_t q_t
+                             // ([BH][n][D]), AHLA y_t = P_t^T q_t ([BH][n][DV]); T
     float gamma[kMaxDecayHeads];  // decay of head h (1 when none)
     short seg_order[kMaxOrder];    // forward: segment run by rank r (nseg <= kMaxOrder)
 };

@@ -8,8 +8,9 @@ into PyTorch autograd:
 
 * ``hla(q, k, v, variant, gamma)`` -- forward through ``hla_forward``,
   gradients through ``hla_backward``; both run in the library's HIP kernels;
-  for "hla2" the forward also keeps its keyed queries z_t = S_t q_t
-  (``hla_forward_z``), which the backward then does not recompute;
+  for "hla2" and "ahla" the forward also keeps the rows of its first chained
+  pass (``hla_forward_z``: z_t = S_t q_t, y_t = P_t^T q_t), which the
+  backward then does not recompute;
 * ``HLAAttention`` -- a sub-layer: bias-free q, k, v projections of the model
   dimension into heads, the HLA operator per head, heads merged, an output
   projection.  The four projections are plain GEMMs (torch, i.e. the ROCm
@@ -39,10 +40,11 @@ class HLAFunction(torch.autograd.Function):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         ctx.gamma_is_tensor = isinstance(gamma, torch.Tensor)
         want_dg = ctx.gamma_is_tensor and ctx.needs_input_grad[4]
-        # HLA-2 keeps the forward's keyed queries for the backward, which then
-        # skips recomputing them (the decay gradient's fp32 passes do not use them)
+        # HLA-2 keeps the forward's keyed queries Z, AHLA its first pass Y, for
+        # the backward, which then skips recomputing them (the decay
+        # gradient's fp32 passes do not use them)
         z = None
-        if variant == "hla2" and not want_dg:
+        if variant in ("hla2", "ahla") and not want_dg:
             o, z = hla_forward_z(q, k, v, variant=variant, gamma=gamma, chunk=chunk)
         else:
             o = hla_forward(q, k, v, variant=variant, gamma=gamma, chunk=chunk)

@@ -164,19 +164,22 @@ hla_status hla_forward(const void *q, const void *k, const void *v, void *o,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * hla_forward that also writes the keyed queries z_t = S^K_t q_t (with a
- * decay, S^K_t = sum_{s<=t} g^(t-s) k_s k_s^T) of every token to z, for a
- * later hla_backward_z (page section "1. HLA de Segundo Orden": z_t is the
- * query keyed by the running key moment; the backward's first pass would
- * otherwise recompute it as Z = LA_g(Q, K, K)).
+ * hla_forward that also writes, for every token, the rows of the first of
+ * the operator's two chained passes, for a later hla_backward_z (which would
+ * otherwise recompute them):
+ *   HLA-2 forms: the keyed queries z_t = S^K_t q_t, S^K_t = sum_{s<=t}
+ *     g^(t-s) k_s k_s^T (page section "1. HLA de Segundo Orden": the query
+ *     keyed by the running key moment; Z = LA_g(Q, K, K)), rows of d;
+ *   AHLA forms: y_t = P_t^T q_t, P_t = sum_{s<=t} g^(t-s) k_s v_s^T (section
+ *     "2. ... (AHLA)": the first-order pass; Y = LA_g(Q, K, V)), rows of dv.
  *
- * z   device, [B][H][n][d], element type = dtype; not q, k, v or o.  Each
- *     row is rounded once from its fp32 accumulation, as the forward stages
- *     it for its own products.
+ * z   device, [B][H][n][d] (HLA-2) or [B][H][n][dv] (AHLA), element type =
+ *     dtype; not q, k, v or o.  Each row is rounded once from its fp32
+ *     accumulation, as the forward stages it for its own products.
  * Other arguments, results and errors as hla_forward (o is bit for bit the
- * same).  variant: HLA_HLA2 or HLA_HLA2_RATIO (z is the same for both),
- * otherwise HLA_ERR_UNSUPPORTED; z NULL with n > 0: HLA_ERR_NULL; z equal
- * to q, k, v or o: HLA_ERR_ARG.
+ * same).  variant: HLA_HLA2, HLA_HLA2_RATIO, HLA_AHLA or HLA_AHLA_RATIO (z
+ * does not depend on the ratio), otherwise HLA_ERR_UNSUPPORTED; z NULL with
+ * n > 0: HLA_ERR_NULL; z equal to q, k, v or o: HLA_ERR_ARG.
  */
 hla_status hla_forward_z(const void *q, const void *k, const void *v, void *o, void *z,
                          int B, int H, int n, int d, int dv, int dtype, int variant,
@@ -330,10 +333,11 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
                         int seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * hla_backward of the HLA_HLA2 output (with or without a decay) given the
- * keyed queries Z that hla_forward_z wrote for the same q, k and decays:
- * the first pass's main launch, Z = LA_g(Q, K, K), is skipped (its segment
- * states of K K^T are still formed, for the last pass), four passes remain.
+ * hla_backward of the HLA_HLA2 or HLA_AHLA output (with or without a decay)
+ * given the rows z that hla_forward_z wrote for the same q, k, v and decays.
+ * HLA-2: the first pass's main launch, Z = LA_g(Q, K, K), is skipped (its
+ * segment states of K K^T are still formed, for the last pass).  AHLA: the
+ * first pass, Y = LA_g(Q, K, V), is skipped whole.  Four passes remain.
  *
  * z   device, [B][H][n][d], element type = dtype, as hla_forward_z wrote it;
  *     not dq, dk or dv_out.
@@ -342,7 +346,8 @@ hla_status hla_backward(const void *q, const void *k, const void *v, const void 
  * workspace size (hla_backward_workspace_bytes with with_dgamma = 0).
  * Results: those of hla_backward up to the rounding of Z (the forward's
  * row for row instead of the backward's own recomputation of it).
- * Errors as hla_backward; variant other than HLA_HLA2: HLA_ERR_UNSUPPORTED;
+ * Errors as hla_backward; variant other than HLA_HLA2 or HLA_AHLA:
+ * HLA_ERR_UNSUPPORTED;
  * z NULL with n > 0: HLA_ERR_NULL; z equal to an output: HLA_ERR_ARG.
  */
 hla_status hla_backward_z(const void *q, const void *k, const void *v, const void *z,

@@ -350,9 +350,9 @@ def test_noalloc_limit_and_validation(lib):
 # ------------------------------------------- keyed queries kept for the backward
 
 def test_forward_z_validation(lib):
-    """hla_forward_z: hla_forward's checks first, then its own (HLA-2 forms
-    only, z needed for n > 0, z not one of q, k, v, o), all before any HIP
-    call."""
+    """hla_forward_z: hla_forward's checks first, then its own (HLA-2 and
+    AHLA forms, z needed for n > 0, z not one of q, k, v, o), all before any
+    HIP call."""
     P = ctypes.c_void_p
     fake, z = 0x1000, 0x2000
     ws = hla.workspace_bytes("hla2", 1, 1, 4096, 64, 64, 64, 4)
@@ -362,8 +362,6 @@ def test_forward_z_validation(lib):
                                  variant, None, 64, 4, None, None, P(fake), wsb, None)
     assert fz(B=0) == ERR_SHAPE                 # the forward's own checks come first
     assert fz(wsb=1) == ERR_WS
-    assert fz(variant=AHLA) == ERR_UNSUP
-    assert fz(variant=AHLA_RATIO) == ERR_UNSUP
     assert fz(variant=4, wsb=1 << 40) == ERR_UNSUP   # third order
     assert fz(zp=None) == ERR_NULL
     assert fz(zp=fake) == ERR_ARG               # z is q (and k, v, o)
@@ -371,7 +369,8 @@ def test_forward_z_validation(lib):
 
 
 def test_backward_z_validation(lib):
-    """hla_backward_z: HLA_HLA2 only, z needed for n > 0 and not an output."""
+    """hla_backward_z: HLA_HLA2 and HLA_AHLA, z needed for n > 0 and not an
+    output."""
     P = ctypes.c_void_p
 
     def bz(z=5, variant=HLA2, n=128, dq=1, B=1):
@@ -379,7 +378,7 @@ def test_backward_z_validation(lib):
                                   64, BF16, variant, None, 0, P(1), 1 << 40, None)
     assert bz(B=0) == ERR_SHAPE
     assert bz(variant=HLA2_RATIO) == ERR_UNSUP
-    assert bz(variant=AHLA) == ERR_UNSUP
+    assert bz(variant=AHLA_RATIO) == ERR_UNSUP
     assert bz(variant=9) == ERR_ARG
     assert bz(z=None) == ERR_NULL
     assert bz(z=1) == ERR_ARG                   # z is dq
