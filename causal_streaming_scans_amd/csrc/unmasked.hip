@@ -132,17 +132,20 @@ __global__ __launch_bounds__(256) void unmasked_gram_kernel(UnmaskedParams p) {
 
 // Step 1 for bf16 inputs, on the matrix cores: the same sums as
 // unmasked_gram_kernel, G[i][j] += sum_t x_t[i] y_t[j], as 16 x 16 tiles of
-// mfma_f32_16x16x32_bf16 over 32-token tiles.  Each tile is staged
+// mfma_f32_16x16x32_bf16 over 64-token tiles.  Each tile is staged
 // row-major ([token][feature], LdsTile layout) with 16-byte copies, and both
 // operands (8 consecutive tokens of one feature per lane) come from the
-// transposing LDS read.  Wave w owns tiles w, w + 4, ... of [G1 tiles | G2
-// tiles]; accumulator element r of lane l is
-// G[16 ti + 4 (l / 16) + r][16 tj + l % 16].
+// transposing LDS read.  The next tile's rows are loaded into registers
+// while the current one is multiplied, and an operand that is another one's
+// tensor (K in K^T K; K in both moments of AHLA) is loaded and staged once.
+// Wave w owns tiles w, w + 4, ... of [G1 tiles | G2 tiles]; accumulator
+// element r of lane l is G[16 ti + 4 (l / 16) + r][16 tj + l % 16].
 template <int D>
 __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams p) {
     using TL = LdsTile<bf16, D>;
-    constexpr int TT = 32, NTD = D / 16, NT1 = NTD * NTD, NT = 2 * NT1;
+    constexpr int TT = 64, NTD = D / 16, NT1 = NTD * NTD, NT = 2 * NT1;
     constexpr int TPW = (NT + 3) / 4;
+    constexpr int VPR = D / 8, NVEC = TT * VPR, NV = (NVEC + 255) / 256;   // 16-byte pieces
     __shared__ alignas(16) bf16 tiles[4][TT * TL::LD];
     const int bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = wave_id();
     const long per = (p.n + p.nblk - 1) / p.nblk;
@@ -151,20 +154,50 @@ __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams 
     const size_t head = (size_t)bh * p.n * D;
     const bf16 *src[4] = {static_cast<const bf16 *>(p.x) + head, static_cast<const bf16 *>(p.y) + head,
                           static_cast<const bf16 *>(p.u) + head, static_cast<const bf16 *>(p.w) + head};
+    // LDS tile of each operand: a tensor that equals an earlier operand's
+    // shares its tile (wave-uniform: kernel arguments only)
+    const int slot[4] = {0, p.y == p.x ? 0 : 1, p.u == p.x ? 0 : (p.u == p.y ? 1 : 2),
+                         p.w == p.x ? 0 : (p.w == p.y ? 1 : (p.w == p.u ? 2 : 3))};
+    uint4 rg[4][NV];
+    auto load = [&](long t0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            if (slot[a] != a) continue;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = tid + 256 * i, r = e / VPR, c = 8 * (e % VPR);
+                const long t = t0 + r;
+                // a row past the range reads the range's first row (in bounds)
+                // and is stored as zeros
+                const long tr = (e < NVEC && t < t_end) ? t : t_begin;
+                rg[a][i] = *reinterpret_cast<const uint4 *>(src[a] + (size_t)tr * D + (e < NVEC ? c : 0));
+            }
+        }
+    };
+    auto stage = [&](long t0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            if (slot[a] != a) continue;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = tid + 256 * i, r = e / VPR, c = 8 * (e % VPR);
+                if (e < NVEC) {
+                    const unsigned m = t0 + r < t_end ? 0xffffffffu : 0u;
+                    uint4 x = rg[a][i];
+                    x.x &= m; x.y &= m; x.z &= m; x.w &= m;
+                    *reinterpret_cast<uint4 *>(&tiles[a][TL::off(r, c)]) = x;
+                }
+            }
+        }
+    };
     f32x4 acc[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t_begin < t_end) load(t_begin);
     for (long t0 = t_begin; t0 < t_end; t0 += TT) {
-        for (int e = tid; e < TT * (D / 8); e += 256) {
-            const int r = e / (D / 8), c = 8 * (e % (D / 8));
-            const long t = t0 + r;
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const bf16x8 v = t < t_end ? *reinterpret_cast<const bf16x8 *>(src[a] + (size_t)t * D + c)
-                                           : bf16x8{};
-                *reinterpret_cast<bf16x8 *>(&tiles[a][TL::off(r, c)]) = v;
-            }
-        }
+        __syncthreads();   // the previous tile's readers are done
+        stage(t0);
+        if (t0 + TT < t_end) load(t0 + TT);
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < TPW; ++m) {
@@ -172,12 +205,13 @@ __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams 
             if (tau < NT) {
                 const int mat = tau / NT1, rem = tau % NT1;
                 const int ti = rem / NTD, tj = rem % NTD;
-                const bf16 *A = tiles[mat == 0 ? 0 : 2], *Bm = tiles[mat == 0 ? 1 : 3];
-                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_op8_tt<TL>(A, 0, 16 * ti),
-                                                                 ld_op8_tt<TL>(Bm, 0, 16 * tj), acc[m], 0, 0, 0);
+                const bf16 *A = tiles[slot[mat == 0 ? 0 : 2]], *Bm = tiles[slot[mat == 0 ? 1 : 3]];
+#pragma unroll
+                for (int k0 = 0; k0 < TT; k0 += 32)
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld_op8_tt<TL>(A, k0, 16 * ti),
+                                                                     ld_op8_tt<TL>(Bm, k0, 16 * tj), acc[m], 0, 0, 0);
             }
         }
-        __syncthreads();
     }
     float *out = p.partial + ((size_t)bh * p.nblk + blockIdx.x) * 2 * D * D;
 #pragma unroll
@@ -194,41 +228,80 @@ __global__ __launch_bounds__(256) void unmasked_gram_mfma_kernel(UnmaskedParams 
 }
 
 // Step 2: workgroup bh sums its partials in block order and forms T = G1 G2.
+// The sums run over 16-byte pieces with every block's loads in flight
+// together; G1 is kept transposed so that each thread's 4 x 4 block of T
+// reads one 16-byte piece of each factor per step over m.
 template <int D>
 __global__ __launch_bounds__(256) void unmasked_product_kernel(UnmaskedParams p) {
-    __shared__ alignas(16) float g1[D * D], g2[D * D];
+    constexpr int Q4 = D * D / 4, NBK = (D / 4) * (D / 4), BPT = (NBK + 255) / 256;
+    __shared__ alignas(16) float g1t[D * D], g2[D * D];
     const int bh = blockIdx.x, tid = threadIdx.x;
     const float *part = p.partial + (size_t)bh * p.nblk * 2 * D * D;
-    for (int e = tid; e < D * D; e += 256) {
-        float s1 = 0.f, s2 = 0.f;
-        for (int x = 0; x < p.nblk; ++x) {
-            s1 += part[(size_t)x * 2 * D * D + e];
-            s2 += part[(size_t)x * 2 * D * D + D * D + e];
+    for (int e = tid; e < Q4; e += 256) {
+        f32x4 s1 = zero4(), s2 = zero4();
+        int x = 0;
+        for (; x + 4 <= p.nblk; x += 4) {
+            f32x4 a[4], b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a[u] = *reinterpret_cast<const f32x4 *>(part + (size_t)(x + u) * 2 * D * D + 4 * e);
+                b[u] = *reinterpret_cast<const f32x4 *>(part + (size_t)(x + u) * 2 * D * D + D * D + 4 * e);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s1 += a[u];
+                s2 += b[u];
+            }
         }
-        g1[e] = s1;
-        g2[e] = s2;
+        for (; x < p.nblk; ++x) {
+            s1 += *reinterpret_cast<const f32x4 *>(part + (size_t)x * 2 * D * D + 4 * e);
+            s2 += *reinterpret_cast<const f32x4 *>(part + (size_t)x * 2 * D * D + D * D + 4 * e);
+        }
+        const int i = (4 * e) / D, j = (4 * e) % D;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g1t[(j + c) * D + i] = s1[c];
+        *reinterpret_cast<f32x4 *>(&g2[4 * e]) = s2;
     }
     __syncthreads();
     float *Tm = p.tmat + (size_t)bh * D * D;
-    for (int e = tid; e < D * D; e += 256) {
-        const int i = e / D, j = e % D;
-        float acc = 0.f;
-        for (int m = 0; m < D; ++m) acc += g1[i * D + m] * g2[m * D + j];
-        Tm[e] = acc;
-        p.tmat_t[(size_t)bh * D * D + j * D + i] = (bf16)acc;
+    bf16 *Tt = p.tmat_t + (size_t)bh * D * D;
+#pragma unroll
+    for (int bb = 0; bb < BPT; ++bb) {
+        const int blk = tid + 256 * bb;
+        if (blk < NBK) {
+            const int i0 = 4 * (blk / (D / 4)), j0 = 4 * (blk % (D / 4));
+            f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+            for (int m = 0; m < D; ++m) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&g1t[m * D + i0]);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(&g2[m * D + j0]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] += a[r] * b;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) *reinterpret_cast<f32x4 *>(Tm + (i0 + r) * D + j0) = acc[r];
+            // T^T rows j0 .. j0+3, columns i0 .. i0+3, in bf16
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                store4(Tt + (j0 + c) * D + i0, f32x4{acc[0][c], acc[1][c], acc[2][c], acc[3][c]});
+        }
     }
 }
 
 // Step 3 for bf16 inputs and D >= 32, on the matrix cores: o = Q T with T
 // rounded to bf16.  Wave w forms tokens t0 + 16 w .. + 15, all D columns, as
-// D/16 tiles of mfma_f32_16x16x32_bf16: lane l's A operand is 8 consecutive
-// features of token 16 w + l % 16 (one 16-byte load from HBM), its B operand
-// 8 consecutive rows of column 16 tj + l % 16 of T, i.e. a 16-byte piece of
-// a row of T^T (staged in LDS); accumulator r is o[16 w + 4 (l / 16) + r].
+// D/16 tiles of o^T = T^T Q^T on mfma_f32_16x16x32_bf16: lane l's operands
+// are 8 consecutive rows of column 16 tj + l % 16 of T, i.e. a 16-byte piece
+// of a row of T^T (staged in LDS), and 8 consecutive features of token
+// 16 w + l % 16 (one 16-byte load from HBM); accumulator r is column
+// 16 tj + 4 (l / 16) + r of that token.  The wave's 16 rows of o go through
+// LDS rows of its own and out as whole rows (stores past the sequence are
+// dropped by the buffer resource's range check).
 template <int D>
 __global__ __launch_bounds__(256) void unmasked_apply_mfma_kernel(UnmaskedParams p) {
     constexpr int NTD = D / 16, LD = D + 8;
+    using TO = LdsTile<bf16, D>;
     __shared__ alignas(16) bf16 tt[D][LD];
+    __shared__ alignas(16) bf16 ost[4][16 * TO::LD];
     const int bh = blockIdx.y, tid = threadIdx.x, l = lane_id(), w = wave_id();
     const bf16 *Tt = p.tmat_t + (size_t)bh * D * D;
     for (int e = tid; e < D * D / 8; e += 256) {
@@ -249,18 +322,17 @@ __global__ __launch_bounds__(256) void unmasked_apply_mfma_kernel(UnmaskedParams
 #pragma unroll
         for (int j = 0; j < NTD; ++j) {
             const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&tt[16 * j + (l & 15)][ks + 8 * (l >> 4)]);
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, acc[j], 0, 0, 0);
         }
     }
     bf16 *O = static_cast<bf16 *>(p.o) + (size_t)bh * p.n * D;
+    bf16 *ot = ost[w];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const long t = t0 + 4 * (l >> 4) + r;
-        if (t < p.n) {
-#pragma unroll
-            for (int j = 0; j < NTD; ++j) O[(size_t)t * D + 16 * j + (l & 15)] = (bf16)acc[j][r];
-        }
-    }
+    for (int j = 0; j < NTD; ++j) store4(ot + TO::off(l & 15, 16 * j + 4 * (l >> 4)), acc[j]);
+    const long valid = p.n - t0;
+    const __amdgpu_buffer_rsrc_t rs =
+        rows_rsrc(O + (size_t)t0 * D, valid <= 0 ? 0 : (valid < 16 ? (int)valid : 16), D);
+    store_rows_out<bf16, TO, D>(ot, rs, 0);
 }
 
 // Step 3: workgroup (x, bh) writes o_t = T^T q_t for 64 tokens; thread
