@@ -150,10 +150,16 @@ def kernel_key(name: str) -> str:
     """Short key of a stage kernel from its (mangled or demangled) name: the
     forward path's hla2_/ahla_ kernels and the up-sweep, and the backward's
     la_ kernels, whose two-slot (SYM) instances get a _sym suffix.  The
-    pipelined HLA-2 forward kernel is stage 3's kernel: hla2_forward_kernel."""
+    pipelined HLA-2 forward kernel is stage 3's kernel: hla2_forward_kernel.
+    The stage-3 forms that also write their first pass's rows (hla_forward_z;
+    the last template flag) get a _z suffix."""
     import re
     m = re.search(_STAGE_RE, name)
     key = (m.group(1) or "") + m.group(2) + "_kernel"
+    if key in ("hla2_forward_kernel", "ahla_forward_kernel"):
+        mz = re.search(r"Lb([01])EEEv", name) or re.search(r"(true|false)>\(", name)
+        if mz and mz.group(1) in ("1", "true"):
+            key = key[:-len("_kernel")] + "_z_kernel"
     if key.startswith("la_"):
         # template flags (SYM, DUAL): mangled ...Lb<0|1>ELb<0|1>E, or demangled
         mm = re.search(r"Lb([01])ELb([01])E", name)
