@@ -155,13 +155,19 @@ struct BwdCtx {
         return fn(p, s, ps.summaries) == hipSuccess;
     }
     // the segment-state launch of a plain pass alone
-    bool states(const Pass &ps) const {
+    static LaParams states_params(const Pass &ps) {
         LaParams p = *ps.base;
         p.b = ps.b;
         p.c = ps.c;
         p.reverse = ps.rev;
         p.sums = ps.sums;
-        return la.states(p, s) == hipSuccess;
+        return p;
+    }
+    bool states(const Pass &ps) const { return la.states(states_params(ps), s) == hipSuccess; }
+    // those of three plain passes in one launch
+    bool states3(const Pass &a, const Pass &b, const Pass &c3) const {
+        const LaParams p3[3] = {states_params(a), states_params(b), states_params(c3)};
+        return la.states3(p3, s) == hipSuccess;
     }
     hla_status run_all(const Pass *ps, int count) const {
         for (int i = 0; i < count; ++i)
@@ -188,9 +194,21 @@ hla_status backward_hla2(const BwdCtx &c, const Grads &x) {
     };
     if (!x.z) return c.run_all(passes, 5);
     // Z from the forward: of the first pass only its segment states, which
-    // the last pass reads
-    if (!c.states(passes[0])) return HLA_ERR_DEVICE;
-    return c.run_all(passes + 1, 4);
+    // the last pass reads.  Those, and the states of the next two passes,
+    // need only the inputs and Z: one launch forms all three, the third
+    // into the unused Z slot when it holds them (at d = 128 with very short
+    // segments it may not: three launches then)
+    if (c.sums_bytes > c.tensor_bytes) {
+        if (!c.states(passes[0])) return HLA_ERR_DEVICE;
+        return c.run_all(passes + 1, 4);
+    }
+    Pass dq = passes[1], dzv = passes[2];
+    dq.summaries = false;
+    dzv.summaries = false;
+    dzv.sums = reinterpret_cast<float *>(c.tensor(0));
+    if (!c.states3(passes[0], dq, dzv)) return HLA_ERR_DEVICE;
+    const Pass rest[4] = {dq, dzv, passes[3], passes[4]};
+    return c.run_all(rest, 4);
 }
 
 // AHLA: Y = LA(Q, K, V), O = LA(Q, K, Y), no decay (Y, dY in tensors 0, 1;

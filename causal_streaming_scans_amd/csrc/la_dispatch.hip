@@ -36,6 +36,18 @@ hipError_t launch_la_states(const LaParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// the segment states of three plain passes with the same sizes (nseg > 1)
+template <typename T, int D>
+hipError_t launch_la_states3(const LaParams *p3, hipStream_t s) {
+    constexpr int C = la_chunk<T, D>();
+    if (p3[0].nseg <= 1) return hipSuccess;
+    LaParams3 ps;
+    for (int i = 0; i < 3; ++i) ps.p[i] = p3[i];
+    hipLaunchKernelGGL((la_summary3_kernel<T, D, C>), dim3(3 * (p3[0].nseg - 1) * p3[0].BH),
+                       dim3(LaCfg<T, D, C, false, false>::NT), 0, s, ps);
+    return hipGetLastError();
+}
+
 // The DUAL form as two plain passes, for shapes whose fused LDS layout does
 // not fit: LA(a, b, c) into out, then LA(a2, c, b) into out2.
 template <typename T, int D>
@@ -106,6 +118,7 @@ bool la_set(LaLaunches *out) {
     static_assert(sizeof(LaLds<T, D, la_chunk<T, D>(), false, false>) <= 160 * 1024, "LDS");
     out->plain = launch_la<T, D, false, false>;
     out->states = launch_la_states<T, D>;
+    out->states3 = launch_la_states3<T, D>;
     if constexpr (sizeof(LaLds<T, D, la_chunk<T, D>(), true, false>) <= 160 * 1024)
         out->sym = launch_la<T, D, true, false>;
     else

@@ -292,11 +292,8 @@ struct LaState {
 // Summary of segment seg (< nseg-1): its state from zero, decayed to its end,
 // into p.sums.  Grid: (nseg-1) * BH workgroups, heads fastest.
 template <typename T, int D, int C, bool SYM, bool DUAL>
-__global__ __launch_bounds__((LaCfg<T, D, C, SYM, DUAL>::NT), (LaCfg<T, D, C, SYM, DUAL>::blocks()))
-void la_summary_kernel(LaParams p) {
+__device__ __forceinline__ void la_summary_body(const LaParams &p, int L, LaLds<T, D, C, SYM, DUAL> &s) {
     using Cfg = LaCfg<T, D, C, SYM, DUAL>;
-    __shared__ LaLds<T, D, C, SYM, DUAL> s;
-    const int L = blockIdx.x;
     const int bh = L % p.BH, seg = L / p.BH;
     const int w = wave_id();
     const float g = p.gamma[gamma_slot(bh, p.H)];
@@ -329,6 +326,28 @@ void la_summary_kernel(LaParams p) {
                 dst[(16 * si + 4 * gq + r) * D + 16 * sj + (l & 15)] = S.acc[i][r];
         }
     }
+}
+
+template <typename T, int D, int C, bool SYM, bool DUAL>
+__global__ __launch_bounds__((LaCfg<T, D, C, SYM, DUAL>::NT), (LaCfg<T, D, C, SYM, DUAL>::blocks()))
+void la_summary_kernel(LaParams p) {
+    __shared__ LaLds<T, D, C, SYM, DUAL> s;
+    la_summary_body<T, D, C, SYM, DUAL>(p, blockIdx.x, s);
+}
+
+// The segment states of three plain passes of the same sizes in one launch:
+// workgroups [i*(nseg-1)*BH, (i+1)*(nseg-1)*BH) form pass i's, so the
+// three fill the compute units together instead of in turn.
+struct LaParams3 {
+    LaParams p[3];
+};
+template <typename T, int D, int C>
+__global__ __launch_bounds__((LaCfg<T, D, C, false, false>::NT), (LaCfg<T, D, C, false, false>::blocks()))
+void la_summary3_kernel(LaParams3 ps) {
+    __shared__ LaLds<T, D, C, false, false> s;
+    const int per = (ps.p[0].nseg - 1) * ps.p[0].BH;
+    const int i = __builtin_amdgcn_readfirstlane(blockIdx.x / per);
+    la_summary_body<T, D, C, false, false>(ps.p[i], blockIdx.x - i * per, s);
 }
 
 // Main pass over segment seg.  Grid: nseg * BH workgroups, heads fastest.

@@ -44,6 +44,8 @@ struct LaLaunches {
     LaLaunch plain, sym, dual;
     // the segment-state launch of the plain form alone (when p.nseg > 1)
     hipError_t (*states)(const LaParams &, hipStream_t);
+    // three such launches (same BH, n, segments) as one: p3[0..2]
+    hipError_t (*states3)(const LaParams *p3, hipStream_t);
     hipError_t (*unit_column)(void *out, long rows, hipStream_t);   // rows (1, 0, ..., 0)
     hipError_t (*ratio_prep)(const RatioPrepParams &, hipStream_t);
     // both steps of the decay gradient; p.nblk is set by the host
