@@ -32,6 +32,17 @@ def test_kernel_keys():
         "la_forward_kernel_sym_f32"
     assert k("void hla::la_forward_kernel<float, 64, 32, false, false>(hla::LaParams)") == \
         "la_forward_kernel_f32"
+    # stage-3 forms that also write their first pass's rows (last template flag)
+    assert k("_ZN3hla24hla2_forward_pipe_kernelIDF16bLi64ELi64ELi64ELb1EEEvNS_9FwdParamsE") == \
+        "hla2_forward_z_kernel"
+    assert k("_ZN3hla24hla2_forward_pipe_kernelIDF16bLi64ELi64ELi64ELb0EEEvNS_9FwdParamsE") == \
+        "hla2_forward_kernel"
+    assert k("_ZN3hla19hla2_forward_kernelIDF16bLi128ELi128ELi64ELb1ELb0EEEvNS_9FwdParamsE") == \
+        "hla2_forward_kernel"
+    assert k("_ZN3hla19hla2_forward_kernelIDF16bLi128ELi128ELi64ELb1ELb1EEEvNS_9FwdParamsE") == \
+        "hla2_forward_z_kernel"
+    assert k("void hla::ahla_forward_kernel<__bf16, 64, 64, 64, false, true>(hla::FwdParams)") == \
+        "ahla_forward_z_kernel"
 
 
 def test_la_kernel_filter():
