@@ -40,28 +40,44 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Blocks of an (nTR x nTC)-tile matrix for NW waves: with WIDE, 2 x 4 when
+// that gives every wave exactly one block (8 waves at d = 128: six operand
+// reads per eight products instead of eight), else TileBlocks' square ones.
+template <int nTR, int nTC, int NW, bool WIDE>
+struct RectBlocks {
+    using Sq = TileBlocks<nTR, nTC, NW>;
+    static constexpr bool wide = WIDE && nTR % 2 == 0 && nTC % 4 == 0 && nTR * nTC == 8 * NW;
+    static constexpr int BRr = wide ? 2 : Sq::BR, BRc = wide ? 4 : Sq::BR;
+    static constexpr int nBR = nTR / BRr, nBC = nTC / BRc, NB = nBR * nBC;
+    static constexpr int PB = (NB + NW - 1) / NW;
+};
+
 // The even layout for any shape: the blocks of S and of W (and C) dealt to
 // the waves in turn, then the stripe tiles, all advanced after the barrier.
+// The summary takes 2 x 4 blocks where RectBlocks gives them (d = 128
+// summary 148 -> 137 us); the forward keeps square ones, since its chunk
+// loop has no registers left for the wider operand sets (with them its
+// spills doubled and the d = 128 forward went from 239 to 256 us).
 template <int nTD, int nTV, int NW, bool SUM>
 struct RoundRobinPlan {
-    using SB = TileBlocks<nTD, nTD, NW>;
-    using WB = TileBlocks<nTD, nTV, NW>;
+    using SB = RectBlocks<nTD, nTD, NW, SUM>;
+    using WB = RectBlocks<nTD, nTV, NW, SUM>;
     static constexpr int UJ = (nTD + NW - 1) / NW;
     static constexpr int NMW = SUM ? 2 : 1;   // W, and C in a summary
-    static constexpr int aS = SB::BR * SB::BR, aW = WB::BR * WB::BR;
+    static constexpr int aS = SB::BRr * SB::BRc, aW = WB::BRr * WB::BRc;
     static constexpr int NG = SB::PB + NMW * WB::PB + NMW * UJ;
     static constexpr int NA = SB::PB * aS + NMW * WB::PB * aW + NMW * UJ;
 
     static constexpr Grp grp(int i) {
         int base = 0;
-        if (i < SB::PB) return Grp{kS, 1, SB::BR, SB::BR, i * aS, -(i + 1), 0};
+        if (i < SB::PB) return Grp{kS, 1, SB::BRr, SB::BRc, i * aS, -(i + 1), 0};
         i -= SB::PB;
         base += SB::PB * aS;
-        if (i < WB::PB) return Grp{kW, 1, WB::BR, WB::BR, base + i * aW, -(i + 1), 0};
+        if (i < WB::PB) return Grp{kW, 1, WB::BRr, WB::BRc, base + i * aW, -(i + 1), 0};
         i -= WB::PB;
         base += WB::PB * aW;
         if (SUM) {
-            if (i < WB::PB) return Grp{kC, 1, WB::BR, WB::BR, base + i * aW, -(i + 1), 0};
+            if (i < WB::PB) return Grp{kC, 1, WB::BRr, WB::BRc, base + i * aW, -(i + 1), 0};
             i -= WB::PB;
             base += WB::PB * aW;
         }
@@ -81,8 +97,8 @@ struct RoundRobinPlan {
         } else {
             using TB = std::conditional_t<g.mat == kS, SB, WB>;
             const int blk = w + slot * NW;
-            ti = (blk / TB::nBC) * TB::BR;
-            tj = (blk % TB::nBC) * TB::BR;
+            ti = (blk / TB::nBC) * TB::BRr;
+            tj = (blk % TB::nBC) * TB::BRc;
             return blk < TB::NB;
         }
     }
